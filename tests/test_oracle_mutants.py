@@ -1,0 +1,75 @@
+"""Plant plausible mistakes in a copy of the oracle (on the CPU) and check that
+the pins catch every one of them."""
+import os
+import shutil
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+import pins
+
+# (name, text in w4a16_oracle.c, replacement)
+MUTANTS = [
+    ("no_mask_after_shift", "int uval = (int)((word >> (4 * (k % 8))) & 0xFu);",
+     "int uval = (int)((word >> (4 * (k % 8))));"),
+    ("signed_shift_no_mask", "uint32_t word = (uint32_t)packed[(k / 8) * N + n];\n    int uval = (int)((word >> (4 * (k % 8))) & 0xFu);",
+     "int32_t word = packed[(k / 8) * N + n];\n    int uval = (int)(word >> (4 * (k % 8)));"),
+    ("unpack_no_mask", "u[k * N + n] = (uint8_t)((word >> (4 * (k % 8))) & 0xFu);",
+     "u[k * N + n] = (uint8_t)((word >> (4 * (k % 8))));"),
+    ("round_half_away", "float q = nearbyintf(r);", "float q = roundf(r);"),
+    ("divide_by_8", "float s = amax / 7.0f;", "float s = amax / 8.0f;"),
+    ("offset_7_quantize", "u[k * N + n] = (uint8_t)((int)q + 8);", "u[k * N + n] = (uint8_t)((int)q + 7);"),
+    ("offset_7_dequant", "return (double)(uval - 8) *", "return (double)(uval - 7) *"),
+    ("reversed_nibble_order", "word |= ((uint32_t)(u[(8 * r + i) * N + n] & 0xF)) << (4 * i);",
+     "word |= ((uint32_t)(u[(8 * r + (7 - i)) * N + n] & 0xF)) << (4 * i);"),
+    ("scale_from_wrong_column", "oracle_f16_to_f64(s16[(k / G) * N + n]);",
+     "oracle_f16_to_f64(s16[(k / G) * N + (N - 1 - n)]);"),
+    ("gemm_dropped_term", "for (int64_t k = 0; k < K; ++k) {\n                double a = oracle_f16_to_f64(A16[m * K + k]);\n                for (int64_t n = n0; n < n1; ++n)\n                    acc[n - n0] += a * exact_weight",
+     "for (int64_t k = 1; k < K; ++k) {\n                double a = oracle_f16_to_f64(A16[m * K + k]);\n                for (int64_t n = n0; n < n1; ++n)\n                    acc[n - n0] += a * exact_weight"),
+    ("gemm_transposed_A", "double a = oracle_f16_to_f64(A16[m * K + k]);\n                for (int64_t n = n0; n < n1; ++n)\n                    acc[n - n0] += a * exact_weight",
+     "double a = oracle_f16_to_f64(A16[k * M + m]);\n                for (int64_t n = n0; n < n1; ++n)\n                    acc[n - n0] += a * exact_weight"),
+    ("f16_ties_away", "double n = nearbyint(a / ldexp(1.0, e - 10));", "double n = round(a / ldexp(1.0, e - 10));"),
+    ("f16_decode_bias", "v = ldexp((double)(1024 + f), e - 25);", "v = ldexp((double)(1024 + f), e - 24);"),
+    ("f16_subnormal_quantum", "v = ldexp((double)f, -24);", "v = ldexp((double)f, -23);"),
+    ("swiglu_swapped", "double g = C[m * N + j];\n            double up = C[m * N + I + j];",
+     "double up = C[m * N + j];\n            double g = C[m * N + I + j];"),
+    ("silu_sign", "g / (1.0 + exp(-g)) * up", "g / (1.0 + exp(g)) * up"),
+    ("scale_clamp_dropped_zero_group", "if (s < 1e-8f)\n                s = 1e-8f;", "if (s < 1e-8f)\n                s = 1.0f;"),
+]
+
+
+@pytest.fixture(scope="module")
+def workdir():
+    d = tempfile.mkdtemp(prefix="oracle_mutants_")
+    yield d
+    shutil.rmtree(d, ignore_errors=True)
+
+
+def _run_checks(o):
+    failed = []
+    for check in pins.FAST_CHECKS:
+        try:
+            check(o)
+        except (AssertionError, ValueError) as e:  # noqa: PERF203
+            failed.append(check.__name__)
+    return failed
+
+
+def test_mutant_list_applies():
+    src = open(oracle.SOURCE).read()
+    for name, old, new in MUTANTS:
+        assert src.count(old) == 1, name
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(workdir, name, old, new):
+    src = open(oracle.SOURCE).read()
+    assert src.count(old) == 1
+    path = os.path.join(workdir, name + ".c")
+    with open(path, "w") as f:
+        f.write(src.replace(old, new))
+    lib = oracle.build(path, os.path.join(workdir, "lib_%s.so" % name))
+    failed = _run_checks(oracle.Oracle(lib))
+    assert failed, "no pin caught mutant %s" % name
