@@ -1,0 +1,167 @@
+/*
+ * w4a16.h -- C ABI of the MI355X (gfx950) W4A16 weight-only INT4 GEMM.
+ *
+ * The operation (page "GPU Kernels for INT4 Inference, in depth",
+ * aicassindra.com, section "The job, stated precisely"): C = A * W with A the
+ * fp16 activations [M,K] and W [K,N] stored as 4-bit integers with one fp16
+ * scale per group of G = 128 consecutive values along K; the weight is
+ * w = (q - 8) * s; accumulation is FP32; the result must equal A times the
+ * dequantized weights up to floating-point rounding.
+ *
+ * Canonical packed format (same page, section "The data contract"):
+ *   packed  int32 [K/8, N]  row-major; value k of column n is the nibble at
+ *                           bits 4(k mod 8) .. 4(k mod 8)+3 of word [k/8, n],
+ *                           stored offset by 8 (0..15);
+ *   scales  fp16  [K/G, N]  row-major, passed as uint16_t bit patterns.
+ * The GEMM consumes a device-friendly permutation of that format built once
+ * at load time by w4a16_repack (the same page, section "Integrating a kernel
+ * into serving": repack once, at load, never per call).
+ *
+ * Conventions shared by every call:
+ *   - Return value: W4A16_OK (0) or a negative W4A16_ERR_* code; no exception
+ *     crosses the ABI.  w4a16_last_error() gives a readable message for the
+ *     calling thread's last failure.
+ *   - Pointers named *_d are device pointers (hipMalloc or equivalent); the
+ *     others are host pointers.  All buffers are owned by the caller; the
+ *     library keeps no reference to them after the call returns.
+ *   - Device work is enqueued on `stream` (a hipStream_t; NULL is the null
+ *     stream) and is asynchronous: a fault inside a kernel surfaces at the
+ *     caller's next synchronisation.  Launch errors are checked right after
+ *     each launch and reported as W4A16_ERR_HIP.
+ *   - fp16 values cross the ABI as uint16_t bit patterns.
+ *   - The GPU paths support G == 128 only (else W4A16_ERR_UNSUPPORTED);
+ *     K % 128 == 0, N % 8 == 0, and 16-byte aligned device pointers are
+ *     required (else W4A16_ERR_INVALID).  M is arbitrary (M == 0 is a no-op).
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define W4A16_OK 0
+#define W4A16_ERR_INVALID (-1)     /* null pointer, bad size or shape, misalignment */
+#define W4A16_ERR_UNSUPPORTED (-2) /* valid in the format, not handled here (G != 128) */
+#define W4A16_ERR_NONFINITE (-3)   /* host pack: W holds a NaN or an infinity */
+#define W4A16_ERR_HIP (-4)         /* a HIP runtime call or kernel launch failed */
+#define W4A16_ERR_WORKSPACE (-5)   /* workspace too small, or its allocation failed */
+
+/* Kernel paths (see w4a16_select_path). */
+#define W4A16_PATH_AUTO 0
+#define W4A16_PATH_DECODE 1  /* weight-streaming split-K kernel, small M */
+#define W4A16_PATH_PREFILL 2 /* LDS-tiled MFMA kernel with in-register dequant */
+#define W4A16_PATH_DENSE 3   /* dequantize to fp16 scratch, then dense fp16 GEMM */
+
+/* Flags for w4a16_gemm_ex: a path in the low 4 bits, OR'ed with: */
+#define W4A16_FLAG_SWIGLU 0x10 /* fused SwiGLU epilogue (see w4a16_gemm_swiglu) */
+
+typedef void *w4a16_stream_t; /* a hipStream_t */
+
+/* ---------------------------------------------------------------------------
+ * Quantize and pack (data contract, quantize_pack).  For each group g of G
+ * rows and column n: s = max|W[gG:(g+1)G, n]| / 7 in fp32, s = max(s, 1e-8),
+ * q = clamp(round_half_even(W / s), -8, 7) + 8 with an fp32 division, scale
+ * stored as fp16(s) (round to nearest even).
+ *   W_d       fp32 [K, N] row-major, device, read only
+ *   packed_d  int32 [K/8, N], device, written
+ *   scales_d  fp16 bits [K/G, N], device, written
+ * Runs one kernel on `stream`.  Non-finite W produces unspecified nibbles for
+ * that group (use w4a16_pack_host to have them rejected).
+ * Errors: W4A16_ERR_INVALID (null pointer, K % G, K % 8, N < 1, G < 1),
+ * W4A16_ERR_HIP.
+ * ------------------------------------------------------------------------- */
+int w4a16_pack(const float *W_d, int64_t K, int64_t N, int G, int32_t *packed_d,
+               uint16_t *scales_d, w4a16_stream_t stream);
+
+/* Same computation on host memory, for loaders that quantize on the CPU.
+ * nthreads <= 0 uses every hardware thread.  Returns W4A16_ERR_NONFINITE if W
+ * holds a NaN or an infinity (outputs are then unspecified). */
+int w4a16_pack_host(const float *W, int64_t K, int64_t N, int G, int32_t *packed,
+                    uint16_t *scales, int nthreads);
+
+/* ---------------------------------------------------------------------------
+ * Repacked layout, built once at load (data contract: "many production
+ * kernels permute this layout further at load time").  Columns are padded to
+ * a multiple of 32 (the pad dequantizes to zero).  Byte sizes of the two
+ * buffers, or a negative error code for an invalid shape.
+ * ------------------------------------------------------------------------- */
+int64_t w4a16_repacked_weight_bytes(int64_t K, int64_t N, int G);
+int64_t w4a16_repacked_scale_bytes(int64_t K, int64_t N, int G);
+
+/* Permute canonical (packed_d, scales_d) into the repacked buffers
+ * (rw_d: w4a16_repacked_weight_bytes, rs_d: w4a16_repacked_scale_bytes, both
+ * device, 16-byte aligned).  A bijection on the data: w4a16_unrepack inverts
+ * it exactly.  One kernel on `stream`.
+ * Errors: W4A16_ERR_INVALID, W4A16_ERR_UNSUPPORTED (G != 128), W4A16_ERR_HIP. */
+int w4a16_repack(const int32_t *packed_d, const uint16_t *scales_d, int64_t K, int64_t N,
+                 int G, void *rw_d, void *rs_d, w4a16_stream_t stream);
+
+/* Inverse of w4a16_repack, for verifying a load ("verify one layer after
+ * repacking").  Writes canonical packed_d [K/8,N] and scales_d [K/G,N]. */
+int w4a16_unrepack(const void *rw_d, const void *rs_d, int64_t K, int64_t N, int G,
+                   int32_t *packed_d, uint16_t *scales_d, w4a16_stream_t stream);
+
+/* Dequantize (data contract, dequantize): W16_d[k,n] = fp16((q - 8) * s),
+ * canonical fp16 [K, N] row-major, device.  Bit-exact with the definition. */
+int w4a16_dequant(const void *rw_d, const void *rs_d, int64_t K, int64_t N, int G,
+                  uint16_t *W16_d, w4a16_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * GEMM (the job, stated precisely): C_d[m,n] = sum_k A_d[m,k] * w[k,n], FP32
+ * accumulation, one fp16 rounding (nearest even) at the end.
+ *   A_d  fp16 bits [M, K] row-major, device
+ *   rw_d, rs_d  repacked weights of a [K, N] matrix (w4a16_repack)
+ *   C_d  fp16 bits [M, N] row-major, device, written
+ * The kernel path is chosen from (M, K, N) by a fixed table (decode for small
+ * M, prefill for large M, dense fallback for very large M).  Deterministic:
+ * the same call gives the same bits on every run.  Uses the library's
+ * per-device workspace, allocated on the first call that needs it; calls that
+ * overlap in time on one device (different streams) must use w4a16_gemm_ex
+ * with separate workspaces.
+ * Errors: W4A16_ERR_INVALID, W4A16_ERR_UNSUPPORTED, W4A16_ERR_WORKSPACE,
+ * W4A16_ERR_HIP.
+ * ------------------------------------------------------------------------- */
+int w4a16_gemm(const uint16_t *A_d, int64_t M, int64_t K, const void *rw_d, const void *rs_d,
+               int64_t N, int G, uint16_t *C_d, w4a16_stream_t stream);
+
+/* GEMM with the SwiGLU epilogue of a concatenated gate/up projection
+ * (FuTransformer, arXiv 2610.23796, section 2.1: Z = SiLU(X W_g) * (X W_u),
+ * gate and up sharing one GEMM).  Columns [0, N/2) of the weight are the gate
+ * projection and [N/2, N) the up projection; N % 64 == 0.  Writes
+ * Z_d[m,j] = fp16(silu(c[m,j]) * c[m,j+N/2]) computed from the FP32
+ * accumulators, Z_d fp16 bits [M, N/2] row-major. */
+int w4a16_gemm_swiglu(const uint16_t *A_d, int64_t M, int64_t K, const void *rw_d,
+                      const void *rs_d, int64_t N, int G, uint16_t *Z_d,
+                      w4a16_stream_t stream);
+
+/* Explicit form of the two calls above.  `flags` = path (W4A16_PATH_*, AUTO
+ * to use the table) | W4A16_FLAG_SWIGLU.  `workspace_d` (device, 256-byte
+ * aligned, at least w4a16_gemm_workspace_bytes) is owned by the caller; its
+ * first 64 KiB hold counters that must be zero before its first use and that
+ * every call leaves zero again.  workspace_d may be NULL to use the library's
+ * per-device workspace. */
+int w4a16_gemm_ex(const uint16_t *A_d, int64_t M, int64_t K, const void *rw_d,
+                  const void *rs_d, int64_t N, int G, uint16_t *out_d, int flags,
+                  void *workspace_d, int64_t workspace_bytes, w4a16_stream_t stream);
+
+/* Workspace bytes that w4a16_gemm_ex needs for this problem and flags. */
+int64_t w4a16_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N, int G, int flags);
+
+/* The path (W4A16_PATH_DECODE / PREFILL / DENSE) that AUTO picks for this
+ * problem, or a negative error code. */
+int w4a16_select_path(int64_t M, int64_t K, int64_t N, int G, int flags);
+
+/* Thread-local message for the calling thread's last error ("" if none). */
+const char *w4a16_last_error(void);
+
+/* Library version string. */
+const char *w4a16_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */

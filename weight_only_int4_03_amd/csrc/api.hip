@@ -1,0 +1,355 @@
+// C ABI of the W4A16 library: argument checks, path dispatch, workspace.
+// The operations and their citations are documented in include/w4a16.h.
+#include "w4a16.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "common.h"
+
+namespace w4a16 {
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+  return fail(W4A16_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Shape rules of the canonical format (data contract) plus this library's.
+int check_shape(int64_t K, int64_t N, int G, const char *who) {
+  if (G <= 0) return fail(W4A16_ERR_INVALID, "%s: G must be positive (got %d)", who, G);
+  if (K <= 0 || N <= 0) return fail(W4A16_ERR_INVALID, "%s: K and N must be positive", who);
+  if (K % 8 != 0 || K % G != 0)
+    return fail(W4A16_ERR_INVALID, "%s: K (%lld) must be a multiple of 8 and of G (%d)", who,
+                (long long)K, G);
+  return W4A16_OK;
+}
+
+int check_gpu_shape(int64_t K, int64_t N, int G, const char *who) {
+  int rc = check_shape(K, N, G, who);
+  if (rc != W4A16_OK) return rc;
+  if (G != kGroup)
+    return fail(W4A16_ERR_UNSUPPORTED, "%s: GPU paths support G == 128 only (got %d)", who, G);
+  if (N % 8 != 0)
+    return fail(W4A16_ERR_INVALID, "%s: N (%lld) must be a multiple of 8", who, (long long)N);
+  if (K > (int64_t)1 << 30 || N > (int64_t)1 << 30)
+    return fail(W4A16_ERR_INVALID, "%s: K or N too large", who);
+  return W4A16_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Library-owned per-device workspace: [counters (zeroed once) | scratch].
+
+struct DeviceWorkspace {
+  void *ptr = nullptr;
+  int64_t bytes = 0;
+};
+
+std::mutex g_ws_mutex;
+std::vector<DeviceWorkspace> g_ws;
+
+__global__ void zero_words(uint32_t *p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+int device_workspace(int64_t need, hipStream_t stream, void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  if ((int)g_ws.size() <= dev) g_ws.resize(dev + 1);
+  DeviceWorkspace &w = g_ws[dev];
+  if (w.bytes < need) {
+    if (w.ptr != nullptr) {
+      e = hipDeviceSynchronize();
+      if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+      hipFree(w.ptr);
+      w.ptr = nullptr;
+      w.bytes = 0;
+    }
+    int64_t bytes = need + need / 4;  // some headroom for later, larger calls
+    e = hipMalloc(&w.ptr, (size_t)bytes);
+    if (e != hipSuccess) {
+      w.ptr = nullptr;
+      return fail(W4A16_ERR_WORKSPACE, "workspace allocation of %lld bytes failed: %s",
+                  (long long)bytes, hipGetErrorString(e));
+    }
+    w.bytes = bytes;
+    const int64_t words = kCounterBytes / 4;
+    hipLaunchKernelGGL(zero_words, dim3((unsigned)ceil_div(words, 256)), dim3(256), 0, stream,
+                       (uint32_t *)w.ptr, words);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "counter zeroing launch");
+  }
+  *out = w.ptr;
+  return W4A16_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Dispatch.  Decode streams the weights once per call and wins while the
+// product is weight-bound; the tiled MFMA kernel takes over when the
+// activation rows make it compute-bound; the dense tier (dequantize once, then
+// a dense fp16 GEMM) is kept for very large M.  Thresholds from measurement
+// on MI355X.
+constexpr int64_t kDecodeMaxM = 32;
+constexpr int64_t kDenseMinM = 1 << 30;  // the fused kernel is kept at every M measured so far
+
+int select_path(int64_t M, int64_t K, int64_t N) {
+  (void)K;
+  (void)N;
+  if (M <= kDecodeMaxM) return W4A16_PATH_DECODE;
+  if (M >= kDenseMinM) return W4A16_PATH_DENSE;
+  return W4A16_PATH_PREFILL;
+}
+
+int64_t workspace_for(int path, const Problem &p) {
+  if (path == W4A16_PATH_DENSE) return kCounterBytes + dense_workspace_bytes(p);
+  if (path == W4A16_PATH_DECODE) {
+    Problem q = p;
+    q.M = p.M < kDecodeMaxM ? p.M : kDecodeMaxM;
+    const int64_t b = decode_workspace_bytes(q);
+    return b > 0 ? kCounterBytes + b : 0;
+  }
+  return 0;
+}
+
+int run_gemm(const uint16_t *A, int64_t M, int64_t K, const void *rw, const void *rs, int64_t N,
+             int G, uint16_t *out, int flags, void *workspace, int64_t ws_bytes,
+             hipStream_t stream) {
+  const char *who = (flags & W4A16_FLAG_SWIGLU) ? "w4a16_gemm_swiglu" : "w4a16_gemm";
+  int rc = check_gpu_shape(K, N, G, who);
+  if (rc != W4A16_OK) return rc;
+  if (M < 0) return fail(W4A16_ERR_INVALID, "%s: M must be >= 0", who);
+  if (M > ((int64_t)1 << 30)) return fail(W4A16_ERR_INVALID, "%s: M too large", who);
+  const bool swiglu = (flags & W4A16_FLAG_SWIGLU) != 0;
+  if (swiglu && N % 64 != 0)
+    return fail(W4A16_ERR_INVALID, "%s: N (%lld) must be a multiple of 64", who, (long long)N);
+  if (M == 0) return W4A16_OK;
+  if (!A || !rw || !rs || !out) return fail(W4A16_ERR_INVALID, "%s: null pointer", who);
+  if (!aligned16(A) || !aligned16(rw) || !aligned16(rs) || !aligned16(out))
+    return fail(W4A16_ERR_INVALID, "%s: device pointers must be 16-byte aligned", who);
+  int path = flags & 0xF;
+  if (path == W4A16_PATH_AUTO) path = select_path(M, K, N);
+  if (path < W4A16_PATH_DECODE || path > W4A16_PATH_DENSE)
+    return fail(W4A16_ERR_INVALID, "%s: unknown path %d", who, path);
+
+  Problem p{A, M, K, N, rw, rs, out, swiglu};
+  const int64_t need = workspace_for(path, p);
+  void *ws = workspace;
+  if (need > 0) {
+    if (ws == nullptr) {
+      rc = device_workspace(need, stream, &ws);
+      if (rc != W4A16_OK) return rc;
+    } else if (ws_bytes < need || ((uintptr_t)ws & 255u) != 0) {
+      return fail(W4A16_ERR_WORKSPACE, "%s: workspace needs %lld bytes, 256-byte aligned", who,
+                  (long long)need);
+    }
+  }
+
+  hipError_t e = hipSuccess;
+  if (path == W4A16_PATH_DECODE) {
+    // The decode kernels take up to 32 rows; larger M runs in 32-row slices.
+    const int64_t ldo = swiglu ? N / 2 : N;
+    for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += kDecodeMaxM) {
+      Problem q = p;
+      q.A = A + m0 * K;
+      q.out = out + m0 * ldo;
+      q.M = M - m0 < kDecodeMaxM ? M - m0 : kDecodeMaxM;
+      e = launch_decode(q, ws, stream);
+    }
+  } else if (path == W4A16_PATH_PREFILL) {
+    e = launch_prefill(p, stream);
+  } else {
+    e = launch_dense(p, ws, stream);
+  }
+  if (e != hipSuccess) return hip_fail(e, who);
+  return W4A16_OK;
+}
+
+}  // namespace
+}  // namespace w4a16
+
+using namespace w4a16;
+
+extern "C" {
+
+const char *w4a16_last_error(void) { return g_last_error.c_str(); }
+
+const char *w4a16_version(void) { return "w4a16-gfx950 0.1"; }
+
+int w4a16_pack(const float *W_d, int64_t K, int64_t N, int G, int32_t *packed_d,
+               uint16_t *scales_d, w4a16_stream_t stream) {
+  int rc = check_shape(K, N, G, "w4a16_pack");
+  if (rc != W4A16_OK) return rc;
+  if (G != kGroup) return fail(W4A16_ERR_UNSUPPORTED, "w4a16_pack: GPU pack supports G == 128");
+  if (K / G > 65535) return fail(W4A16_ERR_INVALID, "w4a16_pack: K too large");
+  if (!W_d || !packed_d || !scales_d) return fail(W4A16_ERR_INVALID, "w4a16_pack: null pointer");
+  hipError_t e = launch_pack(W_d, K, N, packed_d, scales_d, (hipStream_t)stream);
+  return e == hipSuccess ? W4A16_OK : hip_fail(e, "w4a16_pack");
+}
+
+// Host quantize+pack: threads split the columns.  fp32 IEEE division,
+// round-half-to-even (nearbyintf in the default rounding mode) and the
+// compiler's round-to-nearest-even float -> _Float16 conversion.
+int w4a16_pack_host(const float *W, int64_t K, int64_t N, int G, int32_t *packed,
+                    uint16_t *scales, int nthreads) {
+  int rc = check_shape(K, N, G, "w4a16_pack_host");
+  if (rc != W4A16_OK) return rc;
+  if (!W || !packed || !scales) return fail(W4A16_ERR_INVALID, "w4a16_pack_host: null pointer");
+  int nt = nthreads > 0 ? nthreads : (int)std::thread::hardware_concurrency();
+  if (nt < 1) nt = 1;
+  const int64_t chunk = 64;
+  const int64_t nchunks = ceil_div(N, chunk);
+  if (nt > nchunks) nt = (int)nchunks;
+  std::vector<int> bad(nt, 0);
+  auto work = [&](int id) {
+    std::vector<float> scale(chunk);
+    for (int64_t cb = id; cb < nchunks; cb += nt) {
+      const int64_t n0 = cb * chunk, n1 = n0 + chunk < N ? n0 + chunk : N;
+      for (int64_t g = 0; g < K / G; ++g) {
+        for (int64_t n = n0; n < n1; ++n) scale[n - n0] = 0.0f;
+        for (int64_t k = g * G; k < (g + 1) * G; ++k) {
+          const float *row = W + k * N;
+          for (int64_t n = n0; n < n1; ++n) {
+            const float a = std::fabs(row[n]);
+            if (!std::isfinite(row[n])) bad[id] = 1;
+            if (a > scale[n - n0]) scale[n - n0] = a;
+          }
+        }
+        for (int64_t n = n0; n < n1; ++n) {
+          float s = scale[n - n0] / 7.0f;
+          scale[n - n0] = s < 1e-8f ? 1e-8f : s;
+          _Float16 hs = (_Float16)scale[n - n0];
+          std::memcpy(&scales[g * N + n], &hs, 2);
+        }
+        for (int64_t r = g * G / 8; r < (g + 1) * G / 8; ++r) {
+          for (int64_t n = n0; n < n1; ++n) packed[r * N + n] = 0;
+          for (int i = 0; i < 8; ++i) {
+            const float *row = W + (8 * r + i) * N;
+            for (int64_t n = n0; n < n1; ++n) {
+              float q = std::nearbyint(row[n] / scale[n - n0]);
+              q = q < -8.0f ? -8.0f : (q > 7.0f ? 7.0f : q);
+              packed[r * N + n] |= (int32_t)((uint32_t)((int)q + 8) << (4 * i));
+            }
+          }
+        }
+      }
+    }
+  };
+  std::vector<std::thread> pool;
+  for (int i = 1; i < nt; ++i) pool.emplace_back(work, i);
+  work(0);
+  for (auto &t : pool) t.join();
+  for (int i = 0; i < nt; ++i)
+    if (bad[i]) return fail(W4A16_ERR_NONFINITE, "w4a16_pack_host: W holds NaN or Inf");
+  return W4A16_OK;
+}
+
+int64_t w4a16_repacked_weight_bytes(int64_t K, int64_t N, int G) {
+  int rc = check_gpu_shape(K, N, G, "w4a16_repacked_weight_bytes");
+  if (rc != W4A16_OK) return rc;
+  return ceil_div(N, kStrip) * (K / kTileK) * kTileWords * 4;
+}
+
+int64_t w4a16_repacked_scale_bytes(int64_t K, int64_t N, int G) {
+  int rc = check_gpu_shape(K, N, G, "w4a16_repacked_scale_bytes");
+  if (rc != W4A16_OK) return rc;
+  return ceil_div(N, kStrip) * ceil_div(K / kGroup, 8) * 32 * 8 * 2;
+}
+
+int w4a16_repack(const int32_t *packed_d, const uint16_t *scales_d, int64_t K, int64_t N, int G,
+                 void *rw_d, void *rs_d, w4a16_stream_t stream) {
+  int rc = check_gpu_shape(K, N, G, "w4a16_repack");
+  if (rc != W4A16_OK) return rc;
+  if (!packed_d || !scales_d || !rw_d || !rs_d)
+    return fail(W4A16_ERR_INVALID, "w4a16_repack: null pointer");
+  if (!aligned16(rw_d) || !aligned16(rs_d))
+    return fail(W4A16_ERR_INVALID, "w4a16_repack: repacked buffers must be 16-byte aligned");
+  hipError_t e = launch_repack(packed_d, scales_d, K, N, rw_d, rs_d, (hipStream_t)stream);
+  return e == hipSuccess ? W4A16_OK : hip_fail(e, "w4a16_repack");
+}
+
+int w4a16_unrepack(const void *rw_d, const void *rs_d, int64_t K, int64_t N, int G,
+                   int32_t *packed_d, uint16_t *scales_d, w4a16_stream_t stream) {
+  int rc = check_gpu_shape(K, N, G, "w4a16_unrepack");
+  if (rc != W4A16_OK) return rc;
+  if (!packed_d || !scales_d || !rw_d || !rs_d)
+    return fail(W4A16_ERR_INVALID, "w4a16_unrepack: null pointer");
+  if (!aligned16(rw_d) || !aligned16(rs_d))
+    return fail(W4A16_ERR_INVALID, "w4a16_unrepack: repacked buffers must be 16-byte aligned");
+  hipError_t e = launch_unrepack(rw_d, rs_d, K, N, packed_d, scales_d, (hipStream_t)stream);
+  return e == hipSuccess ? W4A16_OK : hip_fail(e, "w4a16_unrepack");
+}
+
+int w4a16_dequant(const void *rw_d, const void *rs_d, int64_t K, int64_t N, int G,
+                  uint16_t *W16_d, w4a16_stream_t stream) {
+  int rc = check_gpu_shape(K, N, G, "w4a16_dequant");
+  if (rc != W4A16_OK) return rc;
+  if (!rw_d || !rs_d || !W16_d) return fail(W4A16_ERR_INVALID, "w4a16_dequant: null pointer");
+  if (!aligned16(rw_d) || !aligned16(rs_d))
+    return fail(W4A16_ERR_INVALID, "w4a16_dequant: repacked buffers must be 16-byte aligned");
+  hipError_t e = launch_dequant_canonical(rw_d, rs_d, K, N, W16_d, (hipStream_t)stream);
+  return e == hipSuccess ? W4A16_OK : hip_fail(e, "w4a16_dequant");
+}
+
+int w4a16_gemm(const uint16_t *A_d, int64_t M, int64_t K, const void *rw_d, const void *rs_d,
+               int64_t N, int G, uint16_t *C_d, w4a16_stream_t stream) {
+  return run_gemm(A_d, M, K, rw_d, rs_d, N, G, C_d, W4A16_PATH_AUTO, nullptr, 0,
+                  (hipStream_t)stream);
+}
+
+int w4a16_gemm_swiglu(const uint16_t *A_d, int64_t M, int64_t K, const void *rw_d,
+                      const void *rs_d, int64_t N, int G, uint16_t *Z_d, w4a16_stream_t stream) {
+  return run_gemm(A_d, M, K, rw_d, rs_d, N, G, Z_d, W4A16_PATH_AUTO | W4A16_FLAG_SWIGLU, nullptr,
+                  0, (hipStream_t)stream);
+}
+
+int w4a16_gemm_ex(const uint16_t *A_d, int64_t M, int64_t K, const void *rw_d, const void *rs_d,
+                  int64_t N, int G, uint16_t *out_d, int flags, void *workspace_d,
+                  int64_t workspace_bytes, w4a16_stream_t stream) {
+  if (flags & ~(0xF | W4A16_FLAG_SWIGLU))
+    return fail(W4A16_ERR_INVALID, "w4a16_gemm_ex: unknown flags 0x%x", flags);
+  return run_gemm(A_d, M, K, rw_d, rs_d, N, G, out_d, flags, workspace_d, workspace_bytes,
+                  (hipStream_t)stream);
+}
+
+int64_t w4a16_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N, int G, int flags) {
+  int rc = check_gpu_shape(K, N, G, "w4a16_gemm_workspace_bytes");
+  if (rc != W4A16_OK) return rc;
+  if (M <= 0) return 0;
+  int path = flags & 0xF;
+  if (path == W4A16_PATH_AUTO) path = select_path(M, K, N);
+  Problem p{nullptr, M, K, N, nullptr, nullptr, nullptr, (flags & W4A16_FLAG_SWIGLU) != 0};
+  return workspace_for(path, p);
+}
+
+int w4a16_select_path(int64_t M, int64_t K, int64_t N, int G, int flags) {
+  int rc = check_gpu_shape(K, N, G, "w4a16_select_path");
+  if (rc != W4A16_OK) return rc;
+  if (M < 0) return fail(W4A16_ERR_INVALID, "w4a16_select_path: M must be >= 0");
+  (void)flags;
+  return select_path(M, K, N);
+}
+
+}  // extern "C"

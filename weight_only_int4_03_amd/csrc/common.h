@@ -1,0 +1,124 @@
+// Internal definitions shared by the library's HIP sources (not part of the ABI).
+//
+// Repacked weight layout.  The canonical [K/8, N] int32 words are grouped into
+// tiles of 32 columns x 64 k (1 KiB).  Strip t (columns 32t .. 32t+31) holds
+// its K/64 tiles contiguously, strip after strip:
+//     word offset of (t, q, l, j) = ((t * KT + q) * 64 + l) * 4 + j,  KT = K/64
+// Lane position l = 32h + c holds the four words of column 32t + c with
+// canonical rows r = 8q + 4h + j (k = 64q + 32h + 8j .. +7), so one 16-byte
+// load per lane brings 32 consecutive k of one column, and one wave-wide load
+// brings a whole contiguous 1 KiB tile.
+//
+// Inside each word the nibbles are permuted so that the four shift-and-mask
+// steps (w >> 4j) & 0x000F000F yield the fp16 pairs (k0,k1), (k2,k3), (k4,k5),
+// (k6,k7) in register order: k offset i sits at nibble position
+// (i % 2) * 4 + i / 2.  Pad columns (n >= N) hold 0x88888888 (all zero weights).
+//
+// Repacked scale layout: fp16 [NS][KG8][32][8], NS = ceil(N/32),
+// KG8 = ceil(K/128 / 8): entry ((t*KG8 + o)*32 + c)*8 + e is the scale of group
+// 8o + e and column 32t + c (zero in padding), so a lane reads eight
+// consecutive groups' scales of its column with one 16-byte load.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4a16 {
+
+constexpr int kGroup = 128;   // quantization group along K
+constexpr int kTileK = 64;    // k per repacked tile
+constexpr int kStrip = 32;    // columns per strip
+constexpr int kTileWords = 256;
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t uint4_t __attribute__((ext_vector_type(4)));
+
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Nibble position of k offset i (0..7) inside a repacked word.
+__host__ __device__ inline int nibble_pos(int i) { return (i & 1) * 4 + (i >> 1); }
+
+template <typename To, typename From>
+__device__ __forceinline__ To bitcast(From v) { return __builtin_bit_cast(To, v); }
+
+// Eight nibbles of a repacked word -> eight fp16 values (u - 8), exact.
+// (w >> 4j) & 0x000F000F | 0x6400_6400 is the fp16 pair (1024 + u, 1024 + u');
+// subtracting 1032 from both halves leaves u - 8 exactly.
+__device__ __forceinline__ half8_t nibbles_to_half8(uint32_t w) {
+  const uint32_t mask = 0x000F000Fu, magic = 0x64006400u;
+  const half2_t bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+  half2_t p0 = bitcast<half2_t>((w & mask) | magic) + bias;
+  half2_t p1 = bitcast<half2_t>(((w >> 4) & mask) | magic) + bias;
+  half2_t p2 = bitcast<half2_t>(((w >> 8) & mask) | magic) + bias;
+  half2_t p3 = bitcast<half2_t>(((w >> 12) & mask) | magic) + bias;
+  uint4_t r = {bitcast<uint32_t>(p0), bitcast<uint32_t>(p1), bitcast<uint32_t>(p2),
+               bitcast<uint32_t>(p3)};
+  return bitcast<half8_t>(r);
+}
+
+// Same, multiplied by the group scale in fp16: each value is the fp16 rounding
+// of the exact product (q - 8) * s, i.e. the dequantized weight bit for bit.
+__device__ __forceinline__ half8_t nibbles_to_half8_scaled(uint32_t w, half2_t s2) {
+  const uint32_t mask = 0x000F000Fu, magic = 0x64006400u;
+  const half2_t bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+  half2_t p0 = (bitcast<half2_t>((w & mask) | magic) + bias) * s2;
+  half2_t p1 = (bitcast<half2_t>(((w >> 4) & mask) | magic) + bias) * s2;
+  half2_t p2 = (bitcast<half2_t>(((w >> 8) & mask) | magic) + bias) * s2;
+  half2_t p3 = (bitcast<half2_t>(((w >> 12) & mask) | magic) + bias) * s2;
+  uint4_t r = {bitcast<uint32_t>(p0), bitcast<uint32_t>(p1), bitcast<uint32_t>(p2),
+               bitcast<uint32_t>(p3)};
+  return bitcast<half8_t>(r);
+}
+
+__device__ __forceinline__ uint4_t load_nt(const uint4_t *p) {
+  return __builtin_nontemporal_load(p);
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g / (1.0f + __expf(-g)) * u;
+}
+
+__device__ __forceinline__ uint16_t to_half_bits(float v) {
+  return bitcast<uint16_t>((_Float16)v);
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launch descriptions (defined in decode.hip / prefill.hip /
+// format.hip, called from api.hip).
+
+struct Problem {
+  const uint16_t *A;
+  int64_t M, K, N;
+  const void *rw;
+  const void *rs;
+  uint16_t *out;   // C [M,N] or Z [M,N/2]
+  bool swiglu;
+};
+
+// Counters for the split-K fixup live at the start of the workspace.
+constexpr int64_t kCounterBytes = 64 * 1024;
+
+hipError_t launch_pack(const float *W, int64_t K, int64_t N, int32_t *packed, uint16_t *scales,
+                       hipStream_t s);
+hipError_t launch_repack(const int32_t *packed, const uint16_t *scales, int64_t K, int64_t N,
+                         void *rw, void *rs, hipStream_t s);
+hipError_t launch_unrepack(const void *rw, const void *rs, int64_t K, int64_t N, int32_t *packed,
+                           uint16_t *scales, hipStream_t s);
+hipError_t launch_dequant_canonical(const void *rw, const void *rs, int64_t K, int64_t N,
+                                    uint16_t *W16, hipStream_t s);
+hipError_t launch_dequant_fragment(const void *rw, const void *rs, int64_t K, int64_t N,
+                                   uint16_t *W16f, hipStream_t s);
+
+// Decode path: workspace bytes beyond the counters, and the launch.
+int64_t decode_workspace_bytes(const Problem &p);
+hipError_t launch_decode(const Problem &p, void *workspace, hipStream_t s);
+
+// Prefill path (fused dequant) and dense path (fp16 fragment-ordered weights).
+hipError_t launch_prefill(const Problem &p, hipStream_t s);
+int64_t dense_workspace_bytes(const Problem &p);
+hipError_t launch_dense(const Problem &p, void *workspace, hipStream_t s);
+
+}  // namespace w4a16

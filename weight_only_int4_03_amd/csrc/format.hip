@@ -1,0 +1,211 @@
+// Format kernels: quantize+pack, repack/unrepack, dequantize.
+//
+// Quantize+pack and dequantize follow the page "GPU Kernels for INT4
+// Inference, in depth" (aicassindra.com), section "The data contract"
+// (quantize_pack and dequantize); the repacked layout is described in
+// common.h.
+#include "common.h"
+
+namespace w4a16 {
+
+// ---------------------------------------------------------------------------
+// Quantize + pack.  One thread per (group g, column n): adjacent threads take
+// adjacent columns, so every row access of W and of the packed output is a
+// coalesced run.  The scale is an IEEE fp32 division, the rounding of W/s is
+// round-half-to-even (v_rndne_f32), and fp16(s) is the round-to-nearest-even
+// conversion -- the same decisions, in the same precision, as the definition.
+__global__ __launch_bounds__(256) void pack_kernel(const float *__restrict__ W, int64_t N,
+                                                   int32_t *__restrict__ packed,
+                                                   uint16_t *__restrict__ scales) {
+  const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t g = blockIdx.y;
+  if (n >= N) return;
+  const float *col = W + g * kGroup * N + n;
+  float amax = 0.0f;
+#pragma unroll 16
+  for (int k = 0; k < kGroup; ++k) amax = fmaxf(amax, fabsf(col[k * N]));
+  float s = __fdiv_rn(amax, 7.0f);
+  s = s < 1e-8f ? 1e-8f : s;
+#pragma unroll 2
+  for (int r = 0; r < kGroup / 8; ++r) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float q = __builtin_rintf(__fdiv_rn(col[(8 * r + i) * N], s));
+      q = fminf(fmaxf(q, -8.0f), 7.0f);
+      word |= (uint32_t)((int)q + 8) << (4 * i);
+    }
+    packed[(g * (kGroup / 8) + r) * N + n] = (int32_t)word;
+  }
+  scales[g * N + n] = to_half_bits(s);
+}
+
+hipError_t launch_pack(const float *W, int64_t K, int64_t N, int32_t *packed, uint16_t *scales,
+                       hipStream_t s) {
+  dim3 grid((unsigned)ceil_div(N, 256), (unsigned)(K / kGroup));
+  hipLaunchKernelGGL(pack_kernel, grid, dim3(256), 0, s, W, N, packed, scales);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Repack / unrepack.  Blocks [0, wblocks) move weight words: one thread per
+// (strip t, tile q, lane position l) writes the 16-byte lane vector of the
+// tile.  The remaining blocks move scales: one thread per (strip, group octet,
+// column) writes eight consecutive groups' scales.
+
+__device__ __forceinline__ uint32_t permute_nibbles(uint32_t w) {
+  uint32_t out = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) out |= ((w >> (4 * i)) & 0xFu) << (4 * nibble_pos(i));
+  return out;
+}
+
+__device__ __forceinline__ uint32_t unpermute_nibbles(uint32_t w) {
+  uint32_t out = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) out |= ((w >> (4 * nibble_pos(i))) & 0xFu) << (4 * i);
+  return out;
+}
+
+template <bool FORWARD>
+__global__ __launch_bounds__(256) void repack_kernel(const int32_t *__restrict__ packed,
+                                                     const uint16_t *__restrict__ scales,
+                                                     uint4_t *__restrict__ rw,
+                                                     uint16_t *__restrict__ rs,
+                                                     int32_t *__restrict__ packed_out,
+                                                     uint16_t *__restrict__ scales_out,
+                                                     int64_t N, int64_t KT, int64_t KG,
+                                                     int64_t KG8, int64_t NS,
+                                                     int64_t wblocks) {
+  if ((int64_t)blockIdx.x < wblocks) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (t*KT + q)*64 + l
+    if (idx >= NS * KT * 64) return;
+    const int l = (int)(idx & 63);
+    const int64_t tq = idx >> 6;
+    const int64_t q = tq % KT, t = tq / KT;
+    const int h = l >> 5, c = l & 31;
+    const int64_t n = t * kStrip + c;
+    const int64_t r0 = 8 * q + 4 * h;
+    if (FORWARD) {
+      uint4_t v;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        v[j] = n < N ? permute_nibbles((uint32_t)packed[(r0 + j) * N + n]) : 0x88888888u;
+      rw[idx] = v;
+    } else {
+      if (n >= N) return;
+      uint4_t v = rw[idx];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) packed_out[(r0 + j) * N + n] = (int32_t)unpermute_nibbles(v[j]);
+    }
+  } else {
+    const int64_t idx = ((int64_t)blockIdx.x - wblocks) * 256 + threadIdx.x;  // (t*KG8+o)*32+c
+    if (idx >= NS * KG8 * 32) return;
+    const int c = (int)(idx & 31);
+    const int64_t to = idx >> 5;
+    const int64_t o = to % KG8, t = to / KG8;
+    const int64_t n = t * kStrip + c;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int64_t g = 8 * o + e;
+      if (FORWARD)
+        rs[idx * 8 + e] = (g < KG && n < N) ? scales[g * N + n] : (uint16_t)0;
+      else if (g < KG && n < N)
+        scales_out[g * N + n] = rs[idx * 8 + e];
+    }
+  }
+}
+
+static void repack_geometry(int64_t K, int64_t N, int64_t &KT, int64_t &KG, int64_t &KG8,
+                            int64_t &NS) {
+  KT = K / kTileK;
+  KG = K / kGroup;
+  KG8 = ceil_div(KG, 8);
+  NS = ceil_div(N, kStrip);
+}
+
+hipError_t launch_repack(const int32_t *packed, const uint16_t *scales, int64_t K, int64_t N,
+                         void *rw, void *rs, hipStream_t s) {
+  int64_t KT, KG, KG8, NS;
+  repack_geometry(K, N, KT, KG, KG8, NS);
+  const int64_t wblocks = ceil_div(NS * KT * 64, 256);
+  const int64_t sblocks = ceil_div(NS * KG8 * 32, 256);
+  hipLaunchKernelGGL(repack_kernel<true>, dim3((unsigned)(wblocks + sblocks)), dim3(256), 0, s,
+                     packed, scales, (uint4_t *)rw, (uint16_t *)rs, (int32_t *)nullptr,
+                     (uint16_t *)nullptr, N, KT, KG, KG8, NS, wblocks);
+  return hipGetLastError();
+}
+
+hipError_t launch_unrepack(const void *rw, const void *rs, int64_t K, int64_t N, int32_t *packed,
+                           uint16_t *scales, hipStream_t s) {
+  int64_t KT, KG, KG8, NS;
+  repack_geometry(K, N, KT, KG, KG8, NS);
+  const int64_t wblocks = ceil_div(NS * KT * 64, 256);
+  const int64_t sblocks = ceil_div(NS * KG8 * 32, 256);
+  hipLaunchKernelGGL(repack_kernel<false>, dim3((unsigned)(wblocks + sblocks)), dim3(256), 0, s,
+                     (const int32_t *)nullptr, (const uint16_t *)nullptr, (uint4_t *)rw,
+                     (uint16_t *)rs, packed, scales, N, KT, KG, KG8, NS, wblocks);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Dequantize.  One thread per repacked lane vector (four words = 32 weights of
+// one column).  Each weight is fp16((q - 8) * s): the fp16 product of the
+// exact value q - 8 and the fp16 scale rounds the exact product once.
+//
+// CANONICAL writes W16 [K, N] row-major (the definition's layout).
+// Otherwise the output is fragment-ordered for the dense GEMM: the lane
+// vector (t, q, l) expands to four 16-byte runs at uint4 index
+// ((t*KT + q)*64 + l)*4 + j, run j holding k = 64q + 32h + 8j .. +7.
+template <bool CANONICAL>
+__global__ __launch_bounds__(256) void dequant_kernel(const uint4_t *__restrict__ rw,
+                                                      const uint16_t *__restrict__ rs,
+                                                      uint16_t *__restrict__ W16, int64_t N,
+                                                      int64_t KT, int64_t KG8, int64_t NS) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= NS * KT * 64) return;
+  const int l = (int)(idx & 63);
+  const int64_t tq = idx >> 6;
+  const int64_t q = tq % KT, t = tq / KT;
+  const int h = l >> 5, c = l & 31;
+  const int64_t n = t * kStrip + c;
+  const int64_t g = q >> 1;
+  const _Float16 sh = bitcast<_Float16>(rs[((t * KG8 + (g >> 3)) * 32 + c) * 8 + (g & 7)]);
+  const half2_t s2 = {sh, sh};
+  const uint4_t v = rw[idx];
+  if (CANONICAL) {
+    if (n >= N) return;
+    const int64_t k0 = 64 * q + 32 * h;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const half8_t w = nibbles_to_half8_scaled(v[j], s2);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) W16[(k0 + 8 * j + i) * N + n] = bitcast<uint16_t>(w[i]);
+    }
+  } else {
+    uint4_t *out = (uint4_t *)W16 + idx * 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[j] = bitcast<uint4_t>(nibbles_to_half8_scaled(v[j], s2));
+  }
+}
+
+hipError_t launch_dequant_canonical(const void *rw, const void *rs, int64_t K, int64_t N,
+                                    uint16_t *W16, hipStream_t s) {
+  int64_t KT, KG, KG8, NS;
+  repack_geometry(K, N, KT, KG, KG8, NS);
+  hipLaunchKernelGGL(dequant_kernel<true>, dim3((unsigned)ceil_div(NS * KT * 64, 256)), dim3(256),
+                     0, s, (const uint4_t *)rw, (const uint16_t *)rs, W16, N, KT, KG8, NS);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_fragment(const void *rw, const void *rs, int64_t K, int64_t N,
+                                   uint16_t *W16f, hipStream_t s) {
+  int64_t KT, KG, KG8, NS;
+  repack_geometry(K, N, KT, KG, KG8, NS);
+  hipLaunchKernelGGL(dequant_kernel<false>, dim3((unsigned)ceil_div(NS * KT * 64, 256)),
+                     dim3(256), 0, s, (const uint4_t *)rw, (const uint16_t *)rs, W16f, N, KT, KG8,
+                     NS);
+  return hipGetLastError();
+}
+
+}  // namespace w4a16

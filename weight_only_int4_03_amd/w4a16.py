@@ -1,0 +1,246 @@
+"""Thin ctypes binding over libw4a16.so (the C ABI in include/w4a16.h).
+
+Argument marshalling only: every step runs in the library's HIP kernels (or,
+for ``pack_host``, its C++ host code).  PyTorch supplies device memory and
+the current stream.  The library must have been built
+(``python -m weight_only_int4_03_amd.build``); loading fails loudly otherwise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(HERE, "libw4a16.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "w4a16.h")
+
+OK = 0
+ERR_INVALID = -1
+ERR_UNSUPPORTED = -2
+ERR_NONFINITE = -3
+ERR_HIP = -4
+ERR_WORKSPACE = -5
+
+PATH_AUTO = 0
+PATH_DECODE = 1
+PATH_PREFILL = 2
+PATH_DENSE = 3
+PATHS = {"auto": PATH_AUTO, "decode": PATH_DECODE, "prefill": PATH_PREFILL, "dense": PATH_DENSE}
+FLAG_SWIGLU = 0x10
+G = 128
+
+
+class W4A16Error(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__("w4a16 error %d: %s" % (code, message))
+        self.code = code
+
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+
+_SIGNATURES = {
+    "w4a16_pack": ([_p, _i64, _i64, _int, _p, _p, _p], _int),
+    "w4a16_pack_host": ([_p, _i64, _i64, _int, _p, _p, _int], _int),
+    "w4a16_repacked_weight_bytes": ([_i64, _i64, _int], _i64),
+    "w4a16_repacked_scale_bytes": ([_i64, _i64, _int], _i64),
+    "w4a16_repack": ([_p, _p, _i64, _i64, _int, _p, _p, _p], _int),
+    "w4a16_unrepack": ([_p, _p, _i64, _i64, _int, _p, _p, _p], _int),
+    "w4a16_dequant": ([_p, _p, _i64, _i64, _int, _p, _p], _int),
+    "w4a16_gemm": ([_p, _i64, _i64, _p, _p, _i64, _int, _p, _p], _int),
+    "w4a16_gemm_swiglu": ([_p, _i64, _i64, _p, _p, _i64, _int, _p, _p], _int),
+    "w4a16_gemm_ex": ([_p, _i64, _i64, _p, _p, _i64, _int, _p, _int, _p, _i64, _p], _int),
+    "w4a16_gemm_workspace_bytes": ([_i64, _i64, _i64, _int, _int], _i64),
+    "w4a16_select_path": ([_i64, _i64, _i64, _int, _int], _int),
+    "w4a16_last_error": ([], ctypes.c_char_p),
+    "w4a16_version": ([], ctypes.c_char_p),
+}
+
+_lib = None
+
+
+def header_functions(path: str = HEADER) -> list[str]:
+    """Names of the functions include/w4a16.h declares."""
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w4a16_[a-z0-9_]+)\s*\(", text)))
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIBRARY):
+            raise RuntimeError("libw4a16.so is not built: run python -m weight_only_int4_03_amd.build")
+        L = ctypes.CDLL(LIBRARY)
+        for name, (args, res) in _SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().w4a16_last_error().decode()
+
+
+def _check(rc: int) -> int:
+    if rc < 0:
+        raise W4A16Error(rc, last_error())
+    return rc
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream=None) -> int:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+# -- host pack -----------------------------------------------------------------
+
+def pack_host(W: np.ndarray, G: int = G, nthreads: int = 0):
+    """Quantize + pack on the host: (packed int32 [K/8,N], scales uint16 [K/G,N])."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    K, N = W.shape
+    packed = np.empty((K // 8, N), np.int32)
+    scales = np.empty((K // G, N), np.uint16)
+    _check(lib().w4a16_pack_host(W.ctypes.data, K, N, G, packed.ctypes.data,
+                                 scales.ctypes.data, nthreads))
+    return packed, scales
+
+
+# -- device calls ------------------------------------------------------------------
+
+def pack(W, G: int = G, stream=None):
+    """Quantize + pack a device fp32 [K,N] tensor: (packed int32 [K/8,N], scales int16 [K/G,N])."""
+    torch = _torch()
+    assert W.is_cuda and W.dtype == torch.float32 and W.is_contiguous()
+    K, N = W.shape
+    packed = torch.empty((K // 8, N), dtype=torch.int32, device=W.device)
+    scales = torch.empty((K // G, N), dtype=torch.int16, device=W.device)
+    _check(lib().w4a16_pack(_ptr(W), K, N, G, _ptr(packed), _ptr(scales), _stream(stream)))
+    return packed, scales
+
+
+class RepackedWeight:
+    """Repacked device buffers of one [K,N] weight (built by :func:`repack`)."""
+
+    def __init__(self, rw, rs, K: int, N: int):
+        self.rw, self.rs, self.K, self.N = rw, rs, K, N
+
+    def clone(self) -> "RepackedWeight":
+        return RepackedWeight(self.rw.clone(), self.rs.clone(), self.K, self.N)
+
+    @property
+    def nbytes(self) -> int:
+        return self.rw.numel() + self.rs.numel()
+
+
+def repacked_bytes(K: int, N: int, G: int = G):
+    return (_check(lib().w4a16_repacked_weight_bytes(K, N, G)),
+            _check(lib().w4a16_repacked_scale_bytes(K, N, G)))
+
+
+def repack(packed, scales, G: int = G, stream=None) -> RepackedWeight:
+    """Canonical device (packed [K/8,N] int32, scales [K/G,N] fp16 bits) -> repacked."""
+    torch = _torch()
+    assert packed.is_cuda and packed.dtype == torch.int32 and packed.is_contiguous()
+    assert scales.is_cuda and scales.element_size() == 2 and scales.is_contiguous()
+    K, N = packed.shape[0] * 8, packed.shape[1]
+    wb, sb = repacked_bytes(K, N, G)
+    rw = torch.empty(wb, dtype=torch.uint8, device=packed.device)
+    rs = torch.empty(sb, dtype=torch.uint8, device=packed.device)
+    _check(lib().w4a16_repack(_ptr(packed), _ptr(scales), K, N, G, _ptr(rw), _ptr(rs),
+                              _stream(stream)))
+    return RepackedWeight(rw, rs, K, N)
+
+
+def unrepack(w: RepackedWeight, G: int = G, stream=None):
+    torch = _torch()
+    packed = torch.empty((w.K // 8, w.N), dtype=torch.int32, device=w.rw.device)
+    scales = torch.empty((w.K // G, w.N), dtype=torch.int16, device=w.rw.device)
+    _check(lib().w4a16_unrepack(_ptr(w.rw), _ptr(w.rs), w.K, w.N, G, _ptr(packed),
+                                _ptr(scales), _stream(stream)))
+    return packed, scales
+
+
+def dequant(w: RepackedWeight, G: int = G, stream=None):
+    """fp16 [K,N] dequantized weights (canonical row-major)."""
+    torch = _torch()
+    W16 = torch.empty((w.K, w.N), dtype=torch.float16, device=w.rw.device)
+    _check(lib().w4a16_dequant(_ptr(w.rw), _ptr(w.rs), w.K, w.N, G, _ptr(W16), _stream(stream)))
+    return W16
+
+
+def gemm(A, w: RepackedWeight, swiglu: bool = False, path: str | int = "auto", out=None,
+         workspace=None, G: int = G, stream=None):
+    """C = A * dequant(W) (fp16 [M,N]); with swiglu, Z = silu(C[:, :N/2]) * C[:, N/2:]."""
+    torch = _torch()
+    assert A.is_cuda and A.dtype == torch.float16 and A.is_contiguous()
+    M, K = A.shape
+    if K != w.K:
+        raise ValueError("A has K=%d, weight has K=%d" % (K, w.K))
+    ncols = w.N // 2 if swiglu else w.N
+    if out is None:
+        out = torch.empty((M, ncols), dtype=torch.float16, device=A.device)
+    flags = (PATHS[path] if isinstance(path, str) else int(path)) | (FLAG_SWIGLU if swiglu else 0)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().w4a16_gemm_ex(_ptr(A), M, K, _ptr(w.rw), _ptr(w.rs), w.N, G, _ptr(out), flags,
+                               _ptr(workspace), ws_bytes, _stream(stream)))
+    return out
+
+
+def gemm_plain(A, w: RepackedWeight, out=None, G: int = G, stream=None):
+    """w4a16_gemm (automatic path, library workspace)."""
+    torch = _torch()
+    M, K = A.shape
+    if out is None:
+        out = torch.empty((M, w.N), dtype=torch.float16, device=A.device)
+    _check(lib().w4a16_gemm(_ptr(A), M, K, _ptr(w.rw), _ptr(w.rs), w.N, G, _ptr(out),
+                            _stream(stream)))
+    return out
+
+
+def gemm_swiglu(A, w: RepackedWeight, out=None, G: int = G, stream=None):
+    """w4a16_gemm_swiglu (automatic path, library workspace)."""
+    torch = _torch()
+    M, K = A.shape
+    if out is None:
+        out = torch.empty((M, w.N // 2), dtype=torch.float16, device=A.device)
+    _check(lib().w4a16_gemm_swiglu(_ptr(A), M, K, _ptr(w.rw), _ptr(w.rs), w.N, G, _ptr(out),
+                                   _stream(stream)))
+    return out
+
+
+def workspace_bytes(M: int, K: int, N: int, swiglu: bool = False, path: str | int = "auto",
+                    G: int = G) -> int:
+    flags = (PATHS[path] if isinstance(path, str) else int(path)) | (FLAG_SWIGLU if swiglu else 0)
+    return _check(lib().w4a16_gemm_workspace_bytes(M, K, N, G, flags))
+
+
+def select_path(M: int, K: int, N: int, swiglu: bool = False, G: int = G) -> str:
+    code = _check(lib().w4a16_select_path(M, K, N, G, FLAG_SWIGLU if swiglu else 0))
+    return {v: k for k, v in PATHS.items()}[code]
+
+
+def load_weight(W_host: np.ndarray, device="cuda", G: int = G) -> RepackedWeight:
+    """Host fp32 W -> device, quantize+pack on the GPU, repack.  (Load-time path.)"""
+    torch = _torch()
+    Wd = torch.from_numpy(np.ascontiguousarray(W_host, dtype=np.float32)).to(device)
+    packed, scales = pack(Wd, G)
+    del Wd
+    return repack(packed, scales, G)
