@@ -139,10 +139,9 @@ int w4a16_gemm_swiglu(const uint16_t *A_d, int64_t M, int64_t K, const void *rw_
 
 /* Explicit form of the two calls above.  `flags` = path (W4A16_PATH_*, AUTO
  * to use the table) | W4A16_FLAG_SWIGLU.  `workspace_d` (device, 256-byte
- * aligned, at least w4a16_gemm_workspace_bytes) is owned by the caller; its
- * first 64 KiB hold counters that must be zero before its first use and that
- * every call leaves zero again.  workspace_d may be NULL to use the library's
- * per-device workspace. */
+ * aligned, at least w4a16_gemm_workspace_bytes) is owned by the caller and
+ * needs no initialisation: it carries nothing from one call to the next.
+ * workspace_d may be NULL to use the library's per-device workspace. */
 int w4a16_gemm_ex(const uint16_t *A_d, int64_t M, int64_t K, const void *rw_d,
                   const void *rs_d, int64_t N, int G, uint16_t *out_d, int flags,
                   void *workspace_d, int64_t workspace_bytes, w4a16_stream_t stream);

@@ -58,7 +58,8 @@ int check_gpu_shape(int64_t K, int64_t N, int G, const char *who) {
 }
 
 // ---------------------------------------------------------------------------
-// Library-owned per-device workspace: [counters (zeroed once) | scratch].
+// Library-owned per-device workspace (split-K partials, dense-tier scratch).
+// It holds no state between calls: every call writes what it later reads.
 
 struct DeviceWorkspace {
   void *ptr = nullptr;
@@ -68,12 +69,7 @@ struct DeviceWorkspace {
 std::mutex g_ws_mutex;
 std::vector<DeviceWorkspace> g_ws;
 
-__global__ void zero_words(uint32_t *p, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < n) p[i] = 0;
-}
-
-int device_workspace(int64_t need, hipStream_t stream, void **out) {
+int device_workspace(int64_t need, void **out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -96,11 +92,6 @@ int device_workspace(int64_t need, hipStream_t stream, void **out) {
                   (long long)bytes, hipGetErrorString(e));
     }
     w.bytes = bytes;
-    const int64_t words = kCounterBytes / 4;
-    hipLaunchKernelGGL(zero_words, dim3((unsigned)ceil_div(words, 256)), dim3(256), 0, stream,
-                       (uint32_t *)w.ptr, words);
-    e = hipGetLastError();
-    if (e != hipSuccess) return hip_fail(e, "counter zeroing launch");
   }
   *out = w.ptr;
   return W4A16_OK;
@@ -124,12 +115,11 @@ int select_path(int64_t M, int64_t K, int64_t N) {
 }
 
 int64_t workspace_for(int path, const Problem &p) {
-  if (path == W4A16_PATH_DENSE) return kCounterBytes + dense_workspace_bytes(p);
+  if (path == W4A16_PATH_DENSE) return dense_workspace_bytes(p);
   if (path == W4A16_PATH_DECODE) {
     Problem q = p;
     q.M = p.M < kDecodeMaxM ? p.M : kDecodeMaxM;
-    const int64_t b = decode_workspace_bytes(q);
-    return b > 0 ? kCounterBytes + b : 0;
+    return decode_workspace_bytes(q);
   }
   return 0;
 }
@@ -159,7 +149,7 @@ int run_gemm(const uint16_t *A, int64_t M, int64_t K, const void *rw, const void
   void *ws = workspace;
   if (need > 0) {
     if (ws == nullptr) {
-      rc = device_workspace(need, stream, &ws);
+      rc = device_workspace(need, &ws);
       if (rc != W4A16_OK) return rc;
     } else if (ws_bytes < need || ((uintptr_t)ws & 255u) != 0) {
       return fail(W4A16_ERR_WORKSPACE, "%s: workspace needs %lld bytes, 256-byte aligned", who,

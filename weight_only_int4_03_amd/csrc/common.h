@@ -44,34 +44,60 @@ __host__ __device__ inline int nibble_pos(int i) { return (i & 1) * 4 + (i >> 1)
 template <typename To, typename From>
 __device__ __forceinline__ To bitcast(From v) { return __builtin_bit_cast(To, v); }
 
-// Eight nibbles of a repacked word -> eight fp16 values (u - 8), exact.
-// (w >> 4j) & 0x000F000F | 0x6400_6400 is the fp16 pair (1024 + u, 1024 + u');
-// subtracting 1032 from both halves leaves u - 8 exactly.
-__device__ __forceinline__ half8_t nibbles_to_half8(uint32_t w) {
-  const uint32_t mask = 0x000F000Fu, magic = 0x64006400u;
-  const half2_t bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-  half2_t p0 = bitcast<half2_t>((w & mask) | magic) + bias;
-  half2_t p1 = bitcast<half2_t>(((w >> 4) & mask) | magic) + bias;
-  half2_t p2 = bitcast<half2_t>(((w >> 8) & mask) | magic) + bias;
-  half2_t p3 = bitcast<half2_t>(((w >> 12) & mask) | magic) + bias;
-  uint4_t r = {bitcast<uint32_t>(p0), bitcast<uint32_t>(p1), bitcast<uint32_t>(p2),
-               bitcast<uint32_t>(p3)};
-  return bitcast<half8_t>(r);
-}
+// Nibble -> fp16 conversion (the magic-number idiom of FuTransformer, arXiv
+// 2610.23796, section 3.3.4, and of the Swordfish page, section "The packed
+// format": place the nibble in the mantissa of a power-of-two 16-bit float
+// and subtract the power plus the offset 8).  For fp16 the exponent pattern
+// 0x6400 is 1024.0 with a mantissa step of 1, so
+//   (w & 0x000F000F) | 0x64006400  = the pair (1024 + u, 1024 + u'),
+//   (w & 0x00F000F0) | 0x64006400  = the pair (1024 + 16u, 1024 + 16u'),
+// both exact.  One packed add of -1032 turns the first into u - 8; one packed
+// FMA (x / 16 - 72) turns the second into u - 8; both results are exact.  The
+// other four nibbles come the same way from w >> 8.  With the repacked in-word
+// order (k offset i at nibble (i % 2) * 4 + i / 2) the four pairs are
+// (k0,k1), (k2,k3), (k4,k5), (k6,k7): 9 VALU instructions per 8 weights
+// (1 shift, 4 v_and_or_b32, 2 v_pk_add_f16, 2 v_pk_fma_f16).
+struct Dequant {
+  uint32_t mask_lo, mask_hi, magic;
+  half2_t bias, sixteenth, bias16;
 
-// Same, multiplied by the group scale in fp16: each value is the fp16 rounding
-// of the exact product (q - 8) * s, i.e. the dequantized weight bit for bit.
-__device__ __forceinline__ half8_t nibbles_to_half8_scaled(uint32_t w, half2_t s2) {
-  const uint32_t mask = 0x000F000Fu, magic = 0x64006400u;
-  const half2_t bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-  half2_t p0 = (bitcast<half2_t>((w & mask) | magic) + bias) * s2;
-  half2_t p1 = (bitcast<half2_t>(((w >> 4) & mask) | magic) + bias) * s2;
-  half2_t p2 = (bitcast<half2_t>(((w >> 8) & mask) | magic) + bias) * s2;
-  half2_t p3 = (bitcast<half2_t>(((w >> 12) & mask) | magic) + bias) * s2;
-  uint4_t r = {bitcast<uint32_t>(p0), bitcast<uint32_t>(p1), bitcast<uint32_t>(p2),
-               bitcast<uint32_t>(p3)};
-  return bitcast<half8_t>(r);
-}
+  __device__ __forceinline__ Dequant() {
+    mask_lo = 0x000F000Fu;
+    mask_hi = 0x00F000F0u;
+    magic = 0x64006400u;
+    // Keep the masks in SGPRs and the exponent pattern in a VGPR, so that the
+    // compiler emits the three-operand v_and_or_b32 (VOP3 on gfx950 takes no
+    // literal and at most one SGPR).
+    asm volatile("" : "+s"(mask_lo), "+s"(mask_hi));
+    asm volatile("" : "+v"(magic));
+    bias = half2_t{(_Float16)-1032.0f, (_Float16)-1032.0f};
+    sixteenth = half2_t{(_Float16)0.0625f, (_Float16)0.0625f};
+    bias16 = half2_t{(_Float16)-72.0f, (_Float16)-72.0f};
+  }
+
+  // Eight fp16 values u - 8 of one repacked word, in k order.
+  __device__ __forceinline__ half8_t operator()(uint32_t w) const {
+    const uint32_t t = w >> 8;
+    const half2_t p0 = bitcast<half2_t>((w & mask_lo) | magic) + bias;
+    const half2_t p1 =
+        __builtin_elementwise_fma(bitcast<half2_t>((w & mask_hi) | magic), sixteenth, bias16);
+    const half2_t p2 = bitcast<half2_t>((t & mask_lo) | magic) + bias;
+    const half2_t p3 =
+        __builtin_elementwise_fma(bitcast<half2_t>((t & mask_hi) | magic), sixteenth, bias16);
+    const uint4_t r = {bitcast<uint32_t>(p0), bitcast<uint32_t>(p1), bitcast<uint32_t>(p2),
+                       bitcast<uint32_t>(p3)};
+    return bitcast<half8_t>(r);
+  }
+
+  // The dequantized weights fp16((u - 8) * s): the exact u - 8 times the fp16
+  // scale, rounded once -- bit-equal to the format's definition.
+  __device__ __forceinline__ half8_t scaled(uint32_t w, half2_t s2) const {
+    const half8_t v = (*this)(w);
+    const half2_t q0 = half2_t{v[0], v[1]} * s2, q1 = half2_t{v[2], v[3]} * s2;
+    const half2_t q2 = half2_t{v[4], v[5]} * s2, q3 = half2_t{v[6], v[7]} * s2;
+    return half8_t{q0[0], q0[1], q1[0], q1[1], q2[0], q2[1], q3[0], q3[1]};
+  }
+};
 
 __device__ __forceinline__ uint4_t load_nt(const uint4_t *p) {
   return __builtin_nontemporal_load(p);
@@ -98,9 +124,6 @@ struct Problem {
   bool swiglu;
 };
 
-// Counters for the split-K fixup live at the start of the workspace.
-constexpr int64_t kCounterBytes = 64 * 1024;
-
 hipError_t launch_pack(const float *W, int64_t K, int64_t N, int32_t *packed, uint16_t *scales,
                        hipStream_t s);
 hipError_t launch_repack(const int32_t *packed, const uint16_t *scales, int64_t K, int64_t N,
@@ -112,7 +135,7 @@ hipError_t launch_dequant_canonical(const void *rw, const void *rs, int64_t K, i
 hipError_t launch_dequant_fragment(const void *rw, const void *rs, int64_t K, int64_t N,
                                    uint16_t *W16f, hipStream_t s);
 
-// Decode path: workspace bytes beyond the counters, and the launch.
+// Decode path: workspace bytes (split-K partials), and the launch.
 int64_t decode_workspace_bytes(const Problem &p);
 hipError_t launch_decode(const Problem &p, void *workspace, hipStream_t s);
 

@@ -4,29 +4,34 @@
 // (aicassindra.com), section "The job, stated precisely": C = A * dequant(W),
 // FP32 accumulation.  The page's section "What this simple kernel leaves on
 // the table" names the decode problems this kernel answers: too few programs
-// at M = 1 (hence split-K, reduced afterwards), dequantization in the loop,
-// and a layout not tuned for the hardware (hence the repacked layout).  The
-// scale is applied after each group's accumulation, as FuTransformer
+// at M = 1 (hence the K split, reduced afterwards), dequantization in the
+// loop, and a layout not tuned for the hardware (hence the repacked layout).
+// The scale is applied after each group's accumulation, as FuTransformer
 // (arXiv 2610.23796) section 3.3.4 does.
 //
 // Mapping on gfx950 (wave64, MFMA):
 //   * M <= 16: v_mfma_f32_16x16x32_f16, activation rows padded to 16;
 //     M <= 32: v_mfma_f32_32x32x16_f16, rows padded to 32.  MFMA is far from
 //     the bound here; it replaces ~8 VALU MACs per weight with one issue slot.
-//   * A workgroup owns SPW column strips (32 columns each; for SwiGLU the
-//     gate strips and the matching up strips) and a slice of K.  Its WAVES
-//     waves split that slice by whole groups of 128; every packed word is read
+//   * A workgroup owns SPW column strips (32 columns each; for SwiGLU a gate
+//     strip and the matching up strip) and a slice of K.  Its WAVES waves
+//     split that slice by whole groups of 128; every packed word is read
 //     exactly once, with 16-byte non-temporal loads (each wave-wide load is a
 //     contiguous 1 KiB tile), D groups ahead of use.
 //   * Nibbles become fp16 (u - 8) in registers (shift, and-or with the 0x6400
 //     exponent, one packed subtract).  Each group of 128 k accumulates into a
 //     zeroed MFMA tile; the tile times the column's fp16 scale is then added
 //     to the FP32 accumulator (one FMA per accumulator per group).
-//   * Waves reduce through LDS.  With KS > 1 workgroups on one strip group,
-//     each writes its partial tile to the workspace; the last one to arrive
-//     (agent-scope counter) sums the KS partials in split order and runs the
-//     epilogue, then resets the counter.  The order is fixed, so results are
-//     bit-identical from run to run.
+//   * Waves reduce through LDS.  With KS = 1 the workgroup then runs the
+//     epilogue.  With KS > 1 workgroups on one strip group, each writes its
+//     partial tile to the workspace and a second kernel sums the KS partials
+//     in split order and runs the epilogue.  No workgroup waits on another:
+//     on gfx950 an agent-scope fence writes back and invalidates the XCD's
+//     L2, so a per-workgroup fence (the "last workgroup finishes" pattern)
+//     serialises the whole grid; the kernel boundary publishes the partials
+//     once instead.  The order is fixed, so results are bit-identical from
+//     run to run.
+#include <cstdlib>
 #include <type_traits>
 
 #include "common.h"
@@ -45,39 +50,64 @@ struct DecodeArgs {
   int nsg;           // strip groups
   int up_off;        // SwiGLU: strip offset from a gate strip to its up strip
   int valid_strips;  // plain: NS; SwiGLU: number of gate strips
-  float *ws;
-  unsigned *counters;
+  float *ws;         // KS > 1: partial tiles [nsg][KS][SPW][M][32]
 };
 
-template <int MT, int SPW, int D>
+template <int MT, int SPW>
 struct DecodeFrag {
-  static constexpr int NB = 2;               // 16-byte weight vectors per strip per group
+  static constexpr int NB = 2;                 // 16-byte weight vectors per strip per group
   static constexpr int NA = MT == 16 ? 4 : 8;  // 16-byte activation vectors per group
   uint4_t b[SPW][NB];
   uint4_t a[NA];
   uint16_t sc[SPW][MT == 16 ? 2 : 1];
 };
 
-template <int MT, int SPW, int WAVES, int D, bool SWIGLU>
+// Epilogue of one element e of strip group sg's tile (tile element order
+// [s][m][c]; for SwiGLU e covers the gate half only and e + SH*M*32 is the
+// matching up element).  value_at(e) is the complete FP32 dot product.
+template <int SPW, bool SWIGLU, typename F>
+__device__ __forceinline__ void decode_epilogue(const DecodeArgs &p, int sg, int e, F value_at) {
+  constexpr int SH = SWIGLU ? SPW / 2 : SPW;
+  const int M = p.M;
+  const int s = e / (M * 32), rem = e - s * M * 32;
+  const int m = rem >> 5, c = rem & 31;
+  if constexpr (SWIGLU) {
+    const int gstrip = sg * SH + s;
+    if (gstrip < p.valid_strips) {
+      const float gv = value_at(e), uv = value_at(e + SH * M * 32);
+      p.out[(int64_t)m * p.ldo + gstrip * 32 + c] = to_half_bits(silu_mul(gv, uv));
+    }
+  } else {
+    const int col = (sg * SPW + s) * 32 + c;
+    if (col < p.N) p.out[(int64_t)m * p.ldo + col] = to_half_bits(value_at(e));
+  }
+}
+
+template <int MT, int SPW, int WAVES, int D, int RPL, bool SWIGLU>
 __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
+  static_assert(MT == 16 ? (RPL >= 1 && RPL <= 4) : RPL == 16, "rows per lane");
   extern __shared__ float lds[];  // [WAVES][SPW][M][32]
-  __shared__ int last_flag;
   constexpr int SH = SWIGLU ? SPW / 2 : SPW;
   constexpr int NPART = MT == 16 ? 2 : 1;  // 16-column halves (MT=16) or whole strip
   typedef typename std::conditional<MT == 16, float4_t, float16_t>::type acc_t;
-  typedef DecodeFrag<MT, SPW, D> Frag;
+  typedef DecodeFrag<MT, SPW> Frag;
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int sg = blockIdx.x % p.nsg, split = blockIdx.x / p.nsg;
   const int M = p.M;
+  const Dequant dq;
 
-  int strip[SPW];
-  bool sval[SPW];
+  // The grid covers exactly the strip groups that exist, so every strip a
+  // workgroup names is a real one (the repacked buffer pads N to 32 columns).
+  const char *wbase[SPW];
+  const char *sbase[SPW];
 #pragma unroll
   for (int s = 0; s < SPW; ++s) {
     const int base = sg * SH + (s % SH);
-    strip[s] = SWIGLU && s >= SH ? base + p.up_off : base;
-    sval[s] = base < p.valid_strips;
+    const int strip = SWIGLU && s >= SH ? base + p.up_off : base;
+    wbase[s] = (const char *)(p.rw + (int64_t)strip * p.KT * 64);
+    sbase[s] = (const char *)(p.rs + (int64_t)strip * p.KG8 * 256);
   }
 
   const int unit = split * WAVES + wave, nunits = p.KS * WAVES;
@@ -87,40 +117,47 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
   // Lane roles.  MT=16: lane = 16*g4 + c16; row of A = c16; lane group g4
   // covers k offsets 32*g4 .. +31 of the group.  MT=32: lane = 32*h + c;
   // row of A = c; lane half h covers k offsets 64x + 32h .. +31 of X-tile x.
-  const int mrow = MT == 16 ? (lane & 15) : (lane & 31);
-  const bool arow = mrow < M;
-  const uint4_t *Arow = (const uint4_t *)(p.A + (int64_t)(arow ? mrow : 0) * p.K);
+  // Rows of the MFMA tile beyond M read row M-1 again: output row m depends
+  // only on activation row m, and rows >= M are never stored.
   const int g4 = lane >> 4, c16 = lane & 15;
   const int h = lane >> 5, c32 = lane & 31;
+  const int mrow = MT == 16 ? c16 : c32;
+  const uint32_t arow_off = (uint32_t)(mrow < M ? mrow : M - 1) * (uint32_t)p.K * 2u;
+  // Byte offsets inside one group's 2 KiB of a strip (two 1 KiB tiles).
+  const uint32_t wlane = MT == 16 ? (uint32_t)(((g4 >> 1) * 64 + (g4 & 1) * 32 + c16) * 16)
+                                  : (uint32_t)(lane * 16);
+  const uint32_t slane = (uint32_t)((MT == 16 ? c16 : c32) * 16);
+  const uint32_t alane = MT == 16 ? (uint32_t)(g4 * 64) : (uint32_t)(h * 64);
+  const char *Ab = (const char *)p.A;
 
+  // Every address is a uniform base plus one 32-bit lane offset (plus a
+  // constant), which maps onto the scalar-base form of the global loads.
   auto load = [&](Frag &f, int g) {
+    const uint32_t ow = (uint32_t)g * 2048u + wlane;
+    const uint32_t os = (uint32_t)(g >> 3) * 512u + (uint32_t)(g & 7) * 2u + slane;
 #pragma unroll
     for (int s = 0; s < SPW; ++s) {
-      const uint4_t *tile = p.rw + ((int64_t)strip[s] * p.KT + 2 * g) * 64;
+      const char *wp = wbase[s] + ow;
       if constexpr (MT == 16) {
 #pragma unroll
-        for (int part = 0; part < 2; ++part)
-          f.b[s][part] = sval[s] ? load_nt(tile + (g4 >> 1) * 64 + (g4 & 1) * 32 + 16 * part + c16)
-                                 : uint4_t{0, 0, 0, 0};
+        for (int part = 0; part < 2; ++part) f.b[s][part] = load_nt((const uint4_t *)(wp + part * 256));
       } else {
 #pragma unroll
-        for (int x = 0; x < 2; ++x)
-          f.b[s][x] = sval[s] ? load_nt(tile + x * 64 + lane) : uint4_t{0, 0, 0, 0};
+        for (int x = 0; x < 2; ++x) f.b[s][x] = load_nt((const uint4_t *)(wp + x * 1024));
       }
-      const uint16_t *sp = p.rs + (((int64_t)strip[s] * p.KG8 + (g >> 3)) * 32) * 8 + (g & 7);
+      const char *sp = sbase[s] + os;
 #pragma unroll
-      for (int part = 0; part < NPART; ++part)
-        f.sc[s][part] = sval[s] ? sp[(MT == 16 ? 16 * part + c16 : c32) * 8] : (uint16_t)0;
+      for (int part = 0; part < NPART; ++part) f.sc[s][part] = *(const uint16_t *)(sp + part * 256);
     }
+    const char *ag = Ab + (uint32_t)(arow_off + (uint32_t)g * 256u + alane);
     if constexpr (MT == 16) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) f.a[j] = arow ? Arow[16 * g + 4 * g4 + j] : uint4_t{0, 0, 0, 0};
+      for (int j = 0; j < 4; ++j) f.a[j] = *(const uint4_t *)(ag + j * 16);
     } else {
 #pragma unroll
       for (int x = 0; x < 2; ++x)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          f.a[4 * x + j] = arow ? Arow[16 * g + 8 * x + 4 * h + j] : uint4_t{0, 0, 0, 0};
+        for (int j = 0; j < 4; ++j) f.a[4 * x + j] = *(const uint4_t *)(ag + x * 128 + j * 16);
     }
   };
 
@@ -140,29 +177,43 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
 #pragma unroll
           for (int j = 0; j < 4; ++j)
             t = __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<half8_t>(f.a[j]),
-                                                       nibbles_to_half8(f.b[s][part][j]), t, 0, 0,
-                                                       0);
+                                                       dq(f.b[s][part][j]), t, 0, 0, 0);
         } else {
 #pragma unroll
           for (int x = 0; x < 2; ++x)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
               t = __builtin_amdgcn_mfma_f32_32x32x16_f16(bitcast<half8_t>(f.a[4 * x + j]),
-                                                         nibbles_to_half8(f.b[s][x][j]), t, 0, 0,
-                                                         0);
+                                                         dq(f.b[s][x][j]), t, 0, 0, 0);
         }
         const float sc = (float)bitcast<_Float16>(f.sc[s][part]);
-        acc[s][part] += t * sc;
+        // Element r of a lane's tile holds row 4*g4 + r (MT=16), so with
+        // M < 4 only elements r < RPL can hold real rows.
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) acc[s][part][r] += t[r] * sc;
       }
     }
   };
 
-  // D-deep register pipeline over this wave's groups [g0, g1).
-  Frag f[D];
+  // D-deep register pipeline over this wave's groups [g0, g1): buffer d
+  // holds group g + d.  The steady-state loop is branch-free, so each buffer
+  // keeps its registers and the loads of groups g + D .. g + 2D - 1 stay in
+  // flight while groups g .. g + D - 1 are consumed.
+  // The prologue loads are unconditional (a wave with fewer than D groups
+  // loads its last group again) so that the loop is always entered with the
+  // same loads outstanding and the compiler's wait counts stay exact.
+  if (g1 > g0) {
+    Frag f[D];
 #pragma unroll
-  for (int d = 0; d < D; ++d)
-    if (g0 + d < g1) load(f[d], g0 + d);
-  for (int g = g0; g < g1; g += D) {
+    for (int d = 0; d < D; ++d) load(f[d], g0 + d < g1 ? g0 + d : g1 - 1);
+    int g = g0;
+    for (; g + 2 * D <= g1; g += D) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        compute(f[d]);
+        load(f[d], g + d + D);
+      }
+    }
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       if (g + d < g1) {
@@ -170,6 +221,9 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
         if (g + d + D < g1) load(f[d], g + d + D);
       }
     }
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+      if (g + D + d < g1) compute(f[d]);
   }
 
   // Cross-wave reduction through LDS: lds[((wave*SPW + s)*M + m)*32 + col].
@@ -188,58 +242,37 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
   __syncthreads();
 
   const int tileE = SPW * M * 32;
-  const int nthreads = WAVES * 64;
+  constexpr int nthreads = WAVES * 64;
   auto wave_sum = [&](int e) {
     float v = 0.0f;
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) v += lds[w * tileE + e];
     return v;
   };
-  auto epilogue = [&](auto value_at) {
-    if constexpr (SWIGLU) {
-      for (int e = threadIdx.x; e < SH * M * 32; e += nthreads) {
-        const int s = e / (M * 32), rem = e - s * M * 32;
-        const int m = rem >> 5, c = rem & 31;
-        const int gstrip = sg * SH + s;
-        if (gstrip < p.valid_strips) {
-          const float gv = value_at(e), uv = value_at(e + SH * M * 32);
-          p.out[(int64_t)m * p.ldo + gstrip * 32 + c] = to_half_bits(silu_mul(gv, uv));
-        }
-      }
-    } else {
-      for (int e = threadIdx.x; e < tileE; e += nthreads) {
-        const int s = e / (M * 32), rem = e - s * M * 32;
-        const int m = rem >> 5, c = rem & 31;
-        const int col = (sg * SPW + s) * 32 + c;
-        if (col < p.N) p.out[(int64_t)m * p.ldo + col] = to_half_bits(value_at(e));
-      }
-    }
-  };
 
   if (p.KS == 1) {
-    epilogue(wave_sum);
+    const int E = SH * M * 32;
+    for (int e = threadIdx.x; e < E; e += nthreads) decode_epilogue<SPW, SWIGLU>(p, sg, e, wave_sum);
     return;
   }
-
   float *mine = p.ws + ((int64_t)sg * p.KS + split) * tileE;
   for (int e = threadIdx.x; e < tileE; e += nthreads) mine[e] = wave_sum(e);
-  __threadfence();  // release this wave's partial stores at agent scope
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned prev = __hip_atomic_fetch_add(p.counters + sg, 1u, __ATOMIC_ACQ_REL,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-    const int is_last = prev == (unsigned)(p.KS - 1);
-    if (is_last)
-      __hip_atomic_store(p.counters + sg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    last_flag = is_last;
-  }
-  __syncthreads();
-  if (!last_flag) return;
-  __threadfence();  // acquire the other workgroups' partials
+}
+
+// Second stage for KS > 1: one thread per output element sums the KS partial
+// tiles of its strip group in split order, then runs the epilogue.
+template <int SPW, bool SWIGLU>
+__global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs p) {
+  constexpr int SH = SWIGLU ? SPW / 2 : SPW;
+  const int E = SH * p.M * 32;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)p.nsg * E) return;
+  const int sg = (int)(idx / E), e = (int)(idx - (int64_t)sg * E);
+  const int tileE = SPW * p.M * 32;
   const float *all = p.ws + (int64_t)sg * p.KS * tileE;
-  epilogue([&](int e) {
+  decode_epilogue<SPW, SWIGLU>(p, sg, e, [&](int x) {
     float v = 0.0f;
-    for (int sp = 0; sp < p.KS; ++sp) v += all[(int64_t)sp * tileE + e];
+    for (int sp = 0; sp < p.KS; ++sp) v += all[(int64_t)sp * tileE + x];
     return v;
   });
 }
@@ -251,22 +284,39 @@ struct DecodeConfig {
   int MT, SPW, WAVES, D, KS, nsg;
 };
 
+static int env_int(const char *name, int fallback) {
+  const char *v = std::getenv(name);
+  if (v == nullptr || *v == 0) return fallback;
+  const int x = std::atoi(v);
+  return x > 0 ? x : fallback;
+}
+
+// Waves per workgroup and K splits.  The aim is enough waves in flight to
+// cover HBM latency (several per SIMD on all 256 CUs) without splitting K
+// across workgroups unless the strip groups alone leave CUs idle.
+// W4A16_DECODE_WAVES (4 or 8), W4A16_DECODE_KS and W4A16_DECODE_DEPTH
+// (groups loaded ahead: 2 or 4) override the choice.
 static DecodeConfig decode_config(const Problem &p) {
   DecodeConfig c;
   c.MT = p.M <= 16 ? 16 : 32;
-  c.WAVES = 4;
-  c.D = 2;
   const int64_t NS = ceil_div(p.N, kStrip);
   const int64_t KG = p.K / kGroup;
   c.SPW = p.swiglu ? 2 : 1;
-  c.nsg = (int)(p.swiglu ? (p.N / 2 / kStrip) : ceil_div(NS, c.SPW));
-  // Enough workgroups to cover the 256 CUs several times over, but never
-  // fewer than one group per wave.
-  int64_t ks = ceil_div(1024, c.nsg);
+  c.nsg = (int)(p.swiglu ? (p.N / 2 / kStrip) : NS);
+  int waves = c.nsg < 512 ? 8 : 4;
+  waves = env_int("W4A16_DECODE_WAVES", waves) >= 8 ? 8 : 4;
+  // LDS for the cross-wave reduction: WAVES * SPW * M * 32 floats < 64 KiB.
+  while (waves > 4 && (int64_t)waves * c.SPW * p.M * 32 * 4 >= 65536) waves /= 2;
+  c.WAVES = waves;
+  c.D = env_int("W4A16_DECODE_DEPTH", 2) >= 4 ? 4 : 2;
+  int64_t ks = 1;
+  if (c.nsg < 256) ks = ceil_div(256, c.nsg);
   const int64_t ks_max = KG / c.WAVES > 0 ? KG / c.WAVES : 1;
   if (ks > ks_max) ks = ks_max;
-  if (ks < 1) ks = 1;
+  ks = env_int("W4A16_DECODE_KS", (int)ks);
+  if (ks > KG) ks = KG;
   if (ks > 64) ks = 64;
+  if (ks < 1) ks = 1;
   c.KS = (int)ks;
   return c;
 }
@@ -277,12 +327,27 @@ int64_t decode_workspace_bytes(const Problem &p) {
   return (int64_t)c.nsg * c.KS * c.SPW * p.M * 32 * (int64_t)sizeof(float);
 }
 
-template <int MT, int SPW, int WAVES, int D, bool SWIGLU>
+template <int MT, int SPW, int WAVES, int D, int RPL, bool SWIGLU>
 static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t s) {
   const size_t lds = (size_t)WAVES * SPW * a.M * 32 * sizeof(float);
-  hipLaunchKernelGGL((decode_kernel<MT, SPW, WAVES, D, SWIGLU>), dim3(a.nsg * a.KS),
+  hipLaunchKernelGGL((decode_kernel<MT, SPW, WAVES, D, RPL, SWIGLU>), dim3(a.nsg * a.KS),
                      dim3(WAVES * 64), lds, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.KS == 1) return e;
+  constexpr int SH = SWIGLU ? SPW / 2 : SPW;
+  const int64_t total = (int64_t)a.nsg * SH * a.M * 32;
+  hipLaunchKernelGGL((decode_reduce_kernel<SPW, SWIGLU>), dim3((unsigned)ceil_div(total, 256)),
+                     dim3(256), 0, s, a);
   return hipGetLastError();
+}
+
+template <int MT, int SPW, int RPL, bool SWIGLU>
+static hipError_t launch_decode_w(const DecodeArgs &a, const DecodeConfig &c, hipStream_t s) {
+  if (c.D == 4)
+    return c.WAVES == 8 ? launch_decode_t<MT, SPW, 8, 4, RPL, SWIGLU>(a, s)
+                        : launch_decode_t<MT, SPW, 4, 4, RPL, SWIGLU>(a, s);
+  return c.WAVES == 8 ? launch_decode_t<MT, SPW, 8, 2, RPL, SWIGLU>(a, s)
+                      : launch_decode_t<MT, SPW, 4, 2, RPL, SWIGLU>(a, s);
 }
 
 hipError_t launch_decode(const Problem &p, void *workspace, hipStream_t s) {
@@ -304,13 +369,16 @@ hipError_t launch_decode(const Problem &p, void *workspace, hipStream_t s) {
   a.nsg = c.nsg;
   a.up_off = (int)(p.N / 2 / kStrip);
   a.valid_strips = p.swiglu ? a.up_off : a.NS;
-  a.counters = (unsigned *)workspace;
-  a.ws = (float *)((char *)workspace + kCounterBytes);
-  if (c.KS > 1 && (workspace == nullptr || c.nsg * 4 > kCounterBytes)) return hipErrorInvalidValue;
-  if (c.MT == 16) {
-    return p.swiglu ? launch_decode_t<16, 2, 4, 2, true>(a, s) : launch_decode_t<16, 1, 4, 2, false>(a, s);
-  }
-  return p.swiglu ? launch_decode_t<32, 2, 4, 2, true>(a, s) : launch_decode_t<32, 1, 4, 2, false>(a, s);
+  a.ws = (float *)workspace;
+  if (c.KS > 1 && workspace == nullptr) return hipErrorInvalidValue;
+  if (c.MT == 16 && p.M == 1)
+    return p.swiglu ? launch_decode_w<16, 2, 1, true>(a, c, s)
+                    : launch_decode_w<16, 1, 1, false>(a, c, s);
+  if (c.MT == 16)
+    return p.swiglu ? launch_decode_w<16, 2, 4, true>(a, c, s)
+                    : launch_decode_w<16, 1, 4, false>(a, c, s);
+  return p.swiglu ? launch_decode_w<32, 2, 16, true>(a, c, s)
+                  : launch_decode_w<32, 1, 16, false>(a, c, s);
 }
 
 }  // namespace w4a16

@@ -173,19 +173,20 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint4_t *__restrict_
   const _Float16 sh = bitcast<_Float16>(rs[((t * KG8 + (g >> 3)) * 32 + c) * 8 + (g & 7)]);
   const half2_t s2 = {sh, sh};
   const uint4_t v = rw[idx];
+  const Dequant dq;
   if (CANONICAL) {
     if (n >= N) return;
     const int64_t k0 = 64 * q + 32 * h;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const half8_t w = nibbles_to_half8_scaled(v[j], s2);
+      const half8_t w = dq.scaled(v[j], s2);
 #pragma unroll
       for (int i = 0; i < 8; ++i) W16[(k0 + 8 * j + i) * N + n] = bitcast<uint16_t>(w[i]);
     }
   } else {
     uint4_t *out = (uint4_t *)W16 + idx * 4;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) out[j] = bitcast<uint4_t>(nibbles_to_half8_scaled(v[j], s2));
+    for (int j = 0; j < 4; ++j) out[j] = bitcast<uint4_t>(dq.scaled(v[j], s2));
   }
 }
 

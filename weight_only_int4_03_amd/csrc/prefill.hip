@@ -64,6 +64,7 @@ void prefill_kernel(PrefillArgs p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, c = lane & 31;
   const int M = p.M;
+  const Dequant dq;
 
   // XCD-aware tile walk.
   const int T = p.tiles_m * p.tiles_n;
@@ -150,7 +151,7 @@ void prefill_kernel(PrefillArgs p) {
         if constexpr (DENSE)
           bf[w] = bitcast<half8_t>(r.v[w][j]);
         else
-          bf[w] = nibbles_to_half8_scaled(r.v[w][0][j], s2[w]);
+          bf[w] = dq.scaled(r.v[w][0][j], s2[w]);
       }
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
@@ -275,7 +276,7 @@ int64_t dense_workspace_bytes(const Problem &p) {
 
 hipError_t launch_dense(const Problem &p, void *workspace, hipStream_t s) {
   if (workspace == nullptr) return hipErrorInvalidValue;
-  void *w16f = (char *)workspace + kCounterBytes;
+  void *w16f = workspace;
   hipError_t e = launch_dequant_fragment(p.rw, p.rs, p.K, p.N, (uint16_t *)w16f, s);
   if (e != hipSuccess) return e;
   return launch_tiled<true>(p, w16f, s);
