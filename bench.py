@@ -93,15 +93,13 @@ def workloads():
 
 
 def kernel_key(M, K, N, swiglu):
-    """Kernel instance that the automatic path launches (for grouping)."""
-    path = w4a16.select_path(M, K, N, swiglu)
-    if path == "decode":
-        return "decode_kernel<%d,%d,%s>" % (16 if M <= 16 else 32, 2 if swiglu else 1,
-                                            "swiglu" if swiglu else "plain")
-    if path == "prefill":
-        mi = 8 if M > 128 else (4 if M > 64 else 2)
-        return "prefill_kernel<%d,%s>" % (mi, "swiglu" if swiglu else "plain")
-    return "dense(dequant+gemm)<%s>" % ("swiglu" if swiglu else "plain")
+    """The kernel instance a GEMM launches under the automatic path, as the
+    profiler names it, marked when a second (split-K reduction) launch
+    follows it."""
+    desc = w4a16.describe(M, K, N, swiglu)
+    first = desc.split(";")[0]
+    name = first.split(" workgroups=")[0].strip()
+    return name + (" + reduce" if ";" in desc else "")
 
 
 def source_digest():
@@ -185,6 +183,8 @@ def main():
     ap.add_argument("--workload", default="llama8b_decode", choices=sorted(workloads()))
     ap.add_argument("--reps", type=int, default=20, help="graph replays per GEMM timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (for hardware-counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -197,6 +197,15 @@ def main():
         raise SystemExit("bench.py needs a GPU")
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        # A plain copy of known size: reads and writes exactly 2^30 bytes each.
+        src = torch.ones(1 << 29, dtype=torch.float16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": 1 << 30, "copy_bytes_written": 1 << 30, "launches": 5}))
+        return
     w4a16.lib()
 
     desc, units = workloads()[args.workload]
@@ -297,11 +306,12 @@ def main():
         us = a.elapsed_time(b) * 1e3 / (args.reps * ncopies)
         by, fl = alg_bytes(m, k, n, sw), flops(m, k, n)
         detail.append({"gemm": label, "M": m, "K": k, "N": n, "swiglu": sw,
-                       "kernel": kernel_key(m, k, n, sw), "us": round(us, 3),
+                       "kernel": kernel_key(m, k, n, sw), "launch": w4a16.describe(m, k, n, sw),
+                       "us": round(us, 3),
                        "GB/s": round(by / us / 1e3, 1), "TFLOP/s": round(fl / us / 1e6, 2),
                        "hbm_frac": round(by / us / 1e3 / HBM_PEAK_GBS, 4),
                        "mfma_frac": round(fl / us / 1e6 / MFMA_F16_PEAK_TFLOPS, 4)})
-        log("  %-22s %-32s %9.2f us %8.1f GB/s %8.2f TFLOP/s" %
+        log("  %-22s %-44s %9.2f us %8.1f GB/s %8.2f TFLOP/s" %
             (label, detail[-1]["kernel"], us, detail[-1]["GB/s"], detail[-1]["TFLOP/s"]))
         del g
 

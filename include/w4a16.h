@@ -15,7 +15,7 @@
  *   scales  fp16  [K/G, N]  row-major, passed as uint16_t bit patterns.
  * The GEMM consumes a device-friendly permutation of that format built once
  * at load time by w4a16_repack (the same page, section "Integrating a kernel
- * into serving": repack once, at load, never per call).
+ * into serving", advises repacking at load time only, not on every call).
  *
  * Conventions shared by every call:
  *   - Return value: W4A16_OK (0) or a negative W4A16_ERR_* code; no exception
@@ -83,10 +83,11 @@ int w4a16_pack_host(const float *W, int64_t K, int64_t N, int G, int32_t *packed
                     uint16_t *scales, int nthreads);
 
 /* ---------------------------------------------------------------------------
- * Repacked layout, built once at load (data contract: "many production
- * kernels permute this layout further at load time").  Columns are padded to
- * a multiple of 32 (the pad dequantizes to zero).  Byte sizes of the two
- * buffers, or a negative error code for an invalid shape.
+ * Repacked layout, built once at load (the data contract section notes that
+ * production kernels often permute the canonical layout at load time).
+ * Columns are padded to a multiple of 32 (the pad dequantizes to zero).
+ * Byte sizes of the two buffers, or a negative error code for an invalid
+ * shape.
  * ------------------------------------------------------------------------- */
 int64_t w4a16_repacked_weight_bytes(int64_t K, int64_t N, int G);
 int64_t w4a16_repacked_scale_bytes(int64_t K, int64_t N, int G);
@@ -99,8 +100,9 @@ int64_t w4a16_repacked_scale_bytes(int64_t K, int64_t N, int G);
 int w4a16_repack(const int32_t *packed_d, const uint16_t *scales_d, int64_t K, int64_t N,
                  int G, void *rw_d, void *rs_d, w4a16_stream_t stream);
 
-/* Inverse of w4a16_repack, for verifying a load ("verify one layer after
- * repacking").  Writes canonical packed_d [K/8,N] and scales_d [K/G,N]. */
+/* Inverse of w4a16_repack, for checking a load after repacking (the same
+ * page's serving section recommends checking one layer).  Writes canonical
+ * packed_d [K/8,N] and scales_d [K/G,N]. */
 int w4a16_unrepack(const void *rw_d, const void *rs_d, int64_t K, int64_t N, int G,
                    int32_t *packed_d, uint16_t *scales_d, w4a16_stream_t stream);
 
@@ -152,6 +154,13 @@ int64_t w4a16_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N, int G, int f
 /* The path (W4A16_PATH_DECODE / PREFILL / DENSE) that AUTO picks for this
  * problem, or a negative error code. */
 int w4a16_select_path(int64_t M, int64_t K, int64_t N, int G, int flags);
+
+/* Writes into buf (len bytes, NUL-terminated, truncated if short) a text
+ * description of the launches w4a16_gemm_ex would make for this problem and
+ * flags: each kernel instance as it is named in profiler output, with its
+ * grid.  Host only; touches no device.  Returns the length written or a
+ * negative error code (W4A16_ERR_INVALID for a bad shape, flag or buffer). */
+int w4a16_describe(int64_t M, int64_t K, int64_t N, int G, int flags, char *buf, int64_t len);
 
 /* Thread-local message for the calling thread's last error ("" if none). */
 const char *w4a16_last_error(void);

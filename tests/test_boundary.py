@@ -99,3 +99,18 @@ def test_dispatch_table():
     assert w4a16.select_path(32, 4096, 4096) == "decode"
     assert w4a16.select_path(4096, 4096, 28672) == "prefill"
     assert w4a16.workspace_bytes(4096, 4096, 4096, path="dense") >= 4096 * 4096 * 2
+
+
+def test_describe_names_the_launches():
+    """The launch description names kernel instances as profilers print them."""
+    d = w4a16.describe(1, 4096, 28672, swiglu=True)
+    assert d.startswith("decode_kernel<16, 2, ") and d.split(">")[0].endswith("true")
+    assert "prefill_kernel<8, 2, false, true>" in w4a16.describe(4096, 4096, 28672, swiglu=True)
+    assert w4a16.describe(4096, 4096, 4096, path="dense").startswith("dequant_kernel<false>; ")
+    assert "row slices" in w4a16.describe(100, 4096, 4096, path="decode")
+    L = w4a16.lib()
+    import ctypes
+    buf = ctypes.create_string_buffer(8)
+    assert L.w4a16_describe(1, 4096, 4096, 128, 0, ctypes.addressof(buf), 8) == 7   # truncated
+    assert L.w4a16_describe(0, 4096, 4096, 128, 0, ctypes.addressof(buf), 8) == w4a16.ERR_INVALID
+    assert L.w4a16_describe(1, 4096, 4096, 128, 0, 0, 8) == w4a16.ERR_INVALID

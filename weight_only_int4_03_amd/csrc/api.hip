@@ -334,6 +334,39 @@ int64_t w4a16_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N, int G, int f
   return workspace_for(path, p);
 }
 
+int w4a16_describe(int64_t M, int64_t K, int64_t N, int G, int flags, char *buf, int64_t len) {
+  int rc = check_gpu_shape(K, N, G, "w4a16_describe");
+  if (rc != W4A16_OK) return rc;
+  if (M < 1) return fail(W4A16_ERR_INVALID, "w4a16_describe: M must be >= 1");
+  if (buf == nullptr || len < 1) return fail(W4A16_ERR_INVALID, "w4a16_describe: no buffer");
+  if (flags & ~(0xF | W4A16_FLAG_SWIGLU))
+    return fail(W4A16_ERR_INVALID, "w4a16_describe: unknown flags 0x%x", flags);
+  const bool swiglu = (flags & W4A16_FLAG_SWIGLU) != 0;
+  if (swiglu && N % 64 != 0)
+    return fail(W4A16_ERR_INVALID, "w4a16_describe: N (%lld) must be a multiple of 64",
+                (long long)N);
+  int path = flags & 0xF;
+  if (path == W4A16_PATH_AUTO) path = select_path(M, K, N);
+  if (path < W4A16_PATH_DECODE || path > W4A16_PATH_DENSE)
+    return fail(W4A16_ERR_INVALID, "w4a16_describe: unknown path %d", path);
+  Problem p{nullptr, M, K, N, nullptr, nullptr, nullptr, swiglu};
+  char tmp[512];
+  int k;
+  if (path == W4A16_PATH_DECODE) {
+    Problem q = p;
+    q.M = M < kDecodeMaxM ? M : kDecodeMaxM;
+    k = decode_describe(q, tmp, sizeof tmp);
+    const int64_t slices = ceil_div(M, kDecodeMaxM);
+    if (slices > 1 && k > 0 && k < (int)sizeof tmp)
+      k += snprintf(tmp + k, sizeof tmp - k, " (x%lld row slices of 32)", (long long)slices);
+  } else {
+    k = tiled_describe(p, path == W4A16_PATH_DENSE, tmp, sizeof tmp);
+  }
+  if (k < 0) return fail(W4A16_ERR_INVALID, "w4a16_describe: formatting failed");
+  snprintf(buf, (size_t)len, "%s", tmp);
+  return k < len ? k : (int)(len - 1);
+}
+
 int w4a16_select_path(int64_t M, int64_t K, int64_t N, int G, int flags) {
   int rc = check_gpu_shape(K, N, G, "w4a16_select_path");
   if (rc != W4A16_OK) return rc;

@@ -135,13 +135,16 @@ hipError_t launch_dequant_canonical(const void *rw, const void *rs, int64_t K, i
 hipError_t launch_dequant_fragment(const void *rw, const void *rs, int64_t K, int64_t N,
                                    uint16_t *W16f, hipStream_t s);
 
-// Decode path: workspace bytes (split-K partials), and the launch.
+// Decode path: workspace bytes (split-K partials), the launch, and a text
+// description of the launch (kernel instances and grid).
 int64_t decode_workspace_bytes(const Problem &p);
+int decode_describe(const Problem &p, char *buf, size_t n);
 hipError_t launch_decode(const Problem &p, void *workspace, hipStream_t s);
 
 // Prefill path (fused dequant) and dense path (fp16 fragment-ordered weights).
 hipError_t launch_prefill(const Problem &p, hipStream_t s);
 int64_t dense_workspace_bytes(const Problem &p);
 hipError_t launch_dense(const Problem &p, void *workspace, hipStream_t s);
+int tiled_describe(const Problem &p, bool dense, char *buf, size_t n);
 
 }  // namespace w4a16

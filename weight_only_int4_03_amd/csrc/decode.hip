@@ -31,6 +31,7 @@
 //     serialises the whole grid; the kernel boundary publishes the partials
 //     once instead.  The order is fixed, so results are bit-identical from
 //     run to run.
+#include <cstdio>
 #include <cstdlib>
 #include <type_traits>
 
@@ -303,22 +304,32 @@ static DecodeConfig decode_config(const Problem &p) {
   const int64_t KG = p.K / kGroup;
   c.SPW = p.swiglu ? 2 : 1;
   c.nsg = (int)(p.swiglu ? (p.N / 2 / kStrip) : NS);
-  int waves = c.nsg < 512 ? 8 : 4;
+  int waves = (c.nsg < 384 || KG >= 128) ? 8 : 4;
   waves = env_int("W4A16_DECODE_WAVES", waves) >= 8 ? 8 : 4;
   // LDS for the cross-wave reduction: WAVES * SPW * M * 32 floats < 64 KiB.
   while (waves > 4 && (int64_t)waves * c.SPW * p.M * 32 * 4 >= 65536) waves /= 2;
   c.WAVES = waves;
   c.D = env_int("W4A16_DECODE_DEPTH", 2) >= 4 ? 4 : 2;
-  int64_t ks = 1;
-  if (c.nsg < 256) ks = ceil_div(256, c.nsg);
-  const int64_t ks_max = KG / c.WAVES > 0 ? KG / c.WAVES : 1;
-  if (ks > ks_max) ks = ks_max;
+  // A second launch (the reduction) costs more than idle CUs unless each
+  // wave still streams a long K slice: split K only for narrow, deep shapes.
+  int64_t ks = (c.nsg < 256 && KG / c.WAVES >= 8) ? 2 : 1;
   ks = env_int("W4A16_DECODE_KS", (int)ks);
   if (ks > KG) ks = KG;
   if (ks > 64) ks = 64;
   if (ks < 1) ks = 1;
   c.KS = (int)ks;
   return c;
+}
+
+int decode_describe(const Problem &p, char *buf, size_t n) {
+  const DecodeConfig c = decode_config(p);
+  const int rpl = c.MT == 16 ? (p.M == 1 ? 1 : 4) : 16;
+  const char *sw = p.swiglu ? "true" : "false";
+  int k = snprintf(buf, n, "decode_kernel<%d, %d, %d, %d, %d, %s> workgroups=%d threads=%d ks=%d",
+                   c.MT, c.SPW, c.WAVES, c.D, rpl, sw, c.nsg * c.KS, c.WAVES * 64, c.KS);
+  if (c.KS > 1 && k > 0 && (size_t)k < n)
+    k += snprintf(buf + k, n - k, "; decode_reduce_kernel<%d, %s>", c.SPW, sw);
+  return k;
 }
 
 int64_t decode_workspace_bytes(const Problem &p) {

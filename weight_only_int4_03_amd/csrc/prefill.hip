@@ -31,6 +31,8 @@
 //     over the 8 XCDs) works on one contiguous range of tiles, walked in
 //     groups of 4 row tiles so that concurrently running tiles share weight
 //     columns and activation rows in that XCD's L2.
+#include <cstdio>
+
 #include "common.h"
 
 namespace w4a16 {
@@ -268,6 +270,14 @@ static hipError_t launch_tiled(const Problem &p, const void *weights, hipStream_
 }
 
 hipError_t launch_prefill(const Problem &p, hipStream_t s) { return launch_tiled<false>(p, p.rw, s); }
+
+int tiled_describe(const Problem &p, bool dense, char *buf, size_t n) {
+  const int MI = p.M > 128 ? 8 : (p.M > 64 ? 4 : 2);
+  const PrefillArgs a = prefill_args(p, 32 * MI, nullptr);
+  return snprintf(buf, n, "%sprefill_kernel<%d, 2, %s, %s> workgroups=%d threads=256",
+                  dense ? "dequant_kernel<false>; " : "", MI, dense ? "true" : "false",
+                  p.swiglu ? "true" : "false", a.tiles_m * a.tiles_n);
+}
 
 int64_t dense_workspace_bytes(const Problem &p) {
   // fp16 weights in fragment order: 64 columns x 64 k x 2 bytes per (strip, tile) half.

@@ -56,6 +56,7 @@ _SIGNATURES = {
     "w4a16_gemm_ex": ([_p, _i64, _i64, _p, _p, _i64, _int, _p, _int, _p, _i64, _p], _int),
     "w4a16_gemm_workspace_bytes": ([_i64, _i64, _i64, _int, _int], _i64),
     "w4a16_select_path": ([_i64, _i64, _i64, _int, _int], _int),
+    "w4a16_describe": ([_i64, _i64, _i64, _int, _int, _p, _i64], _int),
     "w4a16_last_error": ([], ctypes.c_char_p),
     "w4a16_version": ([], ctypes.c_char_p),
 }
@@ -235,6 +236,15 @@ def workspace_bytes(M: int, K: int, N: int, swiglu: bool = False, path: str | in
 def select_path(M: int, K: int, N: int, swiglu: bool = False, G: int = G) -> str:
     code = _check(lib().w4a16_select_path(M, K, N, G, FLAG_SWIGLU if swiglu else 0))
     return {v: k for k, v in PATHS.items()}[code]
+
+
+def describe(M: int, K: int, N: int, swiglu: bool = False, path: str | int = "auto",
+             G: int = G) -> str:
+    """The kernel launches (profiler names and grids) a GEMM of this shape makes."""
+    flags = (PATHS[path] if isinstance(path, str) else int(path)) | (FLAG_SWIGLU if swiglu else 0)
+    buf = ctypes.create_string_buffer(512)
+    _check(lib().w4a16_describe(M, K, N, G, flags, ctypes.addressof(buf), len(buf)))
+    return buf.value.decode()
 
 
 def load_weight(W_host: np.ndarray, device="cuda", G: int = G) -> RepackedWeight:
