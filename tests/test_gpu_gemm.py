@@ -132,3 +132,43 @@ def test_empty_and_single_group():
     assert w4a16.gemm(empty, w).shape == (0, 64)
     for path in PATHS:
         gemm_case(3, 128, 64, path=path, W=W, weight=w, seed=2)
+
+
+COOP_CONFIGS = [(4, 1, 1), (8, 1, 1), (2, 2, 1), (4, 2, 1), (2, 4, 1), (1, 4, 1), (2, 4, 2), (1, 4, 3)]
+
+
+@pytest.mark.parametrize("wc,wk,ks", COOP_CONFIGS)
+@pytest.mark.parametrize("M", [1, 7, 16, 32])
+@pytest.mark.parametrize("K,N,swiglu", [(1152, 1064, False), (1024, 2112, True), (2560, 4160, False)])
+def test_decode_cooperative_forced(monkeypatch, wc, wk, ks, M, K, N, swiglu):
+    """The cooperative decode kernel (activations and scales staged in LDS)
+    in every configuration the library can run, on ragged shapes: a tail
+    strip (N = 1064), an odd number of gate strips (N = 2112), K splits that
+    leave partial rounds (K = 1152, 2560 with KS = 3)."""
+    monkeypatch.setenv("W4A16_DECODE_COOP", "1")
+    monkeypatch.setenv("W4A16_COOP_WC", str(wc))
+    monkeypatch.setenv("W4A16_COOP_WK", str(wk))
+    monkeypatch.setenv("W4A16_COOP_KS", str(ks))
+    desc = w4a16.describe(M, K, N, swiglu, path="decode")
+    say("coop forced:", desc)
+    if M <= 16:   # at M = 32 some configurations need more than 64 KiB of LDS and fall back
+        assert desc.startswith("decode_coop_kernel"), desc
+    gemm_case(M, K, N, swiglu=swiglu, path="decode", seed=wc * 100 + wk * 10 + ks + M)
+
+
+def test_decode_cooperative_bit_exact_integer_inputs(monkeypatch):
+    """Integer-exact inputs through the cooperative kernel with a K split:
+    the result is the oracle's bit for bit."""
+    monkeypatch.setenv("W4A16_DECODE_COOP", "1")
+    monkeypatch.setenv("W4A16_COOP_WC", "2")
+    monkeypatch.setenv("W4A16_COOP_WK", "4")
+    monkeypatch.setenv("W4A16_COOP_KS", "2")
+    K, N = 4096, 2048
+    for M in (1, 16):
+        W = synth.grid_weights(K, N, p=4, seed=M)
+        A = synth.ternary_activations(M, K, density=1.0, seed=M)
+        w = w4a16.load_weight(W)
+        out = fp16_out(w4a16.gemm(to_dev(A), w, path="decode"))
+        packed_o, s16_o = orc().quantize_pack(W)
+        C = orc().gemm_f64(A, packed_o, s16_o)
+        assert np.array_equal(out.astype(np.float64), C)

@@ -36,23 +36,9 @@
 #include <type_traits>
 
 #include "common.h"
+#include "decode_args.h"
 
 namespace w4a16 {
-
-struct DecodeArgs {
-  const uint16_t *A;
-  int M, K;
-  const uint4_t *rw;
-  const uint16_t *rs;
-  int N, NS, KT, KG, KG8;
-  uint16_t *out;
-  int ldo;
-  int KS;            // workgroups per strip group (K splits)
-  int nsg;           // strip groups
-  int up_off;        // SwiGLU: strip offset from a gate strip to its up strip
-  int valid_strips;  // plain: NS; SwiGLU: number of gate strips
-  float *ws;         // KS > 1: partial tiles [nsg][KS][SPW][M][32]
-};
 
 template <int MT, int SPW>
 struct DecodeFrag {
@@ -62,27 +48,6 @@ struct DecodeFrag {
   uint4_t a[NA];
   uint16_t sc[SPW][MT == 16 ? 2 : 1];
 };
-
-// Epilogue of one element e of strip group sg's tile (tile element order
-// [s][m][c]; for SwiGLU e covers the gate half only and e + SH*M*32 is the
-// matching up element).  value_at(e) is the complete FP32 dot product.
-template <int SPW, bool SWIGLU, typename F>
-__device__ __forceinline__ void decode_epilogue(const DecodeArgs &p, int sg, int e, F value_at) {
-  constexpr int SH = SWIGLU ? SPW / 2 : SPW;
-  const int M = p.M;
-  const int s = e / (M * 32), rem = e - s * M * 32;
-  const int m = rem >> 5, c = rem & 31;
-  if constexpr (SWIGLU) {
-    const int gstrip = sg * SH + s;
-    if (gstrip < p.valid_strips) {
-      const float gv = value_at(e), uv = value_at(e + SH * M * 32);
-      p.out[(int64_t)m * p.ldo + gstrip * 32 + c] = to_half_bits(silu_mul(gv, uv));
-    }
-  } else {
-    const int col = (sg * SPW + s) * 32 + c;
-    if (col < p.N) p.out[(int64_t)m * p.ldo + col] = to_half_bits(value_at(e));
-  }
-}
 
 template <int MT, int SPW, int WAVES, int D, int RPL, bool SWIGLU>
 __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
@@ -322,6 +287,19 @@ static DecodeConfig decode_config(const Problem &p) {
 }
 
 int decode_describe(const Problem &p, char *buf, size_t n) {
+  int WC, WK, KS;
+  if (coop_config(p, WC, WK, KS)) {
+    const int mt = p.M <= 16 ? 16 : 32;
+    const int rpl = mt == 16 ? (p.M == 1 ? 1 : 4) : 16;
+    const int spw = p.swiglu ? 2 : 1;
+    const int nsg = (int)(p.swiglu ? (p.N / 2 / kStrip) : ceil_div(p.N, kStrip));
+    const char *sw = p.swiglu ? "true" : "false";
+    int k = snprintf(buf, n, "decode_coop_kernel<%d, %d, %d, %d, %d, %s> workgroups=%d threads=%d ks=%d",
+                     mt, spw, WC, WK, rpl, sw, (int)ceil_div(nsg, WC) * KS, WC * WK * 64, KS);
+    if (KS > 1 && k > 0 && (size_t)k < n)
+      k += snprintf(buf + k, n - k, "; decode_reduce_kernel<%d, %s>", spw, sw);
+    return k;
+  }
   const DecodeConfig c = decode_config(p);
   const int rpl = c.MT == 16 ? (p.M == 1 ? 1 : 4) : 16;
   const char *sw = p.swiglu ? "true" : "false";
@@ -333,6 +311,12 @@ int decode_describe(const Problem &p, char *buf, size_t n) {
 }
 
 int64_t decode_workspace_bytes(const Problem &p) {
+  int WC, WK, KS;
+  if (coop_config(p, WC, WK, KS)) {
+    const int64_t nsg = p.swiglu ? p.N / 2 / kStrip : ceil_div(p.N, kStrip);
+    const int64_t spw = p.swiglu ? 2 : 1;
+    return KS == 1 ? 0 : nsg * KS * spw * p.M * 32 * (int64_t)sizeof(float);
+  }
   const DecodeConfig c = decode_config(p);
   if (c.KS == 1) return 0;
   return (int64_t)c.nsg * c.KS * c.SPW * p.M * 32 * (int64_t)sizeof(float);
@@ -345,11 +329,7 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t s) {
                      dim3(WAVES * 64), lds, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.KS == 1) return e;
-  constexpr int SH = SWIGLU ? SPW / 2 : SPW;
-  const int64_t total = (int64_t)a.nsg * SH * a.M * 32;
-  hipLaunchKernelGGL((decode_reduce_kernel<SPW, SWIGLU>), dim3((unsigned)ceil_div(total, 256)),
-                     dim3(256), 0, s, a);
-  return hipGetLastError();
+  return launch_decode_reduce(a, SWIGLU, s);
 }
 
 template <int MT, int SPW, int RPL, bool SWIGLU>
@@ -361,8 +341,7 @@ static hipError_t launch_decode_w(const DecodeArgs &a, const DecodeConfig &c, hi
                       : launch_decode_t<MT, SPW, 4, 2, RPL, SWIGLU>(a, s);
 }
 
-hipError_t launch_decode(const Problem &p, void *workspace, hipStream_t s) {
-  const DecodeConfig c = decode_config(p);
+DecodeArgs decode_args(const Problem &p, int KS, void *workspace) {
   DecodeArgs a;
   a.A = p.A;
   a.M = (int)p.M;
@@ -376,11 +355,30 @@ hipError_t launch_decode(const Problem &p, void *workspace, hipStream_t s) {
   a.KG8 = (int)ceil_div(a.KG, 8);
   a.out = p.out;
   a.ldo = (int)(p.swiglu ? p.N / 2 : p.N);
-  a.KS = c.KS;
-  a.nsg = c.nsg;
+  a.KS = KS;
   a.up_off = (int)(p.N / 2 / kStrip);
   a.valid_strips = p.swiglu ? a.up_off : a.NS;
+  a.nsg = p.swiglu ? a.up_off : a.NS;
   a.ws = (float *)workspace;
+  return a;
+}
+
+hipError_t launch_decode_reduce(const DecodeArgs &a, bool swiglu, hipStream_t s) {
+  const int64_t total = (int64_t)a.nsg * a.M * 32;
+  if (swiglu)
+    hipLaunchKernelGGL((decode_reduce_kernel<2, true>), dim3((unsigned)ceil_div(total, 256)),
+                       dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_reduce_kernel<1, false>), dim3((unsigned)ceil_div(total, 256)),
+                       dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const Problem &p, void *workspace, hipStream_t s) {
+  int WC, WK, KS;
+  if (coop_config(p, WC, WK, KS)) return launch_decode_coop(p, workspace, WC, WK, KS, s);
+  const DecodeConfig c = decode_config(p);
+  DecodeArgs a = decode_args(p, c.KS, workspace);
   if (c.KS > 1 && workspace == nullptr) return hipErrorInvalidValue;
   if (c.MT == 16 && p.M == 1)
     return p.swiglu ? launch_decode_w<16, 2, 1, true>(a, c, s)

@@ -1,0 +1,391 @@
+// Decode path, cooperative form: activations and scales staged once per
+// workgroup in LDS and shared by waves that own different columns.
+//
+// Same product as decode.hip (page "GPU Kernels for INT4 Inference, in
+// depth", section "The job, stated precisely"; scale after each group's
+// accumulation as in FuTransformer, arXiv 2610.23796, section 3.3.4).  The
+// difference is where the activation fragments and the group scales come
+// from.  In decode.hip every wave loads its own activation fragments and
+// scales from global memory, so each workgroup re-reads A once per wave and
+// the vector-memory path carries as many activation bytes as weight bytes
+// at M = 16 (twice as many at M = 32).  The Swordfish page (section
+// "Decode, counting memory-pipe slots") makes the same observation: load
+// slots, not arithmetic, are the scarce resource of a decode kernel.
+//
+// Workgroup layout: WC x WK waves.  Wave (wc, wk) owns strip group
+// cg*WC + wc (SPW strips of 32 columns: one strip, or a gate strip and its
+// up strip) and, in every round of WK consecutive groups of 128 k, the
+// group with index wk.  Per round the workgroup stages the activation rows
+// of those WK groups and the scales of its WC*SPW strips into LDS (global
+// -> registers -> LDS, double buffered, one barrier per round); weights
+// stream per wave straight into registers, D rounds ahead, and are
+// dequantized in registers into MFMA operands.  At the end the WK partial
+// tiles of each column are summed through LDS; with KS > 1 the partial
+// tiles go to the workspace and decode_reduce_kernel finishes them.
+#include <cstdio>
+#include <cstdlib>
+#include <type_traits>
+
+#include "common.h"
+#include "decode_args.h"
+
+namespace w4a16 {
+
+template <int MT, int SPW>
+struct CoopFrag {
+  uint4_t b[SPW][2];  // weight vectors of the wave's strips for one group
+};
+
+template <int MT, int SPW, int WC, int WK, int RPL, bool SWIGLU>
+__global__ __launch_bounds__(WC * WK * 64) void decode_coop_kernel(DecodeArgs p) {
+  constexpr int NW = WC * WK, NT = NW * 64, D = 2;
+  constexpr int SH = SWIGLU ? SPW / 2 : SPW;
+  constexpr int NPART = MT == 16 ? 2 : 1;
+  typedef typename std::conditional<MT == 16, float4_t, float16_t>::type acc_t;
+  typedef CoopFrag<MT, SPW> Frag;
+  static_assert(MT == 16 ? (RPL >= 1 && RPL <= 4) : RPL == 16, "rows per lane");
+
+  extern __shared__ uint4_t smem[];
+  const int M = p.M;
+  const int ars = WK * 256 + 16;               // bytes per staged activation row
+  const int abuf = M * ars;                    // bytes per activation buffer
+  const int sbuf = WC * SPW * 32 * WK * 2;     // bytes per scale buffer
+  char *lds = (char *)smem;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wc = wave % WC, wk = wave / WC;
+  const int ncg = (p.nsg + WC - 1) / WC;
+  const int cg = blockIdx.x % ncg, split = blockIdx.x / ncg;
+  const int sg_raw = cg * WC + wc;
+  const bool active = sg_raw < p.nsg;          // inactive waves mirror the last group
+  const int sg = active ? sg_raw : p.nsg - 1;
+  const Dequant dq;
+
+  const char *wbase[SPW];
+#pragma unroll
+  for (int s = 0; s < SPW; ++s) {
+    const int base = sg * SH + (s % SH);
+    const int strip = SWIGLU && s >= SH ? base + p.up_off : base;
+    wbase[s] = (const char *)(p.rw + (int64_t)strip * p.KT * 64);
+  }
+
+  const int gb = (int)((int64_t)p.KG * split / p.KS);
+  const int ge = (int)((int64_t)p.KG * (split + 1) / p.KS);
+  const int R = (ge - gb + WK - 1) / WK;      // rounds
+
+  const int g4 = lane >> 4, c16 = lane & 15;
+  const int h = lane >> 5, c32 = lane & 31;
+  const int mrow = MT == 16 ? c16 : c32;
+  const uint32_t wlane = MT == 16 ? (uint32_t)(((g4 >> 1) * 64 + (g4 & 1) * 32 + c16) * 16)
+                                  : (uint32_t)(lane * 16);
+  // LDS byte offset of this lane's activation fragment (row min(mrow, M-1)).
+  const int a_lane = (mrow < M ? mrow : M - 1) * ars + wk * 256 + (MT == 16 ? g4 * 64 : h * 64);
+
+  // ---- cooperative staging of round r into registers, then into LDS ------
+  // Activations: M rows x WK groups = M * WK * 16 vectors of 16 bytes.
+  // Scales: WC*SPW strips x 32 columns x WK groups, 2 bytes each.
+  constexpr int AROWS = RPL == 1 ? 1 : MT;     // activation rows staged (M <= AROWS)
+  constexpr int AV_MAX = (AROWS * WK * 16 + NT - 1) / NT;
+  constexpr int SC_N = (WC * SPW * 32 * WK + NT - 1) / NT;
+  uint4_t av[AV_MAX];
+  uint16_t scv[SC_N];
+  const int nav = M * WK * 16;
+  // Loads are unconditional (indices clamped into range) so that no register
+  // is conditionally rewritten while weight loads are still in flight;
+  // staged groups past the end of the K range are never consumed.
+  auto stage_load = [&](int r) {
+    const int g0 = gb + r * WK;
+#pragma unroll
+    for (int t = 0; t < AV_MAX; ++t) {
+      int e = tid + t * NT;
+      e = e < nav ? e : nav - 1;
+      const int row = e / (WK * 16), c = e - row * (WK * 16);
+      int gg = g0 + c / 16;
+      gg = gg < ge ? gg : ge - 1;
+      av[t] = *(const uint4_t *)((const char *)p.A +
+                                 ((int64_t)row * p.K + (int64_t)gg * 128) * 2 + (c & 15) * 16);
+    }
+#pragma unroll
+    for (int t = 0; t < SC_N; ++t) {
+      int e = tid + t * NT;
+      e = e < WC * SPW * 32 * WK ? e : WC * SPW * 32 * WK - 1;
+      const int wkk = e % WK, c = (e / WK) & 31, sl = e / (WK * 32);
+      const int wcc = sl / SPW, s = sl % SPW;
+      int sgg = cg * WC + wcc;
+      sgg = sgg < p.nsg ? sgg : p.nsg - 1;
+      const int base = sgg * SH + (s % SH);
+      const int strip = SWIGLU && s >= SH ? base + p.up_off : base;
+      int gg = g0 + wkk;
+      gg = gg < ge ? gg : ge - 1;
+      scv[t] = p.rs[(((int64_t)strip * p.KG8 + (gg >> 3)) * 32 + c) * 8 + (gg & 7)];
+    }
+  };
+  // Stores are unconditional too: threads past the end repeat the last
+  // element, writing the same value to the same place.  (A conditional store
+  // lets the compiler sink the global load next to it, where waiting for it
+  // also waits for the weight loads issued in between.)
+  auto stage_store = [&](int buf) {
+    char *ab = lds + buf * abuf;
+#pragma unroll
+    for (int t = 0; t < AV_MAX; ++t) {
+      int e = tid + t * NT;
+      e = e < nav ? e : nav - 1;
+      const int row = e / (WK * 16), c = e - row * (WK * 16);
+      *(uint4_t *)(ab + row * ars + c * 16) = av[t];
+    }
+    uint16_t *sb = (uint16_t *)(lds + 2 * abuf + buf * sbuf);
+#pragma unroll
+    for (int t = 0; t < SC_N; ++t) {
+      int e = tid + t * NT;
+      e = e < WC * SPW * 32 * WK ? e : WC * SPW * 32 * WK - 1;
+      sb[e] = scv[t];
+    }
+  };
+
+  // ---- per-wave weight stream --------------------------------------------
+  // The wave's group in round r is gb + r*WK + wk; past the end of the K
+  // range it re-reads the last group (never consumed).
+  auto group_of = [&](int r) {
+    const int g = gb + r * WK + wk;
+    return g < ge ? g : ge - 1;
+  };
+  auto wload = [&](Frag &f, int r) {
+    const uint32_t ow = (uint32_t)group_of(r) * 2048u + wlane;
+#pragma unroll
+    for (int s = 0; s < SPW; ++s) {
+      const char *wp = wbase[s] + ow;
+      if constexpr (MT == 16) {
+#pragma unroll
+        for (int part = 0; part < 2; ++part) f.b[s][part] = load_nt((const uint4_t *)(wp + part * 256));
+      } else {
+#pragma unroll
+        for (int x = 0; x < 2; ++x) f.b[s][x] = load_nt((const uint4_t *)(wp + x * 1024));
+      }
+    }
+  };
+
+  acc_t acc[SPW][NPART];
+#pragma unroll
+  for (int s = 0; s < SPW; ++s)
+#pragma unroll
+    for (int part = 0; part < NPART; ++part) acc[s][part] = acc_t{};
+
+  auto compute = [&](const Frag &f, int buf) {
+    const char *ab = lds + buf * abuf + a_lane;
+    const uint16_t *sb = (const uint16_t *)(lds + 2 * abuf + buf * sbuf);
+    uint4_t a[MT == 16 ? 4 : 8];
+    if constexpr (MT == 16) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a[j] = *(const uint4_t *)(ab + j * 16);
+    } else {
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) a[4 * x + j] = *(const uint4_t *)(ab + x * 128 + j * 16);
+    }
+#pragma unroll
+    for (int s = 0; s < SPW; ++s) {
+#pragma unroll
+      for (int part = 0; part < NPART; ++part) {
+        acc_t t = acc_t{};
+        if constexpr (MT == 16) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            t = __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<half8_t>(a[j]), dq(f.b[s][part][j]),
+                                                       t, 0, 0, 0);
+        } else {
+#pragma unroll
+          for (int x = 0; x < 2; ++x)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              t = __builtin_amdgcn_mfma_f32_32x32x16_f16(bitcast<half8_t>(a[4 * x + j]),
+                                                         dq(f.b[s][x][j]), t, 0, 0, 0);
+        }
+        const int col = MT == 16 ? 16 * part + c16 : c32;
+        const float sc = (float)bitcast<_Float16>(sb[((wc * SPW + s) * 32 + col) * WK + wk]);
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) acc[s][part][r] += t[r] * sc;
+      }
+    }
+  };
+
+  // ---- main loop: rounds r, two per iteration (buffers 0 and 1) ----------
+  Frag f0, f1;
+  stage_load(0);
+  wload(f0, 0);
+  wload(f1, 1);
+  stage_store(0);
+  __syncthreads();
+  int r = 0;
+  // Steady state: rounds r, r+1 are loaded; rounds r+2, r+3 exist.
+  for (; r + 4 <= R; r += 2) {
+    stage_load(r + 1);
+    compute(f0, 0);
+    wload(f0, r + 2);
+    stage_store(1);
+    __syncthreads();
+    stage_load(r + 2);
+    compute(f1, 1);
+    wload(f1, r + 3);
+    stage_store(0);
+    __syncthreads();
+  }
+  // Tail: at most three rounds left (r .. R-1).
+  for (int q = 0; q < 3; ++q) {
+    if (r + q >= R) break;
+    const int buf = q & 1;
+    const bool more = r + q + 1 < R;
+    if (more) stage_load(r + q + 1);
+    const bool mine = gb + (r + q) * WK + wk < ge;
+    if (q == 1) {
+      if (mine) compute(f1, buf);
+    } else {
+      if (mine) compute(f0, buf);
+      if (q == 0 && r + 2 < R) wload(f0, r + 2);
+    }
+    if (more) stage_store(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- cross-wave sum over wk, then epilogue or partial tile -------------
+  float *red = (float *)lds;  // [WK][WC][SPW][M][32]; the staging buffers are free now
+  const int tileE = SPW * M * 32;
+#pragma unroll
+  for (int s = 0; s < SPW; ++s) {
+#pragma unroll
+    for (int part = 0; part < NPART; ++part) {
+#pragma unroll
+      for (int rr = 0; rr < (MT == 16 ? 4 : 16); ++rr) {
+        const int m = MT == 16 ? 4 * g4 + rr : 8 * (rr >> 2) + 4 * h + (rr & 3);
+        const int col = MT == 16 ? 16 * part + c16 : c32;
+        if (m < M) red[((wk * WC + wc) * SPW + s) * M * 32 + m * 32 + col] = acc[s][part][rr];
+      }
+    }
+  }
+  __syncthreads();
+  auto sum_wk = [&](int wcc, int e) {
+    float v = 0.0f;
+#pragma unroll
+    for (int k = 0; k < WK; ++k) v += red[(k * WC + wcc) * tileE + e];
+    return v;
+  };
+  if (p.KS == 1) {
+    const int E = SH * M * 32;
+    for (int x = tid; x < WC * E; x += NT) {
+      const int wcc = x / E, e = x - wcc * E;
+      const int sgg = cg * WC + wcc;
+      if (sgg < p.nsg)
+        decode_epilogue<SPW, SWIGLU>(p, sgg, e, [&](int y) { return sum_wk(wcc, y); });
+    }
+    return;
+  }
+  for (int x = tid; x < WC * tileE; x += NT) {
+    const int wcc = x / tileE, e = x - wcc * tileE;
+    const int sgg = cg * WC + wcc;
+    if (sgg < p.nsg) p.ws[((int64_t)sgg * p.KS + split) * tileE + e] = sum_wk(wcc, e);
+  }
+  (void)active;
+}
+
+// ---------------------------------------------------------------------------
+// Host side.
+
+size_t coop_lds_bytes(int M, int WC, int WK, int SPW) {
+  const size_t stage = 2 * (size_t)M * (WK * 256 + 16) + 2 * (size_t)WC * SPW * 32 * WK * 2;
+  const size_t red = (size_t)WK * WC * SPW * M * 32 * 4;
+  return stage > red ? stage : red;
+}
+
+template <int MT, int SPW, int WC, int WK, int RPL, bool SWIGLU>
+static hipError_t launch_coop_t(const DecodeArgs &a, hipStream_t s) {
+  const size_t lds = coop_lds_bytes(a.M, WC, WK, SPW);
+  const int ncg = (a.nsg + WC - 1) / WC;
+  hipLaunchKernelGGL((decode_coop_kernel<MT, SPW, WC, WK, RPL, SWIGLU>), dim3(ncg * a.KS),
+                     dim3(WC * WK * 64), lds, s, a);
+  return hipGetLastError();
+}
+
+template <int MT, int SPW, int RPL, bool SWIGLU>
+static hipError_t launch_coop_w(const DecodeArgs &a, int WC, int WK, hipStream_t s) {
+  if (WC == 4 && WK == 1) return launch_coop_t<MT, SPW, 4, 1, RPL, SWIGLU>(a, s);
+  if (WC == 8 && WK == 1) return launch_coop_t<MT, SPW, 8, 1, RPL, SWIGLU>(a, s);
+  if (WC == 2 && WK == 2) return launch_coop_t<MT, SPW, 2, 2, RPL, SWIGLU>(a, s);
+  if (WC == 4 && WK == 2) return launch_coop_t<MT, SPW, 4, 2, RPL, SWIGLU>(a, s);
+  if (WC == 2 && WK == 4) return launch_coop_t<MT, SPW, 2, 4, RPL, SWIGLU>(a, s);
+  return launch_coop_t<MT, SPW, 1, 4, RPL, SWIGLU>(a, s);
+}
+
+// -1 if unset, else the integer value.
+static int coop_env_raw(const char *name) {
+  const char *v = std::getenv(name);
+  if (v == nullptr || *v == 0) return -1;
+  return std::atoi(v);
+}
+
+static int coop_env(const char *name, int fallback) {
+  const char *v = std::getenv(name);
+  if (v == nullptr || *v == 0) return fallback;
+  const int x = std::atoi(v);
+  return x > 0 ? x : fallback;
+}
+
+// Where the cooperative kernel wins (measured on MI355X): wide shapes, whose
+// strip groups alone fill the GPU (fused gate/up), and K-heavy shapes at
+// M >= 8, where the activation rows are the larger share of load slots.
+// Narrow, short-K shapes keep the per-wave kernel.  W4A16_DECODE_COOP=0/1
+// forces the choice; W4A16_COOP_WC / _WK / _KS override the configuration.
+bool coop_config(const Problem &p, int &WC, int &WK, int &KS) {
+  const int nsg = (int)(p.swiglu ? (p.N / 2 / kStrip) : ceil_div(p.N, kStrip));
+  const int KG = (int)(p.K / kGroup);
+  const int force = coop_env_raw("W4A16_DECODE_COOP");
+  bool use;
+  if (nsg >= 384) {
+    use = true;
+    if (p.M == 1) { WC = 1; WK = 4; KS = 1; }
+    else if (p.M <= 16) { WC = 2; WK = 4; KS = 1; }
+    else { WC = 2; WK = 2; KS = 1; }
+  } else if (KG >= 192 && p.M >= 8) {
+    use = true;
+    WC = 2; WK = p.M <= 16 ? 4 : 2; KS = 2;
+  } else {
+    use = false;
+    WC = 2; WK = 4; KS = 1;
+  }
+  if (force == 0) return false;
+  if (force == 1) use = true;
+  if (!use) return false;
+  WC = coop_env("W4A16_COOP_WC", WC);
+  WK = coop_env("W4A16_COOP_WK", WK);
+  KS = coop_env("W4A16_COOP_KS", KS);
+  const int SPW = p.swiglu ? 2 : 1;
+  static const int allowed[6][2] = {{4, 1}, {8, 1}, {2, 2}, {4, 2}, {2, 4}, {1, 4}};
+  bool ok = false;
+  for (auto &c : allowed) ok |= (c[0] == WC && c[1] == WK);
+  if (!ok) return false;
+  if (KS > KG) KS = KG;
+  if (KS < 1) KS = 1;
+  if (coop_lds_bytes((int)p.M, WC, WK, SPW) >= 65536) return false;
+  return true;
+}
+
+hipError_t launch_decode_coop(const Problem &p, void *workspace, int WC, int WK, int KS,
+                              hipStream_t s) {
+  DecodeArgs a = decode_args(p, KS, workspace);
+  if (KS > 1 && workspace == nullptr) return hipErrorInvalidValue;
+  hipError_t e;
+  const bool m1 = p.M == 1, mt16 = p.M <= 16;
+  if (mt16 && m1)
+    e = p.swiglu ? launch_coop_w<16, 2, 1, true>(a, WC, WK, s)
+                 : launch_coop_w<16, 1, 1, false>(a, WC, WK, s);
+  else if (mt16)
+    e = p.swiglu ? launch_coop_w<16, 2, 4, true>(a, WC, WK, s)
+                 : launch_coop_w<16, 1, 4, false>(a, WC, WK, s);
+  else
+    e = p.swiglu ? launch_coop_w<32, 2, 16, true>(a, WC, WK, s)
+                 : launch_coop_w<32, 1, 16, false>(a, WC, WK, s);
+  if (e != hipSuccess || KS == 1) return e;
+  return launch_decode_reduce(a, p.swiglu, s);
+}
+
+}  // namespace w4a16
