@@ -104,7 +104,9 @@ def test_dispatch_table():
 def test_describe_names_the_launches():
     """The launch description names kernel instances as profilers print them."""
     d = w4a16.describe(1, 4096, 28672, swiglu=True)
-    assert d.startswith("decode_kernel<16, 2, ") and d.split(">")[0].endswith("true")
+    assert d.startswith("decode_coop_kernel<16, 2, ") and d.split(">")[0].endswith("true")
+    d = w4a16.describe(1, 4096, 4096)
+    assert d.startswith("decode_kernel<16, 1, ") and d.split(">")[0].endswith("false")
     assert "prefill_kernel<8, 2, false, true>" in w4a16.describe(4096, 4096, 28672, swiglu=True)
     assert w4a16.describe(4096, 4096, 4096, path="dense").startswith("dequant_kernel<false>; ")
     assert "row slices" in w4a16.describe(100, 4096, 4096, path="decode")
