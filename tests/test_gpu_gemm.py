@@ -172,3 +172,13 @@ def test_decode_cooperative_bit_exact_integer_inputs(monkeypatch):
         packed_o, s16_o = orc().quantize_pack(W)
         C = orc().gemm_f64(A, packed_o, s16_o)
         assert np.array_equal(out.astype(np.float64), C)
+
+
+@pytest.mark.parametrize("path", ["prefill", "dense"])
+@pytest.mark.parametrize("M,K,N,swiglu", [(257, 1152, 1088, False), (300, 1024, 2112, True),
+                                          (600, 2048, 4160, False), (513, 1024, 4096, True)])
+def test_prefill_two_waves_per_simd(monkeypatch, path, M, K, N, swiglu):
+    """The 8-wave prefill mainloop (two waves per SIMD) on ragged shapes:
+    partial row tiles, a tail strip, an odd number of gate strips."""
+    monkeypatch.setenv("W4A16_PREFILL_V2", "1")
+    gemm_case(M, K, N, swiglu=swiglu, path=path, seed=M + N)

@@ -32,6 +32,7 @@
 //     groups of 4 row tiles so that concurrently running tiles share weight
 //     columns and activation rows in that XCD's L2.
 #include <cstdio>
+#include <cstdlib>
 
 #include "common.h"
 
@@ -227,6 +228,205 @@ void prefill_kernel(PrefillArgs p) {
 }
 
 // ---------------------------------------------------------------------------
+// Second mainloop: WM x WNW waves, two waves per SIMD.  Each wave owns
+// 32*MI rows and two strips (64 columns; for SwiGLU a gate strip and its up
+// strip); the workgroup tile is (32*MI*WM) x (64*WNW).  With two waves on
+// each SIMD the hardware overlaps one wave's MFMAs with the other's LDS
+// reads and dequantization, which a single wave per SIMD cannot do across
+// its own dependency chains.
+template <int MI, int WM, int WNW, int TPS, bool DENSE, bool SWIGLU>
+__global__ __launch_bounds__(64 * WM * WNW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill2_kernel(PrefillArgs p) {
+  // TPS: 64-k tiles per pipeline step (2 = one whole 128-k scale group).
+  constexpr int BM = 32 * MI * WM;
+  constexpr int NT = 64 * WM * WNW;
+  constexpr int GM = 4;  // row tiles per group in the tile walk
+  constexpr int CH = 8 * TPS;  // 16-byte chunks per staged activation row
+  constexpr int AV = BM * CH / NT;
+  static_assert(BM * CH % NT == 0, "activation tile split");
+  __shared__ uint4_t lds[2][BM * CH];
+  struct BRegs {
+    uint4_t v[2][TPS][DENSE ? 4 : 1];
+    uint16_t sc[2];
+  };
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WNW, wn = wave % WNW;
+  const int h = lane >> 5, c = lane & 31;
+  const int M = p.M;
+  const Dequant dq;
+
+  // XCD-aware tile walk (as in prefill_kernel).
+  const int T = p.tiles_m * p.tiles_n;
+  const int b = blockIdx.x;
+  const int xcd = b & 7, local = b >> 3;
+  const int per = T >> 3, extra = T & 7;
+  const int tau = xcd * per + (xcd < extra ? xcd : extra) + local;
+  const int group = tau / (GM * p.tiles_n);
+  const int first_m = group * GM;
+  const int gsize = p.tiles_m - first_m < GM ? p.tiles_m - first_m : GM;
+  const int in_group = tau - group * GM * p.tiles_n;
+  const int tm = first_m + in_group % gsize;
+  const int tn = in_group / gsize;
+  const int m0 = tm * BM;
+
+  int strip[2];
+  bool sval[2];
+  if constexpr (SWIGLU) {
+    const int base = tn * WNW + wn;
+    strip[0] = base;
+    strip[1] = base + p.up_off;
+    sval[0] = sval[1] = base < p.valid_strips;
+  } else {
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      strip[w] = (tn * WNW + wn) * 2 + w;
+      sval[w] = strip[w] < p.NS;
+    }
+  }
+
+  // LDS swizzle: 16 consecutive rows read at one k land in 16 distinct
+  // 16-byte bank groups (the 64 banks x 4 bytes), so the 16 lanes that an
+  // ds_read_b128 serves together never collide.  Rows are CH*16 bytes long.
+  auto swz = [](int row) {
+    return CH == 16 ? (row & 15) : ((row >> 1) & 7);
+  };
+  // Activation staging: thread tid moves chunk (tid % CH) of rows tid / CH + (NT/CH) i.
+  const int arow = tid / CH, achunk = tid % CH;
+  const uint4_t *Ag = (const uint4_t *)p.A;
+  uint4_t areg[AV];
+  auto load_a = [&](int q) {
+#pragma unroll
+    for (int i = 0; i < AV; ++i) {
+      int row = m0 + arow + (NT / CH) * i;
+      row = row < M ? row : M - 1;  // rows past M are computed and never stored
+      areg[i] = Ag[((int64_t)row * p.K + 64 * TPS * q) / 8 + achunk];
+    }
+  };
+  auto store_a = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < AV; ++i) {
+      const int row = arow + (NT / CH) * i;
+      lds[buf][row * CH + (achunk ^ swz(row))] = areg[i];
+    }
+  };
+  auto load_b = [&](int q, BRegs &r) {
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const int st = sval[w] ? strip[w] : 0;   // invalid strips read strip 0, never stored
+#pragma unroll
+      for (int t = 0; t < TPS; ++t) {
+        const int64_t vec = ((int64_t)st * p.KT + TPS * q + t) * 64 + lane;
+        if constexpr (DENSE) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) r.v[w][t][j] = load_nt(p.rw + vec * 4 + j);
+        } else {
+          r.v[w][t][0] = load_nt(p.rw + vec);
+        }
+      }
+      if constexpr (!DENSE) {
+        const int g = (TPS * q) >> 1;
+        r.sc[w] = p.rs[(((int64_t)st * p.KG8 + (g >> 3)) * 32 + c) * 8 + (g & 7)];
+      }
+    }
+  };
+
+  float16_t acc[2][MI];
+#pragma unroll
+  for (int w = 0; w < 2; ++w)
+#pragma unroll
+    for (int i = 0; i < MI; ++i) acc[w][i] = float16_t{};
+
+  const int rbase = wm * 32 * MI;
+  auto compute = [&](int buf, const BRegs &r) {
+    half2_t s2[2];
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const _Float16 sh = bitcast<_Float16>(r.sc[w]);
+      s2[w] = half2_t{sh, sh};
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4 * TPS; ++jj) {
+      const int t = jj >> 2, j = jj & 3;
+      half8_t bf[2];
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        if constexpr (DENSE)
+          bf[w] = bitcast<half8_t>(r.v[w][t][j]);
+        else
+          bf[w] = dq.scaled(r.v[w][t][0][j], s2[w]);
+      }
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        const int row = rbase + 32 * i + c;
+        const half8_t af =
+            bitcast<half8_t>(lds[buf][row * CH + ((8 * t + 4 * h + j) ^ swz(row))]);
+#pragma unroll
+        for (int w = 0; w < 2; ++w)
+          acc[w][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[w], af, acc[w][i], 0, 0, 0);
+      }
+    }
+  };
+
+  BRegs bcur, bnext;
+  load_a(0);
+  load_b(0, bcur);
+  store_a(0);
+  __syncthreads();
+  const int nsteps = p.KT / TPS;
+  for (int q = 0; q < nsteps; ++q) {
+    const bool more = q + 1 < nsteps;
+    if (more) {
+      load_a(q + 1);
+      load_b(q + 1, bnext);
+    }
+    compute(q & 1, bcur);
+    if (more) store_a((q + 1) & 1);
+    __syncthreads();
+    bcur = bnext;
+  }
+
+  // Epilogue: acc[w][i][4*rg + e] is the output at row m0 + rbase + 32 i + c
+  // and column 32 strip[w] + 8 rg + 4 h + e.
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    const int m = m0 + rbase + 32 * i + c;
+    if (m >= M) continue;
+    uint16_t *orow = p.out + (int64_t)m * p.ldo;
+    if constexpr (SWIGLU) {
+      if (!sval[0]) continue;
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        half2_t lo, hi;
+        lo.x = (_Float16)silu_mul(acc[0][i][4 * rg + 0], acc[1][i][4 * rg + 0]);
+        lo.y = (_Float16)silu_mul(acc[0][i][4 * rg + 1], acc[1][i][4 * rg + 1]);
+        hi.x = (_Float16)silu_mul(acc[0][i][4 * rg + 2], acc[1][i][4 * rg + 2]);
+        hi.y = (_Float16)silu_mul(acc[0][i][4 * rg + 3], acc[1][i][4 * rg + 3]);
+        const int n = strip[0] * 32 + 8 * rg + 4 * h;
+        *(uint2 *)(orow + n) = uint2{bitcast<uint32_t>(lo), bitcast<uint32_t>(hi)};
+      }
+    } else {
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        if (!sval[w]) continue;
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int n = strip[w] * 32 + 8 * rg + 4 * h;
+          if (n >= p.N) continue;
+          half2_t lo, hi;
+          lo.x = (_Float16)acc[w][i][4 * rg + 0];
+          lo.y = (_Float16)acc[w][i][4 * rg + 1];
+          hi.x = (_Float16)acc[w][i][4 * rg + 2];
+          hi.y = (_Float16)acc[w][i][4 * rg + 3];
+          *(uint2 *)(orow + n) = uint2{bitcast<uint32_t>(lo), bitcast<uint32_t>(hi)};
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host side.
 
 static PrefillArgs prefill_args(const Problem &p, int BM, const void *weights) {
@@ -269,7 +469,36 @@ static hipError_t launch_tiled(const Problem &p, const void *weights, hipStream_
   return p.swiglu ? launch_prefill_t<2, DENSE, true>(a, s) : launch_prefill_t<2, DENSE, false>(a, s);
 }
 
-hipError_t launch_prefill(const Problem &p, hipStream_t s) { return launch_tiled<false>(p, p.rw, s); }
+template <int MI, int WM, int WNW, int TPS, bool DENSE, bool SWIGLU>
+static hipError_t launch_prefill2_t(const Problem &p, const void *weights, hipStream_t s) {
+  PrefillArgs a = prefill_args(p, 32 * MI * WM, weights);
+  a.tiles_n = (int)(p.swiglu ? ceil_div(a.up_off, WNW) : ceil_div(a.NS, 2 * WNW));
+  hipLaunchKernelGGL((prefill2_kernel<MI, WM, WNW, TPS, DENSE, SWIGLU>), dim3(a.tiles_m * a.tiles_n),
+                     dim3(64 * WM * WNW), 0, s, a);
+  return hipGetLastError();
+}
+
+template <bool DENSE>
+static hipError_t launch_tiled2(const Problem &p, const void *weights, hipStream_t s) {
+  const char *v = std::getenv("W4A16_PREFILL_TPS");
+  if constexpr (!DENSE) {
+    if (v != nullptr && *v == '2')
+      return p.swiglu ? launch_prefill2_t<4, 2, 4, 2, DENSE, true>(p, weights, s)
+                      : launch_prefill2_t<4, 2, 4, 2, DENSE, false>(p, weights, s);
+  }
+  return p.swiglu ? launch_prefill2_t<4, 2, 4, 1, DENSE, true>(p, weights, s)
+                  : launch_prefill2_t<4, 2, 4, 1, DENSE, false>(p, weights, s);
+}
+
+static bool prefill_v2() {
+  const char *v = std::getenv("W4A16_PREFILL_V2");
+  return v != nullptr && *v == '1';
+}
+
+hipError_t launch_prefill(const Problem &p, hipStream_t s) {
+  if (prefill_v2() && p.M > 256) return launch_tiled2<false>(p, p.rw, s);
+  return launch_tiled<false>(p, p.rw, s);
+}
 
 int tiled_describe(const Problem &p, bool dense, char *buf, size_t n) {
   const int MI = p.M > 128 ? 8 : (p.M > 64 ? 4 : 2);
@@ -289,6 +518,7 @@ hipError_t launch_dense(const Problem &p, void *workspace, hipStream_t s) {
   void *w16f = workspace;
   hipError_t e = launch_dequant_fragment(p.rw, p.rs, p.K, p.N, (uint16_t *)w16f, s);
   if (e != hipSuccess) return e;
+  if (prefill_v2() && p.M > 256) return launch_tiled2<true>(p, w16f, s);
   return launch_tiled<true>(p, w16f, s);
 }
 
