@@ -182,3 +182,49 @@ def test_prefill_two_waves_per_simd(monkeypatch, path, M, K, N, swiglu):
     partial row tiles, a tail strip, an odd number of gate strips."""
     monkeypatch.setenv("W4A16_PREFILL_V2", "1")
     gemm_case(M, K, N, swiglu=swiglu, path=path, seed=M + N)
+
+
+PREFILL2_CONFIGS = [(64, 1, 1), (128, 1, 4), (256, 1, 2), (64, 2, 2), (128, 2, 4), (256, 2, 1),
+                    (64, 1, 8)]
+
+
+@pytest.mark.parametrize("bm,tps,ks", PREFILL2_CONFIGS)
+@pytest.mark.parametrize("M,K,N,swiglu", [(70, 2048, 1088, False), (200, 2048, 2112, True),
+                                          (129, 4096, 4160, False)])
+def test_prefill2_tiles_and_k_slices(monkeypatch, bm, tps, ks, M, K, N, swiglu):
+    """The 8-wave mainloop at each row tile (64/128/256), one or two 64-k tiles
+    per pipeline step, and split K with the FP32 partial reduction; ragged M
+    and N, odd step counts per slice where the split allows."""
+    monkeypatch.setenv("W4A16_PREFILL_BM", str(bm))
+    monkeypatch.setenv("W4A16_PREFILL_TPS", str(tps))
+    monkeypatch.setenv("W4A16_PREFILL_KS", str(ks))
+    d = w4a16.describe(M, K, N, swiglu=swiglu, path="prefill")
+    assert "prefill2_kernel<%d, 2, 4, %d" % (bm // 64, tps) in d, d
+    assert ("ks=%d" % ks) in d, d
+    gemm_case(M, K, N, swiglu=swiglu, path="prefill", seed=M + N + bm + ks)
+
+
+def test_prefill2_split_k_bit_exact_integer_inputs(monkeypatch):
+    """Split K sums FP32 partials in slice order; with small-integer inputs
+    every partial and sum is exact, so the output is bit-exact."""
+    monkeypatch.setenv("W4A16_PREFILL_BM", "64")
+    monkeypatch.setenv("W4A16_PREFILL_KS", "4")
+    for M, K, N in [(96, 2048, 2048), (80, 4096, 1024)]:
+        W = synth.grid_weights(K, N, p=4, seed=M)
+        A = synth.ternary_activations(M, K, density=1.0, seed=M)
+        w = w4a16.load_weight(W)
+        assert "ks=4" in w4a16.describe(M, K, N, path="prefill")
+        out = fp16_out(w4a16.gemm(to_dev(A), w, path="prefill"))
+        packed_o, s16_o = orc().quantize_pack(W)
+        C = orc().gemm_f64(A, packed_o, s16_o)
+        assert np.array_equal(out.astype(np.float64), C)
+
+
+@pytest.mark.parametrize("M,K,N,swiglu", [(40, 1024, 1088, False), (130, 1152, 2112, True),
+                                          (300, 2048, 4096, False)])
+def test_prefill_one_wave_kernel(monkeypatch, M, K, N, swiglu):
+    """The one-wave-per-SIMD mainloop, which the fused path falls back to
+    when an operand exceeds 32-bit buffer offsets (forced here)."""
+    monkeypatch.setenv("W4A16_PREFILL_V2", "0")
+    assert w4a16.describe(M, K, N, swiglu=swiglu, path="prefill").startswith("prefill_kernel<")
+    gemm_case(M, K, N, swiglu=swiglu, path="prefill", seed=M + K)

@@ -116,6 +116,7 @@ int select_path(int64_t M, int64_t K, int64_t N) {
 
 int64_t workspace_for(int path, const Problem &p) {
   if (path == W4A16_PATH_DENSE) return dense_workspace_bytes(p);
+  if (path == W4A16_PATH_PREFILL) return prefill_workspace_bytes(p);
   if (path == W4A16_PATH_DECODE) {
     Problem q = p;
     q.M = p.M < kDecodeMaxM ? p.M : kDecodeMaxM;
@@ -169,7 +170,7 @@ int run_gemm(const uint16_t *A, int64_t M, int64_t K, const void *rw, const void
       e = launch_decode(q, ws, stream);
     }
   } else if (path == W4A16_PATH_PREFILL) {
-    e = launch_prefill(p, stream);
+    e = launch_prefill(p, ws, stream);
   } else {
     e = launch_dense(p, ws, stream);
   }

@@ -103,6 +103,12 @@ __device__ __forceinline__ uint4_t load_nt(const uint4_t *p) {
   return __builtin_nontemporal_load(p);
 }
 
+// Buffer resource word 3 for raw (stride 0, untyped 32-bit) buffers on gfx9
+// class parts, and the cache-policy operand of a streaming (non-temporal)
+// buffer read.
+constexpr int kBufferConfig = 0x00020000;
+constexpr int kBufferNT = 2;
+
 __device__ __forceinline__ float silu_mul(float g, float u) {
   return g / (1.0f + __expf(-g)) * u;
 }
@@ -142,7 +148,8 @@ int decode_describe(const Problem &p, char *buf, size_t n);
 hipError_t launch_decode(const Problem &p, void *workspace, hipStream_t s);
 
 // Prefill path (fused dequant) and dense path (fp16 fragment-ordered weights).
-hipError_t launch_prefill(const Problem &p, hipStream_t s);
+int64_t prefill_workspace_bytes(const Problem &p);
+hipError_t launch_prefill(const Problem &p, void *workspace, hipStream_t s);
 int64_t dense_workspace_bytes(const Problem &p);
 hipError_t launch_dense(const Problem &p, void *workspace, hipStream_t s);
 int tiled_describe(const Problem &p, bool dense, char *buf, size_t n);

@@ -48,6 +48,11 @@ struct PrefillArgs {
   int ldo;
   int tiles_m, tiles_n;
   int up_off, valid_strips;
+  // prefill2_kernel split-K: KS slices of spk pipeline steps each; with
+  // KS > 1 every slice writes FP32 partials ws[KS][M][N] (gate and up columns
+  // alike) and prefill_reduce_kernel finishes the output.
+  int KS, spk;
+  float *ws;
 };
 
 template <int WN, bool DENSE>
@@ -233,36 +238,54 @@ void prefill_kernel(PrefillArgs p) {
 // strip); the workgroup tile is (32*MI*WM) x (64*WNW).  With two waves on
 // each SIMD the hardware overlaps one wave's MFMAs with the other's LDS
 // reads and dequantization, which a single wave per SIMD cannot do across
-// its own dependency chains.
+// its own dependency chains.  Two waves per SIMD leave 256 registers per
+// wave, so nothing is staged in registers that need not be: activations go
+// from memory straight into LDS (buffer loads with the LDS destination), and
+// all operands are addressed with fixed 32-bit lane offsets plus a scalar k
+// offset.  Each step issues the next step's loads, then runs its MFMAs
+// (a scheduling barrier keeps the loads first), then meets the workgroup
+// barrier, which also waits for the loads.
 template <int MI, int WM, int WNW, int TPS, bool DENSE, bool SWIGLU>
 __global__ __launch_bounds__(64 * WM * WNW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill2_kernel(PrefillArgs p) {
   // TPS: 64-k tiles per pipeline step (2 = one whole 128-k scale group).
+  // All global reads are buffer loads: a per-lane 32-bit offset fixed for the
+  // whole k loop plus a scalar offset that advances with k, so the loop does
+  // no address arithmetic and holds no 64-bit pointers.  Buffer reads past the
+  // end of a resource return zero, which also covers activation rows past M.
   constexpr int BM = 32 * MI * WM;
-  constexpr int NT = 64 * WM * WNW;
+  constexpr int NW = WM * WNW;
+  constexpr int NT = 64 * NW;
   constexpr int GM = 4;  // row tiles per group in the tile walk
   constexpr int CH = 8 * TPS;  // 16-byte chunks per staged activation row
-  constexpr int AV = BM * CH / NT;
+  constexpr int AV = BM * CH / NT;  // activation copies per lane and step
+  constexpr int NV = DENSE ? 4 : 1;  // 16-byte vectors per lane, strip and 64-k tile
   static_assert(BM * CH % NT == 0, "activation tile split");
-  __shared__ uint4_t lds[2][BM * CH];
+  static_assert((NT / CH) % 16 == 0, "swizzle period must divide the rows per copy");
+  // The two activation stages are separate arrays so that the compiler can
+  // tell the stage being filled from the stage being read.
+  __shared__ uint4_t lds0[BM * CH];
+  __shared__ uint4_t lds1[BM * CH];
   struct BRegs {
-    uint4_t v[2][TPS][DENSE ? 4 : 1];
-    uint16_t sc[2];
+    uint4_t v[2][TPS][NV];
+    uint32_t sc0, sc1;
   };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WNW, wn = wave % WNW;
   const int h = lane >> 5, c = lane & 31;
-  const int M = p.M;
   const Dequant dq;
 
-  // XCD-aware tile walk (as in prefill_kernel).
+  // XCD-aware tile walk (as in prefill_kernel) over KS slices of T tiles:
+  // each XCD takes a contiguous range of the KS * T (slice, tile) pairs.
   const int T = p.tiles_m * p.tiles_n;
   const int b = blockIdx.x;
   const int xcd = b & 7, local = b >> 3;
-  const int per = T >> 3, extra = T & 7;
-  const int tau = xcd * per + (xcd < extra ? xcd : extra) + local;
+  const int per = (T * p.KS) >> 3, extra = (T * p.KS) & 7;
+  const int tau_all = xcd * per + (xcd < extra ? xcd : extra) + local;
+  const int ks = tau_all / T;
+  const int tau = tau_all - ks * T;
   const int group = tau / (GM * p.tiles_n);
   const int first_m = group * GM;
   const int gsize = p.tiles_m - first_m < GM ? p.tiles_m - first_m : GM;
@@ -286,49 +309,62 @@ void prefill2_kernel(PrefillArgs p) {
     }
   }
 
+  // Buffer resources.  The activation resource starts at this tile's first
+  // row and ends at row M, so rows past M read as zero.
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(p.A + (int64_t)m0 * p.K), (short)0, (p.M - m0) * p.K * 2, kBufferConfig);
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)p.rw, (short)0, p.NS * p.KT * 64 * 16 * NV, kBufferConfig);
+  const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)p.rs, (short)0, p.NS * p.KG8 * 512, kBufferConfig);
+
   // LDS swizzle: 16 consecutive rows read at one k land in 16 distinct
   // 16-byte bank groups (the 64 banks x 4 bytes), so the 16 lanes that an
   // ds_read_b128 serves together never collide.  Rows are CH*16 bytes long.
   auto swz = [](int row) {
     return CH == 16 ? (row & 15) : ((row >> 1) & 7);
   };
-  // Activation staging: thread tid moves chunk (tid % CH) of rows tid / CH + (NT/CH) i.
-  const int arow = tid / CH, achunk = tid % CH;
-  const uint4_t *Ag = (const uint4_t *)p.A;
-  uint4_t areg[AV];
-  auto load_a = [&](int q) {
+  // Activation staging goes straight from memory into LDS: copy i of wave
+  // `wave` fills the 64 consecutive 16-byte LDS slots starting at slot
+  // (i * NW + wave) * 64, one per lane.  Slot s holds row s / CH, physical
+  // chunk s % CH, which is logical chunk (s % CH) ^ swz(row); the rows a lane
+  // fills advance by NT / CH per copy, a multiple of the swizzle period, so
+  // the lane's logical chunk is the same for every copy.
+  const int slot0 = wave * 64 + lane;
+  const int arow0 = slot0 / CH;
+  const int a_off = (arow0 * p.K + ((slot0 % CH) ^ swz(arow0)) * 8) * 2;
+  const int a_rows = (NT / CH) * p.K * 2;  // bytes between successive copies
+  typedef __attribute__((address_space(3))) void *lds_ptr;
+  auto load_a = [&](int q, uint4_t *stage) {
+    const int k_off = 128 * TPS * q;
 #pragma unroll
-    for (int i = 0; i < AV; ++i) {
-      int row = m0 + arow + (NT / CH) * i;
-      row = row < M ? row : M - 1;  // rows past M are computed and never stored
-      areg[i] = Ag[((int64_t)row * p.K + 64 * TPS * q) / 8 + achunk];
-    }
+    for (int i = 0; i < AV; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr)(stage + (i * NW + wave) * 64), 16,
+                                               a_off, k_off + a_rows * i, 0, 0);
   };
-  auto store_a = [&](int buf) {
+  // Weights: invalid strips read strip 0 and are never stored.
+  int w_off[2], s_off[2];
 #pragma unroll
-    for (int i = 0; i < AV; ++i) {
-      const int row = arow + (NT / CH) * i;
-      lds[buf][row * CH + (achunk ^ swz(row))] = areg[i];
-    }
-  };
+  for (int w = 0; w < 2; ++w) {
+    const int st = sval[w] ? strip[w] : 0;
+    w_off[w] = (st * p.KT * 64 + lane) * 16 * NV;
+    s_off[w] = (st * p.KG8 * 32 + c) * 16;
+  }
   auto load_b = [&](int q, BRegs &r) {
 #pragma unroll
     for (int w = 0; w < 2; ++w) {
-      const int st = sval[w] ? strip[w] : 0;   // invalid strips read strip 0, never stored
 #pragma unroll
-      for (int t = 0; t < TPS; ++t) {
-        const int64_t vec = ((int64_t)st * p.KT + TPS * q + t) * 64 + lane;
-        if constexpr (DENSE) {
+      for (int t = 0; t < TPS; ++t)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) r.v[w][t][j] = load_nt(p.rw + vec * 4 + j);
-        } else {
-          r.v[w][t][0] = load_nt(p.rw + vec);
-        }
-      }
-      if constexpr (!DENSE) {
-        const int g = (TPS * q) >> 1;
-        r.sc[w] = p.rs[(((int64_t)st * p.KG8 + (g >> 3)) * 32 + c) * 8 + (g & 7)];
-      }
+        for (int j = 0; j < NV; ++j)
+          r.v[w][t][j] = bitcast<uint4_t>(__builtin_amdgcn_raw_buffer_load_b128(
+              rw, w_off[w] + 16 * j, (TPS * q + t) * 1024 * NV, kBufferNT));
+    }
+    if constexpr (!DENSE) {
+      const int g = (TPS * q) >> 1;
+      const int g_off = (g >> 3) * 512 + (g & 7) * 2;
+      r.sc0 = __builtin_amdgcn_raw_buffer_load_b16(rsc, s_off[0], g_off, 0);
+      r.sc1 = __builtin_amdgcn_raw_buffer_load_b16(rsc, s_off[1], g_off, 0);
     }
   };
 
@@ -339,12 +375,13 @@ void prefill2_kernel(PrefillArgs p) {
     for (int i = 0; i < MI; ++i) acc[w][i] = float16_t{};
 
   const int rbase = wm * 32 * MI;
-  auto compute = [&](int buf, const BRegs &r) {
+  auto compute = [&](const uint4_t *stage, const BRegs &r) {
     half2_t s2[2];
-#pragma unroll
-    for (int w = 0; w < 2; ++w) {
-      const _Float16 sh = bitcast<_Float16>(r.sc[w]);
-      s2[w] = half2_t{sh, sh};
+    {
+      const _Float16 s0 = bitcast<_Float16>((uint16_t)r.sc0);
+      const _Float16 s1 = bitcast<_Float16>((uint16_t)r.sc1);
+      s2[0] = half2_t{s0, s0};
+      s2[1] = half2_t{s1, s1};
     }
 #pragma unroll
     for (int jj = 0; jj < 4 * TPS; ++jj) {
@@ -361,7 +398,7 @@ void prefill2_kernel(PrefillArgs p) {
       for (int i = 0; i < MI; ++i) {
         const int row = rbase + 32 * i + c;
         const half8_t af =
-            bitcast<half8_t>(lds[buf][row * CH + ((8 * t + 4 * h + j) ^ swz(row))]);
+            bitcast<half8_t>(stage[row * CH + ((8 * t + 4 * h + j) ^ swz(row))]);
 #pragma unroll
         for (int w = 0; w < 2; ++w)
           acc[w][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[w], af, acc[w][i], 0, 0, 0);
@@ -369,22 +406,54 @@ void prefill2_kernel(PrefillArgs p) {
     }
   };
 
-  BRegs bcur, bnext;
-  load_a(0);
-  load_b(0, bcur);
-  store_a(0);
+  // Two register sets for the weights and two LDS stages for the activations,
+  // used in turn (the loop is unrolled by two so that nothing is copied).
+  // Every step loads the next step's operands unconditionally (the last step
+  // reloads its own k range into the idle buffers), so the loop has no
+  // conditional loads; the barrier that ends a step waits for those loads.
+  const int q0 = ks * p.spk, q1 = q0 + p.spk;
+  BRegs b0, b1;
+  load_a(q0, lds0);
+  load_b(q0, b0);
   __syncthreads();
-  const int nsteps = p.KT / TPS;
-  for (int q = 0; q < nsteps; ++q) {
-    const bool more = q + 1 < nsteps;
-    if (more) {
-      load_a(q + 1);
-      load_b(q + 1, bnext);
-    }
-    compute(q & 1, bcur);
-    if (more) store_a((q + 1) & 1);
+  auto step = [&](int q, const uint4_t *stage, const BRegs &cur, uint4_t *nstage, BRegs &next) {
+    const int qn = q + 1 < q1 ? q + 1 : q;
+    load_a(qn, nstage);
+    load_b(qn, next);
+    // Keep the loads ahead of the step's MFMAs, so that their latency is
+    // spent under the math rather than at the barrier.
+    __builtin_amdgcn_sched_barrier(0);
+    compute(stage, cur);
     __syncthreads();
-    bcur = bnext;
+  };
+  int q = q0;
+  for (; q + 1 < q1; q += 2) {
+    step(q, lds0, b0, lds1, b1);
+    step(q + 1, lds1, b1, lds0, b0);
+  }
+  if (q < q1) step(q, lds0, b0, lds1, b1);
+
+  if (p.KS > 1) {
+    // Split K: FP32 partials of this slice, columns as in the weights.
+    float *slice = p.ws + (int64_t)ks * p.M * p.N;
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      const int m = m0 + rbase + 32 * i + c;
+      if (m >= p.M) continue;
+      float *prow = slice + (int64_t)m * p.N;
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        if (!sval[w]) continue;
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int n = strip[w] * 32 + 8 * rg + 4 * h;
+          if (n >= p.N) continue;
+          *(float4_t *)(prow + n) = float4_t{acc[w][i][4 * rg + 0], acc[w][i][4 * rg + 1],
+                                             acc[w][i][4 * rg + 2], acc[w][i][4 * rg + 3]};
+        }
+      }
+    }
+    return;
   }
 
   // Epilogue: acc[w][i][4*rg + e] is the output at row m0 + rbase + 32 i + c
@@ -392,7 +461,7 @@ void prefill2_kernel(PrefillArgs p) {
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
     const int m = m0 + rbase + 32 * i + c;
-    if (m >= M) continue;
+    if (m >= p.M) continue;
     uint16_t *orow = p.out + (int64_t)m * p.ldo;
     if constexpr (SWIGLU) {
       if (!sval[0]) continue;
@@ -426,6 +495,34 @@ void prefill2_kernel(PrefillArgs p) {
   }
 }
 
+// Second stage of a split-K prefill: sums the KS FP32 partial slices in
+// slice order and applies the epilogue.  One thread per 4 consecutive
+// outputs of a row.
+template <bool SWIGLU>
+__global__ __launch_bounds__(256) void prefill_reduce_kernel(const float *ws, int KS, int M,
+                                                             int N, uint16_t *out, int ldo) {
+  const int per_row = ldo >> 2;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)M * per_row) return;
+  const int m = (int)(idx / per_row), n = (int)(idx - (int64_t)m * per_row) * 4;
+  const int64_t slice = (int64_t)M * N;
+  const float *src = ws + (int64_t)m * N + n;
+  float4_t g = {0.0f, 0.0f, 0.0f, 0.0f}, u = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int k = 0; k < KS; ++k) {
+    g += *(const float4_t *)(src + k * slice);
+    if constexpr (SWIGLU) u += *(const float4_t *)(src + k * slice + N / 2);
+  }
+  half2_t lo, hi;
+  if constexpr (SWIGLU) {
+    lo = half2_t{(_Float16)silu_mul(g[0], u[0]), (_Float16)silu_mul(g[1], u[1])};
+    hi = half2_t{(_Float16)silu_mul(g[2], u[2]), (_Float16)silu_mul(g[3], u[3])};
+  } else {
+    lo = half2_t{(_Float16)g[0], (_Float16)g[1]};
+    hi = half2_t{(_Float16)g[2], (_Float16)g[3]};
+  }
+  *(uint2 *)(out + (int64_t)m * ldo + n) = uint2{bitcast<uint32_t>(lo), bitcast<uint32_t>(hi)};
+}
+
 // ---------------------------------------------------------------------------
 // Host side.
 
@@ -447,6 +544,9 @@ static PrefillArgs prefill_args(const Problem &p, int BM, const void *weights) {
   a.tiles_m = (int)ceil_div(p.M, BM);
   // Each workgroup covers 8 strips (plain) or 4 gate strips + their up strips.
   a.tiles_n = (int)(p.swiglu ? ceil_div(a.up_off, 4) : ceil_div(a.NS, 8));
+  a.KS = 1;
+  a.spk = a.KT;
+  a.ws = nullptr;
   return a;
 }
 
@@ -469,43 +569,139 @@ static hipError_t launch_tiled(const Problem &p, const void *weights, hipStream_
   return p.swiglu ? launch_prefill_t<2, DENSE, true>(a, s) : launch_prefill_t<2, DENSE, false>(a, s);
 }
 
-template <int MI, int WM, int WNW, int TPS, bool DENSE, bool SWIGLU>
-static hipError_t launch_prefill2_t(const Problem &p, const void *weights, hipStream_t s) {
+static int env_int(const char *name, int fallback) {
+  const char *v = std::getenv(name);
+  if (v == nullptr || *v == 0) return fallback;
+  const int x = std::atoi(v);
+  return x > 0 ? x : fallback;
+}
+
+// prefill2_kernel addresses every operand with 32-bit buffer offsets.
+static bool fits_buffer_offsets(const Problem &p, bool dense) {
+  const int64_t limit = (int64_t)1 << 31;
+  const int64_t ns = ceil_div(p.N, kStrip);
+  return p.M * p.K * 2 < limit && ns * (p.K / kTileK) * 1024 * (dense ? 4 : 1) < limit &&
+         ns * ceil_div(p.K / kGroup, 8) * 512 < limit && p.M * p.N * 4 < limit;
+}
+
+// Compute units of the current device (256 on MI355X), cached per device.
+static int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Launch shape of prefill2_kernel: rows per workgroup tile (64, 128 or 256),
+// 64-k tiles per pipeline step, and K slices.
+struct Prefill2Config {
+  int bm, tps, ks, tiles;
+};
+
+// false: the one-wave kernel (prefill_kernel) runs instead.  The fused path
+// always takes prefill2_kernel (unless an operand is too large for 32-bit
+// offsets or W4A16_PREFILL_V2=0); the dense tier keeps prefill_kernel unless
+// W4A16_PREFILL_V2=1.  Shape, from measurement on MI355X: 64-row tiles up to
+// M = 64, 128-row tiles up to M = 384, then 256-row tiles; two 64-k tiles per
+// step for the smaller tiles; and K split in two while the doubled grid
+// still fits one workgroup per CU (the partial sums cost a round trip through
+// memory, which only pays when CUs would otherwise idle).
+// W4A16_PREFILL_BM, W4A16_PREFILL_TPS and W4A16_PREFILL_KS override.
+static bool prefill2_config(const Problem &p, bool dense, Prefill2Config &c) {
+  const char *v = std::getenv("W4A16_PREFILL_V2");
+  const bool on = v != nullptr ? *v == '1' : !dense;
+  if (!on || !fits_buffer_offsets(p, dense)) return false;
+  const int bm_env = env_int("W4A16_PREFILL_BM", 0);
+  if (dense)
+    c.bm = 256;  // the dense tier always runs the 256-row tile, unsplit
+  else if (bm_env == 64 || bm_env == 128 || bm_env == 256)
+    c.bm = bm_env;
+  else
+    c.bm = p.M <= 64 ? 64 : (p.M <= 384 ? 128 : 256);
+  c.tps = dense ? 1 : env_int("W4A16_PREFILL_TPS", c.bm <= 128 ? 2 : 1) == 2 ? 2 : 1;
+  const int64_t NS = ceil_div(p.N, kStrip);
+  const int64_t tiles_n = p.swiglu ? ceil_div(NS / 2, 4) : ceil_div(NS, 8);
+  c.tiles = (int)(ceil_div(p.M, c.bm) * tiles_n);
+  const int nsteps = (int)(p.K / kTileK / c.tps);
+  int ks = 1;
+  const int cus = device_cus();
+  if (!dense)
+    while ((int64_t)c.tiles * ks * 2 <= cus && ks < 16 && nsteps % (2 * ks) == 0 &&
+           nsteps / (2 * ks) >= 4)
+      ks *= 2;
+  const int ks_env = env_int("W4A16_PREFILL_KS", 0);
+  if (!dense && ks_env > 0 && nsteps % ks_env == 0) ks = ks_env;
+  c.ks = ks;
+  return true;
+}
+
+template <int MI, int TPS, bool DENSE, bool SWIGLU>
+static hipError_t launch_prefill2_t(const Problem &p, const void *weights, const Prefill2Config &c,
+                                    void *workspace, hipStream_t s) {
+  constexpr int WM = 2, WNW = 4;
   PrefillArgs a = prefill_args(p, 32 * MI * WM, weights);
   a.tiles_n = (int)(p.swiglu ? ceil_div(a.up_off, WNW) : ceil_div(a.NS, 2 * WNW));
-  hipLaunchKernelGGL((prefill2_kernel<MI, WM, WNW, TPS, DENSE, SWIGLU>), dim3(a.tiles_m * a.tiles_n),
-                     dim3(64 * WM * WNW), 0, s, a);
+  a.KS = c.ks;
+  a.spk = a.KT / TPS / c.ks;
+  a.ws = (float *)workspace;
+  hipLaunchKernelGGL((prefill2_kernel<MI, WM, WNW, TPS, DENSE, SWIGLU>),
+                     dim3(a.tiles_m * a.tiles_n * c.ks), dim3(64 * WM * WNW), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || c.ks == 1) return e;
+  const int64_t threads = p.M * (a.ldo / 4);
+  hipLaunchKernelGGL((prefill_reduce_kernel<SWIGLU>), dim3((unsigned)ceil_div(threads, 256)),
+                     dim3(256), 0, s, (const float *)workspace, c.ks, a.M, a.N, p.out, a.ldo);
   return hipGetLastError();
 }
 
-template <bool DENSE>
-static hipError_t launch_tiled2(const Problem &p, const void *weights, hipStream_t s) {
-  const char *v = std::getenv("W4A16_PREFILL_TPS");
+template <int MI, bool DENSE>
+static hipError_t launch_prefill2_m(const Problem &p, const void *weights, const Prefill2Config &c,
+                                    void *ws, hipStream_t s) {
   if constexpr (!DENSE) {
-    if (v != nullptr && *v == '2')
-      return p.swiglu ? launch_prefill2_t<4, 2, 4, 2, DENSE, true>(p, weights, s)
-                      : launch_prefill2_t<4, 2, 4, 2, DENSE, false>(p, weights, s);
+    if (c.tps == 2)
+      return p.swiglu ? launch_prefill2_t<MI, 2, DENSE, true>(p, weights, c, ws, s)
+                      : launch_prefill2_t<MI, 2, DENSE, false>(p, weights, c, ws, s);
   }
-  return p.swiglu ? launch_prefill2_t<4, 2, 4, 1, DENSE, true>(p, weights, s)
-                  : launch_prefill2_t<4, 2, 4, 1, DENSE, false>(p, weights, s);
+  return p.swiglu ? launch_prefill2_t<MI, 1, DENSE, true>(p, weights, c, ws, s)
+                  : launch_prefill2_t<MI, 1, DENSE, false>(p, weights, c, ws, s);
 }
 
-static bool prefill_v2() {
-  const char *v = std::getenv("W4A16_PREFILL_V2");
-  return v != nullptr && *v == '1';
+int64_t prefill_workspace_bytes(const Problem &p) {
+  Prefill2Config c;
+  if (!prefill2_config(p, false, c) || c.ks == 1) return 0;
+  return (int64_t)c.ks * p.M * p.N * (int64_t)sizeof(float);
 }
 
-hipError_t launch_prefill(const Problem &p, hipStream_t s) {
-  if (prefill_v2() && p.M > 256) return launch_tiled2<false>(p, p.rw, s);
-  return launch_tiled<false>(p, p.rw, s);
+hipError_t launch_prefill(const Problem &p, void *workspace, hipStream_t s) {
+  Prefill2Config c;
+  if (!prefill2_config(p, false, c)) return launch_tiled<false>(p, p.rw, s);
+  if (c.ks > 1 && workspace == nullptr) return hipErrorInvalidValue;
+  if (c.bm == 64) return launch_prefill2_m<1, false>(p, p.rw, c, workspace, s);
+  if (c.bm == 128) return launch_prefill2_m<2, false>(p, p.rw, c, workspace, s);
+  return launch_prefill2_m<4, false>(p, p.rw, c, workspace, s);
 }
 
 int tiled_describe(const Problem &p, bool dense, char *buf, size_t n) {
+  const char *pre = dense ? "dequant_kernel<false>; " : "";
+  const char *d = dense ? "true" : "false", *sw = p.swiglu ? "true" : "false";
+  Prefill2Config c;
+  if (prefill2_config(p, dense, c)) {
+    int k = snprintf(buf, n, "%sprefill2_kernel<%d, 2, 4, %d, %s, %s> workgroups=%d threads=512 ks=%d",
+                     pre, c.bm / 64, c.tps, d, sw, c.tiles * c.ks, c.ks);
+    if (c.ks > 1 && k > 0 && (size_t)k < n)
+      k += snprintf(buf + k, n - k, "; prefill_reduce_kernel<%s>", sw);
+    return k;
+  }
   const int MI = p.M > 128 ? 8 : (p.M > 64 ? 4 : 2);
   const PrefillArgs a = prefill_args(p, 32 * MI, nullptr);
-  return snprintf(buf, n, "%sprefill_kernel<%d, 2, %s, %s> workgroups=%d threads=256",
-                  dense ? "dequant_kernel<false>; " : "", MI, dense ? "true" : "false",
-                  p.swiglu ? "true" : "false", a.tiles_m * a.tiles_n);
+  return snprintf(buf, n, "%sprefill_kernel<%d, 2, %s, %s> workgroups=%d threads=256", pre, MI, d,
+                  sw, a.tiles_m * a.tiles_n);
 }
 
 int64_t dense_workspace_bytes(const Problem &p) {
@@ -518,7 +714,8 @@ hipError_t launch_dense(const Problem &p, void *workspace, hipStream_t s) {
   void *w16f = workspace;
   hipError_t e = launch_dequant_fragment(p.rw, p.rs, p.K, p.N, (uint16_t *)w16f, s);
   if (e != hipSuccess) return e;
-  if (prefill_v2() && p.M > 256) return launch_tiled2<true>(p, w16f, s);
+  Prefill2Config c;
+  if (prefill2_config(p, true, c)) return launch_prefill2_m<4, true>(p, w16f, c, nullptr, s);
   return launch_tiled<true>(p, w16f, s);
 }
 
