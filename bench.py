@@ -12,12 +12,19 @@ between two uses of one copy exceeds 800 MB (three times the 256 MB
 memory-side cache plus the L2s), so every weight byte comes from HBM.
 
 Timing (HIP events on the stream the kernels run on):
-  * the step: each rotation slot's GEMMs are captured once in a HIP graph;
-    W warm-up steps, then exactly K timed steps between two synchronisations;
+  * the step: each step of the rotation is captured in a HIP graph (for
+    workloads of fewer than 16 GEMMs, runs of consecutive steps share one
+    graph so that graph launches do not dominate); W warm-up steps, then
+    exactly K timed steps between two synchronisations;
   * per GEMM: a HIP graph of one launch per weight copy, replayed between two
     events; the kernel behind the largest share of the step time gives the
     roofline entry (algorithmic bytes = K*N/2 + 2*(K/G)*N + 2*M*K + 2*M*N_out,
     FLOPs = 2*M*N*K).
+
+Ceilings: the library's probe kernels measure the GPU's own streaming-read
+rate and fp16 MFMA rate; the roofline entry gives the fraction of both the
+data-sheet peak and the measured ceiling; clock levels and board power are
+read from sysfs after the timing.
 
 The CPU baseline times the oracle (test infrastructure) on a column sample of
 the same GEMMs.
@@ -48,7 +55,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA
 ROTATE_BYTES = 800e6
 G = 128
-PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.txt")
+PROFILES = os.path.join(ROOT, "profiles")
 
 
 def log(*a):
@@ -116,10 +123,11 @@ def source_digest():
 def stored_traffic(workload, kernel):
     """HBM bytes per launch from the committed counter summary, if it was
     taken on the current kernel sources, for this workload and kernel."""
-    if not os.path.exists(PROFILE_TRAFFIC):
+    path = os.path.join(PROFILES, "traffic_%s.txt" % workload)
+    if not os.path.exists(path):
         return None
     vals = {}
-    for line in open(PROFILE_TRAFFIC):
+    for line in open(path):
         m = re.match(r"^\s*([a-z_]+)\s*=\s*(.+?)\s*$", line)
         if m:
             vals[m.group(1)] = m.group(2)
@@ -173,6 +181,65 @@ def cpu_baseline(units, host_w, target_s=12.0):
                    "the %d GEMMs (all rows, full K), %.1f s on %d threads; quantize/pack untimed"
                    % (100 * frac, len(units), elapsed, threads)),
     }
+
+
+def measure_ceilings(stream, torch, dev):
+    """The GPU's own ceilings, from the library's probe kernels: a streaming
+    read of two alternating 1 GiB buffers (each read exceeds the memory-side
+    cache) and a register-only fp16 MFMA loop with two waves per SIMD."""
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    bufs = [torch.ones(1 << 28, dtype=torch.int32, device=dev) for _ in range(2)]
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    reps = 10
+    with torch.cuda.stream(stream):
+        for b in bufs:
+            w4a16.probe_stream_read(b, sink, stream)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(reps):
+            w4a16.probe_stream_read(bufs[i % 2], sink, stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    read_gbs = reps * (1 << 30) / (a.elapsed_time(b) * 1e-3) / 1e9
+    del bufs
+    iters = 8192
+    with torch.cuda.stream(stream):
+        w4a16.probe_mfma(64, 2 * cus, sink, stream)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fl = 0
+        for _ in range(3):
+            fl += w4a16.probe_mfma(iters, 2 * cus, sink, stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    mfma_tf = fl / (a.elapsed_time(b) * 1e-3) / 1e12
+    return {"stream_read_GBs": round(read_gbs, 1), "mfma_f16_TFLOPs": round(mfma_tf, 1),
+            "how": "w4a16_probe_stream_read over 2 x 1 GiB alternating (10 reads); "
+                   "w4a16_probe_mfma %d workgroups x 4 waves, %d rounds of 4 MFMA 32x32x16 f16"
+                   % (2 * cus, iters)}
+
+
+def clocks_snapshot():
+    """Current shader and memory clock levels and board power, read from the
+    amdgpu sysfs files (best effort; no child process)."""
+    import glob
+    out = {}
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        card = dev.split("/")[-2]
+        for f in ("pp_dpm_sclk", "pp_dpm_mclk"):
+            try:
+                for line in open(os.path.join(dev, f)):
+                    if "*" in line:
+                        out["%s %s" % (card, f)] = line.split(":", 1)[1].replace("*", "").strip()
+            except OSError:
+                pass
+        for f in glob.glob(os.path.join(dev, "hwmon", "hwmon*", "power1_*")):
+            if f.endswith(("_average", "_input")):
+                try:
+                    out["%s %s W" % (card, os.path.basename(f))] = int(open(f).read()) / 1e6
+                except (OSError, ValueError):
+                    pass
+    return out
 
 
 def main():
@@ -258,26 +325,46 @@ def main():
                 run_unit(u, step_copy(s, u[6]))
     torch.cuda.synchronize()
 
-    graphs = []
-    for s in range(period):
+    # Graphs: one per step of the rotation period, and, for workloads of few
+    # GEMMs, graphs of `spg` consecutive steps (at least 16 launches each) so
+    # that graph-launch overhead does not dominate the step.
+    spg = max(1, math.ceil(16 / len(units)))
+
+    def capture(first, count):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
-            for u in units:
-                run_unit(u, step_copy(s, u[6]))
-        graphs.append(g)
+            for s in range(first, first + count):
+                for u in units:
+                    run_unit(u, step_copy(s % period, u[6]))
+        return g
+
+    graphs = [capture(s, 1) for s in range(period)]
+    multi = {}
+    if spg > 1:
+        for s in range(0, period * spg, spg):
+            multi.setdefault(s % period, capture(s % period, spg))
     torch.cuda.synchronize()
+
+    def replay_steps(first, count):
+        """Replay steps first .. first+count-1 (rotation order kept)."""
+        s = first
+        while s < first + count:
+            if spg > 1 and first + count - s >= spg and (s % period) in multi:
+                multi[s % period].replay()
+                s += spg
+            else:
+                graphs[s % period].replay()
+                s += 1
 
     # Warm-up, then exactly K timed steps.
     with torch.cuda.stream(stream):
-        for i in range(args.warmup):
-            graphs[i % period].replay()
+        replay_steps(0, args.warmup)
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     with torch.cuda.stream(stream):
         ev0.record(stream)
-        for i in range(args.steps):
-            graphs[(args.warmup + i) % period].replay()
+        replay_steps(args.warmup, args.steps)
         ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -315,6 +402,14 @@ def main():
             (label, detail[-1]["kernel"], us, detail[-1]["GB/s"], detail[-1]["TFLOP/s"]))
         del g
 
+    log("ceilings ...")
+    ceilings = measure_ceilings(stream, torch, dev)
+    ceilings["clocks_after_timing"] = clocks_snapshot()
+    log("  ", ceilings)
+    for d in detail:
+        d["hbm_frac_of_measured"] = round(d["GB/s"] / ceilings["stream_read_GBs"], 4)
+        d["mfma_frac_of_measured"] = round(d["TFLOP/s"] / ceilings["mfma_f16_TFLOPs"], 4)
+
     # Dominant kernel: the largest share of the per-GEMM times.
     by_kernel = {}
     for d in detail:
@@ -335,8 +430,12 @@ def main():
         achieved = e["flops"] / e["us"] / 1e6
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_F16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4)}
+    ceiling = ceilings["stream_read_GBs"] if hbm_bound else ceilings["mfma_f16_TFLOPs"]
+    roof["frac_of_measured_ceiling"] = round(achieved / ceiling, 4) if ceiling else None
     roof["traffic"] = stored_traffic(args.workload, dom)
     roof["kernel"] = dom
+    roof["launch_workgroups"] = sorted({int(re.search(r"workgroups=(\d+)", d["launch"]).group(1))
+                                        for d in detail if d["kernel"] == dom})
     roof["launches_per_step"] = e["launches"]
     roof["avg_launch_us"] = round(avg_us, 3)
     roof["alg_bytes_per_launch"] = round(e["bytes"] / e["launches"])
@@ -374,8 +473,10 @@ def main():
         "config": {"workload": args.workload, "description": desc, "G": G,
                    "gemms_per_step": len(units), "alg_bytes_per_step": step_bytes,
                    "flops_per_step": step_flops, "weight_copies": ncopies,
-                   "path": "auto", "timing": "HIP graph per step, HIP events"},
+                   "path": "auto",
+                   "timing": "HIP graphs of %d step(s), HIP events" % spg},
         "roofline": roof,
+        "ceilings": ceilings,
         "cpu_baseline": cpu,
         "per_gemm": detail,
     }

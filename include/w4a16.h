@@ -162,6 +162,33 @@ int w4a16_select_path(int64_t M, int64_t K, int64_t N, int G, int flags);
  * negative error code (W4A16_ERR_INVALID for a bad shape, flag or buffer). */
 int w4a16_describe(int64_t M, int64_t K, int64_t N, int G, int flags, char *buf, int64_t len);
 
+/* ---- Measurement probes ------------------------------------------------
+ * The machine's own ceilings, against which the GEMM's roofline fractions are
+ * also reported: the Swordfish page (blog.alpindale.net, section "Decode,
+ * counting memory-pipe slots") rates its decode kernels against the
+ * platform's practical DRAM ceiling rather than the data-sheet figure, and
+ * the INT4 kernels page (aicassindra.com, section "Benchmarking against the
+ * roofline") asks for measurements on one's own GPU. */
+
+/* Streaming read: every 16-byte word of buf_d[0 .. bytes) is read exactly
+ * once with 128-bit non-temporal loads spread over the whole GPU; nothing is
+ * written except, in the unlikely case that the XOR of everything read equals
+ * a fixed tag, one 32-bit word at sink_d (so the reads cannot be removed).
+ * bytes > 0 and a multiple of 16; buf_d 16-byte aligned; sink_d a device
+ * buffer of at least 4 bytes.  Time it with events on `stream`. */
+int w4a16_probe_stream_read(const void *buf_d, int64_t bytes, void *sink_d,
+                            w4a16_stream_t stream);
+
+/* Dense fp16 MFMA loop: `workgroups` workgroups of 256 threads (4 waves)
+ * each run `iterations` rounds of 4 independent v_mfma_f32_32x32x16_f16
+ * (operands held in registers, FP32 accumulators), with no memory traffic
+ * but one conditional 4-byte store to sink_d.  *flops_out (host pointer, may
+ * be NULL) receives the floating-point operations performed:
+ * workgroups * 4 * iterations * 4 * 32768.  1 <= iterations <= 2^24,
+ * 1 <= workgroups <= 2^20. */
+int w4a16_probe_mfma(int64_t iterations, int64_t workgroups, void *sink_d, int64_t *flops_out,
+                     w4a16_stream_t stream);
+
 /* Thread-local message for the calling thread's last error ("" if none). */
 const char *w4a16_last_error(void);
 

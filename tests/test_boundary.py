@@ -85,6 +85,19 @@ def test_other_argument_errors():
     assert L.w4a16_select_path(1, 4096, 4096, 128, 0) == w4a16.PATH_DECODE
 
 
+def test_probe_argument_errors_without_gpu():
+    L = w4a16.lib()
+    assert L.w4a16_probe_stream_read(0, 1024, 16, 0) == w4a16.ERR_INVALID      # null buffer
+    assert L.w4a16_probe_stream_read(16, 1000, 16, 0) == w4a16.ERR_INVALID     # not 16-byte words
+    assert L.w4a16_probe_stream_read(16, 0, 16, 0) == w4a16.ERR_INVALID
+    assert L.w4a16_probe_stream_read(8, 1024, 16, 0) == w4a16.ERR_INVALID      # misaligned
+    assert "aligned" in w4a16.last_error()
+    assert L.w4a16_probe_mfma(0, 1, 16, 0, 0) == w4a16.ERR_INVALID
+    assert L.w4a16_probe_mfma(1, 0, 16, 0, 0) == w4a16.ERR_INVALID
+    assert L.w4a16_probe_mfma(1 << 25, 1, 16, 0, 0) == w4a16.ERR_INVALID
+    assert L.w4a16_probe_mfma(10, 1, 0, 0, 0) == w4a16.ERR_INVALID             # null sink
+
+
 def test_repacked_sizes():
     wb, sb = w4a16.repacked_bytes(4096, 4096)
     assert wb == 4096 * 4096 // 2                      # same bytes as the packed words

@@ -228,3 +228,15 @@ def test_prefill_one_wave_kernel(monkeypatch, M, K, N, swiglu):
     monkeypatch.setenv("W4A16_PREFILL_V2", "0")
     assert w4a16.describe(M, K, N, swiglu=swiglu, path="prefill").startswith("prefill_kernel<")
     gemm_case(M, K, N, swiglu=swiglu, path="prefill", seed=M + K)
+
+
+def test_measurement_probes_run():
+    """The ceiling probes run, report their work, and leave the sink alone."""
+    T = torch()
+    sink = T.zeros(4, dtype=T.int32, device="cuda")
+    buf = T.arange(1 << 20, dtype=T.int32, device="cuda")
+    w4a16.probe_stream_read(buf, sink)
+    fl = w4a16.probe_mfma(16, 8, sink)
+    T.cuda.synchronize()
+    assert fl == 8 * 4 * 16 * 4 * 32768
+    assert int(sink.abs().sum()) == 0

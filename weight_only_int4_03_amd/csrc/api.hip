@@ -185,6 +185,30 @@ using namespace w4a16;
 
 extern "C" {
 
+int w4a16_probe_stream_read(const void *buf_d, int64_t bytes, void *sink_d,
+                            w4a16_stream_t stream) {
+  const char *who = "w4a16_probe_stream_read";
+  if (!buf_d || !sink_d) return fail(W4A16_ERR_INVALID, "%s: null pointer", who);
+  if (bytes <= 0 || bytes % 16 != 0)
+    return fail(W4A16_ERR_INVALID, "%s: bytes must be a positive multiple of 16", who);
+  if (!aligned16(buf_d)) return fail(W4A16_ERR_INVALID, "%s: buffer must be 16-byte aligned", who);
+  hipError_t e = launch_stream_read(buf_d, bytes, sink_d, (hipStream_t)stream);
+  return e == hipSuccess ? W4A16_OK : hip_fail(e, who);
+}
+
+int w4a16_probe_mfma(int64_t iterations, int64_t workgroups, void *sink_d, int64_t *flops_out,
+                     w4a16_stream_t stream) {
+  const char *who = "w4a16_probe_mfma";
+  if (!sink_d) return fail(W4A16_ERR_INVALID, "%s: null pointer", who);
+  if (iterations < 1 || iterations > ((int64_t)1 << 24) || workgroups < 1 ||
+      workgroups > ((int64_t)1 << 20))
+    return fail(W4A16_ERR_INVALID, "%s: iterations or workgroups out of range", who);
+  hipError_t e = launch_mfma_peak((int)iterations, workgroups, sink_d, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, who);
+  if (flops_out) *flops_out = workgroups * 4 * iterations * 4 * 32768;
+  return W4A16_OK;
+}
+
 const char *w4a16_last_error(void) { return g_last_error.c_str(); }
 
 const char *w4a16_version(void) { return "w4a16-gfx950 0.1"; }

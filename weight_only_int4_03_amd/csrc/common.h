@@ -154,4 +154,8 @@ int64_t dense_workspace_bytes(const Problem &p);
 hipError_t launch_dense(const Problem &p, void *workspace, hipStream_t s);
 int tiled_describe(const Problem &p, bool dense, char *buf, size_t n);
 
+// Measurement probes (probe.hip).
+hipError_t launch_stream_read(const void *buf, int64_t bytes, void *sink, hipStream_t s);
+hipError_t launch_mfma_peak(int iterations, int64_t workgroups, void *sink, hipStream_t s);
+
 }  // namespace w4a16

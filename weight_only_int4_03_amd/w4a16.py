@@ -57,6 +57,8 @@ _SIGNATURES = {
     "w4a16_gemm_workspace_bytes": ([_i64, _i64, _i64, _int, _int], _i64),
     "w4a16_select_path": ([_i64, _i64, _i64, _int, _int], _int),
     "w4a16_describe": ([_i64, _i64, _i64, _int, _int, _p, _i64], _int),
+    "w4a16_probe_stream_read": ([_p, _i64, _p, _p], _int),
+    "w4a16_probe_mfma": ([_i64, _i64, _p, _p, _p], _int),
     "w4a16_last_error": ([], ctypes.c_char_p),
     "w4a16_version": ([], ctypes.c_char_p),
 }
@@ -245,6 +247,21 @@ def describe(M: int, K: int, N: int, swiglu: bool = False, path: str | int = "au
     buf = ctypes.create_string_buffer(512)
     _check(lib().w4a16_describe(M, K, N, G, flags, ctypes.addressof(buf), len(buf)))
     return buf.value.decode()
+
+
+def probe_stream_read(buf, sink, stream=None) -> None:
+    """Enqueue one streaming read of every byte of the device tensor `buf`
+    (sink: a device tensor of at least 4 bytes)."""
+    _check(lib().w4a16_probe_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                         _stream(stream)))
+
+
+def probe_mfma(iterations: int, workgroups: int, sink, stream=None) -> int:
+    """Enqueue the dense fp16 MFMA loop; returns the FLOPs it performs."""
+    flops = ctypes.c_int64(0)
+    _check(lib().w4a16_probe_mfma(iterations, workgroups, _ptr(sink), ctypes.byref(flops),
+                                  _stream(stream)))
+    return flops.value
 
 
 def load_weight(W_host: np.ndarray, device="cuda", G: int = G) -> RepackedWeight:
