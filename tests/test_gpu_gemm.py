@@ -184,22 +184,24 @@ def test_prefill_two_waves_per_simd(monkeypatch, path, M, K, N, swiglu):
     gemm_case(M, K, N, swiglu=swiglu, path=path, seed=M + N)
 
 
-PREFILL2_CONFIGS = [(64, 1, 1), (128, 1, 4), (256, 1, 2), (64, 2, 2), (128, 2, 4), (256, 2, 1),
-                    (64, 1, 8)]
+PREFILL2_CONFIGS = [(64, 4, 1, 1), (128, 4, 1, 4), (256, 4, 1, 2), (64, 4, 2, 2), (128, 4, 2, 4),
+                    (256, 4, 2, 1), (64, 4, 1, 8), (256, 2, 1, 1), (256, 2, 1, 4)]
 
 
-@pytest.mark.parametrize("bm,tps,ks", PREFILL2_CONFIGS)
+@pytest.mark.parametrize("bm,wnw,tps,ks", PREFILL2_CONFIGS)
 @pytest.mark.parametrize("M,K,N,swiglu", [(70, 2048, 1088, False), (200, 2048, 2112, True),
                                           (129, 4096, 4160, False)])
-def test_prefill2_tiles_and_k_slices(monkeypatch, bm, tps, ks, M, K, N, swiglu):
-    """The 8-wave mainloop at each row tile (64/128/256), one or two 64-k tiles
-    per pipeline step, and split K with the FP32 partial reduction; ragged M
-    and N, odd step counts per slice where the split allows."""
+def test_prefill2_tiles_and_k_slices(monkeypatch, bm, wnw, tps, ks, M, K, N, swiglu):
+    """The 8-wave mainloop at each row tile (64/128/256), 4 or 2 column waves,
+    one or two 64-k tiles per pipeline step, and split K with the FP32 partial
+    reduction; ragged M and N, odd step counts per slice where the split
+    allows."""
     monkeypatch.setenv("W4A16_PREFILL_BM", str(bm))
+    monkeypatch.setenv("W4A16_PREFILL_WNW", str(wnw))
     monkeypatch.setenv("W4A16_PREFILL_TPS", str(tps))
     monkeypatch.setenv("W4A16_PREFILL_KS", str(ks))
     d = w4a16.describe(M, K, N, swiglu=swiglu, path="prefill")
-    assert "prefill2_kernel<%d, 2, 4, %d" % (bm // 64, tps) in d, d
+    assert "prefill2_kernel<%d, 2, %d, %d" % (bm // 64, wnw, tps) in d, d
     assert ("ks=%d" % ks) in d, d
     gemm_case(M, K, N, swiglu=swiglu, path="prefill", seed=M + N + bm + ks)
 

@@ -331,8 +331,9 @@ static int coop_env(const char *name, int fallback) {
 }
 
 // Where the cooperative kernel wins (measured on MI355X): wide shapes, whose
-// strip groups alone fill the GPU (fused gate/up), and K-heavy shapes at
-// M >= 8, where the activation rows are the larger share of load slots.
+// strip groups alone fill the GPU (fused gate/up), K-heavy shapes at M >= 8
+// (K >= 24576, two K slices) and deep ones at M >= 16 (K >= 12288, four K
+// slices), where the activation rows are the larger share of load slots.
 // Narrow, short-K shapes keep the per-wave kernel.  W4A16_DECODE_COOP=0/1
 // forces the choice; W4A16_COOP_WC / _WK / _KS override the configuration.
 bool coop_config(const Problem &p, int &WC, int &WK, int &KS) {
@@ -348,6 +349,9 @@ bool coop_config(const Problem &p, int &WC, int &WK, int &KS) {
   } else if (KG >= 192 && p.M >= 8) {
     use = true;
     WC = 2; WK = p.M <= 16 ? 4 : 2; KS = 2;
+  } else if (KG >= 96 && p.M >= 16) {
+    use = true;
+    WC = 2; WK = p.M <= 16 ? 4 : 2; KS = 4;
   } else {
     use = false;
     WC = 2; WK = 4; KS = 1;

@@ -601,50 +601,80 @@ static int device_cus() {
 // Launch shape of prefill2_kernel: rows per workgroup tile (64, 128 or 256),
 // 64-k tiles per pipeline step, and K slices.
 struct Prefill2Config {
-  int bm, tps, ks, tiles;
+  int bm, wnw, tps, ks, tiles;
 };
+
+// K slices for a grid of `tiles` workgroups: halve each workgroup's k range
+// while the doubled grid still fits one workgroup per CU (at most 16 slices,
+// at least 4 pipeline steps each).
+static int k_slices(int64_t tiles, int nsteps, int cus) {
+  int ks = 1;
+  while (tiles * ks * 2 <= cus && ks < 16 && nsteps % (2 * ks) == 0 && nsteps / (2 * ks) >= 4)
+    ks *= 2;
+  return ks;
+}
 
 // false: the one-wave kernel (prefill_kernel) runs instead.  The fused path
 // always takes prefill2_kernel (unless an operand is too large for 32-bit
 // offsets or W4A16_PREFILL_V2=0); the dense tier keeps prefill_kernel unless
-// W4A16_PREFILL_V2=1.  Shape, from measurement on MI355X: 64-row tiles up to
-// M = 64, 128-row tiles up to M = 384, then 256-row tiles; two 64-k tiles per
-// step for the smaller tiles; and K split in two while the doubled grid
-// still fits one workgroup per CU (the partial sums cost a round trip through
-// memory, which only pays when CUs would otherwise idle).
-// W4A16_PREFILL_BM, W4A16_PREFILL_TPS and W4A16_PREFILL_KS override.
+// W4A16_PREFILL_V2=1.
+//
+// Tile rows (64, 128 or 256) come from a small time model fitted to
+// measurements on MI355X: a workgroup of a BM-row tile over a k range of
+// K/ks runs at eff(BM) x 4.5 TFLOP/s (eff = 0.6, 0.85, 1.0: smaller tiles
+// reuse each dequantized weight fragment less), the grid runs in
+// ceil(workgroups / CUs) rounds, and a split K adds the round trip of the
+// FP32 partials through memory (2 ks M N 4 bytes at 5 TB/s) plus ~3 us.  Two
+// 64-k tiles per pipeline step for the smaller tiles.  W4A16_PREFILL_BM,
+// W4A16_PREFILL_WNW, W4A16_PREFILL_TPS and W4A16_PREFILL_KS override.
 static bool prefill2_config(const Problem &p, bool dense, Prefill2Config &c) {
   const char *v = std::getenv("W4A16_PREFILL_V2");
   const bool on = v != nullptr ? *v == '1' : !dense;
   if (!on || !fits_buffer_offsets(p, dense)) return false;
-  const int bm_env = env_int("W4A16_PREFILL_BM", 0);
-  if (dense)
-    c.bm = 256;  // the dense tier always runs the 256-row tile, unsplit
-  else if (bm_env == 64 || bm_env == 128 || bm_env == 256)
-    c.bm = bm_env;
-  else
-    c.bm = p.M <= 64 ? 64 : (p.M <= 384 ? 128 : 256);
-  c.tps = dense ? 1 : env_int("W4A16_PREFILL_TPS", c.bm <= 128 ? 2 : 1) == 2 ? 2 : 1;
+  const int cus = device_cus();
   const int64_t NS = ceil_div(p.N, kStrip);
-  const int64_t tiles_n = p.swiglu ? ceil_div(NS / 2, 4) : ceil_div(NS, 8);
+  const int bm_env = env_int("W4A16_PREFILL_BM", 0);
+  if (dense) {
+    c.bm = 256;  // the dense tier always runs the 256-row tile, unsplit
+  } else if (bm_env == 64 || bm_env == 128 || bm_env == 256) {
+    c.bm = bm_env;
+  } else {
+    static const double eff[3] = {0.6, 0.85, 1.0};
+    const int64_t tn = p.swiglu ? ceil_div(NS / 2, 4) : ceil_div(NS, 8);
+    double best = 0.0;
+    for (int i = 0; i < 3; ++i) {
+      const int bm = 64 << i;
+      const int tps = bm <= 128 ? 2 : 1;
+      const int64_t tiles = ceil_div(p.M, bm) * tn;
+      const int ks = k_slices(tiles, (int)(p.K / kTileK / tps), cus);
+      const double rounds = (double)ceil_div(tiles * ks, (int64_t)cus);
+      double t = rounds * 2.0 * bm * 256.0 * ((double)p.K / ks) / (4.5e12 * eff[i]);
+      if (ks > 1) t += 2.0 * ks * (double)p.M * (double)p.N * 4.0 / 5e12 + 3e-6;
+      if (i == 0 || t < best) {
+        best = t;
+        c.bm = bm;
+      }
+    }
+  }
+  c.tps = dense ? 1 : env_int("W4A16_PREFILL_TPS", c.bm <= 128 ? 2 : 1) == 2 ? 2 : 1;
+  // Column waves per workgroup: 4 (256 columns, one workgroup per CU) or,
+  // for the 256-row tile, 2 (128 columns, two workgroups per CU; measured
+  // slower, kept as an option).
+  c.wnw = !dense && c.bm == 256 && c.tps == 1 && env_int("W4A16_PREFILL_WNW", 4) == 2 ? 2 : 4;
+  const int64_t tiles_n = p.swiglu ? ceil_div(NS / 2, c.wnw) : ceil_div(NS, 2 * c.wnw);
   c.tiles = (int)(ceil_div(p.M, c.bm) * tiles_n);
   const int nsteps = (int)(p.K / kTileK / c.tps);
-  int ks = 1;
-  const int cus = device_cus();
-  if (!dense)
-    while ((int64_t)c.tiles * ks * 2 <= cus && ks < 16 && nsteps % (2 * ks) == 0 &&
-           nsteps / (2 * ks) >= 4)
-      ks *= 2;
+  int ks = dense ? 1 : k_slices(c.tiles, nsteps, cus);
   const int ks_env = env_int("W4A16_PREFILL_KS", 0);
   if (!dense && ks_env > 0 && nsteps % ks_env == 0) ks = ks_env;
   c.ks = ks;
   return true;
 }
 
-template <int MI, int TPS, bool DENSE, bool SWIGLU>
+template <int MI, int WNW, int TPS, bool DENSE, bool SWIGLU>
 static hipError_t launch_prefill2_t(const Problem &p, const void *weights, const Prefill2Config &c,
                                     void *workspace, hipStream_t s) {
-  constexpr int WM = 2, WNW = 4;
+  constexpr int WM = 2;
   PrefillArgs a = prefill_args(p, 32 * MI * WM, weights);
   a.tiles_n = (int)(p.swiglu ? ceil_div(a.up_off, WNW) : ceil_div(a.NS, 2 * WNW));
   a.KS = c.ks;
@@ -665,11 +695,16 @@ static hipError_t launch_prefill2_m(const Problem &p, const void *weights, const
                                     void *ws, hipStream_t s) {
   if constexpr (!DENSE) {
     if (c.tps == 2)
-      return p.swiglu ? launch_prefill2_t<MI, 2, DENSE, true>(p, weights, c, ws, s)
-                      : launch_prefill2_t<MI, 2, DENSE, false>(p, weights, c, ws, s);
+      return p.swiglu ? launch_prefill2_t<MI, 4, 2, DENSE, true>(p, weights, c, ws, s)
+                      : launch_prefill2_t<MI, 4, 2, DENSE, false>(p, weights, c, ws, s);
+    if constexpr (MI == 4) {
+      if (c.wnw == 2)
+        return p.swiglu ? launch_prefill2_t<MI, 2, 1, DENSE, true>(p, weights, c, ws, s)
+                        : launch_prefill2_t<MI, 2, 1, DENSE, false>(p, weights, c, ws, s);
+    }
   }
-  return p.swiglu ? launch_prefill2_t<MI, 1, DENSE, true>(p, weights, c, ws, s)
-                  : launch_prefill2_t<MI, 1, DENSE, false>(p, weights, c, ws, s);
+  return p.swiglu ? launch_prefill2_t<MI, 4, 1, DENSE, true>(p, weights, c, ws, s)
+                  : launch_prefill2_t<MI, 4, 1, DENSE, false>(p, weights, c, ws, s);
 }
 
 int64_t prefill_workspace_bytes(const Problem &p) {
@@ -692,8 +727,8 @@ int tiled_describe(const Problem &p, bool dense, char *buf, size_t n) {
   const char *d = dense ? "true" : "false", *sw = p.swiglu ? "true" : "false";
   Prefill2Config c;
   if (prefill2_config(p, dense, c)) {
-    int k = snprintf(buf, n, "%sprefill2_kernel<%d, 2, 4, %d, %s, %s> workgroups=%d threads=512 ks=%d",
-                     pre, c.bm / 64, c.tps, d, sw, c.tiles * c.ks, c.ks);
+    int k = snprintf(buf, n, "%sprefill2_kernel<%d, 2, %d, %d, %s, %s> workgroups=%d threads=%d ks=%d",
+                     pre, c.bm / 64, c.wnw, c.tps, d, sw, c.tiles * c.ks, 128 * c.wnw, c.ks);
     if (c.ks > 1 && k > 0 && (size_t)k < n)
       k += snprintf(buf + k, n - k, "; prefill_reduce_kernel<%s>", sw);
     return k;
