@@ -120,7 +120,7 @@ def test_describe_names_the_launches():
     assert d.startswith("decode_coop_kernel<16, 2, ") and d.split(">")[0].endswith("true")
     d = w4a16.describe(1, 4096, 4096)
     assert d.startswith("decode_kernel<16, 1, ") and d.split(">")[0].endswith("false")
-    assert "prefill2_kernel<4, 2, 4, 1, false, true>" in w4a16.describe(4096, 4096, 28672, swiglu=True)
+    assert "prefill2_kernel<4, 2, 4, 2, false, true>" in w4a16.describe(4096, 4096, 28672, swiglu=True)
     assert w4a16.describe(256, 4096, 28672, swiglu=True).startswith(
         "prefill2_kernel<2, 2, 4, 2, false, true> workgroups=224 threads=512 ks=1")
     assert w4a16.describe(64, 14336, 4096).endswith("ks=16; prefill_reduce_kernel<false>")

@@ -625,7 +625,8 @@ static int k_slices(int64_t tiles, int nsteps, int cus) {
 // reuse each dequantized weight fragment less), the grid runs in
 // ceil(workgroups / CUs) rounds, and a split K adds the round trip of the
 // FP32 partials through memory (2 ks M N 4 bytes at 5 TB/s) plus ~3 us.  Two
-// 64-k tiles per pipeline step for the smaller tiles.  W4A16_PREFILL_BM,
+// 64-k tiles (one scale group) per pipeline step: half the barriers of one
+// 64-k tile, measured 0-5% faster.  W4A16_PREFILL_BM,
 // W4A16_PREFILL_WNW, W4A16_PREFILL_TPS and W4A16_PREFILL_KS override.
 static bool prefill2_config(const Problem &p, bool dense, Prefill2Config &c) {
   const char *v = std::getenv("W4A16_PREFILL_V2");
@@ -644,7 +645,7 @@ static bool prefill2_config(const Problem &p, bool dense, Prefill2Config &c) {
     double best = 0.0;
     for (int i = 0; i < 3; ++i) {
       const int bm = 64 << i;
-      const int tps = bm <= 128 ? 2 : 1;
+      const int tps = 2;
       const int64_t tiles = ceil_div(p.M, bm) * tn;
       const int ks = k_slices(tiles, (int)(p.K / kTileK / tps), cus);
       const double rounds = (double)ceil_div(tiles * ks, (int64_t)cus);
@@ -656,7 +657,7 @@ static bool prefill2_config(const Problem &p, bool dense, Prefill2Config &c) {
       }
     }
   }
-  c.tps = dense ? 1 : env_int("W4A16_PREFILL_TPS", c.bm <= 128 ? 2 : 1) == 2 ? 2 : 1;
+  c.tps = dense ? 1 : env_int("W4A16_PREFILL_TPS", 2) == 2 ? 2 : 1;
   // Column waves per workgroup: 4 (256 columns, one workgroup per CU) or,
   // for the 256-row tile, 2 (128 columns, two workgroups per CU; measured
   // slower, kept as an option).
