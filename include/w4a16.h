@@ -57,6 +57,7 @@ extern "C" {
 
 /* Flags for w4a16_gemm_ex: a path in the low 4 bits, OR'ed with: */
 #define W4A16_FLAG_SWIGLU 0x10 /* fused SwiGLU epilogue (see w4a16_gemm_swiglu) */
+#define W4A16_FLAG_BF16 0x20   /* bf16 activations and output (see w4a16_gemm_ex) */
 
 typedef void *w4a16_stream_t; /* a hipStream_t */
 
@@ -111,6 +112,14 @@ int w4a16_unrepack(const void *rw_d, const void *rs_d, int64_t K, int64_t N, int
 int w4a16_dequant(const void *rw_d, const void *rs_d, int64_t K, int64_t N, int G,
                   uint16_t *W16_d, w4a16_stream_t stream);
 
+/* The same dequantization for bf16 models: Wb_d[k,n] = bf16((q - 8) * s), the
+ * exact product of q - 8 and the fp16 scale rounded once to bf16 (nearest
+ * even), bf16 bits [K, N] row-major, device.  The data contract's dequantize
+ * casts to the activation type (.half() for fp16 activations); this is its
+ * bf16 reading, and it is the weight operand of every bf16-activation GEMM. */
+int w4a16_dequant_bf16(const void *rw_d, const void *rs_d, int64_t K, int64_t N, int G,
+                       uint16_t *Wb_d, w4a16_stream_t stream);
+
 /* ---------------------------------------------------------------------------
  * GEMM (the job, stated precisely): C_d[m,n] = sum_k A_d[m,k] * w[k,n], FP32
  * accumulation, one fp16 rounding (nearest even) at the end.
@@ -140,10 +149,16 @@ int w4a16_gemm_swiglu(const uint16_t *A_d, int64_t M, int64_t K, const void *rw_
                       w4a16_stream_t stream);
 
 /* Explicit form of the two calls above.  `flags` = path (W4A16_PATH_*, AUTO
- * to use the table) | W4A16_FLAG_SWIGLU.  `workspace_d` (device, 256-byte
- * aligned, at least w4a16_gemm_workspace_bytes) is owned by the caller and
- * needs no initialisation: it carries nothing from one call to the next.
- * workspace_d may be NULL to use the library's per-device workspace. */
+ * to use the table) | W4A16_FLAG_SWIGLU | W4A16_FLAG_BF16.  `workspace_d`
+ * (device, 256-byte aligned, at least w4a16_gemm_workspace_bytes) is owned by
+ * the caller and needs no initialisation: it carries nothing from one call to
+ * the next.  workspace_d may be NULL to use the library's per-device
+ * workspace.
+ * W4A16_FLAG_BF16 (bf16 models: FuTransformer and the Swordfish page run
+ * bf16 activations): A_d and out_d hold bf16 bits instead of fp16; the same
+ * repacked weights and fp16 scales are used, each weight entering the product
+ * as bf16((q - 8) * s) (see w4a16_dequant_bf16); FP32 accumulation; the output
+ * (and the SwiGLU epilogue's) is rounded once to bf16, nearest even. */
 int w4a16_gemm_ex(const uint16_t *A_d, int64_t M, int64_t K, const void *rw_d,
                   const void *rs_d, int64_t N, int G, uint16_t *out_d, int flags,
                   void *workspace_d, int64_t workspace_bytes, w4a16_stream_t stream);

@@ -50,6 +50,13 @@ class Oracle:
         lib.oracle_f16_to_f64.restype = ctypes.c_double
         lib.oracle_f64_to_f16.argtypes = [ctypes.c_double]
         lib.oracle_f64_to_f16.restype = ctypes.c_uint16
+        lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
+        lib.oracle_bf16_to_f64.restype = ctypes.c_double
+        lib.oracle_f64_to_bf16.argtypes = [ctypes.c_double]
+        lib.oracle_f64_to_bf16.restype = ctypes.c_uint16
+        lib.oracle_dequant_bf16.argtypes = [_p, _p, _i64, _i64, ctypes.c_int, _p]
+        lib.oracle_gemm_bf16_f64.argtypes = [_p, _i64, _i64, _p, _p, _i64, ctypes.c_int, _p,
+                                             ctypes.c_int]
         lib.oracle_quantize.argtypes = [_p, _i64, _i64, ctypes.c_int, _p, _p]
         lib.oracle_pack.argtypes = [_p, _i64, _i64, _p]
         lib.oracle_unpack.argtypes = [_p, _i64, _i64, _p]
@@ -60,8 +67,8 @@ class Oracle:
         lib.oracle_swiglu_f64.argtypes = [_p, _i64, _i64, _p]
         lib.oracle_max_threads.argtypes = []
         for name in ("oracle_quantize", "oracle_pack", "oracle_unpack", "oracle_dequant",
-                     "oracle_gemm_f64", "oracle_gemm_w16_f64", "oracle_swiglu_f64",
-                     "oracle_max_threads"):
+                     "oracle_dequant_bf16", "oracle_gemm_f64", "oracle_gemm_bf16_f64",
+                     "oracle_gemm_w16_f64", "oracle_swiglu_f64", "oracle_max_threads"):
             getattr(lib, name).restype = ctypes.c_int
         self.lib = lib
         self.path = path
@@ -74,6 +81,16 @@ class Oracle:
     def f64_to_f16(self, values: np.ndarray) -> np.ndarray:
         v = np.ascontiguousarray(values, dtype=np.float64).ravel()
         return np.array([self.lib.oracle_f64_to_f16(float(x)) for x in v],
+                        dtype=np.uint16).reshape(np.shape(values))
+
+    # -- bfloat16 ---------------------------------------------------------
+    def bf16_to_f64(self, bits: np.ndarray) -> np.ndarray:
+        b = np.ascontiguousarray(bits, dtype=np.uint16).ravel()
+        return np.array([self.lib.oracle_bf16_to_f64(int(x)) for x in b]).reshape(np.shape(bits))
+
+    def f64_to_bf16(self, values: np.ndarray) -> np.ndarray:
+        v = np.ascontiguousarray(values, dtype=np.float64).ravel()
+        return np.array([self.lib.oracle_f64_to_bf16(float(x)) for x in v],
                         dtype=np.uint16).reshape(np.shape(values))
 
     # -- format -----------------------------------------------------------
@@ -123,6 +140,18 @@ class Oracle:
             raise ValueError("oracle_dequant failed with status %d" % rc)
         return W16
 
+    def dequant_bf16(self, packed: np.ndarray, s16: np.ndarray, G: int = 128) -> np.ndarray:
+        """bf16 bits [K,N] of (u-8)*s16, rounded once to bf16."""
+        packed = np.ascontiguousarray(packed, dtype=np.int32)
+        s16 = np.ascontiguousarray(s16, dtype=np.uint16)
+        R, N = packed.shape
+        Wb = np.empty((8 * R, N), np.uint16)
+        rc = self.lib.oracle_dequant_bf16(packed.ctypes.data, s16.ctypes.data, 8 * R, N, G,
+                                          Wb.ctypes.data)
+        if rc != OK:
+            raise ValueError("oracle_dequant_bf16 failed with status %d" % rc)
+        return Wb
+
     # -- products ---------------------------------------------------------
     def gemm_f64(self, A16: np.ndarray, packed: np.ndarray, s16: np.ndarray, G: int = 128,
                  nthreads: int = 0) -> np.ndarray:
@@ -142,6 +171,24 @@ class Oracle:
                                       s16.ctypes.data, N, G, C.ctypes.data, nthreads)
         if rc != OK:
             raise ValueError("oracle_gemm_f64 failed with status %d" % rc)
+        return C
+
+    def gemm_bf16_f64(self, Ab: np.ndarray, packed: np.ndarray, s16: np.ndarray, G: int = 128,
+                      nthreads: int = 0) -> np.ndarray:
+        """C = A * dequant_bf16(W) in fp64, A as bf16 bits (uint16) [M,K];
+        returns float64 [M,N]."""
+        Ab = np.ascontiguousarray(np.asarray(Ab).view(np.uint16))
+        packed = np.ascontiguousarray(packed, dtype=np.int32)
+        s16 = np.ascontiguousarray(s16, dtype=np.uint16)
+        M, K = Ab.shape
+        R, N = packed.shape
+        if 8 * R != K:
+            raise ValueError("A has K=%d but packed has %d rows" % (K, R))
+        C = np.empty((M, N), np.float64)
+        rc = self.lib.oracle_gemm_bf16_f64(Ab.ctypes.data, M, K, packed.ctypes.data,
+                                           s16.ctypes.data, N, G, C.ctypes.data, nthreads)
+        if rc != OK:
+            raise ValueError("oracle_gemm_bf16_f64 failed with status %d" % rc)
         return C
 
     def gemm_w16_f64(self, A16: np.ndarray, W16: np.ndarray, nthreads: int = 0) -> np.ndarray:

@@ -21,7 +21,11 @@
  *     fp16 zero; its nibbles are all 8;
  *   - the GEMM reference uses the exact dequantized weight (q-8)*s, with every
  *     product and the running sum in fp64; a second reference uses the
- *     fp16-rounded weight, as the page's test does.
+ *     fp16-rounded weight, as the page's test does;
+ *   - bf16 activations (the bf16 models of FuTransformer and of the Swordfish
+ *     page): the data contract's dequantize casts the exact (q-8)*s to the
+ *     activation type, so for bf16 the weight is bf16((q-8)*s), rounded once
+ *     to nearest even; the GEMM sums A * that weight in fp64.
  *
  * Build: gcc -O2 -std=c11 -fopenmp -ffp-contract=off -fPIC -shared
  * (no fast-math: the quantizer's decisions depend on IEEE fp32 division).
@@ -79,6 +83,52 @@ uint16_t oracle_f64_to_f16(double x)
     double n = nearbyint(a / ldexp(1.0, e - 10)); /* in [1024, 2048] */
     /* n == 2048 carries into the exponent field by plain addition */
     uint32_t code = ((uint32_t)(e + 15) << 10) + ((uint32_t)n - 1024u);
+    return (uint16_t)(sign | code);
+}
+
+/* ------------------------------------------------------------------------
+ * bfloat16, written out from the format's definition: the upper 16 bits of
+ * an IEEE binary32 -- 1 sign bit, 8 exponent bits (bias 127), 7 fraction
+ * bits; subnormals have exponent field 0 and value frac * 2^-133; exponent
+ * field 255 is inf/NaN.
+ * ---------------------------------------------------------------------- */
+
+double oracle_bf16_to_f64(uint16_t b)
+{
+    int sign = (b >> 15) & 1;
+    int e = (b >> 7) & 0xff;
+    int f = b & 0x7f;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -133);
+    else if (e == 255)
+        v = (f == 0) ? INFINITY : NAN;
+    else
+        v = ldexp((double)(128 + f), e - 134);
+    return sign ? -v : v;
+}
+
+/* Round a double to the nearest bfloat16 value, ties to even. */
+uint16_t oracle_f64_to_bf16(double x)
+{
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs(x);
+    if (isnan(x))
+        return (uint16_t)(sign | 0x7fc0);
+    /* the largest finite value is (2^8 - 1) * 2^120; halfway to 2^128 overflows */
+    if (a >= ldexp(255.5, 120))
+        return (uint16_t)(sign | 0x7f80);
+    if (a < ldexp(1.0, -126)) {
+        /* subnormal range: quantum 2^-133; 128 quanta is the smallest normal */
+        double n = nearbyint(a / ldexp(1.0, -133));
+        return (uint16_t)(sign | (uint16_t)n);
+    }
+    int e2;
+    frexp(a, &e2);            /* a = frac * 2^e2, frac in [0.5, 1) */
+    int e = e2 - 1;           /* a in [2^e, 2^(e+1)), e in [-126, 127] */
+    double n = nearbyint(a / ldexp(1.0, e - 7)); /* in [128, 256] */
+    /* n == 256 carries into the exponent field by plain addition */
+    uint32_t code = ((uint32_t)(e + 127) << 7) + ((uint32_t)n - 128u);
     return (uint16_t)(sign | code);
 }
 
@@ -183,6 +233,19 @@ int oracle_dequant(const int32_t *packed, const uint16_t *s16, int64_t K,
     return ORACLE_OK;
 }
 
+/* Dequantize for bf16 activations: Wb[k,n] = bf16((u-8) * s16), the exact
+ * product rounded once. */
+int oracle_dequant_bf16(const int32_t *packed, const uint16_t *s16, int64_t K,
+                        int64_t N, int G, uint16_t *Wb)
+{
+    if (G <= 0 || K % G != 0 || K % 8 != 0)
+        return ORACLE_ERR_SHAPE;
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t n = 0; n < N; ++n)
+            Wb[k * N + n] = oracle_f64_to_bf16(exact_weight(packed, s16, N, G, k, n));
+    return ORACLE_OK;
+}
+
 static void set_threads(int nthreads)
 {
 #ifdef _OPENMP
@@ -264,6 +327,40 @@ int oracle_gemm_w16_f64(const uint16_t *A16, int64_t M, int64_t K,
         }
     }
     return 0;
+}
+
+/* GEMM reference for bf16 activations: Ab bf16 bits [M,K], weights
+ * bf16((u-8) * s16) as oracle_dequant_bf16 defines them, each product exact
+ * in fp64 (8-bit by 8-bit significands) and the sum in fp64 in increasing k. */
+int oracle_gemm_bf16_f64(const uint16_t *Ab, int64_t M, int64_t K,
+                         const int32_t *packed, const uint16_t *s16, int64_t N,
+                         int G, double *C, int nthreads)
+{
+    if (G <= 0 || K % G != 0 || K % 8 != 0)
+        return ORACLE_ERR_SHAPE;
+    set_threads(nthreads);
+    int64_t nchunks = (N + NCHUNK - 1) / NCHUNK;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t c = 0; c < nchunks; ++c) {
+            int64_t n0 = c * NCHUNK;
+            int64_t n1 = n0 + NCHUNK < N ? n0 + NCHUNK : N;
+            double acc[NCHUNK];
+            for (int64_t n = n0; n < n1; ++n)
+                acc[n - n0] = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double a = oracle_bf16_to_f64(Ab[m * K + k]);
+                for (int64_t n = n0; n < n1; ++n) {
+                    double w = oracle_bf16_to_f64(
+                        oracle_f64_to_bf16(exact_weight(packed, s16, N, G, k, n)));
+                    acc[n - n0] += a * w;
+                }
+            }
+            for (int64_t n = n0; n < n1; ++n)
+                C[m * N + n] = acc[n - n0];
+        }
+    }
+    return ORACLE_OK;
 }
 
 /* ------------------------------------------------------------------------

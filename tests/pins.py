@@ -63,6 +63,49 @@ def check_f16_encode(o):
     assert np.array_equal(ours, ref), np.flatnonzero(ours != ref)[:10]
 
 
+# -- bfloat16 ------------------------------------------------------------------
+
+def _torch_bf16_bits(x64):
+    """torch's float32 -> bfloat16 cast (round to nearest even) of values
+    that are exact in float32, as uint16 bits."""
+    import torch
+    t = torch.from_numpy(np.asarray(x64, np.float64).astype(np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def check_bf16_decode(o):
+    """Every sampled bfloat16 bit pattern decodes as the upper half of the
+    binary32 with those bits (numpy's float32)."""
+    bits = np.arange(0, 1 << 16, 61, dtype=np.uint32).astype(np.uint16)
+    bits = np.concatenate([bits, np.array([0x0000, 0x0001, 0x007F, 0x0080, 0x3F80, 0x7F7F,
+                                           0x7F80, 0x8001, 0xFF7F, 0xFF80], np.uint16)])
+    ours = o.bf16_to_f64(bits)
+    ref = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    finite = np.isfinite(ref)
+    assert np.array_equal(ours[finite], ref[finite])
+    assert np.array_equal(np.isinf(ours), np.isinf(ref))
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+
+
+def check_bf16_encode(o):
+    """Rounding to bfloat16 agrees with torch's cast on float32-exact values:
+    exact ties (to even), values between neighbours, subnormals, overflow."""
+    rng = np.random.default_rng(17)
+    bits = np.arange(0, 0x7F80, 41, dtype=np.uint32)
+    vals = (bits << 16).view(np.float32).astype(np.float64)
+    mids = (vals[:-1] + vals[1:]) / 2.0                         # exact ties, fp32-exact
+    frac = np.floor(rng.random(len(vals) - 1) * 65536) / 65536  # fp32-exact offsets
+    offs = vals[:-1] + (vals[1:] - vals[:-1]) * frac
+    specials = np.array([0.0, -0.0, 1.0, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 3.0e38,
+                         float(np.float32(3.39e38)), 2.0 ** -133, 2.0 ** -134,
+                         3 * 2.0 ** -135, 2.0 ** -126 - 2.0 ** -134, 65504.0, 1e-8])
+    x = np.concatenate([vals, mids, offs, -mids, specials, -specials])
+    x = x[np.float32(x).astype(np.float64) == x]                  # keep fp32-exact inputs
+    ours = o.f64_to_bf16(x)
+    ref = _torch_bf16_bits(x)
+    assert np.array_equal(ours, ref), np.flatnonzero(ours != ref)[:10]
+
+
 # -- packing ------------------------------------------------------------------
 
 def check_pack_worked_words(o):
@@ -209,6 +252,19 @@ def check_dequant_rounds_once(o):
     assert np.array_equal(W16, exact.astype(np.float16).view(np.uint16))
 
 
+def check_dequant_bf16_rounds_once(o):
+    """bf16 weights are bf16 of the exact product (fp32-exact: at most 15
+    significant bits), compared with torch's cast."""
+    packed, s16 = synth.random_words(256, 16, seed=14)
+    u = o.unpack(packed).astype(np.float64)
+    s = s16.view(np.float16).astype(np.float64)
+    exact = (u - 8) * np.repeat(s, 128, axis=0)
+    Wb = o.dequant_bf16(packed, s16)
+    assert np.array_equal(Wb, _torch_bf16_bits(exact))
+    # u = 8 gives +0, power-of-two scales are exact.
+    assert (Wb[(o.unpack(packed) == 8)] == 0).all()
+
+
 # -- GEMM ------------------------------------------------------------------------
 
 def _exact_weights(o, packed, s16, G=128):
@@ -273,6 +329,32 @@ def check_gemm_w16_reference(o):
     assert np.allclose(C, ref, rtol=1e-12, atol=1e-12)
 
 
+def check_gemm_bf16_bruteforce(o):
+    """bf16 activations on tiny shapes: numpy's float64 matmul of the bf16
+    activations and torch's bf16 rounding of the exact weights."""
+    rng = np.random.default_rng(15)
+    for M, K, N in ((1, 128, 8), (3, 256, 16)):
+        packed, s16 = synth.random_words(K, N, seed=M * 7 + K + N)
+        Ab = _torch_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+        C = o.gemm_bf16_f64(Ab, packed, s16)
+        A = (Ab.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        Wb = _torch_bf16_bits(_exact_weights(o, packed, s16))
+        W = (Wb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        assert np.allclose(C, np.matmul(A, W), rtol=1e-12, atol=1e-12)
+
+
+def check_gemm_bf16_matches_fp16_when_exact(o):
+    """Ternary activations and power-of-two scales are exact in both formats,
+    so the bf16 product equals the fp16 product bit for bit."""
+    K, N = 512, 16
+    W = synth.grid_weights(K, N, p=4, seed=9)
+    packed, s16 = o.quantize_pack(W)
+    A = synth.ternary_activations(3, K, density=0.8, seed=9)     # fp16 values
+    Ab = _torch_bf16_bits(A.astype(np.float64))
+    assert np.array_equal(o.bf16_to_f64(Ab), A.astype(np.float64))
+    assert np.array_equal(o.gemm_bf16_f64(Ab, packed, s16), o.gemm_f64(A, packed, s16))
+
+
 # -- SwiGLU ----------------------------------------------------------------------
 
 def check_swiglu(o):
@@ -298,4 +380,6 @@ FAST_CHECKS = [
     check_quantization_error_closed_form, check_dequant_special_values,
     check_dequant_rounds_once, check_gemm_bruteforce, check_gemm_onehot,
     check_gemm_integer_exact, check_gemm_all_ones, check_gemm_w16_reference, check_swiglu,
+    check_bf16_decode, check_bf16_encode, check_dequant_bf16_rounds_once,
+    check_gemm_bf16_bruteforce, check_gemm_bf16_matches_fp16_when_exact,
 ]

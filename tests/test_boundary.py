@@ -69,6 +69,8 @@ def test_gemm_argument_errors_without_gpu():
     assert "null" in w4a16.last_error()
     assert _gemm_ex(flags=w4a16.FLAG_SWIGLU, N=4128) == w4a16.ERR_INVALID  # N % 64
     assert _gemm_ex(flags=0x100) == w4a16.ERR_INVALID             # unknown flag
+    assert _gemm_ex(flags=w4a16.FLAG_BF16) == w4a16.ERR_INVALID    # bf16 flag known: null pointers
+    assert "null" in w4a16.last_error()
     assert _gemm_ex(M=0) == w4a16.OK                              # empty product: no-op
     assert _gemm_ex(A=8, rw=16, rs=16, out=16) == w4a16.ERR_INVALID  # misaligned A
     assert "aligned" in w4a16.last_error()
@@ -115,16 +117,25 @@ def test_dispatch_table():
 
 
 def test_describe_names_the_launches():
-    """The launch description names kernel instances as profilers print them."""
+    """The launch description names kernel instances as profilers print them
+    (the last two template arguments: SwiGLU epilogue, bf16 activations)."""
     d = w4a16.describe(1, 4096, 28672, swiglu=True)
-    assert d.startswith("decode_coop_kernel<16, 2, ") and d.split(">")[0].endswith("true")
+    assert d.startswith("decode_coop_kernel<16, 2, ") and d.split(">")[0].endswith("true, false")
+    d = w4a16.describe(1, 4096, 28672, swiglu=True, bf16=True)
+    assert d.startswith("decode_coop_kernel<16, 2, ") and d.split(">")[0].endswith("true, true")
     d = w4a16.describe(1, 4096, 4096)
-    assert d.startswith("decode_kernel<16, 1, ") and d.split(">")[0].endswith("false")
-    assert "prefill2_kernel<4, 2, 4, 2, false, true>" in w4a16.describe(4096, 4096, 28672, swiglu=True)
+    assert d.startswith("decode_kernel<16, 1, ") and d.split(">")[0].endswith("false, false")
+    assert "prefill2_kernel<4, 2, 4, 2, false, true, false>" in w4a16.describe(4096, 4096, 28672,
+                                                                               swiglu=True)
+    assert "prefill2_kernel<4, 2, 4, 2, false, true, true>" in w4a16.describe(
+        4096, 4096, 28672, swiglu=True, bf16=True)
     assert w4a16.describe(256, 4096, 28672, swiglu=True).startswith(
-        "prefill2_kernel<2, 2, 4, 2, false, true> workgroups=224 threads=512 ks=1")
-    assert w4a16.describe(64, 14336, 4096).endswith("ks=16; prefill_reduce_kernel<false>")
-    assert w4a16.describe(4096, 4096, 4096, path="dense").startswith("dequant_kernel<false>; ")
+        "prefill2_kernel<2, 2, 4, 2, false, true, false> workgroups=224 threads=512 ks=1")
+    assert w4a16.describe(64, 14336, 4096).endswith("ks=16; prefill_reduce_kernel<false, false>")
+    assert w4a16.describe(4096, 4096, 4096, path="dense").startswith(
+        "dequant_kernel<false, false>; ")
+    assert w4a16.describe(4096, 4096, 4096, path="dense", bf16=True).startswith(
+        "dequant_kernel<false, true>; ")
     assert "row slices" in w4a16.describe(100, 4096, 4096, path="decode")
     L = w4a16.lib()
     import ctypes

@@ -53,6 +53,18 @@ def test_dequant_bit_exact(K, N):
     assert np.array_equal(W16, orc().dequant(packed, scales))
 
 
+@pytest.mark.parametrize("K,N", SMALL)
+def test_dequant_bf16_bit_exact(K, N):
+    """bf16 dequantization (the bf16 reading of the data contract's
+    dequantize) is bit-exact with the oracle, every nibble value and random
+    fp16 scales included."""
+    say("dequant bf16 K=%d N=%d" % (K, N))
+    packed, scales = synth.random_words(K, N, seed=5 * K + N)
+    w = w4a16.repack(to_dev(packed), to_dev(scales.view(np.int16)))
+    Wb = w4a16.dequant(w, bf16=True).view(torch().int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(Wb, orc().dequant_bf16(packed, scales))
+
+
 @pytest.mark.parametrize("K,N", [(8192, 57344), (28672, 8192)])
 def test_pack_and_dequant_full_size_sampled_columns(K, N):
     """Largest config weights: device pack, repack and dequant at full size,
@@ -71,5 +83,7 @@ def test_pack_and_dequant_full_size_sampled_columns(K, N):
     assert np.array_equal(scales.index_select(1, idx).cpu().numpy().view(np.uint16), so)
     W16 = w4a16.dequant(w).index_select(1, idx).cpu().numpy().view(np.uint16)
     assert np.array_equal(W16, orc().dequant(po, so))
+    Wb = w4a16.dequant(w, bf16=True).index_select(1, idx).view(torch().int16).cpu().numpy()
+    assert np.array_equal(Wb.view(np.uint16), orc().dequant_bf16(po, so))
     p2, s2 = w4a16.unrepack(w)
     assert torch().equal(p2, packed) and torch().equal(s2, scales)

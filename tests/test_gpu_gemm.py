@@ -184,24 +184,22 @@ def test_prefill_two_waves_per_simd(monkeypatch, path, M, K, N, swiglu):
     gemm_case(M, K, N, swiglu=swiglu, path=path, seed=M + N)
 
 
-PREFILL2_CONFIGS = [(64, 4, 1, 1), (128, 4, 1, 4), (256, 4, 1, 2), (64, 4, 2, 2), (128, 4, 2, 4),
-                    (256, 4, 2, 1), (64, 4, 1, 8), (256, 2, 1, 1), (256, 2, 1, 4)]
+PREFILL2_CONFIGS = [(64, 1, 1), (128, 1, 4), (256, 1, 2), (64, 2, 2), (128, 2, 4), (256, 2, 1),
+                    (64, 1, 8), (256, 2, 4)]
 
 
-@pytest.mark.parametrize("bm,wnw,tps,ks", PREFILL2_CONFIGS)
+@pytest.mark.parametrize("bm,tps,ks", PREFILL2_CONFIGS)
 @pytest.mark.parametrize("M,K,N,swiglu", [(70, 2048, 1088, False), (200, 2048, 2112, True),
                                           (129, 4096, 4160, False)])
-def test_prefill2_tiles_and_k_slices(monkeypatch, bm, wnw, tps, ks, M, K, N, swiglu):
-    """The 8-wave mainloop at each row tile (64/128/256), 4 or 2 column waves,
-    one or two 64-k tiles per pipeline step, and split K with the FP32 partial
-    reduction; ragged M and N, odd step counts per slice where the split
-    allows."""
+def test_prefill2_tiles_and_k_slices(monkeypatch, bm, tps, ks, M, K, N, swiglu):
+    """The 8-wave mainloop at each row tile (64/128/256), one or two 64-k tiles
+    per pipeline step, and split K with the FP32 partial reduction; ragged M
+    and N, odd step counts per slice where the split allows."""
     monkeypatch.setenv("W4A16_PREFILL_BM", str(bm))
-    monkeypatch.setenv("W4A16_PREFILL_WNW", str(wnw))
     monkeypatch.setenv("W4A16_PREFILL_TPS", str(tps))
     monkeypatch.setenv("W4A16_PREFILL_KS", str(ks))
     d = w4a16.describe(M, K, N, swiglu=swiglu, path="prefill")
-    assert "prefill2_kernel<%d, 2, %d, %d" % (bm // 64, wnw, tps) in d, d
+    assert "prefill2_kernel<%d, 2, 4, %d" % (bm // 64, tps) in d, d
     assert ("ks=%d" % ks) in d, d
     gemm_case(M, K, N, swiglu=swiglu, path="prefill", seed=M + N + bm + ks)
 
@@ -242,3 +240,55 @@ def test_measurement_probes_run():
     T.cuda.synchronize()
     assert fl == 8 * 4 * 16 * 4 * 32768
     assert int(sink.abs().sum()) == 0
+
+
+
+# -- bf16 activations -------------------------------------------------------------
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("M,K,N,swiglu", [(1, 1024, 1064, False), (7, 2048, 2112, True),
+                                          (32, 1152, 4160, False), (70, 2048, 1088, False),
+                                          (300, 1024, 2112, True), (513, 2048, 4096, False)])
+def test_bf16_each_path(path, M, K, N, swiglu):
+    """bf16 activations and output on every path, ragged M and N, with and
+    without the SwiGLU epilogue."""
+    gemm_case(M, K, N, swiglu=swiglu, path=path, seed=M + K + N, bf16=True)
+
+
+@pytest.mark.parametrize("wc,wk,ks", [(2, 4, 1), (1, 4, 1), (2, 2, 2), (4, 1, 1)])
+@pytest.mark.parametrize("M", [1, 16, 32])
+def test_bf16_decode_cooperative(monkeypatch, wc, wk, ks, M):
+    monkeypatch.setenv("W4A16_DECODE_COOP", "1")
+    monkeypatch.setenv("W4A16_COOP_WC", str(wc))
+    monkeypatch.setenv("W4A16_COOP_WK", str(wk))
+    monkeypatch.setenv("W4A16_COOP_KS", str(ks))
+    gemm_case(M, 2048, 2112, swiglu=True, path="decode", seed=wc + wk + ks + M, bf16=True)
+
+
+@pytest.mark.parametrize("bm,ks", [(64, 1), (128, 4), (256, 2)])
+def test_bf16_prefill_tiles(monkeypatch, bm, ks):
+    monkeypatch.setenv("W4A16_PREFILL_BM", str(bm))
+    monkeypatch.setenv("W4A16_PREFILL_KS", str(ks))
+    gemm_case(200, 2048, 2112, swiglu=True, path="prefill", seed=bm + ks, bf16=True)
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_bf16_bit_exact_integer_inputs(path):
+    """Ternary activations and power-of-two scales make every weight, product
+    and partial sum exact in bf16 / FP32, so the bf16 output is the oracle's
+    sum rounded once: bit-exact."""
+    from gpuhelp import bf16_dev, bf16_out
+    for M, K, N in [(5, 2048, 1088), (96, 2048, 2048)]:
+        W = synth.grid_weights(K, N, p=4, seed=M)
+        A = synth.ternary_activations(M, K, density=1.0, seed=M)
+        Ab = orc().f64_to_bf16(A.astype(np.float64))
+        w = w4a16.load_weight(W)
+        out = bf16_out(w4a16.gemm(bf16_dev(Ab), w, path=path))
+        packed_o, s16_o = orc().quantize_pack(W)
+        C = orc().gemm_bf16_f64(Ab, packed_o, s16_o)
+        assert np.array_equal(out, orc().f64_to_bf16(C)), (path, M, K, N)
+
+
+def test_bf16_transition_with_outliers():
+    """1% of K-channels scaled by 20 (the transition batches' activations)."""
+    gemm_case(128, 4096, 4096, path="auto", seed=3, outliers=True, bf16=True)

@@ -37,6 +37,12 @@ MUTANTS = [
      "double up = C[m * N + j];\n            double g = C[m * N + I + j];"),
     ("silu_sign", "g / (1.0 + exp(-g)) * up", "g / (1.0 + exp(g)) * up"),
     ("scale_clamp_dropped_zero_group", "if (s < 1e-8f)\n                s = 1e-8f;", "if (s < 1e-8f)\n                s = 1.0f;"),
+    ("bf16_ties_away", "double n = nearbyint(a / ldexp(1.0, e - 7));", "double n = round(a / ldexp(1.0, e - 7));"),
+    ("bf16_decode_bias", "v = ldexp((double)(128 + f), e - 134);", "v = ldexp((double)(128 + f), e - 133);"),
+    ("bf16_truncate", "double n = nearbyint(a / ldexp(1.0, e - 7));", "double n = floor(a / ldexp(1.0, e - 7));"),
+    ("bf16_gemm_unrounded_weight", "double w = oracle_bf16_to_f64(\n                        oracle_f64_to_bf16(exact_weight(packed, s16, N, G, k, n)));",
+     "double w = exact_weight(packed, s16, N, G, k, n);"),
+    ("bf16_gemm_fp16_activations", "double a = oracle_bf16_to_f64(Ab[m * K + k]);", "double a = oracle_f16_to_f64(Ab[m * K + k]);"),
 ]
 
 

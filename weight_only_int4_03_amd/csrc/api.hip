@@ -129,6 +129,7 @@ int run_gemm(const uint16_t *A, int64_t M, int64_t K, const void *rw, const void
              int G, uint16_t *out, int flags, void *workspace, int64_t ws_bytes,
              hipStream_t stream) {
   const char *who = (flags & W4A16_FLAG_SWIGLU) ? "w4a16_gemm_swiglu" : "w4a16_gemm";
+  const bool bf16 = (flags & W4A16_FLAG_BF16) != 0;
   int rc = check_gpu_shape(K, N, G, who);
   if (rc != W4A16_OK) return rc;
   if (M < 0) return fail(W4A16_ERR_INVALID, "%s: M must be >= 0", who);
@@ -145,7 +146,7 @@ int run_gemm(const uint16_t *A, int64_t M, int64_t K, const void *rw, const void
   if (path < W4A16_PATH_DECODE || path > W4A16_PATH_DENSE)
     return fail(W4A16_ERR_INVALID, "%s: unknown path %d", who, path);
 
-  Problem p{A, M, K, N, rw, rs, out, swiglu};
+  Problem p{A, M, K, N, rw, rs, out, swiglu, bf16};
   const int64_t need = workspace_for(path, p);
   void *ws = workspace;
   if (need > 0) {
@@ -317,15 +318,26 @@ int w4a16_unrepack(const void *rw_d, const void *rs_d, int64_t K, int64_t N, int
   return e == hipSuccess ? W4A16_OK : hip_fail(e, "w4a16_unrepack");
 }
 
+static int dequant_common(const void *rw_d, const void *rs_d, int64_t K, int64_t N, int G,
+                          uint16_t *W_d, bool bf16, hipStream_t stream, const char *who) {
+  int rc = check_gpu_shape(K, N, G, who);
+  if (rc != W4A16_OK) return rc;
+  if (!rw_d || !rs_d || !W_d) return fail(W4A16_ERR_INVALID, "%s: null pointer", who);
+  if (!aligned16(rw_d) || !aligned16(rs_d))
+    return fail(W4A16_ERR_INVALID, "%s: repacked buffers must be 16-byte aligned", who);
+  hipError_t e = launch_dequant_canonical(rw_d, rs_d, K, N, bf16, W_d, stream);
+  return e == hipSuccess ? W4A16_OK : hip_fail(e, who);
+}
+
 int w4a16_dequant(const void *rw_d, const void *rs_d, int64_t K, int64_t N, int G,
                   uint16_t *W16_d, w4a16_stream_t stream) {
-  int rc = check_gpu_shape(K, N, G, "w4a16_dequant");
-  if (rc != W4A16_OK) return rc;
-  if (!rw_d || !rs_d || !W16_d) return fail(W4A16_ERR_INVALID, "w4a16_dequant: null pointer");
-  if (!aligned16(rw_d) || !aligned16(rs_d))
-    return fail(W4A16_ERR_INVALID, "w4a16_dequant: repacked buffers must be 16-byte aligned");
-  hipError_t e = launch_dequant_canonical(rw_d, rs_d, K, N, W16_d, (hipStream_t)stream);
-  return e == hipSuccess ? W4A16_OK : hip_fail(e, "w4a16_dequant");
+  return dequant_common(rw_d, rs_d, K, N, G, W16_d, false, (hipStream_t)stream, "w4a16_dequant");
+}
+
+int w4a16_dequant_bf16(const void *rw_d, const void *rs_d, int64_t K, int64_t N, int G,
+                       uint16_t *Wb_d, w4a16_stream_t stream) {
+  return dequant_common(rw_d, rs_d, K, N, G, Wb_d, true, (hipStream_t)stream,
+                        "w4a16_dequant_bf16");
 }
 
 int w4a16_gemm(const uint16_t *A_d, int64_t M, int64_t K, const void *rw_d, const void *rs_d,
@@ -343,7 +355,7 @@ int w4a16_gemm_swiglu(const uint16_t *A_d, int64_t M, int64_t K, const void *rw_
 int w4a16_gemm_ex(const uint16_t *A_d, int64_t M, int64_t K, const void *rw_d, const void *rs_d,
                   int64_t N, int G, uint16_t *out_d, int flags, void *workspace_d,
                   int64_t workspace_bytes, w4a16_stream_t stream) {
-  if (flags & ~(0xF | W4A16_FLAG_SWIGLU))
+  if (flags & ~(0xF | W4A16_FLAG_SWIGLU | W4A16_FLAG_BF16))
     return fail(W4A16_ERR_INVALID, "w4a16_gemm_ex: unknown flags 0x%x", flags);
   return run_gemm(A_d, M, K, rw_d, rs_d, N, G, out_d, flags, workspace_d, workspace_bytes,
                   (hipStream_t)stream);
@@ -355,7 +367,8 @@ int64_t w4a16_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N, int G, int f
   if (M <= 0) return 0;
   int path = flags & 0xF;
   if (path == W4A16_PATH_AUTO) path = select_path(M, K, N);
-  Problem p{nullptr, M, K, N, nullptr, nullptr, nullptr, (flags & W4A16_FLAG_SWIGLU) != 0};
+  Problem p{nullptr, M, K, N, nullptr, nullptr, nullptr, (flags & W4A16_FLAG_SWIGLU) != 0,
+            (flags & W4A16_FLAG_BF16) != 0};
   return workspace_for(path, p);
 }
 
@@ -364,7 +377,7 @@ int w4a16_describe(int64_t M, int64_t K, int64_t N, int G, int flags, char *buf,
   if (rc != W4A16_OK) return rc;
   if (M < 1) return fail(W4A16_ERR_INVALID, "w4a16_describe: M must be >= 1");
   if (buf == nullptr || len < 1) return fail(W4A16_ERR_INVALID, "w4a16_describe: no buffer");
-  if (flags & ~(0xF | W4A16_FLAG_SWIGLU))
+  if (flags & ~(0xF | W4A16_FLAG_SWIGLU | W4A16_FLAG_BF16))
     return fail(W4A16_ERR_INVALID, "w4a16_describe: unknown flags 0x%x", flags);
   const bool swiglu = (flags & W4A16_FLAG_SWIGLU) != 0;
   if (swiglu && N % 64 != 0)
@@ -374,7 +387,7 @@ int w4a16_describe(int64_t M, int64_t K, int64_t N, int G, int flags, char *buf,
   if (path == W4A16_PATH_AUTO) path = select_path(M, K, N);
   if (path < W4A16_PATH_DECODE || path > W4A16_PATH_DENSE)
     return fail(W4A16_ERR_INVALID, "w4a16_describe: unknown path %d", path);
-  Problem p{nullptr, M, K, N, nullptr, nullptr, nullptr, swiglu};
+  Problem p{nullptr, M, K, N, nullptr, nullptr, nullptr, swiglu, (flags & W4A16_FLAG_BF16) != 0};
   char tmp[512];
   int k;
   if (path == W4A16_PATH_DECODE) {

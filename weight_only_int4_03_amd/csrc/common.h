@@ -32,6 +32,8 @@ constexpr int kTileWords = 256;
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t uint4_t __attribute__((ext_vector_type(4)));
@@ -97,6 +99,35 @@ struct Dequant {
     const half2_t q2 = half2_t{v[4], v[5]} * s2, q3 = half2_t{v[6], v[7]} * s2;
     return half8_t{q0[0], q0[1], q1[0], q1[1], q2[0], q2[1], q3[0], q3[1]};
   }
+
+  // bf16 activations.  The dequantized weight is then bf16((u - 8) * s): the
+  // exact product of u - 8 and the fp16 scale, rounded once to bf16.  The
+  // magic-number pairs (1024 + u, or 1024 + 16u) go straight into a
+  // mixed-precision FMA (fp16 x fp32 + fp32 -> fp32, v_fma_mix_f32) with
+  // per-column constants of the group: (1024 + u) s - 1032 s, and
+  // (1024 + 16u) (s / 16) - 72 s.  Every product and constant has at most 22
+  // significant bits and the sum is (u - 8) s itself, so the FMA is exact; one
+  // v_cvt_pk_bf16_f32 per pair then rounds.  17 VALU instructions per word.
+  struct BScale {
+    float s, c_lo, s_hi, c_hi;
+    __device__ __forceinline__ explicit BScale(uint16_t s16) {
+      s = (float)bitcast<_Float16>(s16);
+      c_lo = -1032.0f * s;
+      s_hi = s * 0.0625f;
+      c_hi = -72.0f * s;
+    }
+  };
+  __device__ __forceinline__ bf16x8_t scaled_bf16(uint32_t w, const BScale &b) const {
+    const uint32_t t = w >> 8;
+    const half2_t x0 = bitcast<half2_t>((w & mask_lo) | magic);
+    const half2_t x1 = bitcast<half2_t>((w & mask_hi) | magic);
+    const half2_t x2 = bitcast<half2_t>((t & mask_lo) | magic);
+    const half2_t x3 = bitcast<half2_t>((t & mask_hi) | magic);
+    auto lo = [&](_Float16 x) { return (__bf16)__builtin_fmaf((float)x, b.s, b.c_lo); };
+    auto hi = [&](_Float16 x) { return (__bf16)__builtin_fmaf((float)x, b.s_hi, b.c_hi); };
+    return bf16x8_t{lo(x0[0]), lo(x0[1]), hi(x1[0]), hi(x1[1]),
+                    lo(x2[0]), lo(x2[1]), hi(x3[0]), hi(x3[1])};
+  }
 };
 
 __device__ __forceinline__ uint4_t load_nt(const uint4_t *p) {
@@ -117,6 +148,46 @@ __device__ __forceinline__ uint16_t to_half_bits(float v) {
   return bitcast<uint16_t>((_Float16)v);
 }
 
+// Output element bits: fp16, or bf16 (round to nearest even) for bf16
+// activations.
+template <bool BF>
+__device__ __forceinline__ uint16_t to_out_bits(float v) {
+  if constexpr (BF)
+    return bitcast<uint16_t>((__bf16)v);
+  else
+    return bitcast<uint16_t>((_Float16)v);
+}
+
+// A packed pair of output elements (lo in the low half).
+template <bool BF>
+__device__ __forceinline__ uint32_t pack_out2(float lo, float hi) {
+  if constexpr (BF)
+    return bitcast<uint32_t>(bf16x2_t{(__bf16)lo, (__bf16)hi});
+  else
+    return bitcast<uint32_t>(half2_t{(_Float16)lo, (_Float16)hi});
+}
+
+// One MFMA step, fp16 or bf16 operands (raw 16-byte vectors of 8 elements:
+// x is the instruction's first operand, y its second).
+template <bool BF>
+__device__ __forceinline__ float16_t mfma32(uint4_t x, uint4_t y, float16_t c) {
+  if constexpr (BF)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(bitcast<bf16x8_t>(x), bitcast<bf16x8_t>(y), c,
+                                                   0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(bitcast<half8_t>(x), bitcast<half8_t>(y), c, 0,
+                                                  0, 0);
+}
+template <bool BF>
+__device__ __forceinline__ float4_t mfma16(uint4_t x, uint4_t y, float4_t c) {
+  if constexpr (BF)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8_t>(x), bitcast<bf16x8_t>(y), c,
+                                                   0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<half8_t>(x), bitcast<half8_t>(y), c, 0,
+                                                  0, 0);
+}
+
 // ---------------------------------------------------------------------------
 // Host-side launch descriptions (defined in decode.hip / prefill.hip /
 // format.hip, called from api.hip).
@@ -128,6 +199,7 @@ struct Problem {
   const void *rs;
   uint16_t *out;   // C [M,N] or Z [M,N/2]
   bool swiglu;
+  bool bf16;       // A and the output are bf16 (else fp16)
 };
 
 hipError_t launch_pack(const float *W, int64_t K, int64_t N, int32_t *packed, uint16_t *scales,
@@ -137,9 +209,9 @@ hipError_t launch_repack(const int32_t *packed, const uint16_t *scales, int64_t 
 hipError_t launch_unrepack(const void *rw, const void *rs, int64_t K, int64_t N, int32_t *packed,
                            uint16_t *scales, hipStream_t s);
 hipError_t launch_dequant_canonical(const void *rw, const void *rs, int64_t K, int64_t N,
-                                    uint16_t *W16, hipStream_t s);
+                                    bool bf16, uint16_t *W, hipStream_t s);
 hipError_t launch_dequant_fragment(const void *rw, const void *rs, int64_t K, int64_t N,
-                                   uint16_t *W16f, hipStream_t s);
+                                   bool bf16, uint16_t *Wf, hipStream_t s);
 
 // Decode path: workspace bytes (split-K partials), the launch, and a text
 // description of the launch (kernel instances and grid).

@@ -49,7 +49,7 @@ struct DecodeFrag {
   uint16_t sc[SPW][MT == 16 ? 2 : 1];
 };
 
-template <int MT, int SPW, int WAVES, int D, int RPL, bool SWIGLU>
+template <int MT, int SPW, int WAVES, int D, int RPL, bool SWIGLU, bool BF>
 __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
   static_assert(MT == 16 ? (RPL >= 1 && RPL <= 4) : RPL == 16, "rows per lane");
   extern __shared__ float lds[];  // [WAVES][SPW][M][32]
@@ -134,6 +134,32 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
     for (int part = 0; part < NPART; ++part) acc[s][part] = acc_t{};
 
   auto compute = [&](const Frag &f) {
+    if constexpr (BF) {
+      // bf16: the weights are scaled (and rounded to bf16) before the MFMA,
+      // which then accumulates straight into the FP32 accumulator.
+#pragma unroll
+      for (int s = 0; s < SPW; ++s) {
+#pragma unroll
+        for (int part = 0; part < NPART; ++part) {
+          const Dequant::BScale bs(f.sc[s][part]);
+          if constexpr (MT == 16) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              acc[s][part] = mfma16<true>(
+                  f.a[j], bitcast<uint4_t>(dq.scaled_bf16(f.b[s][part][j], bs)), acc[s][part]);
+          } else {
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+                acc[s][part] = mfma32<true>(f.a[4 * x + j],
+                                            bitcast<uint4_t>(dq.scaled_bf16(f.b[s][x][j], bs)),
+                                            acc[s][part]);
+          }
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int s = 0; s < SPW; ++s) {
 #pragma unroll
@@ -218,7 +244,8 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
 
   if (p.KS == 1) {
     const int E = SH * M * 32;
-    for (int e = threadIdx.x; e < E; e += nthreads) decode_epilogue<SPW, SWIGLU>(p, sg, e, wave_sum);
+    for (int e = threadIdx.x; e < E; e += nthreads)
+      decode_epilogue<SPW, SWIGLU, BF>(p, sg, e, wave_sum);
     return;
   }
   float *mine = p.ws + ((int64_t)sg * p.KS + split) * tileE;
@@ -227,7 +254,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
 
 // Second stage for KS > 1: one thread per output element sums the KS partial
 // tiles of its strip group in split order, then runs the epilogue.
-template <int SPW, bool SWIGLU>
+template <int SPW, bool SWIGLU, bool BF>
 __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs p) {
   constexpr int SH = SWIGLU ? SPW / 2 : SPW;
   const int E = SH * p.M * 32;
@@ -236,7 +263,7 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs p) {
   const int sg = (int)(idx / E), e = (int)(idx - (int64_t)sg * E);
   const int tileE = SPW * p.M * 32;
   const float *all = p.ws + (int64_t)sg * p.KS * tileE;
-  decode_epilogue<SPW, SWIGLU>(p, sg, e, [&](int x) {
+  decode_epilogue<SPW, SWIGLU, BF>(p, sg, e, [&](int x) {
     float v = 0.0f;
     for (int sp = 0; sp < p.KS; ++sp) v += all[(int64_t)sp * tileE + x];
     return v;
@@ -288,25 +315,25 @@ static DecodeConfig decode_config(const Problem &p) {
 
 int decode_describe(const Problem &p, char *buf, size_t n) {
   int WC, WK, KS;
+  const char *sw = p.swiglu ? "true" : "false", *bf = p.bf16 ? "true" : "false";
   if (coop_config(p, WC, WK, KS)) {
     const int mt = p.M <= 16 ? 16 : 32;
     const int rpl = mt == 16 ? (p.M == 1 ? 1 : 4) : 16;
     const int spw = p.swiglu ? 2 : 1;
     const int nsg = (int)(p.swiglu ? (p.N / 2 / kStrip) : ceil_div(p.N, kStrip));
-    const char *sw = p.swiglu ? "true" : "false";
-    int k = snprintf(buf, n, "decode_coop_kernel<%d, %d, %d, %d, %d, %s> workgroups=%d threads=%d ks=%d",
-                     mt, spw, WC, WK, rpl, sw, (int)ceil_div(nsg, WC) * KS, WC * WK * 64, KS);
+    int k = snprintf(buf, n,
+                     "decode_coop_kernel<%d, %d, %d, %d, %d, %s, %s> workgroups=%d threads=%d ks=%d",
+                     mt, spw, WC, WK, rpl, sw, bf, (int)ceil_div(nsg, WC) * KS, WC * WK * 64, KS);
     if (KS > 1 && k > 0 && (size_t)k < n)
-      k += snprintf(buf + k, n - k, "; decode_reduce_kernel<%d, %s>", spw, sw);
+      k += snprintf(buf + k, n - k, "; decode_reduce_kernel<%d, %s, %s>", spw, sw, bf);
     return k;
   }
   const DecodeConfig c = decode_config(p);
   const int rpl = c.MT == 16 ? (p.M == 1 ? 1 : 4) : 16;
-  const char *sw = p.swiglu ? "true" : "false";
-  int k = snprintf(buf, n, "decode_kernel<%d, %d, %d, %d, %d, %s> workgroups=%d threads=%d ks=%d",
-                   c.MT, c.SPW, c.WAVES, c.D, rpl, sw, c.nsg * c.KS, c.WAVES * 64, c.KS);
+  int k = snprintf(buf, n, "decode_kernel<%d, %d, %d, %d, %d, %s, %s> workgroups=%d threads=%d ks=%d",
+                   c.MT, c.SPW, c.WAVES, c.D, rpl, sw, bf, c.nsg * c.KS, c.WAVES * 64, c.KS);
   if (c.KS > 1 && k > 0 && (size_t)k < n)
-    k += snprintf(buf + k, n - k, "; decode_reduce_kernel<%d, %s>", c.SPW, sw);
+    k += snprintf(buf + k, n - k, "; decode_reduce_kernel<%d, %s, %s>", c.SPW, sw, bf);
   return k;
 }
 
@@ -322,23 +349,36 @@ int64_t decode_workspace_bytes(const Problem &p) {
   return (int64_t)c.nsg * c.KS * c.SPW * p.M * 32 * (int64_t)sizeof(float);
 }
 
-template <int MT, int SPW, int WAVES, int D, int RPL, bool SWIGLU>
+template <int MT, int SPW, int WAVES, int D, int RPL, bool SWIGLU, bool BF>
 static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t s) {
   const size_t lds = (size_t)WAVES * SPW * a.M * 32 * sizeof(float);
-  hipLaunchKernelGGL((decode_kernel<MT, SPW, WAVES, D, RPL, SWIGLU>), dim3(a.nsg * a.KS),
+  hipLaunchKernelGGL((decode_kernel<MT, SPW, WAVES, D, RPL, SWIGLU, BF>), dim3(a.nsg * a.KS),
                      dim3(WAVES * 64), lds, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.KS == 1) return e;
-  return launch_decode_reduce(a, SWIGLU, s);
+  return launch_decode_reduce(a, SWIGLU, BF, s);
 }
 
-template <int MT, int SPW, int RPL, bool SWIGLU>
+template <int MT, int SPW, int RPL, bool SWIGLU, bool BF>
 static hipError_t launch_decode_w(const DecodeArgs &a, const DecodeConfig &c, hipStream_t s) {
   if (c.D == 4)
-    return c.WAVES == 8 ? launch_decode_t<MT, SPW, 8, 4, RPL, SWIGLU>(a, s)
-                        : launch_decode_t<MT, SPW, 4, 4, RPL, SWIGLU>(a, s);
-  return c.WAVES == 8 ? launch_decode_t<MT, SPW, 8, 2, RPL, SWIGLU>(a, s)
-                      : launch_decode_t<MT, SPW, 4, 2, RPL, SWIGLU>(a, s);
+    return c.WAVES == 8 ? launch_decode_t<MT, SPW, 8, 4, RPL, SWIGLU, BF>(a, s)
+                        : launch_decode_t<MT, SPW, 4, 4, RPL, SWIGLU, BF>(a, s);
+  return c.WAVES == 8 ? launch_decode_t<MT, SPW, 8, 2, RPL, SWIGLU, BF>(a, s)
+                      : launch_decode_t<MT, SPW, 4, 2, RPL, SWIGLU, BF>(a, s);
+}
+
+template <bool BF>
+static hipError_t launch_decode_bf(const Problem &p, const DecodeArgs &a, const DecodeConfig &c,
+                                   hipStream_t s) {
+  if (c.MT == 16 && p.M == 1)
+    return p.swiglu ? launch_decode_w<16, 2, 1, true, BF>(a, c, s)
+                    : launch_decode_w<16, 1, 1, false, BF>(a, c, s);
+  if (c.MT == 16)
+    return p.swiglu ? launch_decode_w<16, 2, 4, true, BF>(a, c, s)
+                    : launch_decode_w<16, 1, 4, false, BF>(a, c, s);
+  return p.swiglu ? launch_decode_w<32, 2, 16, true, BF>(a, c, s)
+                  : launch_decode_w<32, 1, 16, false, BF>(a, c, s);
 }
 
 DecodeArgs decode_args(const Problem &p, int KS, void *workspace) {
@@ -363,14 +403,20 @@ DecodeArgs decode_args(const Problem &p, int KS, void *workspace) {
   return a;
 }
 
-hipError_t launch_decode_reduce(const DecodeArgs &a, bool swiglu, hipStream_t s) {
+hipError_t launch_decode_reduce(const DecodeArgs &a, bool swiglu, bool bf16, hipStream_t s) {
   const int64_t total = (int64_t)a.nsg * a.M * 32;
-  if (swiglu)
-    hipLaunchKernelGGL((decode_reduce_kernel<2, true>), dim3((unsigned)ceil_div(total, 256)),
-                       dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((decode_reduce_kernel<1, false>), dim3((unsigned)ceil_div(total, 256)),
-                       dim3(256), 0, s, a);
+  const dim3 grid((unsigned)ceil_div(total, 256));
+  if (swiglu) {
+    if (bf16)
+      hipLaunchKernelGGL((decode_reduce_kernel<2, true, true>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((decode_reduce_kernel<2, true, false>), grid, dim3(256), 0, s, a);
+  } else {
+    if (bf16)
+      hipLaunchKernelGGL((decode_reduce_kernel<1, false, true>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((decode_reduce_kernel<1, false, false>), grid, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 
@@ -380,14 +426,7 @@ hipError_t launch_decode(const Problem &p, void *workspace, hipStream_t s) {
   const DecodeConfig c = decode_config(p);
   DecodeArgs a = decode_args(p, c.KS, workspace);
   if (c.KS > 1 && workspace == nullptr) return hipErrorInvalidValue;
-  if (c.MT == 16 && p.M == 1)
-    return p.swiglu ? launch_decode_w<16, 2, 1, true>(a, c, s)
-                    : launch_decode_w<16, 1, 1, false>(a, c, s);
-  if (c.MT == 16)
-    return p.swiglu ? launch_decode_w<16, 2, 4, true>(a, c, s)
-                    : launch_decode_w<16, 1, 4, false>(a, c, s);
-  return p.swiglu ? launch_decode_w<32, 2, 16, true>(a, c, s)
-                  : launch_decode_w<32, 1, 16, false>(a, c, s);
+  return p.bf16 ? launch_decode_bf<true>(p, a, c, s) : launch_decode_bf<false>(p, a, c, s);
 }
 
 }  // namespace w4a16

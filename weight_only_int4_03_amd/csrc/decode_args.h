@@ -24,7 +24,7 @@ struct DecodeArgs {
 // Epilogue of one element e of strip group sg's tile (tile element order
 // [s][m][c]; for SwiGLU e covers the gate half only and e + SH*M*32 is the
 // matching up element).  value_at(e) is the complete FP32 dot product.
-template <int SPW, bool SWIGLU, typename F>
+template <int SPW, bool SWIGLU, bool BF, typename F>
 __device__ __forceinline__ void decode_epilogue(const DecodeArgs &p, int sg, int e, F value_at) {
   constexpr int SH = SWIGLU ? SPW / 2 : SPW;
   const int M = p.M;
@@ -34,11 +34,11 @@ __device__ __forceinline__ void decode_epilogue(const DecodeArgs &p, int sg, int
     const int gstrip = sg * SH + s;
     if (gstrip < p.valid_strips) {
       const float gv = value_at(e), uv = value_at(e + SH * M * 32);
-      p.out[(int64_t)m * p.ldo + gstrip * 32 + c] = to_half_bits(silu_mul(gv, uv));
+      p.out[(int64_t)m * p.ldo + gstrip * 32 + c] = to_out_bits<BF>(silu_mul(gv, uv));
     }
   } else {
     const int col = (sg * SPW + s) * 32 + c;
-    if (col < p.N) p.out[(int64_t)m * p.ldo + col] = to_half_bits(value_at(e));
+    if (col < p.N) p.out[(int64_t)m * p.ldo + col] = to_out_bits<BF>(value_at(e));
   }
 }
 
@@ -48,7 +48,7 @@ DecodeArgs decode_args(const Problem &p, int KS, void *workspace);
 
 // Second stage of a split-K decode launch: sums the KS partial tiles of each
 // strip group in split order and runs the epilogue.
-hipError_t launch_decode_reduce(const DecodeArgs &a, bool swiglu, hipStream_t s);
+hipError_t launch_decode_reduce(const DecodeArgs &a, bool swiglu, bool bf16, hipStream_t s);
 
 // Cooperative decode kernel (decode_coop.hip): configuration from the
 // environment (W4A16_COOP_WC, W4A16_COOP_WK, W4A16_COOP_KS); false if the

@@ -36,7 +36,7 @@ struct CoopFrag {
   uint4_t b[SPW][2];  // weight vectors of the wave's strips for one group
 };
 
-template <int MT, int SPW, int WC, int WK, int RPL, bool SWIGLU>
+template <int MT, int SPW, int WC, int WK, int RPL, bool SWIGLU, bool BF>
 __global__ __launch_bounds__(WC * WK * 64) void decode_coop_kernel(DecodeArgs p) {
   constexpr int NW = WC * WK, NT = NW * 64, D = 2;
   constexpr int SH = SWIGLU ? SPW / 2 : SPW;
@@ -184,6 +184,32 @@ __global__ __launch_bounds__(WC * WK * 64) void decode_coop_kernel(DecodeArgs p)
 #pragma unroll
         for (int j = 0; j < 4; ++j) a[4 * x + j] = *(const uint4_t *)(ab + x * 128 + j * 16);
     }
+    if constexpr (BF) {
+      // bf16: weights scaled and rounded before the MFMA (see Dequant).
+#pragma unroll
+      for (int s = 0; s < SPW; ++s) {
+#pragma unroll
+        for (int part = 0; part < NPART; ++part) {
+          const int col = MT == 16 ? 16 * part + c16 : c32;
+          const Dequant::BScale bs(sb[((wc * SPW + s) * 32 + col) * WK + wk]);
+          if constexpr (MT == 16) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              acc[s][part] = mfma16<true>(
+                  a[j], bitcast<uint4_t>(dq.scaled_bf16(f.b[s][part][j], bs)), acc[s][part]);
+          } else {
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+                acc[s][part] = mfma32<true>(a[4 * x + j],
+                                            bitcast<uint4_t>(dq.scaled_bf16(f.b[s][x][j], bs)),
+                                            acc[s][part]);
+          }
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int s = 0; s < SPW; ++s) {
 #pragma unroll
@@ -276,7 +302,7 @@ __global__ __launch_bounds__(WC * WK * 64) void decode_coop_kernel(DecodeArgs p)
       const int wcc = x / E, e = x - wcc * E;
       const int sgg = cg * WC + wcc;
       if (sgg < p.nsg)
-        decode_epilogue<SPW, SWIGLU>(p, sgg, e, [&](int y) { return sum_wk(wcc, y); });
+        decode_epilogue<SPW, SWIGLU, BF>(p, sgg, e, [&](int y) { return sum_wk(wcc, y); });
     }
     return;
   }
@@ -297,23 +323,36 @@ size_t coop_lds_bytes(int M, int WC, int WK, int SPW) {
   return stage > red ? stage : red;
 }
 
-template <int MT, int SPW, int WC, int WK, int RPL, bool SWIGLU>
+template <int MT, int SPW, int WC, int WK, int RPL, bool SWIGLU, bool BF>
 static hipError_t launch_coop_t(const DecodeArgs &a, hipStream_t s) {
   const size_t lds = coop_lds_bytes(a.M, WC, WK, SPW);
   const int ncg = (a.nsg + WC - 1) / WC;
-  hipLaunchKernelGGL((decode_coop_kernel<MT, SPW, WC, WK, RPL, SWIGLU>), dim3(ncg * a.KS),
+  hipLaunchKernelGGL((decode_coop_kernel<MT, SPW, WC, WK, RPL, SWIGLU, BF>), dim3(ncg * a.KS),
                      dim3(WC * WK * 64), lds, s, a);
   return hipGetLastError();
 }
 
-template <int MT, int SPW, int RPL, bool SWIGLU>
+template <int MT, int SPW, int RPL, bool SWIGLU, bool BF>
 static hipError_t launch_coop_w(const DecodeArgs &a, int WC, int WK, hipStream_t s) {
-  if (WC == 4 && WK == 1) return launch_coop_t<MT, SPW, 4, 1, RPL, SWIGLU>(a, s);
-  if (WC == 8 && WK == 1) return launch_coop_t<MT, SPW, 8, 1, RPL, SWIGLU>(a, s);
-  if (WC == 2 && WK == 2) return launch_coop_t<MT, SPW, 2, 2, RPL, SWIGLU>(a, s);
-  if (WC == 4 && WK == 2) return launch_coop_t<MT, SPW, 4, 2, RPL, SWIGLU>(a, s);
-  if (WC == 2 && WK == 4) return launch_coop_t<MT, SPW, 2, 4, RPL, SWIGLU>(a, s);
-  return launch_coop_t<MT, SPW, 1, 4, RPL, SWIGLU>(a, s);
+  if (WC == 4 && WK == 1) return launch_coop_t<MT, SPW, 4, 1, RPL, SWIGLU, BF>(a, s);
+  if (WC == 8 && WK == 1) return launch_coop_t<MT, SPW, 8, 1, RPL, SWIGLU, BF>(a, s);
+  if (WC == 2 && WK == 2) return launch_coop_t<MT, SPW, 2, 2, RPL, SWIGLU, BF>(a, s);
+  if (WC == 4 && WK == 2) return launch_coop_t<MT, SPW, 4, 2, RPL, SWIGLU, BF>(a, s);
+  if (WC == 2 && WK == 4) return launch_coop_t<MT, SPW, 2, 4, RPL, SWIGLU, BF>(a, s);
+  return launch_coop_t<MT, SPW, 1, 4, RPL, SWIGLU, BF>(a, s);
+}
+
+template <bool BF>
+static hipError_t launch_coop_bf(const Problem &p, const DecodeArgs &a, int WC, int WK,
+                                 hipStream_t s) {
+  if (p.M == 1)
+    return p.swiglu ? launch_coop_w<16, 2, 1, true, BF>(a, WC, WK, s)
+                    : launch_coop_w<16, 1, 1, false, BF>(a, WC, WK, s);
+  if (p.M <= 16)
+    return p.swiglu ? launch_coop_w<16, 2, 4, true, BF>(a, WC, WK, s)
+                    : launch_coop_w<16, 1, 4, false, BF>(a, WC, WK, s);
+  return p.swiglu ? launch_coop_w<32, 2, 16, true, BF>(a, WC, WK, s)
+                  : launch_coop_w<32, 1, 16, false, BF>(a, WC, WK, s);
 }
 
 // -1 if unset, else the integer value.
@@ -377,19 +416,10 @@ hipError_t launch_decode_coop(const Problem &p, void *workspace, int WC, int WK,
                               hipStream_t s) {
   DecodeArgs a = decode_args(p, KS, workspace);
   if (KS > 1 && workspace == nullptr) return hipErrorInvalidValue;
-  hipError_t e;
-  const bool m1 = p.M == 1, mt16 = p.M <= 16;
-  if (mt16 && m1)
-    e = p.swiglu ? launch_coop_w<16, 2, 1, true>(a, WC, WK, s)
-                 : launch_coop_w<16, 1, 1, false>(a, WC, WK, s);
-  else if (mt16)
-    e = p.swiglu ? launch_coop_w<16, 2, 4, true>(a, WC, WK, s)
-                 : launch_coop_w<16, 1, 4, false>(a, WC, WK, s);
-  else
-    e = p.swiglu ? launch_coop_w<32, 2, 16, true>(a, WC, WK, s)
-                 : launch_coop_w<32, 1, 16, false>(a, WC, WK, s);
+  const hipError_t e =
+      p.bf16 ? launch_coop_bf<true>(p, a, WC, WK, s) : launch_coop_bf<false>(p, a, WC, WK, s);
   if (e != hipSuccess || KS == 1) return e;
-  return launch_decode_reduce(a, p.swiglu, s);
+  return launch_decode_reduce(a, p.swiglu, p.bf16, s);
 }
 
 }  // namespace w4a16

@@ -151,13 +151,15 @@ hipError_t launch_unrepack(const void *rw, const void *rs, int64_t K, int64_t N,
 // ---------------------------------------------------------------------------
 // Dequantize.  One thread per repacked lane vector (four words = 32 weights of
 // one column).  Each weight is fp16((q - 8) * s): the fp16 product of the
-// exact value q - 8 and the fp16 scale rounds the exact product once.
+// exact value q - 8 and the fp16 scale rounds the exact product once.  With
+// BF the weights are bf16((q - 8) * s), the exact product rounded once to
+// bf16 (the operand the bf16-activation kernels feed their MFMAs).
 //
 // CANONICAL writes W16 [K, N] row-major (the definition's layout).
 // Otherwise the output is fragment-ordered for the dense GEMM: the lane
 // vector (t, q, l) expands to four 16-byte runs at uint4 index
 // ((t*KT + q)*64 + l)*4 + j, run j holding k = 64q + 32h + 8j .. +7.
-template <bool CANONICAL>
+template <bool CANONICAL, bool BF>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint4_t *__restrict__ rw,
                                                       const uint16_t *__restrict__ rs,
                                                       uint16_t *__restrict__ W16, int64_t N,
@@ -170,43 +172,58 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint4_t *__restrict_
   const int h = l >> 5, c = l & 31;
   const int64_t n = t * kStrip + c;
   const int64_t g = q >> 1;
-  const _Float16 sh = bitcast<_Float16>(rs[((t * KG8 + (g >> 3)) * 32 + c) * 8 + (g & 7)]);
+  const uint16_t s16 = rs[((t * KG8 + (g >> 3)) * 32 + c) * 8 + (g & 7)];
+  const _Float16 sh = bitcast<_Float16>(s16);
   const half2_t s2 = {sh, sh};
+  const Dequant::BScale bs(s16);
   const uint4_t v = rw[idx];
   const Dequant dq;
+  auto word = [&](uint32_t x) {
+    if constexpr (BF)
+      return bitcast<uint4_t>(dq.scaled_bf16(x, bs));
+    else
+      return bitcast<uint4_t>(dq.scaled(x, s2));
+  };
   if (CANONICAL) {
     if (n >= N) return;
     const int64_t k0 = 64 * q + 32 * h;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const half8_t w = dq.scaled(v[j], s2);
+      const uint4_t w = word(v[j]);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) W16[(k0 + 8 * j + i) * N + n] = bitcast<uint16_t>(w[i]);
+      for (int i = 0; i < 8; ++i)
+        W16[(k0 + 8 * j + i) * N + n] = (uint16_t)(w[i >> 1] >> (16 * (i & 1)));
     }
   } else {
     uint4_t *out = (uint4_t *)W16 + idx * 4;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) out[j] = bitcast<uint4_t>(dq.scaled(v[j], s2));
+    for (int j = 0; j < 4; ++j) out[j] = word(v[j]);
   }
 }
 
-hipError_t launch_dequant_canonical(const void *rw, const void *rs, int64_t K, int64_t N,
-                                    uint16_t *W16, hipStream_t s) {
+template <bool CANONICAL>
+static hipError_t launch_dequant(const void *rw, const void *rs, int64_t K, int64_t N, bool bf16,
+                                 uint16_t *W, hipStream_t s) {
   int64_t KT, KG, KG8, NS;
   repack_geometry(K, N, KT, KG, KG8, NS);
-  hipLaunchKernelGGL(dequant_kernel<true>, dim3((unsigned)ceil_div(NS * KT * 64, 256)), dim3(256),
-                     0, s, (const uint4_t *)rw, (const uint16_t *)rs, W16, N, KT, KG8, NS);
+  const dim3 grid((unsigned)ceil_div(NS * KT * 64, 256));
+  if (bf16)
+    hipLaunchKernelGGL((dequant_kernel<CANONICAL, true>), grid, dim3(256), 0, s,
+                       (const uint4_t *)rw, (const uint16_t *)rs, W, N, KT, KG8, NS);
+  else
+    hipLaunchKernelGGL((dequant_kernel<CANONICAL, false>), grid, dim3(256), 0, s,
+                       (const uint4_t *)rw, (const uint16_t *)rs, W, N, KT, KG8, NS);
   return hipGetLastError();
 }
 
+hipError_t launch_dequant_canonical(const void *rw, const void *rs, int64_t K, int64_t N,
+                                    bool bf16, uint16_t *W, hipStream_t s) {
+  return launch_dequant<true>(rw, rs, K, N, bf16, W, s);
+}
+
 hipError_t launch_dequant_fragment(const void *rw, const void *rs, int64_t K, int64_t N,
-                                   uint16_t *W16f, hipStream_t s) {
-  int64_t KT, KG, KG8, NS;
-  repack_geometry(K, N, KT, KG, KG8, NS);
-  hipLaunchKernelGGL(dequant_kernel<false>, dim3((unsigned)ceil_div(NS * KT * 64, 256)),
-                     dim3(256), 0, s, (const uint4_t *)rw, (const uint16_t *)rs, W16f, N, KT, KG8,
-                     NS);
-  return hipGetLastError();
+                                   bool bf16, uint16_t *Wf, hipStream_t s) {
+  return launch_dequant<false>(rw, rs, K, N, bf16, Wf, s);
 }
 
 }  // namespace w4a16

@@ -61,7 +61,7 @@ struct PrefillB {
   uint16_t sc[WN];
 };
 
-template <int MI, int WN, bool DENSE, bool SWIGLU>
+template <int MI, int WN, bool DENSE, bool SWIGLU, bool BF>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void prefill_kernel(PrefillArgs p) {
   constexpr int BM = 32 * MI;
@@ -145,29 +145,25 @@ void prefill_kernel(PrefillArgs p) {
     for (int i = 0; i < MI; ++i) acc[w][i] = float16_t{};
 
   auto compute = [&](int buf, const BRegs &r) {
-    half2_t s2[WN];
-#pragma unroll
-    for (int w = 0; w < WN; ++w) {
-      const _Float16 sh = bitcast<_Float16>(r.sc[w]);
-      s2[w] = half2_t{sh, sh};
-    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      half8_t bf[WN];
+      uint4_t bf[WN];
 #pragma unroll
       for (int w = 0; w < WN; ++w) {
-        if constexpr (DENSE)
-          bf[w] = bitcast<half8_t>(r.v[w][j]);
-        else
-          bf[w] = dq.scaled(r.v[w][0][j], s2[w]);
+        if constexpr (DENSE) {
+          bf[w] = r.v[w][j];
+        } else if constexpr (BF) {
+          bf[w] = bitcast<uint4_t>(dq.scaled_bf16(r.v[w][0][j], Dequant::BScale(r.sc[w])));
+        } else {
+          const _Float16 sh = bitcast<_Float16>(r.sc[w]);
+          bf[w] = bitcast<uint4_t>(dq.scaled(r.v[w][0][j], half2_t{sh, sh}));
+        }
       }
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
-        const half8_t af =
-            bitcast<half8_t>(lds[buf][(32 * i + c) * 8 + ((4 * h + j) ^ (c & 7))]);
+        const uint4_t af = lds[buf][(32 * i + c) * 8 + ((4 * h + j) ^ (c & 7))];
 #pragma unroll
-        for (int w = 0; w < WN; ++w)
-          acc[w][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[w], af, acc[w][i], 0, 0, 0);
+        for (int w = 0; w < WN; ++w) acc[w][i] = mfma32<BF>(bf[w], af, acc[w][i]);
       }
     }
   };
@@ -203,13 +199,13 @@ void prefill_kernel(PrefillArgs p) {
         if (!sval[w]) continue;
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
-          half2_t lo, hi;
-          lo.x = (_Float16)silu_mul(acc[w][i][4 * rg + 0], acc[w + HW][i][4 * rg + 0]);
-          lo.y = (_Float16)silu_mul(acc[w][i][4 * rg + 1], acc[w + HW][i][4 * rg + 1]);
-          hi.x = (_Float16)silu_mul(acc[w][i][4 * rg + 2], acc[w + HW][i][4 * rg + 2]);
-          hi.y = (_Float16)silu_mul(acc[w][i][4 * rg + 3], acc[w + HW][i][4 * rg + 3]);
+          const float16_t &g = acc[w][i], &u = acc[w + HW][i];
           const int n = strip[w] * 32 + 8 * rg + 4 * h;
-          *(uint2 *)(orow + n) = uint2{bitcast<uint32_t>(lo), bitcast<uint32_t>(hi)};
+          *(uint2 *)(orow + n) =
+              uint2{pack_out2<BF>(silu_mul(g[4 * rg + 0], u[4 * rg + 0]),
+                                  silu_mul(g[4 * rg + 1], u[4 * rg + 1])),
+                    pack_out2<BF>(silu_mul(g[4 * rg + 2], u[4 * rg + 2]),
+                                  silu_mul(g[4 * rg + 3], u[4 * rg + 3]))};
         }
       }
     } else {
@@ -220,12 +216,9 @@ void prefill_kernel(PrefillArgs p) {
         for (int rg = 0; rg < 4; ++rg) {
           const int n = strip[w] * 32 + 8 * rg + 4 * h;
           if (n >= p.N) continue;
-          half2_t lo, hi;
-          lo.x = (_Float16)acc[w][i][4 * rg + 0];
-          lo.y = (_Float16)acc[w][i][4 * rg + 1];
-          hi.x = (_Float16)acc[w][i][4 * rg + 2];
-          hi.y = (_Float16)acc[w][i][4 * rg + 3];
-          *(uint2 *)(orow + n) = uint2{bitcast<uint32_t>(lo), bitcast<uint32_t>(hi)};
+          const float16_t &v = acc[w][i];
+          *(uint2 *)(orow + n) = uint2{pack_out2<BF>(v[4 * rg + 0], v[4 * rg + 1]),
+                                       pack_out2<BF>(v[4 * rg + 2], v[4 * rg + 3])};
         }
       }
     }
@@ -245,7 +238,7 @@ void prefill_kernel(PrefillArgs p) {
 // offset.  Each step issues the next step's loads, then runs its MFMAs
 // (a scheduling barrier keeps the loads first), then meets the workgroup
 // barrier, which also waits for the loads.
-template <int MI, int WM, int WNW, int TPS, bool DENSE, bool SWIGLU>
+template <int MI, int WM, int WNW, int TPS, bool DENSE, bool SWIGLU, bool BF>
 __global__ __launch_bounds__(64 * WM * WNW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill2_kernel(PrefillArgs p) {
   // TPS: 64-k tiles per pipeline step (2 = one whole 128-k scale group).
@@ -376,32 +369,28 @@ void prefill2_kernel(PrefillArgs p) {
 
   const int rbase = wm * 32 * MI;
   auto compute = [&](const uint4_t *stage, const BRegs &r) {
-    half2_t s2[2];
-    {
-      const _Float16 s0 = bitcast<_Float16>((uint16_t)r.sc0);
-      const _Float16 s1 = bitcast<_Float16>((uint16_t)r.sc1);
-      s2[0] = half2_t{s0, s0};
-      s2[1] = half2_t{s1, s1};
-    }
+    const uint16_t sc[2] = {(uint16_t)r.sc0, (uint16_t)r.sc1};
 #pragma unroll
     for (int jj = 0; jj < 4 * TPS; ++jj) {
       const int t = jj >> 2, j = jj & 3;
-      half8_t bf[2];
+      uint4_t bf[2];
 #pragma unroll
       for (int w = 0; w < 2; ++w) {
-        if constexpr (DENSE)
-          bf[w] = bitcast<half8_t>(r.v[w][t][j]);
-        else
-          bf[w] = dq.scaled(r.v[w][t][0][j], s2[w]);
+        if constexpr (DENSE) {
+          bf[w] = r.v[w][t][j];
+        } else if constexpr (BF) {
+          bf[w] = bitcast<uint4_t>(dq.scaled_bf16(r.v[w][t][0][j], Dequant::BScale(sc[w])));
+        } else {
+          const _Float16 sh = bitcast<_Float16>(sc[w]);
+          bf[w] = bitcast<uint4_t>(dq.scaled(r.v[w][t][0][j], half2_t{sh, sh}));
+        }
       }
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
         const int row = rbase + 32 * i + c;
-        const half8_t af =
-            bitcast<half8_t>(stage[row * CH + ((8 * t + 4 * h + j) ^ swz(row))]);
+        const uint4_t af = stage[row * CH + ((8 * t + 4 * h + j) ^ swz(row))];
 #pragma unroll
-        for (int w = 0; w < 2; ++w)
-          acc[w][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[w], af, acc[w][i], 0, 0, 0);
+        for (int w = 0; w < 2; ++w) acc[w][i] = mfma32<BF>(bf[w], af, acc[w][i]);
       }
     }
   };
@@ -467,13 +456,12 @@ void prefill2_kernel(PrefillArgs p) {
       if (!sval[0]) continue;
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
-        half2_t lo, hi;
-        lo.x = (_Float16)silu_mul(acc[0][i][4 * rg + 0], acc[1][i][4 * rg + 0]);
-        lo.y = (_Float16)silu_mul(acc[0][i][4 * rg + 1], acc[1][i][4 * rg + 1]);
-        hi.x = (_Float16)silu_mul(acc[0][i][4 * rg + 2], acc[1][i][4 * rg + 2]);
-        hi.y = (_Float16)silu_mul(acc[0][i][4 * rg + 3], acc[1][i][4 * rg + 3]);
+        const float16_t &g = acc[0][i], &u = acc[1][i];
         const int n = strip[0] * 32 + 8 * rg + 4 * h;
-        *(uint2 *)(orow + n) = uint2{bitcast<uint32_t>(lo), bitcast<uint32_t>(hi)};
+        *(uint2 *)(orow + n) = uint2{pack_out2<BF>(silu_mul(g[4 * rg + 0], u[4 * rg + 0]),
+                                                   silu_mul(g[4 * rg + 1], u[4 * rg + 1])),
+                                     pack_out2<BF>(silu_mul(g[4 * rg + 2], u[4 * rg + 2]),
+                                                   silu_mul(g[4 * rg + 3], u[4 * rg + 3]))};
       }
     } else {
 #pragma unroll
@@ -483,12 +471,9 @@ void prefill2_kernel(PrefillArgs p) {
         for (int rg = 0; rg < 4; ++rg) {
           const int n = strip[w] * 32 + 8 * rg + 4 * h;
           if (n >= p.N) continue;
-          half2_t lo, hi;
-          lo.x = (_Float16)acc[w][i][4 * rg + 0];
-          lo.y = (_Float16)acc[w][i][4 * rg + 1];
-          hi.x = (_Float16)acc[w][i][4 * rg + 2];
-          hi.y = (_Float16)acc[w][i][4 * rg + 3];
-          *(uint2 *)(orow + n) = uint2{bitcast<uint32_t>(lo), bitcast<uint32_t>(hi)};
+          const float16_t &v = acc[w][i];
+          *(uint2 *)(orow + n) = uint2{pack_out2<BF>(v[4 * rg + 0], v[4 * rg + 1]),
+                                       pack_out2<BF>(v[4 * rg + 2], v[4 * rg + 3])};
         }
       }
     }
@@ -498,7 +483,7 @@ void prefill2_kernel(PrefillArgs p) {
 // Second stage of a split-K prefill: sums the KS FP32 partial slices in
 // slice order and applies the epilogue.  One thread per 4 consecutive
 // outputs of a row.
-template <bool SWIGLU>
+template <bool SWIGLU, bool BF>
 __global__ __launch_bounds__(256) void prefill_reduce_kernel(const float *ws, int KS, int M,
                                                              int N, uint16_t *out, int ldo) {
   const int per_row = ldo >> 2;
@@ -512,15 +497,13 @@ __global__ __launch_bounds__(256) void prefill_reduce_kernel(const float *ws, in
     g += *(const float4_t *)(src + k * slice);
     if constexpr (SWIGLU) u += *(const float4_t *)(src + k * slice + N / 2);
   }
-  half2_t lo, hi;
-  if constexpr (SWIGLU) {
-    lo = half2_t{(_Float16)silu_mul(g[0], u[0]), (_Float16)silu_mul(g[1], u[1])};
-    hi = half2_t{(_Float16)silu_mul(g[2], u[2]), (_Float16)silu_mul(g[3], u[3])};
-  } else {
-    lo = half2_t{(_Float16)g[0], (_Float16)g[1]};
-    hi = half2_t{(_Float16)g[2], (_Float16)g[3]};
-  }
-  *(uint2 *)(out + (int64_t)m * ldo + n) = uint2{bitcast<uint32_t>(lo), bitcast<uint32_t>(hi)};
+  uint2 o;
+  if constexpr (SWIGLU)
+    o = uint2{pack_out2<BF>(silu_mul(g[0], u[0]), silu_mul(g[1], u[1])),
+              pack_out2<BF>(silu_mul(g[2], u[2]), silu_mul(g[3], u[3]))};
+  else
+    o = uint2{pack_out2<BF>(g[0], g[1]), pack_out2<BF>(g[2], g[3])};
+  *(uint2 *)(out + (int64_t)m * ldo + n) = o;
 }
 
 // ---------------------------------------------------------------------------
@@ -550,11 +533,20 @@ static PrefillArgs prefill_args(const Problem &p, int BM, const void *weights) {
   return a;
 }
 
-template <int MI, bool DENSE, bool SWIGLU>
+template <int MI, bool DENSE, bool SWIGLU, bool BF>
 static hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL((prefill_kernel<MI, 2, DENSE, SWIGLU>), dim3(a.tiles_m * a.tiles_n),
+  hipLaunchKernelGGL((prefill_kernel<MI, 2, DENSE, SWIGLU, BF>), dim3(a.tiles_m * a.tiles_n),
                      dim3(256), 0, s, a);
   return hipGetLastError();
+}
+
+template <int MI, bool DENSE>
+static hipError_t launch_prefill_mi(const Problem &p, const PrefillArgs &a, hipStream_t s) {
+  if (p.bf16)
+    return p.swiglu ? launch_prefill_t<MI, DENSE, true, true>(a, s)
+                    : launch_prefill_t<MI, DENSE, false, true>(a, s);
+  return p.swiglu ? launch_prefill_t<MI, DENSE, true, false>(a, s)
+                  : launch_prefill_t<MI, DENSE, false, false>(a, s);
 }
 
 template <bool DENSE>
@@ -562,11 +554,9 @@ static hipError_t launch_tiled(const Problem &p, const void *weights, hipStream_
   // Row tile: 256 rows once M is large, smaller tiles for the transition range.
   const int MI = p.M > 128 ? 8 : (p.M > 64 ? 4 : 2);
   const PrefillArgs a = prefill_args(p, 32 * MI, weights);
-  if (MI == 8)
-    return p.swiglu ? launch_prefill_t<8, DENSE, true>(a, s) : launch_prefill_t<8, DENSE, false>(a, s);
-  if (MI == 4)
-    return p.swiglu ? launch_prefill_t<4, DENSE, true>(a, s) : launch_prefill_t<4, DENSE, false>(a, s);
-  return p.swiglu ? launch_prefill_t<2, DENSE, true>(a, s) : launch_prefill_t<2, DENSE, false>(a, s);
+  if (MI == 8) return launch_prefill_mi<8, DENSE>(p, a, s);
+  if (MI == 4) return launch_prefill_mi<4, DENSE>(p, a, s);
+  return launch_prefill_mi<2, DENSE>(p, a, s);
 }
 
 static int env_int(const char *name, int fallback) {
@@ -601,7 +591,7 @@ static int device_cus() {
 // Launch shape of prefill2_kernel: rows per workgroup tile (64, 128 or 256),
 // 64-k tiles per pipeline step, and K slices.
 struct Prefill2Config {
-  int bm, wnw, tps, ks, tiles;
+  int bm, tps, ks, tiles;
 };
 
 // K slices for a grid of `tiles` workgroups: halve each workgroup's k range
@@ -627,7 +617,7 @@ static int k_slices(int64_t tiles, int nsteps, int cus) {
 // FP32 partials through memory (2 ks M N 4 bytes at 5 TB/s) plus ~3 us.  Two
 // 64-k tiles (one scale group) per pipeline step: half the barriers of one
 // 64-k tile, measured 0-5% faster.  W4A16_PREFILL_BM,
-// W4A16_PREFILL_WNW, W4A16_PREFILL_TPS and W4A16_PREFILL_KS override.
+// W4A16_PREFILL_TPS and W4A16_PREFILL_KS override.
 static bool prefill2_config(const Problem &p, bool dense, Prefill2Config &c) {
   const char *v = std::getenv("W4A16_PREFILL_V2");
   const bool on = v != nullptr ? *v == '1' : !dense;
@@ -658,11 +648,7 @@ static bool prefill2_config(const Problem &p, bool dense, Prefill2Config &c) {
     }
   }
   c.tps = dense ? 1 : env_int("W4A16_PREFILL_TPS", 2) == 2 ? 2 : 1;
-  // Column waves per workgroup: 4 (256 columns, one workgroup per CU) or,
-  // for the 256-row tile, 2 (128 columns, two workgroups per CU; measured
-  // slower, kept as an option).
-  c.wnw = !dense && c.bm == 256 && c.tps == 1 && env_int("W4A16_PREFILL_WNW", 4) == 2 ? 2 : 4;
-  const int64_t tiles_n = p.swiglu ? ceil_div(NS / 2, c.wnw) : ceil_div(NS, 2 * c.wnw);
+  const int64_t tiles_n = p.swiglu ? ceil_div(NS / 2, 4) : ceil_div(NS, 8);
   c.tiles = (int)(ceil_div(p.M, c.bm) * tiles_n);
   const int nsteps = (int)(p.K / kTileK / c.tps);
   int ks = dense ? 1 : k_slices(c.tiles, nsteps, cus);
@@ -672,40 +658,42 @@ static bool prefill2_config(const Problem &p, bool dense, Prefill2Config &c) {
   return true;
 }
 
-template <int MI, int WNW, int TPS, bool DENSE, bool SWIGLU>
+template <int MI, int TPS, bool DENSE, bool SWIGLU, bool BF>
 static hipError_t launch_prefill2_t(const Problem &p, const void *weights, const Prefill2Config &c,
                                     void *workspace, hipStream_t s) {
-  constexpr int WM = 2;
+  constexpr int WM = 2, WNW = 4;
   PrefillArgs a = prefill_args(p, 32 * MI * WM, weights);
   a.tiles_n = (int)(p.swiglu ? ceil_div(a.up_off, WNW) : ceil_div(a.NS, 2 * WNW));
   a.KS = c.ks;
   a.spk = a.KT / TPS / c.ks;
   a.ws = (float *)workspace;
-  hipLaunchKernelGGL((prefill2_kernel<MI, WM, WNW, TPS, DENSE, SWIGLU>),
+  hipLaunchKernelGGL((prefill2_kernel<MI, WM, WNW, TPS, DENSE, SWIGLU, BF>),
                      dim3(a.tiles_m * a.tiles_n * c.ks), dim3(64 * WM * WNW), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || c.ks == 1) return e;
   const int64_t threads = p.M * (a.ldo / 4);
-  hipLaunchKernelGGL((prefill_reduce_kernel<SWIGLU>), dim3((unsigned)ceil_div(threads, 256)),
+  hipLaunchKernelGGL((prefill_reduce_kernel<SWIGLU, BF>), dim3((unsigned)ceil_div(threads, 256)),
                      dim3(256), 0, s, (const float *)workspace, c.ks, a.M, a.N, p.out, a.ldo);
   return hipGetLastError();
+}
+
+template <int MI, int TPS, bool DENSE>
+static hipError_t launch_prefill2_tps(const Problem &p, const void *weights,
+                                      const Prefill2Config &c, void *ws, hipStream_t s) {
+  if (p.bf16)
+    return p.swiglu ? launch_prefill2_t<MI, TPS, DENSE, true, true>(p, weights, c, ws, s)
+                    : launch_prefill2_t<MI, TPS, DENSE, false, true>(p, weights, c, ws, s);
+  return p.swiglu ? launch_prefill2_t<MI, TPS, DENSE, true, false>(p, weights, c, ws, s)
+                  : launch_prefill2_t<MI, TPS, DENSE, false, false>(p, weights, c, ws, s);
 }
 
 template <int MI, bool DENSE>
 static hipError_t launch_prefill2_m(const Problem &p, const void *weights, const Prefill2Config &c,
                                     void *ws, hipStream_t s) {
   if constexpr (!DENSE) {
-    if (c.tps == 2)
-      return p.swiglu ? launch_prefill2_t<MI, 4, 2, DENSE, true>(p, weights, c, ws, s)
-                      : launch_prefill2_t<MI, 4, 2, DENSE, false>(p, weights, c, ws, s);
-    if constexpr (MI == 4) {
-      if (c.wnw == 2)
-        return p.swiglu ? launch_prefill2_t<MI, 2, 1, DENSE, true>(p, weights, c, ws, s)
-                        : launch_prefill2_t<MI, 2, 1, DENSE, false>(p, weights, c, ws, s);
-    }
+    if (c.tps == 2) return launch_prefill2_tps<MI, 2, DENSE>(p, weights, c, ws, s);
   }
-  return p.swiglu ? launch_prefill2_t<MI, 4, 1, DENSE, true>(p, weights, c, ws, s)
-                  : launch_prefill2_t<MI, 4, 1, DENSE, false>(p, weights, c, ws, s);
+  return launch_prefill2_tps<MI, 1, DENSE>(p, weights, c, ws, s);
 }
 
 int64_t prefill_workspace_bytes(const Problem &p) {
@@ -724,20 +712,22 @@ hipError_t launch_prefill(const Problem &p, void *workspace, hipStream_t s) {
 }
 
 int tiled_describe(const Problem &p, bool dense, char *buf, size_t n) {
-  const char *pre = dense ? "dequant_kernel<false>; " : "";
+  const char *pre = !dense ? "" : (p.bf16 ? "dequant_kernel<false, true>; " : "dequant_kernel<false, false>; ");
   const char *d = dense ? "true" : "false", *sw = p.swiglu ? "true" : "false";
+  const char *bf = p.bf16 ? "true" : "false";
   Prefill2Config c;
   if (prefill2_config(p, dense, c)) {
-    int k = snprintf(buf, n, "%sprefill2_kernel<%d, 2, %d, %d, %s, %s> workgroups=%d threads=%d ks=%d",
-                     pre, c.bm / 64, c.wnw, c.tps, d, sw, c.tiles * c.ks, 128 * c.wnw, c.ks);
+    int k = snprintf(buf, n,
+                     "%sprefill2_kernel<%d, 2, 4, %d, %s, %s, %s> workgroups=%d threads=512 ks=%d", pre,
+                     c.bm / 64, c.tps, d, sw, bf, c.tiles * c.ks, c.ks);
     if (c.ks > 1 && k > 0 && (size_t)k < n)
-      k += snprintf(buf + k, n - k, "; prefill_reduce_kernel<%s>", sw);
+      k += snprintf(buf + k, n - k, "; prefill_reduce_kernel<%s, %s>", sw, bf);
     return k;
   }
   const int MI = p.M > 128 ? 8 : (p.M > 64 ? 4 : 2);
   const PrefillArgs a = prefill_args(p, 32 * MI, nullptr);
-  return snprintf(buf, n, "%sprefill_kernel<%d, 2, %s, %s> workgroups=%d threads=256", pre, MI, d,
-                  sw, a.tiles_m * a.tiles_n);
+  return snprintf(buf, n, "%sprefill_kernel<%d, 2, %s, %s, %s> workgroups=%d threads=256", pre, MI,
+                  d, sw, bf, a.tiles_m * a.tiles_n);
 }
 
 int64_t dense_workspace_bytes(const Problem &p) {
@@ -748,7 +738,7 @@ int64_t dense_workspace_bytes(const Problem &p) {
 hipError_t launch_dense(const Problem &p, void *workspace, hipStream_t s) {
   if (workspace == nullptr) return hipErrorInvalidValue;
   void *w16f = workspace;
-  hipError_t e = launch_dequant_fragment(p.rw, p.rs, p.K, p.N, (uint16_t *)w16f, s);
+  hipError_t e = launch_dequant_fragment(p.rw, p.rs, p.K, p.N, p.bf16, (uint16_t *)w16f, s);
   if (e != hipSuccess) return e;
   Prefill2Config c;
   if (prefill2_config(p, true, c)) return launch_prefill2_m<4, true>(p, w16f, c, nullptr, s);

@@ -77,6 +77,18 @@ def activations(M: int, K: int, seed: int = 0, outliers: bool = False) -> np.nda
     return A.astype(np.float16)
 
 
+def activations_bf16(M: int, K: int, seed: int = 0, outliers: bool = False) -> np.ndarray:
+    """The same draw as ``activations`` cast to bf16 (nearest even) instead of
+    fp16; returned as the uint16 bit patterns."""
+    rng = np.random.default_rng(seed + 1)
+    A = rng.standard_normal((M, K), dtype=np.float32)
+    if outliers:
+        idx = outlier_channels(K, rng)
+        A[:, idx] *= np.float32(20.0)
+    import torch
+    return torch.from_numpy(A).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
 def outlier_channels(K: int, rng: np.random.Generator) -> np.ndarray:
     n_out = int(round(0.01 * K))
     return rng.permutation(K)[:n_out]

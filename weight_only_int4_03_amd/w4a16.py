@@ -30,6 +30,7 @@ PATH_PREFILL = 2
 PATH_DENSE = 3
 PATHS = {"auto": PATH_AUTO, "decode": PATH_DECODE, "prefill": PATH_PREFILL, "dense": PATH_DENSE}
 FLAG_SWIGLU = 0x10
+FLAG_BF16 = 0x20
 G = 128
 
 
@@ -51,6 +52,7 @@ _SIGNATURES = {
     "w4a16_repack": ([_p, _p, _i64, _i64, _int, _p, _p, _p], _int),
     "w4a16_unrepack": ([_p, _p, _i64, _i64, _int, _p, _p, _p], _int),
     "w4a16_dequant": ([_p, _p, _i64, _i64, _int, _p, _p], _int),
+    "w4a16_dequant_bf16": ([_p, _p, _i64, _i64, _int, _p, _p], _int),
     "w4a16_gemm": ([_p, _i64, _i64, _p, _p, _i64, _int, _p, _p], _int),
     "w4a16_gemm_swiglu": ([_p, _i64, _i64, _p, _p, _i64, _int, _p, _p], _int),
     "w4a16_gemm_ex": ([_p, _i64, _i64, _p, _p, _i64, _int, _p, _int, _p, _i64, _p], _int),
@@ -181,26 +183,36 @@ def unrepack(w: RepackedWeight, G: int = G, stream=None):
     return packed, scales
 
 
-def dequant(w: RepackedWeight, G: int = G, stream=None):
-    """fp16 [K,N] dequantized weights (canonical row-major)."""
+def dequant(w: RepackedWeight, G: int = G, stream=None, bf16: bool = False):
+    """fp16 (or, with bf16, bf16) [K,N] dequantized weights (canonical row-major)."""
     torch = _torch()
-    W16 = torch.empty((w.K, w.N), dtype=torch.float16, device=w.rw.device)
-    _check(lib().w4a16_dequant(_ptr(w.rw), _ptr(w.rs), w.K, w.N, G, _ptr(W16), _stream(stream)))
-    return W16
+    W = torch.empty((w.K, w.N), dtype=torch.bfloat16 if bf16 else torch.float16,
+                    device=w.rw.device)
+    fn = lib().w4a16_dequant_bf16 if bf16 else lib().w4a16_dequant
+    _check(fn(_ptr(w.rw), _ptr(w.rs), w.K, w.N, G, _ptr(W), _stream(stream)))
+    return W
+
+
+def _flags(path, swiglu: bool, bf16: bool) -> int:
+    return ((PATHS[path] if isinstance(path, str) else int(path)) | (FLAG_SWIGLU if swiglu else 0)
+            | (FLAG_BF16 if bf16 else 0))
 
 
 def gemm(A, w: RepackedWeight, swiglu: bool = False, path: str | int = "auto", out=None,
          workspace=None, G: int = G, stream=None):
-    """C = A * dequant(W) (fp16 [M,N]); with swiglu, Z = silu(C[:, :N/2]) * C[:, N/2:]."""
+    """C = A * dequant(W) ([M,N] in A's dtype, fp16 or bf16); with swiglu,
+    Z = silu(C[:, :N/2]) * C[:, N/2:]."""
     torch = _torch()
-    assert A.is_cuda and A.dtype == torch.float16 and A.is_contiguous()
+    assert A.is_cuda and A.dtype in (torch.float16, torch.bfloat16) and A.is_contiguous()
+    bf16 = A.dtype == torch.bfloat16
     M, K = A.shape
     if K != w.K:
         raise ValueError("A has K=%d, weight has K=%d" % (K, w.K))
     ncols = w.N // 2 if swiglu else w.N
     if out is None:
-        out = torch.empty((M, ncols), dtype=torch.float16, device=A.device)
-    flags = (PATHS[path] if isinstance(path, str) else int(path)) | (FLAG_SWIGLU if swiglu else 0)
+        out = torch.empty((M, ncols), dtype=A.dtype, device=A.device)
+    assert out.dtype == A.dtype
+    flags = _flags(path, swiglu, bf16)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().w4a16_gemm_ex(_ptr(A), M, K, _ptr(w.rw), _ptr(w.rs), w.N, G, _ptr(out), flags,
                                _ptr(workspace), ws_bytes, _stream(stream)))
@@ -230,9 +242,8 @@ def gemm_swiglu(A, w: RepackedWeight, out=None, G: int = G, stream=None):
 
 
 def workspace_bytes(M: int, K: int, N: int, swiglu: bool = False, path: str | int = "auto",
-                    G: int = G) -> int:
-    flags = (PATHS[path] if isinstance(path, str) else int(path)) | (FLAG_SWIGLU if swiglu else 0)
-    return _check(lib().w4a16_gemm_workspace_bytes(M, K, N, G, flags))
+                    G: int = G, bf16: bool = False) -> int:
+    return _check(lib().w4a16_gemm_workspace_bytes(M, K, N, G, _flags(path, swiglu, bf16)))
 
 
 def select_path(M: int, K: int, N: int, swiglu: bool = False, G: int = G) -> str:
@@ -241,11 +252,11 @@ def select_path(M: int, K: int, N: int, swiglu: bool = False, G: int = G) -> str
 
 
 def describe(M: int, K: int, N: int, swiglu: bool = False, path: str | int = "auto",
-             G: int = G) -> str:
+             G: int = G, bf16: bool = False) -> str:
     """The kernel launches (profiler names and grids) a GEMM of this shape makes."""
-    flags = (PATHS[path] if isinstance(path, str) else int(path)) | (FLAG_SWIGLU if swiglu else 0)
     buf = ctypes.create_string_buffer(512)
-    _check(lib().w4a16_describe(M, K, N, G, flags, ctypes.addressof(buf), len(buf)))
+    _check(lib().w4a16_describe(M, K, N, G, _flags(path, swiglu, bf16), ctypes.addressof(buf),
+                                len(buf)))
     return buf.value.decode()
 
 
