@@ -99,11 +99,11 @@ def workloads():
     return w
 
 
-def kernel_key(M, K, N, swiglu):
+def kernel_key(M, K, N, swiglu, bf16=False):
     """The kernel instance a GEMM launches under the automatic path, as the
     profiler names it, marked when a second (split-K reduction) launch
     follows it."""
-    desc = w4a16.describe(M, K, N, swiglu)
+    desc = w4a16.describe(M, K, N, swiglu, bf16=bf16)
     first = desc.split(";")[0]
     name = first.split(" workgroups=")[0].strip()
     return name + (" + reduce" if ";" in desc else "")
@@ -140,7 +140,7 @@ def stored_traffic(workload, kernel):
         return None
 
 
-def cpu_baseline(units, host_w, target_s=12.0):
+def cpu_baseline(units, host_w, target_s=12.0, bf16=False):
     """Time the oracle's fp64 GEMM (+ SwiGLU) on a column sample of every unit
     (host_w: the same seeded fp32 weights the GPU was given, keyed by (K, N))."""
     import oracle
@@ -164,9 +164,9 @@ def cpu_baseline(units, host_w, target_s=12.0):
         W = host_w[(K, N)]
         Ws = np.concatenate([W[:, :ns], W[:, N // 2:N // 2 + ns]], axis=1) if sw else W[:, :ns]
         packed, s16 = o.quantize_pack(np.ascontiguousarray(Ws))
-        A = synth.activations(M, K, seed=0, outliers=outl)
+        A = (synth.activations_bf16 if bf16 else synth.activations)(M, K, seed=0, outliers=outl)
         t0 = time.perf_counter()
-        C = o.gemm_f64(A, packed, s16)
+        C = (o.gemm_bf16_f64 if bf16 else o.gemm_f64)(A, packed, s16)
         if sw:
             o.swiglu_f64(C)
         elapsed += time.perf_counter() - t0
@@ -250,6 +250,8 @@ def main():
     ap.add_argument("--workload", default="llama8b_decode", choices=sorted(workloads()))
     ap.add_argument("--reps", type=int, default=20, help="graph replays per GEMM timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dtype", default="fp16", choices=["fp16", "bf16"],
+                    help="activation and output type (the weights are the same)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for hardware-counter calibration)")
     args = ap.parse_args()
@@ -294,13 +296,21 @@ def main():
     copies = {key: [w] + [w.clone() for _ in range(ncopies - 1)] for key, w in base.items()}
     log("rotation: %d copies of %.1f MB per slot" % (ncopies, per_slot / 1e6))
 
+    bf16 = args.dtype == "bf16"
+    act_dtype = torch.bfloat16 if bf16 else torch.float16
     acts = {}
     for _, m, k, n, sw, outl, _ in units:
         if (m, k, outl) not in acts:
-            acts[(m, k, outl)] = torch.from_numpy(synth.activations(m, k, seed=0, outliers=outl)).to(dev)
+            if bf16:
+                bits = synth.activations_bf16(m, k, seed=0, outliers=outl)
+                acts[(m, k, outl)] = torch.from_numpy(bits.view(np.int16)).to(dev).view(
+                    torch.bfloat16)
+            else:
+                acts[(m, k, outl)] = torch.from_numpy(
+                    synth.activations(m, k, seed=0, outliers=outl)).to(dev)
     outs = {}
     for label, m, k, n, sw, *_ in units:
-        outs[label] = torch.empty((m, n // 2 if sw else n), dtype=torch.float16, device=dev)
+        outs[label] = torch.empty((m, n // 2 if sw else n), dtype=act_dtype, device=dev)
 
     stream = torch.cuda.Stream()
 
@@ -308,7 +318,12 @@ def main():
         label, m, k, n, sw, outl, _ = u
         w = copies[(k, n)][copy]
         if sw:
-            w4a16.gemm_swiglu(acts[(m, k, outl)], w, out=outs[label])
+            if bf16:
+                w4a16.gemm(acts[(m, k, outl)], w, swiglu=True, out=outs[label])
+            else:
+                w4a16.gemm_swiglu(acts[(m, k, outl)], w, out=outs[label])
+        elif bf16:
+            w4a16.gemm(acts[(m, k, outl)], w, out=outs[label])
         else:
             w4a16.gemm_plain(acts[(m, k, outl)], w, out=outs[label])
 
@@ -393,7 +408,8 @@ def main():
         us = a.elapsed_time(b) * 1e3 / (args.reps * ncopies)
         by, fl = alg_bytes(m, k, n, sw), flops(m, k, n)
         detail.append({"gemm": label, "M": m, "K": k, "N": n, "swiglu": sw,
-                       "kernel": kernel_key(m, k, n, sw), "launch": w4a16.describe(m, k, n, sw),
+                       "kernel": kernel_key(m, k, n, sw, bf16),
+                       "launch": w4a16.describe(m, k, n, sw, bf16=bf16),
                        "us": round(us, 3),
                        "GB/s": round(by / us / 1e3, 1), "TFLOP/s": round(fl / us / 1e6, 2),
                        "hbm_frac": round(by / us / 1e3 / HBM_PEAK_GBS, 4),
@@ -432,7 +448,7 @@ def main():
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4)}
     ceiling = ceilings["stream_read_GBs"] if hbm_bound else ceilings["mfma_f16_TFLOPs"]
     roof["frac_of_measured_ceiling"] = round(achieved / ceiling, 4) if ceiling else None
-    roof["traffic"] = stored_traffic(args.workload, dom)
+    roof["traffic"] = stored_traffic(args.workload + ("_bf16" if bf16 else ""), dom)
     roof["kernel"] = dom
     roof["launch_workgroups"] = sorted({int(re.search(r"workgroups=(\d+)", d["launch"]).group(1))
                                         for d in detail if d["kernel"] == dom})
@@ -450,7 +466,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
-        cpu = cpu_baseline(units, host_w)
+        cpu = cpu_baseline(units, host_w, bf16=bf16)
         if unit == "TFLOP/s":
             cpu["value"] = round(cpu["value"] * step_flops / step_bytes / 1e3, 6)
             cpu["unit"] = "TFLOP/s"
@@ -467,10 +483,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp16",
-        "data": "synthetic (seeded N(0,1) fp16 activations, N(0,0.02) weights quantized to int4 "
+        "dtype": "bf16" if bf16 else "fp16",
+        "data": "synthetic (seeded N(0,1) " + args.dtype + " activations, N(0,0.02) weights quantized to int4 "
                 "G=128)",
-        "config": {"workload": args.workload, "description": desc, "G": G,
+        "config": {"workload": args.workload + ("_bf16" if bf16 else ""), "description": desc,
+                   "activations": args.dtype, "G": G,
                    "gemms_per_step": len(units), "alg_bytes_per_step": step_bytes,
                    "flops_per_step": step_flops, "weight_copies": ncopies,
                    "path": "auto",
