@@ -77,6 +77,16 @@ typedef void *w4a16_stream_t; /* a hipStream_t */
 int w4a16_pack(const float *W_d, int64_t K, int64_t N, int G, int32_t *packed_d,
                uint16_t *scales_d, w4a16_stream_t stream);
 
+/* Quantize and pack with a folded RMSNorm gain (FuTransformer, arXiv
+ * 2610.23796, section 3.2.2: the frozen gain gamma of the RMSNorm before a
+ * projection is folded into its weights once, before quantizing, so the GEMM
+ * reads the raw activations).  Same as w4a16_pack applied to
+ * W'[k,n] = fp32(gamma[k] * W[k,n]) (one fp32 rounding per element).
+ *   gamma_d  fp32 [K], device, read only; NULL means w4a16_pack itself.
+ * Pair the packed weights with w4a16_rms_rowscale and w4a16_gemm_rowscale. */
+int w4a16_pack_gain(const float *W_d, const float *gamma_d, int64_t K, int64_t N, int G,
+                    int32_t *packed_d, uint16_t *scales_d, w4a16_stream_t stream);
+
 /* Same computation on host memory, for loaders that quantize on the CPU.
  * nthreads <= 0 uses every hardware thread.  Returns W4A16_ERR_NONFINITE if W
  * holds a NaN or an infinity (outputs are then unspecified). */
@@ -162,6 +172,30 @@ int w4a16_gemm_swiglu(const uint16_t *A_d, int64_t M, int64_t K, const void *rw_
 int w4a16_gemm_ex(const uint16_t *A_d, int64_t M, int64_t K, const void *rw_d,
                   const void *rs_d, int64_t N, int G, uint16_t *out_d, int flags,
                   void *workspace_d, int64_t workspace_bytes, w4a16_stream_t stream);
+
+/* GEMM with a per-row output factor (FuTransformer, section 3.2.2: the
+ * RMSNorm row factor rho_m of the raw activations, applied in the GEMM's
+ * epilogue): out[m,n] = rowscale[m] * sum_k A[m,k] * w[k,n], and with
+ * W4A16_FLAG_SWIGLU the factor multiplies both the gate and the up value
+ * before the epilogue, Z = silu(r g) * (r u).  Everything else as
+ * w4a16_gemm_ex (same flags, workspace and errors).
+ *   rowscale_d  fp32 [M], device, read only (W4A16_ERR_INVALID if NULL and
+ *               M > 0) */
+int w4a16_gemm_rowscale(const uint16_t *A_d, int64_t M, int64_t K, const void *rw_d,
+                        const void *rs_d, int64_t N, int G, const float *rowscale_d,
+                        uint16_t *out_d, int flags, void *workspace_d, int64_t workspace_bytes,
+                        w4a16_stream_t stream);
+
+/* RMSNorm row factors of the raw activations (FuTransformer, section 3.2.2):
+ * rho_d[m] = (sum_k A[m,k]^2 / K + eps)^(-1/2), sums in FP32 (fixed order,
+ * deterministic), correctly rounded division and square root.
+ *   A_d    fp16 bits [M, K] (bf16 with flags = W4A16_FLAG_BF16), device,
+ *          16-byte aligned; K % 8 == 0
+ *   eps    finite, >= 0
+ *   rho_d  fp32 [M], device, written
+ * Errors: W4A16_ERR_INVALID, W4A16_ERR_HIP. */
+int w4a16_rms_rowscale(const uint16_t *A_d, int64_t M, int64_t K, float eps, int flags,
+                       float *rho_d, w4a16_stream_t stream);
 
 /* Workspace bytes that w4a16_gemm_ex needs for this problem and flags. */
 int64_t w4a16_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N, int G, int flags);

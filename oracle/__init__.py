@@ -55,6 +55,9 @@ class Oracle:
         lib.oracle_f64_to_bf16.argtypes = [ctypes.c_double]
         lib.oracle_f64_to_bf16.restype = ctypes.c_uint16
         lib.oracle_dequant_bf16.argtypes = [_p, _p, _i64, _i64, ctypes.c_int, _p]
+        lib.oracle_fold_gain.argtypes = [_p, _p, _i64, _i64, _p]
+        lib.oracle_rms_rowscale_f64.argtypes = [_p, _i64, _i64, ctypes.c_int, ctypes.c_double, _p]
+        lib.oracle_scale_rows.argtypes = [_p, _i64, _i64, _p, _p]
         lib.oracle_gemm_bf16_f64.argtypes = [_p, _i64, _i64, _p, _p, _i64, ctypes.c_int, _p,
                                              ctypes.c_int]
         lib.oracle_quantize.argtypes = [_p, _i64, _i64, ctypes.c_int, _p, _p]
@@ -68,7 +71,8 @@ class Oracle:
         lib.oracle_max_threads.argtypes = []
         for name in ("oracle_quantize", "oracle_pack", "oracle_unpack", "oracle_dequant",
                      "oracle_dequant_bf16", "oracle_gemm_f64", "oracle_gemm_bf16_f64",
-                     "oracle_gemm_w16_f64", "oracle_swiglu_f64", "oracle_max_threads"):
+                     "oracle_gemm_w16_f64", "oracle_swiglu_f64", "oracle_max_threads",
+                     "oracle_fold_gain", "oracle_rms_rowscale_f64", "oracle_scale_rows"):
             getattr(lib, name).restype = ctypes.c_int
         self.lib = lib
         self.path = path
@@ -203,6 +207,38 @@ class Oracle:
         self.lib.oracle_gemm_w16_f64(A16.ctypes.data, M, K, W16.ctypes.data, N,
                                      C.ctypes.data, nthreads)
         return C
+
+    def fold_gain(self, W: np.ndarray, gamma: np.ndarray) -> np.ndarray:
+        """W'[k,n] = fp32(gamma[k] * W[k,n]) (FuTransformer, section 3.2.2)."""
+        W = np.ascontiguousarray(W, dtype=np.float32)
+        gamma = np.ascontiguousarray(gamma, dtype=np.float32)
+        K, N = W.shape
+        if gamma.shape != (K,):
+            raise ValueError("gamma must have K entries")
+        Wf = np.empty_like(W)
+        self.lib.oracle_fold_gain(W.ctypes.data, gamma.ctypes.data, K, N, Wf.ctypes.data)
+        return Wf
+
+    def rms_rowscale_f64(self, A: np.ndarray, eps: float, bf16: bool = False) -> np.ndarray:
+        """rho[m] = (sum_k A[m,k]^2 / K + eps)^(-1/2) in fp64 (A: fp16 values or
+        fp16 bits; bf16 bits with bf16=True)."""
+        A = np.ascontiguousarray(np.asarray(A).view(np.uint16))
+        M, K = A.shape
+        rho = np.empty((M,), np.float64)
+        rc = self.lib.oracle_rms_rowscale_f64(A.ctypes.data, M, K, int(bf16), float(eps),
+                                              rho.ctypes.data)
+        if rc != OK:
+            raise ValueError("oracle_rms_rowscale_f64 failed with status %d" % rc)
+        return rho
+
+    def scale_rows(self, C: np.ndarray, rho: np.ndarray) -> np.ndarray:
+        """out[m,n] = rho[m] * C[m,n]."""
+        C = np.ascontiguousarray(C, dtype=np.float64)
+        rho = np.ascontiguousarray(rho, dtype=np.float64)
+        M, N = C.shape
+        out = np.empty_like(C)
+        self.lib.oracle_scale_rows(C.ctypes.data, M, N, rho.ctypes.data, out.ctypes.data)
+        return out
 
     def swiglu_f64(self, C: np.ndarray) -> np.ndarray:
         """Z[m,j] = silu(C[m,j]) * C[m,j+N/2] for a [M,N] gate|up product."""

@@ -25,7 +25,11 @@
  *   - bf16 activations (the bf16 models of FuTransformer and of the Swordfish
  *     page): the data contract's dequantize casts the exact (q-8)*s to the
  *     activation type, so for bf16 the weight is bf16((q-8)*s), rounded once
- *     to nearest even; the GEMM sums A * that weight in fp64.
+ *     to nearest even; the GEMM sums A * that weight in fp64;
+ *   - the folded RMSNorm gain (FuTransformer, section 3.2.2) is applied to
+ *     the fp32 weights before quantizing, one fp32 rounding per product; the
+ *     row factor rho_m = (q_m / H + eps)^(-1/2) uses H = K, the length of the
+ *     activation row the GEMM reads.
  *
  * Build: gcc -O2 -std=c11 -fopenmp -ffp-contract=off -fPIC -shared
  * (no fast-math: the quantizer's decisions depend on IEEE fp32 division).
@@ -360,6 +364,49 @@ int oracle_gemm_bf16_f64(const uint16_t *Ab, int64_t M, int64_t K,
                 C[m * N + n] = acc[n - n0];
         }
     }
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------
+ * Folded RMSNorm gain (FuTransformer, section 3.2.2):
+ *   C[m,n] = sum_h x[m,h] rho_m gamma_h W[h,n] = rho_m sum_h x[m,h] W'[h,n],
+ *   W'[h,n] = gamma_h W[h,n],  rho_m = (q_m / H + eps)^(-1/2),
+ *   q_m = sum_h x[m,h]^2.
+ * ---------------------------------------------------------------------- */
+
+/* W' = fp32(gamma[k] * W[k,n]): the double product of two floats is exact,
+ * so converting it to float rounds once, as an IEEE fp32 multiply does. */
+int oracle_fold_gain(const float *W, const float *gamma, int64_t K, int64_t N, float *Wf)
+{
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t n = 0; n < N; ++n)
+            Wf[k * N + n] = (float)((double)gamma[k] * (double)W[k * N + n]);
+    return ORACLE_OK;
+}
+
+/* rho[m] in fp64 from fp16 (bf16 = 0) or bf16 (bf16 = 1) activation bits. */
+int oracle_rms_rowscale_f64(const uint16_t *A, int64_t M, int64_t K, int bf16, double eps,
+                            double *rho)
+{
+    if (K <= 0)
+        return ORACLE_ERR_SHAPE;
+    for (int64_t m = 0; m < M; ++m) {
+        double q = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double x = bf16 ? oracle_bf16_to_f64(A[m * K + k]) : oracle_f16_to_f64(A[m * K + k]);
+            q += x * x;
+        }
+        rho[m] = 1.0 / sqrt(q / (double)K + eps);
+    }
+    return ORACLE_OK;
+}
+
+/* The epilogue's row factor: out[m,n] = rho[m] * C[m,n]. */
+int oracle_scale_rows(const double *C, int64_t M, int64_t N, const double *rho, double *out)
+{
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n)
+            out[m * N + n] = rho[m] * C[m * N + n];
     return ORACLE_OK;
 }
 

@@ -355,6 +355,49 @@ def check_gemm_bf16_matches_fp16_when_exact(o):
     assert np.array_equal(o.gemm_bf16_f64(Ab, packed, s16), o.gemm_f64(A, packed, s16))
 
 
+# -- folded RMSNorm gain -------------------------------------------------------------
+
+def check_fold_gain(o):
+    """gamma = 1 leaves W; power-of-two gains scale exactly; any gain equals
+    numpy's float32 multiply (IEEE, one rounding)."""
+    rng = np.random.default_rng(21)
+    W = rng.standard_normal((256, 24)).astype(np.float32)
+    assert np.array_equal(o.fold_gain(W, np.ones(256, np.float32)), W)
+    g2 = np.exp2(rng.integers(-3, 4, 256)).astype(np.float32)
+    assert np.array_equal(o.fold_gain(W, g2), W * g2[:, None].astype(np.float64))
+    g = (rng.random(256) * 2).astype(np.float32)
+    assert np.array_equal(o.fold_gain(W, g), g[:, None] * W)
+
+
+def check_rms_rowscale(o):
+    """Constant rows give (c^2 + eps)^(-1/2); random fp16 and bf16 rows agree
+    with numpy's mean of squares; eps enters once."""
+    K = 512
+    c = np.array([0.5, 2.0, -3.0], np.float16)
+    A = np.repeat(c[:, None], K, axis=1)
+    rho = o.rms_rowscale_f64(A, 1e-5)
+    assert np.allclose(rho, 1.0 / np.sqrt(c.astype(np.float64) ** 2 + 1e-5), rtol=1e-15)
+    rng = np.random.default_rng(22)
+    A = rng.standard_normal((4, K)).astype(np.float16)
+    x = A.astype(np.float64)
+    assert np.allclose(o.rms_rowscale_f64(A, 1e-6), 1.0 / np.sqrt(np.mean(x * x, axis=1) + 1e-6),
+                       rtol=1e-14)
+    Ab = _torch_bf16_bits(rng.standard_normal((3, K)).astype(np.float32))
+    xb = (Ab.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert np.allclose(o.rms_rowscale_f64(Ab, 0.0, bf16=True),
+                       1.0 / np.sqrt(np.mean(xb * xb, axis=1)), rtol=1e-14)
+    assert o.rms_rowscale_f64(np.zeros((1, K), np.float16), 0.25)[0] == 2.0
+
+
+def check_scale_rows(o):
+    """Row m is multiplied by rho[m] (and only by it)."""
+    rng = np.random.default_rng(23)
+    C = rng.standard_normal((3, 5))
+    rho = np.array([2.0, 0.5, -1.0])
+    assert np.array_equal(o.scale_rows(C, rho), C * rho[:, None])
+    assert np.array_equal(o.scale_rows(C, np.ones(3)), C)
+
+
 # -- SwiGLU ----------------------------------------------------------------------
 
 def check_swiglu(o):
@@ -382,4 +425,5 @@ FAST_CHECKS = [
     check_gemm_integer_exact, check_gemm_all_ones, check_gemm_w16_reference, check_swiglu,
     check_bf16_decode, check_bf16_encode, check_dequant_bf16_rounds_once,
     check_gemm_bf16_bruteforce, check_gemm_bf16_matches_fp16_when_exact,
+    check_fold_gain, check_rms_rowscale, check_scale_rows,
 ]

@@ -292,3 +292,90 @@ def test_bf16_bit_exact_integer_inputs(path):
 def test_bf16_transition_with_outliers():
     """1% of K-channels scaled by 20 (the transition batches' activations)."""
     gemm_case(128, 4096, 4096, path="auto", seed=3, outliers=True, bf16=True)
+
+
+# -- folded RMSNorm gain and the row-factor epilogue ----------------------------
+
+def _rowscale(M, seed):
+    """Seeded positive row factors, as an RMSNorm produces (inputs to both sides)."""
+    rng = np.random.default_rng(seed)
+    return (0.25 + 1.5 * rng.random(M)).astype(np.float32)
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("M,K,N,swiglu,bf16", [(1, 1024, 1064, False, False), (7, 2048, 2112, True, False),
+                                               (40, 1152, 1088, False, True), (70, 2048, 2112, True, True),
+                                               (300, 1024, 4096, False, False)])
+def test_gemm_rowscale_each_path(path, M, K, N, swiglu, bf16):
+    """out[m,:] = rho[m] * (A W)[m,:], the factor applied before SwiGLU, on
+    every path (split-K reductions included), fp16 and bf16."""
+    from gpuhelp import bf16_dev, bf16_out
+    say("rowscale M=%d K=%d N=%d swiglu=%s bf16=%s path=%s" % (M, K, N, swiglu, bf16, path))
+    W = synth.weights(K, N, seed=M + K)
+    w = w4a16.load_weight(W)
+    rho = _rowscale(M, M + N)
+    rho_d = torch().from_numpy(rho).cuda()
+    o = orc()
+    packed_o, s16_o = o.quantize_pack(W)
+    if bf16:
+        A = synth.activations_bf16(M, K, seed=M)
+        out = bf16_out(w4a16.gemm(bf16_dev(A), w, swiglu=swiglu, path=path, rowscale=rho_d))
+        C = o.gemm_bf16_f64(A, packed_o, s16_o)
+    else:
+        A = synth.activations(M, K, seed=M)
+        out = fp16_out(w4a16.gemm(to_dev(A), w, swiglu=swiglu, path=path, rowscale=rho_d))
+        C = o.gemm_f64(A, packed_o, s16_o)
+    C = o.scale_rows(C, rho.astype(np.float64))
+    ref = o.swiglu_f64(C) if swiglu else C
+    if bf16:
+        parity.assert_close_bf16(out, ref, "rowscale bf16")
+    else:
+        parity.assert_close(out, ref, "rowscale")
+
+
+def test_pack_gain_bit_exact():
+    """w4a16_pack_gain packs fp32(gamma[k] W[k,n]) bit for bit as the oracle
+    quantizes the folded weights."""
+    for K, N in [(1024, 1064), (4096, 4096)]:
+        W = synth.weights(K, N, seed=K)
+        gamma = (0.5 + np.random.default_rng(K).random(K)).astype(np.float32)
+        p_d, s_d = w4a16.pack(to_dev(W), gamma=to_dev(gamma))
+        po, so = orc().quantize_pack(orc().fold_gain(W, gamma))
+        assert np.array_equal(p_d.cpu().numpy(), po)
+        assert np.array_equal(s_d.cpu().numpy().view(np.uint16), so)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_rms_rowscale_matches_oracle(bf16):
+    """rho in FP32 against the fp64 oracle (relative 1e-6), deterministic."""
+    from gpuhelp import bf16_dev
+    for M, K in [(1, 4096), (33, 14336), (257, 1024)]:
+        if bf16:
+            A = synth.activations_bf16(M, K, seed=K + M, outliers=True)
+            Ad = bf16_dev(A)
+        else:
+            A = synth.activations(M, K, seed=K + M, outliers=True)
+            Ad = to_dev(A)
+        r1 = w4a16.rms_rowscale(Ad, eps=1e-5).cpu().numpy()
+        r2 = w4a16.rms_rowscale(Ad, eps=1e-5).cpu().numpy()
+        ref = orc().rms_rowscale_f64(A, 1e-5, bf16=bf16)
+        assert np.array_equal(r1, r2)
+        assert np.allclose(r1.astype(np.float64), ref, rtol=1e-6, atol=0), np.abs(r1 / ref - 1).max()
+
+
+def test_rmsnorm_folded_projection_end_to_end():
+    """The section's whole identity: raw x, gain folded into W before
+    quantizing, rho from x, rho applied in the epilogue -- against the
+    oracle's rho_m * sum_h x W' (W' quantized), with SwiGLU."""
+    M, K, N = 24, 4096, 2112
+    W = synth.weights(K, N, seed=11)
+    gamma = (0.8 + 0.4 * np.random.default_rng(11).random(K)).astype(np.float32)
+    A = synth.activations(M, K, seed=11, outliers=True)
+    w = w4a16.load_weight(W, gamma=gamma)
+    Ad = to_dev(A)
+    rho = w4a16.rms_rowscale(Ad, eps=1e-6)
+    out = fp16_out(w4a16.gemm(Ad, w, swiglu=True, rowscale=rho))
+    o = orc()
+    po, so = o.quantize_pack(o.fold_gain(W, gamma))
+    C = o.scale_rows(o.gemm_f64(A, po, so), o.rms_rowscale_f64(A, 1e-6))
+    parity.assert_close(out, o.swiglu_f64(C), "rmsnorm folded projection")

@@ -42,6 +42,14 @@ MUTANTS = [
     ("bf16_truncate", "double n = nearbyint(a / ldexp(1.0, e - 7));", "double n = floor(a / ldexp(1.0, e - 7));"),
     ("bf16_gemm_unrounded_weight", "double w = oracle_bf16_to_f64(\n                        oracle_f64_to_bf16(exact_weight(packed, s16, N, G, k, n)));",
      "double w = exact_weight(packed, s16, N, G, k, n);"),
+    ("fold_gain_dropped", "Wf[k * N + n] = (float)((double)gamma[k] * (double)W[k * N + n]);",
+     "Wf[k * N + n] = W[k * N + n];"),
+    ("fold_gain_wrong_index", "Wf[k * N + n] = (float)((double)gamma[k] * (double)W[k * N + n]);",
+     "Wf[k * N + n] = (float)((double)gamma[n % K] * (double)W[k * N + n]);"),
+    ("rms_mean_over_k_minus_1", "rho[m] = 1.0 / sqrt(q / (double)K + eps);", "rho[m] = 1.0 / sqrt(q / (double)(K - 1) + eps);"),
+    ("rms_eps_dropped", "rho[m] = 1.0 / sqrt(q / (double)K + eps);", "rho[m] = 1.0 / sqrt(q / (double)K);"),
+    ("rms_no_sqrt", "rho[m] = 1.0 / sqrt(q / (double)K + eps);", "rho[m] = 1.0 / (q / (double)K + eps);"),
+    ("scale_rows_by_column", "out[m * N + n] = rho[m] * C[m * N + n];", "out[m * N + n] = rho[n % M] * C[m * N + n];"),
     ("bf16_gemm_fp16_activations", "double a = oracle_bf16_to_f64(Ab[m * K + k]);", "double a = oracle_f16_to_f64(Ab[m * K + k]);"),
 ]
 

@@ -127,7 +127,7 @@ int64_t workspace_for(int path, const Problem &p) {
 
 int run_gemm(const uint16_t *A, int64_t M, int64_t K, const void *rw, const void *rs, int64_t N,
              int G, uint16_t *out, int flags, void *workspace, int64_t ws_bytes,
-             hipStream_t stream) {
+             hipStream_t stream, const float *rowscale = nullptr) {
   const char *who = (flags & W4A16_FLAG_SWIGLU) ? "w4a16_gemm_swiglu" : "w4a16_gemm";
   const bool bf16 = (flags & W4A16_FLAG_BF16) != 0;
   int rc = check_gpu_shape(K, N, G, who);
@@ -146,7 +146,7 @@ int run_gemm(const uint16_t *A, int64_t M, int64_t K, const void *rw, const void
   if (path < W4A16_PATH_DECODE || path > W4A16_PATH_DENSE)
     return fail(W4A16_ERR_INVALID, "%s: unknown path %d", who, path);
 
-  Problem p{A, M, K, N, rw, rs, out, swiglu, bf16};
+  Problem p{A, M, K, N, rw, rs, out, swiglu, bf16, rowscale};
   const int64_t need = workspace_for(path, p);
   void *ws = workspace;
   if (need > 0) {
@@ -167,6 +167,7 @@ int run_gemm(const uint16_t *A, int64_t M, int64_t K, const void *rw, const void
       Problem q = p;
       q.A = A + m0 * K;
       q.out = out + m0 * ldo;
+      if (rowscale != nullptr) q.rowscale = rowscale + m0;
       q.M = M - m0 < kDecodeMaxM ? M - m0 : kDecodeMaxM;
       e = launch_decode(q, ws, stream);
     }
@@ -216,13 +217,19 @@ const char *w4a16_version(void) { return "w4a16-gfx950 0.1"; }
 
 int w4a16_pack(const float *W_d, int64_t K, int64_t N, int G, int32_t *packed_d,
                uint16_t *scales_d, w4a16_stream_t stream) {
-  int rc = check_shape(K, N, G, "w4a16_pack");
+  return w4a16_pack_gain(W_d, nullptr, K, N, G, packed_d, scales_d, stream);
+}
+
+int w4a16_pack_gain(const float *W_d, const float *gamma_d, int64_t K, int64_t N, int G,
+                    int32_t *packed_d, uint16_t *scales_d, w4a16_stream_t stream) {
+  const char *who = gamma_d != nullptr ? "w4a16_pack_gain" : "w4a16_pack";
+  int rc = check_shape(K, N, G, who);
   if (rc != W4A16_OK) return rc;
-  if (G != kGroup) return fail(W4A16_ERR_UNSUPPORTED, "w4a16_pack: GPU pack supports G == 128");
-  if (K / G > 65535) return fail(W4A16_ERR_INVALID, "w4a16_pack: K too large");
-  if (!W_d || !packed_d || !scales_d) return fail(W4A16_ERR_INVALID, "w4a16_pack: null pointer");
-  hipError_t e = launch_pack(W_d, K, N, packed_d, scales_d, (hipStream_t)stream);
-  return e == hipSuccess ? W4A16_OK : hip_fail(e, "w4a16_pack");
+  if (G != kGroup) return fail(W4A16_ERR_UNSUPPORTED, "%s: GPU pack supports G == 128", who);
+  if (K / G > 65535) return fail(W4A16_ERR_INVALID, "%s: K too large", who);
+  if (!W_d || !packed_d || !scales_d) return fail(W4A16_ERR_INVALID, "%s: null pointer", who);
+  hipError_t e = launch_pack(W_d, gamma_d, K, N, packed_d, scales_d, (hipStream_t)stream);
+  return e == hipSuccess ? W4A16_OK : hip_fail(e, who);
 }
 
 // Host quantize+pack: threads split the columns.  fp32 IEEE division,
@@ -359,6 +366,36 @@ int w4a16_gemm_ex(const uint16_t *A_d, int64_t M, int64_t K, const void *rw_d, c
     return fail(W4A16_ERR_INVALID, "w4a16_gemm_ex: unknown flags 0x%x", flags);
   return run_gemm(A_d, M, K, rw_d, rs_d, N, G, out_d, flags, workspace_d, workspace_bytes,
                   (hipStream_t)stream);
+}
+
+int w4a16_gemm_rowscale(const uint16_t *A_d, int64_t M, int64_t K, const void *rw_d,
+                        const void *rs_d, int64_t N, int G, const float *rowscale_d,
+                        uint16_t *out_d, int flags, void *workspace_d, int64_t workspace_bytes,
+                        w4a16_stream_t stream) {
+  if (flags & ~(0xF | W4A16_FLAG_SWIGLU | W4A16_FLAG_BF16))
+    return fail(W4A16_ERR_INVALID, "w4a16_gemm_rowscale: unknown flags 0x%x", flags);
+  if (M > 0 && rowscale_d == nullptr)
+    return fail(W4A16_ERR_INVALID, "w4a16_gemm_rowscale: null row scale");
+  return run_gemm(A_d, M, K, rw_d, rs_d, N, G, out_d, flags, workspace_d, workspace_bytes,
+                  (hipStream_t)stream, rowscale_d);
+}
+
+int w4a16_rms_rowscale(const uint16_t *A_d, int64_t M, int64_t K, float eps, int flags,
+                       float *rho_d, w4a16_stream_t stream) {
+  const char *who = "w4a16_rms_rowscale";
+  if (flags & ~W4A16_FLAG_BF16) return fail(W4A16_ERR_INVALID, "%s: unknown flags 0x%x", who, flags);
+  if (M < 0 || K <= 0 || K % 8 != 0)
+    return fail(W4A16_ERR_INVALID, "%s: need M >= 0 and K a positive multiple of 8", who);
+  if (M > ((int64_t)1 << 30) || K > ((int64_t)1 << 30))
+    return fail(W4A16_ERR_INVALID, "%s: M or K too large", who);
+  if (!(eps >= 0.0f) || !std::isfinite(eps))
+    return fail(W4A16_ERR_INVALID, "%s: eps must be finite and >= 0", who);
+  if (M == 0) return W4A16_OK;
+  if (!A_d || !rho_d) return fail(W4A16_ERR_INVALID, "%s: null pointer", who);
+  if (!aligned16(A_d)) return fail(W4A16_ERR_INVALID, "%s: A must be 16-byte aligned", who);
+  hipError_t e = launch_rms_rowscale(A_d, M, K, eps, (flags & W4A16_FLAG_BF16) != 0, rho_d,
+                                     (hipStream_t)stream);
+  return e == hipSuccess ? W4A16_OK : hip_fail(e, who);
 }
 
 int64_t w4a16_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N, int G, int flags) {

@@ -200,10 +200,14 @@ struct Problem {
   uint16_t *out;   // C [M,N] or Z [M,N/2]
   bool swiglu;
   bool bf16;       // A and the output are bf16 (else fp16)
+  const float *rowscale;  // per-row output factor [M], or null
 };
 
-hipError_t launch_pack(const float *W, int64_t K, int64_t N, int32_t *packed, uint16_t *scales,
-                       hipStream_t s);
+hipError_t launch_pack(const float *W, const float *gamma, int64_t K, int64_t N, int32_t *packed,
+                       uint16_t *scales, hipStream_t s);
+// RMSNorm row factors rho[m] = (sum_k A[m,k]^2 / K + eps)^(-1/2) (rms.hip).
+hipError_t launch_rms_rowscale(const uint16_t *A, int64_t M, int64_t K, float eps, bool bf16,
+                               float *rho, hipStream_t s);
 hipError_t launch_repack(const int32_t *packed, const uint16_t *scales, int64_t K, int64_t N,
                          void *rw, void *rs, hipStream_t s);
 hipError_t launch_unrepack(const void *rw, const void *rs, int64_t K, int64_t N, int32_t *packed,

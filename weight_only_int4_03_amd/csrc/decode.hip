@@ -400,6 +400,7 @@ DecodeArgs decode_args(const Problem &p, int KS, void *workspace) {
   a.valid_strips = p.swiglu ? a.up_off : a.NS;
   a.nsg = p.swiglu ? a.up_off : a.NS;
   a.ws = (float *)workspace;
+  a.rowscale = p.rowscale;
   return a;
 }
 

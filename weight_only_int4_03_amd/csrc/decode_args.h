@@ -19,6 +19,7 @@ struct DecodeArgs {
   int up_off;        // SwiGLU: strip offset from a gate strip to its up strip
   int valid_strips;  // plain: NS; SwiGLU: number of gate strips
   float *ws;         // KS > 1: partial tiles [nsg][KS][SPW][M][32]
+  const float *rowscale;  // per-row output factor, or null
 };
 
 // Epilogue of one element e of strip group sg's tile (tile element order
@@ -30,15 +31,16 @@ __device__ __forceinline__ void decode_epilogue(const DecodeArgs &p, int sg, int
   const int M = p.M;
   const int s = e / (M * 32), rem = e - s * M * 32;
   const int m = rem >> 5, c = rem & 31;
+  const float rs = p.rowscale != nullptr ? p.rowscale[m] : 1.0f;
   if constexpr (SWIGLU) {
     const int gstrip = sg * SH + s;
     if (gstrip < p.valid_strips) {
-      const float gv = value_at(e), uv = value_at(e + SH * M * 32);
+      const float gv = value_at(e) * rs, uv = value_at(e + SH * M * 32) * rs;
       p.out[(int64_t)m * p.ldo + gstrip * 32 + c] = to_out_bits<BF>(silu_mul(gv, uv));
     }
   } else {
     const int col = (sg * SPW + s) * 32 + c;
-    if (col < p.N) p.out[(int64_t)m * p.ldo + col] = to_out_bits<BF>(value_at(e));
+    if (col < p.N) p.out[(int64_t)m * p.ldo + col] = to_out_bits<BF>(value_at(e) * rs);
   }
 }
 

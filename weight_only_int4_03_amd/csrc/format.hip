@@ -14,16 +14,22 @@ namespace w4a16 {
 // coalesced run.  The scale is an IEEE fp32 division, the rounding of W/s is
 // round-half-to-even (v_rndne_f32), and fp16(s) is the round-to-nearest-even
 // conversion -- the same decisions, in the same precision, as the definition.
-__global__ __launch_bounds__(256) void pack_kernel(const float *__restrict__ W, int64_t N,
+// With a gain vector (FuTransformer, arXiv 2610.23796, section 3.2.2: the
+// frozen RMSNorm gain folded into the next projection), the matrix quantized
+// is W'[k,n] = fp32(gamma[k] * W[k,n]).
+__global__ __launch_bounds__(256) void pack_kernel(const float *__restrict__ W,
+                                                   const float *__restrict__ gamma, int64_t N,
                                                    int32_t *__restrict__ packed,
                                                    uint16_t *__restrict__ scales) {
   const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t g = blockIdx.y;
   if (n >= N) return;
-  const float *col = W + g * kGroup * N + n;
+  const float *colw = W + g * kGroup * N + n;
+  const float *gam = gamma != nullptr ? gamma + g * kGroup : nullptr;
+  auto col = [&](int k) { return gam != nullptr ? __fmul_rn(gam[k], colw[k * N]) : colw[k * N]; };
   float amax = 0.0f;
 #pragma unroll 16
-  for (int k = 0; k < kGroup; ++k) amax = fmaxf(amax, fabsf(col[k * N]));
+  for (int k = 0; k < kGroup; ++k) amax = fmaxf(amax, fabsf(col(k)));
   float s = __fdiv_rn(amax, 7.0f);
   s = s < 1e-8f ? 1e-8f : s;
 #pragma unroll 2
@@ -31,7 +37,7 @@ __global__ __launch_bounds__(256) void pack_kernel(const float *__restrict__ W, 
     uint32_t word = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      float q = __builtin_rintf(__fdiv_rn(col[(8 * r + i) * N], s));
+      float q = __builtin_rintf(__fdiv_rn(col(8 * r + i), s));
       q = fminf(fmaxf(q, -8.0f), 7.0f);
       word |= (uint32_t)((int)q + 8) << (4 * i);
     }
@@ -40,10 +46,10 @@ __global__ __launch_bounds__(256) void pack_kernel(const float *__restrict__ W, 
   scales[g * N + n] = to_half_bits(s);
 }
 
-hipError_t launch_pack(const float *W, int64_t K, int64_t N, int32_t *packed, uint16_t *scales,
-                       hipStream_t s) {
+hipError_t launch_pack(const float *W, const float *gamma, int64_t K, int64_t N, int32_t *packed,
+                       uint16_t *scales, hipStream_t s) {
   dim3 grid((unsigned)ceil_div(N, 256), (unsigned)(K / kGroup));
-  hipLaunchKernelGGL(pack_kernel, grid, dim3(256), 0, s, W, N, packed, scales);
+  hipLaunchKernelGGL(pack_kernel, grid, dim3(256), 0, s, W, gamma, N, packed, scales);
   return hipGetLastError();
 }
 

@@ -53,6 +53,7 @@ struct PrefillArgs {
   // alike) and prefill_reduce_kernel finishes the output.
   int KS, spk;
   float *ws;
+  const float *rowscale;  // per-row output factor, or null
 };
 
 template <int WN, bool DENSE>
@@ -192,6 +193,7 @@ void prefill_kernel(PrefillArgs p) {
     const int m = m0 + 32 * i + c;
     if (m >= M) continue;
     uint16_t *orow = p.out + (int64_t)m * p.ldo;
+    const float rs = p.rowscale != nullptr ? p.rowscale[m] : 1.0f;
     if constexpr (SWIGLU) {
       constexpr int HW = WN / 2;
 #pragma unroll
@@ -202,10 +204,10 @@ void prefill_kernel(PrefillArgs p) {
           const float16_t &g = acc[w][i], &u = acc[w + HW][i];
           const int n = strip[w] * 32 + 8 * rg + 4 * h;
           *(uint2 *)(orow + n) =
-              uint2{pack_out2<BF>(silu_mul(g[4 * rg + 0], u[4 * rg + 0]),
-                                  silu_mul(g[4 * rg + 1], u[4 * rg + 1])),
-                    pack_out2<BF>(silu_mul(g[4 * rg + 2], u[4 * rg + 2]),
-                                  silu_mul(g[4 * rg + 3], u[4 * rg + 3]))};
+              uint2{pack_out2<BF>(silu_mul(rs * g[4 * rg + 0], rs * u[4 * rg + 0]),
+                                  silu_mul(rs * g[4 * rg + 1], rs * u[4 * rg + 1])),
+                    pack_out2<BF>(silu_mul(rs * g[4 * rg + 2], rs * u[4 * rg + 2]),
+                                  silu_mul(rs * g[4 * rg + 3], rs * u[4 * rg + 3]))};
         }
       }
     } else {
@@ -217,8 +219,8 @@ void prefill_kernel(PrefillArgs p) {
           const int n = strip[w] * 32 + 8 * rg + 4 * h;
           if (n >= p.N) continue;
           const float16_t &v = acc[w][i];
-          *(uint2 *)(orow + n) = uint2{pack_out2<BF>(v[4 * rg + 0], v[4 * rg + 1]),
-                                       pack_out2<BF>(v[4 * rg + 2], v[4 * rg + 3])};
+          *(uint2 *)(orow + n) = uint2{pack_out2<BF>(rs * v[4 * rg + 0], rs * v[4 * rg + 1]),
+                                       pack_out2<BF>(rs * v[4 * rg + 2], rs * v[4 * rg + 3])};
         }
       }
     }
@@ -452,16 +454,17 @@ void prefill2_kernel(PrefillArgs p) {
     const int m = m0 + rbase + 32 * i + c;
     if (m >= p.M) continue;
     uint16_t *orow = p.out + (int64_t)m * p.ldo;
+    const float rs = p.rowscale != nullptr ? p.rowscale[m] : 1.0f;
     if constexpr (SWIGLU) {
       if (!sval[0]) continue;
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
         const float16_t &g = acc[0][i], &u = acc[1][i];
         const int n = strip[0] * 32 + 8 * rg + 4 * h;
-        *(uint2 *)(orow + n) = uint2{pack_out2<BF>(silu_mul(g[4 * rg + 0], u[4 * rg + 0]),
-                                                   silu_mul(g[4 * rg + 1], u[4 * rg + 1])),
-                                     pack_out2<BF>(silu_mul(g[4 * rg + 2], u[4 * rg + 2]),
-                                                   silu_mul(g[4 * rg + 3], u[4 * rg + 3]))};
+        *(uint2 *)(orow + n) = uint2{pack_out2<BF>(silu_mul(rs * g[4 * rg + 0], rs * u[4 * rg + 0]),
+                                                   silu_mul(rs * g[4 * rg + 1], rs * u[4 * rg + 1])),
+                                     pack_out2<BF>(silu_mul(rs * g[4 * rg + 2], rs * u[4 * rg + 2]),
+                                                   silu_mul(rs * g[4 * rg + 3], rs * u[4 * rg + 3]))};
       }
     } else {
 #pragma unroll
@@ -472,8 +475,8 @@ void prefill2_kernel(PrefillArgs p) {
           const int n = strip[w] * 32 + 8 * rg + 4 * h;
           if (n >= p.N) continue;
           const float16_t &v = acc[w][i];
-          *(uint2 *)(orow + n) = uint2{pack_out2<BF>(v[4 * rg + 0], v[4 * rg + 1]),
-                                       pack_out2<BF>(v[4 * rg + 2], v[4 * rg + 3])};
+          *(uint2 *)(orow + n) = uint2{pack_out2<BF>(rs * v[4 * rg + 0], rs * v[4 * rg + 1]),
+                                       pack_out2<BF>(rs * v[4 * rg + 2], rs * v[4 * rg + 3])};
         }
       }
     }
@@ -485,7 +488,8 @@ void prefill2_kernel(PrefillArgs p) {
 // outputs of a row.
 template <bool SWIGLU, bool BF>
 __global__ __launch_bounds__(256) void prefill_reduce_kernel(const float *ws, int KS, int M,
-                                                             int N, uint16_t *out, int ldo) {
+                                                             int N, uint16_t *out, int ldo,
+                                                             const float *rowscale) {
   const int per_row = ldo >> 2;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (int64_t)M * per_row) return;
@@ -496,6 +500,10 @@ __global__ __launch_bounds__(256) void prefill_reduce_kernel(const float *ws, in
   for (int k = 0; k < KS; ++k) {
     g += *(const float4_t *)(src + k * slice);
     if constexpr (SWIGLU) u += *(const float4_t *)(src + k * slice + N / 2);
+  }
+  if (rowscale != nullptr) {
+    g *= rowscale[m];
+    u *= rowscale[m];
   }
   uint2 o;
   if constexpr (SWIGLU)
@@ -530,6 +538,7 @@ static PrefillArgs prefill_args(const Problem &p, int BM, const void *weights) {
   a.KS = 1;
   a.spk = a.KT;
   a.ws = nullptr;
+  a.rowscale = p.rowscale;
   return a;
 }
 
@@ -673,7 +682,8 @@ static hipError_t launch_prefill2_t(const Problem &p, const void *weights, const
   if (e != hipSuccess || c.ks == 1) return e;
   const int64_t threads = p.M * (a.ldo / 4);
   hipLaunchKernelGGL((prefill_reduce_kernel<SWIGLU, BF>), dim3((unsigned)ceil_div(threads, 256)),
-                     dim3(256), 0, s, (const float *)workspace, c.ks, a.M, a.N, p.out, a.ldo);
+                     dim3(256), 0, s, (const float *)workspace, c.ks, a.M, a.N, p.out, a.ldo,
+                     p.rowscale);
   return hipGetLastError();
 }
 

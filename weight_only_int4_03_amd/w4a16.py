@@ -47,6 +47,10 @@ _int = ctypes.c_int
 _SIGNATURES = {
     "w4a16_pack": ([_p, _i64, _i64, _int, _p, _p, _p], _int),
     "w4a16_pack_host": ([_p, _i64, _i64, _int, _p, _p, _int], _int),
+    "w4a16_pack_gain": ([_p, _p, _i64, _i64, _int, _p, _p, _p], _int),
+    "w4a16_gemm_rowscale": ([_p, _i64, _i64, _p, _p, _i64, _int, _p, _p, _int, _p, _i64, _p],
+                            _int),
+    "w4a16_rms_rowscale": ([_p, _i64, _i64, ctypes.c_float, _int, _p, _p], _int),
     "w4a16_repacked_weight_bytes": ([_i64, _i64, _int], _i64),
     "w4a16_repacked_scale_bytes": ([_i64, _i64, _int], _i64),
     "w4a16_repack": ([_p, _p, _i64, _i64, _int, _p, _p, _p], _int),
@@ -130,14 +134,20 @@ def pack_host(W: np.ndarray, G: int = G, nthreads: int = 0):
 
 # -- device calls ------------------------------------------------------------------
 
-def pack(W, G: int = G, stream=None):
-    """Quantize + pack a device fp32 [K,N] tensor: (packed int32 [K/8,N], scales int16 [K/G,N])."""
+def pack(W, G: int = G, stream=None, gamma=None):
+    """Quantize + pack a device fp32 [K,N] tensor: (packed int32 [K/8,N], scales int16 [K/G,N]).
+    With gamma (device fp32 [K]), the folded-gain weights gamma[k] * W[k,n] are packed."""
     torch = _torch()
     assert W.is_cuda and W.dtype == torch.float32 and W.is_contiguous()
     K, N = W.shape
     packed = torch.empty((K // 8, N), dtype=torch.int32, device=W.device)
     scales = torch.empty((K // G, N), dtype=torch.int16, device=W.device)
-    _check(lib().w4a16_pack(_ptr(W), K, N, G, _ptr(packed), _ptr(scales), _stream(stream)))
+    if gamma is None:
+        _check(lib().w4a16_pack(_ptr(W), K, N, G, _ptr(packed), _ptr(scales), _stream(stream)))
+    else:
+        assert gamma.is_cuda and gamma.dtype == torch.float32 and gamma.numel() == K
+        _check(lib().w4a16_pack_gain(_ptr(W), _ptr(gamma), K, N, G, _ptr(packed), _ptr(scales),
+                                     _stream(stream)))
     return packed, scales
 
 
@@ -199,7 +209,7 @@ def _flags(path, swiglu: bool, bf16: bool) -> int:
 
 
 def gemm(A, w: RepackedWeight, swiglu: bool = False, path: str | int = "auto", out=None,
-         workspace=None, G: int = G, stream=None):
+         workspace=None, G: int = G, stream=None, rowscale=None):
     """C = A * dequant(W) ([M,N] in A's dtype, fp16 or bf16); with swiglu,
     Z = silu(C[:, :N/2]) * C[:, N/2:]."""
     torch = _torch()
@@ -214,9 +224,27 @@ def gemm(A, w: RepackedWeight, swiglu: bool = False, path: str | int = "auto", o
     assert out.dtype == A.dtype
     flags = _flags(path, swiglu, bf16)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().w4a16_gemm_ex(_ptr(A), M, K, _ptr(w.rw), _ptr(w.rs), w.N, G, _ptr(out), flags,
-                               _ptr(workspace), ws_bytes, _stream(stream)))
+    if rowscale is None:
+        _check(lib().w4a16_gemm_ex(_ptr(A), M, K, _ptr(w.rw), _ptr(w.rs), w.N, G, _ptr(out),
+                                   flags, _ptr(workspace), ws_bytes, _stream(stream)))
+    else:
+        assert rowscale.is_cuda and rowscale.dtype == torch.float32 and rowscale.numel() == M
+        _check(lib().w4a16_gemm_rowscale(_ptr(A), M, K, _ptr(w.rw), _ptr(w.rs), w.N, G,
+                                         _ptr(rowscale), _ptr(out), flags, _ptr(workspace),
+                                         ws_bytes, _stream(stream)))
     return out
+
+
+def rms_rowscale(A, eps: float = 1e-5, stream=None):
+    """RMSNorm row factors rho[m] = (mean_k A[m,k]^2 + eps)^(-1/2) of an fp16 or
+    bf16 device tensor, as fp32 [M]."""
+    torch = _torch()
+    assert A.is_cuda and A.dtype in (torch.float16, torch.bfloat16) and A.is_contiguous()
+    M, K = A.shape
+    rho = torch.empty((M,), dtype=torch.float32, device=A.device)
+    flags = FLAG_BF16 if A.dtype == torch.bfloat16 else 0
+    _check(lib().w4a16_rms_rowscale(_ptr(A), M, K, eps, flags, _ptr(rho), _stream(stream)))
+    return rho
 
 
 def gemm_plain(A, w: RepackedWeight, out=None, G: int = G, stream=None):
@@ -275,10 +303,13 @@ def probe_mfma(iterations: int, workgroups: int, sink, stream=None) -> int:
     return flops.value
 
 
-def load_weight(W_host: np.ndarray, device="cuda", G: int = G) -> RepackedWeight:
-    """Host fp32 W -> device, quantize+pack on the GPU, repack.  (Load-time path.)"""
+def load_weight(W_host: np.ndarray, device="cuda", G: int = G, gamma=None) -> RepackedWeight:
+    """Host fp32 W -> device, quantize+pack on the GPU (gain gamma folded in
+    when given, host fp32 [K]), repack.  (Load-time path.)"""
     torch = _torch()
     Wd = torch.from_numpy(np.ascontiguousarray(W_host, dtype=np.float32)).to(device)
-    packed, scales = pack(Wd, G)
+    gd = None if gamma is None else torch.from_numpy(
+        np.ascontiguousarray(gamma, dtype=np.float32)).to(device)
+    packed, scales = pack(Wd, G, gamma=gd)
     del Wd
     return repack(packed, scales, G)
