@@ -29,8 +29,12 @@
  *     caller's next synchronisation.  Launch errors are checked right after
  *     each launch and reported as W4A16_ERR_HIP.
  *   - fp16 values cross the ABI as uint16_t bit patterns.
- *   - The GPU paths support G == 128 only (else W4A16_ERR_UNSUPPORTED);
- *     K % 128 == 0, N % 8 == 0, and 16-byte aligned device pointers are
+ *   - Group size G: the GPU paths take G a power of two >= 32 that divides
+ *     K (G = 128 is the data contract's default) or G == K (channelwise: one
+ *     scale per column), else W4A16_ERR_UNSUPPORTED; the GPU packer takes any
+ *     G with G % 8 == 0.  Repacked buffers are built for one G, which every
+ *     call on them must pass again.
+ *   - K % 128 == 0, N % 8 == 0, and 16-byte aligned device pointers are
  *     required (else W4A16_ERR_INVALID).  M is arbitrary (M == 0 is a no-op).
  */
 #ifndef W4A16_H

@@ -53,29 +53,29 @@ def sample_indices(n: int, k: int, seed: int, edge: int = 0) -> np.ndarray:
 
 
 def gemm_case(M, K, N, swiglu=False, path="auto", seed=0, outliers=False, cols=None, rows=None,
-              W=None, A=None, weight=None, bf16=False):
+              W=None, A=None, weight=None, bf16=False, G=128):
     """Run the GPU GEMM on seeded inputs and compare (sampled) outputs with
     the oracle's fp64 result.  Returns the comparison statistics.  With bf16,
     A (and the output) are bf16: A is given as uint16 bit patterns."""
     if bf16:
-        return gemm_case_bf16(M, K, N, swiglu, path, seed, outliers, cols, rows, W, A, weight)
-    say("case M=%d K=%d N=%d swiglu=%s path=%s seed=%d outliers=%s" %
-        (M, K, N, swiglu, path, seed, outliers))
+        return gemm_case_bf16(M, K, N, swiglu, path, seed, outliers, cols, rows, W, A, weight, G)
+    say("case M=%d K=%d N=%d G=%d swiglu=%s path=%s seed=%d outliers=%s" %
+        (M, K, N, G, swiglu, path, seed, outliers))
     t = torch()
     if W is None:
         W = synth.weights(K, N, seed)
     if A is None:
         A = synth.activations(M, K, seed, outliers)
-    w = weight if weight is not None else w4a16.load_weight(W)
-    out = fp16_out(w4a16.gemm(to_dev(A), w, swiglu=swiglu, path=path))
+    w = weight if weight is not None else w4a16.load_weight(W, G=G)
+    out = fp16_out(w4a16.gemm(to_dev(A), w, swiglu=swiglu, path=path, G=G))
     t.cuda.synchronize()
     ncols = N // 2 if swiglu else N
     ocols = np.arange(ncols) if cols is None else np.asarray(cols)
     orows = np.arange(M) if rows is None else np.asarray(rows)
     wcols = np.concatenate([ocols, ocols + N // 2]) if swiglu else ocols
     o = orc()
-    packed_o, s16_o = o.quantize_pack(np.ascontiguousarray(W[:, wcols]))
-    C = o.gemm_f64(np.ascontiguousarray(A[orows]), packed_o, s16_o)
+    packed_o, s16_o = o.quantize_pack(np.ascontiguousarray(W[:, wcols]), G)
+    C = o.gemm_f64(np.ascontiguousarray(A[orows]), packed_o, s16_o, G)
     ref = o.swiglu_f64(C) if swiglu else C
     stats = parity.assert_close(out[np.ix_(orows, ocols)], ref,
                                 "M=%d K=%d N=%d swiglu=%s path=%s" % (M, K, N, swiglu, path))
@@ -95,24 +95,24 @@ def bf16_out(x) -> np.ndarray:
 
 
 def gemm_case_bf16(M, K, N, swiglu=False, path="auto", seed=0, outliers=False, cols=None,
-                   rows=None, W=None, A=None, weight=None):
-    say("case bf16 M=%d K=%d N=%d swiglu=%s path=%s seed=%d outliers=%s" %
-        (M, K, N, swiglu, path, seed, outliers))
+                   rows=None, W=None, A=None, weight=None, G=128):
+    say("case bf16 M=%d K=%d N=%d G=%d swiglu=%s path=%s seed=%d outliers=%s" %
+        (M, K, N, G, swiglu, path, seed, outliers))
     t = torch()
     if W is None:
         W = synth.weights(K, N, seed)
     if A is None:
         A = synth.activations_bf16(M, K, seed, outliers)
-    w = weight if weight is not None else w4a16.load_weight(W)
-    out = bf16_out(w4a16.gemm(bf16_dev(A), w, swiglu=swiglu, path=path))
+    w = weight if weight is not None else w4a16.load_weight(W, G=G)
+    out = bf16_out(w4a16.gemm(bf16_dev(A), w, swiglu=swiglu, path=path, G=G))
     t.cuda.synchronize()
     ncols = N // 2 if swiglu else N
     ocols = np.arange(ncols) if cols is None else np.asarray(cols)
     orows = np.arange(M) if rows is None else np.asarray(rows)
     wcols = np.concatenate([ocols, ocols + N // 2]) if swiglu else ocols
     o = orc()
-    packed_o, s16_o = o.quantize_pack(np.ascontiguousarray(W[:, wcols]))
-    C = o.gemm_bf16_f64(np.ascontiguousarray(A[orows]), packed_o, s16_o)
+    packed_o, s16_o = o.quantize_pack(np.ascontiguousarray(W[:, wcols]), G)
+    C = o.gemm_bf16_f64(np.ascontiguousarray(A[orows]), packed_o, s16_o, G)
     ref = o.swiglu_f64(C) if swiglu else C
     stats = parity.assert_close_bf16(out[np.ix_(orows, ocols)], ref,
                                      "bf16 M=%d K=%d N=%d swiglu=%s path=%s" % (M, K, N, swiglu,

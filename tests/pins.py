@@ -225,6 +225,30 @@ def check_quantization_error_closed_form(o):
     assert abs(rel - theory) < 2.5e-3, (rel, theory)
 
 
+def check_quantize_other_group_sizes(o):
+    """G = 32, 64, 256 and channelwise (G = K): each group's scale is numpy's
+    fp16(fl32(amax / 7)), its largest |w| lands on q = +-7, and the product
+    equals numpy's float64 matmul of the exact weights."""
+    rng = np.random.default_rng(31)
+    K, N = 512, 12
+    W = (rng.standard_normal((K, N)) * 0.02).astype(np.float32)
+    A = rng.standard_normal((2, K)).astype(np.float16)
+    for G in (32, 64, 256, K):
+        packed, s16 = o.quantize_pack(W, G)
+        assert s16.shape == (K // G, N)
+        amax = np.abs(W.reshape(K // G, G, N)).max(axis=1)
+        assert np.array_equal(s16, (amax / np.float32(7.0)).astype(np.float16).view(np.uint16))
+        u = o.unpack(packed).reshape(K // G, G, N)
+        at = np.abs(W.reshape(K // G, G, N)).argmax(axis=1)
+        for g in range(K // G):
+            for n in range(N):
+                assert u[g, at[g, n], n] in (1, 15)
+        Wx = (o.unpack(packed).astype(np.float64) - 8) * np.repeat(
+            s16.view(np.float16).astype(np.float64), G, axis=0)
+        assert np.allclose(o.gemm_f64(A, packed, s16, G), np.matmul(A.astype(np.float64), Wx),
+                           rtol=1e-12, atol=1e-12)
+
+
 # -- dequantization ------------------------------------------------------------
 
 def check_dequant_special_values(o):
@@ -425,5 +449,5 @@ FAST_CHECKS = [
     check_gemm_integer_exact, check_gemm_all_ones, check_gemm_w16_reference, check_swiglu,
     check_bf16_decode, check_bf16_encode, check_dequant_bf16_rounds_once,
     check_gemm_bf16_bruteforce, check_gemm_bf16_matches_fp16_when_exact,
-    check_fold_gain, check_rms_rowscale, check_scale_rows,
+    check_fold_gain, check_rms_rowscale, check_scale_rows, check_quantize_other_group_sizes,
 ]

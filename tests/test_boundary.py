@@ -61,7 +61,11 @@ def _gemm_ex(**kw):
 
 
 def test_gemm_argument_errors_without_gpu():
-    assert _gemm_ex(G=64) == w4a16.ERR_UNSUPPORTED
+    assert _gemm_ex(G=384, K=12288) == w4a16.ERR_UNSUPPORTED   # not a power of two, not K
+    assert _gemm_ex(G=16) == w4a16.ERR_UNSUPPORTED              # below a lane vector
+    assert _gemm_ex(G=64) == w4a16.ERR_INVALID                  # supported G: null pointers
+    assert _gemm_ex(G=4096) == w4a16.ERR_INVALID                # channelwise: null pointers
+    assert _gemm_ex(K=4160, G=64) == w4a16.ERR_INVALID          # K % 128
     assert _gemm_ex(K=4000) == w4a16.ERR_INVALID
     assert _gemm_ex(N=4100) == w4a16.ERR_INVALID
     assert _gemm_ex(M=-1) == w4a16.ERR_INVALID
@@ -79,10 +83,10 @@ def test_gemm_argument_errors_without_gpu():
 def test_other_argument_errors():
     L = w4a16.lib()
     assert L.w4a16_repack(0, 0, 4096, 4096, 128, 0, 0, 0) == w4a16.ERR_INVALID
-    assert L.w4a16_repack(16, 16, 4096, 4096, 32, 16, 16, 0) == w4a16.ERR_UNSUPPORTED
+    assert L.w4a16_repack(16, 16, 12288, 4096, 384, 16, 16, 0) == w4a16.ERR_UNSUPPORTED
     assert L.w4a16_dequant(16, 16, 100, 4096, 128, 16, 0) == w4a16.ERR_INVALID
     assert L.w4a16_pack(0, 4096, 4096, 128, 0, 0, 0) == w4a16.ERR_INVALID
-    assert L.w4a16_pack(16, 4096, 4096, 64, 16, 16, 0) == w4a16.ERR_UNSUPPORTED
+    assert L.w4a16_pack(16, 4080, 4096, 30, 16, 16, 0) == w4a16.ERR_UNSUPPORTED   # G % 8
     assert L.w4a16_repacked_weight_bytes(100, 8, 128) == w4a16.ERR_INVALID
     assert L.w4a16_select_path(1, 4096, 4096, 128, 0) == w4a16.PATH_DECODE
 

@@ -87,3 +87,25 @@ def test_pack_and_dequant_full_size_sampled_columns(K, N):
     assert np.array_equal(Wb.view(np.uint16), orc().dequant_bf16(po, so))
     p2, s2 = w4a16.unrepack(w)
     assert torch().equal(p2, packed) and torch().equal(s2, scales)
+
+
+GROUPS = [(32, 1024, 264), (64, 2048, 1088), (256, 4096, 512), (1152, 1152, 328), (2048, 2048, 96)]
+
+
+@pytest.mark.parametrize("G,K,N", GROUPS)
+def test_other_group_sizes_format_bit_exact(G, K, N):
+    """G = 32, 64, 256 and channelwise (G = K, also not a power of two):
+    device pack, repack / unrepack and fp16 / bf16 dequantization, bit for bit."""
+    say("group G=%d K=%d N=%d" % (G, K, N))
+    W = synth.weights(K, N, seed=G + K + N)
+    packed, scales = w4a16.pack(to_dev(W), G)
+    po, so = orc().quantize_pack(W, G)
+    assert np.array_equal(packed.cpu().numpy(), po)
+    assert np.array_equal(scales.cpu().numpy().view(np.uint16), so)
+    w = w4a16.repack(packed, scales, G)
+    p2, s2 = w4a16.unrepack(w)
+    assert torch().equal(p2, packed) and torch().equal(s2, scales)
+    W16 = w4a16.dequant(w).cpu().numpy().view(np.uint16)
+    assert np.array_equal(W16, orc().dequant(po, so, G))
+    Wb = w4a16.dequant(w, bf16=True).view(torch().int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(Wb, orc().dequant_bf16(po, so, G))

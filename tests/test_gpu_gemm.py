@@ -379,3 +379,46 @@ def test_rmsnorm_folded_projection_end_to_end():
     po, so = o.quantize_pack(o.fold_gain(W, gamma))
     C = o.scale_rows(o.gemm_f64(A, po, so), o.rms_rowscale_f64(A, 1e-6))
     parity.assert_close(out, o.swiglu_f64(C), "rmsnorm folded projection")
+
+
+# -- group sizes other than 128 ---------------------------------------------------
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("G,M,K,N,swiglu,bf16", [(32, 1, 1024, 1064, False, False),
+                                                 (32, 24, 2048, 2112, True, False),
+                                                 (64, 7, 2048, 1088, False, True),
+                                                 (64, 300, 1024, 2112, True, False),
+                                                 (256, 16, 4096, 1088, False, False),
+                                                 (256, 130, 2048, 2112, True, True),
+                                                 (1152, 5, 1152, 1064, False, False),
+                                                 (1152, 70, 1152, 2112, True, False),
+                                                 (2048, 33, 2048, 1088, False, True)])
+def test_group_sizes_each_path(path, G, M, K, N, swiglu, bf16):
+    """Every path with G = 32, 64, 256 and channelwise scales (one scale per
+    column: G = K, including K = 1152, not a power of two)."""
+    gemm_case(M, K, N, swiglu=swiglu, path=path, seed=G + M, bf16=bf16, G=G)
+
+
+@pytest.mark.parametrize("G", [256, 2048])
+def test_group_sizes_cooperative_decode(monkeypatch, G):
+    """The cooperative decode kernel reads one scale per column and 128-k
+    unit, so it takes G >= 128 (smaller groups use the per-wave kernel)."""
+    monkeypatch.setenv("W4A16_DECODE_COOP", "1")
+    assert w4a16.describe(16, 2048, 2112, swiglu=True, path="decode", G=G).startswith(
+        "decode_coop_kernel")
+    assert w4a16.describe(16, 2048, 2112, swiglu=True, path="decode", G=64).startswith(
+        "decode_kernel")
+    gemm_case(16, 2048, 2112, swiglu=True, path="decode", seed=G, G=G)
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_group_size_32_bit_exact_integer_inputs(path):
+    """Ternary activations with power-of-two scales at G = 32: exact sums,
+    bit-exact fp16 output."""
+    for M, K, N in [(3, 1024, 1088), (90, 2048, 2048)]:
+        W = synth.grid_weights(K, N, p=4, seed=M, group=32)
+        A = synth.ternary_activations(M, K, density=1.0, seed=M)
+        w = w4a16.load_weight(W, G=32)
+        out = fp16_out(w4a16.gemm(to_dev(A), w, path=path))
+        packed_o, s16_o = orc().quantize_pack(W, 32)
+        assert np.array_equal(out.astype(np.float64), orc().gemm_f64(A, packed_o, s16_o, 32))

@@ -48,8 +48,11 @@ int check_shape(int64_t K, int64_t N, int G, const char *who) {
 int check_gpu_shape(int64_t K, int64_t N, int G, const char *who) {
   int rc = check_shape(K, N, G, who);
   if (rc != W4A16_OK) return rc;
-  if (G != kGroup)
-    return fail(W4A16_ERR_UNSUPPORTED, "%s: GPU paths support G == 128 only (got %d)", who, G);
+  if (K % kGroup != 0)
+    return fail(W4A16_ERR_INVALID, "%s: K (%lld) must be a multiple of 128", who, (long long)K);
+  if (G < 32 || group_shift(K, G) < 0)
+    return fail(W4A16_ERR_UNSUPPORTED,
+                "%s: G must be a power of two >= 32 dividing K, or K itself (got %d)", who, G);
   if (N % 8 != 0)
     return fail(W4A16_ERR_INVALID, "%s: N (%lld) must be a multiple of 8", who, (long long)N);
   if (K > (int64_t)1 << 30 || N > (int64_t)1 << 30)
@@ -146,7 +149,7 @@ int run_gemm(const uint16_t *A, int64_t M, int64_t K, const void *rw, const void
   if (path < W4A16_PATH_DECODE || path > W4A16_PATH_DENSE)
     return fail(W4A16_ERR_INVALID, "%s: unknown path %d", who, path);
 
-  Problem p{A, M, K, N, rw, rs, out, swiglu, bf16, rowscale};
+  Problem p{A, M, K, N, rw, rs, out, swiglu, bf16, rowscale, G, group_shift(K, G)};
   const int64_t need = workspace_for(path, p);
   void *ws = workspace;
   if (need > 0) {
@@ -225,10 +228,11 @@ int w4a16_pack_gain(const float *W_d, const float *gamma_d, int64_t K, int64_t N
   const char *who = gamma_d != nullptr ? "w4a16_pack_gain" : "w4a16_pack";
   int rc = check_shape(K, N, G, who);
   if (rc != W4A16_OK) return rc;
-  if (G != kGroup) return fail(W4A16_ERR_UNSUPPORTED, "%s: GPU pack supports G == 128", who);
+  if (G % 8 != 0)
+    return fail(W4A16_ERR_UNSUPPORTED, "%s: the GPU packer needs G % 8 == 0 (got %d)", who, G);
   if (K / G > 65535) return fail(W4A16_ERR_INVALID, "%s: K too large", who);
   if (!W_d || !packed_d || !scales_d) return fail(W4A16_ERR_INVALID, "%s: null pointer", who);
-  hipError_t e = launch_pack(W_d, gamma_d, K, N, packed_d, scales_d, (hipStream_t)stream);
+  hipError_t e = launch_pack(W_d, gamma_d, K, N, G, packed_d, scales_d, (hipStream_t)stream);
   return e == hipSuccess ? W4A16_OK : hip_fail(e, who);
 }
 
@@ -298,7 +302,7 @@ int64_t w4a16_repacked_weight_bytes(int64_t K, int64_t N, int G) {
 int64_t w4a16_repacked_scale_bytes(int64_t K, int64_t N, int G) {
   int rc = check_gpu_shape(K, N, G, "w4a16_repacked_scale_bytes");
   if (rc != W4A16_OK) return rc;
-  return ceil_div(N, kStrip) * ceil_div(K / kGroup, 8) * 32 * 8 * 2;
+  return ceil_div(N, kStrip) * ceil_div(groups_of(K, G), 8) * 32 * 8 * 2;
 }
 
 int w4a16_repack(const int32_t *packed_d, const uint16_t *scales_d, int64_t K, int64_t N, int G,
@@ -309,7 +313,7 @@ int w4a16_repack(const int32_t *packed_d, const uint16_t *scales_d, int64_t K, i
     return fail(W4A16_ERR_INVALID, "w4a16_repack: null pointer");
   if (!aligned16(rw_d) || !aligned16(rs_d))
     return fail(W4A16_ERR_INVALID, "w4a16_repack: repacked buffers must be 16-byte aligned");
-  hipError_t e = launch_repack(packed_d, scales_d, K, N, rw_d, rs_d, (hipStream_t)stream);
+  hipError_t e = launch_repack(packed_d, scales_d, K, N, G, rw_d, rs_d, (hipStream_t)stream);
   return e == hipSuccess ? W4A16_OK : hip_fail(e, "w4a16_repack");
 }
 
@@ -321,7 +325,7 @@ int w4a16_unrepack(const void *rw_d, const void *rs_d, int64_t K, int64_t N, int
     return fail(W4A16_ERR_INVALID, "w4a16_unrepack: null pointer");
   if (!aligned16(rw_d) || !aligned16(rs_d))
     return fail(W4A16_ERR_INVALID, "w4a16_unrepack: repacked buffers must be 16-byte aligned");
-  hipError_t e = launch_unrepack(rw_d, rs_d, K, N, packed_d, scales_d, (hipStream_t)stream);
+  hipError_t e = launch_unrepack(rw_d, rs_d, K, N, G, packed_d, scales_d, (hipStream_t)stream);
   return e == hipSuccess ? W4A16_OK : hip_fail(e, "w4a16_unrepack");
 }
 
@@ -332,7 +336,7 @@ static int dequant_common(const void *rw_d, const void *rs_d, int64_t K, int64_t
   if (!rw_d || !rs_d || !W_d) return fail(W4A16_ERR_INVALID, "%s: null pointer", who);
   if (!aligned16(rw_d) || !aligned16(rs_d))
     return fail(W4A16_ERR_INVALID, "%s: repacked buffers must be 16-byte aligned", who);
-  hipError_t e = launch_dequant_canonical(rw_d, rs_d, K, N, bf16, W_d, stream);
+  hipError_t e = launch_dequant_canonical(rw_d, rs_d, K, N, G, bf16, W_d, stream);
   return e == hipSuccess ? W4A16_OK : hip_fail(e, who);
 }
 
@@ -405,7 +409,7 @@ int64_t w4a16_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N, int G, int f
   int path = flags & 0xF;
   if (path == W4A16_PATH_AUTO) path = select_path(M, K, N);
   Problem p{nullptr, M, K, N, nullptr, nullptr, nullptr, (flags & W4A16_FLAG_SWIGLU) != 0,
-            (flags & W4A16_FLAG_BF16) != 0};
+            (flags & W4A16_FLAG_BF16) != 0, nullptr, G, group_shift(K, G)};
   return workspace_for(path, p);
 }
 
@@ -424,7 +428,8 @@ int w4a16_describe(int64_t M, int64_t K, int64_t N, int G, int flags, char *buf,
   if (path == W4A16_PATH_AUTO) path = select_path(M, K, N);
   if (path < W4A16_PATH_DECODE || path > W4A16_PATH_DENSE)
     return fail(W4A16_ERR_INVALID, "w4a16_describe: unknown path %d", path);
-  Problem p{nullptr, M, K, N, nullptr, nullptr, nullptr, swiglu, (flags & W4A16_FLAG_BF16) != 0};
+  Problem p{nullptr, M, K, N, nullptr, nullptr, nullptr, swiglu, (flags & W4A16_FLAG_BF16) != 0,
+            nullptr, G, group_shift(K, G)};
   char tmp[512];
   int k;
   if (path == W4A16_PATH_DECODE) {

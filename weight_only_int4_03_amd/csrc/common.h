@@ -25,7 +25,7 @@
 
 namespace w4a16 {
 
-constexpr int kGroup = 128;   // quantization group along K
+constexpr int kGroup = 128;   // k per decode unit and per prefill step (the default group)
 constexpr int kTileK = 64;    // k per repacked tile
 constexpr int kStrip = 32;    // columns per strip
 constexpr int kTileWords = 256;
@@ -117,6 +117,10 @@ struct Dequant {
       c_hi = -72.0f * s;
     }
   };
+  // The scaled weights of either type as a raw 16-byte MFMA operand.
+  template <bool BF>
+  __device__ __forceinline__ uint4_t scaled_bits(uint32_t w, uint16_t s16) const;
+
   __device__ __forceinline__ bf16x8_t scaled_bf16(uint32_t w, const BScale &b) const {
     const uint32_t t = w >> 8;
     const half2_t x0 = bitcast<half2_t>((w & mask_lo) | magic);
@@ -146,6 +150,16 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
 
 __device__ __forceinline__ uint16_t to_half_bits(float v) {
   return bitcast<uint16_t>((_Float16)v);
+}
+
+template <bool BF>
+__device__ __forceinline__ uint4_t Dequant::scaled_bits(uint32_t w, uint16_t s16) const {
+  if constexpr (BF) {
+    return bitcast<uint4_t>(scaled_bf16(w, BScale(s16)));
+  } else {
+    const _Float16 sh = bitcast<_Float16>(s16);
+    return bitcast<uint4_t>(scaled(w, half2_t{sh, sh}));
+  }
 }
 
 // Output element bits: fp16, or bf16 (round to nearest even) for bf16
@@ -201,20 +215,45 @@ struct Problem {
   bool swiglu;
   bool bf16;       // A and the output are bf16 (else fp16)
   const float *rowscale;  // per-row output factor [M], or null
+  int G = kGroup;  // quantization group along K
+  int gshift = 7;  // group of k = k >> gshift (see group_shift)
 };
 
-hipError_t launch_pack(const float *W, const float *gamma, int64_t K, int64_t N, int32_t *packed,
-                       uint16_t *scales, hipStream_t s);
+// Group sizes: a power of two >= 32 that divides K, or K itself
+// (channelwise).  The kernels find the group of k as k >> gshift; for a
+// channelwise G that is not a power of two gshift is 31, so every k maps to
+// group 0.
+inline int group_shift(int64_t K, int G) {
+  if ((G & (G - 1)) == 0) {
+    int s = 0;
+    while ((1 << s) < G) ++s;
+    return s;
+  }
+  return G == K ? 31 : -1;
+}
+
+// Groups per column and its octets (the repacked scale layout holds eight
+// consecutive groups of a column in one 16-byte run).
+inline int64_t groups_of(int64_t K, int G) { return K / G; }
+
+// Index of the scale of group g, strip st, column c of the strip in the
+// repacked scale buffer [NS][KG8][32][8].
+__host__ __device__ inline int64_t scale_index(int64_t st, int64_t KG8, int c, int g) {
+  return ((st * KG8 + (g >> 3)) * 32 + c) * 8 + (g & 7);
+}
+
+hipError_t launch_pack(const float *W, const float *gamma, int64_t K, int64_t N, int G,
+                       int32_t *packed, uint16_t *scales, hipStream_t s);
 // RMSNorm row factors rho[m] = (sum_k A[m,k]^2 / K + eps)^(-1/2) (rms.hip).
 hipError_t launch_rms_rowscale(const uint16_t *A, int64_t M, int64_t K, float eps, bool bf16,
                                float *rho, hipStream_t s);
 hipError_t launch_repack(const int32_t *packed, const uint16_t *scales, int64_t K, int64_t N,
-                         void *rw, void *rs, hipStream_t s);
-hipError_t launch_unrepack(const void *rw, const void *rs, int64_t K, int64_t N, int32_t *packed,
-                           uint16_t *scales, hipStream_t s);
-hipError_t launch_dequant_canonical(const void *rw, const void *rs, int64_t K, int64_t N,
+                         int G, void *rw, void *rs, hipStream_t s);
+hipError_t launch_unrepack(const void *rw, const void *rs, int64_t K, int64_t N, int G,
+                           int32_t *packed, uint16_t *scales, hipStream_t s);
+hipError_t launch_dequant_canonical(const void *rw, const void *rs, int64_t K, int64_t N, int G,
                                     bool bf16, uint16_t *W, hipStream_t s);
-hipError_t launch_dequant_fragment(const void *rw, const void *rs, int64_t K, int64_t N,
+hipError_t launch_dequant_fragment(const void *rw, const void *rs, int64_t K, int64_t N, int G,
                                    bool bf16, uint16_t *Wf, hipStream_t s);
 
 // Decode path: workspace bytes (split-K partials), the launch, and a text

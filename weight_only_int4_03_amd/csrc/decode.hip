@@ -46,11 +46,18 @@ struct DecodeFrag {
   static constexpr int NA = MT == 16 ? 4 : 8;  // 16-byte activation vectors per group
   uint4_t b[SPW][NB];
   uint4_t a[NA];
-  uint16_t sc[SPW][MT == 16 ? 2 : 1];
+  // Scales per strip, 16-column half (MT=16) and 64-k tile (MT=32, which
+  // can span two groups when G < 128).
+  uint16_t sc[SPW][MT == 16 ? 2 : 1][MT == 16 ? 1 : 2];
 };
 
-template <int MT, int SPW, int WAVES, int D, int RPL, bool SWIGLU, bool BF>
+// PRE: the weights are scaled before the MFMA (bf16 activations, whose
+// weights are rounded to bf16, and groups shorter than the 128-k unit, whose
+// lanes meet different scales within one MFMA); otherwise each 128-k unit is
+// accumulated unscaled and its tile scaled once afterwards.
+template <int MT, int SPW, int WAVES, int D, int RPL, bool SWIGLU, bool BF, bool PRE>
 __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
+  static_assert(PRE || !BF, "bf16 weights are always scaled before the MFMA");
   static_assert(MT == 16 ? (RPL >= 1 && RPL <= 4) : RPL == 16, "rows per lane");
   extern __shared__ float lds[];  // [WAVES][SPW][M][32]
   constexpr int SH = SWIGLU ? SPW / 2 : SPW;
@@ -93,14 +100,16 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
   const uint32_t wlane = MT == 16 ? (uint32_t)(((g4 >> 1) * 64 + (g4 & 1) * 32 + c16) * 16)
                                   : (uint32_t)(lane * 16);
   const uint32_t slane = (uint32_t)((MT == 16 ? c16 : c32) * 16);
+  // k offset, within a 128-k unit, of the lane's first weight (tile x = 0).
+  const int klane = MT == 16 ? 32 * g4 : 32 * h;
   const uint32_t alane = MT == 16 ? (uint32_t)(g4 * 64) : (uint32_t)(h * 64);
   const char *Ab = (const char *)p.A;
 
   // Every address is a uniform base plus one 32-bit lane offset (plus a
   // constant), which maps onto the scalar-base form of the global loads.
+  auto soff = [&](int grp) { return (uint32_t)(grp >> 3) * 512u + (uint32_t)(grp & 7) * 2u + slane; };
   auto load = [&](Frag &f, int g) {
     const uint32_t ow = (uint32_t)g * 2048u + wlane;
-    const uint32_t os = (uint32_t)(g >> 3) * 512u + (uint32_t)(g & 7) * 2u + slane;
 #pragma unroll
     for (int s = 0; s < SPW; ++s) {
       const char *wp = wbase[s] + ow;
@@ -111,9 +120,24 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
 #pragma unroll
         for (int x = 0; x < 2; ++x) f.b[s][x] = load_nt((const uint4_t *)(wp + x * 1024));
       }
-      const char *sp = sbase[s] + os;
+      if constexpr (PRE) {
+        if constexpr (MT == 16) {
+          const char *sp = sbase[s] + soff((128 * g + klane) >> p.gshift);
 #pragma unroll
-      for (int part = 0; part < NPART; ++part) f.sc[s][part] = *(const uint16_t *)(sp + part * 256);
+          for (int part = 0; part < 2; ++part)
+            f.sc[s][part][0] = *(const uint16_t *)(sp + part * 256);
+        } else {
+#pragma unroll
+          for (int x = 0; x < 2; ++x)
+            f.sc[s][0][x] =
+                *(const uint16_t *)(sbase[s] + soff((128 * g + 64 * x + klane) >> p.gshift));
+        }
+      } else {
+        const char *sp = sbase[s] + soff((128 * g) >> p.gshift);
+#pragma unroll
+        for (int part = 0; part < NPART; ++part)
+          f.sc[s][part][0] = *(const uint16_t *)(sp + part * 256);
+      }
     }
     const char *ag = Ab + (uint32_t)(arow_off + (uint32_t)g * 256u + alane);
     if constexpr (MT == 16) {
@@ -134,27 +158,27 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
     for (int part = 0; part < NPART; ++part) acc[s][part] = acc_t{};
 
   auto compute = [&](const Frag &f) {
-    if constexpr (BF) {
-      // bf16: the weights are scaled (and rounded to bf16) before the MFMA,
-      // which then accumulates straight into the FP32 accumulator.
+    if constexpr (PRE) {
+      // Scaled weights (rounded to fp16 or bf16) into the MFMA, which
+      // accumulates straight into the FP32 accumulator.
 #pragma unroll
       for (int s = 0; s < SPW; ++s) {
 #pragma unroll
         for (int part = 0; part < NPART; ++part) {
-          const Dequant::BScale bs(f.sc[s][part]);
           if constexpr (MT == 16) {
+            const uint16_t sc = f.sc[s][part][0];
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-              acc[s][part] = mfma16<true>(
-                  f.a[j], bitcast<uint4_t>(dq.scaled_bf16(f.b[s][part][j], bs)), acc[s][part]);
+              acc[s][part] = mfma16<BF>(f.a[j], dq.scaled_bits<BF>(f.b[s][part][j], sc),
+                                        acc[s][part]);
           } else {
 #pragma unroll
             for (int x = 0; x < 2; ++x)
 #pragma unroll
               for (int j = 0; j < 4; ++j)
-                acc[s][part] = mfma32<true>(f.a[4 * x + j],
-                                            bitcast<uint4_t>(dq.scaled_bf16(f.b[s][x][j], bs)),
-                                            acc[s][part]);
+                acc[s][part] = mfma32<BF>(f.a[4 * x + j],
+                                          dq.scaled_bits<BF>(f.b[s][x][j], f.sc[s][0][x]),
+                                          acc[s][part]);
           }
         }
       }
@@ -178,7 +202,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
               t = __builtin_amdgcn_mfma_f32_32x32x16_f16(bitcast<half8_t>(f.a[4 * x + j]),
                                                          dq(f.b[s][x][j]), t, 0, 0, 0);
         }
-        const float sc = (float)bitcast<_Float16>(f.sc[s][part]);
+        const float sc = (float)bitcast<_Float16>(f.sc[s][part][0]);
         // Element r of a lane's tile holds row 4*g4 + r (MT=16), so with
         // M < 4 only elements r < RPL can hold real rows.
 #pragma unroll
@@ -330,8 +354,10 @@ int decode_describe(const Problem &p, char *buf, size_t n) {
   }
   const DecodeConfig c = decode_config(p);
   const int rpl = c.MT == 16 ? (p.M == 1 ? 1 : 4) : 16;
-  int k = snprintf(buf, n, "decode_kernel<%d, %d, %d, %d, %d, %s, %s> workgroups=%d threads=%d ks=%d",
-                   c.MT, c.SPW, c.WAVES, c.D, rpl, sw, bf, c.nsg * c.KS, c.WAVES * 64, c.KS);
+  const char *pre = (p.bf16 || p.G < kGroup) ? "true" : "false";
+  int k = snprintf(buf, n,
+                   "decode_kernel<%d, %d, %d, %d, %d, %s, %s, %s> workgroups=%d threads=%d ks=%d",
+                   c.MT, c.SPW, c.WAVES, c.D, rpl, sw, bf, pre, c.nsg * c.KS, c.WAVES * 64, c.KS);
   if (c.KS > 1 && k > 0 && (size_t)k < n)
     k += snprintf(buf + k, n - k, "; decode_reduce_kernel<%d, %s, %s>", c.SPW, sw, bf);
   return k;
@@ -349,36 +375,36 @@ int64_t decode_workspace_bytes(const Problem &p) {
   return (int64_t)c.nsg * c.KS * c.SPW * p.M * 32 * (int64_t)sizeof(float);
 }
 
-template <int MT, int SPW, int WAVES, int D, int RPL, bool SWIGLU, bool BF>
+template <int MT, int SPW, int WAVES, int D, int RPL, bool SWIGLU, bool BF, bool PRE>
 static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t s) {
   const size_t lds = (size_t)WAVES * SPW * a.M * 32 * sizeof(float);
-  hipLaunchKernelGGL((decode_kernel<MT, SPW, WAVES, D, RPL, SWIGLU, BF>), dim3(a.nsg * a.KS),
+  hipLaunchKernelGGL((decode_kernel<MT, SPW, WAVES, D, RPL, SWIGLU, BF, PRE>), dim3(a.nsg * a.KS),
                      dim3(WAVES * 64), lds, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.KS == 1) return e;
   return launch_decode_reduce(a, SWIGLU, BF, s);
 }
 
-template <int MT, int SPW, int RPL, bool SWIGLU, bool BF>
+template <int MT, int SPW, int RPL, bool SWIGLU, bool BF, bool PRE>
 static hipError_t launch_decode_w(const DecodeArgs &a, const DecodeConfig &c, hipStream_t s) {
   if (c.D == 4)
-    return c.WAVES == 8 ? launch_decode_t<MT, SPW, 8, 4, RPL, SWIGLU, BF>(a, s)
-                        : launch_decode_t<MT, SPW, 4, 4, RPL, SWIGLU, BF>(a, s);
-  return c.WAVES == 8 ? launch_decode_t<MT, SPW, 8, 2, RPL, SWIGLU, BF>(a, s)
-                      : launch_decode_t<MT, SPW, 4, 2, RPL, SWIGLU, BF>(a, s);
+    return c.WAVES == 8 ? launch_decode_t<MT, SPW, 8, 4, RPL, SWIGLU, BF, PRE>(a, s)
+                        : launch_decode_t<MT, SPW, 4, 4, RPL, SWIGLU, BF, PRE>(a, s);
+  return c.WAVES == 8 ? launch_decode_t<MT, SPW, 8, 2, RPL, SWIGLU, BF, PRE>(a, s)
+                      : launch_decode_t<MT, SPW, 4, 2, RPL, SWIGLU, BF, PRE>(a, s);
 }
 
-template <bool BF>
+template <bool BF, bool PRE>
 static hipError_t launch_decode_bf(const Problem &p, const DecodeArgs &a, const DecodeConfig &c,
                                    hipStream_t s) {
   if (c.MT == 16 && p.M == 1)
-    return p.swiglu ? launch_decode_w<16, 2, 1, true, BF>(a, c, s)
-                    : launch_decode_w<16, 1, 1, false, BF>(a, c, s);
+    return p.swiglu ? launch_decode_w<16, 2, 1, true, BF, PRE>(a, c, s)
+                    : launch_decode_w<16, 1, 1, false, BF, PRE>(a, c, s);
   if (c.MT == 16)
-    return p.swiglu ? launch_decode_w<16, 2, 4, true, BF>(a, c, s)
-                    : launch_decode_w<16, 1, 4, false, BF>(a, c, s);
-  return p.swiglu ? launch_decode_w<32, 2, 16, true, BF>(a, c, s)
-                  : launch_decode_w<32, 1, 16, false, BF>(a, c, s);
+    return p.swiglu ? launch_decode_w<16, 2, 4, true, BF, PRE>(a, c, s)
+                    : launch_decode_w<16, 1, 4, false, BF, PRE>(a, c, s);
+  return p.swiglu ? launch_decode_w<32, 2, 16, true, BF, PRE>(a, c, s)
+                  : launch_decode_w<32, 1, 16, false, BF, PRE>(a, c, s);
 }
 
 DecodeArgs decode_args(const Problem &p, int KS, void *workspace) {
@@ -392,7 +418,8 @@ DecodeArgs decode_args(const Problem &p, int KS, void *workspace) {
   a.NS = (int)ceil_div(p.N, kStrip);
   a.KT = (int)(p.K / kTileK);
   a.KG = (int)(p.K / kGroup);
-  a.KG8 = (int)ceil_div(a.KG, 8);
+  a.KG8 = (int)ceil_div(groups_of(p.K, p.G), 8);
+  a.gshift = p.gshift;
   a.out = p.out;
   a.ldo = (int)(p.swiglu ? p.N / 2 : p.N);
   a.KS = KS;
@@ -427,7 +454,9 @@ hipError_t launch_decode(const Problem &p, void *workspace, hipStream_t s) {
   const DecodeConfig c = decode_config(p);
   DecodeArgs a = decode_args(p, c.KS, workspace);
   if (c.KS > 1 && workspace == nullptr) return hipErrorInvalidValue;
-  return p.bf16 ? launch_decode_bf<true>(p, a, c, s) : launch_decode_bf<false>(p, a, c, s);
+  if (p.bf16) return launch_decode_bf<true, true>(p, a, c, s);
+  return p.G < kGroup ? launch_decode_bf<false, true>(p, a, c, s)
+                      : launch_decode_bf<false, false>(p, a, c, s);
 }
 
 }  // namespace w4a16

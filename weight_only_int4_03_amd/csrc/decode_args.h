@@ -20,6 +20,7 @@ struct DecodeArgs {
   int valid_strips;  // plain: NS; SwiGLU: number of gate strips
   float *ws;         // KS > 1: partial tiles [nsg][KS][SPW][M][32]
   const float *rowscale;  // per-row output factor, or null
+  int gshift;        // group of k = k >> gshift (KG counts 128-k units, KG8 scale octets)
 };
 
 // Epilogue of one element e of strip group sg's tile (tile element order

@@ -118,7 +118,7 @@ __global__ __launch_bounds__(WC * WK * 64) void decode_coop_kernel(DecodeArgs p)
       const int strip = SWIGLU && s >= SH ? base + p.up_off : base;
       int gg = g0 + wkk;
       gg = gg < ge ? gg : ge - 1;
-      scv[t] = p.rs[(((int64_t)strip * p.KG8 + (gg >> 3)) * 32 + c) * 8 + (gg & 7)];
+      scv[t] = p.rs[scale_index(strip, p.KG8, c, (gg * 128) >> p.gshift)];
     }
   };
   // Stores are unconditional too: threads past the end repeat the last
@@ -379,6 +379,7 @@ bool coop_config(const Problem &p, int &WC, int &WK, int &KS) {
   const int nsg = (int)(p.swiglu ? (p.N / 2 / kStrip) : ceil_div(p.N, kStrip));
   const int KG = (int)(p.K / kGroup);
   const int force = coop_env_raw("W4A16_DECODE_COOP");
+  if (p.G < kGroup) return false;  // one scale per column and 128-k unit
   bool use;
   if (nsg >= 384) {
     use = true;

@@ -19,21 +19,21 @@ namespace w4a16 {
 // is W'[k,n] = fp32(gamma[k] * W[k,n]).
 __global__ __launch_bounds__(256) void pack_kernel(const float *__restrict__ W,
                                                    const float *__restrict__ gamma, int64_t N,
-                                                   int32_t *__restrict__ packed,
+                                                   int G, int32_t *__restrict__ packed,
                                                    uint16_t *__restrict__ scales) {
   const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t g = blockIdx.y;
   if (n >= N) return;
-  const float *colw = W + g * kGroup * N + n;
-  const float *gam = gamma != nullptr ? gamma + g * kGroup : nullptr;
+  const float *colw = W + g * G * N + n;
+  const float *gam = gamma != nullptr ? gamma + g * G : nullptr;
   auto col = [&](int k) { return gam != nullptr ? __fmul_rn(gam[k], colw[k * N]) : colw[k * N]; };
   float amax = 0.0f;
 #pragma unroll 16
-  for (int k = 0; k < kGroup; ++k) amax = fmaxf(amax, fabsf(col(k)));
+  for (int k = 0; k < G; ++k) amax = fmaxf(amax, fabsf(col(k)));
   float s = __fdiv_rn(amax, 7.0f);
   s = s < 1e-8f ? 1e-8f : s;
 #pragma unroll 2
-  for (int r = 0; r < kGroup / 8; ++r) {
+  for (int r = 0; r < G / 8; ++r) {
     uint32_t word = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -41,15 +41,15 @@ __global__ __launch_bounds__(256) void pack_kernel(const float *__restrict__ W,
       q = fminf(fmaxf(q, -8.0f), 7.0f);
       word |= (uint32_t)((int)q + 8) << (4 * i);
     }
-    packed[(g * (kGroup / 8) + r) * N + n] = (int32_t)word;
+    packed[(g * (G / 8) + r) * N + n] = (int32_t)word;
   }
   scales[g * N + n] = to_half_bits(s);
 }
 
-hipError_t launch_pack(const float *W, const float *gamma, int64_t K, int64_t N, int32_t *packed,
-                       uint16_t *scales, hipStream_t s) {
-  dim3 grid((unsigned)ceil_div(N, 256), (unsigned)(K / kGroup));
-  hipLaunchKernelGGL(pack_kernel, grid, dim3(256), 0, s, W, gamma, N, packed, scales);
+hipError_t launch_pack(const float *W, const float *gamma, int64_t K, int64_t N, int G,
+                       int32_t *packed, uint16_t *scales, hipStream_t s) {
+  dim3 grid((unsigned)ceil_div(N, 256), (unsigned)(K / G));
+  hipLaunchKernelGGL(pack_kernel, grid, dim3(256), 0, s, W, gamma, N, G, packed, scales);
   return hipGetLastError();
 }
 
@@ -122,18 +122,18 @@ __global__ __launch_bounds__(256) void repack_kernel(const int32_t *__restrict__
   }
 }
 
-static void repack_geometry(int64_t K, int64_t N, int64_t &KT, int64_t &KG, int64_t &KG8,
+static void repack_geometry(int64_t K, int64_t N, int G, int64_t &KT, int64_t &KG, int64_t &KG8,
                             int64_t &NS) {
   KT = K / kTileK;
-  KG = K / kGroup;
+  KG = groups_of(K, G);
   KG8 = ceil_div(KG, 8);
   NS = ceil_div(N, kStrip);
 }
 
 hipError_t launch_repack(const int32_t *packed, const uint16_t *scales, int64_t K, int64_t N,
-                         void *rw, void *rs, hipStream_t s) {
+                         int G, void *rw, void *rs, hipStream_t s) {
   int64_t KT, KG, KG8, NS;
-  repack_geometry(K, N, KT, KG, KG8, NS);
+  repack_geometry(K, N, G, KT, KG, KG8, NS);
   const int64_t wblocks = ceil_div(NS * KT * 64, 256);
   const int64_t sblocks = ceil_div(NS * KG8 * 32, 256);
   hipLaunchKernelGGL(repack_kernel<true>, dim3((unsigned)(wblocks + sblocks)), dim3(256), 0, s,
@@ -142,10 +142,10 @@ hipError_t launch_repack(const int32_t *packed, const uint16_t *scales, int64_t 
   return hipGetLastError();
 }
 
-hipError_t launch_unrepack(const void *rw, const void *rs, int64_t K, int64_t N, int32_t *packed,
-                           uint16_t *scales, hipStream_t s) {
+hipError_t launch_unrepack(const void *rw, const void *rs, int64_t K, int64_t N, int G,
+                           int32_t *packed, uint16_t *scales, hipStream_t s) {
   int64_t KT, KG, KG8, NS;
-  repack_geometry(K, N, KT, KG, KG8, NS);
+  repack_geometry(K, N, G, KT, KG, KG8, NS);
   const int64_t wblocks = ceil_div(NS * KT * 64, 256);
   const int64_t sblocks = ceil_div(NS * KG8 * 32, 256);
   hipLaunchKernelGGL(repack_kernel<false>, dim3((unsigned)(wblocks + sblocks)), dim3(256), 0, s,
@@ -169,7 +169,8 @@ template <bool CANONICAL, bool BF>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint4_t *__restrict__ rw,
                                                       const uint16_t *__restrict__ rs,
                                                       uint16_t *__restrict__ W16, int64_t N,
-                                                      int64_t KT, int64_t KG8, int64_t NS) {
+                                                      int64_t KT, int64_t KG8, int64_t NS,
+                                                      int gshift) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= NS * KT * 64) return;
   const int l = (int)(idx & 63);
@@ -177,8 +178,8 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint4_t *__restrict_
   const int64_t q = tq % KT, t = tq / KT;
   const int h = l >> 5, c = l & 31;
   const int64_t n = t * kStrip + c;
-  const int64_t g = q >> 1;
-  const uint16_t s16 = rs[((t * KG8 + (g >> 3)) * 32 + c) * 8 + (g & 7)];
+  const int g = (int)((64 * q + 32 * h) >> gshift);
+  const uint16_t s16 = rs[scale_index(t, KG8, c, g)];
   const _Float16 sh = bitcast<_Float16>(s16);
   const half2_t s2 = {sh, sh};
   const Dequant::BScale bs(s16);
@@ -208,28 +209,29 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint4_t *__restrict_
 }
 
 template <bool CANONICAL>
-static hipError_t launch_dequant(const void *rw, const void *rs, int64_t K, int64_t N, bool bf16,
-                                 uint16_t *W, hipStream_t s) {
+static hipError_t launch_dequant(const void *rw, const void *rs, int64_t K, int64_t N, int G,
+                                 bool bf16, uint16_t *W, hipStream_t s) {
   int64_t KT, KG, KG8, NS;
-  repack_geometry(K, N, KT, KG, KG8, NS);
+  repack_geometry(K, N, G, KT, KG, KG8, NS);
+  const int gshift = group_shift(K, G);
   const dim3 grid((unsigned)ceil_div(NS * KT * 64, 256));
   if (bf16)
     hipLaunchKernelGGL((dequant_kernel<CANONICAL, true>), grid, dim3(256), 0, s,
-                       (const uint4_t *)rw, (const uint16_t *)rs, W, N, KT, KG8, NS);
+                       (const uint4_t *)rw, (const uint16_t *)rs, W, N, KT, KG8, NS, gshift);
   else
     hipLaunchKernelGGL((dequant_kernel<CANONICAL, false>), grid, dim3(256), 0, s,
-                       (const uint4_t *)rw, (const uint16_t *)rs, W, N, KT, KG8, NS);
+                       (const uint4_t *)rw, (const uint16_t *)rs, W, N, KT, KG8, NS, gshift);
   return hipGetLastError();
 }
 
-hipError_t launch_dequant_canonical(const void *rw, const void *rs, int64_t K, int64_t N,
+hipError_t launch_dequant_canonical(const void *rw, const void *rs, int64_t K, int64_t N, int G,
                                     bool bf16, uint16_t *W, hipStream_t s) {
-  return launch_dequant<true>(rw, rs, K, N, bf16, W, s);
+  return launch_dequant<true>(rw, rs, K, N, G, bf16, W, s);
 }
 
-hipError_t launch_dequant_fragment(const void *rw, const void *rs, int64_t K, int64_t N,
+hipError_t launch_dequant_fragment(const void *rw, const void *rs, int64_t K, int64_t N, int G,
                                    bool bf16, uint16_t *Wf, hipStream_t s) {
-  return launch_dequant<false>(rw, rs, K, N, bf16, Wf, s);
+  return launch_dequant<false>(rw, rs, K, N, G, bf16, Wf, s);
 }
 
 }  // namespace w4a16

@@ -54,6 +54,7 @@ struct PrefillArgs {
   int KS, spk;
   float *ws;
   const float *rowscale;  // per-row output factor, or null
+  int gshift;             // group of k = k >> gshift
 };
 
 template <int WN, bool DENSE>
@@ -132,8 +133,8 @@ void prefill_kernel(PrefillArgs p) {
           r.v[w][j] = sval[w] ? load_nt(p.rw + vec * 4 + j) : uint4_t{0, 0, 0, 0};
       } else {
         r.v[w][0] = sval[w] ? load_nt(p.rw + vec) : uint4_t{0, 0, 0, 0};
-        const int g = q >> 1;
-        r.sc[w] = sval[w] ? p.rs[(((int64_t)strip[w] * p.KG8 + (g >> 3)) * 32 + c) * 8 + (g & 7)]
+        const int g = (64 * q + 32 * h) >> p.gshift;
+        r.sc[w] = sval[w] ? p.rs[scale_index(strip[w], p.KG8, c, g)]
                           : (uint16_t)0;
       }
     }
@@ -263,7 +264,7 @@ void prefill2_kernel(PrefillArgs p) {
   __shared__ uint4_t lds1[BM * CH];
   struct BRegs {
     uint4_t v[2][TPS][NV];
-    uint32_t sc0, sc1;
+    uint32_t sc[2][TPS];  // per strip and 64-k tile (tiles may lie in different groups)
   };
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -356,10 +357,14 @@ void prefill2_kernel(PrefillArgs p) {
               rw, w_off[w] + 16 * j, (TPS * q + t) * 1024 * NV, kBufferNT));
     }
     if constexpr (!DENSE) {
-      const int g = (TPS * q) >> 1;
-      const int g_off = (g >> 3) * 512 + (g & 7) * 2;
-      r.sc0 = __builtin_amdgcn_raw_buffer_load_b16(rsc, s_off[0], g_off, 0);
-      r.sc1 = __builtin_amdgcn_raw_buffer_load_b16(rsc, s_off[1], g_off, 0);
+#pragma unroll
+      for (int t = 0; t < TPS; ++t) {
+        const int g = (64 * (TPS * q + t) + 32 * h) >> p.gshift;
+        const int g_off = (g >> 3) * 512 + (g & 7) * 2;
+#pragma unroll
+        for (int w = 0; w < 2; ++w)
+          r.sc[w][t] = __builtin_amdgcn_raw_buffer_load_b16(rsc, s_off[w] + g_off, 0, 0);
+      }
     }
   };
 
@@ -371,7 +376,6 @@ void prefill2_kernel(PrefillArgs p) {
 
   const int rbase = wm * 32 * MI;
   auto compute = [&](const uint4_t *stage, const BRegs &r) {
-    const uint16_t sc[2] = {(uint16_t)r.sc0, (uint16_t)r.sc1};
 #pragma unroll
     for (int jj = 0; jj < 4 * TPS; ++jj) {
       const int t = jj >> 2, j = jj & 3;
@@ -381,9 +385,10 @@ void prefill2_kernel(PrefillArgs p) {
         if constexpr (DENSE) {
           bf[w] = r.v[w][t][j];
         } else if constexpr (BF) {
-          bf[w] = bitcast<uint4_t>(dq.scaled_bf16(r.v[w][t][0][j], Dequant::BScale(sc[w])));
+          bf[w] = bitcast<uint4_t>(
+              dq.scaled_bf16(r.v[w][t][0][j], Dequant::BScale((uint16_t)r.sc[w][t])));
         } else {
-          const _Float16 sh = bitcast<_Float16>(sc[w]);
+          const _Float16 sh = bitcast<_Float16>((uint16_t)r.sc[w][t]);
           bf[w] = bitcast<uint4_t>(dq.scaled(r.v[w][t][0][j], half2_t{sh, sh}));
         }
       }
@@ -527,7 +532,8 @@ static PrefillArgs prefill_args(const Problem &p, int BM, const void *weights) {
   a.N = (int)p.N;
   a.NS = (int)ceil_div(p.N, kStrip);
   a.KT = (int)(p.K / kTileK);
-  a.KG8 = (int)ceil_div(p.K / kGroup, 8);
+  a.KG8 = (int)ceil_div(groups_of(p.K, p.G), 8);
+  a.gshift = p.gshift;
   a.out = p.out;
   a.ldo = (int)(p.swiglu ? p.N / 2 : p.N);
   a.up_off = (int)(p.N / 2 / kStrip);
@@ -580,7 +586,7 @@ static bool fits_buffer_offsets(const Problem &p, bool dense) {
   const int64_t limit = (int64_t)1 << 31;
   const int64_t ns = ceil_div(p.N, kStrip);
   return p.M * p.K * 2 < limit && ns * (p.K / kTileK) * 1024 * (dense ? 4 : 1) < limit &&
-         ns * ceil_div(p.K / kGroup, 8) * 512 < limit && p.M * p.N * 4 < limit;
+         ns * ceil_div(groups_of(p.K, p.G), 8) * 512 < limit && p.M * p.N * 4 < limit;
 }
 
 // Compute units of the current device (256 on MI355X), cached per device.
@@ -748,7 +754,7 @@ int64_t dense_workspace_bytes(const Problem &p) {
 hipError_t launch_dense(const Problem &p, void *workspace, hipStream_t s) {
   if (workspace == nullptr) return hipErrorInvalidValue;
   void *w16f = workspace;
-  hipError_t e = launch_dequant_fragment(p.rw, p.rs, p.K, p.N, p.bf16, (uint16_t *)w16f, s);
+  hipError_t e = launch_dequant_fragment(p.rw, p.rs, p.K, p.N, p.G, p.bf16, (uint16_t *)w16f, s);
   if (e != hipSuccess) return e;
   Prefill2Config c;
   if (prefill2_config(p, true, c)) return launch_prefill2_m<4, true>(p, w16f, c, nullptr, s);

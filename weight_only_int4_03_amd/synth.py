@@ -96,14 +96,15 @@ def outlier_channels(K: int, rng: np.random.Generator) -> np.ndarray:
 
 # -- structured inputs for exact-result tests ------------------------------
 
-def grid_weights(K: int, N: int, p: int = 6, seed: int = 0) -> np.ndarray:
+def grid_weights(K: int, N: int, p: int = 6, seed: int = 0, group: int = G) -> np.ndarray:
     """W = j * 2^-p with integer j in [-7, 7], and one entry of every
     (group, column) set to +-7 * 2^-p, so that each group's maximum is exactly
-    7 * 2^-p (its scale is then 2^-p and the quantization is lossless)."""
+    7 * 2^-p (its scale is then 2^-p and the quantization is lossless).
+    ``group`` is the group size the property is built for."""
     rng = np.random.default_rng(seed)
     j = rng.integers(-7, 8, size=(K, N)).astype(np.float32)
-    rows = np.arange(0, K, G)[:, None] + rng.integers(0, G, size=(K // G, N))
-    sign = np.where(rng.integers(0, 2, size=(K // G, N)) == 0, -7.0, 7.0).astype(np.float32)
+    rows = np.arange(0, K, group)[:, None] + rng.integers(0, group, size=(K // group, N))
+    sign = np.where(rng.integers(0, 2, size=(K // group, N)) == 0, -7.0, 7.0).astype(np.float32)
     j[rows, np.arange(N)[None, :]] = sign
     return j * np.float32(2.0 ** -p)
 

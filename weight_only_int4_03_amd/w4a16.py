@@ -154,11 +154,11 @@ def pack(W, G: int = G, stream=None, gamma=None):
 class RepackedWeight:
     """Repacked device buffers of one [K,N] weight (built by :func:`repack`)."""
 
-    def __init__(self, rw, rs, K: int, N: int):
-        self.rw, self.rs, self.K, self.N = rw, rs, K, N
+    def __init__(self, rw, rs, K: int, N: int, G: int = G):
+        self.rw, self.rs, self.K, self.N, self.G = rw, rs, K, N, G
 
     def clone(self) -> "RepackedWeight":
-        return RepackedWeight(self.rw.clone(), self.rs.clone(), self.K, self.N)
+        return RepackedWeight(self.rw.clone(), self.rs.clone(), self.K, self.N, self.G)
 
     @property
     def nbytes(self) -> int:
@@ -181,11 +181,12 @@ def repack(packed, scales, G: int = G, stream=None) -> RepackedWeight:
     rs = torch.empty(sb, dtype=torch.uint8, device=packed.device)
     _check(lib().w4a16_repack(_ptr(packed), _ptr(scales), K, N, G, _ptr(rw), _ptr(rs),
                               _stream(stream)))
-    return RepackedWeight(rw, rs, K, N)
+    return RepackedWeight(rw, rs, K, N, G)
 
 
-def unrepack(w: RepackedWeight, G: int = G, stream=None):
+def unrepack(w: RepackedWeight, G: int | None = None, stream=None):
     torch = _torch()
+    G = w.G if G is None else G
     packed = torch.empty((w.K // 8, w.N), dtype=torch.int32, device=w.rw.device)
     scales = torch.empty((w.K // G, w.N), dtype=torch.int16, device=w.rw.device)
     _check(lib().w4a16_unrepack(_ptr(w.rw), _ptr(w.rs), w.K, w.N, G, _ptr(packed),
@@ -193,9 +194,10 @@ def unrepack(w: RepackedWeight, G: int = G, stream=None):
     return packed, scales
 
 
-def dequant(w: RepackedWeight, G: int = G, stream=None, bf16: bool = False):
+def dequant(w: RepackedWeight, G: int | None = None, stream=None, bf16: bool = False):
     """fp16 (or, with bf16, bf16) [K,N] dequantized weights (canonical row-major)."""
     torch = _torch()
+    G = w.G if G is None else G
     W = torch.empty((w.K, w.N), dtype=torch.bfloat16 if bf16 else torch.float16,
                     device=w.rw.device)
     fn = lib().w4a16_dequant_bf16 if bf16 else lib().w4a16_dequant
@@ -209,10 +211,11 @@ def _flags(path, swiglu: bool, bf16: bool) -> int:
 
 
 def gemm(A, w: RepackedWeight, swiglu: bool = False, path: str | int = "auto", out=None,
-         workspace=None, G: int = G, stream=None, rowscale=None):
+         workspace=None, G: int | None = None, stream=None, rowscale=None):
     """C = A * dequant(W) ([M,N] in A's dtype, fp16 or bf16); with swiglu,
     Z = silu(C[:, :N/2]) * C[:, N/2:]."""
     torch = _torch()
+    G = w.G if G is None else G
     assert A.is_cuda and A.dtype in (torch.float16, torch.bfloat16) and A.is_contiguous()
     bf16 = A.dtype == torch.bfloat16
     M, K = A.shape
@@ -247,23 +250,25 @@ def rms_rowscale(A, eps: float = 1e-5, stream=None):
     return rho
 
 
-def gemm_plain(A, w: RepackedWeight, out=None, G: int = G, stream=None):
+def gemm_plain(A, w: RepackedWeight, out=None, G: int | None = None, stream=None):
     """w4a16_gemm (automatic path, library workspace)."""
     torch = _torch()
     M, K = A.shape
     if out is None:
         out = torch.empty((M, w.N), dtype=torch.float16, device=A.device)
+    G = w.G if G is None else G
     _check(lib().w4a16_gemm(_ptr(A), M, K, _ptr(w.rw), _ptr(w.rs), w.N, G, _ptr(out),
                             _stream(stream)))
     return out
 
 
-def gemm_swiglu(A, w: RepackedWeight, out=None, G: int = G, stream=None):
+def gemm_swiglu(A, w: RepackedWeight, out=None, G: int | None = None, stream=None):
     """w4a16_gemm_swiglu (automatic path, library workspace)."""
     torch = _torch()
     M, K = A.shape
     if out is None:
         out = torch.empty((M, w.N // 2), dtype=torch.float16, device=A.device)
+    G = w.G if G is None else G
     _check(lib().w4a16_gemm_swiglu(_ptr(A), M, K, _ptr(w.rw), _ptr(w.rs), w.N, G, _ptr(out),
                                    _stream(stream)))
     return out
