@@ -7,7 +7,10 @@ with the HIP library (``weight_only_int4_03_amd``) and imports nothing from it.
 Every function follows the page "GPU Kernels for INT4 Inference, in depth"
 (aicassindra.com), sections "The job, stated precisely" and "The data
 contract", except ``swiglu_f64``, which follows the SwiGLU line of the block
-equations in FuTransformer (arXiv 2610.23796), section 2.1.
+equations in FuTransformer (arXiv 2610.23796), section 2.1, the RMSNorm
+folding helpers (FuTransformer, section 3.2.2), and the zero-point functions
+(``zero_rows``, ``dequant_zp``), which follow the Swordfish page
+(blog.alpindale.net), section "The packed format".
 """
 from __future__ import annotations
 
@@ -58,6 +61,9 @@ class Oracle:
         lib.oracle_fold_gain.argtypes = [_p, _p, _i64, _i64, _p]
         lib.oracle_rms_rowscale_f64.argtypes = [_p, _i64, _i64, ctypes.c_int, ctypes.c_double, _p]
         lib.oracle_scale_rows.argtypes = [_p, _i64, _i64, _p, _p]
+        lib.oracle_zero_rows.argtypes = [_p, _p, _i64, _i64, _p]
+        lib.oracle_dequant_zp.argtypes = [_p, _p, _p, _i64, _i64, ctypes.c_int, ctypes.c_int, _p]
+        lib.oracle_gemm_wb_f64.argtypes = [_p, _i64, _i64, _p, _i64, _p, ctypes.c_int]
         lib.oracle_gemm_bf16_f64.argtypes = [_p, _i64, _i64, _p, _p, _i64, ctypes.c_int, _p,
                                              ctypes.c_int]
         lib.oracle_quantize.argtypes = [_p, _i64, _i64, ctypes.c_int, _p, _p]
@@ -156,6 +162,36 @@ class Oracle:
             raise ValueError("oracle_dequant_bf16 failed with status %d" % rc)
         return Wb
 
+    # -- zero points (Swordfish page, section "The packed format") ---------
+    def zero_rows(self, s16: np.ndarray, zp: np.ndarray) -> np.ndarray:
+        """fp16 bits [K/G,N] of the prescaled zero rows fp16((8 - zp) * s16)."""
+        s16 = np.ascontiguousarray(s16, dtype=np.uint16)
+        zp = np.ascontiguousarray(zp, dtype=np.uint8)
+        if zp.shape != s16.shape:
+            raise ValueError("zero points and scales differ in shape")
+        KG, N = s16.shape
+        z16 = np.empty((KG, N), np.uint16)
+        rc = self.lib.oracle_zero_rows(s16.ctypes.data, zp.ctypes.data, KG, N, z16.ctypes.data)
+        if rc != OK:
+            raise ValueError("oracle_zero_rows failed with status %d" % rc)
+        return z16
+
+    def dequant_zp(self, packed: np.ndarray, s16: np.ndarray, z16: np.ndarray, G: int = 128,
+                   bf16: bool = False) -> np.ndarray:
+        """fp16 (or bf16) bits [K,N] of (u-8)*s16 + z16, rounded once."""
+        packed = np.ascontiguousarray(packed, dtype=np.int32)
+        s16 = np.ascontiguousarray(s16, dtype=np.uint16)
+        z16 = np.ascontiguousarray(z16, dtype=np.uint16)
+        if z16.shape != s16.shape:
+            raise ValueError("zero rows and scales differ in shape")
+        R, N = packed.shape
+        W = np.empty((8 * R, N), np.uint16)
+        rc = self.lib.oracle_dequant_zp(packed.ctypes.data, s16.ctypes.data, z16.ctypes.data,
+                                        8 * R, N, G, int(bf16), W.ctypes.data)
+        if rc != OK:
+            raise ValueError("oracle_dequant_zp failed with status %d" % rc)
+        return W
+
     # -- products ---------------------------------------------------------
     def gemm_f64(self, A16: np.ndarray, packed: np.ndarray, s16: np.ndarray, G: int = 128,
                  nthreads: int = 0) -> np.ndarray:
@@ -206,6 +242,19 @@ class Oracle:
         C = np.empty((M, N), np.float64)
         self.lib.oracle_gemm_w16_f64(A16.ctypes.data, M, K, W16.ctypes.data, N,
                                      C.ctypes.data, nthreads)
+        return C
+
+    def gemm_wb_f64(self, Ab: np.ndarray, Wb: np.ndarray, nthreads: int = 0) -> np.ndarray:
+        """bf16 activations times given bf16 weights (both bits), summed in fp64."""
+        Ab = np.ascontiguousarray(np.asarray(Ab).view(np.uint16))
+        Wb = np.ascontiguousarray(np.asarray(Wb).view(np.uint16))
+        M, K = Ab.shape
+        K2, N = Wb.shape
+        if K != K2:
+            raise ValueError("shape mismatch")
+        C = np.empty((M, N), np.float64)
+        self.lib.oracle_gemm_wb_f64(Ab.ctypes.data, M, K, Wb.ctypes.data, N, C.ctypes.data,
+                                    nthreads)
         return C
 
     def fold_gain(self, W: np.ndarray, gamma: np.ndarray) -> np.ndarray:

@@ -29,7 +29,12 @@
  *   - the folded RMSNorm gain (FuTransformer, section 3.2.2) is applied to
  *     the fp32 weights before quantizing, one fp32 rounding per product; the
  *     row factor rho_m = (q_m / H + eps)^(-1/2) uses H = K, the length of the
- *     activation row the GEMM reads.
+ *     activation row the GEMM reads;
+ *   - zero points (Swordfish page, blog.alpindale.net, section "The packed
+ *     format"): the prescaled row (8 - zp) * s is stored in the scales' type,
+ *     fp16, rounded once; the weight (q - 8) * s + z is rounded once to the
+ *     activation type (the page's fused multiply-add), and the zero-point
+ *     GEMM references multiply A by those rounded weights.
  *
  * Build: gcc -O2 -std=c11 -fopenmp -ffp-contract=off -fPIC -shared
  * (no fast-math: the quantizer's decisions depend on IEEE fp32 division).
@@ -250,6 +255,52 @@ int oracle_dequant_bf16(const int32_t *packed, const uint16_t *s16, int64_t K,
     return ORACLE_OK;
 }
 
+/* ------------------------------------------------------------------------
+ * Zero points (Swordfish page, blog.alpindale.net, section "The packed
+ * format").  Asymmetric (AWQ) checkpoints give each group and column a zero
+ * point zp besides the scale, the weight being (q - zp) * s.  The kernel
+ * receives them as a second tensor shaped like the scales, holding the
+ * prescaled value (8 - zp) * s, so that the weight becomes
+ * (q - 8) * s + (8 - zp) * s: the scale multiply and the zero-point add are
+ * one fused multiply-add.
+ * ---------------------------------------------------------------------- */
+
+/* Prescaled zero rows: z16[g,n] = fp16((8 - zp[g,n]) * s16[g,n]), the exact
+ * product (an 8-bit integer times an fp16 value) rounded once, stored in the
+ * scales' type. */
+int oracle_zero_rows(const uint16_t *s16, const uint8_t *zp, int64_t KG, int64_t N,
+                     uint16_t *z16)
+{
+    if (KG < 0 || N < 0)
+        return ORACLE_ERR_SHAPE;
+    for (int64_t i = 0; i < KG * N; ++i)
+        z16[i] = oracle_f64_to_f16((8.0 - (double)zp[i]) * oracle_f16_to_f64(s16[i]));
+    return ORACLE_OK;
+}
+
+/* (q - 8) * s + z before its rounding.  Both terms are multiples of 2^-24
+ * smaller than 2^20 in magnitude, so the double sum is exact. */
+static double exact_weight_zp(const int32_t *packed, const uint16_t *s16, const uint16_t *z16,
+                              int64_t N, int G, int64_t k, int64_t n)
+{
+    return exact_weight(packed, s16, N, G, k, n) + oracle_f16_to_f64(z16[(k / G) * N + n]);
+}
+
+/* Dequantize with zero rows: W[k,n] = round((q - 8) * s + z) with one
+ * rounding (the fused multiply-add) to fp16, or to bf16 when bf16 != 0. */
+int oracle_dequant_zp(const int32_t *packed, const uint16_t *s16, const uint16_t *z16,
+                      int64_t K, int64_t N, int G, int bf16, uint16_t *W)
+{
+    if (G <= 0 || K % G != 0 || K % 8 != 0)
+        return ORACLE_ERR_SHAPE;
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t n = 0; n < N; ++n) {
+            double w = exact_weight_zp(packed, s16, z16, N, G, k, n);
+            W[k * N + n] = bf16 ? oracle_f64_to_bf16(w) : oracle_f64_to_f16(w);
+        }
+    return ORACLE_OK;
+}
+
 static void set_threads(int nthreads)
 {
 #ifdef _OPENMP
@@ -325,6 +376,33 @@ int oracle_gemm_w16_f64(const uint16_t *A16, int64_t M, int64_t K,
                 double a = oracle_f16_to_f64(A16[m * K + k]);
                 for (int64_t n = n0; n < n1; ++n)
                     acc[n - n0] += a * oracle_f16_to_f64(W16[k * N + n]);
+            }
+            for (int64_t n = n0; n < n1; ++n)
+                C[m * N + n] = acc[n - n0];
+        }
+    }
+    return 0;
+}
+
+/* The same for bf16: A times given bf16 weights Wb (bits, [K,N]), summed in
+ * fp64 (the weights of a zero-point format with bf16 activations). */
+int oracle_gemm_wb_f64(const uint16_t *Ab, int64_t M, int64_t K, const uint16_t *Wb,
+                       int64_t N, double *C, int nthreads)
+{
+    set_threads(nthreads);
+    int64_t nchunks = (N + NCHUNK - 1) / NCHUNK;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t c = 0; c < nchunks; ++c) {
+            int64_t n0 = c * NCHUNK;
+            int64_t n1 = n0 + NCHUNK < N ? n0 + NCHUNK : N;
+            double acc[NCHUNK];
+            for (int64_t n = n0; n < n1; ++n)
+                acc[n - n0] = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double a = oracle_bf16_to_f64(Ab[m * K + k]);
+                for (int64_t n = n0; n < n1; ++n)
+                    acc[n - n0] += a * oracle_bf16_to_f64(Wb[k * N + n]);
             }
             for (int64_t n = n0; n < n1; ++n)
                 C[m * N + n] = acc[n - n0];

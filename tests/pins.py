@@ -289,6 +289,109 @@ def check_dequant_bf16_rounds_once(o):
     assert (Wb[(o.unpack(packed) == 8)] == 0).all()
 
 
+# -- zero points (Swordfish page, section "The packed format") -------------------
+
+def _f16(x):
+    return np.asarray(x, np.float64).astype(np.float16).view(np.uint16)
+
+
+def check_zero_rows(o):
+    """z = fp16((8 - zp) s): zp = 8 gives +0, zp = 0 gives 8 s exactly,
+    power-of-two scales are exact, z(16 - zp) = -z(zp) (round to nearest even
+    is odd-symmetric), and arbitrary scales round as numpy's correctly rounded
+    float64 -> float16 cast of the exact product."""
+    rng = np.random.default_rng(31)
+    s16 = _f16(rng.random((4, 24)) * 0.05 + 1e-3)
+    zp = rng.integers(0, 16, (4, 24)).astype(np.uint8)
+    s = s16.view(np.float16).astype(np.float64)
+    z = o.zero_rows(s16, zp)
+    assert np.array_equal(z, _f16((8.0 - zp) * s))
+    assert (o.zero_rows(s16, np.full_like(zp, 8)) == 0).all()
+    assert np.array_equal(o.zero_rows(s16, np.zeros_like(zp)), _f16(8.0 * s))
+    p2 = _f16(np.exp2(rng.integers(-14, -2, (4, 24))))
+    assert np.array_equal(o.zero_rows(p2, zp).view(np.float16).astype(np.float64),
+                          (8.0 - zp) * p2.view(np.float16).astype(np.float64))
+    inner = (zp >= 1) & (zp <= 15)
+    mirrored = o.zero_rows(s16, np.where(inner, 16 - zp, zp).astype(np.uint8))
+    f = lambda b: b.view(np.float16).astype(np.float64)
+    assert np.array_equal(f(mirrored[inner]), -f(z[inner]))
+
+
+def check_dequant_zp_worked_examples(o):
+    """The hand-worked binary16 cases of tests/golden/zero_point_examples.json
+    (a single rounding of (q - 8) s + z, with z itself rounded)."""
+    for c in _golden("zero_point_examples.json")["cases"]:
+        u = np.full((128, 1), 8, np.uint8)
+        u[0, 0] = c["q"]
+        s16 = np.array([[int(c["s_bits"], 16)]], np.uint16)
+        z = o.zero_rows(s16, np.array([[c["zp"]]], np.uint8))
+        assert z[0, 0] == int(c["z_bits"], 16)
+        packed = o.pack(u)
+        assert o.dequant_zp(packed, s16, z)[0, 0] == int(c["w_f16_bits"], 16)
+        assert o.dequant_zp(packed, s16, z, bf16=True)[0, 0] == int(c["w_bf16_bits"], 16)
+
+
+def check_dequant_zp_reduces_to_symmetric(o):
+    """zp = 8 makes every zero row +0, and the weights are then the symmetric
+    format's, fp16 and bf16, for any group size."""
+    for G in (32, 128):
+        packed, s16 = synth.random_words(256, 16, seed=32 + G, group=G)
+        z = o.zero_rows(s16, np.full(s16.shape, 8, np.uint8))
+        assert np.array_equal(o.dequant_zp(packed, s16, z, G), o.dequant(packed, s16, G))
+        assert np.array_equal(o.dequant_zp(packed, s16, z, G, bf16=True),
+                              o.dequant_bf16(packed, s16, G))
+
+
+def check_dequant_zp_power_of_two_exact(o):
+    """Power-of-two scales make z and the weight exact: w = (q - zp) s, the
+    textbook asymmetric dequantization, with the zero point of the right group
+    and column."""
+    rng = np.random.default_rng(33)
+    K, N, G = 256, 16, 64
+    u = rng.integers(0, 16, (K, N)).astype(np.uint8)
+    zp = rng.integers(0, 16, (K // G, N)).astype(np.uint8)
+    s16 = _f16(np.exp2(rng.integers(-12, -4, (K // G, N))))
+    z = o.zero_rows(s16, zp)
+    want = (u.astype(np.float64) - np.repeat(zp, G, axis=0)) * \
+        np.repeat(s16.view(np.float16).astype(np.float64), G, axis=0)
+    for bf16 in (False, True):
+        W = o.dequant_zp(o.pack(u), s16, z, G, bf16=bf16)
+        got = o.bf16_to_f64(W) if bf16 else W.view(np.float16).astype(np.float64)
+        assert np.array_equal(got, want)
+
+
+def check_dequant_zp_error_bound(o):
+    """For arbitrary scales the weight is within half an fp16 ulp of z plus
+    half an ulp of the result of the exact (q - zp) s."""
+    rng = np.random.default_rng(34)
+    K, N = 256, 24
+    u = rng.integers(0, 16, (K, N)).astype(np.uint8)
+    zp = rng.integers(0, 16, (K // 128, N)).astype(np.uint8)
+    s16 = _f16(rng.random((K // 128, N)) * 0.02 + 1e-3)
+    z = o.zero_rows(s16, zp)
+    W = o.dequant_zp(o.pack(u), s16, z).view(np.float16).astype(np.float64)
+    s = np.repeat(s16.view(np.float16).astype(np.float64), 128, axis=0)
+    zf = np.repeat(z.view(np.float16).astype(np.float64), 128, axis=0)
+    exact = (u.astype(np.float64) - np.repeat(zp, 128, axis=0)) * s
+    ulp = lambda x: np.spacing(np.abs(x).astype(np.float16)).astype(np.float64)
+    assert (np.abs(W - exact) <= ulp(zf) / 2 + ulp(W) / 2).all()
+    assert np.array_equal(o.dequant_zp(o.pack(u), s16, z).view(np.float16).astype(np.float64),
+                          W)
+
+
+def check_gemm_wb_reference(o):
+    """The bf16 given-weight product equals numpy's float64 matmul and, for
+    the symmetric weights, the bf16 GEMM reference bit for bit."""
+    rng = np.random.default_rng(35)
+    packed, s16 = synth.random_words(256, 16, seed=35)
+    Ab = _torch_bf16_bits(rng.standard_normal((3, 256)).astype(np.float32))
+    Wb = o.dequant_bf16(packed, s16)
+    C = o.gemm_wb_f64(Ab, Wb)
+    assert np.array_equal(C, o.gemm_bf16_f64(Ab, packed, s16))
+    ref = np.matmul(o.bf16_to_f64(Ab), o.bf16_to_f64(Wb))
+    assert np.allclose(C, ref, rtol=1e-12, atol=1e-12)
+
+
 # -- GEMM ------------------------------------------------------------------------
 
 def _exact_weights(o, packed, s16, G=128):
@@ -450,4 +553,6 @@ FAST_CHECKS = [
     check_bf16_decode, check_bf16_encode, check_dequant_bf16_rounds_once,
     check_gemm_bf16_bruteforce, check_gemm_bf16_matches_fp16_when_exact,
     check_fold_gain, check_rms_rowscale, check_scale_rows, check_quantize_other_group_sizes,
+    check_zero_rows, check_dequant_zp_worked_examples, check_dequant_zp_reduces_to_symmetric,
+    check_dequant_zp_power_of_two_exact, check_dequant_zp_error_bound, check_gemm_wb_reference,
 ]

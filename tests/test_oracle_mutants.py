@@ -50,7 +50,26 @@ MUTANTS = [
     ("rms_eps_dropped", "rho[m] = 1.0 / sqrt(q / (double)K + eps);", "rho[m] = 1.0 / sqrt(q / (double)K);"),
     ("rms_no_sqrt", "rho[m] = 1.0 / sqrt(q / (double)K + eps);", "rho[m] = 1.0 / (q / (double)K + eps);"),
     ("scale_rows_by_column", "out[m * N + n] = rho[m] * C[m * N + n];", "out[m * N + n] = rho[n % M] * C[m * N + n];"),
-    ("bf16_gemm_fp16_activations", "double a = oracle_bf16_to_f64(Ab[m * K + k]);", "double a = oracle_f16_to_f64(Ab[m * K + k]);"),
+    ("bf16_gemm_fp16_activations", "double a = oracle_bf16_to_f64(Ab[m * K + k]);\n                for (int64_t n = n0; n < n1; ++n) {",
+     "double a = oracle_f16_to_f64(Ab[m * K + k]);\n                for (int64_t n = n0; n < n1; ++n) {"),
+    ("gemm_wb_fp16_activations", "double a = oracle_bf16_to_f64(Ab[m * K + k]);\n                for (int64_t n = n0; n < n1; ++n)\n                    acc[n - n0] += a * oracle_bf16_to_f64(Wb",
+     "double a = oracle_f16_to_f64(Ab[m * K + k]);\n                for (int64_t n = n0; n < n1; ++n)\n                    acc[n - n0] += a * oracle_bf16_to_f64(Wb"),
+    ("zero_point_sign", "z16[i] = oracle_f64_to_f16((8.0 - (double)zp[i]) * oracle_f16_to_f64(s16[i]));",
+     "z16[i] = oracle_f64_to_f16(((double)zp[i] - 8.0) * oracle_f16_to_f64(s16[i]));"),
+    ("zero_point_offset_7", "z16[i] = oracle_f64_to_f16((8.0 - (double)zp[i]) * oracle_f16_to_f64(s16[i]));",
+     "z16[i] = oracle_f64_to_f16((7.0 - (double)zp[i]) * oracle_f16_to_f64(s16[i]));"),
+    ("zero_row_bf16_rounded", "z16[i] = oracle_f64_to_f16((8.0 - (double)zp[i]) * oracle_f16_to_f64(s16[i]));",
+     "z16[i] = oracle_f64_to_f16(oracle_bf16_to_f64(oracle_f64_to_bf16((8.0 - (double)zp[i]) * oracle_f16_to_f64(s16[i]))));"),
+    ("zero_point_two_roundings", "double w = exact_weight_zp(packed, s16, z16, N, G, k, n);",
+     "double w = oracle_f16_to_f64(oracle_f64_to_f16(exact_weight(packed, s16, N, G, k, n))) + oracle_f16_to_f64(z16[(k / G) * N + n]);"),
+    ("zero_row_wrong_group", "return exact_weight(packed, s16, N, G, k, n) + oracle_f16_to_f64(z16[(k / G) * N + n]);",
+     "return exact_weight(packed, s16, N, G, k, n) + oracle_f16_to_f64(z16[(k / 128) * N + n]);"),
+    ("zero_row_dropped", "return exact_weight(packed, s16, N, G, k, n) + oracle_f16_to_f64(z16[(k / G) * N + n]);",
+     "return exact_weight(packed, s16, N, G, k, n);"),
+    ("zero_point_bf16_flag_ignored", "W[k * N + n] = bf16 ? oracle_f64_to_bf16(w) : oracle_f64_to_f16(w);",
+     "W[k * N + n] = oracle_f64_to_f16(w);"),
+    ("gemm_wb_fp16_weights", "acc[n - n0] += a * oracle_bf16_to_f64(Wb[k * N + n]);",
+     "acc[n - n0] += a * oracle_f16_to_f64(Wb[k * N + n]);"),
 ]
 
 

@@ -126,11 +126,12 @@ def ternary_activations(M: int, K: int, density: float = 1.0, seed: int = 0) -> 
     return np.where(keep, vals, 0.0).astype(np.float16)
 
 
-def random_words(K: int, N: int, seed: int = 0) -> tuple[np.ndarray, np.ndarray]:
+def random_words(K: int, N: int, seed: int = 0, group: int = G) -> tuple[np.ndarray, np.ndarray]:
     """Arbitrary packed words (every nibble 0..15, including 0, which the RTN
-    quantizer never emits) with positive fp16 scales in [2^-9, 2^-5)."""
+    quantizer never emits) with positive fp16 scales in [2^-9, 2^-5), one per
+    `group` rows."""
     rng = np.random.default_rng(seed + 4)
     packed = rng.integers(0, 2 ** 32, size=(K // 8, N), dtype=np.uint64).astype(np.uint32)
-    scales = (rng.random((K // G, N), dtype=np.float32) * np.float32(2.0 ** -5 - 2.0 ** -9)
+    scales = (rng.random((K // group, N), dtype=np.float32) * np.float32(2.0 ** -5 - 2.0 ** -9)
               + np.float32(2.0 ** -9)).astype(np.float16)
     return packed.view(np.int32), scales.view(np.uint16)
