@@ -62,6 +62,9 @@ extern "C" {
 /* Flags for w4a16_gemm_ex: a path in the low 4 bits, OR'ed with: */
 #define W4A16_FLAG_SWIGLU 0x10 /* fused SwiGLU epilogue (see w4a16_gemm_swiglu) */
 #define W4A16_FLAG_BF16 0x20   /* bf16 activations and output (see w4a16_gemm_ex) */
+#define W4A16_FLAG_ZP 0x40     /* zero rows in use: for w4a16_describe,
+                                  w4a16_gemm_workspace_bytes (w4a16_gemm_zp
+                                  implies it) */
 
 typedef void *w4a16_stream_t; /* a hipStream_t */
 
@@ -135,6 +138,33 @@ int w4a16_dequant_bf16(const void *rw_d, const void *rs_d, int64_t K, int64_t N,
                        uint16_t *Wb_d, w4a16_stream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * Zero points (Swordfish page, blog.alpindale.net, section "The packed
+ * format"): asymmetric (AWQ) weights are w = (q - zp) * s with a 4-bit zero
+ * point zp per group and column.  The kernels take them as a third tensor
+ * shaped like the scales, the prescaled zero rows z = fp16((8 - zp) * s), and
+ * form each weight as one fused multiply-add, round((q - 8) * s + z), rounded
+ * once to the activation type.  The nibbles q are stored as they are (0..15,
+ * the same packed format and w4a16_repack as the symmetric weights).
+ *
+ * Build the zero rows of repacked weights:
+ *   scales_d  fp16 bits [K/G, N] canonical, device (the same scales given to
+ *             w4a16_repack)
+ *   zeros_d   uint8 [K/G, N] row-major, device: zp (AWQ checkpoints hold
+ *             0..15; any byte value is computed as given)
+ *   rz_d      device, 16-byte aligned, w4a16_repacked_scale_bytes(K, N, G)
+ *             bytes, written in the repacked scales' layout (padding zero)
+ * One kernel on `stream`.  Errors: W4A16_ERR_INVALID, W4A16_ERR_UNSUPPORTED
+ * (G), W4A16_ERR_HIP. */
+int w4a16_zero_rows(const uint16_t *scales_d, const uint8_t *zeros_d, int64_t K, int64_t N,
+                    int G, void *rz_d, w4a16_stream_t stream);
+
+/* Dequantize weights with zero rows: W_d[k,n] = round((q - 8) * s + z), fp16
+ * bits [K, N] row-major (bf16 with flags = W4A16_FLAG_BF16), bit-exact with
+ * that definition.  rz_d as written by w4a16_zero_rows (not NULL). */
+int w4a16_dequant_zp(const void *rw_d, const void *rs_d, const void *rz_d, int64_t K, int64_t N,
+                     int G, int flags, uint16_t *W_d, w4a16_stream_t stream);
+
+/* ---------------------------------------------------------------------------
  * GEMM (the job, stated precisely): C_d[m,n] = sum_k A_d[m,k] * w[k,n], FP32
  * accumulation, one fp16 rounding (nearest even) at the end.
  *   A_d  fp16 bits [M, K] row-major, device
@@ -190,6 +220,15 @@ int w4a16_gemm_rowscale(const uint16_t *A_d, int64_t M, int64_t K, const void *r
                         uint16_t *out_d, int flags, void *workspace_d, int64_t workspace_bytes,
                         w4a16_stream_t stream);
 
+/* GEMM on weights with zero points: out[m,n] = r_m * sum_k A[m,k] * w[k,n]
+ * with w = round((q - 8) * s + z) in the activation type (w4a16_dequant_zp)
+ * and r_m = rowscale_d[m], or 1 when rowscale_d is NULL.  rz_d (not NULL when
+ * M > 0) as written by w4a16_zero_rows; flags, workspace, outputs and errors
+ * as w4a16_gemm_ex (W4A16_FLAG_ZP is implied and may be given). */
+int w4a16_gemm_zp(const uint16_t *A_d, int64_t M, int64_t K, const void *rw_d, const void *rs_d,
+                  const void *rz_d, int64_t N, int G, const float *rowscale_d, uint16_t *out_d,
+                  int flags, void *workspace_d, int64_t workspace_bytes, w4a16_stream_t stream);
+
 /* RMSNorm row factors of the raw activations (FuTransformer, section 3.2.2):
  * rho_d[m] = (sum_k A[m,k]^2 / K + eps)^(-1/2), sums in FP32 (fixed order,
  * deterministic), correctly rounded division and square root.
@@ -201,7 +240,8 @@ int w4a16_gemm_rowscale(const uint16_t *A_d, int64_t M, int64_t K, const void *r
 int w4a16_rms_rowscale(const uint16_t *A_d, int64_t M, int64_t K, float eps, int flags,
                        float *rho_d, w4a16_stream_t stream);
 
-/* Workspace bytes that w4a16_gemm_ex needs for this problem and flags. */
+/* Workspace bytes that w4a16_gemm_ex (w4a16_gemm_zp: add W4A16_FLAG_ZP) needs
+ * for this problem and flags. */
 int64_t w4a16_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N, int G, int flags);
 
 /* The path (W4A16_PATH_DECODE / PREFILL / DENSE) that AUTO picks for this

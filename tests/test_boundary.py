@@ -80,6 +80,36 @@ def test_gemm_argument_errors_without_gpu():
     assert "aligned" in w4a16.last_error()
 
 
+def test_zero_point_argument_errors_without_gpu():
+    L = w4a16.lib()
+    ok = dict(A=16, M=1, K=4096, rw=16, rs=16, rz=16, N=4096, G=128, rowscale=0, out=16,
+              flags=0, ws=0, wsb=0, stream=0)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return L.w4a16_gemm_zp(a["A"], a["M"], a["K"], a["rw"], a["rs"], a["rz"], a["N"],
+                               a["G"], a["rowscale"], a["out"], a["flags"], a["ws"], a["wsb"],
+                               a["stream"])
+    assert call(rz=0) == w4a16.ERR_INVALID
+    assert "zero rows" in w4a16.last_error()
+    assert call(rz=8) == w4a16.ERR_INVALID                       # misaligned
+    assert "aligned" in w4a16.last_error()
+    assert call(flags=0x100) == w4a16.ERR_INVALID
+    assert call(G=384, K=12288) == w4a16.ERR_UNSUPPORTED
+    assert call(M=0, rz=0) == w4a16.OK                             # empty product: no-op
+    # A flag that only the zero-point entry point takes.
+    assert _gemm_ex(flags=w4a16.FLAG_ZP) == w4a16.ERR_INVALID
+    assert "flags" in w4a16.last_error()
+    assert L.w4a16_zero_rows(0, 16, 4096, 4096, 128, 16, 0) == w4a16.ERR_INVALID
+    assert L.w4a16_zero_rows(16, 16, 4096, 4096, 128, 8, 0) == w4a16.ERR_INVALID
+    assert L.w4a16_zero_rows(16, 16, 4096, 4096, 100, 16, 0) == w4a16.ERR_INVALID  # K % G
+    assert L.w4a16_dequant_zp(16, 16, 0, 4096, 4096, 128, 0, 16, 0) == w4a16.ERR_INVALID
+    assert L.w4a16_dequant_zp(16, 16, 16, 4096, 4096, 128, 0x10, 16, 0) == w4a16.ERR_INVALID
+    # Workspace sizes follow the zero-point dispatch (no cooperative decode).
+    assert w4a16.workspace_bytes(16, 14336, 4096, zp=True) >= 0
+
+
 def test_other_argument_errors():
     L = w4a16.lib()
     assert L.w4a16_repack(0, 0, 4096, 4096, 128, 0, 0, 0) == w4a16.ERR_INVALID
@@ -122,19 +152,34 @@ def test_dispatch_table():
 
 def test_describe_names_the_launches():
     """The launch description names kernel instances as profilers print them
-    (the last two template arguments: SwiGLU epilogue, bf16 activations)."""
+    (template arguments after the tile shape: SwiGLU epilogue, bf16
+    activations, then for decode_kernel the scaling before the MFMA, and for
+    decode_kernel and prefill2_kernel the zero rows)."""
     d = w4a16.describe(1, 4096, 28672, swiglu=True)
     assert d.startswith("decode_coop_kernel<16, 2, ") and d.split(">")[0].endswith("true, false")
     d = w4a16.describe(1, 4096, 28672, swiglu=True, bf16=True)
     assert d.startswith("decode_coop_kernel<16, 2, ") and d.split(">")[0].endswith("true, true")
     d = w4a16.describe(1, 4096, 4096)
-    assert d.startswith("decode_kernel<16, 1, ") and d.split(">")[0].endswith("false, false")
-    assert "prefill2_kernel<4, 2, 4, 2, false, true, false>" in w4a16.describe(4096, 4096, 28672,
-                                                                               swiglu=True)
-    assert "prefill2_kernel<4, 2, 4, 2, false, true, true>" in w4a16.describe(
+    assert d.startswith("decode_kernel<16, 1, ") and d.split(">")[0].endswith(
+        "false, false, false, false")
+    assert "prefill2_kernel<4, 2, 4, 2, false, true, false, false>" in w4a16.describe(
+        4096, 4096, 28672, swiglu=True)
+    assert "prefill2_kernel<4, 2, 4, 2, false, true, true, false>" in w4a16.describe(
         4096, 4096, 28672, swiglu=True, bf16=True)
     assert w4a16.describe(256, 4096, 28672, swiglu=True).startswith(
-        "prefill2_kernel<2, 2, 4, 2, false, true, false> workgroups=224 threads=512 ks=1")
+        "prefill2_kernel<2, 2, 4, 2, false, true, false, false> workgroups=224 threads=512 ks=1")
+    # Zero rows: decode scales before the MFMA (never the cooperative kernel),
+    # prefill takes the ZP instance, the dense tier folds them into its dequant.
+    d = w4a16.describe(1, 4096, 28672, swiglu=True, zp=True)
+    assert d.startswith("decode_kernel<16, 2, ") and d.split(">")[0].endswith(
+        "true, false, true, true"), d
+    d = w4a16.describe(4, 4096, 4096, bf16=True, zp=True)
+    assert d.startswith("decode_kernel<16, 1, ") and d.split(">")[0].endswith(
+        "false, true, true, true"), d
+    assert "prefill2_kernel<4, 2, 4, 2, false, false, false, true>" in w4a16.describe(
+        4096, 4096, 4096, zp=True)
+    assert w4a16.describe(4096, 4096, 4096, path="dense", zp=True).startswith(
+        "dequant_kernel<false, false>; prefill")
     assert w4a16.describe(64, 14336, 4096).endswith("ks=16; prefill_reduce_kernel<false, false>")
     assert w4a16.describe(4096, 4096, 4096, path="dense").startswith(
         "dequant_kernel<false, false>; ")

@@ -33,7 +33,7 @@ int hip_fail(hipError_t e, const char *what) {
   return fail(W4A16_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }  // null passes
 
 // Shape rules of the canonical format (data contract) plus this library's.
 int check_shape(int64_t K, int64_t N, int G, const char *who) {
@@ -130,8 +130,9 @@ int64_t workspace_for(int path, const Problem &p) {
 
 int run_gemm(const uint16_t *A, int64_t M, int64_t K, const void *rw, const void *rs, int64_t N,
              int G, uint16_t *out, int flags, void *workspace, int64_t ws_bytes,
-             hipStream_t stream, const float *rowscale = nullptr) {
-  const char *who = (flags & W4A16_FLAG_SWIGLU) ? "w4a16_gemm_swiglu" : "w4a16_gemm";
+             hipStream_t stream, const float *rowscale = nullptr, const void *rz = nullptr,
+             const char *who = nullptr) {
+  if (who == nullptr) who = (flags & W4A16_FLAG_SWIGLU) ? "w4a16_gemm_swiglu" : "w4a16_gemm";
   const bool bf16 = (flags & W4A16_FLAG_BF16) != 0;
   int rc = check_gpu_shape(K, N, G, who);
   if (rc != W4A16_OK) return rc;
@@ -142,14 +143,14 @@ int run_gemm(const uint16_t *A, int64_t M, int64_t K, const void *rw, const void
     return fail(W4A16_ERR_INVALID, "%s: N (%lld) must be a multiple of 64", who, (long long)N);
   if (M == 0) return W4A16_OK;
   if (!A || !rw || !rs || !out) return fail(W4A16_ERR_INVALID, "%s: null pointer", who);
-  if (!aligned16(A) || !aligned16(rw) || !aligned16(rs) || !aligned16(out))
+  if (!aligned16(A) || !aligned16(rw) || !aligned16(rs) || !aligned16(out) || !aligned16(rz))
     return fail(W4A16_ERR_INVALID, "%s: device pointers must be 16-byte aligned", who);
   int path = flags & 0xF;
   if (path == W4A16_PATH_AUTO) path = select_path(M, K, N);
   if (path < W4A16_PATH_DECODE || path > W4A16_PATH_DENSE)
     return fail(W4A16_ERR_INVALID, "%s: unknown path %d", who, path);
 
-  Problem p{A, M, K, N, rw, rs, out, swiglu, bf16, rowscale, G, group_shift(K, G)};
+  Problem p{A, M, K, N, rw, rs, out, swiglu, bf16, rowscale, G, group_shift(K, G), rz, rz != nullptr};
   const int64_t need = workspace_for(path, p);
   void *ws = workspace;
   if (need > 0) {
@@ -329,26 +330,49 @@ int w4a16_unrepack(const void *rw_d, const void *rs_d, int64_t K, int64_t N, int
   return e == hipSuccess ? W4A16_OK : hip_fail(e, "w4a16_unrepack");
 }
 
-static int dequant_common(const void *rw_d, const void *rs_d, int64_t K, int64_t N, int G,
-                          uint16_t *W_d, bool bf16, hipStream_t stream, const char *who) {
+static int dequant_common(const void *rw_d, const void *rs_d, const void *rz_d, int64_t K,
+                          int64_t N, int G, uint16_t *W_d, bool bf16, hipStream_t stream,
+                          const char *who) {
   int rc = check_gpu_shape(K, N, G, who);
   if (rc != W4A16_OK) return rc;
   if (!rw_d || !rs_d || !W_d) return fail(W4A16_ERR_INVALID, "%s: null pointer", who);
-  if (!aligned16(rw_d) || !aligned16(rs_d))
+  if (!aligned16(rw_d) || !aligned16(rs_d) || !aligned16(rz_d))
     return fail(W4A16_ERR_INVALID, "%s: repacked buffers must be 16-byte aligned", who);
-  hipError_t e = launch_dequant_canonical(rw_d, rs_d, K, N, G, bf16, W_d, stream);
+  hipError_t e = launch_dequant_canonical(rw_d, rs_d, rz_d, K, N, G, bf16, W_d, stream);
   return e == hipSuccess ? W4A16_OK : hip_fail(e, who);
 }
 
 int w4a16_dequant(const void *rw_d, const void *rs_d, int64_t K, int64_t N, int G,
                   uint16_t *W16_d, w4a16_stream_t stream) {
-  return dequant_common(rw_d, rs_d, K, N, G, W16_d, false, (hipStream_t)stream, "w4a16_dequant");
+  return dequant_common(rw_d, rs_d, nullptr, K, N, G, W16_d, false, (hipStream_t)stream,
+                        "w4a16_dequant");
 }
 
 int w4a16_dequant_bf16(const void *rw_d, const void *rs_d, int64_t K, int64_t N, int G,
                        uint16_t *Wb_d, w4a16_stream_t stream) {
-  return dequant_common(rw_d, rs_d, K, N, G, Wb_d, true, (hipStream_t)stream,
+  return dequant_common(rw_d, rs_d, nullptr, K, N, G, Wb_d, true, (hipStream_t)stream,
                         "w4a16_dequant_bf16");
+}
+
+int w4a16_zero_rows(const uint16_t *scales_d, const uint8_t *zeros_d, int64_t K, int64_t N,
+                    int G, void *rz_d, w4a16_stream_t stream) {
+  const char *who = "w4a16_zero_rows";
+  int rc = check_gpu_shape(K, N, G, who);
+  if (rc != W4A16_OK) return rc;
+  if (!scales_d || !zeros_d || !rz_d) return fail(W4A16_ERR_INVALID, "%s: null pointer", who);
+  if (!aligned16(rz_d))
+    return fail(W4A16_ERR_INVALID, "%s: the zero-row buffer must be 16-byte aligned", who);
+  hipError_t e = launch_zero_rows(scales_d, zeros_d, K, N, G, rz_d, (hipStream_t)stream);
+  return e == hipSuccess ? W4A16_OK : hip_fail(e, who);
+}
+
+int w4a16_dequant_zp(const void *rw_d, const void *rs_d, const void *rz_d, int64_t K, int64_t N,
+                     int G, int flags, uint16_t *W_d, w4a16_stream_t stream) {
+  const char *who = "w4a16_dequant_zp";
+  if (flags & ~W4A16_FLAG_BF16) return fail(W4A16_ERR_INVALID, "%s: unknown flags 0x%x", who, flags);
+  if (!rz_d) return fail(W4A16_ERR_INVALID, "%s: null pointer", who);
+  return dequant_common(rw_d, rs_d, rz_d, K, N, G, W_d, (flags & W4A16_FLAG_BF16) != 0,
+                        (hipStream_t)stream, who);
 }
 
 int w4a16_gemm(const uint16_t *A_d, int64_t M, int64_t K, const void *rw_d, const void *rs_d,
@@ -384,6 +408,16 @@ int w4a16_gemm_rowscale(const uint16_t *A_d, int64_t M, int64_t K, const void *r
                   (hipStream_t)stream, rowscale_d);
 }
 
+int w4a16_gemm_zp(const uint16_t *A_d, int64_t M, int64_t K, const void *rw_d, const void *rs_d,
+                  const void *rz_d, int64_t N, int G, const float *rowscale_d, uint16_t *out_d,
+                  int flags, void *workspace_d, int64_t workspace_bytes, w4a16_stream_t stream) {
+  if (flags & ~(0xF | W4A16_FLAG_SWIGLU | W4A16_FLAG_BF16 | W4A16_FLAG_ZP))
+    return fail(W4A16_ERR_INVALID, "w4a16_gemm_zp: unknown flags 0x%x", flags);
+  if (M > 0 && rz_d == nullptr) return fail(W4A16_ERR_INVALID, "w4a16_gemm_zp: null zero rows");
+  return run_gemm(A_d, M, K, rw_d, rs_d, N, G, out_d, flags & ~W4A16_FLAG_ZP, workspace_d,
+                  workspace_bytes, (hipStream_t)stream, rowscale_d, rz_d, "w4a16_gemm_zp");
+}
+
 int w4a16_rms_rowscale(const uint16_t *A_d, int64_t M, int64_t K, float eps, int flags,
                        float *rho_d, w4a16_stream_t stream) {
   const char *who = "w4a16_rms_rowscale";
@@ -409,7 +443,8 @@ int64_t w4a16_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N, int G, int f
   int path = flags & 0xF;
   if (path == W4A16_PATH_AUTO) path = select_path(M, K, N);
   Problem p{nullptr, M, K, N, nullptr, nullptr, nullptr, (flags & W4A16_FLAG_SWIGLU) != 0,
-            (flags & W4A16_FLAG_BF16) != 0, nullptr, G, group_shift(K, G)};
+            (flags & W4A16_FLAG_BF16) != 0, nullptr, G, group_shift(K, G), nullptr,
+            (flags & W4A16_FLAG_ZP) != 0};
   return workspace_for(path, p);
 }
 
@@ -418,7 +453,7 @@ int w4a16_describe(int64_t M, int64_t K, int64_t N, int G, int flags, char *buf,
   if (rc != W4A16_OK) return rc;
   if (M < 1) return fail(W4A16_ERR_INVALID, "w4a16_describe: M must be >= 1");
   if (buf == nullptr || len < 1) return fail(W4A16_ERR_INVALID, "w4a16_describe: no buffer");
-  if (flags & ~(0xF | W4A16_FLAG_SWIGLU | W4A16_FLAG_BF16))
+  if (flags & ~(0xF | W4A16_FLAG_SWIGLU | W4A16_FLAG_BF16 | W4A16_FLAG_ZP))
     return fail(W4A16_ERR_INVALID, "w4a16_describe: unknown flags 0x%x", flags);
   const bool swiglu = (flags & W4A16_FLAG_SWIGLU) != 0;
   if (swiglu && N % 64 != 0)
@@ -429,7 +464,7 @@ int w4a16_describe(int64_t M, int64_t K, int64_t N, int G, int flags, char *buf,
   if (path < W4A16_PATH_DECODE || path > W4A16_PATH_DENSE)
     return fail(W4A16_ERR_INVALID, "w4a16_describe: unknown path %d", path);
   Problem p{nullptr, M, K, N, nullptr, nullptr, nullptr, swiglu, (flags & W4A16_FLAG_BF16) != 0,
-            nullptr, G, group_shift(K, G)};
+            nullptr, G, group_shift(K, G), nullptr, (flags & W4A16_FLAG_ZP) != 0};
   char tmp[512];
   int k;
   if (path == W4A16_PATH_DECODE) {

@@ -100,6 +100,17 @@ struct Dequant {
     return half8_t{q0[0], q0[1], q1[0], q1[1], q2[0], q2[1], q3[0], q3[1]};
   }
 
+  // With a zero row (AWQ zero points prescaled as z = fp16((8 - zp) s)):
+  // fp16((u - 8) * s + z), one fused multiply-add per pair, rounded once.
+  __device__ __forceinline__ half8_t scaled_zp(uint32_t w, half2_t s2, half2_t z2) const {
+    const half8_t v = (*this)(w);
+    const half2_t q0 = __builtin_elementwise_fma(half2_t{v[0], v[1]}, s2, z2);
+    const half2_t q1 = __builtin_elementwise_fma(half2_t{v[2], v[3]}, s2, z2);
+    const half2_t q2 = __builtin_elementwise_fma(half2_t{v[4], v[5]}, s2, z2);
+    const half2_t q3 = __builtin_elementwise_fma(half2_t{v[6], v[7]}, s2, z2);
+    return half8_t{q0[0], q0[1], q1[0], q1[1], q2[0], q2[1], q3[0], q3[1]};
+  }
+
   // bf16 activations.  The dequantized weight is then bf16((u - 8) * s): the
   // exact product of u - 8 and the fp16 scale, rounded once to bf16.  The
   // magic-number pairs (1024 + u, or 1024 + 16u) go straight into a
@@ -108,6 +119,12 @@ struct Dequant {
   // (1024 + 16u) (s / 16) - 72 s.  Every product and constant has at most 22
   // significant bits and the sum is (u - 8) s itself, so the FMA is exact; one
   // v_cvt_pk_bf16_f32 per pair then rounds.  17 VALU instructions per word.
+  //
+  // A zero row z (fp16) joins the constants: (1024 + u) s + (z - 1032 s) and
+  // (1024 + 16u) (s / 16) + (z - 72 s).  z is 0 or at least |s| in magnitude,
+  // so it is a multiple of the fp16 spacing of s, and so are both constants
+  // (below 2^22 of those spacings: exact in fp32); the FMA result
+  // (u - 8) s + z is exact as well, and the conversion is the one rounding.
   struct BScale {
     float s, c_lo, s_hi, c_hi;
     __device__ __forceinline__ explicit BScale(uint16_t s16) {
@@ -116,10 +133,20 @@ struct Dequant {
       s_hi = s * 0.0625f;
       c_hi = -72.0f * s;
     }
+    __device__ __forceinline__ BScale(uint16_t s16, uint16_t z16) {
+      s = (float)bitcast<_Float16>(s16);
+      const float z = (float)bitcast<_Float16>(z16);
+      c_lo = __builtin_fmaf(-1032.0f, s, z);
+      s_hi = s * 0.0625f;
+      c_hi = __builtin_fmaf(-72.0f, s, z);
+    }
   };
-  // The scaled weights of either type as a raw 16-byte MFMA operand.
+  // The scaled weights of either type as a raw 16-byte MFMA operand (ZP: with
+  // the zero row z16).
   template <bool BF>
   __device__ __forceinline__ uint4_t scaled_bits(uint32_t w, uint16_t s16) const;
+  template <bool BF, bool ZP>
+  __device__ __forceinline__ uint4_t scaled_bits(uint32_t w, uint16_t s16, uint16_t z16) const;
 
   __device__ __forceinline__ bf16x8_t scaled_bf16(uint32_t w, const BScale &b) const {
     const uint32_t t = w >> 8;
@@ -159,6 +186,19 @@ __device__ __forceinline__ uint4_t Dequant::scaled_bits(uint32_t w, uint16_t s16
   } else {
     const _Float16 sh = bitcast<_Float16>(s16);
     return bitcast<uint4_t>(scaled(w, half2_t{sh, sh}));
+  }
+}
+
+template <bool BF, bool ZP>
+__device__ __forceinline__ uint4_t Dequant::scaled_bits(uint32_t w, uint16_t s16,
+                                                        uint16_t z16) const {
+  if constexpr (!ZP) {
+    return scaled_bits<BF>(w, s16);
+  } else if constexpr (BF) {
+    return bitcast<uint4_t>(scaled_bf16(w, BScale(s16, z16)));
+  } else {
+    const _Float16 sh = bitcast<_Float16>(s16), zh = bitcast<_Float16>(z16);
+    return bitcast<uint4_t>(scaled_zp(w, half2_t{sh, sh}, half2_t{zh, zh}));
   }
 }
 
@@ -217,6 +257,8 @@ struct Problem {
   const float *rowscale;  // per-row output factor [M], or null
   int G = kGroup;  // quantization group along K
   int gshift = 7;  // group of k = k >> gshift (see group_shift)
+  const void *rz = nullptr;  // prescaled zero rows, laid out as rs, or null
+  bool zp = false;           // zero rows in use (rz != null when launching)
 };
 
 // Group sizes: a power of two >= 32 that divides K, or K itself
@@ -251,10 +293,14 @@ hipError_t launch_repack(const int32_t *packed, const uint16_t *scales, int64_t 
                          int G, void *rw, void *rs, hipStream_t s);
 hipError_t launch_unrepack(const void *rw, const void *rs, int64_t K, int64_t N, int G,
                            int32_t *packed, uint16_t *scales, hipStream_t s);
-hipError_t launch_dequant_canonical(const void *rw, const void *rs, int64_t K, int64_t N, int G,
-                                    bool bf16, uint16_t *W, hipStream_t s);
-hipError_t launch_dequant_fragment(const void *rw, const void *rs, int64_t K, int64_t N, int G,
-                                   bool bf16, uint16_t *Wf, hipStream_t s);
+// Prescaled zero rows fp16((8 - zp) s) in the repacked scale layout.
+hipError_t launch_zero_rows(const uint16_t *scales, const uint8_t *zeros, int64_t K, int64_t N,
+                            int G, void *rz, hipStream_t s);
+// rz: prescaled zero rows (repacked layout) or null.
+hipError_t launch_dequant_canonical(const void *rw, const void *rs, const void *rz, int64_t K,
+                                    int64_t N, int G, bool bf16, uint16_t *W, hipStream_t s);
+hipError_t launch_dequant_fragment(const void *rw, const void *rs, const void *rz, int64_t K,
+                                   int64_t N, int G, bool bf16, uint16_t *Wf, hipStream_t s);
 
 // Decode path: workspace bytes (split-K partials), the launch, and a text
 // description of the launch (kernel instances and grid).

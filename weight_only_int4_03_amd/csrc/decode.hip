@@ -47,17 +47,22 @@ struct DecodeFrag {
   uint4_t b[SPW][NB];
   uint4_t a[NA];
   // Scales per strip, 16-column half (MT=16) and 64-k tile (MT=32, which
-  // can span two groups when G < 128).
-  uint16_t sc[SPW][MT == 16 ? 2 : 1][MT == 16 ? 1 : 2];
+  // can span two groups when G < 128), and the zero rows likewise (16-bit
+  // values held in 32-bit words, which keeps the arrays in registers).
+  uint32_t sc[SPW][MT == 16 ? 2 : 1][MT == 16 ? 1 : 2];
+  uint32_t zs[SPW][MT == 16 ? 2 : 1][MT == 16 ? 1 : 2];
 };
 
 // PRE: the weights are scaled before the MFMA (bf16 activations, whose
 // weights are rounded to bf16, and groups shorter than the 128-k unit, whose
 // lanes meet different scales within one MFMA); otherwise each 128-k unit is
 // accumulated unscaled and its tile scaled once afterwards.
-template <int MT, int SPW, int WAVES, int D, int RPL, bool SWIGLU, bool BF, bool PRE>
+// ZP: zero rows (AWQ zero points prescaled as fp16((8 - zp) s)); each weight
+// is then the one rounding of (u - 8) s + z, so it is scaled before the MFMA.
+template <int MT, int SPW, int WAVES, int D, int RPL, bool SWIGLU, bool BF, bool PRE, bool ZP>
 __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
   static_assert(PRE || !BF, "bf16 weights are always scaled before the MFMA");
+  static_assert(PRE || !ZP, "weights with zero points are scaled before the MFMA");
   static_assert(MT == 16 ? (RPL >= 1 && RPL <= 4) : RPL == 16, "rows per lane");
   extern __shared__ float lds[];  // [WAVES][SPW][M][32]
   constexpr int SH = SWIGLU ? SPW / 2 : SPW;
@@ -75,12 +80,14 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
   // workgroup names is a real one (the repacked buffer pads N to 32 columns).
   const char *wbase[SPW];
   const char *sbase[SPW];
+  const char *zbase[SPW];
 #pragma unroll
   for (int s = 0; s < SPW; ++s) {
     const int base = sg * SH + (s % SH);
     const int strip = SWIGLU && s >= SH ? base + p.up_off : base;
     wbase[s] = (const char *)(p.rw + (int64_t)strip * p.KT * 64);
     sbase[s] = (const char *)(p.rs + (int64_t)strip * p.KG8 * 256);
+    zbase[s] = ZP ? (const char *)(p.rz + (int64_t)strip * p.KG8 * 256) : nullptr;
   }
 
   const int unit = split * WAVES + wave, nunits = p.KS * WAVES;
@@ -122,15 +129,19 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
       }
       if constexpr (PRE) {
         if constexpr (MT == 16) {
-          const char *sp = sbase[s] + soff((128 * g + klane) >> p.gshift);
+          const uint32_t so = soff((128 * g + klane) >> p.gshift);
 #pragma unroll
-          for (int part = 0; part < 2; ++part)
-            f.sc[s][part][0] = *(const uint16_t *)(sp + part * 256);
+          for (int part = 0; part < 2; ++part) {
+            f.sc[s][part][0] = *(const uint16_t *)(sbase[s] + so + part * 256);
+            if constexpr (ZP) f.zs[s][part][0] = *(const uint16_t *)(zbase[s] + so + part * 256);
+          }
         } else {
 #pragma unroll
-          for (int x = 0; x < 2; ++x)
-            f.sc[s][0][x] =
-                *(const uint16_t *)(sbase[s] + soff((128 * g + 64 * x + klane) >> p.gshift));
+          for (int x = 0; x < 2; ++x) {
+            const uint32_t so = soff((128 * g + 64 * x + klane) >> p.gshift);
+            f.sc[s][0][x] = *(const uint16_t *)(sbase[s] + so);
+            if constexpr (ZP) f.zs[s][0][x] = *(const uint16_t *)(zbase[s] + so);
+          }
         }
       } else {
         const char *sp = sbase[s] + soff((128 * g) >> p.gshift);
@@ -166,19 +177,21 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
 #pragma unroll
         for (int part = 0; part < NPART; ++part) {
           if constexpr (MT == 16) {
-            const uint16_t sc = f.sc[s][part][0];
+            const uint16_t sc = (uint16_t)f.sc[s][part][0], zs = (uint16_t)f.zs[s][part][0];
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-              acc[s][part] = mfma16<BF>(f.a[j], dq.scaled_bits<BF>(f.b[s][part][j], sc),
+              acc[s][part] = mfma16<BF>(f.a[j], dq.scaled_bits<BF, ZP>(f.b[s][part][j], sc, zs),
                                         acc[s][part]);
           } else {
 #pragma unroll
             for (int x = 0; x < 2; ++x)
 #pragma unroll
               for (int j = 0; j < 4; ++j)
-                acc[s][part] = mfma32<BF>(f.a[4 * x + j],
-                                          dq.scaled_bits<BF>(f.b[s][x][j], f.sc[s][0][x]),
-                                          acc[s][part]);
+                acc[s][part] = mfma32<BF>(
+                    f.a[4 * x + j],
+                    dq.scaled_bits<BF, ZP>(f.b[s][x][j], (uint16_t)f.sc[s][0][x],
+                                           (uint16_t)f.zs[s][0][x]),
+                    acc[s][part]);
           }
         }
       }
@@ -202,7 +215,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
               t = __builtin_amdgcn_mfma_f32_32x32x16_f16(bitcast<half8_t>(f.a[4 * x + j]),
                                                          dq(f.b[s][x][j]), t, 0, 0, 0);
         }
-        const float sc = (float)bitcast<_Float16>(f.sc[s][part][0]);
+        const float sc = (float)bitcast<_Float16>((uint16_t)f.sc[s][part][0]);
         // Element r of a lane's tile holds row 4*g4 + r (MT=16), so with
         // M < 4 only elements r < RPL can hold real rows.
 #pragma unroll
@@ -354,10 +367,12 @@ int decode_describe(const Problem &p, char *buf, size_t n) {
   }
   const DecodeConfig c = decode_config(p);
   const int rpl = c.MT == 16 ? (p.M == 1 ? 1 : 4) : 16;
-  const char *pre = (p.bf16 || p.G < kGroup) ? "true" : "false";
+  const char *pre = (p.bf16 || p.G < kGroup || p.zp) ? "true" : "false";
+  const char *zp = p.zp ? "true" : "false";
   int k = snprintf(buf, n,
-                   "decode_kernel<%d, %d, %d, %d, %d, %s, %s, %s> workgroups=%d threads=%d ks=%d",
-                   c.MT, c.SPW, c.WAVES, c.D, rpl, sw, bf, pre, c.nsg * c.KS, c.WAVES * 64, c.KS);
+                   "decode_kernel<%d, %d, %d, %d, %d, %s, %s, %s, %s> workgroups=%d threads=%d ks=%d",
+                   c.MT, c.SPW, c.WAVES, c.D, rpl, sw, bf, pre, zp, c.nsg * c.KS, c.WAVES * 64,
+                   c.KS);
   if (c.KS > 1 && k > 0 && (size_t)k < n)
     k += snprintf(buf + k, n - k, "; decode_reduce_kernel<%d, %s, %s>", c.SPW, sw, bf);
   return k;
@@ -375,36 +390,37 @@ int64_t decode_workspace_bytes(const Problem &p) {
   return (int64_t)c.nsg * c.KS * c.SPW * p.M * 32 * (int64_t)sizeof(float);
 }
 
-template <int MT, int SPW, int WAVES, int D, int RPL, bool SWIGLU, bool BF, bool PRE>
+template <int MT, int SPW, int WAVES, int D, int RPL, bool SWIGLU, bool BF, bool PRE, bool ZP>
 static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t s) {
   const size_t lds = (size_t)WAVES * SPW * a.M * 32 * sizeof(float);
-  hipLaunchKernelGGL((decode_kernel<MT, SPW, WAVES, D, RPL, SWIGLU, BF, PRE>), dim3(a.nsg * a.KS),
+  hipLaunchKernelGGL((decode_kernel<MT, SPW, WAVES, D, RPL, SWIGLU, BF, PRE, ZP>),
+                     dim3(a.nsg * a.KS),
                      dim3(WAVES * 64), lds, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.KS == 1) return e;
   return launch_decode_reduce(a, SWIGLU, BF, s);
 }
 
-template <int MT, int SPW, int RPL, bool SWIGLU, bool BF, bool PRE>
+template <int MT, int SPW, int RPL, bool SWIGLU, bool BF, bool PRE, bool ZP>
 static hipError_t launch_decode_w(const DecodeArgs &a, const DecodeConfig &c, hipStream_t s) {
   if (c.D == 4)
-    return c.WAVES == 8 ? launch_decode_t<MT, SPW, 8, 4, RPL, SWIGLU, BF, PRE>(a, s)
-                        : launch_decode_t<MT, SPW, 4, 4, RPL, SWIGLU, BF, PRE>(a, s);
-  return c.WAVES == 8 ? launch_decode_t<MT, SPW, 8, 2, RPL, SWIGLU, BF, PRE>(a, s)
-                      : launch_decode_t<MT, SPW, 4, 2, RPL, SWIGLU, BF, PRE>(a, s);
+    return c.WAVES == 8 ? launch_decode_t<MT, SPW, 8, 4, RPL, SWIGLU, BF, PRE, ZP>(a, s)
+                        : launch_decode_t<MT, SPW, 4, 4, RPL, SWIGLU, BF, PRE, ZP>(a, s);
+  return c.WAVES == 8 ? launch_decode_t<MT, SPW, 8, 2, RPL, SWIGLU, BF, PRE, ZP>(a, s)
+                      : launch_decode_t<MT, SPW, 4, 2, RPL, SWIGLU, BF, PRE, ZP>(a, s);
 }
 
-template <bool BF, bool PRE>
+template <bool BF, bool PRE, bool ZP>
 static hipError_t launch_decode_bf(const Problem &p, const DecodeArgs &a, const DecodeConfig &c,
                                    hipStream_t s) {
   if (c.MT == 16 && p.M == 1)
-    return p.swiglu ? launch_decode_w<16, 2, 1, true, BF, PRE>(a, c, s)
-                    : launch_decode_w<16, 1, 1, false, BF, PRE>(a, c, s);
+    return p.swiglu ? launch_decode_w<16, 2, 1, true, BF, PRE, ZP>(a, c, s)
+                    : launch_decode_w<16, 1, 1, false, BF, PRE, ZP>(a, c, s);
   if (c.MT == 16)
-    return p.swiglu ? launch_decode_w<16, 2, 4, true, BF, PRE>(a, c, s)
-                    : launch_decode_w<16, 1, 4, false, BF, PRE>(a, c, s);
-  return p.swiglu ? launch_decode_w<32, 2, 16, true, BF, PRE>(a, c, s)
-                  : launch_decode_w<32, 1, 16, false, BF, PRE>(a, c, s);
+    return p.swiglu ? launch_decode_w<16, 2, 4, true, BF, PRE, ZP>(a, c, s)
+                    : launch_decode_w<16, 1, 4, false, BF, PRE, ZP>(a, c, s);
+  return p.swiglu ? launch_decode_w<32, 2, 16, true, BF, PRE, ZP>(a, c, s)
+                  : launch_decode_w<32, 1, 16, false, BF, PRE, ZP>(a, c, s);
 }
 
 DecodeArgs decode_args(const Problem &p, int KS, void *workspace) {
@@ -414,6 +430,7 @@ DecodeArgs decode_args(const Problem &p, int KS, void *workspace) {
   a.K = (int)p.K;
   a.rw = (const uint4_t *)p.rw;
   a.rs = (const uint16_t *)p.rs;
+  a.rz = (const uint16_t *)p.rz;
   a.N = (int)p.N;
   a.NS = (int)ceil_div(p.N, kStrip);
   a.KT = (int)(p.K / kTileK);
@@ -454,9 +471,12 @@ hipError_t launch_decode(const Problem &p, void *workspace, hipStream_t s) {
   const DecodeConfig c = decode_config(p);
   DecodeArgs a = decode_args(p, c.KS, workspace);
   if (c.KS > 1 && workspace == nullptr) return hipErrorInvalidValue;
-  if (p.bf16) return launch_decode_bf<true, true>(p, a, c, s);
-  return p.G < kGroup ? launch_decode_bf<false, true>(p, a, c, s)
-                      : launch_decode_bf<false, false>(p, a, c, s);
+  if (p.zp)
+    return p.bf16 ? launch_decode_bf<true, true, true>(p, a, c, s)
+                  : launch_decode_bf<false, true, true>(p, a, c, s);
+  if (p.bf16) return launch_decode_bf<true, true, false>(p, a, c, s);
+  return p.G < kGroup ? launch_decode_bf<false, true, false>(p, a, c, s)
+                      : launch_decode_bf<false, false, false>(p, a, c, s);
 }
 
 }  // namespace w4a16

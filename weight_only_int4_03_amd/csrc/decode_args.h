@@ -11,6 +11,7 @@ struct DecodeArgs {
   int M, K;
   const uint4_t *rw;
   const uint16_t *rs;
+  const uint16_t *rz;  // prescaled zero rows (laid out as rs), or null
   int N, NS, KT, KG, KG8;
   uint16_t *out;
   int ldo;

@@ -380,6 +380,7 @@ bool coop_config(const Problem &p, int &WC, int &WK, int &KS) {
   const int KG = (int)(p.K / kGroup);
   const int force = coop_env_raw("W4A16_DECODE_COOP");
   if (p.G < kGroup) return false;  // one scale per column and 128-k unit
+  if (p.zp) return false;          // zero rows: decode_kernel's pre-scaled form
   bool use;
   if (nsg >= 384) {
     use = true;

@@ -155,11 +155,52 @@ hipError_t launch_unrepack(const void *rw, const void *rs, int64_t K, int64_t N,
 }
 
 // ---------------------------------------------------------------------------
+// Prescaled zero rows (Swordfish page, blog.alpindale.net, section "The packed
+// format": AWQ zero points enter as rows shaped like the scales holding
+// (8 - zp) * s).  One thread per (strip, group octet, column), as the scale
+// half of repack_kernel, writing z = fp16((8 - zp) s) into the repacked scale
+// layout; padding entries are zero.  (8 - zp) s is an integer of at most 9
+// bits times an fp16 value, exact in fp32, so the conversion is the one
+// rounding.
+__global__ __launch_bounds__(256) void zero_rows_kernel(const uint16_t *__restrict__ scales,
+                                                        const uint8_t *__restrict__ zeros,
+                                                        uint16_t *__restrict__ rz, int64_t N,
+                                                        int64_t KG, int64_t KG8, int64_t NS) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (t*KG8+o)*32+c
+  if (idx >= NS * KG8 * 32) return;
+  const int c = (int)(idx & 31);
+  const int64_t to = idx >> 5;
+  const int64_t o = to % KG8, t = to / KG8;
+  const int64_t n = t * kStrip + c;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int64_t g = 8 * o + e;
+    uint16_t z = 0;
+    if (g < KG && n < N) {
+      const float s = (float)bitcast<_Float16>(scales[g * N + n]);
+      z = to_half_bits(__fmul_rn((float)(8 - (int)zeros[g * N + n]), s));
+    }
+    rz[idx * 8 + e] = z;
+  }
+}
+
+hipError_t launch_zero_rows(const uint16_t *scales, const uint8_t *zeros, int64_t K, int64_t N,
+                            int G, void *rz, hipStream_t s) {
+  int64_t KT, KG, KG8, NS;
+  repack_geometry(K, N, G, KT, KG, KG8, NS);
+  hipLaunchKernelGGL(zero_rows_kernel, dim3((unsigned)ceil_div(NS * KG8 * 32, 256)), dim3(256),
+                     0, s, scales, zeros, (uint16_t *)rz, N, KG, KG8, NS);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Dequantize.  One thread per repacked lane vector (four words = 32 weights of
 // one column).  Each weight is fp16((q - 8) * s): the fp16 product of the
 // exact value q - 8 and the fp16 scale rounds the exact product once.  With
 // BF the weights are bf16((q - 8) * s), the exact product rounded once to
-// bf16 (the operand the bf16-activation kernels feed their MFMAs).
+// bf16 (the operand the bf16-activation kernels feed their MFMAs).  With
+// zero rows rz (null: none) each weight is the single rounding of
+// (q - 8) * s + z, as the GEMM kernels compute it.
 //
 // CANONICAL writes W16 [K, N] row-major (the definition's layout).
 // Otherwise the output is fragment-ordered for the dense GEMM: the lane
@@ -168,6 +209,7 @@ hipError_t launch_unrepack(const void *rw, const void *rs, int64_t K, int64_t N,
 template <bool CANONICAL, bool BF>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint4_t *__restrict__ rw,
                                                       const uint16_t *__restrict__ rs,
+                                                      const uint16_t *__restrict__ rz,
                                                       uint16_t *__restrict__ W16, int64_t N,
                                                       int64_t KT, int64_t KG8, int64_t NS,
                                                       int gshift) {
@@ -179,17 +221,20 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint4_t *__restrict_
   const int h = l >> 5, c = l & 31;
   const int64_t n = t * kStrip + c;
   const int g = (int)((64 * q + 32 * h) >> gshift);
-  const uint16_t s16 = rs[scale_index(t, KG8, c, g)];
-  const _Float16 sh = bitcast<_Float16>(s16);
-  const half2_t s2 = {sh, sh};
-  const Dequant::BScale bs(s16);
+  const int64_t si = scale_index(t, KG8, c, g);
+  const uint16_t s16 = rs[si];
+  const uint16_t z16 = rz != nullptr ? rz[si] : (uint16_t)0;
+  const _Float16 sh = bitcast<_Float16>(s16), zh = bitcast<_Float16>(z16);
+  const half2_t s2 = {sh, sh}, z2 = {zh, zh};
+  const Dequant::BScale bs = rz != nullptr ? Dequant::BScale(s16, z16) : Dequant::BScale(s16);
   const uint4_t v = rw[idx];
   const Dequant dq;
   auto word = [&](uint32_t x) {
     if constexpr (BF)
       return bitcast<uint4_t>(dq.scaled_bf16(x, bs));
     else
-      return bitcast<uint4_t>(dq.scaled(x, s2));
+      return rz != nullptr ? bitcast<uint4_t>(dq.scaled_zp(x, s2, z2))
+                           : bitcast<uint4_t>(dq.scaled(x, s2));
   };
   if (CANONICAL) {
     if (n >= N) return;
@@ -209,29 +254,31 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint4_t *__restrict_
 }
 
 template <bool CANONICAL>
-static hipError_t launch_dequant(const void *rw, const void *rs, int64_t K, int64_t N, int G,
-                                 bool bf16, uint16_t *W, hipStream_t s) {
+static hipError_t launch_dequant(const void *rw, const void *rs, const void *rz, int64_t K,
+                                 int64_t N, int G, bool bf16, uint16_t *W, hipStream_t s) {
   int64_t KT, KG, KG8, NS;
   repack_geometry(K, N, G, KT, KG, KG8, NS);
   const int gshift = group_shift(K, G);
   const dim3 grid((unsigned)ceil_div(NS * KT * 64, 256));
   if (bf16)
     hipLaunchKernelGGL((dequant_kernel<CANONICAL, true>), grid, dim3(256), 0, s,
-                       (const uint4_t *)rw, (const uint16_t *)rs, W, N, KT, KG8, NS, gshift);
+                       (const uint4_t *)rw, (const uint16_t *)rs, (const uint16_t *)rz, W, N, KT,
+                       KG8, NS, gshift);
   else
     hipLaunchKernelGGL((dequant_kernel<CANONICAL, false>), grid, dim3(256), 0, s,
-                       (const uint4_t *)rw, (const uint16_t *)rs, W, N, KT, KG8, NS, gshift);
+                       (const uint4_t *)rw, (const uint16_t *)rs, (const uint16_t *)rz, W, N, KT,
+                       KG8, NS, gshift);
   return hipGetLastError();
 }
 
-hipError_t launch_dequant_canonical(const void *rw, const void *rs, int64_t K, int64_t N, int G,
-                                    bool bf16, uint16_t *W, hipStream_t s) {
-  return launch_dequant<true>(rw, rs, K, N, G, bf16, W, s);
+hipError_t launch_dequant_canonical(const void *rw, const void *rs, const void *rz, int64_t K,
+                                    int64_t N, int G, bool bf16, uint16_t *W, hipStream_t s) {
+  return launch_dequant<true>(rw, rs, rz, K, N, G, bf16, W, s);
 }
 
-hipError_t launch_dequant_fragment(const void *rw, const void *rs, int64_t K, int64_t N, int G,
-                                   bool bf16, uint16_t *Wf, hipStream_t s) {
-  return launch_dequant<false>(rw, rs, K, N, G, bf16, Wf, s);
+hipError_t launch_dequant_fragment(const void *rw, const void *rs, const void *rz, int64_t K,
+                                   int64_t N, int G, bool bf16, uint16_t *Wf, hipStream_t s) {
+  return launch_dequant<false>(rw, rs, rz, K, N, G, bf16, Wf, s);
 }
 
 }  // namespace w4a16

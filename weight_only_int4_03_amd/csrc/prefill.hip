@@ -55,12 +55,14 @@ struct PrefillArgs {
   float *ws;
   const float *rowscale;  // per-row output factor, or null
   int gshift;             // group of k = k >> gshift
+  const uint16_t *rz;     // prescaled zero rows (laid out as rs), or null
 };
 
 template <int WN, bool DENSE>
 struct PrefillB {
   uint4_t v[WN][DENSE ? 4 : 1];
   uint16_t sc[WN];
+  uint16_t zs[WN];  // zero row of the group (0 without zero points)
 };
 
 template <int MI, int WN, bool DENSE, bool SWIGLU, bool BF>
@@ -134,8 +136,9 @@ void prefill_kernel(PrefillArgs p) {
       } else {
         r.v[w][0] = sval[w] ? load_nt(p.rw + vec) : uint4_t{0, 0, 0, 0};
         const int g = (64 * q + 32 * h) >> p.gshift;
-        r.sc[w] = sval[w] ? p.rs[scale_index(strip[w], p.KG8, c, g)]
-                          : (uint16_t)0;
+        const int64_t si = scale_index(strip[w], p.KG8, c, g);
+        r.sc[w] = sval[w] ? p.rs[si] : (uint16_t)0;
+        r.zs[w] = sval[w] && p.rz != nullptr ? p.rz[si] : (uint16_t)0;
       }
     }
   };
@@ -154,11 +157,9 @@ void prefill_kernel(PrefillArgs p) {
       for (int w = 0; w < WN; ++w) {
         if constexpr (DENSE) {
           bf[w] = r.v[w][j];
-        } else if constexpr (BF) {
-          bf[w] = bitcast<uint4_t>(dq.scaled_bf16(r.v[w][0][j], Dequant::BScale(r.sc[w])));
         } else {
-          const _Float16 sh = bitcast<_Float16>(r.sc[w]);
-          bf[w] = bitcast<uint4_t>(dq.scaled(r.v[w][0][j], half2_t{sh, sh}));
+          // A zero row of 0 leaves every weight as the plain scaled value.
+          bf[w] = dq.scaled_bits<BF, true>(r.v[w][0][j], r.sc[w], r.zs[w]);
         }
       }
 #pragma unroll
@@ -241,10 +242,12 @@ void prefill_kernel(PrefillArgs p) {
 // offset.  Each step issues the next step's loads, then runs its MFMAs
 // (a scheduling barrier keeps the loads first), then meets the workgroup
 // barrier, which also waits for the loads.
-template <int MI, int WM, int WNW, int TPS, bool DENSE, bool SWIGLU, bool BF>
+template <int MI, int WM, int WNW, int TPS, bool DENSE, bool SWIGLU, bool BF, bool ZP>
 __global__ __launch_bounds__(64 * WM * WNW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill2_kernel(PrefillArgs p) {
   // TPS: 64-k tiles per pipeline step (2 = one whole 128-k scale group).
+  // ZP: zero rows (AWQ zero points prescaled as fp16((8 - zp) s)), loaded
+  // with the scales into the high half of the same register.
   // All global reads are buffer loads: a per-lane 32-bit offset fixed for the
   // whole k loop plus a scalar offset that advances with k, so the loop does
   // no address arithmetic and holds no 64-bit pointers.  Buffer reads past the
@@ -262,9 +265,11 @@ void prefill2_kernel(PrefillArgs p) {
   // tell the stage being filled from the stage being read.
   __shared__ uint4_t lds0[BM * CH];
   __shared__ uint4_t lds1[BM * CH];
+  static_assert(!(DENSE && ZP), "the dense tier's weights are already dequantized");
   struct BRegs {
     uint4_t v[2][TPS][NV];
-    uint32_t sc[2][TPS];  // per strip and 64-k tile (tiles may lie in different groups)
+    uint32_t sc[2][TPS];  // per strip and 64-k tile (tiles may lie in different groups):
+                          // scale bits, and with ZP the zero row's in the high half
   };
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -313,6 +318,8 @@ void prefill2_kernel(PrefillArgs p) {
       (void *)p.rw, (short)0, p.NS * p.KT * 64 * 16 * NV, kBufferConfig);
   const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
       (void *)p.rs, (short)0, p.NS * p.KG8 * 512, kBufferConfig);
+  const __amdgpu_buffer_rsrc_t rzr = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(ZP ? p.rz : p.rs), (short)0, p.NS * p.KG8 * 512, kBufferConfig);
 
   // LDS swizzle: 16 consecutive rows read at one k land in 16 distinct
   // 16-byte bank groups (the 64 banks x 4 bytes), so the 16 lanes that an
@@ -362,8 +369,13 @@ void prefill2_kernel(PrefillArgs p) {
         const int g = (64 * (TPS * q + t) + 32 * h) >> p.gshift;
         const int g_off = (g >> 3) * 512 + (g & 7) * 2;
 #pragma unroll
-        for (int w = 0; w < 2; ++w)
+        for (int w = 0; w < 2; ++w) {
           r.sc[w][t] = __builtin_amdgcn_raw_buffer_load_b16(rsc, s_off[w] + g_off, 0, 0);
+          if constexpr (ZP)
+            r.sc[w][t] |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rzr, s_off[w] + g_off,
+                                                                          0, 0)
+                          << 16;
+        }
       }
     }
   };
@@ -384,6 +396,9 @@ void prefill2_kernel(PrefillArgs p) {
       for (int w = 0; w < 2; ++w) {
         if constexpr (DENSE) {
           bf[w] = r.v[w][t][j];
+        } else if constexpr (ZP) {
+          bf[w] = dq.scaled_bits<BF, true>(r.v[w][t][0][j], (uint16_t)r.sc[w][t],
+                                           (uint16_t)(r.sc[w][t] >> 16));
         } else if constexpr (BF) {
           bf[w] = bitcast<uint4_t>(
               dq.scaled_bf16(r.v[w][t][0][j], Dequant::BScale((uint16_t)r.sc[w][t])));
@@ -545,6 +560,7 @@ static PrefillArgs prefill_args(const Problem &p, int BM, const void *weights) {
   a.spk = a.KT;
   a.ws = nullptr;
   a.rowscale = p.rowscale;
+  a.rz = (const uint16_t *)p.rz;
   return a;
 }
 
@@ -673,7 +689,7 @@ static bool prefill2_config(const Problem &p, bool dense, Prefill2Config &c) {
   return true;
 }
 
-template <int MI, int TPS, bool DENSE, bool SWIGLU, bool BF>
+template <int MI, int TPS, bool DENSE, bool SWIGLU, bool BF, bool ZP>
 static hipError_t launch_prefill2_t(const Problem &p, const void *weights, const Prefill2Config &c,
                                     void *workspace, hipStream_t s) {
   constexpr int WM = 2, WNW = 4;
@@ -682,7 +698,7 @@ static hipError_t launch_prefill2_t(const Problem &p, const void *weights, const
   a.KS = c.ks;
   a.spk = a.KT / TPS / c.ks;
   a.ws = (float *)workspace;
-  hipLaunchKernelGGL((prefill2_kernel<MI, WM, WNW, TPS, DENSE, SWIGLU, BF>),
+  hipLaunchKernelGGL((prefill2_kernel<MI, WM, WNW, TPS, DENSE, SWIGLU, BF, ZP>),
                      dim3(a.tiles_m * a.tiles_n * c.ks), dim3(64 * WM * WNW), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || c.ks == 1) return e;
@@ -693,14 +709,23 @@ static hipError_t launch_prefill2_t(const Problem &p, const void *weights, const
   return hipGetLastError();
 }
 
+template <int MI, int TPS, bool DENSE, bool ZP>
+static hipError_t launch_prefill2_z(const Problem &p, const void *weights,
+                                    const Prefill2Config &c, void *ws, hipStream_t s) {
+  if (p.bf16)
+    return p.swiglu ? launch_prefill2_t<MI, TPS, DENSE, true, true, ZP>(p, weights, c, ws, s)
+                    : launch_prefill2_t<MI, TPS, DENSE, false, true, ZP>(p, weights, c, ws, s);
+  return p.swiglu ? launch_prefill2_t<MI, TPS, DENSE, true, false, ZP>(p, weights, c, ws, s)
+                  : launch_prefill2_t<MI, TPS, DENSE, false, false, ZP>(p, weights, c, ws, s);
+}
+
 template <int MI, int TPS, bool DENSE>
 static hipError_t launch_prefill2_tps(const Problem &p, const void *weights,
                                       const Prefill2Config &c, void *ws, hipStream_t s) {
-  if (p.bf16)
-    return p.swiglu ? launch_prefill2_t<MI, TPS, DENSE, true, true>(p, weights, c, ws, s)
-                    : launch_prefill2_t<MI, TPS, DENSE, false, true>(p, weights, c, ws, s);
-  return p.swiglu ? launch_prefill2_t<MI, TPS, DENSE, true, false>(p, weights, c, ws, s)
-                  : launch_prefill2_t<MI, TPS, DENSE, false, false>(p, weights, c, ws, s);
+  if constexpr (!DENSE) {
+    if (p.zp) return launch_prefill2_z<MI, TPS, DENSE, true>(p, weights, c, ws, s);
+  }
+  return launch_prefill2_z<MI, TPS, DENSE, false>(p, weights, c, ws, s);
 }
 
 template <int MI, bool DENSE>
@@ -731,11 +756,13 @@ int tiled_describe(const Problem &p, bool dense, char *buf, size_t n) {
   const char *pre = !dense ? "" : (p.bf16 ? "dequant_kernel<false, true>; " : "dequant_kernel<false, false>; ");
   const char *d = dense ? "true" : "false", *sw = p.swiglu ? "true" : "false";
   const char *bf = p.bf16 ? "true" : "false";
+  const char *zp = p.zp && !dense ? "true" : "false";
   Prefill2Config c;
   if (prefill2_config(p, dense, c)) {
     int k = snprintf(buf, n,
-                     "%sprefill2_kernel<%d, 2, 4, %d, %s, %s, %s> workgroups=%d threads=512 ks=%d", pre,
-                     c.bm / 64, c.tps, d, sw, bf, c.tiles * c.ks, c.ks);
+                     "%sprefill2_kernel<%d, 2, 4, %d, %s, %s, %s, %s> workgroups=%d threads=512 "
+                     "ks=%d",
+                     pre, c.bm / 64, c.tps, d, sw, bf, zp, c.tiles * c.ks, c.ks);
     if (c.ks > 1 && k > 0 && (size_t)k < n)
       k += snprintf(buf + k, n - k, "; prefill_reduce_kernel<%s, %s>", sw, bf);
     return k;
@@ -754,7 +781,8 @@ int64_t dense_workspace_bytes(const Problem &p) {
 hipError_t launch_dense(const Problem &p, void *workspace, hipStream_t s) {
   if (workspace == nullptr) return hipErrorInvalidValue;
   void *w16f = workspace;
-  hipError_t e = launch_dequant_fragment(p.rw, p.rs, p.K, p.N, p.G, p.bf16, (uint16_t *)w16f, s);
+  hipError_t e =
+      launch_dequant_fragment(p.rw, p.rs, p.rz, p.K, p.N, p.G, p.bf16, (uint16_t *)w16f, s);
   if (e != hipSuccess) return e;
   Prefill2Config c;
   if (prefill2_config(p, true, c)) return launch_prefill2_m<4, true>(p, w16f, c, nullptr, s);

@@ -126,6 +126,17 @@ def ternary_activations(M: int, K: int, density: float = 1.0, seed: int = 0) -> 
     return np.where(keep, vals, 0.0).astype(np.float16)
 
 
+def zero_points(KG: int, N: int, seed: int = 0) -> np.ndarray:
+    """Zero points [KG, N] (uint8) of asymmetric 4-bit weights: mostly near
+    the middle of 0..15, as min/max quantization of roughly centred groups
+    gives, with every value 0..15 present."""
+    rng = np.random.default_rng(seed + 5)
+    z = np.clip(np.rint(rng.normal(7.5, 2.5, (KG, N))), 0, 15).astype(np.uint8)
+    flat = z.reshape(-1)
+    flat[: min(16, flat.size)] = np.arange(min(16, flat.size), dtype=np.uint8)
+    return z
+
+
 def random_words(K: int, N: int, seed: int = 0, group: int = G) -> tuple[np.ndarray, np.ndarray]:
     """Arbitrary packed words (every nibble 0..15, including 0, which the RTN
     quantizer never emits) with positive fp16 scales in [2^-9, 2^-5), one per

@@ -31,6 +31,7 @@ PATH_DENSE = 3
 PATHS = {"auto": PATH_AUTO, "decode": PATH_DECODE, "prefill": PATH_PREFILL, "dense": PATH_DENSE}
 FLAG_SWIGLU = 0x10
 FLAG_BF16 = 0x20
+FLAG_ZP = 0x40
 G = 128
 
 
@@ -57,6 +58,10 @@ _SIGNATURES = {
     "w4a16_unrepack": ([_p, _p, _i64, _i64, _int, _p, _p, _p], _int),
     "w4a16_dequant": ([_p, _p, _i64, _i64, _int, _p, _p], _int),
     "w4a16_dequant_bf16": ([_p, _p, _i64, _i64, _int, _p, _p], _int),
+    "w4a16_zero_rows": ([_p, _p, _i64, _i64, _int, _p, _p], _int),
+    "w4a16_dequant_zp": ([_p, _p, _p, _i64, _i64, _int, _int, _p, _p], _int),
+    "w4a16_gemm_zp": ([_p, _i64, _i64, _p, _p, _p, _i64, _int, _p, _p, _int, _p, _i64, _p],
+                      _int),
     "w4a16_gemm": ([_p, _i64, _i64, _p, _p, _i64, _int, _p, _p], _int),
     "w4a16_gemm_swiglu": ([_p, _i64, _i64, _p, _p, _i64, _int, _p, _p], _int),
     "w4a16_gemm_ex": ([_p, _i64, _i64, _p, _p, _i64, _int, _p, _int, _p, _i64, _p], _int),
@@ -152,17 +157,19 @@ def pack(W, G: int = G, stream=None, gamma=None):
 
 
 class RepackedWeight:
-    """Repacked device buffers of one [K,N] weight (built by :func:`repack`)."""
+    """Repacked device buffers of one [K,N] weight (built by :func:`repack`;
+    rz: prescaled zero rows of asymmetric weights, see :func:`zero_rows`)."""
 
-    def __init__(self, rw, rs, K: int, N: int, G: int = G):
-        self.rw, self.rs, self.K, self.N, self.G = rw, rs, K, N, G
+    def __init__(self, rw, rs, K: int, N: int, G: int = G, rz=None):
+        self.rw, self.rs, self.K, self.N, self.G, self.rz = rw, rs, K, N, G, rz
 
     def clone(self) -> "RepackedWeight":
-        return RepackedWeight(self.rw.clone(), self.rs.clone(), self.K, self.N, self.G)
+        return RepackedWeight(self.rw.clone(), self.rs.clone(), self.K, self.N, self.G,
+                              None if self.rz is None else self.rz.clone())
 
     @property
     def nbytes(self) -> int:
-        return self.rw.numel() + self.rs.numel()
+        return self.rw.numel() + self.rs.numel() + (0 if self.rz is None else self.rz.numel())
 
 
 def repacked_bytes(K: int, N: int, G: int = G):
@@ -194,26 +201,46 @@ def unrepack(w: RepackedWeight, G: int | None = None, stream=None):
     return packed, scales
 
 
+def zero_rows(w: RepackedWeight, scales, zeros, stream=None) -> RepackedWeight:
+    """Attach AWQ zero points to repacked weights: builds the prescaled zero
+    rows fp16((8 - zp) s) from the canonical scales [K/G,N] (fp16 bits) and the
+    zero points [K/G,N] (uint8), both device tensors.  Returns the weight with rz."""
+    torch = _torch()
+    assert scales.is_cuda and scales.element_size() == 2 and scales.is_contiguous()
+    assert zeros.is_cuda and zeros.dtype == torch.uint8 and zeros.is_contiguous()
+    assert tuple(zeros.shape) == tuple(scales.shape) == (w.K // w.G, w.N)
+    rz = torch.empty(repacked_bytes(w.K, w.N, w.G)[1], dtype=torch.uint8, device=w.rw.device)
+    _check(lib().w4a16_zero_rows(_ptr(scales), _ptr(zeros), w.K, w.N, w.G, _ptr(rz),
+                                 _stream(stream)))
+    return RepackedWeight(w.rw, w.rs, w.K, w.N, w.G, rz)
+
+
 def dequant(w: RepackedWeight, G: int | None = None, stream=None, bf16: bool = False):
-    """fp16 (or, with bf16, bf16) [K,N] dequantized weights (canonical row-major)."""
+    """fp16 (or, with bf16, bf16) [K,N] dequantized weights (canonical row-major),
+    with the zero rows when the weight has them."""
     torch = _torch()
     G = w.G if G is None else G
     W = torch.empty((w.K, w.N), dtype=torch.bfloat16 if bf16 else torch.float16,
                     device=w.rw.device)
+    if w.rz is not None:
+        _check(lib().w4a16_dequant_zp(_ptr(w.rw), _ptr(w.rs), _ptr(w.rz), w.K, w.N, G,
+                                      FLAG_BF16 if bf16 else 0, _ptr(W), _stream(stream)))
+        return W
     fn = lib().w4a16_dequant_bf16 if bf16 else lib().w4a16_dequant
     _check(fn(_ptr(w.rw), _ptr(w.rs), w.K, w.N, G, _ptr(W), _stream(stream)))
     return W
 
 
-def _flags(path, swiglu: bool, bf16: bool) -> int:
+def _flags(path, swiglu: bool, bf16: bool, zp: bool = False) -> int:
     return ((PATHS[path] if isinstance(path, str) else int(path)) | (FLAG_SWIGLU if swiglu else 0)
-            | (FLAG_BF16 if bf16 else 0))
+            | (FLAG_BF16 if bf16 else 0) | (FLAG_ZP if zp else 0))
 
 
 def gemm(A, w: RepackedWeight, swiglu: bool = False, path: str | int = "auto", out=None,
          workspace=None, G: int | None = None, stream=None, rowscale=None):
     """C = A * dequant(W) ([M,N] in A's dtype, fp16 or bf16); with swiglu,
-    Z = silu(C[:, :N/2]) * C[:, N/2:]."""
+    Z = silu(C[:, :N/2]) * C[:, N/2:].  Weights with zero rows (w.rz) go
+    through w4a16_gemm_zp."""
     torch = _torch()
     G = w.G if G is None else G
     assert A.is_cuda and A.dtype in (torch.float16, torch.bfloat16) and A.is_contiguous()
@@ -227,11 +254,16 @@ def gemm(A, w: RepackedWeight, swiglu: bool = False, path: str | int = "auto", o
     assert out.dtype == A.dtype
     flags = _flags(path, swiglu, bf16)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    if rowscale is None:
+    if rowscale is not None:
+        assert rowscale.is_cuda and rowscale.dtype == torch.float32 and rowscale.numel() == M
+    if w.rz is not None:
+        _check(lib().w4a16_gemm_zp(_ptr(A), M, K, _ptr(w.rw), _ptr(w.rs), _ptr(w.rz), w.N, G,
+                                   _ptr(rowscale), _ptr(out), flags, _ptr(workspace), ws_bytes,
+                                   _stream(stream)))
+    elif rowscale is None:
         _check(lib().w4a16_gemm_ex(_ptr(A), M, K, _ptr(w.rw), _ptr(w.rs), w.N, G, _ptr(out),
                                    flags, _ptr(workspace), ws_bytes, _stream(stream)))
     else:
-        assert rowscale.is_cuda and rowscale.dtype == torch.float32 and rowscale.numel() == M
         _check(lib().w4a16_gemm_rowscale(_ptr(A), M, K, _ptr(w.rw), _ptr(w.rs), w.N, G,
                                          _ptr(rowscale), _ptr(out), flags, _ptr(workspace),
                                          ws_bytes, _stream(stream)))
@@ -275,8 +307,8 @@ def gemm_swiglu(A, w: RepackedWeight, out=None, G: int | None = None, stream=Non
 
 
 def workspace_bytes(M: int, K: int, N: int, swiglu: bool = False, path: str | int = "auto",
-                    G: int = G, bf16: bool = False) -> int:
-    return _check(lib().w4a16_gemm_workspace_bytes(M, K, N, G, _flags(path, swiglu, bf16)))
+                    G: int = G, bf16: bool = False, zp: bool = False) -> int:
+    return _check(lib().w4a16_gemm_workspace_bytes(M, K, N, G, _flags(path, swiglu, bf16, zp)))
 
 
 def select_path(M: int, K: int, N: int, swiglu: bool = False, G: int = G) -> str:
@@ -285,11 +317,11 @@ def select_path(M: int, K: int, N: int, swiglu: bool = False, G: int = G) -> str
 
 
 def describe(M: int, K: int, N: int, swiglu: bool = False, path: str | int = "auto",
-             G: int = G, bf16: bool = False) -> str:
+             G: int = G, bf16: bool = False, zp: bool = False) -> str:
     """The kernel launches (profiler names and grids) a GEMM of this shape makes."""
     buf = ctypes.create_string_buffer(512)
-    _check(lib().w4a16_describe(M, K, N, G, _flags(path, swiglu, bf16), ctypes.addressof(buf),
-                                len(buf)))
+    _check(lib().w4a16_describe(M, K, N, G, _flags(path, swiglu, bf16, zp),
+                                ctypes.addressof(buf), len(buf)))
     return buf.value.decode()
 
 
@@ -318,3 +350,21 @@ def load_weight(W_host: np.ndarray, device="cuda", G: int = G, gamma=None) -> Re
     packed, scales = pack(Wd, G, gamma=gd)
     del Wd
     return repack(packed, scales, G)
+
+
+def load_weight_zp(q: np.ndarray, scales: np.ndarray, zeros: np.ndarray, device="cuda",
+                   G: int = G) -> RepackedWeight:
+    """Asymmetric (AWQ-style) host weights -> device: nibbles q [K,N] (uint8,
+    0..15), fp16 scale bits [K/G,N] and zero points [K/G,N] (uint8); packs q
+    in the canonical format on the host (eight nibbles per int32 along K),
+    repacks, and builds the prescaled zero rows."""
+    torch = _torch()
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    K, N = q.shape
+    words = np.zeros((K // 8, N), np.uint32)
+    for i in range(8):
+        words |= (q[i::8].astype(np.uint32) & 0xF) << np.uint32(4 * i)
+    packed = torch.from_numpy(words.view(np.int32)).to(device)
+    sd = torch.from_numpy(np.ascontiguousarray(scales, dtype=np.uint16).view(np.int16)).to(device)
+    zd = torch.from_numpy(np.ascontiguousarray(zeros, dtype=np.uint8)).to(device)
+    return zero_rows(repack(packed, sd, G), sd, zd)
