@@ -62,9 +62,11 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def alg_bytes(M, K, N, swiglu):
+def alg_bytes(M, K, N, swiglu, zp=False):
+    """Bytes a GEMM must move at least once: packed weights, scales (and zero
+    rows), activations, output."""
     n_out = N // 2 if swiglu else N
-    return K * N // 2 + 2 * (K // G) * N + 2 * M * K + 2 * M * n_out
+    return K * N // 2 + 2 * (K // G) * N * (2 if zp else 1) + 2 * M * K + 2 * M * n_out
 
 
 def flops(M, K, N):
@@ -99,11 +101,11 @@ def workloads():
     return w
 
 
-def kernel_key(M, K, N, swiglu, bf16=False):
+def kernel_key(M, K, N, swiglu, bf16=False, zp=False):
     """The kernel instance a GEMM launches under the automatic path, as the
     profiler names it, marked when a second (split-K reduction) launch
     follows it."""
-    desc = w4a16.describe(M, K, N, swiglu, bf16=bf16)
+    desc = w4a16.describe(M, K, N, swiglu, bf16=bf16, zp=zp)
     first = desc.split(";")[0]
     name = first.split(" workgroups=")[0].strip()
     return name + (" + reduce" if ";" in desc else "")
@@ -140,7 +142,7 @@ def stored_traffic(workload, kernel):
         return None
 
 
-def cpu_baseline(units, host_w, target_s=12.0, bf16=False):
+def cpu_baseline(units, host_w, target_s=12.0, bf16=False, host_zp=None):
     """Time the oracle's fp64 GEMM (+ SwiGLU) on a column sample of every unit
     (host_w: the same seeded fp32 weights the GPU was given, keyed by (K, N))."""
     import oracle
@@ -165,12 +167,20 @@ def cpu_baseline(units, host_w, target_s=12.0, bf16=False):
         Ws = np.concatenate([W[:, :ns], W[:, N // 2:N // 2 + ns]], axis=1) if sw else W[:, :ns]
         packed, s16 = o.quantize_pack(np.ascontiguousarray(Ws))
         A = (synth.activations_bf16 if bf16 else synth.activations)(M, K, seed=0, outliers=outl)
+        if host_zp is not None:
+            Z = host_zp[(K, N)]
+            Zs = np.concatenate([Z[:, :ns], Z[:, N // 2:N // 2 + ns]], axis=1) if sw else Z[:, :ns]
+            z16 = o.zero_rows(s16, np.ascontiguousarray(Zs))
         t0 = time.perf_counter()
-        C = (o.gemm_bf16_f64 if bf16 else o.gemm_f64)(A, packed, s16)
+        if host_zp is not None:
+            Wz = o.dequant_zp(packed, s16, z16, bf16=bf16)
+            C = (o.gemm_wb_f64 if bf16 else o.gemm_w16_f64)(A, Wz)
+        else:
+            C = (o.gemm_bf16_f64 if bf16 else o.gemm_f64)(A, packed, s16)
         if sw:
             o.swiglu_f64(C)
         elapsed += time.perf_counter() - t0
-        done_bytes += alg_bytes(M, K, Ws.shape[1], sw)
+        done_bytes += alg_bytes(M, K, Ws.shape[1], sw, host_zp is not None)
         cols_desc.append(ns)
     return {
         "value": round(done_bytes / elapsed / 1e9, 4),
@@ -252,6 +262,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--dtype", default="fp16", choices=["fp16", "bf16"],
                     help="activation and output type (the weights are the same)")
+    ap.add_argument("--zero-points", action="store_true",
+                    help="asymmetric weights: seeded zero points as prescaled zero rows")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for hardware-counter calibration)")
     args = ap.parse_args()
@@ -283,11 +295,17 @@ def main():
     # Weights: one seeded W per distinct projection, quantized, packed and
     # repacked on the device, then cloned into rotation copies.
     shapes = sorted({(k, n) for _, _, k, n, *_ in units})
-    base, host_w = {}, {}
+    zp = args.zero_points
+    base, host_w, host_zp = {}, {}, ({} if zp else None)
     for (k, n) in shapes:
         log("weights K=%d N=%d" % (k, n))
         host_w[(k, n)] = synth.weights(k, n, seed=0)
         base[(k, n)] = w4a16.load_weight(host_w[(k, n)])
+        if zp:
+            host_zp[(k, n)] = synth.zero_points(k // G, n, seed=0)
+            _, scales = w4a16.unrepack(base[(k, n)])
+            base[(k, n)] = w4a16.zero_rows(base[(k, n)], scales,
+                                           torch.from_numpy(host_zp[(k, n)]).to(dev))
     torch.cuda.synchronize()
     slot_bytes = [sum(base[(k, n)].nbytes for _, _, k, n, _, _, s in units if s == slot)
                   for slot in range(nslots)]
@@ -317,7 +335,9 @@ def main():
     def run_unit(u, copy):
         label, m, k, n, sw, outl, _ = u
         w = copies[(k, n)][copy]
-        if sw:
+        if zp:
+            w4a16.gemm(acts[(m, k, outl)], w, swiglu=sw, out=outs[label])
+        elif sw:
             if bf16:
                 w4a16.gemm(acts[(m, k, outl)], w, swiglu=True, out=outs[label])
             else:
@@ -384,7 +404,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = ev0.elapsed_time(ev1) / args.steps
-    step_bytes = sum(alg_bytes(m, k, n, sw) for _, m, k, n, sw, *_ in units)
+    step_bytes = sum(alg_bytes(m, k, n, sw, zp) for _, m, k, n, sw, *_ in units)
     step_flops = sum(flops(m, k, n) for _, m, k, n, *_ in units)
     log("step: %.2f us (wall %.2f us), %.1f MB, %.2f GFLOP"
         % (ms_step * 1e3, wall / args.steps * 1e6, step_bytes / 1e6, step_flops / 1e9))
@@ -406,10 +426,10 @@ def main():
             b.record(stream)
         torch.cuda.synchronize()
         us = a.elapsed_time(b) * 1e3 / (args.reps * ncopies)
-        by, fl = alg_bytes(m, k, n, sw), flops(m, k, n)
+        by, fl = alg_bytes(m, k, n, sw, zp), flops(m, k, n)
         detail.append({"gemm": label, "M": m, "K": k, "N": n, "swiglu": sw,
-                       "kernel": kernel_key(m, k, n, sw, bf16),
-                       "launch": w4a16.describe(m, k, n, sw, bf16=bf16),
+                       "kernel": kernel_key(m, k, n, sw, bf16, zp),
+                       "launch": w4a16.describe(m, k, n, sw, bf16=bf16, zp=zp),
                        "us": round(us, 3),
                        "GB/s": round(by / us / 1e3, 1), "TFLOP/s": round(fl / us / 1e6, 2),
                        "hbm_frac": round(by / us / 1e3 / HBM_PEAK_GBS, 4),
@@ -431,7 +451,7 @@ def main():
     for d in detail:
         e = by_kernel.setdefault(d["kernel"], {"us": 0.0, "bytes": 0, "flops": 0, "launches": 0})
         e["us"] += d["us"]
-        e["bytes"] += alg_bytes(d["M"], d["K"], d["N"], d["swiglu"])
+        e["bytes"] += alg_bytes(d["M"], d["K"], d["N"], d["swiglu"], zp)
         e["flops"] += flops(d["M"], d["K"], d["N"])
         e["launches"] += 1
     dom = max(by_kernel, key=lambda k: by_kernel[k]["us"])
@@ -448,7 +468,8 @@ def main():
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4)}
     ceiling = ceilings["stream_read_GBs"] if hbm_bound else ceilings["mfma_f16_TFLOPs"]
     roof["frac_of_measured_ceiling"] = round(achieved / ceiling, 4) if ceiling else None
-    roof["traffic"] = stored_traffic(args.workload + ("_bf16" if bf16 else ""), dom)
+    suffix = ("_bf16" if bf16 else "") + ("_zp" if zp else "")
+    roof["traffic"] = stored_traffic(args.workload + suffix, dom)
     roof["kernel"] = dom
     roof["launch_workgroups"] = sorted({int(re.search(r"workgroups=(\d+)", d["launch"]).group(1))
                                         for d in detail if d["kernel"] == dom})
@@ -466,7 +487,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
-        cpu = cpu_baseline(units, host_w, bf16=bf16)
+        cpu = cpu_baseline(units, host_w, bf16=bf16, host_zp=host_zp)
         if unit == "TFLOP/s":
             cpu["value"] = round(cpu["value"] * step_flops / step_bytes / 1e3, 6)
             cpu["unit"] = "TFLOP/s"
@@ -485,9 +506,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if bf16 else "fp16",
         "data": "synthetic (seeded N(0,1) " + args.dtype + " activations, N(0,0.02) weights quantized to int4 "
-                "G=128)",
-        "config": {"workload": args.workload + ("_bf16" if bf16 else ""), "description": desc,
-                   "activations": args.dtype, "G": G,
+                "G=128" + (", seeded zero points near 8 as prescaled zero rows" if zp else "") + ")",
+        "config": {"workload": args.workload + suffix, "description": desc,
+                   "activations": args.dtype, "G": G, "zero_points": zp,
                    "gemms_per_step": len(units), "alg_bytes_per_step": step_bytes,
                    "flops_per_step": step_flops, "weight_copies": ncopies,
                    "path": "auto",
