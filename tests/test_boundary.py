@@ -154,14 +154,18 @@ def test_describe_names_the_launches():
     """The launch description names kernel instances as profilers print them
     (template arguments after the tile shape: SwiGLU epilogue, bf16
     activations, then for decode_kernel the scaling before the MFMA, and for
-    decode_kernel and prefill2_kernel the zero rows)."""
+    decode_kernel and prefill2_kernel the zero rows, and for decode_kernel the
+    half-strip workgroups)."""
     d = w4a16.describe(1, 4096, 28672, swiglu=True)
     assert d.startswith("decode_coop_kernel<16, 2, ") and d.split(">")[0].endswith("true, false")
     d = w4a16.describe(1, 4096, 28672, swiglu=True, bf16=True)
     assert d.startswith("decode_coop_kernel<16, 2, ") and d.split(">")[0].endswith("true, true")
     d = w4a16.describe(1, 4096, 4096)
     assert d.startswith("decode_kernel<16, 1, ") and d.split(">")[0].endswith(
-        "false, false, false, false")
+        "false, false, false, false, true"), d        # 128 strips: half strips
+    assert " workgroups=256 " in d and d.endswith("ks=1"), d
+    d = w4a16.describe(24, 4096, 4096)
+    assert d.startswith("decode_kernel<32, 1, ") and d.split(">")[0].endswith("false, false"), d
     assert "prefill2_kernel<4, 2, 4, 2, false, true, false, false>" in w4a16.describe(
         4096, 4096, 28672, swiglu=True)
     assert "prefill2_kernel<4, 2, 4, 2, false, true, true, false>" in w4a16.describe(
@@ -172,10 +176,10 @@ def test_describe_names_the_launches():
     # prefill takes the ZP instance, the dense tier folds them into its dequant.
     d = w4a16.describe(1, 4096, 28672, swiglu=True, zp=True)
     assert d.startswith("decode_kernel<16, 2, ") and d.split(">")[0].endswith(
-        "true, false, true, true"), d
+        "true, false, true, true, false"), d
     d = w4a16.describe(4, 4096, 4096, bf16=True, zp=True)
     assert d.startswith("decode_kernel<16, 1, ") and d.split(">")[0].endswith(
-        "false, true, true, true"), d
+        "false, true, true, true, true"), d
     assert "prefill2_kernel<4, 2, 4, 2, false, false, false, true>" in w4a16.describe(
         4096, 4096, 4096, zp=True)
     assert w4a16.describe(4096, 4096, 4096, path="dense", zp=True).startswith(

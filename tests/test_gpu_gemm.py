@@ -184,6 +184,42 @@ def test_prefill_two_waves_per_simd(monkeypatch, path, M, K, N, swiglu):
     gemm_case(M, K, N, swiglu=swiglu, path=path, seed=M + N)
 
 
+@pytest.mark.parametrize("half,ks,waves,depth", [(1, 1, 8, 4), (1, 2, 8, 4), (1, 3, 4, 2),
+                                                (1, 1, 4, 4), (0, 1, 8, 2), (0, 2, 8, 4)])
+@pytest.mark.parametrize("M,K,N,swiglu", [(1, 2048, 1064, False), (5, 4096, 2112, True),
+                                          (16, 1024, 1088, False), (12, 14336, 1024, False)])
+def test_decode_half_strips(monkeypatch, half, ks, waves, depth, M, K, N, swiglu):
+    """The per-wave decode kernel with each workgroup on one 16-column half of
+    its strips (and on whole strips), with and without split K, at both wave
+    counts and pipeline depths; ragged N (a partial last strip)."""
+    monkeypatch.setenv("W4A16_DECODE_COOP", "0")
+    monkeypatch.setenv("W4A16_DECODE_HALF", str(half))
+    monkeypatch.setenv("W4A16_DECODE_KS", str(ks))
+    monkeypatch.setenv("W4A16_DECODE_WAVES", str(waves))
+    monkeypatch.setenv("W4A16_DECODE_DEPTH", str(depth))
+    d = w4a16.describe(M, K, N, swiglu=swiglu, path="decode")
+    assert d.split(">")[0].endswith("true" if half else "false"), d
+    assert ("ks=%d" % ks) in d, d
+    gemm_case(M, K, N, swiglu=swiglu, path="decode", seed=M + K + ks)
+
+
+def test_decode_half_strips_bit_exact_integer_inputs(monkeypatch):
+    """Half-strip workgroups with split K: ternary activations and power-of-two
+    scales give exact sums, so both halves of every partial tile must land in
+    place for the output to be bit-exact."""
+    monkeypatch.setenv("W4A16_DECODE_COOP", "0")
+    monkeypatch.setenv("W4A16_DECODE_HALF", "1")
+    for ks in (1, 2):
+        monkeypatch.setenv("W4A16_DECODE_KS", str(ks))
+        for M, K, N in [(3, 2048, 1088), (16, 4096, 2048)]:
+            W = synth.grid_weights(K, N, p=4, seed=M)
+            A = synth.ternary_activations(M, K, density=1.0, seed=M)
+            w = w4a16.load_weight(W)
+            out = fp16_out(w4a16.gemm(to_dev(A), w, path="decode"))
+            packed_o, s16_o = orc().quantize_pack(W)
+            assert np.array_equal(out.astype(np.float64), orc().gemm_f64(A, packed_o, s16_o))
+
+
 PREFILL2_CONFIGS = [(64, 1, 1), (128, 1, 4), (256, 1, 2), (64, 2, 2), (128, 2, 4), (256, 2, 1),
                     (64, 1, 8), (256, 2, 4)]
 

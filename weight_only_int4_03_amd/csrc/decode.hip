@@ -59,20 +59,28 @@ struct DecodeFrag {
 // accumulated unscaled and its tile scaled once afterwards.
 // ZP: zero rows (AWQ zero points prescaled as fp16((8 - zp) s)); each weight
 // is then the one rounding of (u - 8) s + z, so it is scaled before the MFMA.
-template <int MT, int SPW, int WAVES, int D, int RPL, bool SWIGLU, bool BF, bool PRE, bool ZP>
+// HALF (MT=16 only): the workgroup owns one 16-column half of each of its
+// strips (workgroups 2b and 2b+1 share strip group b), which doubles the
+// workgroups of a narrow projection without splitting K.
+template <int MT, int SPW, int WAVES, int D, int RPL, bool SWIGLU, bool BF, bool PRE, bool ZP,
+          bool HALF>
 __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
   static_assert(PRE || !BF, "bf16 weights are always scaled before the MFMA");
   static_assert(PRE || !ZP, "weights with zero points are scaled before the MFMA");
+  static_assert(!HALF || MT == 16, "half strips need the 16-column MFMA");
   static_assert(MT == 16 ? (RPL >= 1 && RPL <= 4) : RPL == 16, "rows per lane");
   extern __shared__ float lds[];  // [WAVES][SPW][M][32]
   constexpr int SH = SWIGLU ? SPW / 2 : SPW;
-  constexpr int NPART = MT == 16 ? 2 : 1;  // 16-column halves (MT=16) or whole strip
+  // 16-column halves per workgroup (MT=16) or the whole strip (MT=32).
+  constexpr int NPART = MT == 16 ? (HALF ? 1 : 2) : 1;
   typedef typename std::conditional<MT == 16, float4_t, float16_t>::type acc_t;
   typedef DecodeFrag<MT, SPW> Frag;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-  const int sg = blockIdx.x % p.nsg, split = blockIdx.x / p.nsg;
+  const int half = HALF ? (int)(blockIdx.x & 1) : 0;  // first 16-column half owned
+  const int bid = HALF ? (int)(blockIdx.x >> 1) : (int)blockIdx.x;
+  const int sg = bid % p.nsg, split = bid / p.nsg;
   const int M = p.M;
   const Dequant dq;
 
@@ -122,16 +130,17 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
       const char *wp = wbase[s] + ow;
       if constexpr (MT == 16) {
 #pragma unroll
-        for (int part = 0; part < 2; ++part) f.b[s][part] = load_nt((const uint4_t *)(wp + part * 256));
+        for (int part = 0; part < NPART; ++part)
+          f.b[s][part] = load_nt((const uint4_t *)(wp + (half + part) * 256));
       } else {
 #pragma unroll
         for (int x = 0; x < 2; ++x) f.b[s][x] = load_nt((const uint4_t *)(wp + x * 1024));
       }
       if constexpr (PRE) {
         if constexpr (MT == 16) {
-          const uint32_t so = soff((128 * g + klane) >> p.gshift);
+          const uint32_t so = soff((128 * g + klane) >> p.gshift) + half * 256;
 #pragma unroll
-          for (int part = 0; part < 2; ++part) {
+          for (int part = 0; part < NPART; ++part) {
             f.sc[s][part][0] = *(const uint16_t *)(sbase[s] + so + part * 256);
             if constexpr (ZP) f.zs[s][part][0] = *(const uint16_t *)(zbase[s] + so + part * 256);
           }
@@ -144,7 +153,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
           }
         }
       } else {
-        const char *sp = sbase[s] + soff((128 * g) >> p.gshift);
+        const char *sp = sbase[s] + soff((128 * g) >> p.gshift) + half * 256;
 #pragma unroll
         for (int part = 0; part < NPART; ++part)
           f.sc[s][part][0] = *(const uint16_t *)(sp + part * 256);
@@ -263,7 +272,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
 #pragma unroll
       for (int r = 0; r < (MT == 16 ? 4 : 16); ++r) {
         const int m = MT == 16 ? 4 * g4 + r : 8 * (r >> 2) + 4 * h + (r & 3);
-        const int col = MT == 16 ? 16 * part + c16 : c32;
+        const int col = MT == 16 ? 16 * (half + part) + c16 : c32;
         if (m < M) lds[((wave * SPW + s) * M + m) * 32 + col] = acc[s][part][r];
       }
     }
@@ -279,14 +288,18 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
     return v;
   };
 
+  // Tile element e of the columns this workgroup owns, in the [s][m][32]
+  // order of the tile (with HALF: 16 of each 32).
+  auto owned = [&](int e) { return HALF ? ((e >> 4) << 5) + 16 * half + (e & 15) : e; };
+  constexpr int OWN = HALF ? 16 : 32;
   if (p.KS == 1) {
-    const int E = SH * M * 32;
+    const int E = SH * M * OWN;
     for (int e = threadIdx.x; e < E; e += nthreads)
-      decode_epilogue<SPW, SWIGLU, BF>(p, sg, e, wave_sum);
+      decode_epilogue<SPW, SWIGLU, BF>(p, sg, owned(e), wave_sum);
     return;
   }
   float *mine = p.ws + ((int64_t)sg * p.KS + split) * tileE;
-  for (int e = threadIdx.x; e < tileE; e += nthreads) mine[e] = wave_sum(e);
+  for (int e = threadIdx.x; e < SPW * M * OWN; e += nthreads) mine[owned(e)] = wave_sum(owned(e));
 }
 
 // Second stage for KS > 1: one thread per output element sums the KS partial
@@ -312,6 +325,7 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs p) {
 
 struct DecodeConfig {
   int MT, SPW, WAVES, D, KS, nsg;
+  bool half;  // one 16-column half of each strip per workgroup (MT=16)
 };
 
 static int env_int(const char *name, int fallback) {
@@ -323,9 +337,16 @@ static int env_int(const char *name, int fallback) {
 
 // Waves per workgroup and K splits.  The aim is enough waves in flight to
 // cover HBM latency (several per SIMD on all 256 CUs) without splitting K
-// across workgroups unless the strip groups alone leave CUs idle.
-// W4A16_DECODE_WAVES (4 or 8), W4A16_DECODE_KS and W4A16_DECODE_DEPTH
-// (groups loaded ahead: 2 or 4) override the choice.
+// across workgroups unless the strip groups alone leave CUs idle.  Half
+// strips (M <= 16) double the workgroups of a narrow projection; measured on
+// MI355X they pay off where the doubled grid is at most one workgroup per CU
+// and K is short (or M <= 4): each half-strip workgroup reads the whole
+// activation slice for half the weights, so at larger M and long K the
+// activation loads dominate, and a grid of 1.5 workgroups per CU leaves half
+// the CUs with twice the work.  Four groups in flight instead of two above
+// M = 8.  W4A16_DECODE_HALF (0 or 1), W4A16_DECODE_WAVES (4 or 8),
+// W4A16_DECODE_KS and W4A16_DECODE_DEPTH (groups loaded ahead: 2 or 4)
+// override the choice.
 static DecodeConfig decode_config(const Problem &p) {
   DecodeConfig c;
   c.MT = p.M <= 16 ? 16 : 32;
@@ -333,15 +354,19 @@ static DecodeConfig decode_config(const Problem &p) {
   const int64_t KG = p.K / kGroup;
   c.SPW = p.swiglu ? 2 : 1;
   c.nsg = (int)(p.swiglu ? (p.N / 2 / kStrip) : NS);
-  int waves = (c.nsg < 384 || KG >= 128) ? 8 : 4;
+  const char *hv = std::getenv("W4A16_DECODE_HALF");
+  const bool half_fits = 2 * (int64_t)c.nsg <= 256 && (KG <= 64 || p.M <= 4);
+  c.half = c.MT == 16 && (hv != nullptr && *hv != 0 ? *hv == '1' : half_fits);
+  const int64_t units = (int64_t)c.nsg * (c.half ? 2 : 1);
+  int waves = (units < 384 || KG >= 128) ? 8 : 4;
   waves = env_int("W4A16_DECODE_WAVES", waves) >= 8 ? 8 : 4;
   // LDS for the cross-wave reduction: WAVES * SPW * M * 32 floats < 64 KiB.
   while (waves > 4 && (int64_t)waves * c.SPW * p.M * 32 * 4 >= 65536) waves /= 2;
   c.WAVES = waves;
-  c.D = env_int("W4A16_DECODE_DEPTH", 2) >= 4 ? 4 : 2;
+  c.D = env_int("W4A16_DECODE_DEPTH", c.half && p.M > 8 ? 4 : 2) >= 4 ? 4 : 2;
   // A second launch (the reduction) costs more than idle CUs unless each
   // wave still streams a long K slice: split K only for narrow, deep shapes.
-  int64_t ks = (c.nsg < 256 && KG / c.WAVES >= 8) ? 2 : 1;
+  int64_t ks = (units < 256 && KG / c.WAVES >= 8) ? 2 : 1;
   ks = env_int("W4A16_DECODE_KS", (int)ks);
   if (ks > KG) ks = KG;
   if (ks > 64) ks = 64;
@@ -368,11 +393,12 @@ int decode_describe(const Problem &p, char *buf, size_t n) {
   const DecodeConfig c = decode_config(p);
   const int rpl = c.MT == 16 ? (p.M == 1 ? 1 : 4) : 16;
   const char *pre = (p.bf16 || p.G < kGroup || p.zp) ? "true" : "false";
-  const char *zp = p.zp ? "true" : "false";
+  const char *zp = p.zp ? "true" : "false", *hf = c.half ? "true" : "false";
   int k = snprintf(buf, n,
-                   "decode_kernel<%d, %d, %d, %d, %d, %s, %s, %s, %s> workgroups=%d threads=%d ks=%d",
-                   c.MT, c.SPW, c.WAVES, c.D, rpl, sw, bf, pre, zp, c.nsg * c.KS, c.WAVES * 64,
-                   c.KS);
+                   "decode_kernel<%d, %d, %d, %d, %d, %s, %s, %s, %s, %s> workgroups=%d threads=%d "
+                   "ks=%d",
+                   c.MT, c.SPW, c.WAVES, c.D, rpl, sw, bf, pre, zp, hf,
+                   c.nsg * c.KS * (c.half ? 2 : 1), c.WAVES * 64, c.KS);
   if (c.KS > 1 && k > 0 && (size_t)k < n)
     k += snprintf(buf + k, n - k, "; decode_reduce_kernel<%d, %s, %s>", c.SPW, sw, bf);
   return k;
@@ -390,24 +416,33 @@ int64_t decode_workspace_bytes(const Problem &p) {
   return (int64_t)c.nsg * c.KS * c.SPW * p.M * 32 * (int64_t)sizeof(float);
 }
 
-template <int MT, int SPW, int WAVES, int D, int RPL, bool SWIGLU, bool BF, bool PRE, bool ZP>
+template <int MT, int SPW, int WAVES, int D, int RPL, bool SWIGLU, bool BF, bool PRE, bool ZP,
+          bool HALF>
 static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t s) {
   const size_t lds = (size_t)WAVES * SPW * a.M * 32 * sizeof(float);
-  hipLaunchKernelGGL((decode_kernel<MT, SPW, WAVES, D, RPL, SWIGLU, BF, PRE, ZP>),
-                     dim3(a.nsg * a.KS),
+  hipLaunchKernelGGL((decode_kernel<MT, SPW, WAVES, D, RPL, SWIGLU, BF, PRE, ZP, HALF>),
+                     dim3(a.nsg * a.KS * (HALF ? 2 : 1)),
                      dim3(WAVES * 64), lds, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.KS == 1) return e;
   return launch_decode_reduce(a, SWIGLU, BF, s);
 }
 
+template <int MT, int SPW, int RPL, bool SWIGLU, bool BF, bool PRE, bool ZP, bool HALF>
+static hipError_t launch_decode_h(const DecodeArgs &a, const DecodeConfig &c, hipStream_t s) {
+  if (c.D == 4)
+    return c.WAVES == 8 ? launch_decode_t<MT, SPW, 8, 4, RPL, SWIGLU, BF, PRE, ZP, HALF>(a, s)
+                        : launch_decode_t<MT, SPW, 4, 4, RPL, SWIGLU, BF, PRE, ZP, HALF>(a, s);
+  return c.WAVES == 8 ? launch_decode_t<MT, SPW, 8, 2, RPL, SWIGLU, BF, PRE, ZP, HALF>(a, s)
+                      : launch_decode_t<MT, SPW, 4, 2, RPL, SWIGLU, BF, PRE, ZP, HALF>(a, s);
+}
+
 template <int MT, int SPW, int RPL, bool SWIGLU, bool BF, bool PRE, bool ZP>
 static hipError_t launch_decode_w(const DecodeArgs &a, const DecodeConfig &c, hipStream_t s) {
-  if (c.D == 4)
-    return c.WAVES == 8 ? launch_decode_t<MT, SPW, 8, 4, RPL, SWIGLU, BF, PRE, ZP>(a, s)
-                        : launch_decode_t<MT, SPW, 4, 4, RPL, SWIGLU, BF, PRE, ZP>(a, s);
-  return c.WAVES == 8 ? launch_decode_t<MT, SPW, 8, 2, RPL, SWIGLU, BF, PRE, ZP>(a, s)
-                      : launch_decode_t<MT, SPW, 4, 2, RPL, SWIGLU, BF, PRE, ZP>(a, s);
+  if constexpr (MT == 16) {
+    if (c.half) return launch_decode_h<MT, SPW, RPL, SWIGLU, BF, PRE, ZP, true>(a, c, s);
+  }
+  return launch_decode_h<MT, SPW, RPL, SWIGLU, BF, PRE, ZP, false>(a, c, s);
 }
 
 template <bool BF, bool PRE, bool ZP>

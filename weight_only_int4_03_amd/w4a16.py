@@ -90,6 +90,10 @@ def lib() -> ctypes.CDLL:
     if _lib is None:
         if not os.path.exists(LIBRARY):
             raise RuntimeError("libw4a16.so is not built: run python -m weight_only_int4_03_amd.build")
+        # torch ships its own HIP runtime; loading it first makes the library
+        # bind to that same runtime (a second runtime in the process would not
+        # see torch's device memory, streams or device).
+        _torch()
         L = ctypes.CDLL(LIBRARY)
         for name, (args, res) in _SIGNATURES.items():
             fn = getattr(L, name)
