@@ -170,8 +170,10 @@ def test_describe_names_the_launches():
         4096, 4096, 28672, swiglu=True)
     assert "prefill2_kernel<4, 2, 4, 2, false, true, true, false>" in w4a16.describe(
         4096, 4096, 28672, swiglu=True, bf16=True)
+    # Transition batches: 64-row tiles, the eight waves side by side.
     assert w4a16.describe(256, 4096, 28672, swiglu=True).startswith(
-        "prefill2_kernel<2, 2, 4, 2, false, true, false, false> workgroups=224 threads=512 ks=1")
+        "prefill2_kernel<2, 1, 8, 2, false, true, false, false> workgroups=224 threads=512 ks=1")
+    assert w4a16.describe(300, 4096, 28672, swiglu=True).startswith("prefill2_kernel<4, 2, 4, 2")
     # Zero rows: decode scales before the MFMA (never the cooperative kernel),
     # prefill takes the ZP instance, the dense tier folds them into its dequant.
     d = w4a16.describe(1, 4096, 28672, swiglu=True, zp=True)

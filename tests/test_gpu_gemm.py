@@ -224,20 +224,60 @@ PREFILL2_CONFIGS = [(64, 1, 1), (128, 1, 4), (256, 1, 2), (64, 2, 2), (128, 2, 4
                     (64, 1, 8), (256, 2, 4)]
 
 
+@pytest.mark.parametrize("wm", [2, 1])
 @pytest.mark.parametrize("bm,tps,ks", PREFILL2_CONFIGS)
 @pytest.mark.parametrize("M,K,N,swiglu", [(70, 2048, 1088, False), (200, 2048, 2112, True),
                                           (129, 4096, 4160, False)])
-def test_prefill2_tiles_and_k_slices(monkeypatch, bm, tps, ks, M, K, N, swiglu):
-    """The 8-wave mainloop at each row tile (64/128/256), one or two 64-k tiles
-    per pipeline step, and split K with the FP32 partial reduction; ragged M
-    and N, odd step counts per slice where the split allows."""
+def test_prefill2_tiles_and_k_slices(monkeypatch, wm, bm, tps, ks, M, K, N, swiglu):
+    """The 8-wave mainloop at each row tile (64/128/256), with the waves as
+    2 x 4 (two waves share each weight fragment) or, for 64 and 128 rows,
+    1 x 8 (each wave's fragments feed all the tile's rows); one or two 64-k
+    tiles per pipeline step, and split K with the FP32 partial reduction;
+    ragged M and N, odd step counts per slice where the split allows."""
+    if wm == 1 and bm == 256:
+        pytest.skip("the 256-row tile keeps two waves along the rows")
     monkeypatch.setenv("W4A16_PREFILL_BM", str(bm))
     monkeypatch.setenv("W4A16_PREFILL_TPS", str(tps))
     monkeypatch.setenv("W4A16_PREFILL_KS", str(ks))
+    monkeypatch.setenv("W4A16_PREFILL_WM", str(wm))
     d = w4a16.describe(M, K, N, swiglu=swiglu, path="prefill")
-    assert "prefill2_kernel<%d, 2, 4, %d" % (bm // 64, tps) in d, d
+    assert "prefill2_kernel<%d, %d, %d, %d" % (bm // (32 * wm), wm, 8 // wm, tps) in d, d
     assert ("ks=%d" % ks) in d, d
     gemm_case(M, K, N, swiglu=swiglu, path="prefill", seed=M + N + bm + ks)
+
+
+def test_prefill2_one_wave_rows_bit_exact_integer_inputs(monkeypatch):
+    """The 1 x 8 wave layout with split K on exact sums: every row block of
+    every wave lands in place."""
+    monkeypatch.setenv("W4A16_PREFILL_WM", "1")
+    for bm, ks in ((64, 4), (128, 2), (128, 1)):
+        monkeypatch.setenv("W4A16_PREFILL_BM", str(bm))
+        monkeypatch.setenv("W4A16_PREFILL_KS", str(ks))
+        for M, K, N in [(96, 2048, 2048), (150, 1024, 1088)]:
+            W = synth.grid_weights(K, N, p=4, seed=M)
+            A = synth.ternary_activations(M, K, density=1.0, seed=M)
+            w = w4a16.load_weight(W)
+            out = fp16_out(w4a16.gemm(to_dev(A), w, path="prefill"))
+            packed_o, s16_o = orc().quantize_pack(W)
+            assert np.array_equal(out.astype(np.float64), orc().gemm_f64(A, packed_o, s16_o))
+
+
+@pytest.mark.parametrize("wm", [2, 1])
+@pytest.mark.parametrize("ks", [2, 3, 4, 7])
+def test_prefill2_uneven_k_slices_bit_exact(monkeypatch, wm, ks):
+    """K slices that differ by one pipeline step (K = 1152: 9 steps of 128 k;
+    K = 11008: 86 steps): exact sums, bit-exact output."""
+    monkeypatch.setenv("W4A16_PREFILL_BM", "64")
+    monkeypatch.setenv("W4A16_PREFILL_WM", str(wm))
+    monkeypatch.setenv("W4A16_PREFILL_KS", str(ks))
+    for M, K, N in [(70, 1152, 1088), (40, 11008, 1024)]:
+        assert ("ks=%d" % ks) in w4a16.describe(M, K, N, path="prefill")
+        W = synth.grid_weights(K, N, p=4, seed=M + ks)
+        A = synth.ternary_activations(M, K, density=0.3 if K > 4096 else 1.0, seed=M)
+        w = w4a16.load_weight(W)
+        out = fp16_out(w4a16.gemm(to_dev(A), w, path="prefill"))
+        packed_o, s16_o = orc().quantize_pack(W)
+        assert np.array_equal(out.astype(np.float64), orc().gemm_f64(A, packed_o, s16_o)), (M, K)
 
 
 def test_prefill2_split_k_bit_exact_integer_inputs(monkeypatch):

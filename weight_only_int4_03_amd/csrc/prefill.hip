@@ -48,10 +48,11 @@ struct PrefillArgs {
   int ldo;
   int tiles_m, tiles_n;
   int up_off, valid_strips;
-  // prefill2_kernel split-K: KS slices of spk pipeline steps each; with
-  // KS > 1 every slice writes FP32 partials ws[KS][M][N] (gate and up columns
-  // alike) and prefill_reduce_kernel finishes the output.
-  int KS, spk;
+  // prefill2_kernel split-K: the nsteps pipeline steps are cut into KS
+  // slices (slice j: steps [j nsteps / KS, (j+1) nsteps / KS)); with KS > 1
+  // every slice writes FP32 partials ws[KS][M][N] (gate and up columns alike)
+  // and prefill_reduce_kernel finishes the output.
+  int KS, nsteps;
   float *ws;
   const float *rowscale;  // per-row output factor, or null
   int gshift;             // group of k = k >> gshift
@@ -422,7 +423,8 @@ void prefill2_kernel(PrefillArgs p) {
   // Every step loads the next step's operands unconditionally (the last step
   // reloads its own k range into the idle buffers), so the loop has no
   // conditional loads; the barrier that ends a step waits for those loads.
-  const int q0 = ks * p.spk, q1 = q0 + p.spk;
+  const int q0 = (int)((int64_t)ks * p.nsteps / p.KS);
+  const int q1 = (int)((int64_t)(ks + 1) * p.nsteps / p.KS);
   BRegs b0, b1;
   load_a(q0, lds0);
   load_b(q0, b0);
@@ -557,7 +559,7 @@ static PrefillArgs prefill_args(const Problem &p, int BM, const void *weights) {
   // Each workgroup covers 8 strips (plain) or 4 gate strips + their up strips.
   a.tiles_n = (int)(p.swiglu ? ceil_div(a.up_off, 4) : ceil_div(a.NS, 8));
   a.KS = 1;
-  a.spk = a.KT;
+  a.nsteps = a.KT;
   a.ws = nullptr;
   a.rowscale = p.rowscale;
   a.rz = (const uint16_t *)p.rz;
@@ -623,15 +625,17 @@ static int device_cus() {
 // 64-k tiles per pipeline step, and K slices.
 struct Prefill2Config {
   int bm, tps, ks, tiles;
+  int wm;  // waves along the rows: 2 (4 along the columns) or 1 (8 along the columns)
+  int mi() const { return bm / (32 * wm); }   // 32-row MFMA blocks per wave
+  int wnw() const { return 8 / wm; }          // waves along the columns
 };
 
 // K slices for a grid of `tiles` workgroups: halve each workgroup's k range
 // while the doubled grid still fits one workgroup per CU (at most 16 slices,
-// at least 4 pipeline steps each).
+// at least 4 pipeline steps each; slices may differ by one step).
 static int k_slices(int64_t tiles, int nsteps, int cus) {
   int ks = 1;
-  while (tiles * ks * 2 <= cus && ks < 16 && nsteps % (2 * ks) == 0 && nsteps / (2 * ks) >= 4)
-    ks *= 2;
+  while (tiles * ks * 2 <= cus && ks < 16 && nsteps / (2 * ks) >= 4) ks *= 2;
   return ks;
 }
 
@@ -647,8 +651,12 @@ static int k_slices(int64_t tiles, int nsteps, int cus) {
 // ceil(workgroups / CUs) rounds, and a split K adds the round trip of the
 // FP32 partials through memory (2 ks M N 4 bytes at 5 TB/s) plus ~3 us.  Two
 // 64-k tiles (one scale group) per pipeline step: half the barriers of one
-// 64-k tile, measured 0-5% faster.  W4A16_PREFILL_BM,
-// W4A16_PREFILL_TPS and W4A16_PREFILL_KS override.
+// 64-k tile, measured 0-5% faster.  Up to M = 256 the tile is 64 rows with
+// the waves as 1 x 8 instead of 2 x 4 (W4A16_PREFILL_WM): two waves then no
+// longer dequantize the same weight fragment, which halves the
+// dequantization work per MFMA; its 512-column tiles need more K slices to
+// fill the GPU.  W4A16_PREFILL_BM, W4A16_PREFILL_TPS and W4A16_PREFILL_KS
+// override.
 static bool prefill2_config(const Problem &p, bool dense, Prefill2Config &c) {
   const char *v = std::getenv("W4A16_PREFILL_V2");
   const bool on = v != nullptr ? *v == '1' : !dense;
@@ -660,6 +668,13 @@ static bool prefill2_config(const Problem &p, bool dense, Prefill2Config &c) {
     c.bm = 256;  // the dense tier always runs the 256-row tile, unsplit
   } else if (bm_env == 64 || bm_env == 128 || bm_env == 256) {
     c.bm = bm_env;
+  } else if (p.M <= 256 && (p.K <= 8192 || p.M > 128)) {
+    // Transition batches: 64-row tiles with the eight waves side by side
+    // (each wave's dequantized fragments feed all 64 rows), measured 3-16%
+    // faster on the K = 4096 projections and at M = 256; the deep, narrow
+    // down projection at M <= 128 keeps the 2 x 4 layout, whose smaller tiles
+    // need fewer K slices.
+    c.bm = 64;
   } else {
     static const double eff[3] = {0.6, 0.85, 1.0};
     const int64_t tn = p.swiglu ? ceil_div(NS / 2, 4) : ceil_div(NS, 8);
@@ -679,24 +694,27 @@ static bool prefill2_config(const Problem &p, bool dense, Prefill2Config &c) {
     }
   }
   c.tps = dense ? 1 : env_int("W4A16_PREFILL_TPS", 2) == 2 ? 2 : 1;
-  const int64_t tiles_n = p.swiglu ? ceil_div(NS / 2, 4) : ceil_div(NS, 8);
+  c.wm = !dense && bm_env == 0 && p.M <= 256 && (p.K <= 8192 || p.M > 128) ? 1 : 2;
+  const int wm_env = env_int("W4A16_PREFILL_WM", 0);
+  if (!dense && c.bm <= 128 && (wm_env == 1 || wm_env == 2)) c.wm = wm_env;
+  const int64_t tiles_n = p.swiglu ? ceil_div(NS / 2, c.wnw()) : ceil_div(NS, 2 * c.wnw());
   c.tiles = (int)(ceil_div(p.M, c.bm) * tiles_n);
   const int nsteps = (int)(p.K / kTileK / c.tps);
   int ks = dense ? 1 : k_slices(c.tiles, nsteps, cus);
   const int ks_env = env_int("W4A16_PREFILL_KS", 0);
-  if (!dense && ks_env > 0 && nsteps % ks_env == 0) ks = ks_env;
+  if (!dense && ks_env > 0 && ks_env <= nsteps) ks = ks_env;
   c.ks = ks;
   return true;
 }
 
-template <int MI, int TPS, bool DENSE, bool SWIGLU, bool BF, bool ZP>
+template <int MI, int WM, int TPS, bool DENSE, bool SWIGLU, bool BF, bool ZP>
 static hipError_t launch_prefill2_t(const Problem &p, const void *weights, const Prefill2Config &c,
                                     void *workspace, hipStream_t s) {
-  constexpr int WM = 2, WNW = 4;
+  constexpr int WNW = 8 / WM;
   PrefillArgs a = prefill_args(p, 32 * MI * WM, weights);
   a.tiles_n = (int)(p.swiglu ? ceil_div(a.up_off, WNW) : ceil_div(a.NS, 2 * WNW));
   a.KS = c.ks;
-  a.spk = a.KT / TPS / c.ks;
+  a.nsteps = a.KT / TPS;
   a.ws = (float *)workspace;
   hipLaunchKernelGGL((prefill2_kernel<MI, WM, WNW, TPS, DENSE, SWIGLU, BF, ZP>),
                      dim3(a.tiles_m * a.tiles_n * c.ks), dim3(64 * WM * WNW), 0, s, a);
@@ -709,32 +727,32 @@ static hipError_t launch_prefill2_t(const Problem &p, const void *weights, const
   return hipGetLastError();
 }
 
-template <int MI, int TPS, bool DENSE, bool ZP>
+template <int MI, int WM, int TPS, bool DENSE, bool ZP>
 static hipError_t launch_prefill2_z(const Problem &p, const void *weights,
                                     const Prefill2Config &c, void *ws, hipStream_t s) {
   if (p.bf16)
-    return p.swiglu ? launch_prefill2_t<MI, TPS, DENSE, true, true, ZP>(p, weights, c, ws, s)
-                    : launch_prefill2_t<MI, TPS, DENSE, false, true, ZP>(p, weights, c, ws, s);
-  return p.swiglu ? launch_prefill2_t<MI, TPS, DENSE, true, false, ZP>(p, weights, c, ws, s)
-                  : launch_prefill2_t<MI, TPS, DENSE, false, false, ZP>(p, weights, c, ws, s);
+    return p.swiglu ? launch_prefill2_t<MI, WM, TPS, DENSE, true, true, ZP>(p, weights, c, ws, s)
+                    : launch_prefill2_t<MI, WM, TPS, DENSE, false, true, ZP>(p, weights, c, ws, s);
+  return p.swiglu ? launch_prefill2_t<MI, WM, TPS, DENSE, true, false, ZP>(p, weights, c, ws, s)
+                  : launch_prefill2_t<MI, WM, TPS, DENSE, false, false, ZP>(p, weights, c, ws, s);
 }
 
-template <int MI, int TPS, bool DENSE>
+template <int MI, int WM, int TPS, bool DENSE>
 static hipError_t launch_prefill2_tps(const Problem &p, const void *weights,
                                       const Prefill2Config &c, void *ws, hipStream_t s) {
   if constexpr (!DENSE) {
-    if (p.zp) return launch_prefill2_z<MI, TPS, DENSE, true>(p, weights, c, ws, s);
+    if (p.zp) return launch_prefill2_z<MI, WM, TPS, DENSE, true>(p, weights, c, ws, s);
   }
-  return launch_prefill2_z<MI, TPS, DENSE, false>(p, weights, c, ws, s);
+  return launch_prefill2_z<MI, WM, TPS, DENSE, false>(p, weights, c, ws, s);
 }
 
-template <int MI, bool DENSE>
+template <int MI, int WM, bool DENSE>
 static hipError_t launch_prefill2_m(const Problem &p, const void *weights, const Prefill2Config &c,
                                     void *ws, hipStream_t s) {
   if constexpr (!DENSE) {
-    if (c.tps == 2) return launch_prefill2_tps<MI, 2, DENSE>(p, weights, c, ws, s);
+    if (c.tps == 2) return launch_prefill2_tps<MI, WM, 2, DENSE>(p, weights, c, ws, s);
   }
-  return launch_prefill2_tps<MI, 1, DENSE>(p, weights, c, ws, s);
+  return launch_prefill2_tps<MI, WM, 1, DENSE>(p, weights, c, ws, s);
 }
 
 int64_t prefill_workspace_bytes(const Problem &p) {
@@ -747,9 +765,12 @@ hipError_t launch_prefill(const Problem &p, void *workspace, hipStream_t s) {
   Prefill2Config c;
   if (!prefill2_config(p, false, c)) return launch_tiled<false>(p, p.rw, s);
   if (c.ks > 1 && workspace == nullptr) return hipErrorInvalidValue;
-  if (c.bm == 64) return launch_prefill2_m<1, false>(p, p.rw, c, workspace, s);
-  if (c.bm == 128) return launch_prefill2_m<2, false>(p, p.rw, c, workspace, s);
-  return launch_prefill2_m<4, false>(p, p.rw, c, workspace, s);
+  if (c.wm == 1)
+    return c.bm == 64 ? launch_prefill2_m<2, 1, false>(p, p.rw, c, workspace, s)
+                      : launch_prefill2_m<4, 1, false>(p, p.rw, c, workspace, s);
+  if (c.bm == 64) return launch_prefill2_m<1, 2, false>(p, p.rw, c, workspace, s);
+  if (c.bm == 128) return launch_prefill2_m<2, 2, false>(p, p.rw, c, workspace, s);
+  return launch_prefill2_m<4, 2, false>(p, p.rw, c, workspace, s);
 }
 
 int tiled_describe(const Problem &p, bool dense, char *buf, size_t n) {
@@ -760,9 +781,9 @@ int tiled_describe(const Problem &p, bool dense, char *buf, size_t n) {
   Prefill2Config c;
   if (prefill2_config(p, dense, c)) {
     int k = snprintf(buf, n,
-                     "%sprefill2_kernel<%d, 2, 4, %d, %s, %s, %s, %s> workgroups=%d threads=512 "
+                     "%sprefill2_kernel<%d, %d, %d, %d, %s, %s, %s, %s> workgroups=%d threads=512 "
                      "ks=%d",
-                     pre, c.bm / 64, c.tps, d, sw, bf, zp, c.tiles * c.ks, c.ks);
+                     pre, c.mi(), c.wm, c.wnw(), c.tps, d, sw, bf, zp, c.tiles * c.ks, c.ks);
     if (c.ks > 1 && k > 0 && (size_t)k < n)
       k += snprintf(buf + k, n - k, "; prefill_reduce_kernel<%s, %s>", sw, bf);
     return k;
@@ -785,7 +806,7 @@ hipError_t launch_dense(const Problem &p, void *workspace, hipStream_t s) {
       launch_dequant_fragment(p.rw, p.rs, p.rz, p.K, p.N, p.G, p.bf16, (uint16_t *)w16f, s);
   if (e != hipSuccess) return e;
   Prefill2Config c;
-  if (prefill2_config(p, true, c)) return launch_prefill2_m<4, true>(p, w16f, c, nullptr, s);
+  if (prefill2_config(p, true, c)) return launch_prefill2_m<4, 2, true>(p, w16f, c, nullptr, s);
   return launch_tiled<true>(p, w16f, s);
 }
 
