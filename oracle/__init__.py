@@ -10,7 +10,9 @@ contract", except ``swiglu_f64``, which follows the SwiGLU line of the block
 equations in FuTransformer (arXiv 2610.23796), section 2.1, the RMSNorm
 folding helpers (FuTransformer, section 3.2.2), and the zero-point functions
 (``zero_rows``, ``dequant_zp``), which follow the Swordfish page
-(blog.alpindale.net), section "The packed format".
+(blog.alpindale.net), section "The packed format", and the INT8 functions
+(``quantize8`` ... ``gemm8_f64``), which follow the same section and "Making a
+Single GPU Go Fast" (arunshar.com), section 9.3.2.
 """
 from __future__ import annotations
 
@@ -64,6 +66,12 @@ class Oracle:
         lib.oracle_zero_rows.argtypes = [_p, _p, _i64, _i64, _p]
         lib.oracle_dequant_zp.argtypes = [_p, _p, _p, _i64, _i64, ctypes.c_int, ctypes.c_int, _p]
         lib.oracle_gemm_wb_f64.argtypes = [_p, _i64, _i64, _p, _i64, _p, ctypes.c_int]
+        lib.oracle_quantize8.argtypes = [_p, _i64, _i64, ctypes.c_int, _p, _p]
+        lib.oracle_pack8.argtypes = [_p, _i64, _i64, _p]
+        lib.oracle_unpack8.argtypes = [_p, _i64, _i64, _p]
+        lib.oracle_dequant8.argtypes = [_p, _p, _i64, _i64, ctypes.c_int, ctypes.c_int, _p]
+        lib.oracle_gemm8_f64.argtypes = [_p, _i64, _i64, _p, _p, _i64, ctypes.c_int, ctypes.c_int,
+                                         _p, ctypes.c_int]
         lib.oracle_gemm_bf16_f64.argtypes = [_p, _i64, _i64, _p, _p, _i64, ctypes.c_int, _p,
                                              ctypes.c_int]
         lib.oracle_quantize.argtypes = [_p, _i64, _i64, ctypes.c_int, _p, _p]
@@ -161,6 +169,72 @@ class Oracle:
         if rc != OK:
             raise ValueError("oracle_dequant_bf16 failed with status %d" % rc)
         return Wb
+
+    # -- INT8 weights (Swordfish, "The packed format"; "Making a Single GPU
+    #    Go Fast", section 9.3.2) ------------------------------------------
+    def quantize8(self, W: np.ndarray, G: int = 128):
+        """(u uint8 [K,N] = q + 128, s16 bits [K/G,N]) with s = max|W|/127."""
+        W = np.ascontiguousarray(W, dtype=np.float32)
+        K, N = W.shape
+        u = np.empty((K, N), np.uint8)
+        s16 = np.empty((K // G, N), np.uint16)
+        rc = self.lib.oracle_quantize8(W.ctypes.data, K, N, G, u.ctypes.data, s16.ctypes.data)
+        if rc != OK:
+            raise ValueError("oracle_quantize8 failed with status %d" % rc)
+        return u, s16
+
+    def pack8(self, u: np.ndarray) -> np.ndarray:
+        """int32 [K/4,N]: byte k at bits 8(k mod 4)."""
+        u = np.ascontiguousarray(u, dtype=np.uint8)
+        K, N = u.shape
+        packed = np.empty((K // 4, N), np.int32)
+        rc = self.lib.oracle_pack8(u.ctypes.data, K, N, packed.ctypes.data)
+        if rc != OK:
+            raise ValueError("oracle_pack8 failed with status %d" % rc)
+        return packed
+
+    def unpack8(self, packed: np.ndarray) -> np.ndarray:
+        packed = np.ascontiguousarray(packed, dtype=np.int32)
+        R, N = packed.shape
+        u = np.empty((4 * R, N), np.uint8)
+        rc = self.lib.oracle_unpack8(packed.ctypes.data, 4 * R, N, u.ctypes.data)
+        if rc != OK:
+            raise ValueError("oracle_unpack8 failed with status %d" % rc)
+        return u
+
+    def quantize_pack8(self, W: np.ndarray, G: int = 128):
+        u, s16 = self.quantize8(W, G)
+        return self.pack8(u), s16
+
+    def dequant8(self, packed: np.ndarray, s16: np.ndarray, G: int = 128,
+                 bf16: bool = False) -> np.ndarray:
+        """fp16 (or bf16) bits [K,N] of (u - 128) * s16, rounded once."""
+        packed = np.ascontiguousarray(packed, dtype=np.int32)
+        s16 = np.ascontiguousarray(s16, dtype=np.uint16)
+        R, N = packed.shape
+        W = np.empty((4 * R, N), np.uint16)
+        rc = self.lib.oracle_dequant8(packed.ctypes.data, s16.ctypes.data, 4 * R, N, G,
+                                      int(bf16), W.ctypes.data)
+        if rc != OK:
+            raise ValueError("oracle_dequant8 failed with status %d" % rc)
+        return W
+
+    def gemm8_f64(self, A: np.ndarray, packed: np.ndarray, s16: np.ndarray, G: int = 128,
+                  bf16: bool = False, nthreads: int = 0) -> np.ndarray:
+        """C = A * W for INT8 weights in fp64 (A fp16, or bf16 bits with bf16)."""
+        A = np.ascontiguousarray(np.asarray(A).view(np.uint16))
+        packed = np.ascontiguousarray(packed, dtype=np.int32)
+        s16 = np.ascontiguousarray(s16, dtype=np.uint16)
+        M, K = A.shape
+        R, N = packed.shape
+        if 4 * R != K:
+            raise ValueError("A has K=%d but packed has %d rows" % (K, R))
+        C = np.empty((M, N), np.float64)
+        rc = self.lib.oracle_gemm8_f64(A.ctypes.data, M, K, packed.ctypes.data, s16.ctypes.data,
+                                       N, G, int(bf16), C.ctypes.data, nthreads)
+        if rc != OK:
+            raise ValueError("oracle_gemm8_f64 failed with status %d" % rc)
+        return C
 
     # -- zero points (Swordfish page, section "The packed format") ---------
     def zero_rows(self, s16: np.ndarray, zp: np.ndarray) -> np.ndarray:

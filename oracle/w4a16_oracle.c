@@ -30,6 +30,10 @@
  *     the fp32 weights before quantizing, one fp32 rounding per product; the
  *     row factor rho_m = (q_m / H + eps)^(-1/2) uses H = K, the length of the
  *     activation row the GEMM reads;
+ *   - INT8 weights (Swordfish page, section "The packed format";
+ *     "Making a Single GPU Go Fast", section 9.3.2): the int4 contract with
+ *     8-bit codes, s = max|W| / 127, codes stored offset by 128, four per
+ *     int32 along K;
  *   - zero points (Swordfish page, blog.alpindale.net, section "The packed
  *     format"): the prescaled row (8 - zp) * s is stored in the scales' type,
  *     fp16, rounded once; the weight (q - 8) * s + z is rounded once to the
@@ -301,6 +305,107 @@ int oracle_dequant_zp(const int32_t *packed, const uint16_t *s16, const uint16_t
     return ORACLE_OK;
 }
 
+/* ------------------------------------------------------------------------
+ * INT8 weights (W8A16).  The Swordfish page (blog.alpindale.net, section "The
+ * packed format") runs an int8 variant of unsigned 8-bit codes with a bias of
+ * 128 through the same dequantization idiom; "Making a Single GPU Go Fast"
+ * (arunshar.com, chapter 9, section 9.3.2) recommends weight-only INT8 with
+ * per-output-channel scales and gives the signed range [-128, 127].  Reading:
+ * the int4 data contract with 8-bit codes.  Per group g of G rows along K
+ * and column n:
+ *   s   = max_k |W[k,n]| / 127      (fp32 division)
+ *   s   = max(s, 1e-8)              (fp32 comparison against fl32(1e-8))
+ *   q   = clamp(round(W/s), -128, 127)   (fp32 division, ties to even)
+ *   u   = q + 128                   (stored byte, 0..255)
+ *   s16 = fp16(s)
+ * and four bytes consecutive along K share one int32, byte k at bits
+ * 8(k mod 4) .. 8(k mod 4)+7 of word [k/4, n].  The weight is (u - 128) * s16.
+ * Per-output-channel scales are G = K.
+ * ---------------------------------------------------------------------- */
+int oracle_quantize8(const float *W, int64_t K, int64_t N, int G, uint8_t *u, uint16_t *s16)
+{
+    if (G <= 0 || K <= 0 || N <= 0 || K % G != 0 || K % 4 != 0)
+        return ORACLE_ERR_SHAPE;
+    for (int64_t i = 0; i < K * N; ++i)
+        if (!isfinite(W[i]))
+            return ORACLE_ERR_NONFINITE;
+    fesetround(FE_TONEAREST);
+    for (int64_t g = 0; g < K / G; ++g) {
+        for (int64_t n = 0; n < N; ++n) {
+            float amax = 0.0f;
+            for (int64_t k = g * G; k < (g + 1) * G; ++k) {
+                float a = fabsf(W[k * N + n]);
+                if (a > amax)
+                    amax = a;
+            }
+            float s = amax / 127.0f;
+            if (s < 1e-8f)
+                s = 1e-8f;
+            for (int64_t k = g * G; k < (g + 1) * G; ++k) {
+                float q = nearbyintf(W[k * N + n] / s); /* ties to even */
+                if (q < -128.0f)
+                    q = -128.0f;
+                if (q > 127.0f)
+                    q = 127.0f;
+                u[k * N + n] = (uint8_t)((int)q + 128);
+            }
+            s16[g * N + n] = oracle_f64_to_f16((double)s);
+        }
+    }
+    return ORACLE_OK;
+}
+
+int oracle_pack8(const uint8_t *u, int64_t K, int64_t N, int32_t *packed)
+{
+    if (K % 4 != 0)
+        return ORACLE_ERR_SHAPE;
+    for (int64_t r = 0; r < K / 4; ++r)
+        for (int64_t n = 0; n < N; ++n) {
+            uint32_t word = 0;
+            for (int i = 0; i < 4; ++i)
+                word |= (uint32_t)u[(4 * r + i) * N + n] << (8 * i);
+            packed[r * N + n] = (int32_t)word;
+        }
+    return ORACLE_OK;
+}
+
+/* Unpack: shift the unsigned word, then mask with 0xFF. */
+int oracle_unpack8(const int32_t *packed, int64_t K, int64_t N, uint8_t *u)
+{
+    if (K % 4 != 0)
+        return ORACLE_ERR_SHAPE;
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t n = 0; n < N; ++n) {
+            uint32_t word = (uint32_t)packed[(k / 4) * N + n];
+            u[k * N + n] = (uint8_t)((word >> (8 * (k % 4))) & 0xFFu);
+        }
+    return ORACLE_OK;
+}
+
+/* The exact weight (u - 128) * s16, a double (8-bit integer times fp16). */
+static double exact_weight8(const int32_t *packed, const uint16_t *s16, int64_t N, int G,
+                            int64_t k, int64_t n)
+{
+    uint32_t word = (uint32_t)packed[(k / 4) * N + n];
+    int uval = (int)((word >> (8 * (k % 4))) & 0xFFu);
+    return (double)(uval - 128) * oracle_f16_to_f64(s16[(k / G) * N + n]);
+}
+
+/* Dequantize: W[k,n] = round((u - 128) * s16), one rounding to fp16, or to
+ * bf16 when bf16 != 0. */
+int oracle_dequant8(const int32_t *packed, const uint16_t *s16, int64_t K, int64_t N, int G,
+                    int bf16, uint16_t *W)
+{
+    if (G <= 0 || K % G != 0 || K % 4 != 0)
+        return ORACLE_ERR_SHAPE;
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t n = 0; n < N; ++n) {
+            double w = exact_weight8(packed, s16, N, G, k, n);
+            W[k * N + n] = bf16 ? oracle_f64_to_bf16(w) : oracle_f64_to_f16(w);
+        }
+    return ORACLE_OK;
+}
+
 static void set_threads(int nthreads)
 {
 #ifdef _OPENMP
@@ -435,6 +540,41 @@ int oracle_gemm_bf16_f64(const uint16_t *Ab, int64_t M, int64_t K,
                 for (int64_t n = n0; n < n1; ++n) {
                     double w = oracle_bf16_to_f64(
                         oracle_f64_to_bf16(exact_weight(packed, s16, N, G, k, n)));
+                    acc[n - n0] += a * w;
+                }
+            }
+            for (int64_t n = n0; n < n1; ++n)
+                C[m * N + n] = acc[n - n0];
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* GEMM reference for INT8 weights: C[m,n] = sum_k A[m,k] * w[k,n] in fp64,
+ * increasing k.  fp16 activations use the exact weight (u - 128) * s16 (as
+ * the int4 reference does); bf16 activations (A as bf16 bits) use the weight
+ * rounded once to bf16. */
+int oracle_gemm8_f64(const uint16_t *A, int64_t M, int64_t K, const int32_t *packed,
+                     const uint16_t *s16, int64_t N, int G, int bf16, double *C, int nthreads)
+{
+    if (G <= 0 || K % G != 0 || K % 4 != 0)
+        return ORACLE_ERR_SHAPE;
+    set_threads(nthreads);
+    int64_t nchunks = (N + NCHUNK - 1) / NCHUNK;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t c = 0; c < nchunks; ++c) {
+            int64_t n0 = c * NCHUNK;
+            int64_t n1 = n0 + NCHUNK < N ? n0 + NCHUNK : N;
+            double acc[NCHUNK];
+            for (int64_t n = n0; n < n1; ++n)
+                acc[n - n0] = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double a = bf16 ? oracle_bf16_to_f64(A[m * K + k]) : oracle_f16_to_f64(A[m * K + k]);
+                for (int64_t n = n0; n < n1; ++n) {
+                    double w = exact_weight8(packed, s16, N, G, k, n);
+                    if (bf16)
+                        w = oracle_bf16_to_f64(oracle_f64_to_bf16(w));
                     acc[n - n0] += a * w;
                 }
             }

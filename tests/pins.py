@@ -392,6 +392,122 @@ def check_gemm_wb_reference(o):
     assert np.allclose(C, ref, rtol=1e-12, atol=1e-12)
 
 
+# -- INT8 weights (Swordfish, "The packed format"; "Making a Single GPU Go
+#    Fast", section 9.3.2) ----------------------------------------------------
+
+def check_pack8_worked_words(o):
+    """The hand-derived words of tests/golden/packed_bytes.json."""
+    for c in _golden("packed_bytes.json")["cases"]:
+        u = np.array(c["bytes"], np.uint8).reshape(4, 1)
+        w = o.pack8(u)
+        assert w.shape == (1, 1) and int(w[0, 0]) == c["int32"], c
+        assert np.array_equal(o.unpack8(w)[:, 0], u[:, 0]), c
+
+
+def check_pack8_roundtrip(o):
+    """unpack8(pack8(u)) == u, and the packed words are numpy's little-endian
+    view of the bytes taken four at a time along K."""
+    rng = np.random.default_rng(41)
+    u = rng.integers(0, 256, (64, 12)).astype(np.uint8)
+    w = o.pack8(u)
+    assert np.array_equal(o.unpack8(w), u)
+    le = np.ascontiguousarray(u.reshape(16, 4, 12).transpose(0, 2, 1)).view("<u4")[..., 0]
+    assert np.array_equal(w.view(np.uint32), le)
+
+
+def check_quantize8_grid_roundtrip(o):
+    """Grid weights j 2^-p with a +-127 2^-p entry per group quantize
+    losslessly: scale 2^-p, codes j + 128, dequantized weights equal W."""
+    for G in (128, 64):
+        W = synth.grid_weights8(512, 16, p=10, seed=G, group=G)
+        u, s16 = o.quantize8(W, G)
+        assert (s16 == np.float16(2.0 ** -10).view(np.uint16)).all()
+        assert np.array_equal(u.astype(np.int64) - 128, np.rint(W * 2.0 ** 10).astype(np.int64))
+        Wd = o.dequant8(o.pack8(u), s16, G).view(np.float16).astype(np.float64)
+        assert np.array_equal(Wd, W.astype(np.float64))
+
+
+def check_quantize8_group_max_and_zero_group(o):
+    """The group maximum maps to code 255 (or 1 for a negative maximum), the
+    scale is fp16(max / 127); an all-zero group has scale fp16(1e-8) = 0 and
+    codes 128."""
+    W = np.zeros((256, 3), np.float32)
+    W[5, 0], W[6, 0] = 0.3, -0.1
+    W[130, 1] = -2.5
+    u, s16 = o.quantize8(W)
+    assert u[5, 0] == 255 and u[130, 1] == 1
+    assert s16[0, 0] == np.float16(np.float32(0.3) / np.float32(127)).view(np.uint16)
+    assert (s16[:, 2] == 0).all() and (u[:, 2] == 128).all()
+
+
+def check_quantize8_ties_to_even(o):
+    """Exact ties (k + 1/2) s round to the even k."""
+    s = 2.0 ** -7
+    W = np.zeros((128, 1), np.float32)
+    W[0, 0] = 127 * s                                   # sets the scale to 2^-7
+    W[1:6, 0] = np.array([0.5, 1.5, 2.5, -0.5, -3.5]) * s
+    u, _ = o.quantize8(W)
+    assert list(u[1:6, 0].astype(int) - 128) == [0, 2, 2, 0, -4]
+
+
+def check_quantize8_error_bound(o):
+    """|W - (u - 128) s| <= s / 2 with the quantizer's fp32 scale s (random
+    Gaussian weights, no clamping at +-127 since |W| <= 127 s)."""
+    rng = np.random.default_rng(42)
+    W = (rng.standard_normal((256, 24)) * 0.02).astype(np.float32)
+    u, _ = o.quantize8(W)
+    amax = np.abs(W.reshape(2, 128, 24)).max(axis=1)
+    s = np.repeat((amax / np.float32(127)).astype(np.float32), 128, axis=0).astype(np.float64)
+    err = np.abs(W.astype(np.float64) - (u.astype(np.float64) - 128) * s)
+    assert (err <= s / 2 * (1 + 1e-6)).all()
+
+
+def check_dequant8_values(o):
+    """Code 0 gives -128 s, 128 gives +0, 255 gives 127 s; arbitrary scales
+    round once (numpy's correctly rounded cast of the exact product); bf16 as
+    torch rounds."""
+    packed, s16 = synth.random_bytes(256, 16, seed=43)
+    u = o.unpack8(packed).astype(np.float64)
+    s = np.repeat(s16.view(np.float16).astype(np.float64), 128, axis=0)
+    exact = (u - 128) * s
+    assert np.array_equal(o.dequant8(packed, s16), exact.astype(np.float16).view(np.uint16))
+    assert np.array_equal(o.dequant8(packed, s16, bf16=True), _torch_bf16_bits(exact))
+    p2 = np.full((128, 3), 128, np.uint8)
+    p2[1, 0], p2[2, 1] = 0, 255
+    s2 = np.array([[np.float16(2.0 ** -7).view(np.uint16)] * 3], np.uint16)
+    W = o.dequant8(o.pack8(p2), s2).view(np.float16).astype(np.float64)
+    assert W[1, 0] == -1.0 and W[2, 1] == 127 * 2.0 ** -7 and (W[:, 2] == 0).all()
+
+
+def check_gemm8_bruteforce_and_exact(o):
+    """Tiny shapes against numpy's float64 matmul of the exact weights (fp16
+    activations) and of the bf16-rounded weights (bf16 activations); one-hot
+    rows select weight rows exactly; grid weights with ternary activations
+    give numpy's exact product."""
+    rng = np.random.default_rng(44)
+    for M, K, N, G in ((1, 128, 8, 128), (3, 256, 16, 64)):
+        packed, s16 = synth.random_bytes(K, N, seed=M + K, group=G)
+        Wx = (o.unpack8(packed).astype(np.float64) - 128) * np.repeat(
+            s16.view(np.float16).astype(np.float64), G, axis=0)
+        A = rng.standard_normal((M, K)).astype(np.float16)
+        assert np.allclose(o.gemm8_f64(A, packed, s16, G), A.astype(np.float64) @ Wx,
+                           rtol=1e-12, atol=1e-12)
+        Ab = _torch_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+        Wb = o.bf16_to_f64(_torch_bf16_bits(Wx))
+        assert np.allclose(o.gemm8_f64(Ab, packed, s16, G, bf16=True), o.bf16_to_f64(Ab) @ Wb,
+                           rtol=1e-12, atol=1e-12)
+    packed, s16 = synth.random_bytes(256, 8, seed=45)
+    A, ks = synth.onehot_activations(4, 256, seed=45)
+    C = o.gemm8_f64(A, packed, s16)
+    u = o.unpack8(packed).astype(np.float64)
+    for m, k in enumerate(ks):
+        assert np.array_equal(C[m], (u[k] - 128) * s16[k // 128].view(np.float16).astype(np.float64))
+    W = synth.grid_weights8(512, 16, seed=46)
+    p8, s8 = o.quantize_pack8(W)
+    A = synth.ternary_activations(3, 512, density=0.5, seed=46)
+    assert np.array_equal(o.gemm8_f64(A, p8, s8), A.astype(np.float64) @ W.astype(np.float64))
+
+
 # -- GEMM ------------------------------------------------------------------------
 
 def _exact_weights(o, packed, s16, G=128):
@@ -555,4 +671,7 @@ FAST_CHECKS = [
     check_fold_gain, check_rms_rowscale, check_scale_rows, check_quantize_other_group_sizes,
     check_zero_rows, check_dequant_zp_worked_examples, check_dequant_zp_reduces_to_symmetric,
     check_dequant_zp_power_of_two_exact, check_dequant_zp_error_bound, check_gemm_wb_reference,
+    check_pack8_worked_words, check_pack8_roundtrip, check_quantize8_grid_roundtrip,
+    check_quantize8_group_max_and_zero_group, check_quantize8_ties_to_even,
+    check_quantize8_error_bound, check_dequant8_values, check_gemm8_bruteforce_and_exact,
 ]

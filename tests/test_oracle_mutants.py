@@ -24,8 +24,8 @@ MUTANTS = [
     ("offset_7_dequant", "return (double)(uval - 8) *", "return (double)(uval - 7) *"),
     ("reversed_nibble_order", "word |= ((uint32_t)(u[(8 * r + i) * N + n] & 0xF)) << (4 * i);",
      "word |= ((uint32_t)(u[(8 * r + (7 - i)) * N + n] & 0xF)) << (4 * i);"),
-    ("scale_from_wrong_column", "oracle_f16_to_f64(s16[(k / G) * N + n]);",
-     "oracle_f16_to_f64(s16[(k / G) * N + (N - 1 - n)]);"),
+    ("scale_from_wrong_column", "(uval - 8) * oracle_f16_to_f64(s16[(k / G) * N + n]);",
+     "(uval - 8) * oracle_f16_to_f64(s16[(k / G) * N + (N - 1 - n)]);"),
     ("gemm_dropped_term", "for (int64_t k = 0; k < K; ++k) {\n                double a = oracle_f16_to_f64(A16[m * K + k]);\n                for (int64_t n = n0; n < n1; ++n)\n                    acc[n - n0] += a * exact_weight",
      "for (int64_t k = 1; k < K; ++k) {\n                double a = oracle_f16_to_f64(A16[m * K + k]);\n                for (int64_t n = n0; n < n1; ++n)\n                    acc[n - n0] += a * exact_weight"),
     ("gemm_transposed_A", "double a = oracle_f16_to_f64(A16[m * K + k]);\n                for (int64_t n = n0; n < n1; ++n)\n                    acc[n - n0] += a * exact_weight",
@@ -36,7 +36,10 @@ MUTANTS = [
     ("swiglu_swapped", "double g = C[m * N + j];\n            double up = C[m * N + I + j];",
      "double up = C[m * N + j];\n            double g = C[m * N + I + j];"),
     ("silu_sign", "g / (1.0 + exp(-g)) * up", "g / (1.0 + exp(g)) * up"),
-    ("scale_clamp_dropped_zero_group", "if (s < 1e-8f)\n                s = 1e-8f;", "if (s < 1e-8f)\n                s = 1.0f;"),
+    ("scale_clamp_dropped_zero_group", "float s = amax / 7.0f;\n            if (s < 1e-8f)\n                s = 1e-8f;",
+     "float s = amax / 7.0f;\n            if (s < 1e-8f)\n                s = 1.0f;"),
+    ("int8_scale_clamp_dropped_zero_group", "float s = amax / 127.0f;\n            if (s < 1e-8f)\n                s = 1e-8f;",
+     "float s = amax / 127.0f;\n            if (s < 1e-8f)\n                s = 1.0f;"),
     ("bf16_ties_away", "double n = nearbyint(a / ldexp(1.0, e - 7));", "double n = round(a / ldexp(1.0, e - 7));"),
     ("bf16_decode_bias", "v = ldexp((double)(128 + f), e - 134);", "v = ldexp((double)(128 + f), e - 133);"),
     ("bf16_truncate", "double n = nearbyint(a / ldexp(1.0, e - 7));", "double n = floor(a / ldexp(1.0, e - 7));"),
@@ -66,8 +69,27 @@ MUTANTS = [
      "return exact_weight(packed, s16, N, G, k, n) + oracle_f16_to_f64(z16[(k / 128) * N + n]);"),
     ("zero_row_dropped", "return exact_weight(packed, s16, N, G, k, n) + oracle_f16_to_f64(z16[(k / G) * N + n]);",
      "return exact_weight(packed, s16, N, G, k, n);"),
-    ("zero_point_bf16_flag_ignored", "W[k * N + n] = bf16 ? oracle_f64_to_bf16(w) : oracle_f64_to_f16(w);",
-     "W[k * N + n] = oracle_f64_to_f16(w);"),
+    ("zero_point_bf16_flag_ignored", "double w = exact_weight_zp(packed, s16, z16, N, G, k, n);\n            W[k * N + n] = bf16 ? oracle_f64_to_bf16(w) : oracle_f64_to_f16(w);",
+     "double w = exact_weight_zp(packed, s16, z16, N, G, k, n);\n            W[k * N + n] = oracle_f64_to_f16(w);"),
+    ("int8_bf16_flag_ignored", "double w = exact_weight8(packed, s16, N, G, k, n);\n            W[k * N + n] = bf16 ? oracle_f64_to_bf16(w) : oracle_f64_to_f16(w);",
+     "double w = exact_weight8(packed, s16, N, G, k, n);\n            W[k * N + n] = oracle_f64_to_f16(w);"),
+    ("int8_divide_by_128", "float s = amax / 127.0f;", "float s = amax / 128.0f;"),
+    ("int8_offset_127", "u[k * N + n] = (uint8_t)((int)q + 128);", "u[k * N + n] = (uint8_t)((int)q + 127);"),
+    ("int8_clamp_upper_126", "if (q > 127.0f)\n                    q = 127.0f;", "if (q > 126.0f)\n                    q = 126.0f;"),
+    ("int8_round_half_away", "float q = nearbyintf(W[k * N + n] / s); /* ties to even */",
+     "float q = roundf(W[k * N + n] / s); /* ties to even */"),
+    ("int8_pack_reversed", "word |= (uint32_t)u[(4 * r + i) * N + n] << (8 * i);",
+     "word |= (uint32_t)u[(4 * r + (3 - i)) * N + n] << (8 * i);"),
+    ("int8_unpack_nibble_shift", "u[k * N + n] = (uint8_t)((word >> (8 * (k % 4))) & 0xFFu);",
+     "u[k * N + n] = (uint8_t)((word >> (4 * (k % 4))) & 0xFFu);"),
+    ("int8_dequant_bias_127", "return (double)(uval - 128) * oracle_f16_to_f64(s16[(k / G) * N + n]);",
+     "return (double)(uval - 127) * oracle_f16_to_f64(s16[(k / G) * N + n]);"),
+    ("int8_weight_scale_group_128", "return (double)(uval - 128) * oracle_f16_to_f64(s16[(k / G) * N + n]);",
+     "return (double)(uval - 128) * oracle_f16_to_f64(s16[(k / 128) * N + n]);"),
+    ("int8_gemm_bf16_unrounded", "if (bf16)\n                        w = oracle_bf16_to_f64(oracle_f64_to_bf16(w));",
+     "if (0)\n                        w = oracle_bf16_to_f64(oracle_f64_to_bf16(w));"),
+    ("int8_gemm_dropped_term", "for (int64_t k = 0; k < K; ++k) {\n                double a = bf16 ? oracle_bf16_to_f64",
+     "for (int64_t k = 1; k < K; ++k) {\n                double a = bf16 ? oracle_bf16_to_f64"),
     ("gemm_wb_fp16_weights", "acc[n - n0] += a * oracle_bf16_to_f64(Wb[k * N + n]);",
      "acc[n - n0] += a * oracle_f16_to_f64(Wb[k * N + n]);"),
 ]

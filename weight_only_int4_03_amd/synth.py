@@ -109,6 +109,30 @@ def grid_weights(K: int, N: int, p: int = 6, seed: int = 0, group: int = G) -> n
     return j * np.float32(2.0 ** -p)
 
 
+def grid_weights8(K: int, N: int, p: int = 10, seed: int = 0, group: int = G) -> np.ndarray:
+    """The 8-bit counterpart of ``grid_weights``: W = j * 2^-p with integer j in
+    [-127, 127] and one entry of every (group, column) set to +-127 * 2^-p, so
+    that each group's scale is exactly 2^-p and 8-bit quantization is lossless."""
+    rng = np.random.default_rng(seed)
+    j = rng.integers(-127, 128, size=(K, N)).astype(np.float32)
+    rows = np.arange(0, K, group)[:, None] + rng.integers(0, group, size=(K // group, N))
+    sign = np.where(rng.integers(0, 2, size=(K // group, N)) == 0, -127.0, 127.0).astype(np.float32)
+    j[rows, np.arange(N)[None, :]] = sign
+    return j * np.float32(2.0 ** -p)
+
+
+def random_bytes(K: int, N: int, seed: int = 0, group: int = G) -> tuple[np.ndarray, np.ndarray]:
+    """Arbitrary 8-bit codes (every value 0..255, including 0, which the
+    quantizer never emits) packed four per int32 along K (byte k at bits
+    8(k mod 4)), with positive fp16 scales in [2^-12, 2^-8), one per ``group``
+    rows."""
+    rng = np.random.default_rng(seed + 6)
+    packed = rng.integers(0, 2 ** 32, size=(K // 4, N), dtype=np.uint64).astype(np.uint32)
+    scales = (rng.random((K // group, N), dtype=np.float32) * np.float32(2.0 ** -8 - 2.0 ** -12)
+              + np.float32(2.0 ** -12)).astype(np.float16)
+    return packed.view(np.int32), scales.view(np.uint16)
+
+
 def onehot_activations(M: int, K: int, seed: int = 0) -> tuple[np.ndarray, np.ndarray]:
     """A[m, k(m)] = 1, zero elsewhere; returns (A fp16, k(m))."""
     rng = np.random.default_rng(seed + 2)
