@@ -62,11 +62,13 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def alg_bytes(M, K, N, swiglu, zp=False):
-    """Bytes a GEMM must move at least once: packed weights, scales (and zero
-    rows), activations, output."""
+def alg_bytes(M, K, N, swiglu, zp=False, int8=False):
+    """Bytes a GEMM must move at least once: packed weights (half a byte per
+    INT4 weight, one per INT8 weight), scales (and zero rows), activations,
+    output."""
     n_out = N // 2 if swiglu else N
-    return K * N // 2 + 2 * (K // G) * N * (2 if zp else 1) + 2 * M * K + 2 * M * n_out
+    wbytes = K * N if int8 else K * N // 2
+    return wbytes + 2 * (K // G) * N * (2 if zp else 1) + 2 * M * K + 2 * M * n_out
 
 
 def flops(M, K, N):
@@ -101,11 +103,11 @@ def workloads():
     return w
 
 
-def kernel_key(M, K, N, swiglu, bf16=False, zp=False):
+def kernel_key(M, K, N, swiglu, bf16=False, zp=False, int8=False):
     """The kernel instance a GEMM launches under the automatic path, as the
     profiler names it, marked when a second (split-K reduction) launch
     follows it."""
-    desc = w4a16.describe(M, K, N, swiglu, bf16=bf16, zp=zp)
+    desc = w4a16.describe(M, K, N, swiglu, bf16=bf16, zp=zp, int8=int8)
     first = desc.split(";")[0]
     name = first.split(" workgroups=")[0].strip()
     return name + (" + reduce" if ";" in desc else "")
@@ -142,7 +144,7 @@ def stored_traffic(workload, kernel):
         return None
 
 
-def cpu_baseline(units, host_w, target_s=12.0, bf16=False, host_zp=None):
+def cpu_baseline(units, host_w, target_s=12.0, bf16=False, host_zp=None, int8=False):
     """Time the oracle's fp64 GEMM (+ SwiGLU) on a column sample of every unit
     (host_w: the same seeded fp32 weights the GPU was given, keyed by (K, N))."""
     import oracle
@@ -165,7 +167,7 @@ def cpu_baseline(units, host_w, target_s=12.0, bf16=False, host_zp=None):
         ns = min(ns, ncols)
         W = host_w[(K, N)]
         Ws = np.concatenate([W[:, :ns], W[:, N // 2:N // 2 + ns]], axis=1) if sw else W[:, :ns]
-        packed, s16 = o.quantize_pack(np.ascontiguousarray(Ws))
+        packed, s16 = (o.quantize_pack8 if int8 else o.quantize_pack)(np.ascontiguousarray(Ws))
         A = (synth.activations_bf16 if bf16 else synth.activations)(M, K, seed=0, outliers=outl)
         if host_zp is not None:
             Z = host_zp[(K, N)]
@@ -175,12 +177,14 @@ def cpu_baseline(units, host_w, target_s=12.0, bf16=False, host_zp=None):
         if host_zp is not None:
             Wz = o.dequant_zp(packed, s16, z16, bf16=bf16)
             C = (o.gemm_wb_f64 if bf16 else o.gemm_w16_f64)(A, Wz)
+        elif int8:
+            C = o.gemm8_f64(A, packed, s16, bf16=bf16)
         else:
             C = (o.gemm_bf16_f64 if bf16 else o.gemm_f64)(A, packed, s16)
         if sw:
             o.swiglu_f64(C)
         elapsed += time.perf_counter() - t0
-        done_bytes += alg_bytes(M, K, Ws.shape[1], sw, host_zp is not None)
+        done_bytes += alg_bytes(M, K, Ws.shape[1], sw, host_zp is not None, int8)
         cols_desc.append(ns)
     return {
         "value": round(done_bytes / elapsed / 1e9, 4),
@@ -264,6 +268,8 @@ def main():
                     help="activation and output type (the weights are the same)")
     ap.add_argument("--zero-points", action="store_true",
                     help="asymmetric weights: seeded zero points as prescaled zero rows")
+    ap.add_argument("--int8", action="store_true",
+                    help="INT8 weights (W8A16) instead of INT4")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for hardware-counter calibration)")
     args = ap.parse_args()
@@ -296,11 +302,14 @@ def main():
     # repacked on the device, then cloned into rotation copies.
     shapes = sorted({(k, n) for _, _, k, n, *_ in units})
     zp = args.zero_points
+    int8 = args.int8
+    if zp and int8:
+        raise SystemExit("--zero-points and --int8 do not combine (INT8 weights have no zero points)")
     base, host_w, host_zp = {}, {}, ({} if zp else None)
     for (k, n) in shapes:
         log("weights K=%d N=%d" % (k, n))
         host_w[(k, n)] = synth.weights(k, n, seed=0)
-        base[(k, n)] = w4a16.load_weight(host_w[(k, n)])
+        base[(k, n)] = (w4a16.load_weight_int8 if int8 else w4a16.load_weight)(host_w[(k, n)])
         if zp:
             host_zp[(k, n)] = synth.zero_points(k // G, n, seed=0)
             _, scales = w4a16.unrepack(base[(k, n)])
@@ -335,7 +344,7 @@ def main():
     def run_unit(u, copy):
         label, m, k, n, sw, outl, _ = u
         w = copies[(k, n)][copy]
-        if zp:
+        if zp or int8:
             w4a16.gemm(acts[(m, k, outl)], w, swiglu=sw, out=outs[label])
         elif sw:
             if bf16:
@@ -404,7 +413,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = ev0.elapsed_time(ev1) / args.steps
-    step_bytes = sum(alg_bytes(m, k, n, sw, zp) for _, m, k, n, sw, *_ in units)
+    step_bytes = sum(alg_bytes(m, k, n, sw, zp, int8) for _, m, k, n, sw, *_ in units)
     step_flops = sum(flops(m, k, n) for _, m, k, n, *_ in units)
     log("step: %.2f us (wall %.2f us), %.1f MB, %.2f GFLOP"
         % (ms_step * 1e3, wall / args.steps * 1e6, step_bytes / 1e6, step_flops / 1e9))
@@ -426,10 +435,10 @@ def main():
             b.record(stream)
         torch.cuda.synchronize()
         us = a.elapsed_time(b) * 1e3 / (args.reps * ncopies)
-        by, fl = alg_bytes(m, k, n, sw, zp), flops(m, k, n)
+        by, fl = alg_bytes(m, k, n, sw, zp, int8), flops(m, k, n)
         detail.append({"gemm": label, "M": m, "K": k, "N": n, "swiglu": sw,
-                       "kernel": kernel_key(m, k, n, sw, bf16, zp),
-                       "launch": w4a16.describe(m, k, n, sw, bf16=bf16, zp=zp),
+                       "kernel": kernel_key(m, k, n, sw, bf16, zp, int8),
+                       "launch": w4a16.describe(m, k, n, sw, bf16=bf16, zp=zp, int8=int8),
                        "us": round(us, 3),
                        "GB/s": round(by / us / 1e3, 1), "TFLOP/s": round(fl / us / 1e6, 2),
                        "hbm_frac": round(by / us / 1e3 / HBM_PEAK_GBS, 4),
@@ -451,7 +460,7 @@ def main():
     for d in detail:
         e = by_kernel.setdefault(d["kernel"], {"us": 0.0, "bytes": 0, "flops": 0, "launches": 0})
         e["us"] += d["us"]
-        e["bytes"] += alg_bytes(d["M"], d["K"], d["N"], d["swiglu"], zp)
+        e["bytes"] += alg_bytes(d["M"], d["K"], d["N"], d["swiglu"], zp, int8)
         e["flops"] += flops(d["M"], d["K"], d["N"])
         e["launches"] += 1
     dom = max(by_kernel, key=lambda k: by_kernel[k]["us"])
@@ -468,7 +477,7 @@ def main():
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4)}
     ceiling = ceilings["stream_read_GBs"] if hbm_bound else ceilings["mfma_f16_TFLOPs"]
     roof["frac_of_measured_ceiling"] = round(achieved / ceiling, 4) if ceiling else None
-    suffix = ("_bf16" if bf16 else "") + ("_zp" if zp else "")
+    suffix = ("_bf16" if bf16 else "") + ("_zp" if zp else "") + ("_int8" if int8 else "")
     roof["traffic"] = stored_traffic(args.workload + suffix, dom)
     roof["kernel"] = dom
     roof["launch_workgroups"] = sorted({int(re.search(r"workgroups=(\d+)", d["launch"]).group(1))
@@ -487,7 +496,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
-        cpu = cpu_baseline(units, host_w, bf16=bf16, host_zp=host_zp)
+        cpu = cpu_baseline(units, host_w, bf16=bf16, host_zp=host_zp, int8=int8)
         if unit == "TFLOP/s":
             cpu["value"] = round(cpu["value"] * step_flops / step_bytes / 1e3, 6)
             cpu["unit"] = "TFLOP/s"
@@ -505,10 +514,12 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if bf16 else "fp16",
-        "data": "synthetic (seeded N(0,1) " + args.dtype + " activations, N(0,0.02) weights quantized to int4 "
-                "G=128" + (", seeded zero points near 8 as prescaled zero rows" if zp else "") + ")",
+        "data": "synthetic (seeded N(0,1) " + args.dtype + " activations, N(0,0.02) weights quantized to "
+                + ("int8" if int8 else "int4") + " G=128"
+                + (", seeded zero points near 8 as prescaled zero rows" if zp else "") + ")",
         "config": {"workload": args.workload + suffix, "description": desc,
                    "activations": args.dtype, "G": G, "zero_points": zp,
+                   "weights": "int8" if int8 else "int4",
                    "gemms_per_step": len(units), "alg_bytes_per_step": step_bytes,
                    "flops_per_step": step_flops, "weight_copies": ncopies,
                    "path": "auto",

@@ -65,6 +65,9 @@ extern "C" {
 #define W4A16_FLAG_ZP 0x40     /* zero rows in use: for w4a16_describe,
                                   w4a16_gemm_workspace_bytes (w4a16_gemm_zp
                                   implies it) */
+#define W4A16_FLAG_INT8 0x80   /* INT8 weights: for w4a16_describe,
+                                  w4a16_gemm_workspace_bytes, w4a16_select_path
+                                  (w4a16_gemm_int8 implies it) */
 
 typedef void *w4a16_stream_t; /* a hipStream_t */
 
@@ -163,6 +166,50 @@ int w4a16_zero_rows(const uint16_t *scales_d, const uint8_t *zeros_d, int64_t K,
  * that definition.  rz_d as written by w4a16_zero_rows (not NULL). */
 int w4a16_dequant_zp(const void *rw_d, const void *rs_d, const void *rz_d, int64_t K, int64_t N,
                      int G, int flags, uint16_t *W_d, w4a16_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * INT8 weights (W8A16).  The Swordfish page (blog.alpindale.net, section "The
+ * packed format") runs an int8 variant whose unsigned 8-bit codes carry a
+ * bias of 128, dequantized with the same idiom; "Making a Single GPU Go Fast"
+ * (arunshar.com, chapter 9, section 9.3.2) recommends weight-only INT8 with
+ * per-output-channel scales (G = K here).  Format, by analogy with the int4
+ * data contract: per group of G rows along K and column n,
+ * s = max|W| / 127 (fp32), s = max(s, 1e-8), q = clamp(round_half_even(W / s),
+ * -128, 127) + 128, scale stored as fp16(s); four codes consecutive along K
+ * share one int32, code k at bits 8(k mod 4) .. 8(k mod 4)+7:
+ *   packed  int32 [K/4, N];  scales fp16 bits [K/G, N];  w = (q - 128) * s.
+ * Group sizes, alignment and errors as for INT4 weights; the packer needs
+ * G % 4 == 0. */
+int w4a16_pack_int8(const float *W_d, int64_t K, int64_t N, int G, int32_t *packed_d,
+                    uint16_t *scales_d, w4a16_stream_t stream);
+
+/* Repacked INT8 weights: 1 byte per weight, N padded to 32 (the pad
+ * dequantizes to zero); the scale buffer is w4a16_repacked_scale_bytes. */
+int64_t w4a16_repacked_weight_bytes_int8(int64_t K, int64_t N, int G);
+
+/* Permute canonical INT8 (packed_d [K/4,N], scales_d) into the repacked
+ * buffers; w4a16_unrepack_int8 inverts it exactly. */
+int w4a16_repack_int8(const int32_t *packed_d, const uint16_t *scales_d, int64_t K, int64_t N,
+                      int G, void *rw_d, void *rs_d, w4a16_stream_t stream);
+int w4a16_unrepack_int8(const void *rw_d, const void *rs_d, int64_t K, int64_t N, int G,
+                        int32_t *packed_d, uint16_t *scales_d, w4a16_stream_t stream);
+
+/* W_d[k,n] = round((q - 128) * s), fp16 bits [K, N] (bf16 with
+ * flags = W4A16_FLAG_BF16), rounded once; bit-exact with that definition. */
+int w4a16_dequant_int8(const void *rw_d, const void *rs_d, int64_t K, int64_t N, int G, int flags,
+                       uint16_t *W_d, w4a16_stream_t stream);
+
+/* GEMM on INT8 weights: out[m,n] = r_m * sum_k A[m,k] * w[k,n], FP32
+ * accumulation, with w = (q - 128) * s (fp16 activations: the product with
+ * the exact weight; bf16 activations: with bf16((q - 128) * s)) and r_m =
+ * rowscale_d[m] or 1 when rowscale_d is NULL.  M <= 32 streams the weights
+ * (the decode path); larger M, and an explicit W4A16_PATH_PREFILL, run the
+ * dense tier (dequantize into the workspace, then the dense fp16 GEMM).
+ * Flags, workspace, outputs and errors as w4a16_gemm_ex (W4A16_FLAG_INT8 is
+ * implied and may be given). */
+int w4a16_gemm_int8(const uint16_t *A_d, int64_t M, int64_t K, const void *rw_d, const void *rs_d,
+                    int64_t N, int G, const float *rowscale_d, uint16_t *out_d, int flags,
+                    void *workspace_d, int64_t workspace_bytes, w4a16_stream_t stream);
 
 /* ---------------------------------------------------------------------------
  * GEMM (the job, stated precisely): C_d[m,n] = sum_k A_d[m,k] * w[k,n], FP32

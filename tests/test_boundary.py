@@ -110,6 +110,25 @@ def test_zero_point_argument_errors_without_gpu():
     assert w4a16.workspace_bytes(16, 14336, 4096, zp=True) >= 0
 
 
+def test_int8_argument_errors_without_gpu():
+    L = w4a16.lib()
+    assert L.w4a16_pack_int8(16, 4096, 4096, 6, 16, 16, 0) == w4a16.ERR_INVALID     # K % G
+    assert L.w4a16_pack_int8(16, 4104, 4096, 1026, 16, 16, 0) == w4a16.ERR_UNSUPPORTED  # G % 4
+    assert L.w4a16_pack_int8(0, 4096, 4096, 128, 16, 16, 0) == w4a16.ERR_INVALID
+    assert L.w4a16_repack_int8(16, 16, 12288, 4096, 384, 16, 16, 0) == w4a16.ERR_UNSUPPORTED
+    assert L.w4a16_repack_int8(16, 16, 4096, 4096, 128, 8, 16, 0) == w4a16.ERR_INVALID  # align
+    assert L.w4a16_dequant_int8(16, 16, 4096, 4096, 128, 0x10, 16, 0) == w4a16.ERR_INVALID
+    assert L.w4a16_gemm_int8(16, 1, 4096, 16, 16, 4096, 128, 0, 16, 0x100, 0, 0, 0) == w4a16.ERR_INVALID
+    assert L.w4a16_gemm_int8(0, 1, 4096, 16, 16, 4096, 128, 0, 16, 0, 0, 0, 0) == w4a16.ERR_INVALID
+    assert L.w4a16_gemm_int8(0, 0, 4096, 0, 0, 4096, 128, 0, 0, 0, 0, 0, 0) == w4a16.OK
+    assert _gemm_ex(flags=w4a16.FLAG_INT8) == w4a16.ERR_INVALID    # only w4a16_gemm_int8 takes it
+    assert w4a16.lib().w4a16_repacked_weight_bytes_int8(4096, 4104, 128) == 4096 * 4128
+    assert w4a16.workspace_bytes(100, 4096, 4096, int8=True) >= 4096 * 4096 * 2   # dense scratch
+    buf = ctypes.create_string_buffer(64)
+    assert L.w4a16_describe(1, 4096, 4096, 128, w4a16.FLAG_INT8 | w4a16.FLAG_ZP,
+                            ctypes.addressof(buf), 64) == w4a16.ERR_UNSUPPORTED
+
+
 def test_other_argument_errors():
     L = w4a16.lib()
     assert L.w4a16_repack(0, 0, 4096, 4096, 128, 0, 0, 0) == w4a16.ERR_INVALID
@@ -162,10 +181,10 @@ def test_describe_names_the_launches():
     assert d.startswith("decode_coop_kernel<16, 2, ") and d.split(">")[0].endswith("true, true")
     d = w4a16.describe(1, 4096, 4096)
     assert d.startswith("decode_kernel<16, 1, ") and d.split(">")[0].endswith(
-        "false, false, false, false, true"), d        # 128 strips: half strips
+        "false, false, false, false, true, 4"), d     # 128 strips: half strips; INT4
     assert " workgroups=256 " in d and d.endswith("ks=1"), d
     d = w4a16.describe(24, 4096, 4096)
-    assert d.startswith("decode_kernel<32, 1, ") and d.split(">")[0].endswith("false, false"), d
+    assert d.startswith("decode_kernel<32, 1, ") and d.split(">")[0].endswith("false, false, 4"), d
     assert "prefill2_kernel<4, 2, 4, 2, false, true, false, false>" in w4a16.describe(
         4096, 4096, 28672, swiglu=True)
     assert "prefill2_kernel<4, 2, 4, 2, false, true, true, false>" in w4a16.describe(
@@ -178,10 +197,19 @@ def test_describe_names_the_launches():
     # prefill takes the ZP instance, the dense tier folds them into its dequant.
     d = w4a16.describe(1, 4096, 28672, swiglu=True, zp=True)
     assert d.startswith("decode_kernel<16, 2, ") and d.split(">")[0].endswith(
-        "true, false, true, true, false"), d
+        "true, false, true, true, false, 4"), d
     d = w4a16.describe(4, 4096, 4096, bf16=True, zp=True)
     assert d.startswith("decode_kernel<16, 1, ") and d.split(">")[0].endswith(
-        "false, true, true, true, true"), d
+        "false, true, true, true, true, 4"), d
+    # INT8 weights: the decode kernel's 8-bit instances, the dense tier above.
+    d = w4a16.describe(1, 4096, 28672, swiglu=True, int8=True)
+    assert d.startswith("decode_kernel<16, 2, ") and d.split(">")[0].endswith(", 8"), d
+    d = w4a16.describe(3, 4096, 4096, bf16=True, int8=True)
+    assert d.split(">")[0].endswith("false, true, true, false, true, 8"), d
+    assert w4a16.describe(100, 4096, 4096, int8=True).startswith("dequant8_kernel<false, false>; ")
+    assert w4a16.describe(100, 4096, 4096, path="prefill", int8=True).startswith("dequant8_kernel")
+    assert w4a16.select_path(100, 4096, 4096, int8=True) == "dense"
+    assert w4a16.select_path(100, 4096, 4096) == "prefill"
     assert "prefill2_kernel<4, 2, 4, 2, false, false, false, true>" in w4a16.describe(
         4096, 4096, 4096, zp=True)
     assert w4a16.describe(4096, 4096, 4096, path="dense", zp=True).startswith(

@@ -198,7 +198,7 @@ def test_decode_half_strips(monkeypatch, half, ks, waves, depth, M, K, N, swiglu
     monkeypatch.setenv("W4A16_DECODE_WAVES", str(waves))
     monkeypatch.setenv("W4A16_DECODE_DEPTH", str(depth))
     d = w4a16.describe(M, K, N, swiglu=swiglu, path="decode")
-    assert d.split(">")[0].endswith("true" if half else "false"), d
+    assert d.split(">")[0].endswith(("true" if half else "false") + ", 4"), d
     assert ("ks=%d" % ks) in d, d
     gemm_case(M, K, N, swiglu=swiglu, path="decode", seed=M + K + ks)
 

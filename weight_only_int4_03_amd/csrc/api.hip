@@ -109,11 +109,14 @@ int device_workspace(int64_t need, void **out) {
 constexpr int64_t kDecodeMaxM = 32;
 constexpr int64_t kDenseMinM = 1 << 30;  // the fused kernel is kept at every M measured so far
 
-int select_path(int64_t M, int64_t K, int64_t N) {
+int select_path(int64_t M, int64_t K, int64_t N, int bits = 4) {
   (void)K;
   (void)N;
   if (M <= kDecodeMaxM) return W4A16_PATH_DECODE;
-  if (M >= kDenseMinM) return W4A16_PATH_DENSE;
+  // INT8 weights above decode sizes run the dense tier: the Swordfish page
+  // (section "The dense tier") finds that at int8 the halved traffic gap lets
+  // dequantize-then-dense-GEMM overtake the fused mainloop.
+  if (M >= kDenseMinM || bits == 8) return W4A16_PATH_DENSE;
   return W4A16_PATH_PREFILL;
 }
 
@@ -131,7 +134,7 @@ int64_t workspace_for(int path, const Problem &p) {
 int run_gemm(const uint16_t *A, int64_t M, int64_t K, const void *rw, const void *rs, int64_t N,
              int G, uint16_t *out, int flags, void *workspace, int64_t ws_bytes,
              hipStream_t stream, const float *rowscale = nullptr, const void *rz = nullptr,
-             const char *who = nullptr) {
+             const char *who = nullptr, int bits = 4) {
   if (who == nullptr) who = (flags & W4A16_FLAG_SWIGLU) ? "w4a16_gemm_swiglu" : "w4a16_gemm";
   const bool bf16 = (flags & W4A16_FLAG_BF16) != 0;
   int rc = check_gpu_shape(K, N, G, who);
@@ -146,11 +149,13 @@ int run_gemm(const uint16_t *A, int64_t M, int64_t K, const void *rw, const void
   if (!aligned16(A) || !aligned16(rw) || !aligned16(rs) || !aligned16(out) || !aligned16(rz))
     return fail(W4A16_ERR_INVALID, "%s: device pointers must be 16-byte aligned", who);
   int path = flags & 0xF;
-  if (path == W4A16_PATH_AUTO) path = select_path(M, K, N);
+  if (path == W4A16_PATH_AUTO) path = select_path(M, K, N, bits);
   if (path < W4A16_PATH_DECODE || path > W4A16_PATH_DENSE)
     return fail(W4A16_ERR_INVALID, "%s: unknown path %d", who, path);
+  if (bits == 8 && path == W4A16_PATH_PREFILL) path = W4A16_PATH_DENSE;
 
-  Problem p{A, M, K, N, rw, rs, out, swiglu, bf16, rowscale, G, group_shift(K, G), rz, rz != nullptr};
+  Problem p{A, M, K, N, rw, rs, out, swiglu, bf16, rowscale, G, group_shift(K, G), rz,
+            rz != nullptr, bits};
   const int64_t need = workspace_for(path, p);
   void *ws = workspace;
   if (need > 0) {
@@ -375,6 +380,72 @@ int w4a16_dequant_zp(const void *rw_d, const void *rs_d, const void *rz_d, int64
                         (hipStream_t)stream, who);
 }
 
+int w4a16_pack_int8(const float *W_d, int64_t K, int64_t N, int G, int32_t *packed_d,
+                    uint16_t *scales_d, w4a16_stream_t stream) {
+  const char *who = "w4a16_pack_int8";
+  int rc = check_shape(K, N, G, who);
+  if (rc != W4A16_OK) return rc;
+  if (G % 4 != 0)
+    return fail(W4A16_ERR_UNSUPPORTED, "%s: the GPU packer needs G % 4 == 0 (got %d)", who, G);
+  if (K / G > 65535) return fail(W4A16_ERR_INVALID, "%s: K too large", who);
+  if (!W_d || !packed_d || !scales_d) return fail(W4A16_ERR_INVALID, "%s: null pointer", who);
+  hipError_t e = launch_pack8(W_d, K, N, G, packed_d, scales_d, (hipStream_t)stream);
+  return e == hipSuccess ? W4A16_OK : hip_fail(e, who);
+}
+
+int64_t w4a16_repacked_weight_bytes_int8(int64_t K, int64_t N, int G) {
+  int rc = check_gpu_shape(K, N, G, "w4a16_repacked_weight_bytes_int8");
+  if (rc != W4A16_OK) return rc;
+  return ceil_div(N, kStrip) * (K / kTileK) * 2 * kTileWords * 4;
+}
+
+int w4a16_repack_int8(const int32_t *packed_d, const uint16_t *scales_d, int64_t K, int64_t N,
+                      int G, void *rw_d, void *rs_d, w4a16_stream_t stream) {
+  const char *who = "w4a16_repack_int8";
+  int rc = check_gpu_shape(K, N, G, who);
+  if (rc != W4A16_OK) return rc;
+  if (!packed_d || !scales_d || !rw_d || !rs_d) return fail(W4A16_ERR_INVALID, "%s: null pointer", who);
+  if (!aligned16(rw_d) || !aligned16(rs_d))
+    return fail(W4A16_ERR_INVALID, "%s: repacked buffers must be 16-byte aligned", who);
+  hipError_t e = launch_repack8(packed_d, scales_d, K, N, G, rw_d, rs_d, (hipStream_t)stream);
+  return e == hipSuccess ? W4A16_OK : hip_fail(e, who);
+}
+
+int w4a16_unrepack_int8(const void *rw_d, const void *rs_d, int64_t K, int64_t N, int G,
+                        int32_t *packed_d, uint16_t *scales_d, w4a16_stream_t stream) {
+  const char *who = "w4a16_unrepack_int8";
+  int rc = check_gpu_shape(K, N, G, who);
+  if (rc != W4A16_OK) return rc;
+  if (!packed_d || !scales_d || !rw_d || !rs_d) return fail(W4A16_ERR_INVALID, "%s: null pointer", who);
+  if (!aligned16(rw_d) || !aligned16(rs_d))
+    return fail(W4A16_ERR_INVALID, "%s: repacked buffers must be 16-byte aligned", who);
+  hipError_t e = launch_unrepack8(rw_d, rs_d, K, N, G, packed_d, scales_d, (hipStream_t)stream);
+  return e == hipSuccess ? W4A16_OK : hip_fail(e, who);
+}
+
+int w4a16_dequant_int8(const void *rw_d, const void *rs_d, int64_t K, int64_t N, int G, int flags,
+                       uint16_t *W_d, w4a16_stream_t stream) {
+  const char *who = "w4a16_dequant_int8";
+  if (flags & ~W4A16_FLAG_BF16) return fail(W4A16_ERR_INVALID, "%s: unknown flags 0x%x", who, flags);
+  int rc = check_gpu_shape(K, N, G, who);
+  if (rc != W4A16_OK) return rc;
+  if (!rw_d || !rs_d || !W_d) return fail(W4A16_ERR_INVALID, "%s: null pointer", who);
+  if (!aligned16(rw_d) || !aligned16(rs_d))
+    return fail(W4A16_ERR_INVALID, "%s: repacked buffers must be 16-byte aligned", who);
+  hipError_t e = launch_dequant8_canonical(rw_d, rs_d, K, N, G, (flags & W4A16_FLAG_BF16) != 0,
+                                           W_d, (hipStream_t)stream);
+  return e == hipSuccess ? W4A16_OK : hip_fail(e, who);
+}
+
+int w4a16_gemm_int8(const uint16_t *A_d, int64_t M, int64_t K, const void *rw_d, const void *rs_d,
+                    int64_t N, int G, const float *rowscale_d, uint16_t *out_d, int flags,
+                    void *workspace_d, int64_t workspace_bytes, w4a16_stream_t stream) {
+  if (flags & ~(0xF | W4A16_FLAG_SWIGLU | W4A16_FLAG_BF16 | W4A16_FLAG_INT8))
+    return fail(W4A16_ERR_INVALID, "w4a16_gemm_int8: unknown flags 0x%x", flags);
+  return run_gemm(A_d, M, K, rw_d, rs_d, N, G, out_d, flags & ~W4A16_FLAG_INT8, workspace_d,
+                  workspace_bytes, (hipStream_t)stream, rowscale_d, nullptr, "w4a16_gemm_int8", 8);
+}
+
 int w4a16_gemm(const uint16_t *A_d, int64_t M, int64_t K, const void *rw_d, const void *rs_d,
                int64_t N, int G, uint16_t *C_d, w4a16_stream_t stream) {
   return run_gemm(A_d, M, K, rw_d, rs_d, N, G, C_d, W4A16_PATH_AUTO, nullptr, 0,
@@ -440,11 +511,13 @@ int64_t w4a16_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N, int G, int f
   int rc = check_gpu_shape(K, N, G, "w4a16_gemm_workspace_bytes");
   if (rc != W4A16_OK) return rc;
   if (M <= 0) return 0;
+  const int bits = (flags & W4A16_FLAG_INT8) ? 8 : 4;
   int path = flags & 0xF;
-  if (path == W4A16_PATH_AUTO) path = select_path(M, K, N);
+  if (path == W4A16_PATH_AUTO) path = select_path(M, K, N, bits);
+  if (bits == 8 && path == W4A16_PATH_PREFILL) path = W4A16_PATH_DENSE;
   Problem p{nullptr, M, K, N, nullptr, nullptr, nullptr, (flags & W4A16_FLAG_SWIGLU) != 0,
             (flags & W4A16_FLAG_BF16) != 0, nullptr, G, group_shift(K, G), nullptr,
-            (flags & W4A16_FLAG_ZP) != 0};
+            (flags & W4A16_FLAG_ZP) != 0, bits};
   return workspace_for(path, p);
 }
 
@@ -453,18 +526,22 @@ int w4a16_describe(int64_t M, int64_t K, int64_t N, int G, int flags, char *buf,
   if (rc != W4A16_OK) return rc;
   if (M < 1) return fail(W4A16_ERR_INVALID, "w4a16_describe: M must be >= 1");
   if (buf == nullptr || len < 1) return fail(W4A16_ERR_INVALID, "w4a16_describe: no buffer");
-  if (flags & ~(0xF | W4A16_FLAG_SWIGLU | W4A16_FLAG_BF16 | W4A16_FLAG_ZP))
+  if (flags & ~(0xF | W4A16_FLAG_SWIGLU | W4A16_FLAG_BF16 | W4A16_FLAG_ZP | W4A16_FLAG_INT8))
     return fail(W4A16_ERR_INVALID, "w4a16_describe: unknown flags 0x%x", flags);
+  if ((flags & W4A16_FLAG_ZP) && (flags & W4A16_FLAG_INT8))
+    return fail(W4A16_ERR_UNSUPPORTED, "w4a16_describe: INT8 weights have no zero points");
+  const int bits = (flags & W4A16_FLAG_INT8) ? 8 : 4;
   const bool swiglu = (flags & W4A16_FLAG_SWIGLU) != 0;
   if (swiglu && N % 64 != 0)
     return fail(W4A16_ERR_INVALID, "w4a16_describe: N (%lld) must be a multiple of 64",
                 (long long)N);
   int path = flags & 0xF;
-  if (path == W4A16_PATH_AUTO) path = select_path(M, K, N);
+  if (path == W4A16_PATH_AUTO) path = select_path(M, K, N, bits);
   if (path < W4A16_PATH_DECODE || path > W4A16_PATH_DENSE)
     return fail(W4A16_ERR_INVALID, "w4a16_describe: unknown path %d", path);
+  if (bits == 8 && path == W4A16_PATH_PREFILL) path = W4A16_PATH_DENSE;
   Problem p{nullptr, M, K, N, nullptr, nullptr, nullptr, swiglu, (flags & W4A16_FLAG_BF16) != 0,
-            nullptr, G, group_shift(K, G), nullptr, (flags & W4A16_FLAG_ZP) != 0};
+            nullptr, G, group_shift(K, G), nullptr, (flags & W4A16_FLAG_ZP) != 0, bits};
   char tmp[512];
   int k;
   if (path == W4A16_PATH_DECODE) {
@@ -486,8 +563,7 @@ int w4a16_select_path(int64_t M, int64_t K, int64_t N, int G, int flags) {
   int rc = check_gpu_shape(K, N, G, "w4a16_select_path");
   if (rc != W4A16_OK) return rc;
   if (M < 0) return fail(W4A16_ERR_INVALID, "w4a16_select_path: M must be >= 0");
-  (void)flags;
-  return select_path(M, K, N);
+  return select_path(M, K, N, (flags & W4A16_FLAG_INT8) ? 8 : 4);
 }
 
 }  // extern "C"

@@ -14,6 +14,17 @@
 // (k6,k7) in register order: k offset i sits at nibble position
 // (i % 2) * 4 + i / 2.  Pad columns (n >= N) hold 0x88888888 (all zero weights).
 //
+// INT8 weights (8-bit codes offset by 128, canonical [K/4, N] int32 with
+// byte k at bits 8(k mod 4)) use the same strips and 64-k tiles at twice the
+// bytes: a tile is 2 KiB, two 1 KiB halves; in half j lane position
+// l = 32h + c holds four words of column 32t + c with k = 64q + 32h + 16j +
+// 4i .. +3 in word i, so a lane's two 16-byte vectors bring its 32
+// consecutive k and every wave-wide load is still one contiguous KiB:
+//     uint4 offset of (t, q, j, l) = ((t * KT + q) * 2 + j) * 64 + l.
+// Inside each word the bytes hold k offsets (0, 2, 1, 3), so
+// w & 0x00FF00FF and (w >> 8) & 0x00FF00FF yield the pairs (k0,k1), (k2,k3).
+// Pad columns hold 0x80808080 (all zero weights).
+//
 // Repacked scale layout: fp16 [NS][KG8][32][8], NS = ceil(N/32),
 // KG8 = ceil(K/128 / 8): entry ((t*KG8 + o)*32 + c)*8 + e is the scale of group
 // 8o + e and column 32t + c (zero in padding), so a lane reads eight
@@ -98,6 +109,50 @@ struct Dequant {
     const half2_t q0 = half2_t{v[0], v[1]} * s2, q1 = half2_t{v[2], v[3]} * s2;
     const half2_t q2 = half2_t{v[4], v[5]} * s2, q3 = half2_t{v[6], v[7]} * s2;
     return half8_t{q0[0], q0[1], q1[0], q1[1], q2[0], q2[1], q3[0], q3[1]};
+  }
+
+  // INT8: the eight codes of two repacked words (k order) as fp16 u - 128,
+  // exact: (w & 0x00FF00FF) | 0x64006400 is the pair (1024 + u, 1024 + u'),
+  // and one packed add of -1152 leaves u - 128 (Swordfish page, "The packed
+  // format": the same idiom over byte lanes with a bias of 128).  5 VALU
+  // instructions per 4 weights.
+  __device__ __forceinline__ half8_t bytes8(uint32_t w0, uint32_t w1) const {
+    const half2_t b = half2_t{(_Float16)-1152.0f, (_Float16)-1152.0f};
+    const uint32_t m = 0x00FF00FFu;
+    const half2_t p0 = bitcast<half2_t>((w0 & m) | magic) + b;
+    const half2_t p1 = bitcast<half2_t>(((w0 >> 8) & m) | magic) + b;
+    const half2_t p2 = bitcast<half2_t>((w1 & m) | magic) + b;
+    const half2_t p3 = bitcast<half2_t>(((w1 >> 8) & m) | magic) + b;
+    return half8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+  }
+  // fp16((u - 128) * s), one rounding.
+  __device__ __forceinline__ half8_t scaled8(uint32_t w0, uint32_t w1, half2_t s2) const {
+    const half8_t v = bytes8(w0, w1);
+    const half2_t q0 = half2_t{v[0], v[1]} * s2, q1 = half2_t{v[2], v[3]} * s2;
+    const half2_t q2 = half2_t{v[4], v[5]} * s2, q3 = half2_t{v[6], v[7]} * s2;
+    return half8_t{q0[0], q0[1], q1[0], q1[1], q2[0], q2[1], q3[0], q3[1]};
+  }
+  // bf16((u - 128) * s): (1024 + u) s - 1152 s in one exact mixed-precision
+  // FMA (19-bit product, 15-bit constant), then one rounding to bf16.
+  __device__ __forceinline__ bf16x8_t scaled8_bf16(uint32_t w0, uint32_t w1, float s) const {
+    const uint32_t m = 0x00FF00FFu;
+    const float c = -1152.0f * s;
+    const half2_t x0 = bitcast<half2_t>((w0 & m) | magic);
+    const half2_t x1 = bitcast<half2_t>(((w0 >> 8) & m) | magic);
+    const half2_t x2 = bitcast<half2_t>((w1 & m) | magic);
+    const half2_t x3 = bitcast<half2_t>(((w1 >> 8) & m) | magic);
+    auto f = [&](_Float16 x) { return (__bf16)__builtin_fmaf((float)x, s, c); };
+    return bf16x8_t{f(x0[0]), f(x0[1]), f(x1[0]), f(x1[1]),
+                    f(x2[0]), f(x2[1]), f(x3[0]), f(x3[1])};
+  }
+  template <bool BF>
+  __device__ __forceinline__ uint4_t scaled8_bits(uint32_t w0, uint32_t w1, uint16_t s16) const {
+    if constexpr (BF) {
+      return bitcast<uint4_t>(scaled8_bf16(w0, w1, (float)bitcast<_Float16>(s16)));
+    } else {
+      const _Float16 sh = bitcast<_Float16>(s16);
+      return bitcast<uint4_t>(scaled8(w0, w1, half2_t{sh, sh}));
+    }
   }
 
   // With a zero row (AWQ zero points prescaled as z = fp16((8 - zp) s)):
@@ -259,6 +314,7 @@ struct Problem {
   int gshift = 7;  // group of k = k >> gshift (see group_shift)
   const void *rz = nullptr;  // prescaled zero rows, laid out as rs, or null
   bool zp = false;           // zero rows in use (rz != null when launching)
+  int bits = 4;              // weight code width: 4 (INT4) or 8 (INT8)
 };
 
 // Group sizes: a power of two >= 32 that divides K, or K itself
@@ -293,6 +349,18 @@ hipError_t launch_repack(const int32_t *packed, const uint16_t *scales, int64_t 
                          int G, void *rw, void *rs, hipStream_t s);
 hipError_t launch_unrepack(const void *rw, const void *rs, int64_t K, int64_t N, int G,
                            int32_t *packed, uint16_t *scales, hipStream_t s);
+// INT8 weights: quantize + pack ([K/4, N] words), repack / unrepack, dequantize.
+hipError_t launch_pack8(const float *W, int64_t K, int64_t N, int G, int32_t *packed,
+                        uint16_t *scales, hipStream_t s);
+hipError_t launch_repack8(const int32_t *packed, const uint16_t *scales, int64_t K, int64_t N,
+                          int G, void *rw, void *rs, hipStream_t s);
+hipError_t launch_unrepack8(const void *rw, const void *rs, int64_t K, int64_t N, int G,
+                            int32_t *packed, uint16_t *scales, hipStream_t s);
+hipError_t launch_dequant8_canonical(const void *rw, const void *rs, int64_t K, int64_t N, int G,
+                                     bool bf16, uint16_t *W, hipStream_t s);
+hipError_t launch_dequant8_fragment(const void *rw, const void *rs, int64_t K, int64_t N, int G,
+                                    bool bf16, uint16_t *Wf, hipStream_t s);
+
 // Prescaled zero rows fp16((8 - zp) s) in the repacked scale layout.
 hipError_t launch_zero_rows(const uint16_t *scales, const uint8_t *zeros, int64_t K, int64_t N,
                             int G, void *rz, hipStream_t s);

@@ -40,11 +40,12 @@
 
 namespace w4a16 {
 
-template <int MT, int SPW>
+template <int MT, int SPW, int BITS = 4>
 struct DecodeFrag {
   static constexpr int NB = 2;                 // 16-byte weight vectors per strip per group
+  static constexpr int NV = BITS == 8 ? 2 : 1;  // vectors per lane and MFMA unit (INT8: two)
   static constexpr int NA = MT == 16 ? 4 : 8;  // 16-byte activation vectors per group
-  uint4_t b[SPW][NB];
+  uint4_t b[SPW][NB][NV];
   uint4_t a[NA];
   // Scales per strip, 16-column half (MT=16) and 64-k tile (MT=32, which
   // can span two groups when G < 128), and the zero rows likewise (16-bit
@@ -62,19 +63,25 @@ struct DecodeFrag {
 // HALF (MT=16 only): the workgroup owns one 16-column half of each of its
 // strips (workgroups 2b and 2b+1 share strip group b), which doubles the
 // workgroups of a narrow projection without splitting K.
+// BITS: 4 (INT4 codes offset by 8) or 8 (INT8 codes offset by 128, the
+// repacked INT8 layout: twice the bytes per tile, two vectors per lane).
 template <int MT, int SPW, int WAVES, int D, int RPL, bool SWIGLU, bool BF, bool PRE, bool ZP,
-          bool HALF>
+          bool HALF, int BITS = 4>
 __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
   static_assert(PRE || !BF, "bf16 weights are always scaled before the MFMA");
   static_assert(PRE || !ZP, "weights with zero points are scaled before the MFMA");
   static_assert(!HALF || MT == 16, "half strips need the 16-column MFMA");
+  static_assert(BITS == 4 || (BITS == 8 && !ZP), "INT8 weights have no zero rows");
   static_assert(MT == 16 ? (RPL >= 1 && RPL <= 4) : RPL == 16, "rows per lane");
   extern __shared__ float lds[];  // [WAVES][SPW][M][32]
   constexpr int SH = SWIGLU ? SPW / 2 : SPW;
   // 16-column halves per workgroup (MT=16) or the whole strip (MT=32).
   constexpr int NPART = MT == 16 ? (HALF ? 1 : 2) : 1;
   typedef typename std::conditional<MT == 16, float4_t, float16_t>::type acc_t;
-  typedef DecodeFrag<MT, SPW> Frag;
+  typedef DecodeFrag<MT, SPW, BITS> Frag;
+  constexpr int NV = Frag::NV;
+  constexpr uint32_t TILE = 1024u * NV;   // bytes per 64-k tile of a strip
+  constexpr uint32_t GROUP = 2u * TILE;   // bytes per 128-k unit of a strip
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -93,7 +100,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
   for (int s = 0; s < SPW; ++s) {
     const int base = sg * SH + (s % SH);
     const int strip = SWIGLU && s >= SH ? base + p.up_off : base;
-    wbase[s] = (const char *)(p.rw + (int64_t)strip * p.KT * 64);
+    wbase[s] = (const char *)(p.rw + (int64_t)strip * p.KT * 64 * NV);
     sbase[s] = (const char *)(p.rs + (int64_t)strip * p.KG8 * 256);
     zbase[s] = ZP ? (const char *)(p.rz + (int64_t)strip * p.KG8 * 256) : nullptr;
   }
@@ -111,8 +118,9 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
   const int h = lane >> 5, c32 = lane & 31;
   const int mrow = MT == 16 ? c16 : c32;
   const uint32_t arow_off = (uint32_t)(mrow < M ? mrow : M - 1) * (uint32_t)p.K * 2u;
-  // Byte offsets inside one group's 2 KiB of a strip (two 1 KiB tiles).
-  const uint32_t wlane = MT == 16 ? (uint32_t)(((g4 >> 1) * 64 + (g4 & 1) * 32 + c16) * 16)
+  // Byte offsets inside one group's bytes of a strip (two 64-k tiles; an
+  // INT8 tile holds a lane's second vector 1 KiB after its first).
+  const uint32_t wlane = MT == 16 ? (uint32_t)((g4 >> 1) * TILE + ((g4 & 1) * 32 + c16) * 16)
                                   : (uint32_t)(lane * 16);
   const uint32_t slane = (uint32_t)((MT == 16 ? c16 : c32) * 16);
   // k offset, within a 128-k unit, of the lane's first weight (tile x = 0).
@@ -124,17 +132,22 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
   // constant), which maps onto the scalar-base form of the global loads.
   auto soff = [&](int grp) { return (uint32_t)(grp >> 3) * 512u + (uint32_t)(grp & 7) * 2u + slane; };
   auto load = [&](Frag &f, int g) {
-    const uint32_t ow = (uint32_t)g * 2048u + wlane;
+    const uint32_t ow = (uint32_t)g * GROUP + wlane;
 #pragma unroll
     for (int s = 0; s < SPW; ++s) {
       const char *wp = wbase[s] + ow;
       if constexpr (MT == 16) {
 #pragma unroll
         for (int part = 0; part < NPART; ++part)
-          f.b[s][part] = load_nt((const uint4_t *)(wp + (half + part) * 256));
+#pragma unroll
+          for (int v = 0; v < NV; ++v)
+            f.b[s][part][v] = load_nt((const uint4_t *)(wp + (half + part) * 256 + v * 1024));
       } else {
 #pragma unroll
-        for (int x = 0; x < 2; ++x) f.b[s][x] = load_nt((const uint4_t *)(wp + x * 1024));
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+          for (int v = 0; v < NV; ++v)
+            f.b[s][x][v] = load_nt((const uint4_t *)(wp + x * TILE + v * 1024));
       }
       if constexpr (PRE) {
         if constexpr (MT == 16) {
@@ -177,6 +190,21 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
 #pragma unroll
     for (int part = 0; part < NPART; ++part) acc[s][part] = acc_t{};
 
+  // MFMA weight operand j (k offsets 8j .. 8j+7 of the lane's 32) of one
+  // strip part: unscaled (exact code minus offset, fp16) or scaled.
+  auto wq = [&](const uint4_t(&v)[NV], int j) {
+    if constexpr (BITS == 8)
+      return dq.bytes8(v[j >> 1][(j & 1) * 2], v[j >> 1][(j & 1) * 2 + 1]);
+    else
+      return dq(v[0][j]);
+  };
+  auto wsc = [&](const uint4_t(&v)[NV], int j, uint16_t sc, uint16_t zs) {
+    if constexpr (BITS == 8)
+      return dq.scaled8_bits<BF>(v[j >> 1][(j & 1) * 2], v[j >> 1][(j & 1) * 2 + 1], sc);
+    else
+      return dq.scaled_bits<BF, ZP>(v[0][j], sc, zs);
+  };
+
   auto compute = [&](const Frag &f) {
     if constexpr (PRE) {
       // Scaled weights (rounded to fp16 or bf16) into the MFMA, which
@@ -189,8 +217,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
             const uint16_t sc = (uint16_t)f.sc[s][part][0], zs = (uint16_t)f.zs[s][part][0];
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-              acc[s][part] = mfma16<BF>(f.a[j], dq.scaled_bits<BF, ZP>(f.b[s][part][j], sc, zs),
-                                        acc[s][part]);
+              acc[s][part] = mfma16<BF>(f.a[j], wsc(f.b[s][part], j, sc, zs), acc[s][part]);
           } else {
 #pragma unroll
             for (int x = 0; x < 2; ++x)
@@ -198,8 +225,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
               for (int j = 0; j < 4; ++j)
                 acc[s][part] = mfma32<BF>(
                     f.a[4 * x + j],
-                    dq.scaled_bits<BF, ZP>(f.b[s][x][j], (uint16_t)f.sc[s][0][x],
-                                           (uint16_t)f.zs[s][0][x]),
+                    wsc(f.b[s][x], j, (uint16_t)f.sc[s][0][x], (uint16_t)f.zs[s][0][x]),
                     acc[s][part]);
           }
         }
@@ -215,14 +241,14 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
 #pragma unroll
           for (int j = 0; j < 4; ++j)
             t = __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<half8_t>(f.a[j]),
-                                                       dq(f.b[s][part][j]), t, 0, 0, 0);
+                                                       wq(f.b[s][part], j), t, 0, 0, 0);
         } else {
 #pragma unroll
           for (int x = 0; x < 2; ++x)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
               t = __builtin_amdgcn_mfma_f32_32x32x16_f16(bitcast<half8_t>(f.a[4 * x + j]),
-                                                         dq(f.b[s][x][j]), t, 0, 0, 0);
+                                                         wq(f.b[s][x], j), t, 0, 0, 0);
         }
         const float sc = (float)bitcast<_Float16>((uint16_t)f.sc[s][part][0]);
         // Element r of a lane's tile holds row 4*g4 + r (MT=16), so with
@@ -395,9 +421,9 @@ int decode_describe(const Problem &p, char *buf, size_t n) {
   const char *pre = (p.bf16 || p.G < kGroup || p.zp) ? "true" : "false";
   const char *zp = p.zp ? "true" : "false", *hf = c.half ? "true" : "false";
   int k = snprintf(buf, n,
-                   "decode_kernel<%d, %d, %d, %d, %d, %s, %s, %s, %s, %s> workgroups=%d threads=%d "
-                   "ks=%d",
-                   c.MT, c.SPW, c.WAVES, c.D, rpl, sw, bf, pre, zp, hf,
+                   "decode_kernel<%d, %d, %d, %d, %d, %s, %s, %s, %s, %s, %d> workgroups=%d "
+                   "threads=%d ks=%d",
+                   c.MT, c.SPW, c.WAVES, c.D, rpl, sw, bf, pre, zp, hf, p.bits,
                    c.nsg * c.KS * (c.half ? 2 : 1), c.WAVES * 64, c.KS);
   if (c.KS > 1 && k > 0 && (size_t)k < n)
     k += snprintf(buf + k, n - k, "; decode_reduce_kernel<%d, %s, %s>", c.SPW, sw, bf);
@@ -417,45 +443,44 @@ int64_t decode_workspace_bytes(const Problem &p) {
 }
 
 template <int MT, int SPW, int WAVES, int D, int RPL, bool SWIGLU, bool BF, bool PRE, bool ZP,
-          bool HALF>
+          bool HALF, int BITS>
 static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t s) {
   const size_t lds = (size_t)WAVES * SPW * a.M * 32 * sizeof(float);
-  hipLaunchKernelGGL((decode_kernel<MT, SPW, WAVES, D, RPL, SWIGLU, BF, PRE, ZP, HALF>),
-                     dim3(a.nsg * a.KS * (HALF ? 2 : 1)),
-                     dim3(WAVES * 64), lds, s, a);
+  hipLaunchKernelGGL((decode_kernel<MT, SPW, WAVES, D, RPL, SWIGLU, BF, PRE, ZP, HALF, BITS>),
+                     dim3(a.nsg * a.KS * (HALF ? 2 : 1)), dim3(WAVES * 64), lds, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.KS == 1) return e;
   return launch_decode_reduce(a, SWIGLU, BF, s);
 }
 
-template <int MT, int SPW, int RPL, bool SWIGLU, bool BF, bool PRE, bool ZP, bool HALF>
+template <int MT, int SPW, int RPL, bool SWIGLU, bool BF, bool PRE, bool ZP, bool HALF, int BITS>
 static hipError_t launch_decode_h(const DecodeArgs &a, const DecodeConfig &c, hipStream_t s) {
   if (c.D == 4)
-    return c.WAVES == 8 ? launch_decode_t<MT, SPW, 8, 4, RPL, SWIGLU, BF, PRE, ZP, HALF>(a, s)
-                        : launch_decode_t<MT, SPW, 4, 4, RPL, SWIGLU, BF, PRE, ZP, HALF>(a, s);
-  return c.WAVES == 8 ? launch_decode_t<MT, SPW, 8, 2, RPL, SWIGLU, BF, PRE, ZP, HALF>(a, s)
-                      : launch_decode_t<MT, SPW, 4, 2, RPL, SWIGLU, BF, PRE, ZP, HALF>(a, s);
+    return c.WAVES == 8 ? launch_decode_t<MT, SPW, 8, 4, RPL, SWIGLU, BF, PRE, ZP, HALF, BITS>(a, s)
+                        : launch_decode_t<MT, SPW, 4, 4, RPL, SWIGLU, BF, PRE, ZP, HALF, BITS>(a, s);
+  return c.WAVES == 8 ? launch_decode_t<MT, SPW, 8, 2, RPL, SWIGLU, BF, PRE, ZP, HALF, BITS>(a, s)
+                      : launch_decode_t<MT, SPW, 4, 2, RPL, SWIGLU, BF, PRE, ZP, HALF, BITS>(a, s);
 }
 
-template <int MT, int SPW, int RPL, bool SWIGLU, bool BF, bool PRE, bool ZP>
+template <int MT, int SPW, int RPL, bool SWIGLU, bool BF, bool PRE, bool ZP, int BITS>
 static hipError_t launch_decode_w(const DecodeArgs &a, const DecodeConfig &c, hipStream_t s) {
   if constexpr (MT == 16) {
-    if (c.half) return launch_decode_h<MT, SPW, RPL, SWIGLU, BF, PRE, ZP, true>(a, c, s);
+    if (c.half) return launch_decode_h<MT, SPW, RPL, SWIGLU, BF, PRE, ZP, true, BITS>(a, c, s);
   }
-  return launch_decode_h<MT, SPW, RPL, SWIGLU, BF, PRE, ZP, false>(a, c, s);
+  return launch_decode_h<MT, SPW, RPL, SWIGLU, BF, PRE, ZP, false, BITS>(a, c, s);
 }
 
-template <bool BF, bool PRE, bool ZP>
+template <bool BF, bool PRE, bool ZP, int BITS = 4>
 static hipError_t launch_decode_bf(const Problem &p, const DecodeArgs &a, const DecodeConfig &c,
                                    hipStream_t s) {
   if (c.MT == 16 && p.M == 1)
-    return p.swiglu ? launch_decode_w<16, 2, 1, true, BF, PRE, ZP>(a, c, s)
-                    : launch_decode_w<16, 1, 1, false, BF, PRE, ZP>(a, c, s);
+    return p.swiglu ? launch_decode_w<16, 2, 1, true, BF, PRE, ZP, BITS>(a, c, s)
+                    : launch_decode_w<16, 1, 1, false, BF, PRE, ZP, BITS>(a, c, s);
   if (c.MT == 16)
-    return p.swiglu ? launch_decode_w<16, 2, 4, true, BF, PRE, ZP>(a, c, s)
-                    : launch_decode_w<16, 1, 4, false, BF, PRE, ZP>(a, c, s);
-  return p.swiglu ? launch_decode_w<32, 2, 16, true, BF, PRE, ZP>(a, c, s)
-                  : launch_decode_w<32, 1, 16, false, BF, PRE, ZP>(a, c, s);
+    return p.swiglu ? launch_decode_w<16, 2, 4, true, BF, PRE, ZP, BITS>(a, c, s)
+                    : launch_decode_w<16, 1, 4, false, BF, PRE, ZP, BITS>(a, c, s);
+  return p.swiglu ? launch_decode_w<32, 2, 16, true, BF, PRE, ZP, BITS>(a, c, s)
+                  : launch_decode_w<32, 1, 16, false, BF, PRE, ZP, BITS>(a, c, s);
 }
 
 DecodeArgs decode_args(const Problem &p, int KS, void *workspace) {
@@ -506,6 +531,11 @@ hipError_t launch_decode(const Problem &p, void *workspace, hipStream_t s) {
   const DecodeConfig c = decode_config(p);
   DecodeArgs a = decode_args(p, c.KS, workspace);
   if (c.KS > 1 && workspace == nullptr) return hipErrorInvalidValue;
+  if (p.bits == 8) {
+    if (p.bf16) return launch_decode_bf<true, true, false, 8>(p, a, c, s);
+    return p.G < kGroup ? launch_decode_bf<false, true, false, 8>(p, a, c, s)
+                        : launch_decode_bf<false, false, false, 8>(p, a, c, s);
+  }
   if (p.zp)
     return p.bf16 ? launch_decode_bf<true, true, true>(p, a, c, s)
                   : launch_decode_bf<false, true, true>(p, a, c, s);

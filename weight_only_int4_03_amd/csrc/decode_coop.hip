@@ -381,6 +381,7 @@ bool coop_config(const Problem &p, int &WC, int &WK, int &KS) {
   const int force = coop_env_raw("W4A16_DECODE_COOP");
   if (p.G < kGroup) return false;  // one scale per column and 128-k unit
   if (p.zp) return false;          // zero rows: decode_kernel's pre-scaled form
+  if (p.bits != 4) return false;   // INT8 weights: decode_kernel's 8-bit instances
   bool use;
   if (nsg >= 384) {
     use = true;

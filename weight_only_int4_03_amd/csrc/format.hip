@@ -155,6 +155,179 @@ hipError_t launch_unrepack(const void *rw, const void *rs, int64_t K, int64_t N,
 }
 
 // ---------------------------------------------------------------------------
+// INT8 weights.  Quantize + pack: the int4 kernel's steps with 8-bit codes
+// (s = max|W| / 127 as an IEEE fp32 division, round half to even, clamp to
+// [-128, 127], stored offset by 128), four codes per int32 along K.
+__global__ __launch_bounds__(256) void pack8_kernel(const float *__restrict__ W, int64_t N, int G,
+                                                    int32_t *__restrict__ packed,
+                                                    uint16_t *__restrict__ scales) {
+  const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t g = blockIdx.y;
+  if (n >= N) return;
+  const float *col = W + g * G * N + n;
+  float amax = 0.0f;
+#pragma unroll 16
+  for (int k = 0; k < G; ++k) amax = fmaxf(amax, fabsf(col[k * N]));
+  float s = __fdiv_rn(amax, 127.0f);
+  s = s < 1e-8f ? 1e-8f : s;
+#pragma unroll 2
+  for (int r = 0; r < G / 4; ++r) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float q = __builtin_rintf(__fdiv_rn(col[(4 * r + i) * N], s));
+      q = fminf(fmaxf(q, -128.0f), 127.0f);
+      word |= (uint32_t)((int)q + 128) << (8 * i);
+    }
+    packed[(g * (G / 4) + r) * N + n] = (int32_t)word;
+  }
+  scales[g * N + n] = to_half_bits(s);
+}
+
+hipError_t launch_pack8(const float *W, int64_t K, int64_t N, int G, int32_t *packed,
+                        uint16_t *scales, hipStream_t s) {
+  dim3 grid((unsigned)ceil_div(N, 256), (unsigned)(K / G));
+  hipLaunchKernelGGL(pack8_kernel, grid, dim3(256), 0, s, W, N, G, packed, scales);
+  return hipGetLastError();
+}
+
+// Bytes (k0, k1, k2, k3) of a canonical word go to byte slots (0, 2, 1, 3):
+// swapping the middle two bytes, its own inverse.
+__device__ __forceinline__ uint32_t swap_mid_bytes(uint32_t w) {
+  return (w & 0xFF0000FFu) | ((w & 0x0000FF00u) << 8) | ((w & 0x00FF0000u) >> 8);
+}
+
+// One thread per repacked 16-byte vector (t, q, j, l): canonical rows
+// r = 16q + 8h + 4j + i (i = 0..3) of column 32t + c, l = 32h + c.
+template <bool FORWARD>
+__global__ __launch_bounds__(256) void repack8_kernel(const int32_t *__restrict__ packed,
+                                                      uint4_t *__restrict__ rw,
+                                                      int32_t *__restrict__ packed_out,
+                                                      int64_t N, int64_t KT, int64_t NS) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;  // ((t*KT + q)*2 + j)*64 + l
+  if (idx >= NS * KT * 128) return;
+  const int l = (int)(idx & 63);
+  const int j = (int)((idx >> 6) & 1);
+  const int64_t tq = idx >> 7;
+  const int64_t q = tq % KT, t = tq / KT;
+  const int h = l >> 5, c = l & 31;
+  const int64_t n = t * kStrip + c;
+  const int64_t r0 = 16 * q + 8 * h + 4 * j;
+  if (FORWARD) {
+    uint4_t v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      v[i] = n < N ? swap_mid_bytes((uint32_t)packed[(r0 + i) * N + n]) : 0x80808080u;
+    rw[idx] = v;
+  } else {
+    if (n >= N) return;
+    const uint4_t v = rw[idx];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) packed_out[(r0 + i) * N + n] = (int32_t)swap_mid_bytes(v[i]);
+  }
+}
+
+hipError_t launch_repack8(const int32_t *packed, const uint16_t *scales, int64_t K, int64_t N,
+                          int G, void *rw, void *rs, hipStream_t s) {
+  int64_t KT, KG, KG8, NS;
+  repack_geometry(K, N, G, KT, KG, KG8, NS);
+  hipLaunchKernelGGL(repack8_kernel<true>, dim3((unsigned)ceil_div(NS * KT * 128, 256)),
+                     dim3(256), 0, s, packed, (uint4_t *)rw, (int32_t *)nullptr, N, KT, NS);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // The scales are laid out as for INT4 weights: the scale half of repack_kernel.
+  const int64_t sblocks = ceil_div(NS * KG8 * 32, 256);
+  hipLaunchKernelGGL(repack_kernel<true>, dim3((unsigned)sblocks), dim3(256), 0, s,
+                     (const int32_t *)nullptr, scales, (uint4_t *)nullptr, (uint16_t *)rs,
+                     (int32_t *)nullptr, (uint16_t *)nullptr, N, KT, KG, KG8, NS, (int64_t)0);
+  return hipGetLastError();
+}
+
+hipError_t launch_unrepack8(const void *rw, const void *rs, int64_t K, int64_t N, int G,
+                            int32_t *packed, uint16_t *scales, hipStream_t s) {
+  int64_t KT, KG, KG8, NS;
+  repack_geometry(K, N, G, KT, KG, KG8, NS);
+  hipLaunchKernelGGL(repack8_kernel<false>, dim3((unsigned)ceil_div(NS * KT * 128, 256)),
+                     dim3(256), 0, s, (const int32_t *)nullptr, (uint4_t *)rw, packed, N, KT, NS);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t sblocks = ceil_div(NS * KG8 * 32, 256);
+  hipLaunchKernelGGL(repack_kernel<false>, dim3((unsigned)sblocks), dim3(256), 0, s,
+                     (const int32_t *)nullptr, (const uint16_t *)nullptr, (uint4_t *)nullptr,
+                     (uint16_t *)rs, (int32_t *)nullptr, scales, N, KT, KG, KG8, NS, (int64_t)0);
+  return hipGetLastError();
+}
+
+// Dequantize INT8 weights: one thread per lane position (t, q, l), its two
+// vectors = 32 consecutive k of one column; weights fp16((u - 128) s) or
+// bf16((u - 128) s), each rounded once.  CANONICAL writes W [K, N]; otherwise
+// the fragment order of dequant_kernel (the dense tier's operand layout).
+template <bool CANONICAL, bool BF>
+__global__ __launch_bounds__(256) void dequant8_kernel(const uint4_t *__restrict__ rw,
+                                                       const uint16_t *__restrict__ rs,
+                                                       uint16_t *__restrict__ W16, int64_t N,
+                                                       int64_t KT, int64_t KG8, int64_t NS,
+                                                       int gshift) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (t*KT + q)*64 + l
+  if (idx >= NS * KT * 64) return;
+  const int l = (int)(idx & 63);
+  const int64_t tq = idx >> 6;
+  const int64_t q = tq % KT, t = tq / KT;
+  const int h = l >> 5, c = l & 31;
+  const int64_t n = t * kStrip + c;
+  const int g = (int)((64 * q + 32 * h) >> gshift);
+  const uint16_t s16 = rs[scale_index(t, KG8, c, g)];
+  const uint4_t v0 = rw[tq * 128 + l], v1 = rw[tq * 128 + 64 + l];
+  const Dequant dq;
+  auto run = [&](int jj) {  // k offsets 8 jj .. +7 of the lane's 32
+    const uint4_t &v = jj < 2 ? v0 : v1;
+    const int w = (jj & 1) * 2;
+    return dq.scaled8_bits<BF>(v[w], v[w + 1], s16);
+  };
+  if (CANONICAL) {
+    if (n >= N) return;
+    const int64_t k0 = 64 * q + 32 * h;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const uint4_t w = run(jj);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        W16[(k0 + 8 * jj + i) * N + n] = (uint16_t)(w[i >> 1] >> (16 * (i & 1)));
+    }
+  } else {
+    uint4_t *out = (uint4_t *)W16 + idx * 4;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) out[jj] = run(jj);
+  }
+}
+
+template <bool CANONICAL>
+static hipError_t launch_dequant8(const void *rw, const void *rs, int64_t K, int64_t N, int G,
+                                  bool bf16, uint16_t *W, hipStream_t s) {
+  int64_t KT, KG, KG8, NS;
+  repack_geometry(K, N, G, KT, KG, KG8, NS);
+  const int gshift = group_shift(K, G);
+  const dim3 grid((unsigned)ceil_div(NS * KT * 64, 256));
+  if (bf16)
+    hipLaunchKernelGGL((dequant8_kernel<CANONICAL, true>), grid, dim3(256), 0, s,
+                       (const uint4_t *)rw, (const uint16_t *)rs, W, N, KT, KG8, NS, gshift);
+  else
+    hipLaunchKernelGGL((dequant8_kernel<CANONICAL, false>), grid, dim3(256), 0, s,
+                       (const uint4_t *)rw, (const uint16_t *)rs, W, N, KT, KG8, NS, gshift);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant8_canonical(const void *rw, const void *rs, int64_t K, int64_t N, int G,
+                                     bool bf16, uint16_t *W, hipStream_t s) {
+  return launch_dequant8<true>(rw, rs, K, N, G, bf16, W, s);
+}
+
+hipError_t launch_dequant8_fragment(const void *rw, const void *rs, int64_t K, int64_t N, int G,
+                                    bool bf16, uint16_t *Wf, hipStream_t s) {
+  return launch_dequant8<false>(rw, rs, K, N, G, bf16, Wf, s);
+}
+
+// ---------------------------------------------------------------------------
 // Prescaled zero rows (Swordfish page, blog.alpindale.net, section "The packed
 // format": AWQ zero points enter as rows shaped like the scales holding
 // (8 - zp) * s).  One thread per (strip, group octet, column), as the scale

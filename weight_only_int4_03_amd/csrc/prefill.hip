@@ -774,7 +774,11 @@ hipError_t launch_prefill(const Problem &p, void *workspace, hipStream_t s) {
 }
 
 int tiled_describe(const Problem &p, bool dense, char *buf, size_t n) {
-  const char *pre = !dense ? "" : (p.bf16 ? "dequant_kernel<false, true>; " : "dequant_kernel<false, false>; ");
+  const char *pre = !dense ? ""
+                   : p.bits == 8 ? (p.bf16 ? "dequant8_kernel<false, true>; "
+                                           : "dequant8_kernel<false, false>; ")
+                                 : (p.bf16 ? "dequant_kernel<false, true>; "
+                                           : "dequant_kernel<false, false>; ");
   const char *d = dense ? "true" : "false", *sw = p.swiglu ? "true" : "false";
   const char *bf = p.bf16 ? "true" : "false";
   const char *zp = p.zp && !dense ? "true" : "false";
@@ -803,7 +807,9 @@ hipError_t launch_dense(const Problem &p, void *workspace, hipStream_t s) {
   if (workspace == nullptr) return hipErrorInvalidValue;
   void *w16f = workspace;
   hipError_t e =
-      launch_dequant_fragment(p.rw, p.rs, p.rz, p.K, p.N, p.G, p.bf16, (uint16_t *)w16f, s);
+      p.bits == 8
+          ? launch_dequant8_fragment(p.rw, p.rs, p.K, p.N, p.G, p.bf16, (uint16_t *)w16f, s)
+          : launch_dequant_fragment(p.rw, p.rs, p.rz, p.K, p.N, p.G, p.bf16, (uint16_t *)w16f, s);
   if (e != hipSuccess) return e;
   Prefill2Config c;
   if (prefill2_config(p, true, c)) return launch_prefill2_m<4, 2, true>(p, w16f, c, nullptr, s);

@@ -32,6 +32,7 @@ PATHS = {"auto": PATH_AUTO, "decode": PATH_DECODE, "prefill": PATH_PREFILL, "den
 FLAG_SWIGLU = 0x10
 FLAG_BF16 = 0x20
 FLAG_ZP = 0x40
+FLAG_INT8 = 0x80
 G = 128
 
 
@@ -59,6 +60,12 @@ _SIGNATURES = {
     "w4a16_dequant": ([_p, _p, _i64, _i64, _int, _p, _p], _int),
     "w4a16_dequant_bf16": ([_p, _p, _i64, _i64, _int, _p, _p], _int),
     "w4a16_zero_rows": ([_p, _p, _i64, _i64, _int, _p, _p], _int),
+    "w4a16_pack_int8": ([_p, _i64, _i64, _int, _p, _p, _p], _int),
+    "w4a16_repacked_weight_bytes_int8": ([_i64, _i64, _int], _i64),
+    "w4a16_repack_int8": ([_p, _p, _i64, _i64, _int, _p, _p, _p], _int),
+    "w4a16_unrepack_int8": ([_p, _p, _i64, _i64, _int, _p, _p, _p], _int),
+    "w4a16_dequant_int8": ([_p, _p, _i64, _i64, _int, _int, _p, _p], _int),
+    "w4a16_gemm_int8": ([_p, _i64, _i64, _p, _p, _i64, _int, _p, _p, _int, _p, _i64, _p], _int),
     "w4a16_dequant_zp": ([_p, _p, _p, _i64, _i64, _int, _int, _p, _p], _int),
     "w4a16_gemm_zp": ([_p, _i64, _i64, _p, _p, _p, _i64, _int, _p, _p, _int, _p, _i64, _p],
                       _int),
@@ -164,12 +171,13 @@ class RepackedWeight:
     """Repacked device buffers of one [K,N] weight (built by :func:`repack`;
     rz: prescaled zero rows of asymmetric weights, see :func:`zero_rows`)."""
 
-    def __init__(self, rw, rs, K: int, N: int, G: int = G, rz=None):
+    def __init__(self, rw, rs, K: int, N: int, G: int = G, rz=None, bits: int = 4):
         self.rw, self.rs, self.K, self.N, self.G, self.rz = rw, rs, K, N, G, rz
+        self.bits = bits  # 4: INT4 codes; 8: INT8 codes (see repack_int8)
 
     def clone(self) -> "RepackedWeight":
         return RepackedWeight(self.rw.clone(), self.rs.clone(), self.K, self.N, self.G,
-                              None if self.rz is None else self.rz.clone())
+                              None if self.rz is None else self.rz.clone(), self.bits)
 
     @property
     def nbytes(self) -> int:
@@ -196,13 +204,43 @@ def repack(packed, scales, G: int = G, stream=None) -> RepackedWeight:
 
 
 def unrepack(w: RepackedWeight, G: int | None = None, stream=None):
+    """Canonical device (packed, scales) of repacked weights (INT8 weights:
+    packed [K/4,N])."""
     torch = _torch()
     G = w.G if G is None else G
-    packed = torch.empty((w.K // 8, w.N), dtype=torch.int32, device=w.rw.device)
+    per = 4 if w.bits == 8 else 8
+    packed = torch.empty((w.K // per, w.N), dtype=torch.int32, device=w.rw.device)
     scales = torch.empty((w.K // G, w.N), dtype=torch.int16, device=w.rw.device)
-    _check(lib().w4a16_unrepack(_ptr(w.rw), _ptr(w.rs), w.K, w.N, G, _ptr(packed),
-                                _ptr(scales), _stream(stream)))
+    fn = lib().w4a16_unrepack_int8 if w.bits == 8 else lib().w4a16_unrepack
+    _check(fn(_ptr(w.rw), _ptr(w.rs), w.K, w.N, G, _ptr(packed), _ptr(scales), _stream(stream)))
     return packed, scales
+
+
+def pack_int8(W, G: int = G, stream=None):
+    """Quantize + pack a device fp32 [K,N] tensor to INT8 codes:
+    (packed int32 [K/4,N], scales int16 [K/G,N])."""
+    torch = _torch()
+    assert W.is_cuda and W.dtype == torch.float32 and W.is_contiguous()
+    K, N = W.shape
+    packed = torch.empty((K // 4, N), dtype=torch.int32, device=W.device)
+    scales = torch.empty((K // G, N), dtype=torch.int16, device=W.device)
+    _check(lib().w4a16_pack_int8(_ptr(W), K, N, G, _ptr(packed), _ptr(scales), _stream(stream)))
+    return packed, scales
+
+
+def repack_int8(packed, scales, G: int = G, stream=None) -> RepackedWeight:
+    """Canonical INT8 device (packed [K/4,N] int32, scales [K/G,N] fp16 bits) -> repacked."""
+    torch = _torch()
+    assert packed.is_cuda and packed.dtype == torch.int32 and packed.is_contiguous()
+    assert scales.is_cuda and scales.element_size() == 2 and scales.is_contiguous()
+    K, N = packed.shape[0] * 4, packed.shape[1]
+    wb = _check(lib().w4a16_repacked_weight_bytes_int8(K, N, G))
+    sb = _check(lib().w4a16_repacked_scale_bytes(K, N, G))
+    rw = torch.empty(wb, dtype=torch.uint8, device=packed.device)
+    rs = torch.empty(sb, dtype=torch.uint8, device=packed.device)
+    _check(lib().w4a16_repack_int8(_ptr(packed), _ptr(scales), K, N, G, _ptr(rw), _ptr(rs),
+                                   _stream(stream)))
+    return RepackedWeight(rw, rs, K, N, G, bits=8)
 
 
 def zero_rows(w: RepackedWeight, scales, zeros, stream=None) -> RepackedWeight:
@@ -226,6 +264,10 @@ def dequant(w: RepackedWeight, G: int | None = None, stream=None, bf16: bool = F
     G = w.G if G is None else G
     W = torch.empty((w.K, w.N), dtype=torch.bfloat16 if bf16 else torch.float16,
                     device=w.rw.device)
+    if w.bits == 8:
+        _check(lib().w4a16_dequant_int8(_ptr(w.rw), _ptr(w.rs), w.K, w.N, G,
+                                        FLAG_BF16 if bf16 else 0, _ptr(W), _stream(stream)))
+        return W
     if w.rz is not None:
         _check(lib().w4a16_dequant_zp(_ptr(w.rw), _ptr(w.rs), _ptr(w.rz), w.K, w.N, G,
                                       FLAG_BF16 if bf16 else 0, _ptr(W), _stream(stream)))
@@ -235,9 +277,9 @@ def dequant(w: RepackedWeight, G: int | None = None, stream=None, bf16: bool = F
     return W
 
 
-def _flags(path, swiglu: bool, bf16: bool, zp: bool = False) -> int:
+def _flags(path, swiglu: bool, bf16: bool, zp: bool = False, int8: bool = False) -> int:
     return ((PATHS[path] if isinstance(path, str) else int(path)) | (FLAG_SWIGLU if swiglu else 0)
-            | (FLAG_BF16 if bf16 else 0) | (FLAG_ZP if zp else 0))
+            | (FLAG_BF16 if bf16 else 0) | (FLAG_ZP if zp else 0) | (FLAG_INT8 if int8 else 0))
 
 
 def gemm(A, w: RepackedWeight, swiglu: bool = False, path: str | int = "auto", out=None,
@@ -260,7 +302,11 @@ def gemm(A, w: RepackedWeight, swiglu: bool = False, path: str | int = "auto", o
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if rowscale is not None:
         assert rowscale.is_cuda and rowscale.dtype == torch.float32 and rowscale.numel() == M
-    if w.rz is not None:
+    if w.bits == 8:
+        _check(lib().w4a16_gemm_int8(_ptr(A), M, K, _ptr(w.rw), _ptr(w.rs), w.N, G,
+                                     _ptr(rowscale), _ptr(out), flags, _ptr(workspace), ws_bytes,
+                                     _stream(stream)))
+    elif w.rz is not None:
         _check(lib().w4a16_gemm_zp(_ptr(A), M, K, _ptr(w.rw), _ptr(w.rs), _ptr(w.rz), w.N, G,
                                    _ptr(rowscale), _ptr(out), flags, _ptr(workspace), ws_bytes,
                                    _stream(stream)))
@@ -311,20 +357,22 @@ def gemm_swiglu(A, w: RepackedWeight, out=None, G: int | None = None, stream=Non
 
 
 def workspace_bytes(M: int, K: int, N: int, swiglu: bool = False, path: str | int = "auto",
-                    G: int = G, bf16: bool = False, zp: bool = False) -> int:
-    return _check(lib().w4a16_gemm_workspace_bytes(M, K, N, G, _flags(path, swiglu, bf16, zp)))
+                    G: int = G, bf16: bool = False, zp: bool = False, int8: bool = False) -> int:
+    return _check(lib().w4a16_gemm_workspace_bytes(M, K, N, G,
+                                                   _flags(path, swiglu, bf16, zp, int8)))
 
 
-def select_path(M: int, K: int, N: int, swiglu: bool = False, G: int = G) -> str:
-    code = _check(lib().w4a16_select_path(M, K, N, G, FLAG_SWIGLU if swiglu else 0))
+def select_path(M: int, K: int, N: int, swiglu: bool = False, G: int = G,
+                int8: bool = False) -> str:
+    code = _check(lib().w4a16_select_path(M, K, N, G, _flags(0, swiglu, False, False, int8)))
     return {v: k for k, v in PATHS.items()}[code]
 
 
 def describe(M: int, K: int, N: int, swiglu: bool = False, path: str | int = "auto",
-             G: int = G, bf16: bool = False, zp: bool = False) -> str:
+             G: int = G, bf16: bool = False, zp: bool = False, int8: bool = False) -> str:
     """The kernel launches (profiler names and grids) a GEMM of this shape makes."""
     buf = ctypes.create_string_buffer(512)
-    _check(lib().w4a16_describe(M, K, N, G, _flags(path, swiglu, bf16, zp),
+    _check(lib().w4a16_describe(M, K, N, G, _flags(path, swiglu, bf16, zp, int8),
                                 ctypes.addressof(buf), len(buf)))
     return buf.value.decode()
 
@@ -372,3 +420,12 @@ def load_weight_zp(q: np.ndarray, scales: np.ndarray, zeros: np.ndarray, device=
     sd = torch.from_numpy(np.ascontiguousarray(scales, dtype=np.uint16).view(np.int16)).to(device)
     zd = torch.from_numpy(np.ascontiguousarray(zeros, dtype=np.uint8)).to(device)
     return zero_rows(repack(packed, sd, G), sd, zd)
+
+
+def load_weight_int8(W_host: np.ndarray, device="cuda", G: int = G) -> RepackedWeight:
+    """Host fp32 W -> device, INT8 quantize+pack on the GPU, repack."""
+    torch = _torch()
+    Wd = torch.from_numpy(np.ascontiguousarray(W_host, dtype=np.float32)).to(device)
+    packed, scales = pack_int8(Wd, G)
+    del Wd
+    return repack_int8(packed, scales, G)
