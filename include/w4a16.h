@@ -202,9 +202,10 @@ int w4a16_dequant_int8(const void *rw_d, const void *rs_d, int64_t K, int64_t N,
 /* GEMM on INT8 weights: out[m,n] = r_m * sum_k A[m,k] * w[k,n], FP32
  * accumulation, with w = (q - 128) * s (fp16 activations: the product with
  * the exact weight; bf16 activations: with bf16((q - 128) * s)) and r_m =
- * rowscale_d[m] or 1 when rowscale_d is NULL.  M <= 32 streams the weights
- * (the decode path); larger M, and an explicit W4A16_PATH_PREFILL, run the
- * dense tier (dequantize into the workspace, then the dense fp16 GEMM).
+ * rowscale_d[m] or 1 when rowscale_d is NULL.  The same paths as INT4
+ * weights: M <= 32 streams the weights (decode), larger M runs the fused
+ * MFMA kernel (prefill; operands beyond its 32-bit offsets fall back to the
+ * dense tier), W4A16_PATH_DENSE dequantizes into the workspace first.
  * Flags, workspace, outputs and errors as w4a16_gemm_ex (W4A16_FLAG_INT8 is
  * implied and may be given). */
 int w4a16_gemm_int8(const uint16_t *A_d, int64_t M, int64_t K, const void *rw_d, const void *rs_d,

@@ -123,7 +123,7 @@ def test_int8_argument_errors_without_gpu():
     assert L.w4a16_gemm_int8(0, 0, 4096, 0, 0, 4096, 128, 0, 0, 0, 0, 0, 0) == w4a16.OK
     assert _gemm_ex(flags=w4a16.FLAG_INT8) == w4a16.ERR_INVALID    # only w4a16_gemm_int8 takes it
     assert w4a16.lib().w4a16_repacked_weight_bytes_int8(4096, 4104, 128) == 4096 * 4128
-    assert w4a16.workspace_bytes(100, 4096, 4096, int8=True) >= 4096 * 4096 * 2   # dense scratch
+    assert w4a16.workspace_bytes(100, 4096, 4096, path="dense", int8=True) >= 4096 * 4096 * 2
     buf = ctypes.create_string_buffer(64)
     assert L.w4a16_describe(1, 4096, 4096, 128, w4a16.FLAG_INT8 | w4a16.FLAG_ZP,
                             ctypes.addressof(buf), 64) == w4a16.ERR_UNSUPPORTED
@@ -185,13 +185,13 @@ def test_describe_names_the_launches():
     assert " workgroups=256 " in d and d.endswith("ks=1"), d
     d = w4a16.describe(24, 4096, 4096)
     assert d.startswith("decode_kernel<32, 1, ") and d.split(">")[0].endswith("false, false, 4"), d
-    assert "prefill2_kernel<4, 2, 4, 2, false, true, false, false>" in w4a16.describe(
+    assert "prefill2_kernel<4, 2, 4, 2, false, true, false, false, 4>" in w4a16.describe(
         4096, 4096, 28672, swiglu=True)
-    assert "prefill2_kernel<4, 2, 4, 2, false, true, true, false>" in w4a16.describe(
+    assert "prefill2_kernel<4, 2, 4, 2, false, true, true, false, 4>" in w4a16.describe(
         4096, 4096, 28672, swiglu=True, bf16=True)
     # Transition batches: 64-row tiles, the eight waves side by side.
     assert w4a16.describe(256, 4096, 28672, swiglu=True).startswith(
-        "prefill2_kernel<2, 1, 8, 2, false, true, false, false> workgroups=224 threads=512 ks=1")
+        "prefill2_kernel<2, 1, 8, 2, false, true, false, false, 4> workgroups=224 threads=512 ks=1")
     assert w4a16.describe(300, 4096, 28672, swiglu=True).startswith("prefill2_kernel<4, 2, 4, 2")
     # Zero rows: decode scales before the MFMA (never the cooperative kernel),
     # prefill takes the ZP instance, the dense tier folds them into its dequant.
@@ -201,16 +201,17 @@ def test_describe_names_the_launches():
     d = w4a16.describe(4, 4096, 4096, bf16=True, zp=True)
     assert d.startswith("decode_kernel<16, 1, ") and d.split(">")[0].endswith(
         "false, true, true, true, true, 4"), d
-    # INT8 weights: the decode kernel's 8-bit instances, the dense tier above.
+    # INT8 weights: the decode and prefill kernels' 8-bit instances.
     d = w4a16.describe(1, 4096, 28672, swiglu=True, int8=True)
     assert d.startswith("decode_kernel<16, 2, ") and d.split(">")[0].endswith(", 8"), d
     d = w4a16.describe(3, 4096, 4096, bf16=True, int8=True)
     assert d.split(">")[0].endswith("false, true, true, false, true, 8"), d
-    assert w4a16.describe(100, 4096, 4096, int8=True).startswith("dequant8_kernel<false, false>; ")
-    assert w4a16.describe(100, 4096, 4096, path="prefill", int8=True).startswith("dequant8_kernel")
-    assert w4a16.select_path(100, 4096, 4096, int8=True) == "dense"
-    assert w4a16.select_path(100, 4096, 4096) == "prefill"
-    assert "prefill2_kernel<4, 2, 4, 2, false, false, false, true>" in w4a16.describe(
+    assert w4a16.describe(100, 4096, 4096, int8=True).startswith("prefill2_kernel<")
+    assert w4a16.describe(100, 4096, 4096, int8=True).split(">")[0].endswith(", 8")
+    assert w4a16.describe(100, 4096, 4096, path="dense", int8=True).startswith(
+        "dequant8_kernel<false, false>; ")
+    assert w4a16.select_path(100, 4096, 4096, int8=True) == "prefill"
+    assert "prefill2_kernel<4, 2, 4, 2, false, false, false, true, 4>" in w4a16.describe(
         4096, 4096, 4096, zp=True)
     assert w4a16.describe(4096, 4096, 4096, path="dense", zp=True).startswith(
         "dequant_kernel<false, false>; prefill")

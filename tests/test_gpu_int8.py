@@ -87,7 +87,7 @@ def test_dequant_int8_bit_exact(K, N, G, bf16):
     assert np.array_equal(got, orc().dequant8(packed, s16, G, bf16=bf16))
 
 
-@pytest.mark.parametrize("path", ["decode", "dense", "auto"])
+@pytest.mark.parametrize("path", ["decode", "prefill", "dense", "auto"])
 @pytest.mark.parametrize("M,K,N,G,swiglu,bf16", [(1, 4096, 1064, 128, False, False),
                                                  (5, 4096, 2112, 128, True, False),
                                                  (16, 2048, 1088, 64, False, True),
@@ -97,8 +97,9 @@ def test_dequant_int8_bit_exact(K, N, G, bf16):
                                                  (70, 2048, 2112, 128, True, False),
                                                  (300, 1024, 4160, 128, False, True)])
 def test_int8_each_path(path, M, K, N, G, swiglu, bf16):
-    """The decode kernel's 8-bit instances and the dense tier, fp16 and bf16,
-    several group sizes (channelwise included), SwiGLU, ragged M and N."""
+    """The decode and prefill kernels' 8-bit instances and the dense tier,
+    fp16 and bf16, several group sizes (channelwise included), SwiGLU, ragged
+    M and N."""
     gemm8_case(M, K, N, G=G, swiglu=swiglu, path=path, bf16=bf16, seed=M + N + G)
 
 
@@ -113,7 +114,7 @@ def test_int8_decode_configs(monkeypatch, half, ks):
     gemm8_case(1, 2048, 1088, path="decode", seed=7 + ks, bf16=True)
 
 
-@pytest.mark.parametrize("path", ["decode", "dense"])
+@pytest.mark.parametrize("path", ["decode", "prefill", "dense"])
 @pytest.mark.parametrize("bf16", [False, True])
 def test_int8_onehot_rows_bit_exact(path, bf16):
     """One-hot activation rows return rows of the dequantized weights exactly."""
@@ -121,7 +122,7 @@ def test_int8_onehot_rows_bit_exact(path, bf16):
     packed, s16 = synth.random_bytes(K, N, seed=11 + bf16)
     w = w4a16.repack_int8(to_dev(packed), to_dev(s16.view(np.int16)))
     Wo = orc().dequant8(packed, s16, bf16=bf16)
-    for M in (3, 40 if path == "dense" else 17):
+    for M in (3, 17 if path == "decode" else 40):
         A, ks = synth.onehot_activations(M, K, seed=M)
         if bf16:
             Ab = np.zeros((M, K), np.uint16)
@@ -134,7 +135,7 @@ def test_int8_onehot_rows_bit_exact(path, bf16):
             assert same.all(), (path, bf16, M, m, k)
 
 
-@pytest.mark.parametrize("path", ["decode", "dense"])
+@pytest.mark.parametrize("path", ["decode", "prefill", "dense"])
 def test_int8_integer_exact_inputs(path):
     """Grid weights (lossless 8-bit codes, power-of-two scales) and sparse
     ternary activations: exact sums, the correctly rounded fp16 output."""
@@ -149,17 +150,56 @@ def test_int8_integer_exact_inputs(path):
 
 
 def test_int8_with_rowscale():
-    """INT8 weights with the RMSNorm row factor, decode and dense."""
+    """INT8 weights with the RMSNorm row factor, decode, prefill and dense."""
     gemm8_case(9, 2048, 2112, swiglu=True, path="decode", seed=9, rowscale=True)
     gemm8_case(70, 2048, 1088, path="dense", seed=70, rowscale=True, bf16=True)
+    gemm8_case(300, 2048, 2112, swiglu=True, path="prefill", seed=300, rowscale=True)
+
+
+@pytest.mark.parametrize("wm", [2, 1])
+@pytest.mark.parametrize("bm,tps,ks", [(64, 1, 1), (128, 2, 4), (256, 2, 1), (64, 2, 3)])
+def test_int8_prefill_tiles(monkeypatch, wm, bm, tps, ks):
+    """The fused kernel's 8-bit instances at each row tile, wave layout,
+    pipeline step and K split."""
+    if wm == 1 and bm == 256:
+        pytest.skip("the 256-row tile keeps two waves along the rows")
+    monkeypatch.setenv("W4A16_PREFILL_BM", str(bm))
+    monkeypatch.setenv("W4A16_PREFILL_TPS", str(tps))
+    monkeypatch.setenv("W4A16_PREFILL_KS", str(ks))
+    monkeypatch.setenv("W4A16_PREFILL_WM", str(wm))
+    d = w4a16.describe(200, 4096, 2112, swiglu=True, path="prefill", int8=True)
+    assert d.startswith("prefill2_kernel<%d, %d, %d, %d" % (bm // (32 * wm), wm, 8 // wm, tps)), d
+    assert d.split(">")[0].endswith(", 8") and ("ks=%d" % ks) in d, d
+    gemm8_case(200, 4096, 2112, swiglu=True, path="prefill", seed=bm + ks + wm)
 
 
 @pytest.mark.parametrize("M,K,N,swiglu", [(1, 4096, 28672, True), (16, 14336, 4096, False),
-                                          (4096, 4096, 6144, False)])
+                                          (4096, 4096, 6144, False), (8191, 14336, 4096, False)])
 def test_int8_full_size_sampled(M, K, N, swiglu):
     """Llama-3.1-8B projection sizes on the automatic path (decode, and the
-    dense tier for a 4096-token prefill), checked on sampled rows and columns."""
+    fused prefill kernel for 4096- and 8191-token prefills), checked on
+    sampled rows and columns."""
     ncols = N // 2 if swiglu else N
     rows = sample_indices(M, 24, seed=M, edge=2) if M > 64 else None
     cols = sample_indices(ncols, 96, seed=N, edge=2)
     gemm8_case(M, K, N, swiglu=swiglu, seed=M + K, rows=rows, cols=cols)
+
+
+@pytest.mark.parametrize("wm,ks", [(1, 3), (2, 2)])
+def test_int8_prefill_split_bit_exact_integer_inputs(monkeypatch, wm, ks):
+    """Split K with uneven slices on exact sums: the FP32 partials add up to
+    the same integer multiple of 2^-10 in any order, so the fp16 output is the
+    correctly rounded exact product."""
+    monkeypatch.setenv("W4A16_PREFILL_BM", "64")
+    monkeypatch.setenv("W4A16_PREFILL_KS", str(ks))
+    monkeypatch.setenv("W4A16_PREFILL_WM", str(wm))
+    o = orc()
+    M, K, N = 130, 4608, 1088
+    W = synth.grid_weights8(K, N, p=10, seed=ks)
+    A = synth.ternary_activations(M, K, density=0.25, seed=ks)
+    w = w4a16.load_weight_int8(W)
+    d = w4a16.describe(M, K, N, path="prefill", int8=True)
+    assert ("ks=%d" % ks) in d and d.split(">")[0].endswith(", 8"), d
+    out = fp16_out(w4a16.gemm(to_dev(A), w, path="prefill")).view(np.uint16)
+    packed, s16 = o.quantize_pack8(W)
+    assert np.array_equal(out, o.f64_to_f16(o.gemm8_f64(A, packed, s16)))

@@ -160,7 +160,7 @@ def test_zp_prefill_tiles_and_k_slices(monkeypatch, bm, tps, ks):
     monkeypatch.setenv("W4A16_PREFILL_TPS", str(tps))
     monkeypatch.setenv("W4A16_PREFILL_KS", str(ks))
     d = w4a16.describe(200, 4096, 2112, swiglu=True, path="prefill", zp=True)
-    assert "prefill2_kernel<%d, 2, 4, %d, false, true, false, true>" % (bm // 64, tps) in d, d
+    assert "prefill2_kernel<%d, 2, 4, %d, false, true, false, true, 4>" % (bm // 64, tps) in d, d
     zp_case(200, 4096, 2112, swiglu=True, path="prefill", seed=bm + ks)
 
 

@@ -112,11 +112,9 @@ constexpr int64_t kDenseMinM = 1 << 30;  // the fused kernel is kept at every M 
 int select_path(int64_t M, int64_t K, int64_t N, int bits = 4) {
   (void)K;
   (void)N;
+  (void)bits;
   if (M <= kDecodeMaxM) return W4A16_PATH_DECODE;
-  // INT8 weights above decode sizes run the dense tier: the Swordfish page
-  // (section "The dense tier") finds that at int8 the halved traffic gap lets
-  // dequantize-then-dense-GEMM overtake the fused mainloop.
-  if (M >= kDenseMinM || bits == 8) return W4A16_PATH_DENSE;
+  if (M >= kDenseMinM) return W4A16_PATH_DENSE;
   return W4A16_PATH_PREFILL;
 }
 
@@ -152,10 +150,9 @@ int run_gemm(const uint16_t *A, int64_t M, int64_t K, const void *rw, const void
   if (path == W4A16_PATH_AUTO) path = select_path(M, K, N, bits);
   if (path < W4A16_PATH_DECODE || path > W4A16_PATH_DENSE)
     return fail(W4A16_ERR_INVALID, "%s: unknown path %d", who, path);
-  if (bits == 8 && path == W4A16_PATH_PREFILL) path = W4A16_PATH_DENSE;
-
   Problem p{A, M, K, N, rw, rs, out, swiglu, bf16, rowscale, G, group_shift(K, G), rz,
             rz != nullptr, bits};
+  if (path == W4A16_PATH_PREFILL && !prefill_fused_available(p)) path = W4A16_PATH_DENSE;
   const int64_t need = workspace_for(path, p);
   void *ws = workspace;
   if (need > 0) {
@@ -514,10 +511,10 @@ int64_t w4a16_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N, int G, int f
   const int bits = (flags & W4A16_FLAG_INT8) ? 8 : 4;
   int path = flags & 0xF;
   if (path == W4A16_PATH_AUTO) path = select_path(M, K, N, bits);
-  if (bits == 8 && path == W4A16_PATH_PREFILL) path = W4A16_PATH_DENSE;
   Problem p{nullptr, M, K, N, nullptr, nullptr, nullptr, (flags & W4A16_FLAG_SWIGLU) != 0,
             (flags & W4A16_FLAG_BF16) != 0, nullptr, G, group_shift(K, G), nullptr,
             (flags & W4A16_FLAG_ZP) != 0, bits};
+  if (path == W4A16_PATH_PREFILL && !prefill_fused_available(p)) path = W4A16_PATH_DENSE;
   return workspace_for(path, p);
 }
 
@@ -539,9 +536,9 @@ int w4a16_describe(int64_t M, int64_t K, int64_t N, int G, int flags, char *buf,
   if (path == W4A16_PATH_AUTO) path = select_path(M, K, N, bits);
   if (path < W4A16_PATH_DECODE || path > W4A16_PATH_DENSE)
     return fail(W4A16_ERR_INVALID, "w4a16_describe: unknown path %d", path);
-  if (bits == 8 && path == W4A16_PATH_PREFILL) path = W4A16_PATH_DENSE;
   Problem p{nullptr, M, K, N, nullptr, nullptr, nullptr, swiglu, (flags & W4A16_FLAG_BF16) != 0,
             nullptr, G, group_shift(K, G), nullptr, (flags & W4A16_FLAG_ZP) != 0, bits};
+  if (path == W4A16_PATH_PREFILL && !prefill_fused_available(p)) path = W4A16_PATH_DENSE;
   char tmp[512];
   int k;
   if (path == W4A16_PATH_DECODE) {

@@ -379,6 +379,9 @@ hipError_t launch_decode(const Problem &p, void *workspace, hipStream_t s);
 // Prefill path (fused dequant) and dense path (fp16 fragment-ordered weights).
 int64_t prefill_workspace_bytes(const Problem &p);
 hipError_t launch_prefill(const Problem &p, void *workspace, hipStream_t s);
+// False when the fused path cannot take the problem (INT8 weights outside the
+// 8-wave kernel's limits: the one-wave kernel reads INT4 codes only).
+bool prefill_fused_available(const Problem &p);
 int64_t dense_workspace_bytes(const Problem &p);
 hipError_t launch_dense(const Problem &p, void *workspace, hipStream_t s);
 int tiled_describe(const Problem &p, bool dense, char *buf, size_t n);

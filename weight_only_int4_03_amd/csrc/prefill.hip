@@ -243,7 +243,7 @@ void prefill_kernel(PrefillArgs p) {
 // offset.  Each step issues the next step's loads, then runs its MFMAs
 // (a scheduling barrier keeps the loads first), then meets the workgroup
 // barrier, which also waits for the loads.
-template <int MI, int WM, int WNW, int TPS, bool DENSE, bool SWIGLU, bool BF, bool ZP>
+template <int MI, int WM, int WNW, int TPS, bool DENSE, bool SWIGLU, bool BF, bool ZP, int BITS>
 __global__ __launch_bounds__(64 * WM * WNW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill2_kernel(PrefillArgs p) {
   // TPS: 64-k tiles per pipeline step (2 = one whole 128-k scale group).
@@ -259,7 +259,11 @@ void prefill2_kernel(PrefillArgs p) {
   constexpr int GM = 4;  // row tiles per group in the tile walk
   constexpr int CH = 8 * TPS;  // 16-byte chunks per staged activation row
   constexpr int AV = BM * CH / NT;  // activation copies per lane and step
-  constexpr int NV = DENSE ? 4 : 1;  // 16-byte vectors per lane, strip and 64-k tile
+  // BITS: 4 (INT4 codes) or 8 (INT8 codes in the repacked INT8 layout, whose
+  // two vectors per lane and tile lie 1 KiB apart).
+  static_assert(BITS == 4 || (BITS == 8 && !DENSE && !ZP), "INT8: fused, no zero rows");
+  constexpr int NV = DENSE ? 4 : (BITS == 8 ? 2 : 1);  // 16-byte vectors per lane, strip, tile
+  constexpr int VSTEP = BITS == 8 ? 1024 : 16;          // bytes between a lane's vectors
   static_assert(BM * CH % NT == 0, "activation tile split");
   static_assert((NT / CH) % 16 == 0, "swizzle period must divide the rows per copy");
   // The two activation stages are separate arrays so that the compiler can
@@ -351,7 +355,7 @@ void prefill2_kernel(PrefillArgs p) {
 #pragma unroll
   for (int w = 0; w < 2; ++w) {
     const int st = sval[w] ? strip[w] : 0;
-    w_off[w] = (st * p.KT * 64 + lane) * 16 * NV;
+    w_off[w] = st * p.KT * 64 * 16 * NV + lane * (BITS == 8 ? 16 : 16 * NV);
     s_off[w] = (st * p.KG8 * 32 + c) * 16;
   }
   auto load_b = [&](int q, BRegs &r) {
@@ -362,7 +366,7 @@ void prefill2_kernel(PrefillArgs p) {
 #pragma unroll
         for (int j = 0; j < NV; ++j)
           r.v[w][t][j] = bitcast<uint4_t>(__builtin_amdgcn_raw_buffer_load_b128(
-              rw, w_off[w] + 16 * j, (TPS * q + t) * 1024 * NV, kBufferNT));
+              rw, w_off[w] + VSTEP * j, (TPS * q + t) * 1024 * NV, kBufferNT));
     }
     if constexpr (!DENSE) {
 #pragma unroll
@@ -397,6 +401,9 @@ void prefill2_kernel(PrefillArgs p) {
       for (int w = 0; w < 2; ++w) {
         if constexpr (DENSE) {
           bf[w] = r.v[w][t][j];
+        } else if constexpr (BITS == 8) {
+          const uint4_t &v = r.v[w][t][j >> 1];
+          bf[w] = dq.scaled8_bits<BF>(v[(j & 1) * 2], v[(j & 1) * 2 + 1], (uint16_t)r.sc[w][t]);
         } else if constexpr (ZP) {
           bf[w] = dq.scaled_bits<BF, true>(r.v[w][t][0][j], (uint16_t)r.sc[w][t],
                                            (uint16_t)(r.sc[w][t] >> 16));
@@ -603,7 +610,8 @@ static int env_int(const char *name, int fallback) {
 static bool fits_buffer_offsets(const Problem &p, bool dense) {
   const int64_t limit = (int64_t)1 << 31;
   const int64_t ns = ceil_div(p.N, kStrip);
-  return p.M * p.K * 2 < limit && ns * (p.K / kTileK) * 1024 * (dense ? 4 : 1) < limit &&
+  return p.M * p.K * 2 < limit &&
+         ns * (p.K / kTileK) * 1024 * (dense ? 4 : (p.bits == 8 ? 2 : 1)) < limit &&
          ns * ceil_div(groups_of(p.K, p.G), 8) * 512 < limit && p.M * p.N * 4 < limit;
 }
 
@@ -707,7 +715,7 @@ static bool prefill2_config(const Problem &p, bool dense, Prefill2Config &c) {
   return true;
 }
 
-template <int MI, int WM, int TPS, bool DENSE, bool SWIGLU, bool BF, bool ZP>
+template <int MI, int WM, int TPS, bool DENSE, bool SWIGLU, bool BF, bool ZP, int BITS>
 static hipError_t launch_prefill2_t(const Problem &p, const void *weights, const Prefill2Config &c,
                                     void *workspace, hipStream_t s) {
   constexpr int WNW = 8 / WM;
@@ -716,7 +724,7 @@ static hipError_t launch_prefill2_t(const Problem &p, const void *weights, const
   a.KS = c.ks;
   a.nsteps = a.KT / TPS;
   a.ws = (float *)workspace;
-  hipLaunchKernelGGL((prefill2_kernel<MI, WM, WNW, TPS, DENSE, SWIGLU, BF, ZP>),
+  hipLaunchKernelGGL((prefill2_kernel<MI, WM, WNW, TPS, DENSE, SWIGLU, BF, ZP, BITS>),
                      dim3(a.tiles_m * a.tiles_n * c.ks), dim3(64 * WM * WNW), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || c.ks == 1) return e;
@@ -727,23 +735,26 @@ static hipError_t launch_prefill2_t(const Problem &p, const void *weights, const
   return hipGetLastError();
 }
 
-template <int MI, int WM, int TPS, bool DENSE, bool ZP>
+template <int MI, int WM, int TPS, bool DENSE, bool ZP, int BITS>
 static hipError_t launch_prefill2_z(const Problem &p, const void *weights,
                                     const Prefill2Config &c, void *ws, hipStream_t s) {
   if (p.bf16)
-    return p.swiglu ? launch_prefill2_t<MI, WM, TPS, DENSE, true, true, ZP>(p, weights, c, ws, s)
-                    : launch_prefill2_t<MI, WM, TPS, DENSE, false, true, ZP>(p, weights, c, ws, s);
-  return p.swiglu ? launch_prefill2_t<MI, WM, TPS, DENSE, true, false, ZP>(p, weights, c, ws, s)
-                  : launch_prefill2_t<MI, WM, TPS, DENSE, false, false, ZP>(p, weights, c, ws, s);
+    return p.swiglu
+               ? launch_prefill2_t<MI, WM, TPS, DENSE, true, true, ZP, BITS>(p, weights, c, ws, s)
+               : launch_prefill2_t<MI, WM, TPS, DENSE, false, true, ZP, BITS>(p, weights, c, ws, s);
+  return p.swiglu
+             ? launch_prefill2_t<MI, WM, TPS, DENSE, true, false, ZP, BITS>(p, weights, c, ws, s)
+             : launch_prefill2_t<MI, WM, TPS, DENSE, false, false, ZP, BITS>(p, weights, c, ws, s);
 }
 
 template <int MI, int WM, int TPS, bool DENSE>
 static hipError_t launch_prefill2_tps(const Problem &p, const void *weights,
                                       const Prefill2Config &c, void *ws, hipStream_t s) {
   if constexpr (!DENSE) {
-    if (p.zp) return launch_prefill2_z<MI, WM, TPS, DENSE, true>(p, weights, c, ws, s);
+    if (p.bits == 8) return launch_prefill2_z<MI, WM, TPS, DENSE, false, 8>(p, weights, c, ws, s);
+    if (p.zp) return launch_prefill2_z<MI, WM, TPS, DENSE, true, 4>(p, weights, c, ws, s);
   }
-  return launch_prefill2_z<MI, WM, TPS, DENSE, false>(p, weights, c, ws, s);
+  return launch_prefill2_z<MI, WM, TPS, DENSE, false, 4>(p, weights, c, ws, s);
 }
 
 template <int MI, int WM, bool DENSE>
@@ -753,6 +764,11 @@ static hipError_t launch_prefill2_m(const Problem &p, const void *weights, const
     if (c.tps == 2) return launch_prefill2_tps<MI, WM, 2, DENSE>(p, weights, c, ws, s);
   }
   return launch_prefill2_tps<MI, WM, 1, DENSE>(p, weights, c, ws, s);
+}
+
+bool prefill_fused_available(const Problem &p) {
+  Prefill2Config c;
+  return p.bits == 4 || prefill2_config(p, false, c);
 }
 
 int64_t prefill_workspace_bytes(const Problem &p) {
@@ -785,9 +801,10 @@ int tiled_describe(const Problem &p, bool dense, char *buf, size_t n) {
   Prefill2Config c;
   if (prefill2_config(p, dense, c)) {
     int k = snprintf(buf, n,
-                     "%sprefill2_kernel<%d, %d, %d, %d, %s, %s, %s, %s> workgroups=%d threads=512 "
-                     "ks=%d",
-                     pre, c.mi(), c.wm, c.wnw(), c.tps, d, sw, bf, zp, c.tiles * c.ks, c.ks);
+                     "%sprefill2_kernel<%d, %d, %d, %d, %s, %s, %s, %s, %d> workgroups=%d "
+                     "threads=512 ks=%d",
+                     pre, c.mi(), c.wm, c.wnw(), c.tps, d, sw, bf, zp, dense ? 4 : p.bits,
+                     c.tiles * c.ks, c.ks);
     if (c.ks > 1 && k > 0 && (size_t)k < n)
       k += snprintf(buf + k, n - k, "; prefill_reduce_kernel<%s, %s>", sw, bf);
     return k;
