@@ -88,13 +88,15 @@ __global__ __launch_bounds__(WC * WK * 64) void decode_coop_kernel(DecodeArgs p)
   constexpr int AROWS = RPL == 1 ? 1 : MT;     // activation rows staged (M <= AROWS)
   constexpr int AV_MAX = (AROWS * WK * 16 + NT - 1) / NT;
   constexpr int SC_N = (WC * SPW * 32 * WK + NT - 1) / NT;
-  uint4_t av[AV_MAX];
-  uint16_t scv[SC_N];
+  struct Stage {
+    uint4_t av[AV_MAX];
+    uint16_t scv[SC_N];
+  };
   const int nav = M * WK * 16;
   // Loads are unconditional (indices clamped into range) so that no register
   // is conditionally rewritten while weight loads are still in flight;
   // staged groups past the end of the K range are never consumed.
-  auto stage_load = [&](int r) {
+  auto stage_load = [&](Stage &st, int r) {
     const int g0 = gb + r * WK;
 #pragma unroll
     for (int t = 0; t < AV_MAX; ++t) {
@@ -103,8 +105,8 @@ __global__ __launch_bounds__(WC * WK * 64) void decode_coop_kernel(DecodeArgs p)
       const int row = e / (WK * 16), c = e - row * (WK * 16);
       int gg = g0 + c / 16;
       gg = gg < ge ? gg : ge - 1;
-      av[t] = *(const uint4_t *)((const char *)p.A +
-                                 ((int64_t)row * p.K + (int64_t)gg * 128) * 2 + (c & 15) * 16);
+      st.av[t] = *(const uint4_t *)((const char *)p.A +
+                                    ((int64_t)row * p.K + (int64_t)gg * 128) * 2 + (c & 15) * 16);
     }
 #pragma unroll
     for (int t = 0; t < SC_N; ++t) {
@@ -118,28 +120,28 @@ __global__ __launch_bounds__(WC * WK * 64) void decode_coop_kernel(DecodeArgs p)
       const int strip = SWIGLU && s >= SH ? base + p.up_off : base;
       int gg = g0 + wkk;
       gg = gg < ge ? gg : ge - 1;
-      scv[t] = p.rs[scale_index(strip, p.KG8, c, (gg * 128) >> p.gshift)];
+      st.scv[t] = p.rs[scale_index(strip, p.KG8, c, (gg * 128) >> p.gshift)];
     }
   };
   // Stores are unconditional too: threads past the end repeat the last
   // element, writing the same value to the same place.  (A conditional store
   // lets the compiler sink the global load next to it, where waiting for it
   // also waits for the weight loads issued in between.)
-  auto stage_store = [&](int buf) {
+  auto stage_store = [&](const Stage &st, int buf) {
     char *ab = lds + buf * abuf;
 #pragma unroll
     for (int t = 0; t < AV_MAX; ++t) {
       int e = tid + t * NT;
       e = e < nav ? e : nav - 1;
       const int row = e / (WK * 16), c = e - row * (WK * 16);
-      *(uint4_t *)(ab + row * ars + c * 16) = av[t];
+      *(uint4_t *)(ab + row * ars + c * 16) = st.av[t];
     }
     uint16_t *sb = (uint16_t *)(lds + 2 * abuf + buf * sbuf);
 #pragma unroll
     for (int t = 0; t < SC_N; ++t) {
       int e = tid + t * NT;
       e = e < WC * SPW * 32 * WK ? e : WC * SPW * 32 * WK - 1;
-      sb[e] = scv[t];
+      sb[e] = st.scv[t];
     }
   };
 
@@ -237,41 +239,64 @@ __global__ __launch_bounds__(WC * WK * 64) void decode_coop_kernel(DecodeArgs p)
   };
 
   // ---- main loop: rounds r, two per iteration (buffers 0 and 1) ----------
+  // Round r's activations and scales are loaded two rounds ahead, just
+  // before its weights, and reach LDS one round ahead.  Loads complete in
+  // issue order, so waiting for a round's staged values never waits for the
+  // weights of that round or the next, and at every barrier two rounds of
+  // weights stay in flight.  Scheduling barriers keep that issue order and
+  // keep the next round's dequantization below the workgroup barrier (hoisted
+  // above it, it would wait there for that round's weights).
+  auto round_barrier = [] {
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
   Frag f0, f1;
-  stage_load(0);
+  Stage s0, s1;
+  stage_load(s0, 0);
+  __builtin_amdgcn_sched_barrier(0);
   wload(f0, 0);
+  stage_load(s1, 1);
+  __builtin_amdgcn_sched_barrier(0);
   wload(f1, 1);
-  stage_store(0);
-  __syncthreads();
+  stage_store(s0, 0);
+  round_barrier();
   int r = 0;
-  // Steady state: rounds r, r+1 are loaded; rounds r+2, r+3 exist.
+  // Steady state: rounds r, r+1 are loaded, round r is in LDS buffer 0 and
+  // round r+1 in s1; rounds r+2, r+3 exist.
   for (; r + 4 <= R; r += 2) {
-    stage_load(r + 1);
     compute(f0, 0);
+    stage_load(s0, r + 2);
+    __builtin_amdgcn_sched_barrier(0);
     wload(f0, r + 2);
-    stage_store(1);
-    __syncthreads();
-    stage_load(r + 2);
+    stage_store(s1, 1);
+    round_barrier();
     compute(f1, 1);
+    stage_load(s1, r + 3);
+    __builtin_amdgcn_sched_barrier(0);
     wload(f1, r + 3);
-    stage_store(0);
-    __syncthreads();
+    stage_store(s0, 0);
+    round_barrier();
   }
-  // Tail: at most three rounds left (r .. R-1).
-  for (int q = 0; q < 3; ++q) {
-    if (r + q >= R) break;
-    const int buf = q & 1;
-    const bool more = r + q + 1 < R;
-    if (more) stage_load(r + q + 1);
-    const bool mine = gb + (r + q) * WK + wk < ge;
-    if (q == 1) {
-      if (mine) compute(f1, buf);
-    } else {
-      if (mine) compute(f0, buf);
-      if (q == 0 && r + 2 < R) wload(f0, r + 2);
+  // Tail: at most three rounds left (r .. R-1), in the same state.
+  if (r < R) {
+    if (gb + r * WK + wk < ge) compute(f0, 0);
+    if (r + 2 < R) {
+      stage_load(s0, r + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      wload(f0, r + 2);
     }
-    if (more) stage_store(buf ^ 1);
-    __syncthreads();
+    if (r + 1 < R) stage_store(s1, 1);
+    round_barrier();
+  }
+  if (r + 1 < R) {
+    if (gb + (r + 1) * WK + wk < ge) compute(f1, 1);
+    if (r + 2 < R) stage_store(s0, 0);
+    round_barrier();
+  }
+  if (r + 2 < R) {
+    if (gb + (r + 2) * WK + wk < ge) compute(f0, 0);
+    round_barrier();
   }
 
   // ---- cross-wave sum over wk, then epilogue or partial tile -------------
