@@ -266,6 +266,19 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
   // The prologue loads are unconditional (a wave with fewer than D groups
   // loads its last group again) so that the loop is always entered with the
   // same loads outstanding and the compiler's wait counts stay exact.
+  // After each reload the next buffer's weight registers pass through an
+  // empty asm statement that is ordered after the reload's loads: left free,
+  // the compiler hoists the next buffer's dequantization above the reload,
+  // waits there for that buffer, and the loads then arrive in batches of D
+  // instead of streaming.
+  auto after_reload = [&](Frag &f) {
+#pragma unroll
+    for (int s = 0; s < SPW; ++s)
+#pragma unroll
+      for (int x = 0; x < (MT == 16 ? NPART : 2); ++x)
+#pragma unroll
+        for (int v = 0; v < NV; ++v) asm volatile("" : "+v"(f.b[s][x][v]) : : "memory");
+  };
   if (g1 > g0) {
     Frag f[D];
 #pragma unroll
@@ -276,6 +289,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
       for (int d = 0; d < D; ++d) {
         compute(f[d]);
         load(f[d], g + d + D);
+        after_reload(f[(d + 1) % D]);
       }
     }
 #pragma unroll
