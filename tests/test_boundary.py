@@ -183,8 +183,13 @@ def test_describe_names_the_launches():
     assert d.startswith("decode_kernel<16, 1, ") and d.split(">")[0].endswith(
         "false, false, false, false, true, 4"), d     # 128 strips: half strips; INT4
     assert " workgroups=256 " in d and d.endswith("ks=1"), d
+    # 32-row tiles: the cooperative kernel, K split to fill the CUs; INT8
+    # weights keep the per-wave kernel's 8-bit instance.
     d = w4a16.describe(24, 4096, 4096)
-    assert d.startswith("decode_kernel<32, 1, ") and d.split(">")[0].endswith("false, false, 4"), d
+    assert d.startswith("decode_coop_kernel<32, 1, 2, 2, 16, false, false> workgroups=256 "), d
+    assert d.endswith("ks=4; decode_reduce_kernel<1, false, false>"), d
+    d = w4a16.describe(24, 4096, 4096, int8=True)
+    assert d.startswith("decode_kernel<32, 1, ") and d.split(">")[0].endswith("false, false, 8"), d
     assert "prefill2_kernel<4, 2, 4, 2, false, true, false, false, 4>" in w4a16.describe(
         4096, 4096, 28672, swiglu=True)
     assert "prefill2_kernel<4, 2, 4, 2, false, true, true, false, 4>" in w4a16.describe(

@@ -383,8 +383,9 @@ static int env_int(const char *name, int fallback) {
 // and K is short (or M <= 4): each half-strip workgroup reads the whole
 // activation slice for half the weights, so at larger M and long K the
 // activation loads dominate, and a grid of 1.5 workgroups per CU leaves half
-// the CUs with twice the work.  Four groups in flight instead of two above
-// M = 8.  W4A16_DECODE_HALF (0 or 1), W4A16_DECODE_WAVES (4 or 8),
+// the CUs with twice the work.  Half strips at M = 1 (fp16, symmetric INT4)
+// run four waves with four groups in flight each; everything else keeps two
+// groups in flight.  W4A16_DECODE_HALF (0 or 1), W4A16_DECODE_WAVES (4 or 8),
 // W4A16_DECODE_KS and W4A16_DECODE_DEPTH (groups loaded ahead: 2 or 4)
 // override the choice.
 static DecodeConfig decode_config(const Problem &p) {
@@ -398,12 +399,13 @@ static DecodeConfig decode_config(const Problem &p) {
   const bool half_fits = 2 * (int64_t)c.nsg <= 256 && (KG <= 64 || p.M <= 4);
   c.half = c.MT == 16 && (hv != nullptr && *hv != 0 ? *hv == '1' : half_fits);
   const int64_t units = (int64_t)c.nsg * (c.half ? 2 : 1);
-  int waves = (units < 384 || KG >= 128) ? 8 : 4;
+  const bool gemv = c.half && p.M == 1 && p.bits == 4 && !p.zp && !p.bf16;
+  int waves = gemv ? 4 : (units < 384 || KG >= 128) ? 8 : 4;
   waves = env_int("W4A16_DECODE_WAVES", waves) >= 8 ? 8 : 4;
   // LDS for the cross-wave reduction: WAVES * SPW * M * 32 floats < 64 KiB.
   while (waves > 4 && (int64_t)waves * c.SPW * p.M * 32 * 4 >= 65536) waves /= 2;
   c.WAVES = waves;
-  c.D = env_int("W4A16_DECODE_DEPTH", c.half && p.M > 8 ? 4 : 2) >= 4 ? 4 : 2;
+  c.D = env_int("W4A16_DECODE_DEPTH", gemv ? 4 : 2) >= 4 ? 4 : 2;
   // A second launch (the reduction) costs more than idle CUs unless each
   // wave still streams a long K slice: split K only for narrow, deep shapes.
   int64_t ks = (units < 256 && KG / c.WAVES >= 8) ? 2 : 1;

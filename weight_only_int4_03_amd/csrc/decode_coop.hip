@@ -394,34 +394,48 @@ static int coop_env(const char *name, int fallback) {
   return x > 0 ? x : fallback;
 }
 
-// Where the cooperative kernel wins (measured on MI355X): wide shapes, whose
-// strip groups alone fill the GPU (fused gate/up), K-heavy shapes at M >= 8
-// (K >= 24576, two K slices) and deep ones at M >= 16 (K >= 12288, four K
-// slices), where the activation rows are the larger share of load slots.
-// Narrow, short-K shapes keep the per-wave kernel.  W4A16_DECODE_COOP=0/1
+// Where the cooperative kernel wins (measured on MI355X, sweeping both
+// kernels' configurations over the Llama-8B and -70B projections):
+//  * 32-row tiles (M > 16): every shape.  Two waves per column group along
+//    K; four column groups per workgroup when there are at least 256 strip
+//    groups and the LDS allows it, else two; K is split (power of two) while
+//    the grid stays within 256 workgroups.
+//  * M <= 16: wide shapes (>= 384 strip groups: the fused gate/up
+//    projections), deep ones (K >= 24576), grids that the per-wave kernel
+//    would spread unevenly (more than 256 strip groups, not a multiple of
+//    256), and at M > 8 shapes with >= 192 strip groups or K >= 12288.  Four
+//    waves per column group along K (two when four column groups share a
+//    workgroup); the fewest column groups per workgroup that keep the grid
+//    within 256 workgroups.  M = 1 on wide shapes keeps one column group.
+// Narrow, short-K shapes at small M keep the per-wave kernel (its half-strip
+// grid fills the CUs without sharing activations).  W4A16_DECODE_COOP=0/1
 // forces the choice; W4A16_COOP_WC / _WK / _KS override the configuration.
 bool coop_config(const Problem &p, int &WC, int &WK, int &KS) {
   const int nsg = (int)(p.swiglu ? (p.N / 2 / kStrip) : ceil_div(p.N, kStrip));
   const int KG = (int)(p.K / kGroup);
+  const int SPW = p.swiglu ? 2 : 1;
   const int force = coop_env_raw("W4A16_DECODE_COOP");
   if (p.G < kGroup) return false;  // one scale per column and 128-k unit
   if (p.zp) return false;          // zero rows: decode_kernel's pre-scaled form
   if (p.bits != 4) return false;   // INT8 weights: decode_kernel's 8-bit instances
+  const bool wide = nsg >= 384, deep = KG >= 192;
+  const bool uneven = nsg > 256 && nsg % 256 != 0;
   bool use;
-  if (nsg >= 384) {
+  if (p.M > 16) {
     use = true;
-    if (p.M == 1) { WC = 1; WK = 4; KS = 1; }
-    else if (p.M <= 16) { WC = 2; WK = 4; KS = 1; }
-    else { WC = 2; WK = 2; KS = 1; }
-  } else if (KG >= 192 && p.M >= 8) {
+    WK = 2;
+    WC = nsg >= 256 && coop_lds_bytes((int)p.M, 4, 2, SPW) < 65536 ? 4 : 2;
+    KS = 1;
+    while ((int64_t)ceil_div(nsg, WC) * KS * 2 <= 256 && KG / (KS * 2) >= 8) KS *= 2;
+  } else if (p.M == 1 && wide) {
     use = true;
-    WC = 2; WK = p.M <= 16 ? 4 : 2; KS = 2;
-  } else if (KG >= 96 && p.M >= 16) {
-    use = true;
-    WC = 2; WK = p.M <= 16 ? 4 : 2; KS = 4;
+    WC = 1; WK = 4; KS = 1;
   } else {
-    use = false;
-    WC = 2; WK = 4; KS = 1;
+    use = wide || deep || uneven || (p.M > 8 && (nsg >= 192 || KG >= 96));
+    KS = deep ? 2 : (KG >= 96 && p.M > 8 ? 4 : 1);
+    WC = 1;
+    while (WC < 4 && (int64_t)ceil_div(nsg, WC) * KS > 256) WC *= 2;
+    WK = WC == 4 ? 2 : 4;
   }
   if (force == 0) return false;
   if (force == 1) use = true;
@@ -429,7 +443,6 @@ bool coop_config(const Problem &p, int &WC, int &WK, int &KS) {
   WC = coop_env("W4A16_COOP_WC", WC);
   WK = coop_env("W4A16_COOP_WK", WK);
   KS = coop_env("W4A16_COOP_KS", KS);
-  const int SPW = p.swiglu ? 2 : 1;
   static const int allowed[6][2] = {{4, 1}, {8, 1}, {2, 2}, {4, 2}, {2, 4}, {1, 4}};
   bool ok = false;
   for (auto &c : allowed) ok |= (c[0] == WC && c[1] == WK);
