@@ -134,11 +134,12 @@ def test_empty_and_single_group():
         gemm_case(3, 128, 64, path=path, W=W, weight=w, seed=2)
 
 
-COOP_CONFIGS = [(4, 1, 1), (8, 1, 1), (2, 2, 1), (4, 2, 1), (2, 4, 1), (1, 4, 1), (2, 4, 2), (1, 4, 3)]
+COOP_CONFIGS = [(4, 1, 1), (8, 1, 1), (2, 2, 1), (4, 2, 1), (2, 4, 1), (1, 4, 1), (2, 4, 2), (1, 4, 3),
+                (4, 2, 2), (4, 2, 4), (2, 2, 4)]
 
 
 @pytest.mark.parametrize("wc,wk,ks", COOP_CONFIGS)
-@pytest.mark.parametrize("M", [1, 7, 16, 32])
+@pytest.mark.parametrize("M", [1, 7, 16, 24, 32])
 @pytest.mark.parametrize("K,N,swiglu", [(1152, 1064, False), (1024, 2112, True), (2560, 4160, False)])
 def test_decode_cooperative_forced(monkeypatch, wc, wk, ks, M, K, N, swiglu):
     """The cooperative decode kernel (activations and scales staged in LDS)
@@ -165,6 +166,19 @@ def test_decode_cooperative_bit_exact_integer_inputs(monkeypatch):
     monkeypatch.setenv("W4A16_COOP_KS", "2")
     K, N = 4096, 2048
     for M in (1, 16):
+        W = synth.grid_weights(K, N, p=4, seed=M)
+        A = synth.ternary_activations(M, K, density=1.0, seed=M)
+        w = w4a16.load_weight(W)
+        out = fp16_out(w4a16.gemm(to_dev(A), w, path="decode"))
+        packed_o, s16_o = orc().quantize_pack(W)
+        C = orc().gemm_f64(A, packed_o, s16_o)
+        assert np.array_equal(out.astype(np.float64), C)
+    # 32-row tiles, four column groups per workgroup, four K slices.
+    monkeypatch.setenv("W4A16_COOP_WC", "4")
+    monkeypatch.setenv("W4A16_COOP_WK", "2")
+    monkeypatch.setenv("W4A16_COOP_KS", "4")
+    for M in (23, 32):
+        assert w4a16.describe(M, K, N, path="decode").startswith("decode_coop_kernel<32, 1, 4, 2")
         W = synth.grid_weights(K, N, p=4, seed=M)
         A = synth.ternary_activations(M, K, density=1.0, seed=M)
         w = w4a16.load_weight(W)
