@@ -176,9 +176,11 @@ def test_describe_names_the_launches():
     decode_kernel and prefill2_kernel the zero rows, and for decode_kernel the
     half-strip workgroups)."""
     d = w4a16.describe(1, 4096, 28672, swiglu=True)
-    assert d.startswith("decode_coop_kernel<16, 2, ") and d.split(">")[0].endswith("true, false")
+    assert d.startswith("decode_coop_kernel<16, 2, ") and d.split(">")[0].endswith(
+        "true, false, false"), d
     d = w4a16.describe(1, 4096, 28672, swiglu=True, bf16=True)
-    assert d.startswith("decode_coop_kernel<16, 2, ") and d.split(">")[0].endswith("true, true")
+    assert d.startswith("decode_coop_kernel<16, 2, ") and d.split(">")[0].endswith(
+        "true, true, false"), d
     d = w4a16.describe(1, 4096, 4096)
     assert d.startswith("decode_kernel<16, 1, ") and d.split(">")[0].endswith(
         "false, false, false, false, true, 4"), d     # 128 strips: half strips; INT4
@@ -186,7 +188,7 @@ def test_describe_names_the_launches():
     # 32-row tiles: the cooperative kernel, K split to fill the CUs; INT8
     # weights keep the per-wave kernel's 8-bit instance.
     d = w4a16.describe(24, 4096, 4096)
-    assert d.startswith("decode_coop_kernel<32, 1, 2, 2, 16, false, false> workgroups=256 "), d
+    assert d.startswith("decode_coop_kernel<32, 1, 2, 2, 16, false, false, false> workgroups=256 "), d
     assert d.endswith("ks=4; decode_reduce_kernel<1, false, false>"), d
     d = w4a16.describe(24, 4096, 4096, int8=True)
     assert d.startswith("decode_kernel<32, 1, ") and d.split(">")[0].endswith("false, false, 8"), d
@@ -198,11 +200,11 @@ def test_describe_names_the_launches():
     assert w4a16.describe(256, 4096, 28672, swiglu=True).startswith(
         "prefill2_kernel<2, 1, 8, 2, false, true, false, false, 4> workgroups=224 threads=512 ks=1")
     assert w4a16.describe(300, 4096, 28672, swiglu=True).startswith("prefill2_kernel<4, 2, 4, 2")
-    # Zero rows: decode scales before the MFMA (never the cooperative kernel),
+    # Zero rows: both decode kernels scale before the MFMA (ZP instances),
     # prefill takes the ZP instance, the dense tier folds them into its dequant.
     d = w4a16.describe(1, 4096, 28672, swiglu=True, zp=True)
-    assert d.startswith("decode_kernel<16, 2, ") and d.split(">")[0].endswith(
-        "true, false, true, true, false, 4"), d
+    assert d.startswith("decode_coop_kernel<16, 2, ") and d.split(">")[0].endswith(
+        "true, false, true"), d
     d = w4a16.describe(4, 4096, 4096, bf16=True, zp=True)
     assert d.startswith("decode_kernel<16, 1, ") and d.split(">")[0].endswith(
         "false, true, true, true, true, 4"), d

@@ -182,3 +182,45 @@ def test_zp_full_size_sampled(M, K, N, swiglu):
     rows = sample_indices(M, 24, seed=M, edge=2) if M > 64 else None
     cols = sample_indices(ncols, 96, seed=N, edge=2)
     zp_case(M, K, N, swiglu=swiglu, seed=M + K, rows=rows, cols=cols)
+
+
+@pytest.mark.parametrize("wc,wk,ks", [(1, 4, 1), (2, 4, 2), (4, 2, 1), (2, 2, 4), (4, 2, 4), (8, 1, 3)])
+@pytest.mark.parametrize("M", [1, 7, 16, 24, 32])
+@pytest.mark.parametrize("bf16", [False, True])
+def test_zp_cooperative_decode(monkeypatch, wc, wk, ks, M, bf16):
+    """The cooperative decode kernel's zero-row instances (zero rows staged in
+    LDS beside the scales) in several configurations, with K splits that leave
+    partial rounds, gate/up with an odd number of strips (N = 2112)."""
+    monkeypatch.setenv("W4A16_DECODE_COOP", "1")
+    monkeypatch.setenv("W4A16_COOP_WC", str(wc))
+    monkeypatch.setenv("W4A16_COOP_WK", str(wk))
+    monkeypatch.setenv("W4A16_COOP_KS", str(ks))
+    swiglu = (wc + M) % 2 == 1
+    K, N = (1152, 2112) if swiglu else (2560, 1064)
+    d = w4a16.describe(M, K, N, swiglu, path="decode", bf16=bf16, zp=True)
+    if M <= 16:   # at M > 16 some configurations need more than 64 KiB of LDS and fall back
+        assert d.startswith("decode_coop_kernel") and d.split(">")[0].endswith(", true"), d
+    zp_case(M, K, N, swiglu=swiglu, path="decode", bf16=bf16, seed=wc * 100 + wk * 10 + ks + M)
+
+
+def test_zp_cooperative_integer_exact(monkeypatch):
+    """Integer-exact inputs through the cooperative zero-row instances with a
+    K split: the correctly rounded exact product, bit for bit."""
+    o = orc()
+    monkeypatch.setenv("W4A16_DECODE_COOP", "1")
+    for (wc, wk, ks), M in [((2, 4, 2), 1), ((2, 4, 2), 16), ((4, 2, 4), 32)]:
+        monkeypatch.setenv("W4A16_COOP_WC", str(wc))
+        monkeypatch.setenv("W4A16_COOP_WK", str(wk))
+        monkeypatch.setenv("W4A16_COOP_KS", str(ks))
+        K, N, G = 4096, 2048, 128
+        rng = np.random.default_rng(M)
+        packed, _ = synth.random_words(K, N, seed=M, group=G)
+        s16 = np.exp2(rng.integers(-6, -3, (K // G, N))).astype(np.float16).view(np.uint16)
+        zp = synth.zero_points(K // G, N, seed=M)
+        sd = to_dev(s16.view(np.int16))
+        w = w4a16.zero_rows(w4a16.repack(to_dev(packed), sd, G), sd, to_dev(zp))
+        A = synth.ternary_activations(M, K, density=0.1, seed=M)
+        assert w4a16.describe(M, K, N, path="decode", zp=True).startswith("decode_coop_kernel")
+        out = fp16_out(w4a16.gemm(to_dev(A), w, path="decode")).view(np.uint16)
+        C = o.gemm_w16_f64(A, o.dequant_zp(packed, s16, o.zero_rows(s16, zp), G))
+        assert np.array_equal(out, o.f64_to_f16(C)), (wc, wk, ks, M)

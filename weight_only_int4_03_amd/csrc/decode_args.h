@@ -58,7 +58,7 @@ hipError_t launch_decode_reduce(const DecodeArgs &a, bool swiglu, bool bf16, hip
 // environment (W4A16_COOP_WC, W4A16_COOP_WK, W4A16_COOP_KS); false if the
 // configuration does not fit.
 bool coop_config(const Problem &p, int &WC, int &WK, int &KS);
-size_t coop_lds_bytes(int M, int WC, int WK, int SPW);
+size_t coop_lds_bytes(int M, int WC, int WK, int SPW, bool zp);
 hipError_t launch_decode_coop(const Problem &p, void *workspace, int WC, int WK, int KS,
                               hipStream_t s);
 

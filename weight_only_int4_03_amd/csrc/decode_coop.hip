@@ -36,7 +36,7 @@ struct CoopFrag {
   uint4_t b[SPW][2];  // weight vectors of the wave's strips for one group
 };
 
-template <int MT, int SPW, int WC, int WK, int RPL, bool SWIGLU, bool BF>
+template <int MT, int SPW, int WC, int WK, int RPL, bool SWIGLU, bool BF, bool ZP>
 __global__ __launch_bounds__(WC * WK * 64) void decode_coop_kernel(DecodeArgs p) {
   constexpr int NW = WC * WK, NT = NW * 64, D = 2;
   constexpr int SH = SWIGLU ? SPW / 2 : SPW;
@@ -49,7 +49,7 @@ __global__ __launch_bounds__(WC * WK * 64) void decode_coop_kernel(DecodeArgs p)
   const int M = p.M;
   const int ars = WK * 256 + 16;               // bytes per staged activation row
   const int abuf = M * ars;                    // bytes per activation buffer
-  const int sbuf = WC * SPW * 32 * WK * 2;     // bytes per scale buffer
+  const int sbuf = (ZP ? 2 : 1) * WC * SPW * 32 * WK * 2;  // bytes per scale (+ zero row) buffer
   char *lds = (char *)smem;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -91,6 +91,7 @@ __global__ __launch_bounds__(WC * WK * 64) void decode_coop_kernel(DecodeArgs p)
   struct Stage {
     uint4_t av[AV_MAX];
     uint16_t scv[SC_N];
+    uint16_t zsv[ZP ? SC_N : 1];
   };
   const int nav = M * WK * 16;
   // Loads are unconditional (indices clamped into range) so that no register
@@ -120,7 +121,9 @@ __global__ __launch_bounds__(WC * WK * 64) void decode_coop_kernel(DecodeArgs p)
       const int strip = SWIGLU && s >= SH ? base + p.up_off : base;
       int gg = g0 + wkk;
       gg = gg < ge ? gg : ge - 1;
-      st.scv[t] = p.rs[scale_index(strip, p.KG8, c, (gg * 128) >> p.gshift)];
+      const int64_t si = scale_index(strip, p.KG8, c, (gg * 128) >> p.gshift);
+      st.scv[t] = p.rs[si];
+      if constexpr (ZP) st.zsv[t] = p.rz[si];
     }
   };
   // Stores are unconditional too: threads past the end repeat the last
@@ -142,6 +145,7 @@ __global__ __launch_bounds__(WC * WK * 64) void decode_coop_kernel(DecodeArgs p)
       int e = tid + t * NT;
       e = e < WC * SPW * 32 * WK ? e : WC * SPW * 32 * WK - 1;
       sb[e] = st.scv[t];
+      if constexpr (ZP) sb[WC * SPW * 32 * WK + e] = st.zsv[t];
     }
   };
 
@@ -186,27 +190,30 @@ __global__ __launch_bounds__(WC * WK * 64) void decode_coop_kernel(DecodeArgs p)
 #pragma unroll
         for (int j = 0; j < 4; ++j) a[4 * x + j] = *(const uint4_t *)(ab + x * 128 + j * 16);
     }
-    if constexpr (BF) {
-      // bf16: weights scaled and rounded before the MFMA (see Dequant).
+    if constexpr (BF || ZP) {
+      // bf16, and weights with zero rows: scaled (and shifted) and rounded
+      // before the MFMA, which accumulates straight into the FP32 tile.
 #pragma unroll
       for (int s = 0; s < SPW; ++s) {
 #pragma unroll
         for (int part = 0; part < NPART; ++part) {
           const int col = MT == 16 ? 16 * part + c16 : c32;
-          const Dequant::BScale bs(sb[((wc * SPW + s) * 32 + col) * WK + wk]);
+          const int si = ((wc * SPW + s) * 32 + col) * WK + wk;
+          const uint16_t s16 = sb[si];
+          const uint16_t z16 = ZP ? sb[WC * SPW * 32 * WK + si] : 0;
+          auto wop = [&](uint32_t w) -> uint4_t {
+            return dq.scaled_bits<BF, ZP>(w, s16, z16);
+          };
           if constexpr (MT == 16) {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-              acc[s][part] = mfma16<true>(
-                  a[j], bitcast<uint4_t>(dq.scaled_bf16(f.b[s][part][j], bs)), acc[s][part]);
+              acc[s][part] = mfma16<BF>(a[j], wop(f.b[s][part][j]), acc[s][part]);
           } else {
 #pragma unroll
             for (int x = 0; x < 2; ++x)
 #pragma unroll
               for (int j = 0; j < 4; ++j)
-                acc[s][part] = mfma32<true>(a[4 * x + j],
-                                            bitcast<uint4_t>(dq.scaled_bf16(f.b[s][x][j], bs)),
-                                            acc[s][part]);
+                acc[s][part] = mfma32<BF>(a[4 * x + j], wop(f.b[s][x][j]), acc[s][part]);
           }
         }
       }
@@ -342,42 +349,43 @@ __global__ __launch_bounds__(WC * WK * 64) void decode_coop_kernel(DecodeArgs p)
 // ---------------------------------------------------------------------------
 // Host side.
 
-size_t coop_lds_bytes(int M, int WC, int WK, int SPW) {
-  const size_t stage = 2 * (size_t)M * (WK * 256 + 16) + 2 * (size_t)WC * SPW * 32 * WK * 2;
+size_t coop_lds_bytes(int M, int WC, int WK, int SPW, bool zp) {
+  const size_t stage =
+      2 * (size_t)M * (WK * 256 + 16) + 2 * (size_t)(zp ? 2 : 1) * WC * SPW * 32 * WK * 2;
   const size_t red = (size_t)WK * WC * SPW * M * 32 * 4;
   return stage > red ? stage : red;
 }
 
-template <int MT, int SPW, int WC, int WK, int RPL, bool SWIGLU, bool BF>
+template <int MT, int SPW, int WC, int WK, int RPL, bool SWIGLU, bool BF, bool ZP>
 static hipError_t launch_coop_t(const DecodeArgs &a, hipStream_t s) {
-  const size_t lds = coop_lds_bytes(a.M, WC, WK, SPW);
+  const size_t lds = coop_lds_bytes(a.M, WC, WK, SPW, ZP);
   const int ncg = (a.nsg + WC - 1) / WC;
-  hipLaunchKernelGGL((decode_coop_kernel<MT, SPW, WC, WK, RPL, SWIGLU, BF>), dim3(ncg * a.KS),
+  hipLaunchKernelGGL((decode_coop_kernel<MT, SPW, WC, WK, RPL, SWIGLU, BF, ZP>), dim3(ncg * a.KS),
                      dim3(WC * WK * 64), lds, s, a);
   return hipGetLastError();
 }
 
-template <int MT, int SPW, int RPL, bool SWIGLU, bool BF>
+template <int MT, int SPW, int RPL, bool SWIGLU, bool BF, bool ZP>
 static hipError_t launch_coop_w(const DecodeArgs &a, int WC, int WK, hipStream_t s) {
-  if (WC == 4 && WK == 1) return launch_coop_t<MT, SPW, 4, 1, RPL, SWIGLU, BF>(a, s);
-  if (WC == 8 && WK == 1) return launch_coop_t<MT, SPW, 8, 1, RPL, SWIGLU, BF>(a, s);
-  if (WC == 2 && WK == 2) return launch_coop_t<MT, SPW, 2, 2, RPL, SWIGLU, BF>(a, s);
-  if (WC == 4 && WK == 2) return launch_coop_t<MT, SPW, 4, 2, RPL, SWIGLU, BF>(a, s);
-  if (WC == 2 && WK == 4) return launch_coop_t<MT, SPW, 2, 4, RPL, SWIGLU, BF>(a, s);
-  return launch_coop_t<MT, SPW, 1, 4, RPL, SWIGLU, BF>(a, s);
+  if (WC == 4 && WK == 1) return launch_coop_t<MT, SPW, 4, 1, RPL, SWIGLU, BF, ZP>(a, s);
+  if (WC == 8 && WK == 1) return launch_coop_t<MT, SPW, 8, 1, RPL, SWIGLU, BF, ZP>(a, s);
+  if (WC == 2 && WK == 2) return launch_coop_t<MT, SPW, 2, 2, RPL, SWIGLU, BF, ZP>(a, s);
+  if (WC == 4 && WK == 2) return launch_coop_t<MT, SPW, 4, 2, RPL, SWIGLU, BF, ZP>(a, s);
+  if (WC == 2 && WK == 4) return launch_coop_t<MT, SPW, 2, 4, RPL, SWIGLU, BF, ZP>(a, s);
+  return launch_coop_t<MT, SPW, 1, 4, RPL, SWIGLU, BF, ZP>(a, s);
 }
 
-template <bool BF>
+template <bool BF, bool ZP>
 static hipError_t launch_coop_bf(const Problem &p, const DecodeArgs &a, int WC, int WK,
                                  hipStream_t s) {
   if (p.M == 1)
-    return p.swiglu ? launch_coop_w<16, 2, 1, true, BF>(a, WC, WK, s)
-                    : launch_coop_w<16, 1, 1, false, BF>(a, WC, WK, s);
+    return p.swiglu ? launch_coop_w<16, 2, 1, true, BF, ZP>(a, WC, WK, s)
+                    : launch_coop_w<16, 1, 1, false, BF, ZP>(a, WC, WK, s);
   if (p.M <= 16)
-    return p.swiglu ? launch_coop_w<16, 2, 4, true, BF>(a, WC, WK, s)
-                    : launch_coop_w<16, 1, 4, false, BF>(a, WC, WK, s);
-  return p.swiglu ? launch_coop_w<32, 2, 16, true, BF>(a, WC, WK, s)
-                  : launch_coop_w<32, 1, 16, false, BF>(a, WC, WK, s);
+    return p.swiglu ? launch_coop_w<16, 2, 4, true, BF, ZP>(a, WC, WK, s)
+                    : launch_coop_w<16, 1, 4, false, BF, ZP>(a, WC, WK, s);
+  return p.swiglu ? launch_coop_w<32, 2, 16, true, BF, ZP>(a, WC, WK, s)
+                  : launch_coop_w<32, 1, 16, false, BF, ZP>(a, WC, WK, s);
 }
 
 // -1 if unset, else the integer value.
@@ -416,7 +424,6 @@ bool coop_config(const Problem &p, int &WC, int &WK, int &KS) {
   const int SPW = p.swiglu ? 2 : 1;
   const int force = coop_env_raw("W4A16_DECODE_COOP");
   if (p.G < kGroup) return false;  // one scale per column and 128-k unit
-  if (p.zp) return false;          // zero rows: decode_kernel's pre-scaled form
   if (p.bits != 4) return false;   // INT8 weights: decode_kernel's 8-bit instances
   const bool wide = nsg >= 384, deep = KG >= 192;
   const bool uneven = nsg > 256 && nsg % 256 != 0;
@@ -424,7 +431,7 @@ bool coop_config(const Problem &p, int &WC, int &WK, int &KS) {
   if (p.M > 16) {
     use = true;
     WK = 2;
-    WC = nsg >= 256 && coop_lds_bytes((int)p.M, 4, 2, SPW) < 65536 ? 4 : 2;
+    WC = nsg >= 256 && coop_lds_bytes((int)p.M, 4, 2, SPW, p.zp) < 65536 ? 4 : 2;
     KS = 1;
     while ((int64_t)ceil_div(nsg, WC) * KS * 2 <= 256 && KG / (KS * 2) >= 8) KS *= 2;
   } else if (p.M == 1 && wide) {
@@ -449,7 +456,7 @@ bool coop_config(const Problem &p, int &WC, int &WK, int &KS) {
   if (!ok) return false;
   if (KS > KG) KS = KG;
   if (KS < 1) KS = 1;
-  if (coop_lds_bytes((int)p.M, WC, WK, SPW) >= 65536) return false;
+  if (coop_lds_bytes((int)p.M, WC, WK, SPW, p.zp) >= 65536) return false;
   return true;
 }
 
@@ -458,7 +465,10 @@ hipError_t launch_decode_coop(const Problem &p, void *workspace, int WC, int WK,
   DecodeArgs a = decode_args(p, KS, workspace);
   if (KS > 1 && workspace == nullptr) return hipErrorInvalidValue;
   const hipError_t e =
-      p.bf16 ? launch_coop_bf<true>(p, a, WC, WK, s) : launch_coop_bf<false>(p, a, WC, WK, s);
+      p.zp ? (p.bf16 ? launch_coop_bf<true, true>(p, a, WC, WK, s)
+                     : launch_coop_bf<false, true>(p, a, WC, WK, s))
+           : (p.bf16 ? launch_coop_bf<true, false>(p, a, WC, WK, s)
+                     : launch_coop_bf<false, false>(p, a, WC, WK, s));
   if (e != hipSuccess || KS == 1) return e;
   return launch_decode_reduce(a, p.swiglu, p.bf16, s);
 }
