@@ -177,21 +177,21 @@ def test_describe_names_the_launches():
     half-strip workgroups)."""
     d = w4a16.describe(1, 4096, 28672, swiglu=True)
     assert d.startswith("decode_coop_kernel<16, 2, ") and d.split(">")[0].endswith(
-        "true, false, false"), d
+        "true, false, false, 4"), d
     d = w4a16.describe(1, 4096, 28672, swiglu=True, bf16=True)
     assert d.startswith("decode_coop_kernel<16, 2, ") and d.split(">")[0].endswith(
-        "true, true, false"), d
+        "true, true, false, 4"), d
     d = w4a16.describe(1, 4096, 4096)
     assert d.startswith("decode_kernel<16, 1, ") and d.split(">")[0].endswith(
         "false, false, false, false, true, 4"), d     # 128 strips: half strips; INT4
     assert " workgroups=256 " in d and d.endswith("ks=1"), d
-    # 32-row tiles: the cooperative kernel, K split to fill the CUs; INT8
-    # weights keep the per-wave kernel's 8-bit instance.
+    # 32-row tiles: the cooperative kernel, K split to fill the CUs (its
+    # 8-bit instance for INT8 weights).
     d = w4a16.describe(24, 4096, 4096)
-    assert d.startswith("decode_coop_kernel<32, 1, 2, 2, 16, false, false, false> workgroups=256 "), d
+    assert d.startswith("decode_coop_kernel<32, 1, 2, 2, 16, false, false, false, 4> workgroups=256 "), d
     assert d.endswith("ks=4; decode_reduce_kernel<1, false, false>"), d
     d = w4a16.describe(24, 4096, 4096, int8=True)
-    assert d.startswith("decode_kernel<32, 1, ") and d.split(">")[0].endswith("false, false, 8"), d
+    assert d.startswith("decode_coop_kernel<32, 1, 2, 2, 16, false, false, false, 8>"), d
     assert "prefill2_kernel<4, 2, 4, 2, false, true, false, false, 4>" in w4a16.describe(
         4096, 4096, 28672, swiglu=True)
     assert "prefill2_kernel<4, 2, 4, 2, false, true, true, false, 4>" in w4a16.describe(
@@ -204,13 +204,13 @@ def test_describe_names_the_launches():
     # prefill takes the ZP instance, the dense tier folds them into its dequant.
     d = w4a16.describe(1, 4096, 28672, swiglu=True, zp=True)
     assert d.startswith("decode_coop_kernel<16, 2, ") and d.split(">")[0].endswith(
-        "true, false, true"), d
+        "true, false, true, 4"), d
     d = w4a16.describe(4, 4096, 4096, bf16=True, zp=True)
     assert d.startswith("decode_kernel<16, 1, ") and d.split(">")[0].endswith(
         "false, true, true, true, true, 4"), d
-    # INT8 weights: the decode and prefill kernels' 8-bit instances.
+    # INT8 weights: the decode kernels' and the prefill kernel's 8-bit instances.
     d = w4a16.describe(1, 4096, 28672, swiglu=True, int8=True)
-    assert d.startswith("decode_kernel<16, 2, ") and d.split(">")[0].endswith(", 8"), d
+    assert d.startswith("decode_coop_kernel<16, 2, 1, 4, 1, true, false, false, 8>"), d
     d = w4a16.describe(3, 4096, 4096, bf16=True, int8=True)
     assert d.split(">")[0].endswith("false, true, true, false, true, 8"), d
     assert w4a16.describe(100, 4096, 4096, int8=True).startswith("prefill2_kernel<")

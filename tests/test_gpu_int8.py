@@ -203,3 +203,41 @@ def test_int8_prefill_split_bit_exact_integer_inputs(monkeypatch, wm, ks):
     out = fp16_out(w4a16.gemm(to_dev(A), w, path="prefill")).view(np.uint16)
     packed, s16 = o.quantize_pack8(W)
     assert np.array_equal(out, o.f64_to_f16(o.gemm8_f64(A, packed, s16)))
+
+
+@pytest.mark.parametrize("wc,wk,ks", [(1, 4, 1), (2, 4, 2), (4, 2, 1), (2, 2, 4), (4, 2, 4), (8, 1, 3)])
+@pytest.mark.parametrize("M", [1, 7, 16, 24, 32])
+@pytest.mark.parametrize("bf16", [False, True])
+def test_int8_cooperative_decode(monkeypatch, wc, wk, ks, M, bf16):
+    """The cooperative decode kernel's 8-bit instances (two 16-byte vectors
+    per lane and unit) in several configurations, with K splits that leave
+    partial rounds and gate/up with an odd number of strips (N = 2112)."""
+    monkeypatch.setenv("W4A16_DECODE_COOP", "1")
+    monkeypatch.setenv("W4A16_COOP_WC", str(wc))
+    monkeypatch.setenv("W4A16_COOP_WK", str(wk))
+    monkeypatch.setenv("W4A16_COOP_KS", str(ks))
+    swiglu = (wc + M) % 2 == 1
+    K, N = (1152, 2112) if swiglu else (2560, 1064)
+    d = w4a16.describe(M, K, N, swiglu, path="decode", bf16=bf16, int8=True)
+    if M <= 16:   # at M > 16 some configurations need more than 64 KiB of LDS and fall back
+        assert d.startswith("decode_coop_kernel") and d.split(">")[0].endswith(", 8"), d
+    gemm8_case(M, K, N, swiglu=swiglu, path="decode", bf16=bf16, seed=wc * 100 + wk * 10 + ks + M)
+
+
+def test_int8_cooperative_integer_exact(monkeypatch):
+    """Grid weights and sparse ternary activations through the cooperative
+    8-bit instances with K splits: the correctly rounded exact product."""
+    o = orc()
+    monkeypatch.setenv("W4A16_DECODE_COOP", "1")
+    K, N = 4096, 2048
+    for (wc, wk, ks), M in [((2, 4, 2), 1), ((1, 4, 1), 16), ((4, 2, 4), 32)]:
+        monkeypatch.setenv("W4A16_COOP_WC", str(wc))
+        monkeypatch.setenv("W4A16_COOP_WK", str(wk))
+        monkeypatch.setenv("W4A16_COOP_KS", str(ks))
+        assert w4a16.describe(M, K, N, path="decode", int8=True).startswith("decode_coop_kernel")
+        W = synth.grid_weights8(K, N, p=10, seed=M)
+        A = synth.ternary_activations(M, K, density=0.25, seed=M)
+        w = w4a16.load_weight_int8(W)
+        out = fp16_out(w4a16.gemm(to_dev(A), w, path="decode")).view(np.uint16)
+        packed, s16 = o.quantize_pack8(W)
+        assert np.array_equal(out, o.f64_to_f16(o.gemm8_f64(A, packed, s16))), (wc, wk, ks, M)

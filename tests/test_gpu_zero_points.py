@@ -199,7 +199,7 @@ def test_zp_cooperative_decode(monkeypatch, wc, wk, ks, M, bf16):
     K, N = (1152, 2112) if swiglu else (2560, 1064)
     d = w4a16.describe(M, K, N, swiglu, path="decode", bf16=bf16, zp=True)
     if M <= 16:   # at M > 16 some configurations need more than 64 KiB of LDS and fall back
-        assert d.startswith("decode_coop_kernel") and d.split(">")[0].endswith(", true"), d
+        assert d.startswith("decode_coop_kernel") and d.split(">")[0].endswith(", true, 4"), d
     zp_case(M, K, N, swiglu=swiglu, path="decode", bf16=bf16, seed=wc * 100 + wk * 10 + ks + M)
 
 

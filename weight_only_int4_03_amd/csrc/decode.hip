@@ -426,9 +426,9 @@ int decode_describe(const Problem &p, char *buf, size_t n) {
     const int spw = p.swiglu ? 2 : 1;
     const int nsg = (int)(p.swiglu ? (p.N / 2 / kStrip) : ceil_div(p.N, kStrip));
     int k = snprintf(buf, n,
-                     "decode_coop_kernel<%d, %d, %d, %d, %d, %s, %s, %s> workgroups=%d threads=%d "
-                     "ks=%d",
-                     mt, spw, WC, WK, rpl, sw, bf, p.zp ? "true" : "false",
+                     "decode_coop_kernel<%d, %d, %d, %d, %d, %s, %s, %s, %d> workgroups=%d "
+                     "threads=%d ks=%d",
+                     mt, spw, WC, WK, rpl, sw, bf, p.zp ? "true" : "false", p.bits,
                      (int)ceil_div(nsg, WC) * KS, WC * WK * 64, KS);
     if (KS > 1 && k > 0 && (size_t)k < n)
       k += snprintf(buf + k, n - k, "; decode_reduce_kernel<%d, %s, %s>", spw, sw, bf);

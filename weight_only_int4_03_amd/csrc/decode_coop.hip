@@ -31,19 +31,24 @@
 
 namespace w4a16 {
 
-template <int MT, int SPW>
+template <int MT, int SPW, int BITS>
 struct CoopFrag {
-  uint4_t b[SPW][2];  // weight vectors of the wave's strips for one group
+  static constexpr int NV = BITS == 8 ? 2 : 1;  // 16-byte vectors per lane and MFMA unit
+  uint4_t b[SPW][2][NV];  // weight vectors of the wave's strips for one group
 };
 
-template <int MT, int SPW, int WC, int WK, int RPL, bool SWIGLU, bool BF, bool ZP>
+template <int MT, int SPW, int WC, int WK, int RPL, bool SWIGLU, bool BF, bool ZP, int BITS>
 __global__ __launch_bounds__(WC * WK * 64) void decode_coop_kernel(DecodeArgs p) {
   constexpr int NW = WC * WK, NT = NW * 64, D = 2;
   constexpr int SH = SWIGLU ? SPW / 2 : SPW;
   constexpr int NPART = MT == 16 ? 2 : 1;
   typedef typename std::conditional<MT == 16, float4_t, float16_t>::type acc_t;
-  typedef CoopFrag<MT, SPW> Frag;
+  typedef CoopFrag<MT, SPW, BITS> Frag;
+  constexpr int NV = Frag::NV;
+  constexpr uint32_t TILE = 1024u * NV;   // bytes per 64-k tile of a strip
+  constexpr uint32_t GROUP = 2u * TILE;   // bytes per 128-k unit of a strip
   static_assert(MT == 16 ? (RPL >= 1 && RPL <= 4) : RPL == 16, "rows per lane");
+  static_assert(BITS == 4 || (BITS == 8 && !ZP), "INT8 weights have no zero rows");
 
   extern __shared__ uint4_t smem[];
   const int M = p.M;
@@ -67,7 +72,7 @@ __global__ __launch_bounds__(WC * WK * 64) void decode_coop_kernel(DecodeArgs p)
   for (int s = 0; s < SPW; ++s) {
     const int base = sg * SH + (s % SH);
     const int strip = SWIGLU && s >= SH ? base + p.up_off : base;
-    wbase[s] = (const char *)(p.rw + (int64_t)strip * p.KT * 64);
+    wbase[s] = (const char *)(p.rw + (int64_t)strip * p.KT * 64 * NV);
   }
 
   const int gb = (int)((int64_t)p.KG * split / p.KS);
@@ -77,7 +82,8 @@ __global__ __launch_bounds__(WC * WK * 64) void decode_coop_kernel(DecodeArgs p)
   const int g4 = lane >> 4, c16 = lane & 15;
   const int h = lane >> 5, c32 = lane & 31;
   const int mrow = MT == 16 ? c16 : c32;
-  const uint32_t wlane = MT == 16 ? (uint32_t)(((g4 >> 1) * 64 + (g4 & 1) * 32 + c16) * 16)
+  // An INT8 tile holds a lane's second vector 1 KiB after its first.
+  const uint32_t wlane = MT == 16 ? (uint32_t)((g4 >> 1) * TILE + ((g4 & 1) * 32 + c16) * 16)
                                   : (uint32_t)(lane * 16);
   // LDS byte offset of this lane's activation fragment (row min(mrow, M-1)).
   const int a_lane = (mrow < M ? mrow : M - 1) * ars + wk * 256 + (MT == 16 ? g4 * 64 : h * 64);
@@ -157,17 +163,16 @@ __global__ __launch_bounds__(WC * WK * 64) void decode_coop_kernel(DecodeArgs p)
     return g < ge ? g : ge - 1;
   };
   auto wload = [&](Frag &f, int r) {
-    const uint32_t ow = (uint32_t)group_of(r) * 2048u + wlane;
+    const uint32_t ow = (uint32_t)group_of(r) * GROUP + wlane;
 #pragma unroll
     for (int s = 0; s < SPW; ++s) {
       const char *wp = wbase[s] + ow;
-      if constexpr (MT == 16) {
 #pragma unroll
-        for (int part = 0; part < 2; ++part) f.b[s][part] = load_nt((const uint4_t *)(wp + part * 256));
-      } else {
+      for (int x = 0; x < 2; ++x)
 #pragma unroll
-        for (int x = 0; x < 2; ++x) f.b[s][x] = load_nt((const uint4_t *)(wp + x * 1024));
-      }
+        for (int v = 0; v < NV; ++v)
+          f.b[s][x][v] =
+              load_nt((const uint4_t *)(wp + (MT == 16 ? x * 256 : x * TILE) + v * 1024));
     }
   };
 
@@ -176,6 +181,21 @@ __global__ __launch_bounds__(WC * WK * 64) void decode_coop_kernel(DecodeArgs p)
   for (int s = 0; s < SPW; ++s)
 #pragma unroll
     for (int part = 0; part < NPART; ++part) acc[s][part] = acc_t{};
+
+  // MFMA weight operand j (k offsets 8j .. 8j+7 of the lane's 32) of one
+  // strip part: unscaled (exact code minus offset, fp16) or scaled.
+  auto wq = [&](const uint4_t(&v)[NV], int j) {
+    if constexpr (BITS == 8)
+      return dq.bytes8(v[j >> 1][(j & 1) * 2], v[j >> 1][(j & 1) * 2 + 1]);
+    else
+      return dq(v[0][j]);
+  };
+  auto wsc = [&](const uint4_t(&v)[NV], int j, uint16_t s16, uint16_t z16) {
+    if constexpr (BITS == 8)
+      return dq.scaled8_bits<BF>(v[j >> 1][(j & 1) * 2], v[j >> 1][(j & 1) * 2 + 1], s16);
+    else
+      return dq.scaled_bits<BF, ZP>(v[0][j], s16, z16);
+  };
 
   auto compute = [&](const Frag &f, int buf) {
     const char *ab = lds + buf * abuf + a_lane;
@@ -201,19 +221,16 @@ __global__ __launch_bounds__(WC * WK * 64) void decode_coop_kernel(DecodeArgs p)
           const int si = ((wc * SPW + s) * 32 + col) * WK + wk;
           const uint16_t s16 = sb[si];
           const uint16_t z16 = ZP ? sb[WC * SPW * 32 * WK + si] : 0;
-          auto wop = [&](uint32_t w) -> uint4_t {
-            return dq.scaled_bits<BF, ZP>(w, s16, z16);
-          };
           if constexpr (MT == 16) {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-              acc[s][part] = mfma16<BF>(a[j], wop(f.b[s][part][j]), acc[s][part]);
+              acc[s][part] = mfma16<BF>(a[j], wsc(f.b[s][part], j, s16, z16), acc[s][part]);
           } else {
 #pragma unroll
             for (int x = 0; x < 2; ++x)
 #pragma unroll
               for (int j = 0; j < 4; ++j)
-                acc[s][part] = mfma32<BF>(a[4 * x + j], wop(f.b[s][x][j]), acc[s][part]);
+                acc[s][part] = mfma32<BF>(a[4 * x + j], wsc(f.b[s][x], j, s16, z16), acc[s][part]);
           }
         }
       }
@@ -227,7 +244,7 @@ __global__ __launch_bounds__(WC * WK * 64) void decode_coop_kernel(DecodeArgs p)
         if constexpr (MT == 16) {
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            t = __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<half8_t>(a[j]), dq(f.b[s][part][j]),
+            t = __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<half8_t>(a[j]), wq(f.b[s][part], j),
                                                        t, 0, 0, 0);
         } else {
 #pragma unroll
@@ -235,7 +252,7 @@ __global__ __launch_bounds__(WC * WK * 64) void decode_coop_kernel(DecodeArgs p)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
               t = __builtin_amdgcn_mfma_f32_32x32x16_f16(bitcast<half8_t>(a[4 * x + j]),
-                                                         dq(f.b[s][x][j]), t, 0, 0, 0);
+                                                         wq(f.b[s][x], j), t, 0, 0, 0);
         }
         const int col = MT == 16 ? 16 * part + c16 : c32;
         const float sc = (float)bitcast<_Float16>(sb[((wc * SPW + s) * 32 + col) * WK + wk]);
@@ -356,36 +373,36 @@ size_t coop_lds_bytes(int M, int WC, int WK, int SPW, bool zp) {
   return stage > red ? stage : red;
 }
 
-template <int MT, int SPW, int WC, int WK, int RPL, bool SWIGLU, bool BF, bool ZP>
+template <int MT, int SPW, int WC, int WK, int RPL, bool SWIGLU, bool BF, bool ZP, int BITS>
 static hipError_t launch_coop_t(const DecodeArgs &a, hipStream_t s) {
   const size_t lds = coop_lds_bytes(a.M, WC, WK, SPW, ZP);
   const int ncg = (a.nsg + WC - 1) / WC;
-  hipLaunchKernelGGL((decode_coop_kernel<MT, SPW, WC, WK, RPL, SWIGLU, BF, ZP>), dim3(ncg * a.KS),
+  hipLaunchKernelGGL((decode_coop_kernel<MT, SPW, WC, WK, RPL, SWIGLU, BF, ZP, BITS>), dim3(ncg * a.KS),
                      dim3(WC * WK * 64), lds, s, a);
   return hipGetLastError();
 }
 
-template <int MT, int SPW, int RPL, bool SWIGLU, bool BF, bool ZP>
+template <int MT, int SPW, int RPL, bool SWIGLU, bool BF, bool ZP, int BITS>
 static hipError_t launch_coop_w(const DecodeArgs &a, int WC, int WK, hipStream_t s) {
-  if (WC == 4 && WK == 1) return launch_coop_t<MT, SPW, 4, 1, RPL, SWIGLU, BF, ZP>(a, s);
-  if (WC == 8 && WK == 1) return launch_coop_t<MT, SPW, 8, 1, RPL, SWIGLU, BF, ZP>(a, s);
-  if (WC == 2 && WK == 2) return launch_coop_t<MT, SPW, 2, 2, RPL, SWIGLU, BF, ZP>(a, s);
-  if (WC == 4 && WK == 2) return launch_coop_t<MT, SPW, 4, 2, RPL, SWIGLU, BF, ZP>(a, s);
-  if (WC == 2 && WK == 4) return launch_coop_t<MT, SPW, 2, 4, RPL, SWIGLU, BF, ZP>(a, s);
-  return launch_coop_t<MT, SPW, 1, 4, RPL, SWIGLU, BF, ZP>(a, s);
+  if (WC == 4 && WK == 1) return launch_coop_t<MT, SPW, 4, 1, RPL, SWIGLU, BF, ZP, BITS>(a, s);
+  if (WC == 8 && WK == 1) return launch_coop_t<MT, SPW, 8, 1, RPL, SWIGLU, BF, ZP, BITS>(a, s);
+  if (WC == 2 && WK == 2) return launch_coop_t<MT, SPW, 2, 2, RPL, SWIGLU, BF, ZP, BITS>(a, s);
+  if (WC == 4 && WK == 2) return launch_coop_t<MT, SPW, 4, 2, RPL, SWIGLU, BF, ZP, BITS>(a, s);
+  if (WC == 2 && WK == 4) return launch_coop_t<MT, SPW, 2, 4, RPL, SWIGLU, BF, ZP, BITS>(a, s);
+  return launch_coop_t<MT, SPW, 1, 4, RPL, SWIGLU, BF, ZP, BITS>(a, s);
 }
 
-template <bool BF, bool ZP>
+template <bool BF, bool ZP, int BITS>
 static hipError_t launch_coop_bf(const Problem &p, const DecodeArgs &a, int WC, int WK,
                                  hipStream_t s) {
   if (p.M == 1)
-    return p.swiglu ? launch_coop_w<16, 2, 1, true, BF, ZP>(a, WC, WK, s)
-                    : launch_coop_w<16, 1, 1, false, BF, ZP>(a, WC, WK, s);
+    return p.swiglu ? launch_coop_w<16, 2, 1, true, BF, ZP, BITS>(a, WC, WK, s)
+                    : launch_coop_w<16, 1, 1, false, BF, ZP, BITS>(a, WC, WK, s);
   if (p.M <= 16)
-    return p.swiglu ? launch_coop_w<16, 2, 4, true, BF, ZP>(a, WC, WK, s)
-                    : launch_coop_w<16, 1, 4, false, BF, ZP>(a, WC, WK, s);
-  return p.swiglu ? launch_coop_w<32, 2, 16, true, BF, ZP>(a, WC, WK, s)
-                  : launch_coop_w<32, 1, 16, false, BF, ZP>(a, WC, WK, s);
+    return p.swiglu ? launch_coop_w<16, 2, 4, true, BF, ZP, BITS>(a, WC, WK, s)
+                    : launch_coop_w<16, 1, 4, false, BF, ZP, BITS>(a, WC, WK, s);
+  return p.swiglu ? launch_coop_w<32, 2, 16, true, BF, ZP, BITS>(a, WC, WK, s)
+                  : launch_coop_w<32, 1, 16, false, BF, ZP, BITS>(a, WC, WK, s);
 }
 
 // -1 if unset, else the integer value.
@@ -424,7 +441,7 @@ bool coop_config(const Problem &p, int &WC, int &WK, int &KS) {
   const int SPW = p.swiglu ? 2 : 1;
   const int force = coop_env_raw("W4A16_DECODE_COOP");
   if (p.G < kGroup) return false;  // one scale per column and 128-k unit
-  if (p.bits != 4) return false;   // INT8 weights: decode_kernel's 8-bit instances
+  if (p.bits == 8 && p.zp) return false;  // INT8 weights have no zero rows
   const bool wide = nsg >= 384, deep = KG >= 192;
   const bool uneven = nsg > 256 && nsg % 256 != 0;
   bool use;
@@ -465,10 +482,12 @@ hipError_t launch_decode_coop(const Problem &p, void *workspace, int WC, int WK,
   DecodeArgs a = decode_args(p, KS, workspace);
   if (KS > 1 && workspace == nullptr) return hipErrorInvalidValue;
   const hipError_t e =
-      p.zp ? (p.bf16 ? launch_coop_bf<true, true>(p, a, WC, WK, s)
-                     : launch_coop_bf<false, true>(p, a, WC, WK, s))
-           : (p.bf16 ? launch_coop_bf<true, false>(p, a, WC, WK, s)
-                     : launch_coop_bf<false, false>(p, a, WC, WK, s));
+      p.bits == 8 ? (p.bf16 ? launch_coop_bf<true, false, 8>(p, a, WC, WK, s)
+                            : launch_coop_bf<false, false, 8>(p, a, WC, WK, s))
+      : p.zp      ? (p.bf16 ? launch_coop_bf<true, true, 4>(p, a, WC, WK, s)
+                            : launch_coop_bf<false, true, 4>(p, a, WC, WK, s))
+                  : (p.bf16 ? launch_coop_bf<true, false, 4>(p, a, WC, WK, s)
+                            : launch_coop_bf<false, false, 4>(p, a, WC, WK, s));
   if (e != hipSuccess || KS == 1) return e;
   return launch_decode_reduce(a, p.swiglu, p.bf16, s);
 }
