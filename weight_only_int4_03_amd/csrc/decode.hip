@@ -343,7 +343,9 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
 }
 
 // Second stage for KS > 1: one thread per output element sums the KS partial
-// tiles of its strip group in split order, then runs the epilogue.
+// tiles of its strip group in split order, then runs the epilogue.  The
+// partials of up to eight splits are loaded before any is added, so their
+// memory latencies overlap instead of adding up.
 template <int SPW, bool SWIGLU, bool BF>
 __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs p) {
   constexpr int SH = SWIGLU ? SPW / 2 : SPW;
@@ -355,7 +357,15 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs p) {
   const float *all = p.ws + (int64_t)sg * p.KS * tileE;
   decode_epilogue<SPW, SWIGLU, BF>(p, sg, e, [&](int x) {
     float v = 0.0f;
-    for (int sp = 0; sp < p.KS; ++sp) v += all[(int64_t)sp * tileE + x];
+    for (int sp0 = 0; sp0 < p.KS; sp0 += 8) {
+      float t[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        t[i] = sp0 + i < p.KS ? all[(int64_t)(sp0 + i) * tileE + x] : 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (sp0 + i < p.KS) v += t[i];
+    }
     return v;
   });
 }
