@@ -169,6 +169,27 @@ def test_dispatch_table():
     assert w4a16.workspace_bytes(4096, 4096, 4096, path="dense") >= 4096 * 4096 * 2
 
 
+def test_decode_stagger_rule(monkeypatch):
+    """The rotated K order of the decode kernels is on where a strip's byte
+    stride is a multiple of 128 KiB (INT4 at K = 8192, INT8 at K = 4096) and
+    off elsewhere; the environment overrides it either way."""
+    monkeypatch.delenv("W4A16_DECODE_STAGGER", raising=False)
+    assert " stagger" in w4a16.describe(1, 8192, 10240)
+    assert " stagger" in w4a16.describe(16, 8192, 57344, swiglu=True)
+    assert " stagger" in w4a16.describe(1, 4096, 4096, int8=True)
+    assert " stagger" not in w4a16.describe(1, 4096, 4096)
+    assert " stagger" not in w4a16.describe(32, 14336, 4096)
+    assert " stagger" not in w4a16.describe(16, 28672, 8192)
+    d = w4a16.describe(16, 14336, 4096)
+    assert d.index(" stagger") if " stagger" in d else True
+    monkeypatch.setenv("W4A16_DECODE_STAGGER", "0")
+    assert " stagger" not in w4a16.describe(1, 8192, 10240)
+    monkeypatch.setenv("W4A16_DECODE_STAGGER", "1")
+    d = w4a16.describe(16, 14336, 4096)
+    assert " stagger" in d and d.index(" stagger") < d.index(";"), d
+    assert " stagger" not in w4a16.describe(4096, 4096, 28672, swiglu=True)  # prefill
+
+
 def test_describe_names_the_launches():
     """The launch description names kernel instances as profilers print them
     (template arguments after the tile shape: SwiGLU epilogue, bf16

@@ -234,6 +234,68 @@ def test_decode_half_strips_bit_exact_integer_inputs(monkeypatch):
             assert np.array_equal(out.astype(np.float64), orc().gemm_f64(A, packed_o, s16_o))
 
 
+@pytest.mark.parametrize("half,ks,waves,depth", [(1, 1, 4, 4), (1, 3, 4, 2), (0, 1, 8, 2),
+                                                (0, 2, 8, 4)])
+@pytest.mark.parametrize("M,K,N,swiglu", [(1, 2048, 1064, False), (5, 4096, 2112, True),
+                                          (12, 14336, 1024, False), (32, 2560, 1088, False)])
+def test_decode_stagger_per_wave_kernel(monkeypatch, half, ks, waves, depth, M, K, N, swiglu):
+    """The per-wave decode kernel with its K order rotated per workgroup, on
+    half and whole strips, with and without split K (uneven wave ranges at
+    KS = 3), both wave counts and depths, ragged N."""
+    monkeypatch.setenv("W4A16_DECODE_STAGGER", "1")
+    monkeypatch.setenv("W4A16_DECODE_COOP", "0")
+    monkeypatch.setenv("W4A16_DECODE_HALF", str(half))
+    monkeypatch.setenv("W4A16_DECODE_KS", str(ks))
+    monkeypatch.setenv("W4A16_DECODE_WAVES", str(waves))
+    monkeypatch.setenv("W4A16_DECODE_DEPTH", str(depth))
+    d = w4a16.describe(M, K, N, swiglu=swiglu, path="decode")
+    assert d.startswith("decode_kernel<") and " stagger" in d, d
+    gemm_case(M, K, N, swiglu=swiglu, path="decode", seed=M + K + ks + 7)
+
+
+@pytest.mark.parametrize("wc,wk,ks", [(1, 4, 1), (2, 4, 2), (1, 4, 3), (4, 2, 4), (2, 2, 1), (8, 1, 1)])
+@pytest.mark.parametrize("M", [1, 16, 32])
+@pytest.mark.parametrize("K,N,swiglu", [(1152, 1064, False), (1024, 2112, True), (2560, 4160, False)])
+def test_decode_stagger_cooperative(monkeypatch, wc, wk, ks, M, K, N, swiglu):
+    """The cooperative decode kernel with its rounds rotated per workgroup:
+    partial last rounds (K = 1152: nine groups in rounds of four or two; K
+    slices of uneven length at KS = 3) stay last, ragged N."""
+    monkeypatch.setenv("W4A16_DECODE_STAGGER", "1")
+    monkeypatch.setenv("W4A16_DECODE_COOP", "1")
+    monkeypatch.setenv("W4A16_COOP_WC", str(wc))
+    monkeypatch.setenv("W4A16_COOP_WK", str(wk))
+    monkeypatch.setenv("W4A16_COOP_KS", str(ks))
+    d = w4a16.describe(M, K, N, swiglu, path="decode")
+    assert " stagger" in d, d
+    gemm_case(M, K, N, swiglu=swiglu, path="decode", seed=wc * 100 + wk * 10 + ks + M + 3)
+
+
+def test_decode_stagger_bit_exact_integer_inputs(monkeypatch):
+    """Integer-exact inputs through both decode kernels with the rotated K
+    order (the partial sums are exact, so only a lost, repeated or misplaced
+    group could change the output): bit for bit the oracle's."""
+    monkeypatch.setenv("W4A16_DECODE_STAGGER", "1")
+    cases = [({"W4A16_DECODE_COOP": "0", "W4A16_DECODE_HALF": "1", "W4A16_DECODE_KS": "3"}, 3, 4608, 1088),
+             ({"W4A16_DECODE_COOP": "0", "W4A16_DECODE_HALF": "0", "W4A16_DECODE_KS": "1"}, 16, 4096, 2048),
+             ({"W4A16_DECODE_COOP": "1", "W4A16_COOP_WC": "1", "W4A16_COOP_WK": "4",
+               "W4A16_COOP_KS": "1"}, 1, 4736, 2048),
+             ({"W4A16_DECODE_COOP": "1", "W4A16_COOP_WC": "2", "W4A16_COOP_WK": "4",
+               "W4A16_COOP_KS": "3"}, 16, 4736, 2048),
+             ({"W4A16_DECODE_COOP": "1", "W4A16_COOP_WC": "4", "W4A16_COOP_WK": "2",
+               "W4A16_COOP_KS": "2"}, 32, 4224, 2048)]
+    for env, M, K, N in cases:
+        for k, v in env.items():
+            monkeypatch.setenv(k, v)
+        d = w4a16.describe(M, K, N, path="decode")
+        assert " stagger" in d, d
+        W = synth.grid_weights(K, N, p=4, seed=M + K)
+        A = synth.ternary_activations(M, K, density=1.0, seed=M)
+        w = w4a16.load_weight(W)
+        out = fp16_out(w4a16.gemm(to_dev(A), w, path="decode"))
+        packed_o, s16_o = orc().quantize_pack(W)
+        assert np.array_equal(out.astype(np.float64), orc().gemm_f64(A, packed_o, s16_o)), d
+
+
 PREFILL2_CONFIGS = [(64, 1, 1), (128, 1, 4), (256, 1, 2), (64, 2, 2), (128, 2, 4), (256, 2, 1),
                     (64, 1, 8), (256, 2, 4)]
 

@@ -279,16 +279,25 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
 #pragma unroll
         for (int v = 0; v < NV; ++v) asm volatile("" : "+v"(f.b[s][x][v]) : : "memory");
   };
+  // Rotated order (p.stagger): loop index g reads group gmap(g), so that the
+  // waves of different workgroups are not at the same offset of their
+  // strips at the same time.  Only the order of the per-group additions to
+  // the FP32 accumulators changes.
+  const int ng = g1 - g0;
+  const int rot = (p.stagger != 0 && ng > 0)
+                      ? (int)(((uint32_t)blockIdx.x * 2654435761u >> 8) % (uint32_t)ng) : 0;
+  auto gmap = [&](int g) { int t = g - g0 + rot; return g0 + (t >= ng ? t - ng : t); };
+  auto load_g = [&](Frag &f, int g) { load(f, gmap(g)); };
   if (g1 > g0) {
     Frag f[D];
 #pragma unroll
-    for (int d = 0; d < D; ++d) load(f[d], g0 + d < g1 ? g0 + d : g1 - 1);
+    for (int d = 0; d < D; ++d) load_g(f[d], g0 + d < g1 ? g0 + d : g1 - 1);
     int g = g0;
     for (; g + 2 * D <= g1; g += D) {
 #pragma unroll
       for (int d = 0; d < D; ++d) {
         compute(f[d]);
-        load(f[d], g + d + D);
+        load_g(f[d], g + d + D);
         after_reload(f[(d + 1) % D]);
       }
     }
@@ -296,7 +305,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
     for (int d = 0; d < D; ++d) {
       if (g + d < g1) {
         compute(f[d]);
-        if (g + d + D < g1) load(f[d], g + d + D);
+        if (g + d + D < g1) load_g(f[d], g + d + D);
       }
     }
 #pragma unroll
@@ -427,6 +436,23 @@ static DecodeConfig decode_config(const Problem &p) {
   return c;
 }
 
+// Rotated K order (each wave starts its K range, or the coop kernel its
+// sequence of rounds, at an offset hashed from the workgroup index).  Strips
+// are contiguous in K, so without it the concurrently running waves read
+// addresses that agree modulo the strip stride.  Measured on MI355X: where
+// that stride is a multiple of 128 KiB (INT4 at K = 8192: the Llama-70B QKV,
+// O and gate/up projections) rotating gains up to 13% (gate/up M = 4, 16:
+// 46.5 -> 40.5 us, 48.8 -> 42.7 us; QKV M = 1: 18.5 -> 15.0 us); at other
+// strides it changes nothing or costs 1-3% (Llama-8B gate/up, 64 KiB), so it
+// is off there.  W4A16_DECODE_STAGGER (0 or 1) overrides the choice.
+static bool decode_stagger(const Problem &p) {
+  const int64_t strip_bytes = p.K * kStrip * p.bits / 8;
+  bool on = strip_bytes % (128 * 1024) == 0;
+  const char *v = std::getenv("W4A16_DECODE_STAGGER");
+  if (v != nullptr && *v != 0) on = *v == '1';
+  return on;
+}
+
 int decode_describe(const Problem &p, char *buf, size_t n) {
   int WC, WK, KS;
   const char *sw = p.swiglu ? "true" : "false", *bf = p.bf16 ? "true" : "false";
@@ -440,6 +466,7 @@ int decode_describe(const Problem &p, char *buf, size_t n) {
                      "threads=%d ks=%d",
                      mt, spw, WC, WK, rpl, sw, bf, p.zp ? "true" : "false", p.bits,
                      (int)ceil_div(nsg, WC) * KS, WC * WK * 64, KS);
+    if (decode_stagger(p) && k > 0 && (size_t)k < n) k += snprintf(buf + k, n - k, " stagger");
     if (KS > 1 && k > 0 && (size_t)k < n)
       k += snprintf(buf + k, n - k, "; decode_reduce_kernel<%d, %s, %s>", spw, sw, bf);
     return k;
@@ -453,6 +480,7 @@ int decode_describe(const Problem &p, char *buf, size_t n) {
                    "threads=%d ks=%d",
                    c.MT, c.SPW, c.WAVES, c.D, rpl, sw, bf, pre, zp, hf, p.bits,
                    c.nsg * c.KS * (c.half ? 2 : 1), c.WAVES * 64, c.KS);
+  if (decode_stagger(p) && k > 0 && (size_t)k < n) k += snprintf(buf + k, n - k, " stagger");
   if (c.KS > 1 && k > 0 && (size_t)k < n)
     k += snprintf(buf + k, n - k, "; decode_reduce_kernel<%d, %s, %s>", c.SPW, sw, bf);
   return k;
@@ -533,6 +561,7 @@ DecodeArgs decode_args(const Problem &p, int KS, void *workspace) {
   a.nsg = p.swiglu ? a.up_off : a.NS;
   a.ws = (float *)workspace;
   a.rowscale = p.rowscale;
+  a.stagger = decode_stagger(p) ? 1 : 0;
   return a;
 }
 

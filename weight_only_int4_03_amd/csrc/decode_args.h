@@ -22,6 +22,7 @@ struct DecodeArgs {
   float *ws;         // KS > 1: partial tiles [nsg][KS][SPW][M][32]
   const float *rowscale;  // per-row output factor, or null
   int gshift;        // group of k = k >> gshift (KG counts 128-k units, KG8 scale octets)
+  int stagger;       // nonzero: K order rotated by an offset hashed from the workgroup index
 };
 
 // Epilogue of one element e of strip group sg's tile (tile element order

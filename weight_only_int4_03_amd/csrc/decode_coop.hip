@@ -78,6 +78,17 @@ __global__ __launch_bounds__(WC * WK * 64) void decode_coop_kernel(DecodeArgs p)
   const int gb = (int)((int64_t)p.KG * split / p.KS);
   const int ge = (int)((int64_t)p.KG * (split + 1) / p.KS);
   const int R = (ge - gb + WK - 1) / WK;      // rounds
+  // Rotation of the order of the full rounds: loop round r works on round
+  // rm(r); a partial last round stays last (the steady-state loop computes
+  // every wave's group unconditionally).
+  const int RF = (ge - gb) / WK;              // full rounds
+  const int rot = (p.stagger != 0 && RF > 0)
+                      ? (int)(((uint32_t)blockIdx.x * 2654435761u >> 8) % (uint32_t)RF) : 0;
+  auto rm = [&](int r) {
+    if (r >= RF) return r;
+    const int t = r + rot;
+    return t >= RF ? t - RF : t;
+  };
 
   const int g4 = lane >> 4, c16 = lane & 15;
   const int h = lane >> 5, c32 = lane & 31;
@@ -104,7 +115,7 @@ __global__ __launch_bounds__(WC * WK * 64) void decode_coop_kernel(DecodeArgs p)
   // is conditionally rewritten while weight loads are still in flight;
   // staged groups past the end of the K range are never consumed.
   auto stage_load = [&](Stage &st, int r) {
-    const int g0 = gb + r * WK;
+    const int g0 = gb + rm(r) * WK;
 #pragma unroll
     for (int t = 0; t < AV_MAX; ++t) {
       int e = tid + t * NT;
@@ -159,7 +170,7 @@ __global__ __launch_bounds__(WC * WK * 64) void decode_coop_kernel(DecodeArgs p)
   // The wave's group in round r is gb + r*WK + wk; past the end of the K
   // range it re-reads the last group (never consumed).
   auto group_of = [&](int r) {
-    const int g = gb + r * WK + wk;
+    const int g = gb + rm(r) * WK + wk;
     return g < ge ? g : ge - 1;
   };
   auto wload = [&](Frag &f, int r) {
@@ -304,7 +315,7 @@ __global__ __launch_bounds__(WC * WK * 64) void decode_coop_kernel(DecodeArgs p)
   }
   // Tail: at most three rounds left (r .. R-1), in the same state.
   if (r < R) {
-    if (gb + r * WK + wk < ge) compute(f0, 0);
+    if (gb + rm(r) * WK + wk < ge) compute(f0, 0);
     if (r + 2 < R) {
       stage_load(s0, r + 2);
       __builtin_amdgcn_sched_barrier(0);
@@ -314,12 +325,12 @@ __global__ __launch_bounds__(WC * WK * 64) void decode_coop_kernel(DecodeArgs p)
     round_barrier();
   }
   if (r + 1 < R) {
-    if (gb + (r + 1) * WK + wk < ge) compute(f1, 1);
+    if (gb + rm(r + 1) * WK + wk < ge) compute(f1, 1);
     if (r + 2 < R) stage_store(s0, 0);
     round_barrier();
   }
   if (r + 2 < R) {
-    if (gb + (r + 2) * WK + wk < ge) compute(f0, 0);
+    if (gb + rm(r + 2) * WK + wk < ge) compute(f0, 0);
     round_barrier();
   }
 
