@@ -113,12 +113,22 @@ def kernel_key(M, K, N, swiglu, bf16=False, zp=False, int8=False):
     return name + (" + reduce" if ";" in desc else "")
 
 
-def source_digest():
-    """Digest of the HIP sources, to tell whether stored counters still apply."""
+# HIP sources that define each kernel family (the digest of stored counters
+# covers these; a kernel of no listed family is covered by every source).
+KERNEL_SOURCES = {
+    "decode": ("common.h", "decode.hip", "decode_args.h", "decode_coop.hip"),
+    "prefill": ("common.h", "prefill.hip"),
+}
+
+
+def source_digest(kernel=None):
+    """Digest of the HIP sources that define ``kernel``, to tell whether
+    stored counters still apply."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "weight_only_int4_03_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    fam = next((f for f in KERNEL_SOURCES if kernel and kernel.startswith(f)), None)
+    for f in (KERNEL_SOURCES[fam] if fam else sorted(os.listdir(csrc))):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -135,7 +145,7 @@ def stored_traffic(workload, kernel):
         m = re.match(r"^\s*([a-z_]+)\s*=\s*(.+?)\s*$", line)
         if m:
             vals[m.group(1)] = m.group(2)
-    if (vals.get("source_digest") != source_digest() or vals.get("workload") != workload
+    if (vals.get("source_digest") != source_digest(kernel) or vals.get("workload") != workload
             or vals.get("kernel") != kernel):
         return None
     try:

@@ -209,10 +209,20 @@ def test_describe_names_the_launches():
     # 32-row tiles: the cooperative kernel, K split to fill the CUs (its
     # 8-bit instance for INT8 weights).
     d = w4a16.describe(24, 4096, 4096)
-    assert d.startswith("decode_coop_kernel<32, 1, 2, 2, 16, false, false, false, 4> workgroups=256 "), d
+    assert d.startswith("decode_coop_kernel<32, 1, 2, 4, 16, false, false, false, 4> workgroups=256 "), d
     assert d.endswith("ks=4; decode_reduce_kernel<1, false, false>"), d
     d = w4a16.describe(24, 4096, 4096, int8=True)
-    assert d.startswith("decode_coop_kernel<32, 1, 2, 2, 16, false, false, false, 8>"), d
+    assert d.startswith("decode_coop_kernel<32, 1, 2, 4, 16, false, false, false, 8>"), d
+    # Mid-width plain projections: one column group, no K split; the widest
+    # fused ones: four column groups, two groups of 128 k per round.
+    assert w4a16.describe(32, 4096, 6144).startswith(
+        "decode_coop_kernel<32, 1, 1, 4, 16, false, false, false, 4> workgroups=192 threads=256 ks=1")
+    assert w4a16.describe(32, 8192, 57344, swiglu=True).startswith(
+        "decode_coop_kernel<32, 2, 4, 2, 16, true, false, false, 4> workgroups=224 threads=512 ks=1")
+    assert w4a16.describe(32, 28672, 8192).startswith(
+        "decode_coop_kernel<32, 1, 4, 2, 16, false, false, false, 4> workgroups=256 threads=512 ks=4")
+    assert w4a16.describe(32, 4096, 28672, swiglu=True).startswith(
+        "decode_coop_kernel<32, 2, 2, 4, 16, true, false, false, 4> workgroups=224 threads=512 ks=1")
     assert "prefill2_kernel<4, 2, 4, 2, false, true, false, false, 4>" in w4a16.describe(
         4096, 4096, 28672, swiglu=True)
     assert "prefill2_kernel<4, 2, 4, 2, false, true, true, false, 4>" in w4a16.describe(

@@ -377,6 +377,9 @@ __global__ __launch_bounds__(WC * WK * 64) void decode_coop_kernel(DecodeArgs p)
 // ---------------------------------------------------------------------------
 // Host side.
 
+// LDS one workgroup may allocate on gfx950 (the CU's 160 KiB).
+constexpr size_t kMaxLdsPerWorkgroup = 160 * 1024;
+
 size_t coop_lds_bytes(int M, int WC, int WK, int SPW, bool zp) {
   const size_t stage =
       2 * (size_t)M * (WK * 256 + 16) + 2 * (size_t)(zp ? 2 : 1) * WC * SPW * 32 * WK * 2;
@@ -432,10 +435,16 @@ static int coop_env(const char *name, int fallback) {
 
 // Where the cooperative kernel wins (measured on MI355X, sweeping both
 // kernels' configurations over the Llama-8B and -70B projections):
-//  * 32-row tiles (M > 16): every shape.  Two waves per column group along
-//    K; four column groups per workgroup when there are at least 256 strip
-//    groups and the LDS allows it, else two; K is split (power of two) while
-//    the grid stays within 256 workgroups.
+//  * 32-row tiles (M > 16): every shape.  Four waves per column group along
+//    K and two column groups per workgroup (the fused projections with at
+//    least 512 strip groups and plain ones with K >= 24576: four column
+//    groups, two waves along K; plain ones with 129-255 strip groups: one
+//    column group); K is split (power of two) while the grid stays within
+//    256 workgroups.  Measured at M = 32 against two waves along K with two
+//    column groups: Llama-8B QKV 11.4 -> 10.6 us, gate/up 20.8 -> 19.6 us,
+//    down 15.9 -> 15.1 us; Llama-70B QKV 21.3 -> 19.6 us, O 17.0 -> 15.9 us,
+//    gate/up 63.2 -> 54.7 us (the 70B down projection, K = 28672: 37.5 us
+//    with four column groups against 38.0 us with two).
 //  * M <= 16: wide shapes (>= 384 strip groups: the fused gate/up
 //    projections), deep ones (K >= 24576), grids that the per-wave kernel
 //    would spread unevenly (more than 256 strip groups, not a multiple of
@@ -457,11 +466,25 @@ bool coop_config(const Problem &p, int &WC, int &WK, int &KS) {
   const bool uneven = nsg > 256 && nsg % 256 != 0;
   bool use;
   if (p.M > 16) {
+    // Eight waves per workgroup, four groups of 128 k per round (67 KiB of
+    // LDS at M = 32), except for the widest fused projections and the
+    // deepest plain ones (four column groups, two groups per round) and
+    // mid-width plain ones that fill the CUs with one column group per
+    // workgroup and no K split.
     use = true;
-    WK = 2;
-    WC = nsg >= 256 && coop_lds_bytes((int)p.M, 4, 2, SPW, p.zp) < 65536 ? 4 : 2;
+    if (p.swiglu) {
+      WC = nsg >= 512 ? 4 : 2;
+      WK = nsg >= 512 ? 2 : 4;
+    } else if (KG >= 192) {
+      WC = 4;
+      WK = 2;
+    } else {
+      WC = nsg > 128 && nsg < 256 ? 1 : 2;
+      WK = 4;
+    }
     KS = 1;
-    while ((int64_t)ceil_div(nsg, WC) * KS * 2 <= 256 && KG / (KS * 2) >= 8) KS *= 2;
+    if (WC > 1)
+      while ((int64_t)ceil_div(nsg, WC) * KS * 2 <= 256 && KG / (KS * 2) >= 8) KS *= 2;
   } else if (p.M == 1 && wide) {
     use = true;
     WC = 1; WK = 4; KS = 1;
@@ -484,7 +507,7 @@ bool coop_config(const Problem &p, int &WC, int &WK, int &KS) {
   if (!ok) return false;
   if (KS > KG) KS = KG;
   if (KS < 1) KS = 1;
-  if (coop_lds_bytes((int)p.M, WC, WK, SPW, p.zp) >= 65536) return false;
+  if (coop_lds_bytes((int)p.M, WC, WK, SPW, p.zp) > kMaxLdsPerWorkgroup) return false;
   return true;
 }
 
