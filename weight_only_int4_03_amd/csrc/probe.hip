@@ -11,19 +11,19 @@ namespace w4a16 {
 
 constexpr uint32_t kProbeTag = 0x9e3779b9u;
 
-// Streaming read: each wave owns a contiguous 16 KiB chunk and walks it in
-// 1 KiB wave-wide rows, four 128-bit non-temporal loads in flight per lane,
-// folding everything into a running XOR.
-constexpr int kProbeChunk = 1024;  // 16-byte words per wave
-
+// Streaming read: each wave owns a contiguous chunk (16 KiB; 4 KiB for
+// buffers under 256 MiB, so that small reads still spread over many more
+// waves than the CUs hold) and walks it in 1 KiB wave-wide rows, four
+// 128-bit non-temporal loads in flight per lane, folding everything into a
+// running XOR.
 __global__ __launch_bounds__(256) void stream_read_kernel(const uint4_t *buf, int64_t n16,
-                                                          uint32_t *sink) {
+                                                          int chunk, uint32_t *sink) {
   const int lane = threadIdx.x & 63;
   const int64_t wave = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6;
-  const int64_t begin = wave * kProbeChunk;
-  const int64_t end = begin + kProbeChunk < n16 ? begin + kProbeChunk : n16;
+  const int64_t begin = wave * chunk;
+  const int64_t end = begin + chunk < n16 ? begin + chunk : n16;
   uint4_t x = {0u, 0u, 0u, 0u};
-  if (end - begin == kProbeChunk) {
+  if (end - begin == chunk) {
 #pragma unroll 1
     for (int64_t o = begin + lane; o < end; o += 256) {
       const uint4_t a = load_nt(buf + o), b = load_nt(buf + o + 64);
@@ -58,10 +58,11 @@ __global__ __launch_bounds__(256) void mfma_peak_kernel(int iterations, float *s
 
 hipError_t launch_stream_read(const void *buf, int64_t bytes, void *sink, hipStream_t s) {
   const int64_t n16 = bytes / 16;
-  const int64_t blocks = ceil_div(ceil_div(n16, (int64_t)kProbeChunk), (int64_t)4);
+  const int chunk = bytes >= ((int64_t)256 << 20) ? 1024 : 256;  // 16-byte words per wave
+  const int64_t blocks = ceil_div(ceil_div(n16, (int64_t)chunk), (int64_t)4);
   if (blocks > ((int64_t)1 << 31) - 1) return hipErrorInvalidValue;
   hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
-                     (const uint4_t *)buf, n16, (uint32_t *)sink);
+                     (const uint4_t *)buf, n16, chunk, (uint32_t *)sink);
   return hipGetLastError();
 }
 
