@@ -235,6 +235,25 @@ def test_decode_half_strips_bit_exact_integer_inputs(monkeypatch):
 
 
 @pytest.mark.parametrize("half,ks,waves,depth", [(1, 1, 4, 4), (1, 3, 4, 2), (0, 1, 8, 2),
+                                                (0, 2, 8, 4), (1, 5, 8, 2)])
+@pytest.mark.parametrize("K,N,swiglu", [(28672, 1088, False), (14336, 2112, True), (1152, 1064, False)])
+def test_decode_one_row_lds_slices(monkeypatch, half, ks, waves, depth, K, N, swiglu):
+    """M = 1 through the per-wave kernel, whose two-deep one-row instances
+    stage each wave's K range of the activation row in LDS: the longest
+    slices (K = 28672 unsplit, 56 KiB per workgroup), uneven slices (KS = 3,
+    5), K ranges shorter than the pipeline (K = 1152), both wave counts, and
+    the four-deep instances that load activations per group."""
+    monkeypatch.setenv("W4A16_DECODE_COOP", "0")
+    monkeypatch.setenv("W4A16_DECODE_HALF", str(half))
+    monkeypatch.setenv("W4A16_DECODE_KS", str(ks))
+    monkeypatch.setenv("W4A16_DECODE_WAVES", str(waves))
+    monkeypatch.setenv("W4A16_DECODE_DEPTH", str(depth))
+    d = w4a16.describe(1, K, N, swiglu=swiglu, path="decode")
+    assert d.startswith("decode_kernel<16, %d, %d, %d, 1, " % (2 if swiglu else 1, waves, depth)), d
+    gemm_case(1, K, N, swiglu=swiglu, path="decode", seed=K + ks + waves)
+
+
+@pytest.mark.parametrize("half,ks,waves,depth", [(1, 1, 4, 4), (1, 3, 4, 2), (0, 1, 8, 2),
                                                 (0, 2, 8, 4)])
 @pytest.mark.parametrize("M,K,N,swiglu", [(1, 2048, 1064, False), (5, 4096, 2112, True),
                                           (12, 14336, 1024, False), (32, 2560, 1088, False)])

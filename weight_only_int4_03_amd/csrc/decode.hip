@@ -47,6 +47,7 @@ struct DecodeFrag {
   static constexpr int NA = MT == 16 ? 4 : 8;  // 16-byte activation vectors per group
   uint4_t b[SPW][NB][NV];
   uint4_t a[NA];
+  int gi;  // group held (one-row instances read its activations from LDS)
   // Scales per strip, 16-column half (MT=16) and 64-k tile (MT=32, which
   // can span two groups when G < 128), and the zero rows likewise (16-bit
   // values held in 32-bit words, which keeps the arrays in registers).
@@ -73,7 +74,9 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
   static_assert(!HALF || MT == 16, "half strips need the 16-column MFMA");
   static_assert(BITS == 4 || (BITS == 8 && !ZP), "INT8 weights have no zero rows");
   static_assert(MT == 16 ? (RPL >= 1 && RPL <= 4) : RPL == 16, "rows per lane");
-  extern __shared__ float lds[];  // [WAVES][SPW][M][32]
+  // LDS: the cross-wave reduction [WAVES][SPW][M][32] floats; one-row
+  // instances (M = 1) add the workgroup's activation slice after it.
+  extern __shared__ float lds[];
   constexpr int SH = SWIGLU ? SPW / 2 : SPW;
   // 16-column halves per workgroup (MT=16) or the whole strip (MT=32).
   constexpr int NPART = MT == 16 ? (HALF ? 1 : 2) : 1;
@@ -108,6 +111,20 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
   const int unit = split * WAVES + wave, nunits = p.KS * WAVES;
   const int g0 = (int)((int64_t)p.KG * unit / nunits);
   const int g1 = (int)((int64_t)p.KG * (unit + 1) / nunits);
+  // One-row instances (M = 1): the MFMA activation operand is 16 copies of
+  // one row; loaded from global memory per group that is four 16-byte loads
+  // per 1 KiB of weights, which occupy the wave's memory requests (measured
+  // on MI355X: the one-row GEMMs ran 13-22% faster with those loads
+  // removed).  With a two-deep pipeline each wave instead copies its own K
+  // range of the row into a private LDS region with one 16-byte load per
+  // lane and KiB, and reads each group's fragment from there one group ahead
+  // of its use; no other wave touches the region, so no workgroup barrier is
+  // needed.  (A four-deep pipeline would wait for its first four weight
+  // groups before consuming the staged row: the 4096 x 4096 GEMV ran 4.74 ->
+  // 5.22 us that way.)
+  constexpr bool AL = MT == 16 && RPL == 1 && D == 2;
+  const int wslice = (int)ceil_div((int64_t)p.KG, (int64_t)nunits) * 256;  // bytes per wave
+  char *lds_a = (char *)lds + WAVES * SPW * 32 * 4 + wave * wslice;  // after the reduction tile
 
   // Lane roles.  MT=16: lane = 16*g4 + c16; row of A = c16; lane group g4
   // covers k offsets 32*g4 .. +31 of the group.  MT=32: lane = 32*h + c;
@@ -173,7 +190,9 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
       }
     }
     const char *ag = Ab + (uint32_t)(arow_off + (uint32_t)g * 256u + alane);
-    if constexpr (MT == 16) {
+    if constexpr (AL) {
+      f.gi = g;  // activations are read from LDS just ahead of use
+    } else if constexpr (MT == 16) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) f.a[j] = *(const uint4_t *)(ag + j * 16);
     } else {
@@ -288,14 +307,38 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
                       ? (int)(((uint32_t)blockIdx.x * 2654435761u >> 8) % (uint32_t)ng) : 0;
   auto gmap = [&](int g) { int t = g - g0 + rot; return g0 + (t >= ng ? t - ng : t); };
   auto load_g = [&](Frag &f, int g) { load(f, gmap(g)); };
+  // One-row instances: the MFMA activation operand of the group f holds.
+  auto fill_a = [&](Frag &f) {
+    if constexpr (AL) {
+      const char *src = lds_a + (f.gi - g0) * 256 + alane;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) f.a[j] = *(const uint4_t *)(src + j * 16);
+    }
+  };
+  Frag f[D];
   if (g1 > g0) {
-    Frag f[D];
 #pragma unroll
     for (int d = 0; d < D; ++d) load_g(f[d], g0 + d < g1 ? g0 + d : g1 - 1);
+  }
+  if constexpr (AL) {
+    // The wave's range [g0, g1) of activation row 0, issued after its first
+    // weight loads so that both are in flight together; a wave-scope fence
+    // orders the lanes' LDS writes before any lane's reads.
+    const uint4_t *src = (const uint4_t *)p.A + (int64_t)g0 * 16;
+    uint4_t *dst = (uint4_t *)lds_a;
+    const int n16 = (g1 - g0) * 16;
+    for (int e = lane; e < n16; e += 64) dst[e] = src[e];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+  if (g1 > g0) {
+    fill_a(f[0]);
     int g = g0;
     for (; g + 2 * D <= g1; g += D) {
 #pragma unroll
       for (int d = 0; d < D; ++d) {
+        fill_a(f[(d + 1) % D]);
         compute(f[d]);
         load_g(f[d], g + d + D);
         after_reload(f[(d + 1) % D]);
@@ -304,13 +347,17 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       if (g + d < g1) {
+        fill_a(f[d]);
         compute(f[d]);
         if (g + d + D < g1) load_g(f[d], g + d + D);
       }
     }
 #pragma unroll
     for (int d = 0; d < D; ++d)
-      if (g + D + d < g1) compute(f[d]);
+      if (g + D + d < g1) {
+        fill_a(f[d]);
+        compute(f[d]);
+      }
   }
 
   // Cross-wave reduction through LDS: lds[((wave*SPW + s)*M + m)*32 + col].
@@ -402,9 +449,11 @@ static int env_int(const char *name, int fallback) {
 // and K is short (or M <= 4): each half-strip workgroup reads the whole
 // activation slice for half the weights, so at larger M and long K the
 // activation loads dominate, and a grid of 1.5 workgroups per CU leaves half
-// the CUs with twice the work.  Half strips at M = 1 (fp16, symmetric INT4)
-// run four waves with four groups in flight each; everything else keeps two
-// groups in flight.  W4A16_DECODE_HALF (0 or 1), W4A16_DECODE_WAVES (4 or 8),
+// the CUs with twice the work.  Two groups in flight per wave (at M = 1 the
+// two-deep instances stage the activation row in LDS: eight waves of two
+// replaced four waves of four for the half-strip GEMVs, Llama-8B down
+// 10.4 -> 9.5 us, the 4096 x 4096 GEMV unchanged at 4.7 us).
+// W4A16_DECODE_HALF (0 or 1), W4A16_DECODE_WAVES (4 or 8),
 // W4A16_DECODE_KS and W4A16_DECODE_DEPTH (groups loaded ahead: 2 or 4)
 // override the choice.
 static DecodeConfig decode_config(const Problem &p) {
@@ -418,13 +467,12 @@ static DecodeConfig decode_config(const Problem &p) {
   const bool half_fits = 2 * (int64_t)c.nsg <= 256 && (KG <= 64 || p.M <= 4);
   c.half = c.MT == 16 && (hv != nullptr && *hv != 0 ? *hv == '1' : half_fits);
   const int64_t units = (int64_t)c.nsg * (c.half ? 2 : 1);
-  const bool gemv = c.half && p.M == 1 && p.bits == 4 && !p.zp && !p.bf16;
-  int waves = gemv ? 4 : (units < 384 || KG >= 128) ? 8 : 4;
+  int waves = (units < 384 || KG >= 128) ? 8 : 4;
   waves = env_int("W4A16_DECODE_WAVES", waves) >= 8 ? 8 : 4;
   // LDS for the cross-wave reduction: WAVES * SPW * M * 32 floats < 64 KiB.
   while (waves > 4 && (int64_t)waves * c.SPW * p.M * 32 * 4 >= 65536) waves /= 2;
   c.WAVES = waves;
-  c.D = env_int("W4A16_DECODE_DEPTH", gemv ? 4 : 2) >= 4 ? 4 : 2;
+  c.D = env_int("W4A16_DECODE_DEPTH", 2) >= 4 ? 4 : 2;
   // A second launch (the reduction) costs more than idle CUs unless each
   // wave still streams a long K slice: split K only for narrow, deep shapes.
   int64_t ks = (units < 256 && KG / c.WAVES >= 8) ? 2 : 1;
@@ -434,6 +482,22 @@ static DecodeConfig decode_config(const Problem &p) {
   if (ks < 1) ks = 1;
   c.KS = (int)ks;
   return c;
+}
+
+// LDS of the one-row instances' activation slices: one region per wave,
+// each the longest per-wave K range.
+static size_t one_row_slice_bytes(int KG, int KS, int WAVES) {
+  return (size_t)WAVES * ceil_div(KG, KS * WAVES) * 256;
+}
+
+// One-row instances serve M = 1; those with a two-deep pipeline stage the
+// activation row per wave in LDS, when the slices fit (otherwise M = 1 runs
+// the four-rows-per-lane instances).
+static bool one_row(const Problem &p, const DecodeConfig &c) {
+  return c.MT == 16 && p.M == 1 &&
+         (c.D != 2 || (size_t)c.WAVES * c.SPW * 32 * 4 +
+                              one_row_slice_bytes((int)(p.K / kGroup), c.KS, c.WAVES) <=
+                          kMaxLdsPerWorkgroup);
 }
 
 // Rotated K order (each wave starts its K range, or the coop kernel its
@@ -472,7 +536,7 @@ int decode_describe(const Problem &p, char *buf, size_t n) {
     return k;
   }
   const DecodeConfig c = decode_config(p);
-  const int rpl = c.MT == 16 ? (p.M == 1 ? 1 : 4) : 16;
+  const int rpl = c.MT == 16 ? (one_row(p, c) ? 1 : 4) : 16;
   const char *pre = (p.bf16 || p.G < kGroup || p.zp) ? "true" : "false";
   const char *zp = p.zp ? "true" : "false", *hf = c.half ? "true" : "false";
   int k = snprintf(buf, n,
@@ -501,7 +565,8 @@ int64_t decode_workspace_bytes(const Problem &p) {
 template <int MT, int SPW, int WAVES, int D, int RPL, bool SWIGLU, bool BF, bool PRE, bool ZP,
           bool HALF, int BITS>
 static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t s) {
-  const size_t lds = (size_t)WAVES * SPW * a.M * 32 * sizeof(float);
+  const size_t lds = (size_t)WAVES * SPW * a.M * 32 * sizeof(float) +
+                     (MT == 16 && RPL == 1 && D == 2 ? one_row_slice_bytes(a.KG, a.KS, WAVES) : 0);
   hipLaunchKernelGGL((decode_kernel<MT, SPW, WAVES, D, RPL, SWIGLU, BF, PRE, ZP, HALF, BITS>),
                      dim3(a.nsg * a.KS * (HALF ? 2 : 1)), dim3(WAVES * 64), lds, s, a);
   hipError_t e = hipGetLastError();
@@ -529,7 +594,7 @@ static hipError_t launch_decode_w(const DecodeArgs &a, const DecodeConfig &c, hi
 template <bool BF, bool PRE, bool ZP, int BITS = 4>
 static hipError_t launch_decode_bf(const Problem &p, const DecodeArgs &a, const DecodeConfig &c,
                                    hipStream_t s) {
-  if (c.MT == 16 && p.M == 1)
+  if (one_row(p, c))
     return p.swiglu ? launch_decode_w<16, 2, 1, true, BF, PRE, ZP, BITS>(a, c, s)
                     : launch_decode_w<16, 1, 1, false, BF, PRE, ZP, BITS>(a, c, s);
   if (c.MT == 16)

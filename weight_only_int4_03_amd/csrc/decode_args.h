@@ -6,6 +6,9 @@
 
 namespace w4a16 {
 
+// LDS one workgroup may allocate on gfx950 (the CU's 160 KiB).
+constexpr size_t kMaxLdsPerWorkgroup = 160 * 1024;
+
 struct DecodeArgs {
   const uint16_t *A;
   int M, K;

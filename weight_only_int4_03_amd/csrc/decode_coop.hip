@@ -377,9 +377,6 @@ __global__ __launch_bounds__(WC * WK * 64) void decode_coop_kernel(DecodeArgs p)
 // ---------------------------------------------------------------------------
 // Host side.
 
-// LDS one workgroup may allocate on gfx950 (the CU's 160 KiB).
-constexpr size_t kMaxLdsPerWorkgroup = 160 * 1024;
-
 size_t coop_lds_bytes(int M, int WC, int WK, int SPW, bool zp) {
   const size_t stage =
       2 * (size_t)M * (WK * 256 + 16) + 2 * (size_t)(zp ? 2 : 1) * WC * SPW * 32 * WK * 2;
