@@ -36,6 +36,12 @@
  *     call on them must pass again.
  *   - K % 128 == 0, N % 8 == 0, and 16-byte aligned device pointers are
  *     required (else W4A16_ERR_INVALID).  M is arbitrary (M == 0 is a no-op).
+ *   - Launch configurations are the library's measured choices.  For tests
+ *     and measurement, environment variables read at every call override
+ *     them (W4A16_DECODE_COOP, _HALF, _WAVES, _DEPTH, _KS, _STAGGER;
+ *     W4A16_COOP_WC, _WK, _KS; W4A16_PREFILL_V2, _BM, _WM, _TPS, _KS); a value
+ *     no kernel supports is clamped to a supported one or ignored.  The
+ *     result of a GEMM does not depend on them beyond FP32 summation order.
  */
 #ifndef W4A16_H
 #define W4A16_H
