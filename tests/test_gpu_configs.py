@@ -48,3 +48,29 @@ def test_config(M, K, N, swiglu, outliers, path):
     cols = sample_indices(ncols, 256, seed=K + N, edge=16)
     gemm_case(M, K, N, swiglu=swiglu, path=path, seed=0, outliers=outliers, cols=cols,
               rows=_rows(M), W=W, weight=w)
+
+
+@pytest.mark.parametrize("M,K,N,density", [(1, 8192, 10240, 0.25), (4, 8192, 10240, 0.25),
+                                           (16, 8192, 10240, 0.25), (32, 8192, 10240, 0.25),
+                                           (32, 4096, 6144, 1.0), (32, 4096, 4096, 1.0),
+                                           (32, 14336, 4096, 0.1), (1, 14336, 4096, 0.1)])
+def test_config_integer_exact(M, K, N, density):
+    """Integer-exact inputs (power-of-two scales, activations in {-1, 0, 1})
+    at full projection sizes on the automatic path: the rotated K order of
+    the Llama-70B QKV projection (strips 128 KiB apart), the eight-wave
+    32-row layouts of the Llama-8B projections and the one-row LDS staging
+    of the down projection.  Every partial sum is exact, so the sampled
+    outputs must equal the oracle's bit for bit."""
+    from gpuhelp import fp16_out, orc, to_dev
+    d = w4a16.describe(M, K, N)
+    say("integer-exact M=%d K=%d N=%d: %s" % (M, K, N, d))
+    if K == 8192:
+        assert " stagger" in d, d
+    W = synth.grid_weights(K, N, p=4, seed=M + K)
+    A = synth.ternary_activations(M, K, density=density, seed=M)
+    out = fp16_out(w4a16.gemm(to_dev(A), w4a16.load_weight(W)))
+    cols = sample_indices(N, 256, seed=K + N + M, edge=16)
+    packed_o, s16_o = orc().quantize_pack(np.ascontiguousarray(W[:, cols]))
+    C = orc().gemm_f64(A, packed_o, s16_o)
+    assert np.abs(C).max() < 128, "inputs not fp16-exact"
+    assert np.array_equal(out[:, cols].astype(np.float64), C), d
