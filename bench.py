@@ -17,7 +17,8 @@ Timing (HIP events on the stream the kernels run on):
     graph so that graph launches do not dominate); W warm-up steps, then
     exactly K timed steps between two synchronisations;
   * per GEMM: a HIP graph of one launch per weight copy, replayed between two
-    events; the kernel behind the largest share of the step time gives the
+    events (median of three trials); the kernel behind the largest share of
+    the step time gives the
     roofline entry (algorithmic bytes = K*N/2 + 2*(K/G)*N + 2*M*K + 2*M*N_out,
     FLOPs = 2*M*N*K).
 
@@ -436,15 +437,22 @@ def main():
         with torch.cuda.graph(g, stream=stream):
             for c in range(ncopies):
                 run_unit(u, c)
+        # Three replays of warm-up, then the median of three trials of
+        # `reps` replays each (the first GEMM timed after the step graphs
+        # otherwise reads high on some runs).
+        trials = []
         with torch.cuda.stream(stream):
-            g.replay()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            for _ in range(args.reps):
+            for _ in range(3):
                 g.replay()
-            b.record(stream)
+            for _ in range(3):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                for _ in range(args.reps):
+                    g.replay()
+                b.record(stream)
+                trials.append((a, b))
         torch.cuda.synchronize()
-        us = a.elapsed_time(b) * 1e3 / (args.reps * ncopies)
+        us = sorted(a.elapsed_time(b) for a, b in trials)[1] * 1e3 / (args.reps * ncopies)
         by, fl = alg_bytes(m, k, n, sw, zp, int8), flops(m, k, n)
         detail.append({"gemm": label, "M": m, "K": k, "N": n, "swiglu": sw,
                        "kernel": kernel_key(m, k, n, sw, bf16, zp, int8),

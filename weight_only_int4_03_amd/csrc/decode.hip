@@ -115,14 +115,12 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
   // one row; loaded from global memory per group that is four 16-byte loads
   // per 1 KiB of weights, which occupy the wave's memory requests (measured
   // on MI355X: the one-row GEMMs ran 13-22% faster with those loads
-  // removed).  With a two-deep pipeline each wave instead copies its own K
-  // range of the row into a private LDS region with one 16-byte load per
-  // lane and KiB, and reads each group's fragment from there one group ahead
-  // of its use; no other wave touches the region, so no workgroup barrier is
-  // needed.  (A four-deep pipeline would wait for its first four weight
-  // groups before consuming the staged row: the 4096 x 4096 GEMV ran 4.74 ->
-  // 5.22 us that way.)
-  constexpr bool AL = MT == 16 && RPL == 1 && D == 2;
+  // removed).  Each wave instead copies its own K range of the row into a
+  // private LDS region with one 16-byte load per lane and KiB, and reads each
+  // group's fragment from there one group ahead of its use; no other wave
+  // touches the region, so no workgroup barrier is
+  // needed.
+  constexpr bool AL = MT == 16 && RPL == 1;
   const int wslice = (int)ceil_div((int64_t)p.KG, (int64_t)nunits) * 256;  // bytes per wave
   char *lds_a = (char *)lds + WAVES * SPW * 32 * 4 + wave * wslice;  // after the reduction tile
 
@@ -315,19 +313,38 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
       for (int j = 0; j < 4; ++j) f.a[j] = *(const uint4_t *)(src + j * 16);
     }
   };
+  // The wave's range [g0, g1) of activation row 0: its first 16 groups are
+  // loaded into registers before the first weight loads and stored to LDS
+  // after them, so the stores wait only for the activations (loads complete
+  // in issue order) while the weights stay in flight; longer ranges copy the
+  // rest afterwards.  A wave-scope fence orders the lanes' LDS writes before
+  // any lane's reads.
+  constexpr int AV = AL ? 4 : 1;  // 16-byte activation vectors per lane (16 groups)
+  uint4_t av[AV];
+  const uint4_t *asrc = (const uint4_t *)p.A + (int64_t)g0 * 16;
+  const int n16 = (g1 - g0) * 16;
+  if constexpr (AL) {
+    if (n16 > 0) {
+#pragma unroll
+      for (int t = 0; t < AV; ++t) {
+        const int e = lane + 64 * t;
+        av[t] = asrc[e < n16 ? e : n16 - 1];
+      }
+    }
+  }
   Frag f[D];
   if (g1 > g0) {
 #pragma unroll
     for (int d = 0; d < D; ++d) load_g(f[d], g0 + d < g1 ? g0 + d : g1 - 1);
   }
   if constexpr (AL) {
-    // The wave's range [g0, g1) of activation row 0, issued after its first
-    // weight loads so that both are in flight together; a wave-scope fence
-    // orders the lanes' LDS writes before any lane's reads.
-    const uint4_t *src = (const uint4_t *)p.A + (int64_t)g0 * 16;
     uint4_t *dst = (uint4_t *)lds_a;
-    const int n16 = (g1 - g0) * 16;
-    for (int e = lane; e < n16; e += 64) dst[e] = src[e];
+#pragma unroll
+    for (int t = 0; t < AV; ++t) {
+      const int e = lane + 64 * t;
+      if (e < n16) dst[e] = av[t];
+    }
+    for (int e = lane + 64 * AV; e < n16; e += 64) dst[e] = asrc[e];
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -449,10 +466,11 @@ static int env_int(const char *name, int fallback) {
 // and K is short (or M <= 4): each half-strip workgroup reads the whole
 // activation slice for half the weights, so at larger M and long K the
 // activation loads dominate, and a grid of 1.5 workgroups per CU leaves half
-// the CUs with twice the work.  Two groups in flight per wave (at M = 1 the
-// two-deep instances stage the activation row in LDS: eight waves of two
-// replaced four waves of four for the half-strip GEMVs, Llama-8B down
-// 10.4 -> 9.5 us, the 4096 x 4096 GEMV unchanged at 4.7 us).
+// the CUs with twice the work.  Two groups in flight per wave, four for
+// one-row GEMVs with long per-wave K ranges (at M = 1 the activation row is
+// staged per wave in LDS; eight waves replaced four waves of four for the
+// half-strip GEMVs: Llama-8B down 10.4 -> 8.5 us, the 4096 x 4096 GEMV
+// unchanged at 4.7 us).
 // W4A16_DECODE_HALF (0 or 1), W4A16_DECODE_WAVES (4 or 8),
 // W4A16_DECODE_KS and W4A16_DECODE_DEPTH (groups loaded ahead: 2 or 4)
 // override the choice.
@@ -472,7 +490,7 @@ static DecodeConfig decode_config(const Problem &p) {
   // LDS for the cross-wave reduction: WAVES * SPW * M * 32 floats < 64 KiB.
   while (waves > 4 && (int64_t)waves * c.SPW * p.M * 32 * 4 >= 65536) waves /= 2;
   c.WAVES = waves;
-  c.D = env_int("W4A16_DECODE_DEPTH", 2) >= 4 ? 4 : 2;
+
   // A second launch (the reduction) costs more than idle CUs unless each
   // wave still streams a long K slice: split K only for narrow, deep shapes.
   int64_t ks = (units < 256 && KG / c.WAVES >= 8) ? 2 : 1;
@@ -481,6 +499,11 @@ static DecodeConfig decode_config(const Problem &p) {
   if (ks > 64) ks = 64;
   if (ks < 1) ks = 1;
   c.KS = (int)ks;
+  // Four groups in flight for the one-row GEMVs whose waves stream at least
+  // 12 groups (Llama-8B down: 9.2 -> 8.5 us); shorter ranges lose more to
+  // the deeper prologue than they gain (4096 x 4096: 4.8 -> 5.0 us).
+  const bool deep_row = p.M == 1 && KG / (c.KS * c.WAVES) >= 12;
+  c.D = env_int("W4A16_DECODE_DEPTH", deep_row ? 4 : 2) >= 4 ? 4 : 2;
   return c;
 }
 
@@ -490,14 +513,13 @@ static size_t one_row_slice_bytes(int KG, int KS, int WAVES) {
   return (size_t)WAVES * ceil_div(KG, KS * WAVES) * 256;
 }
 
-// One-row instances serve M = 1; those with a two-deep pipeline stage the
-// activation row per wave in LDS, when the slices fit (otherwise M = 1 runs
-// the four-rows-per-lane instances).
+// One-row instances (activation row staged per wave in LDS) serve M = 1
+// when the slices fit; otherwise M = 1 runs the four-rows-per-lane
+// instances.
 static bool one_row(const Problem &p, const DecodeConfig &c) {
   return c.MT == 16 && p.M == 1 &&
-         (c.D != 2 || (size_t)c.WAVES * c.SPW * 32 * 4 +
-                              one_row_slice_bytes((int)(p.K / kGroup), c.KS, c.WAVES) <=
-                          kMaxLdsPerWorkgroup);
+         (size_t)c.WAVES * c.SPW * 32 * 4 + one_row_slice_bytes((int)(p.K / kGroup), c.KS, c.WAVES) <=
+             kMaxLdsPerWorkgroup;
 }
 
 // Rotated K order (each wave starts its K range, or the coop kernel its
@@ -566,7 +588,7 @@ template <int MT, int SPW, int WAVES, int D, int RPL, bool SWIGLU, bool BF, bool
           bool HALF, int BITS>
 static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t s) {
   const size_t lds = (size_t)WAVES * SPW * a.M * 32 * sizeof(float) +
-                     (MT == 16 && RPL == 1 && D == 2 ? one_row_slice_bytes(a.KG, a.KS, WAVES) : 0);
+                     (MT == 16 && RPL == 1 ? one_row_slice_bytes(a.KG, a.KS, WAVES) : 0);
   hipLaunchKernelGGL((decode_kernel<MT, SPW, WAVES, D, RPL, SWIGLU, BF, PRE, ZP, HALF, BITS>),
                      dim3(a.nsg * a.KS * (HALF ? 2 : 1)), dim3(WAVES * 64), lds, s, a);
   hipError_t e = hipGetLastError();
