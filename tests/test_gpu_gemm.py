@@ -253,6 +253,22 @@ def test_decode_one_row_lds_slices(monkeypatch, half, ks, waves, depth, K, N, sw
     gemm_case(1, K, N, swiglu=swiglu, path="decode", seed=K + ks + waves)
 
 
+@pytest.mark.parametrize("ks", [1, 2])
+def test_decode_one_row_slices_beyond_lds(monkeypatch, ks):
+    """M = 1 with K = 81920 unsplit: eight waves' activation slices (160 KiB)
+    plus the reduction tile exceed a workgroup's LDS, so M = 1 runs the
+    four-rows-per-lane instance (activations loaded per group); split in two
+    it fits again and stages the row."""
+    monkeypatch.setenv("W4A16_DECODE_COOP", "0")
+    monkeypatch.setenv("W4A16_DECODE_KS", str(ks))
+    monkeypatch.setenv("W4A16_DECODE_WAVES", "8")
+    K, N = 81920, 72
+    d = w4a16.describe(1, K, N, path="decode")
+    rpl = 4 if ks == 1 else 1
+    assert d.startswith("decode_kernel<16, 1, 8, 4, %d, " % rpl), d
+    gemm_case(1, K, N, path="decode", seed=ks)
+
+
 @pytest.mark.parametrize("half,ks,waves,depth", [(1, 1, 4, 4), (1, 3, 4, 2), (0, 1, 8, 2),
                                                 (0, 2, 8, 4)])
 @pytest.mark.parametrize("M,K,N,swiglu", [(1, 2048, 1064, False), (5, 4096, 2112, True),
