@@ -501,8 +501,10 @@ static DecodeConfig decode_config(const Problem &p) {
   c.KS = (int)ks;
   // Four groups in flight for the one-row GEMVs whose waves stream at least
   // 12 groups (Llama-8B down: 9.2 -> 8.5 us); shorter ranges lose more to
-  // the deeper prologue than they gain (4096 x 4096: 4.8 -> 5.0 us).
-  const bool deep_row = p.M == 1 && KG / (c.KS * c.WAVES) >= 12;
+  // the deeper prologue than they gain (4096 x 4096: 4.8 -> 5.0 us), and so
+  // do the fused gate/up instances, with two strips' registers per group
+  // (Llama-70B gate/up: 42.7 us two deep, 45.4 us four deep).
+  const bool deep_row = p.M == 1 && !p.swiglu && KG / (c.KS * c.WAVES) >= 12;
   c.D = env_int("W4A16_DECODE_DEPTH", deep_row ? 4 : 2) >= 4 ? 4 : 2;
   return c;
 }

@@ -448,7 +448,9 @@ static int coop_env(const char *name, int fallback) {
 //    256), and at M > 8 shapes with >= 192 strip groups or K >= 12288.  Four
 //    waves per column group along K (two when four column groups share a
 //    workgroup); the fewest column groups per workgroup that keep the grid
-//    within 256 workgroups.  M = 1 on wide shapes keeps one column group.
+//    within 256 workgroups.  M = 1 on wide shapes keeps one column group;
+//    the widest fused ones (>= 512 strip groups, fp16 INT4) take the
+//    per-wave kernel.
 // Narrow, short-K shapes at small M keep the per-wave kernel (its half-strip
 // grid fills the CUs without sharing activations).  W4A16_DECODE_COOP=0/1
 // forces the choice; W4A16_COOP_WC / _WK / _KS override the configuration.
@@ -482,6 +484,12 @@ bool coop_config(const Problem &p, int &WC, int &WK, int &KS) {
     KS = 1;
     if (WC > 1)
       while ((int64_t)ceil_div(nsg, WC) * KS * 2 <= 256 && KG / (KS * 2) >= 8) KS *= 2;
+  } else if (p.M == 1 && nsg >= 512 && p.bits == 4 && !p.zp && !p.bf16) {
+    // The widest fused projections at M = 1 (Llama-70B gate/up): the
+    // per-wave kernel, which stages the activation row per wave without
+    // workgroup barriers, measured 42.7 us against 46.5 us.
+    use = false;
+    WC = 1; WK = 4; KS = 1;
   } else if (p.M == 1 && wide) {
     use = true;
     WC = 1; WK = 4; KS = 1;
