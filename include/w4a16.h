@@ -227,9 +227,18 @@ int w4a16_gemm_int8(const uint16_t *A_d, int64_t M, int64_t K, const void *rw_d,
  * The kernel path is chosen from (M, K, N) by a fixed table (decode for small
  * M, prefill for large M, dense fallback for very large M).  Deterministic:
  * the same call gives the same bits on every run.  Uses the library's
- * per-device workspace, allocated on the first call that needs it; calls that
+ * per-device workspace (split-K partials): the call never synchronises and
+ * never frees; when the workspace is too small it allocates a larger one,
+ * except under stream capture (HIP graphs), where it returns
+ * W4A16_ERR_WORKSPACE instead -- size it beforehand with
+ * w4a16_reserve_workspace(w4a16_gemm_workspace_bytes(...)).  Calls that
  * overlap in time on one device (different streams) must use w4a16_gemm_ex
  * with separate workspaces.
+ * A shape the selected kernel cannot take (operands beyond a kernel's 32-bit
+ * offsets) runs a slower kernel instead; each such fallback is reported once
+ * per process on stderr and by w4a16_last_fallback (the INT4 kernels page,
+ * section "Integrating a kernel into serving", keeps a logged
+ * dequantize-then-matmul fallback).
  * Errors: W4A16_ERR_INVALID, W4A16_ERR_UNSUPPORTED, W4A16_ERR_WORKSPACE,
  * W4A16_ERR_HIP.
  * ------------------------------------------------------------------------- */
@@ -299,8 +308,28 @@ int w4a16_rms_rowscale(const uint16_t *A_d, int64_t M, int64_t K, float eps, int
 int64_t w4a16_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N, int G, int flags);
 
 /* The path (W4A16_PATH_DECODE / PREFILL / DENSE) that AUTO picks for this
- * problem, or a negative error code. */
+ * problem (after fallbacks), or a negative error code. */
 int w4a16_select_path(int64_t M, int64_t K, int64_t N, int G, int flags);
+
+/* The library's per-device workspace (used by the GEMM calls given no
+ * workspace).  Host calls on the calling thread's current device; they may
+ * synchronise the device, so make them at load time, outside stream capture.
+ *   w4a16_reserve_workspace(bytes): grow the workspace to at least `bytes`
+ *     (bytes >= 0; a smaller request keeps the current buffer), freeing any
+ *     buffers that earlier GEMM calls replaced.  Errors: W4A16_ERR_INVALID,
+ *     W4A16_ERR_WORKSPACE (allocation failed), W4A16_ERR_HIP.
+ *   w4a16_workspace_reserved(): bytes the current workspace holds (or a
+ *     negative error code).
+ *   w4a16_release_workspace(): synchronise the device and free its workspace
+ *     buffers (a later GEMM call allocates again). */
+int w4a16_reserve_workspace(int64_t bytes);
+int64_t w4a16_workspace_reserved(void);
+int w4a16_release_workspace(void);
+
+/* The most recent fallback of any thread ("" if none): the calling entry
+ * point or tier, then what ran instead and why.  Each kind of fallback is also
+ * written once per process to stderr. */
+const char *w4a16_last_fallback(void);
 
 /* Writes into buf (len bytes, NUL-terminated, truncated if short) a text
  * description of the launches w4a16_gemm_ex would make for this problem and

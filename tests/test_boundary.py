@@ -265,3 +265,45 @@ def test_describe_names_the_launches():
     assert L.w4a16_describe(1, 4096, 4096, 128, 0, ctypes.addressof(buf), 8) == 7   # truncated
     assert L.w4a16_describe(0, 4096, 4096, 128, 0, ctypes.addressof(buf), 8) == w4a16.ERR_INVALID
     assert L.w4a16_describe(1, 4096, 4096, 128, 0, 0, 8) == w4a16.ERR_INVALID
+
+
+def test_forced_decode_slices_size_the_workspace_for_the_tail():
+    """M > 32 on the forced decode path runs 32-row slices; the trailing
+    M % 32 rows may take a split-K configuration that the full slices do
+    not, and the workspace size covers it (M = 33: a one-row slice)."""
+    need = w4a16.workspace_bytes(33, 8192, 6144, path="decode")
+    tail = w4a16.workspace_bytes(1, 8192, 6144, path="decode")
+    full = w4a16.workspace_bytes(32, 8192, 6144, path="decode")
+    assert need == max(tail, full) and need > 0
+    d = w4a16.describe(33, 8192, 6144, path="decode")
+    assert "(x1 row slices of 32); last 1 rows: " in d, d
+
+
+def test_decode_offsets_fall_back_to_prefill():
+    """Shapes whose activation rows or strips exceed the decode kernels'
+    32-bit offsets: the automatic path runs the prefill kernel instead and
+    says so; a forced decode path is refused."""
+    K = 1 << 27                     # 32 * K * 2 bytes of activations = 8 GiB
+    assert w4a16.select_path(32, 4096, 4096) == "decode"
+    assert w4a16.select_path(32, K, 64) == "prefill"
+    d = w4a16.describe(32, K, 64)
+    assert "(fallback decode-offsets:" in d, d
+    L = w4a16.lib()
+    import ctypes
+    buf = ctypes.create_string_buffer(64)
+    assert L.w4a16_describe(32, K, 64, 128, w4a16.PATH_DECODE, ctypes.addressof(buf),
+                            64) == w4a16.ERR_UNSUPPORTED
+    # M * K * 2 below 4 GiB at M = 1, and K * 16 below 4 GiB: still decode.
+    assert w4a16.select_path(1, 1 << 27, 64) == "decode"
+    assert w4a16.select_path(1, 1 << 28, 64) == "prefill"
+
+
+def test_workspace_calls_without_gpu():
+    """The workspace management calls report the HIP failure on a machine
+    without a GPU instead of crashing."""
+    import torch as T
+    if T.cuda.is_available():
+        pytest.skip("host-only check")
+    assert w4a16.lib().w4a16_reserve_workspace(-1) == w4a16.ERR_INVALID
+    assert w4a16.lib().w4a16_reserve_workspace(1024) == w4a16.ERR_HIP
+    assert w4a16.last_fallback() == ""

@@ -407,14 +407,17 @@ def test_prefill2_split_k_bit_exact_integer_inputs(monkeypatch):
         assert np.array_equal(out.astype(np.float64), C)
 
 
+@pytest.mark.parametrize("path", ["prefill", "dense"])
 @pytest.mark.parametrize("M,K,N,swiglu", [(40, 1024, 1088, False), (130, 1152, 2112, True),
                                           (300, 2048, 4096, False)])
-def test_prefill_one_wave_kernel(monkeypatch, M, K, N, swiglu):
-    """The one-wave-per-SIMD mainloop, which the fused path falls back to
-    when an operand exceeds 32-bit buffer offsets (forced here)."""
+def test_prefill_one_wave_kernel(monkeypatch, path, M, K, N, swiglu):
+    """The one-wave-per-SIMD mainloop, which the fused path and the dense
+    tier fall back to when an operand exceeds 32-bit buffer offsets (forced
+    here)."""
     monkeypatch.setenv("W4A16_PREFILL_V2", "0")
-    assert w4a16.describe(M, K, N, swiglu=swiglu, path="prefill").startswith("prefill_kernel<")
-    gemm_case(M, K, N, swiglu=swiglu, path="prefill", seed=M + K)
+    d = w4a16.describe(M, K, N, swiglu=swiglu, path=path)
+    assert ("prefill_kernel<" if path == "prefill" else "; prefill_kernel<") in d, d
+    gemm_case(M, K, N, swiglu=swiglu, path=path, seed=M + K)
 
 
 def test_measurement_probes_run():

@@ -30,8 +30,17 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src: str) -> str:
+def _headers_mtime() -> float:
+    hs = [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".h")]
+    hs.append(os.path.join(INCLUDE, "w4a16.h"))
+    return max(os.path.getmtime(h) for h in hs)
+
+
+def _compile(src: str, incremental: bool = False) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+    if incremental and os.path.exists(obj) and os.path.getmtime(obj) > max(
+            os.path.getmtime(src), _headers_mtime()):
+        return obj
     cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -39,11 +48,13 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, incremental: bool = False) -> str:
+    """Compile every source (incremental: only those newer than their object
+    file, for development) and link the library."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     srcs = sources()
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
+        objs = list(ex.map(lambda s: _compile(s, incremental), srcs))
     tmp = LIBRARY + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -56,5 +67,5 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, incremental="--incremental" in sys.argv)
     sys.exit(0)

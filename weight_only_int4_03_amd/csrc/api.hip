@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <cstring>
 #include <mutex>
+#include <set>
 #include <string>
 #include <thread>
 #include <vector>
@@ -63,42 +64,107 @@ int check_gpu_shape(int64_t K, int64_t N, int G, const char *who) {
 // ---------------------------------------------------------------------------
 // Library-owned per-device workspace (split-K partials, dense-tier scratch).
 // It holds no state between calls: every call writes what it later reads.
+//
+// A GEMM call never synchronises and never frees: when a call needs more than
+// the device's workspace holds, a larger buffer is allocated (outside stream
+// capture only) and the old one is retired, to be freed by the next
+// w4a16_reserve_workspace or w4a16_release_workspace, which synchronise the
+// device first.  Under capture a call that needs more returns
+// W4A16_ERR_WORKSPACE: size the workspace with w4a16_reserve_workspace
+// before capturing.
 
 struct DeviceWorkspace {
   void *ptr = nullptr;
   int64_t bytes = 0;
+  std::vector<void *> retired;  // replaced buffers, possibly still in use by queued kernels
 };
 
 std::mutex g_ws_mutex;
 std::vector<DeviceWorkspace> g_ws;
 
-int device_workspace(int64_t need, void **out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  std::lock_guard<std::mutex> lock(g_ws_mutex);
+int current_device(int *dev) {
+  hipError_t e = hipGetDevice(dev);
+  return e == hipSuccess ? W4A16_OK : hip_fail(e, "hipGetDevice");
+}
+
+DeviceWorkspace &workspace_of(int dev) {
   if ((int)g_ws.size() <= dev) g_ws.resize(dev + 1);
-  DeviceWorkspace &w = g_ws[dev];
+  return g_ws[dev];
+}
+
+// True when `stream` is recording into a HIP graph.
+bool capturing(hipStream_t stream) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &st) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return st != hipStreamCaptureStatusNone;
+}
+
+int device_workspace(int64_t need, hipStream_t stream, void **out) {
+  int dev = 0;
+  int rc = current_device(&dev);
+  if (rc != W4A16_OK) return rc;
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  DeviceWorkspace &w = workspace_of(dev);
   if (w.bytes < need) {
-    if (w.ptr != nullptr) {
-      e = hipDeviceSynchronize();
-      if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
-      hipFree(w.ptr);
-      w.ptr = nullptr;
-      w.bytes = 0;
-    }
-    int64_t bytes = need + need / 4;  // some headroom for later, larger calls
-    e = hipMalloc(&w.ptr, (size_t)bytes);
-    if (e != hipSuccess) {
-      w.ptr = nullptr;
+    if (capturing(stream))
+      return fail(W4A16_ERR_WORKSPACE,
+                  "the library workspace holds %lld bytes and this call needs %lld; a call under "
+                  "stream capture does not allocate: call w4a16_reserve_workspace(%lld) first",
+                  (long long)w.bytes, (long long)need, (long long)need);
+    const int64_t bytes = need + need / 4;  // some headroom for later, larger calls
+    void *p = nullptr;
+    hipError_t e = hipMalloc(&p, (size_t)bytes);
+    if (e != hipSuccess)
       return fail(W4A16_ERR_WORKSPACE, "workspace allocation of %lld bytes failed: %s",
                   (long long)bytes, hipGetErrorString(e));
-    }
+    if (w.ptr != nullptr) w.retired.push_back(w.ptr);
+    w.ptr = p;
     w.bytes = bytes;
   }
   *out = w.ptr;
   return W4A16_OK;
 }
+
+// Synchronise the device and free its retired buffers (and, with all, the
+// current one).  Called with g_ws_mutex held.
+int drain_workspace(DeviceWorkspace &w, bool all) {
+  if (w.retired.empty() && !(all && w.ptr != nullptr)) return W4A16_OK;
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+  for (void *p : w.retired) (void)hipFree(p);
+  w.retired.clear();
+  if (all && w.ptr != nullptr) {
+    (void)hipFree(w.ptr);
+    w.ptr = nullptr;
+    w.bytes = 0;
+  }
+  return W4A16_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Fallbacks.  A shape that the selected kernel cannot take runs a slower
+// kernel instead; each kind is reported once per process on stderr (the INT4
+// kernels page, section "Integrating a kernel into serving", keeps a logged
+// dequantize-then-matmul fallback), and the most recent one is kept for
+// w4a16_last_fallback.
+
+std::mutex g_fb_mutex;
+std::set<std::string> g_fb_seen;
+std::string g_fb_last;
+
+}  // namespace
+
+void note_fallback(const char *what, const char *who) {
+  std::lock_guard<std::mutex> lock(g_fb_mutex);
+  g_fb_last = std::string(who) + ": " + what;
+  if (g_fb_seen.insert(what).second)
+    fprintf(stderr, "w4a16: fallback in %s: %s (reported once per process)\n", who, what);
+}
+
+namespace {
 
 // ---------------------------------------------------------------------------
 // Dispatch.  Decode streams the weights once per call and wins while the
@@ -118,13 +184,52 @@ int select_path(int64_t M, int64_t K, int64_t N, int bits = 4) {
   return W4A16_PATH_PREFILL;
 }
 
+// The decode kernels form activation and weight offsets in 32 bits: the
+// activation rows of one call (M * K * 2 bytes) and one strip's weights
+// (K / 2 bytes, K for INT8, times 32 columns) must stay below 4 GiB.
+bool decode_fits(const Problem &p) {
+  const int64_t limit = (int64_t)1 << 32;
+  const int64_t m = p.M < kDecodeMaxM ? p.M : kDecodeMaxM;
+  return m * p.K * 2 < limit && p.K * 16 * (p.bits == 8 ? 2 : 1) < limit;
+}
+
+// The path a call takes: the requested (or automatic) path with the
+// fallbacks applied.  *why names the fallback when one replaced the path
+// (nullptr otherwise); a forced decode path that the decode kernels cannot
+// take gives -1.
+int resolve_path(const Problem &p, int requested, const char **why) {
+  *why = nullptr;
+  int path = requested == W4A16_PATH_AUTO ? select_path(p.M, p.K, p.N, p.bits) : requested;
+  if (path == W4A16_PATH_DECODE && !decode_fits(p)) {
+    if (requested == W4A16_PATH_DECODE) return -1;
+    path = W4A16_PATH_PREFILL;
+    *why = "decode-offsets: M*K or K beyond the decode kernels' 32-bit offsets, running the "
+           "prefill path";
+  }
+  if (path == W4A16_PATH_PREFILL && !prefill_fused_available(p)) {
+    path = W4A16_PATH_DENSE;
+    *why = "int8-prefill-dense: INT8 operands beyond the fused kernel's 32-bit offsets, running "
+           "the dense tier (dequantize, then dense GEMM)";
+  }
+  return path;
+}
+
+// Workspace of a call on `path`.  The decode path runs M > 32 in 32-row
+// slices; a trailing slice of M % 32 rows may take another configuration,
+// so the need is the larger of the two slice sizes'.
 int64_t workspace_for(int path, const Problem &p) {
   if (path == W4A16_PATH_DENSE) return dense_workspace_bytes(p);
   if (path == W4A16_PATH_PREFILL) return prefill_workspace_bytes(p);
   if (path == W4A16_PATH_DECODE) {
     Problem q = p;
     q.M = p.M < kDecodeMaxM ? p.M : kDecodeMaxM;
-    return decode_workspace_bytes(q);
+    int64_t need = decode_workspace_bytes(q);
+    if (p.M > kDecodeMaxM && p.M % kDecodeMaxM != 0) {
+      q.M = p.M % kDecodeMaxM;
+      const int64_t tail = decode_workspace_bytes(q);
+      if (tail > need) need = tail;
+    }
+    return need;
   }
   return 0;
 }
@@ -132,7 +237,7 @@ int64_t workspace_for(int path, const Problem &p) {
 int run_gemm(const uint16_t *A, int64_t M, int64_t K, const void *rw, const void *rs, int64_t N,
              int G, uint16_t *out, int flags, void *workspace, int64_t ws_bytes,
              hipStream_t stream, const float *rowscale = nullptr, const void *rz = nullptr,
-             const char *who = nullptr, int bits = 4) {
+             const char *who = nullptr, int bits = 4, bool no_alloc = false) {
   if (who == nullptr) who = (flags & W4A16_FLAG_SWIGLU) ? "w4a16_gemm_swiglu" : "w4a16_gemm";
   const bool bf16 = (flags & W4A16_FLAG_BF16) != 0;
   int rc = check_gpu_shape(K, N, G, who);
@@ -146,24 +251,28 @@ int run_gemm(const uint16_t *A, int64_t M, int64_t K, const void *rw, const void
   if (!A || !rw || !rs || !out) return fail(W4A16_ERR_INVALID, "%s: null pointer", who);
   if (!aligned16(A) || !aligned16(rw) || !aligned16(rs) || !aligned16(out) || !aligned16(rz))
     return fail(W4A16_ERR_INVALID, "%s: device pointers must be 16-byte aligned", who);
-  int path = flags & 0xF;
-  if (path == W4A16_PATH_AUTO) path = select_path(M, K, N, bits);
-  if (path < W4A16_PATH_DECODE || path > W4A16_PATH_DENSE)
-    return fail(W4A16_ERR_INVALID, "%s: unknown path %d", who, path);
+  const int requested = flags & 0xF;
+  if (requested > W4A16_PATH_DENSE)
+    return fail(W4A16_ERR_INVALID, "%s: unknown path %d", who, requested);
   Problem p{A, M, K, N, rw, rs, out, swiglu, bf16, rowscale, G, group_shift(K, G), rz,
             rz != nullptr, bits};
-  if (path == W4A16_PATH_PREFILL && !prefill_fused_available(p)) path = W4A16_PATH_DENSE;
+  const char *why = nullptr;
+  const int path = resolve_path(p, requested, &why);
+  if (path < 0)
+    return fail(W4A16_ERR_UNSUPPORTED,
+                "%s: the decode path takes M*K*2 and 16*K (32*K for INT8) below 2^32", who);
   const int64_t need = workspace_for(path, p);
   void *ws = workspace;
   if (need > 0) {
-    if (ws == nullptr) {
-      rc = device_workspace(need, &ws);
+    if (ws == nullptr && !no_alloc) {
+      rc = device_workspace(need, stream, &ws);
       if (rc != W4A16_OK) return rc;
     } else if (ws_bytes < need || ((uintptr_t)ws & 255u) != 0) {
-      return fail(W4A16_ERR_WORKSPACE, "%s: workspace needs %lld bytes, 256-byte aligned", who,
-                  (long long)need);
+      return fail(W4A16_ERR_WORKSPACE, "%s: workspace needs %lld bytes, 256-byte aligned%s", who,
+                  (long long)need, no_alloc ? " (beyond this entry point's fixed scratch)" : "");
     }
   }
+  if (why != nullptr) note_fallback(why, who);
 
   hipError_t e = hipSuccess;
   if (path == W4A16_PATH_DECODE) {
@@ -509,12 +618,13 @@ int64_t w4a16_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N, int G, int f
   if (rc != W4A16_OK) return rc;
   if (M <= 0) return 0;
   const int bits = (flags & W4A16_FLAG_INT8) ? 8 : 4;
-  int path = flags & 0xF;
-  if (path == W4A16_PATH_AUTO) path = select_path(M, K, N, bits);
   Problem p{nullptr, M, K, N, nullptr, nullptr, nullptr, (flags & W4A16_FLAG_SWIGLU) != 0,
             (flags & W4A16_FLAG_BF16) != 0, nullptr, G, group_shift(K, G), nullptr,
             (flags & W4A16_FLAG_ZP) != 0, bits};
-  if (path == W4A16_PATH_PREFILL && !prefill_fused_available(p)) path = W4A16_PATH_DENSE;
+  const char *why = nullptr;
+  const int path = resolve_path(p, flags & 0xF, &why);
+  if (path < 0)
+    return fail(W4A16_ERR_UNSUPPORTED, "w4a16_gemm_workspace_bytes: beyond the decode path");
   return workspace_for(path, p);
 }
 
@@ -532,14 +642,15 @@ int w4a16_describe(int64_t M, int64_t K, int64_t N, int G, int flags, char *buf,
   if (swiglu && N % 64 != 0)
     return fail(W4A16_ERR_INVALID, "w4a16_describe: N (%lld) must be a multiple of 64",
                 (long long)N);
-  int path = flags & 0xF;
-  if (path == W4A16_PATH_AUTO) path = select_path(M, K, N, bits);
-  if (path < W4A16_PATH_DECODE || path > W4A16_PATH_DENSE)
-    return fail(W4A16_ERR_INVALID, "w4a16_describe: unknown path %d", path);
+  if ((flags & 0xF) > W4A16_PATH_DENSE)
+    return fail(W4A16_ERR_INVALID, "w4a16_describe: unknown path %d", flags & 0xF);
   Problem p{nullptr, M, K, N, nullptr, nullptr, nullptr, swiglu, (flags & W4A16_FLAG_BF16) != 0,
             nullptr, G, group_shift(K, G), nullptr, (flags & W4A16_FLAG_ZP) != 0, bits};
-  if (path == W4A16_PATH_PREFILL && !prefill_fused_available(p)) path = W4A16_PATH_DENSE;
-  char tmp[512];
+  const char *why = nullptr;
+  const int path = resolve_path(p, flags & 0xF, &why);
+  if (path < 0)
+    return fail(W4A16_ERR_UNSUPPORTED, "w4a16_describe: beyond the decode kernels' offsets");
+  char tmp[1024];
   int k;
   if (path == W4A16_PATH_DECODE) {
     Problem q = p;
@@ -547,10 +658,22 @@ int w4a16_describe(int64_t M, int64_t K, int64_t N, int G, int flags, char *buf,
     k = decode_describe(q, tmp, sizeof tmp);
     const int64_t slices = ceil_div(M, kDecodeMaxM);
     if (slices > 1 && k > 0 && k < (int)sizeof tmp)
-      k += snprintf(tmp + k, sizeof tmp - k, " (x%lld row slices of 32)", (long long)slices);
+      k += snprintf(tmp + k, sizeof tmp - k, " (x%lld row slices of 32)", (long long)(M / 32));
+    if (slices > 1 && M % kDecodeMaxM != 0 && k > 0 && k < (int)sizeof tmp) {
+      // The trailing slice may take another configuration.
+      q.M = M % kDecodeMaxM;
+      k += snprintf(tmp + k, sizeof tmp - k, "; last %lld rows: ", (long long)q.M);
+      if (k > 0 && k < (int)sizeof tmp) {
+        const int t = decode_describe(q, tmp + k, sizeof tmp - k);
+        if (t < 0) return fail(W4A16_ERR_INVALID, "w4a16_describe: formatting failed");
+        k += t;
+      }
+    }
   } else {
     k = tiled_describe(p, path == W4A16_PATH_DENSE, tmp, sizeof tmp);
   }
+  if (why != nullptr && k > 0 && k < (int)sizeof tmp)
+    k += snprintf(tmp + k, sizeof tmp - k, " (fallback %s)", why);
   if (k < 0) return fail(W4A16_ERR_INVALID, "w4a16_describe: formatting failed");
   snprintf(buf, (size_t)len, "%s", tmp);
   return k < len ? k : (int)(len - 1);
@@ -560,7 +683,58 @@ int w4a16_select_path(int64_t M, int64_t K, int64_t N, int G, int flags) {
   int rc = check_gpu_shape(K, N, G, "w4a16_select_path");
   if (rc != W4A16_OK) return rc;
   if (M < 0) return fail(W4A16_ERR_INVALID, "w4a16_select_path: M must be >= 0");
-  return select_path(M, K, N, (flags & W4A16_FLAG_INT8) ? 8 : 4);
+  Problem p{nullptr, M, K, N, nullptr, nullptr, nullptr, (flags & W4A16_FLAG_SWIGLU) != 0,
+            (flags & W4A16_FLAG_BF16) != 0, nullptr, G, group_shift(K, G), nullptr,
+            (flags & W4A16_FLAG_ZP) != 0, (flags & W4A16_FLAG_INT8) ? 8 : 4};
+  const char *why = nullptr;
+  return resolve_path(p, W4A16_PATH_AUTO, &why);
+}
+
+int w4a16_reserve_workspace(int64_t bytes) {
+  if (bytes < 0) return fail(W4A16_ERR_INVALID, "w4a16_reserve_workspace: bytes must be >= 0");
+  int dev = 0;
+  int rc = current_device(&dev);
+  if (rc != W4A16_OK) return rc;
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  DeviceWorkspace &w = workspace_of(dev);
+  if (w.bytes >= bytes) return drain_workspace(w, false);
+  if (w.ptr != nullptr) w.retired.push_back(w.ptr);
+  w.ptr = nullptr;
+  w.bytes = 0;
+  rc = drain_workspace(w, false);
+  if (rc != W4A16_OK) return rc;
+  if (bytes == 0) return W4A16_OK;
+  void *p = nullptr;
+  hipError_t e = hipMalloc(&p, (size_t)bytes);
+  if (e != hipSuccess)
+    return fail(W4A16_ERR_WORKSPACE, "w4a16_reserve_workspace: allocation of %lld bytes failed: %s",
+                (long long)bytes, hipGetErrorString(e));
+  w.ptr = p;
+  w.bytes = bytes;
+  return W4A16_OK;
+}
+
+int64_t w4a16_workspace_reserved(void) {
+  int dev = 0;
+  int rc = current_device(&dev);
+  if (rc != W4A16_OK) return rc;
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  return workspace_of(dev).bytes;
+}
+
+int w4a16_release_workspace(void) {
+  int dev = 0;
+  int rc = current_device(&dev);
+  if (rc != W4A16_OK) return rc;
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  return drain_workspace(workspace_of(dev), true);
+}
+
+const char *w4a16_last_fallback(void) {
+  static thread_local std::string copy;
+  std::lock_guard<std::mutex> lock(g_fb_mutex);
+  copy = g_fb_last;
+  return copy.c_str();
 }
 
 }  // extern "C"

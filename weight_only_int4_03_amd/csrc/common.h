@@ -370,6 +370,10 @@ hipError_t launch_dequant_canonical(const void *rw, const void *rs, const void *
 hipError_t launch_dequant_fragment(const void *rw, const void *rs, const void *rz, int64_t K,
                                    int64_t N, int G, bool bf16, uint16_t *Wf, hipStream_t s);
 
+// Reports a fallback (a slower kernel taking a shape the selected one cannot):
+// once per kind `what` on stderr, and as w4a16_last_fallback (api.hip).
+void note_fallback(const char *what, const char *who);
+
 // Decode path: workspace bytes (split-K partials), the launch, and a text
 // description of the launch (kernel instances and grid).
 int64_t decode_workspace_bytes(const Problem &p);

@@ -484,7 +484,7 @@ bool coop_config(const Problem &p, int &WC, int &WK, int &KS) {
     KS = 1;
     if (WC > 1)
       while ((int64_t)ceil_div(nsg, WC) * KS * 2 <= 256 && KG / (KS * 2) >= 8) KS *= 2;
-  } else if (p.M == 1 && nsg >= 512 && p.bits == 4 && !p.zp && !p.bf16) {
+  } else if (p.M == 1 && p.swiglu && nsg >= 512 && p.bits == 4 && !p.zp && !p.bf16) {
     // The widest fused projections at M = 1 (Llama-70B gate/up): the
     // per-wave kernel, which stages the activation row per wave without
     // workgroup barriers, measured 42.7 us against 46.5 us.

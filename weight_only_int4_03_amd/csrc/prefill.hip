@@ -662,10 +662,9 @@ static int k_slices(int64_t tiles, int nsteps, int cus) {
   return ks;
 }
 
-// false: the one-wave kernel (prefill_kernel) runs instead.  The fused path
-// always takes prefill2_kernel (unless an operand is too large for 32-bit
-// offsets or W4A16_PREFILL_V2=0); the dense tier keeps prefill_kernel unless
-// W4A16_PREFILL_V2=1.
+// false: the one-wave kernel (prefill_kernel) runs instead.  Both the fused
+// path and the dense tier take prefill2_kernel unless an operand is too large
+// for 32-bit offsets (a logged fallback) or W4A16_PREFILL_V2=0.
 //
 // Tile rows (64, 128 or 256) come from a small time model fitted to
 // measurements on MI355X: a workgroup of a BM-row tile over a k range of
@@ -682,7 +681,7 @@ static int k_slices(int64_t tiles, int nsteps, int cus) {
 // override.
 static bool prefill2_config(const Problem &p, bool dense, Prefill2Config &c) {
   const char *v = std::getenv("W4A16_PREFILL_V2");
-  const bool on = v != nullptr ? *v == '1' : !dense;
+  const bool on = v == nullptr || *v != '0';
   if (!on || !fits_buffer_offsets(p, dense)) return false;
   const int cus = device_cus();
   const int64_t NS = ceil_div(p.N, kStrip);
@@ -792,9 +791,16 @@ int64_t prefill_workspace_bytes(const Problem &p) {
   return (int64_t)c.ks * p.M * p.N * (int64_t)sizeof(float);
 }
 
+static const char *kOneWaveFallback =
+    "prefill-one-wave: operands beyond the 8-wave kernel's 32-bit offsets (or "
+    "W4A16_PREFILL_V2=0), running the one-wave kernel";
+
 hipError_t launch_prefill(const Problem &p, void *workspace, hipStream_t s) {
   Prefill2Config c;
-  if (!prefill2_config(p, false, c)) return launch_tiled<false>(p, p.rw, s);
+  if (!prefill2_config(p, false, c)) {
+    note_fallback(kOneWaveFallback, "fused prefill");
+    return launch_tiled<false>(p, p.rw, s);
+  }
   if (c.ks > 1 && workspace == nullptr) return hipErrorInvalidValue;
   if (c.wm == 1)
     return c.bm == 64 ? launch_prefill2_m<2, 1, false>(p, p.rw, c, workspace, s)
@@ -845,6 +851,7 @@ hipError_t launch_dense(const Problem &p, void *workspace, hipStream_t s) {
   if (e != hipSuccess) return e;
   Prefill2Config c;
   if (prefill2_config(p, true, c)) return launch_prefill2_m<4, 2, true>(p, w16f, c, nullptr, s);
+  note_fallback(kOneWaveFallback, "dense tier");
   return launch_tiled<true>(p, w16f, s);
 }
 

@@ -77,6 +77,10 @@ _SIGNATURES = {
     "w4a16_describe": ([_i64, _i64, _i64, _int, _int, _p, _i64], _int),
     "w4a16_probe_stream_read": ([_p, _i64, _p, _p], _int),
     "w4a16_probe_mfma": ([_i64, _i64, _p, _p, _p], _int),
+    "w4a16_reserve_workspace": ([_i64], _int),
+    "w4a16_workspace_reserved": ([], _i64),
+    "w4a16_release_workspace": ([], _int),
+    "w4a16_last_fallback": ([], ctypes.c_char_p),
     "w4a16_last_error": ([], ctypes.c_char_p),
     "w4a16_version": ([], ctypes.c_char_p),
 }
@@ -371,10 +375,28 @@ def select_path(M: int, K: int, N: int, swiglu: bool = False, G: int = G,
 def describe(M: int, K: int, N: int, swiglu: bool = False, path: str | int = "auto",
              G: int = G, bf16: bool = False, zp: bool = False, int8: bool = False) -> str:
     """The kernel launches (profiler names and grids) a GEMM of this shape makes."""
-    buf = ctypes.create_string_buffer(512)
+    buf = ctypes.create_string_buffer(1024)
     _check(lib().w4a16_describe(M, K, N, G, _flags(path, swiglu, bf16, zp, int8),
                                 ctypes.addressof(buf), len(buf)))
     return buf.value.decode()
+
+
+def reserve_workspace(nbytes: int) -> None:
+    """Grow the current device's library workspace to at least nbytes (a
+    load-time call: it may synchronise the device)."""
+    _check(lib().w4a16_reserve_workspace(int(nbytes)))
+
+
+def workspace_reserved() -> int:
+    return _check(lib().w4a16_workspace_reserved())
+
+
+def release_workspace() -> None:
+    _check(lib().w4a16_release_workspace())
+
+
+def last_fallback() -> str:
+    return lib().w4a16_last_fallback().decode()
 
 
 def probe_stream_read(buf, sink, stream=None) -> None:
@@ -402,24 +424,6 @@ def load_weight(W_host: np.ndarray, device="cuda", G: int = G, gamma=None) -> Re
     packed, scales = pack(Wd, G, gamma=gd)
     del Wd
     return repack(packed, scales, G)
-
-
-def load_weight_zp(q: np.ndarray, scales: np.ndarray, zeros: np.ndarray, device="cuda",
-                   G: int = G) -> RepackedWeight:
-    """Asymmetric (AWQ-style) host weights -> device: nibbles q [K,N] (uint8,
-    0..15), fp16 scale bits [K/G,N] and zero points [K/G,N] (uint8); packs q
-    in the canonical format on the host (eight nibbles per int32 along K),
-    repacks, and builds the prescaled zero rows."""
-    torch = _torch()
-    q = np.ascontiguousarray(q, dtype=np.uint8)
-    K, N = q.shape
-    words = np.zeros((K // 8, N), np.uint32)
-    for i in range(8):
-        words |= (q[i::8].astype(np.uint32) & 0xF) << np.uint32(4 * i)
-    packed = torch.from_numpy(words.view(np.int32)).to(device)
-    sd = torch.from_numpy(np.ascontiguousarray(scales, dtype=np.uint16).view(np.int16)).to(device)
-    zd = torch.from_numpy(np.ascontiguousarray(zeros, dtype=np.uint8)).to(device)
-    return zero_rows(repack(packed, sd, G), sd, zd)
 
 
 def load_weight_int8(W_host: np.ndarray, device="cuda", G: int = G) -> RepackedWeight:
