@@ -270,6 +270,25 @@ int w4a16_gemm_ex(const uint16_t *A_d, int64_t M, int64_t K, const void *rw_d,
                   const void *rs_d, int64_t N, int G, uint16_t *out_d, int flags,
                   void *workspace_d, int64_t workspace_bytes, w4a16_stream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops, harnesses that forbid allocation): w4a16_gemm_ex
+ * with the split-K partials in a fixed scratch array that the library holds
+ * per GPU (w4a16_noalloc_scratch_bytes() bytes, 64 MiB, allocated with the
+ * library's code object and held until the process ends) instead of a
+ * workspace.  Same flags (path | W4A16_FLAG_SWIGLU | W4A16_FLAG_BF16),
+ * arguments, outputs and results as w4a16_gemm_ex; the call makes no
+ * allocation, free or synchronisation of any kind.  A problem whose
+ * workspace (w4a16_gemm_workspace_bytes) exceeds the scratch returns
+ * W4A16_ERR_WORKSPACE before any launch (e.g. the dense tier of a large
+ * weight).  All calls on one GPU share its scratch: calls that overlap in
+ * time on one GPU (different streams) race and must not be issued; calls on
+ * one stream are safe.  The first call on each device looks up the scratch's
+ * device address (make it outside capture). */
+int w4a16_gemm_noalloc(const uint16_t *A_d, int64_t M, int64_t K, const void *rw_d,
+                       const void *rs_d, int64_t N, int G, uint16_t *out_d, int flags,
+                       w4a16_stream_t stream);
+int64_t w4a16_noalloc_scratch_bytes(void);
+
 /* GEMM with a per-row output factor (FuTransformer, section 3.2.2: the
  * RMSNorm row factor rho_m of the raw activations, applied in the GEMM's
  * epilogue): out[m,n] = rowscale[m] * sum_k A[m,k] * w[k,n], and with

@@ -145,6 +145,40 @@ int drain_workspace(DeviceWorkspace &w, bool all) {
 }
 
 // ---------------------------------------------------------------------------
+// Fixed scratch of w4a16_gemm_noalloc, for callers that cannot allocate (code
+// under stream capture, serving loops that forbid allocation): the split-K
+// partials of a call live in this array, one copy per GPU, held until the
+// process ends.  Host code never passes the array's name to a kernel (on the
+// host it is only a stand-in for the symbol): the device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current.
+// Every call on a GPU shares that GPU's copy, so calls that overlap in time on
+// one GPU race.  Nothing in it needs clearing: each call writes every element
+// it later reads.
+constexpr int64_t kScratchBytes = (int64_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mutex;
+std::vector<void *> g_scratch;  // device address of `scratch`, per device (null: not looked up)
+
+int scratch_address(void **out) {
+  int dev = 0;
+  int rc = current_device(&dev);
+  if (rc != W4A16_OK) return rc;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if ((int)g_scratch.size() <= dev) g_scratch.resize(dev + 1, nullptr);
+  if (g_scratch[dev] == nullptr) {
+    void *p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (p == nullptr || ((uintptr_t)p & 255u) != 0)
+      return fail(W4A16_ERR_HIP, "scratch symbol has no 256-byte aligned device address");
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return W4A16_OK;
+}
+
+// ---------------------------------------------------------------------------
 // Fallbacks.  A shape that the selected kernel cannot take runs a slower
 // kernel instead; each kind is reported once per process on stderr (the INT4
 // kernels page, section "Integrating a kernel into serving", keeps a logged
@@ -572,6 +606,21 @@ int w4a16_gemm_ex(const uint16_t *A_d, int64_t M, int64_t K, const void *rw_d, c
   return run_gemm(A_d, M, K, rw_d, rs_d, N, G, out_d, flags, workspace_d, workspace_bytes,
                   (hipStream_t)stream);
 }
+
+int w4a16_gemm_noalloc(const uint16_t *A_d, int64_t M, int64_t K, const void *rw_d,
+                       const void *rs_d, int64_t N, int G, uint16_t *out_d, int flags,
+                       w4a16_stream_t stream) {
+  const char *who = "w4a16_gemm_noalloc";
+  if (flags & ~(0xF | W4A16_FLAG_SWIGLU | W4A16_FLAG_BF16))
+    return fail(W4A16_ERR_INVALID, "%s: unknown flags 0x%x", who, flags);
+  void *ws = nullptr;
+  int rc = scratch_address(&ws);
+  if (rc != W4A16_OK) return rc;
+  return run_gemm(A_d, M, K, rw_d, rs_d, N, G, out_d, flags, ws, kScratchBytes,
+                  (hipStream_t)stream, nullptr, nullptr, who, 4, true);
+}
+
+int64_t w4a16_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 int w4a16_gemm_rowscale(const uint16_t *A_d, int64_t M, int64_t K, const void *rw_d,
                         const void *rs_d, int64_t N, int G, const float *rowscale_d,

@@ -72,6 +72,8 @@ _SIGNATURES = {
     "w4a16_gemm": ([_p, _i64, _i64, _p, _p, _i64, _int, _p, _p], _int),
     "w4a16_gemm_swiglu": ([_p, _i64, _i64, _p, _p, _i64, _int, _p, _p], _int),
     "w4a16_gemm_ex": ([_p, _i64, _i64, _p, _p, _i64, _int, _p, _int, _p, _i64, _p], _int),
+    "w4a16_gemm_noalloc": ([_p, _i64, _i64, _p, _p, _i64, _int, _p, _int, _p], _int),
+    "w4a16_noalloc_scratch_bytes": ([], _i64),
     "w4a16_gemm_workspace_bytes": ([_i64, _i64, _i64, _int, _int], _i64),
     "w4a16_select_path": ([_i64, _i64, _i64, _int, _int], _int),
     "w4a16_describe": ([_i64, _i64, _i64, _int, _int, _p, _i64], _int),
@@ -321,6 +323,24 @@ def gemm(A, w: RepackedWeight, swiglu: bool = False, path: str | int = "auto", o
         _check(lib().w4a16_gemm_rowscale(_ptr(A), M, K, _ptr(w.rw), _ptr(w.rs), w.N, G,
                                          _ptr(rowscale), _ptr(out), flags, _ptr(workspace),
                                          ws_bytes, _stream(stream)))
+    return out
+
+
+def gemm_noalloc(A, w: RepackedWeight, swiglu: bool = False, path: str | int = "auto", out=None,
+                 G: int | None = None, stream=None):
+    """w4a16_gemm_noalloc: as :func:`gemm` (fp16 or bf16 INT4 weights without
+    zero points or row factor) with the split-K partials in the library's
+    fixed per-GPU scratch; makes no allocation."""
+    torch = _torch()
+    G = w.G if G is None else G
+    assert A.is_cuda and A.dtype in (torch.float16, torch.bfloat16) and A.is_contiguous()
+    assert w.bits == 4 and w.rz is None
+    M, K = A.shape
+    if out is None:
+        out = torch.empty((M, w.N // 2 if swiglu else w.N), dtype=A.dtype, device=A.device)
+    _check(lib().w4a16_gemm_noalloc(_ptr(A), M, K, _ptr(w.rw), _ptr(w.rs), w.N, G, _ptr(out),
+                                    _flags(path, swiglu, A.dtype == torch.bfloat16),
+                                    _stream(stream)))
     return out
 
 
