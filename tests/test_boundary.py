@@ -227,10 +227,19 @@ def test_describe_names_the_launches():
         4096, 4096, 28672, swiglu=True)
     assert "prefill2_kernel<4, 2, 4, 2, false, true, true, false, 4>" in w4a16.describe(
         4096, 4096, 28672, swiglu=True, bf16=True)
-    # Transition batches: 64-row tiles, the eight waves side by side.
+    # Transition batches: the skinny-tile kernel (64-row tiles with four waves
+    # along K up to M = 64, 128-row tiles with two above), K split only where
+    # the tiles leave CUs idle; above M = 256 the prefill tiles.
+    assert w4a16.describe(64, 4096, 28672, swiglu=True).startswith(
+        "transition_kernel<2, 2, 4, true, false, false, 4> workgroups=224 threads=512 ks=1")
     assert w4a16.describe(256, 4096, 28672, swiglu=True).startswith(
-        "prefill2_kernel<2, 1, 8, 2, false, true, false, false, 4> workgroups=224 threads=512 ks=1")
+        "transition_kernel<4, 4, 2, true, false, false, 4> workgroups=224 threads=512 ks=1")
+    assert w4a16.describe(64, 14336, 4096).startswith(
+        "transition_kernel<2, 2, 4, false, false, false, 4> workgroups=256 threads=512 ks=8; "
+        "prefill_reduce_kernel<false, false>")
     assert w4a16.describe(300, 4096, 28672, swiglu=True).startswith("prefill2_kernel<4, 2, 4, 2")
+    assert w4a16.describe(33, 4096, 4096).startswith("transition_kernel<2, ")
+    assert w4a16.describe(257, 4096, 4096).startswith("prefill2_kernel<")
     # Zero rows: both decode kernels scale before the MFMA (ZP instances),
     # prefill takes the ZP instance, the dense tier folds them into its dequant.
     d = w4a16.describe(1, 4096, 28672, swiglu=True, zp=True)
@@ -244,8 +253,9 @@ def test_describe_names_the_launches():
     assert d.startswith("decode_coop_kernel<16, 2, 1, 4, 1, true, false, false, 8>"), d
     d = w4a16.describe(3, 4096, 4096, bf16=True, int8=True)
     assert d.split(">")[0].endswith("false, true, true, false, true, 8"), d
-    assert w4a16.describe(100, 4096, 4096, int8=True).startswith("prefill2_kernel<")
+    assert w4a16.describe(100, 4096, 4096, int8=True).startswith("transition_kernel<2, ")
     assert w4a16.describe(100, 4096, 4096, int8=True).split(">")[0].endswith(", 8")
+    assert w4a16.describe(400, 4096, 4096, int8=True).startswith("prefill2_kernel<")
     assert w4a16.describe(100, 4096, 4096, path="dense", int8=True).startswith(
         "dequant8_kernel<false, false>; ")
     assert w4a16.select_path(100, 4096, 4096, int8=True) == "prefill"
@@ -253,7 +263,7 @@ def test_describe_names_the_launches():
         4096, 4096, 4096, zp=True)
     assert w4a16.describe(4096, 4096, 4096, path="dense", zp=True).startswith(
         "dequant_kernel<false, false>; prefill")
-    assert w4a16.describe(64, 14336, 4096).endswith("ks=16; prefill_reduce_kernel<false, false>")
+    assert w4a16.describe(64, 14336, 4096).endswith("ks=8; prefill_reduce_kernel<false, false>")
     assert w4a16.describe(4096, 4096, 4096, path="dense").startswith(
         "dequant_kernel<false, false>; ")
     assert w4a16.describe(4096, 4096, 4096, path="dense", bf16=True).startswith(

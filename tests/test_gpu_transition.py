@@ -1,0 +1,119 @@
+"""GPU parity of the transition-regime kernel (skinny row tiles whose waves
+split K inside the workgroup) against the oracle on the same seeded inputs:
+ragged row counts and column tails, both tile heights, split and unsplit K
+(uneven slices, partial last rounds), the SwiGLU epilogue, bf16 activations,
+zero points, INT8 weights, other group sizes and the row factor; one-hot and
+integer-exact inputs bit for bit."""
+import numpy as np
+import pytest
+
+from gpuhelp import fp16_out, gemm_case, orc, say, to_dev
+from test_gpu_int8 import gemm8_case
+from test_gpu_zero_points import zp_case
+from weight_only_int4_03_amd import synth, w4a16
+
+pytestmark = pytest.mark.gpu
+
+
+def _kernel(M, K, N, swiglu=False, **kw):
+    d = w4a16.describe(M, K, N, swiglu=swiglu, path="prefill", **kw)
+    assert d.startswith("transition_kernel<"), d
+    return d
+
+
+@pytest.mark.parametrize("M", [33, 50, 64, 65, 100, 128, 129, 200, 256])
+@pytest.mark.parametrize("N", [1088, 1064])
+def test_transition_ragged_auto(M, N):
+    """M = 33 .. 256 take the transition kernel on the automatic path; N = 1064
+    leaves an 8-column tail strip (and an odd strip count: a half-empty strip
+    pair), K = 1152 nine groups (a partial last round)."""
+    d = _kernel(M, 1152, N)
+    say(d)
+    gemm_case(M, 1152, N, seed=M + N)
+
+
+@pytest.mark.parametrize("mi", [2, 4])
+@pytest.mark.parametrize("ks", [1, 2, 3, 5])
+@pytest.mark.parametrize("M,K,N,swiglu", [(70, 2048, 2112, True), (130, 3072, 1064, False)])
+def test_transition_tiles_and_slices(monkeypatch, mi, ks, M, K, N, swiglu):
+    """Both tile heights (64 rows with four waves along K, 128 rows with two)
+    and forced K slices, including uneven slices and slices shorter than a
+    round; N = 2112 with SwiGLU gives 33 gate strips."""
+    monkeypatch.setenv("W4A16_TRANSITION_MI", str(mi))
+    monkeypatch.setenv("W4A16_TRANSITION_KS", str(ks))
+    d = _kernel(M, K, N, swiglu)
+    assert d.startswith("transition_kernel<%d, " % mi) and ("ks=%d" % ks) in d, d
+    gemm_case(M, K, N, swiglu=swiglu, path="prefill", seed=M + K + ks)
+
+
+@pytest.mark.parametrize("M", [1, 17, 32, 300])
+def test_transition_forced_outside_its_range(monkeypatch, M):
+    """Forced on, the kernel also takes row counts outside its default range
+    (one row, a partial single tile, several 128-row tiles)."""
+    monkeypatch.setenv("W4A16_TRANSITION", "1")
+    _kernel(M, 1024, 1088)
+    gemm_case(M, 1024, 1088, path="prefill", seed=M)
+
+
+@pytest.mark.parametrize("mi", [2, 4])
+@pytest.mark.parametrize("M", [64, 130])
+def test_transition_onehot_rows_bit_exact(monkeypatch, mi, M):
+    """One-hot activation rows return dequantized weight rows bit for bit
+    (every nibble value; pins the staged activation swizzle and the weight
+    layout)."""
+    monkeypatch.setenv("W4A16_TRANSITION", "1")
+    monkeypatch.setenv("W4A16_TRANSITION_MI", str(mi))
+    K, N = 2048, 1056
+    packed, scales = synth.random_words(K, N, seed=M + mi)
+    w = w4a16.repack(to_dev(packed), to_dev(scales.view(np.int16)))
+    A, ks = synth.onehot_activations(M, K, seed=M)
+    _kernel(M, K, N)
+    out = fp16_out(w4a16.gemm(to_dev(A), w, path="prefill"))
+    want = orc().dequant(packed, scales)[ks].view(np.float16).astype(np.float64)
+    assert np.array_equal(out.astype(np.float64), want)
+
+
+@pytest.mark.parametrize("M,K,N,ks", [(256, 4096, 4096, 1), (64, 4096, 2048, 1),
+                                      (128, 8192, 1024, 4), (96, 3072, 1088, 3)])
+def test_transition_integer_exact(monkeypatch, M, K, N, ks):
+    """Power-of-two scales and activations in {-1, 0, 1}: every partial sum is
+    exact, so the output equals the oracle's bit for bit whatever the
+    summation order, split K included."""
+    monkeypatch.setenv("W4A16_TRANSITION_KS", str(ks))
+    _kernel(M, K, N)
+    W = synth.grid_weights(K, N, p=4, seed=M + K)
+    A = synth.ternary_activations(M, K, density=0.5, seed=M)
+    out = fp16_out(w4a16.gemm(to_dev(A), w4a16.load_weight(W)))
+    packed_o, s16_o = orc().quantize_pack(W)
+    C = orc().gemm_f64(A, packed_o, s16_o)
+    assert np.abs(C).max() < 128, "inputs not fp16-exact"
+    assert np.array_equal(out.astype(np.float64), C)
+
+
+@pytest.mark.parametrize("M,swiglu", [(48, False), (100, True), (256, False)])
+def test_transition_bf16(M, swiglu):
+    _kernel(M, 2048, 2112, swiglu, bf16=True)
+    gemm_case(M, 2048, 2112, swiglu=swiglu, seed=M, bf16=True)
+
+
+@pytest.mark.parametrize("M,G,swiglu,bf16", [(64, 128, False, False), (100, 64, True, False),
+                                             (200, 128, False, True), (40, 32, True, True)])
+def test_transition_zero_points(M, G, swiglu, bf16):
+    _kernel(M, 2048, 1088 if not swiglu else 2112, swiglu, zp=True, bf16=bf16)
+    zp_case(M, 2048, 1088 if not swiglu else 2112, G=G, swiglu=swiglu, bf16=bf16, seed=M,
+            rowscale=True)
+
+
+@pytest.mark.parametrize("M,G,swiglu,bf16", [(64, 128, False, False), (100, 32, True, False),
+                                             (256, 2048, False, True)])
+def test_transition_int8(M, G, swiglu, bf16):
+    _kernel(M, 2048, 2112, swiglu, int8=True)
+    gemm8_case(M, 2048, 2112, G=G, swiglu=swiglu, bf16=bf16, seed=M, rowscale=True)
+
+
+@pytest.mark.parametrize("G", [32, 64, 2048])
+def test_transition_group_sizes(G):
+    """Groups shorter than the 128-k round unit (scales per 64-k tile and lane
+    half) and channelwise scales."""
+    _kernel(100, 2048, 1088)
+    gemm_case(100, 2048, 1088, seed=G, G=G)

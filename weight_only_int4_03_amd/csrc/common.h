@@ -390,6 +390,20 @@ int64_t dense_workspace_bytes(const Problem &p);
 hipError_t launch_dense(const Problem &p, void *workspace, hipStream_t s);
 int tiled_describe(const Problem &p, bool dense, char *buf, size_t n);
 
+// Transition-regime kernel (transition.hip): launch shape, workspace (FP32
+// partials when K is split), description and launch.  transition_config
+// returns false where the kernel does not take the problem.
+struct TransConfig {
+  int mi, wc, wk, ks, tiles, row_tiles, col_groups;
+};
+bool transition_config(const Problem &p, TransConfig &c);
+int64_t transition_workspace_bytes(const Problem &p);
+int transition_describe(const Problem &p, const TransConfig &c, char *buf, size_t n);
+hipError_t launch_transition(const Problem &p, const TransConfig &c, void *ws, hipStream_t s);
+// Second stage of a split-K tiled GEMM: sums KS FP32 partial slices
+// ws[KS][M][N] in slice order and runs the epilogue into p.out (prefill.hip).
+hipError_t launch_prefill_reduce(const float *ws, int KS, const Problem &p, hipStream_t s);
+
 // Measurement probes (probe.hip).
 hipError_t launch_stream_read(const void *buf, int64_t bytes, void *sink, hipStream_t s);
 hipError_t launch_mfma_peak(int iterations, int64_t workgroups, void *sink, hipStream_t s);

@@ -343,12 +343,15 @@ void prefill2_kernel(PrefillArgs p) {
   const int a_off = (arow0 * p.K + ((slot0 % CH) ^ swz(arow0)) * 8) * 2;
   const int a_rows = (NT / CH) * p.K * 2;  // bytes between successive copies
   typedef __attribute__((address_space(3))) void *lds_ptr;
+  // The row advance of copy i goes into the lane offset, which the buffer's
+  // range check covers (rows past M read as zero); the k offset, always
+  // inside the row, is the scalar offset.
   auto load_a = [&](int q, uint4_t *stage) {
     const int k_off = 128 * TPS * q;
 #pragma unroll
     for (int i = 0; i < AV; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr)(stage + (i * NW + wave) * 64), 16,
-                                               a_off, k_off + a_rows * i, 0, 0);
+                                               a_off + a_rows * i, k_off, 0, 0);
   };
   // Weights: invalid strips read strip 0 and are never stored.
   int w_off[2], s_off[2];
@@ -561,6 +564,27 @@ __global__ __launch_bounds__(256) void prefill_reduce_kernel(const float *ws, in
 // ---------------------------------------------------------------------------
 // Host side.
 
+hipError_t launch_prefill_reduce(const float *ws, int KS, const Problem &p, hipStream_t s) {
+  const int ldo = (int)(p.swiglu ? p.N / 2 : p.N);
+  const dim3 grid((unsigned)ceil_div(p.M * (ldo / 4), 256));
+  if (p.swiglu) {
+    if (p.bf16)
+      hipLaunchKernelGGL((prefill_reduce_kernel<true, true>), grid, dim3(256), 0, s, ws, KS,
+                         (int)p.M, (int)p.N, p.out, ldo, p.rowscale);
+    else
+      hipLaunchKernelGGL((prefill_reduce_kernel<true, false>), grid, dim3(256), 0, s, ws, KS,
+                         (int)p.M, (int)p.N, p.out, ldo, p.rowscale);
+  } else {
+    if (p.bf16)
+      hipLaunchKernelGGL((prefill_reduce_kernel<false, true>), grid, dim3(256), 0, s, ws, KS,
+                         (int)p.M, (int)p.N, p.out, ldo, p.rowscale);
+    else
+      hipLaunchKernelGGL((prefill_reduce_kernel<false, false>), grid, dim3(256), 0, s, ws, KS,
+                         (int)p.M, (int)p.N, p.out, ldo, p.rowscale);
+  }
+  return hipGetLastError();
+}
+
 static PrefillArgs prefill_args(const Problem &p, int BM, const void *weights) {
   PrefillArgs a;
   a.A = p.A;
@@ -742,11 +766,7 @@ static hipError_t launch_prefill2_t(const Problem &p, const void *weights, const
                      dim3(a.tiles_m * a.tiles_n * c.ks), dim3(64 * WM * WNW), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || c.ks == 1) return e;
-  const int64_t threads = p.M * (a.ldo / 4);
-  hipLaunchKernelGGL((prefill_reduce_kernel<SWIGLU, BF>), dim3((unsigned)ceil_div(threads, 256)),
-                     dim3(256), 0, s, (const float *)workspace, c.ks, a.M, a.N, p.out, a.ldo,
-                     p.rowscale);
-  return hipGetLastError();
+  return launch_prefill_reduce((const float *)workspace, c.ks, p, s);
 }
 
 template <int MI, int WM, int TPS, bool DENSE, bool ZP, int BITS>
@@ -786,6 +806,8 @@ bool prefill_fused_available(const Problem &p) {
 }
 
 int64_t prefill_workspace_bytes(const Problem &p) {
+  TransConfig tc;
+  if (transition_config(p, tc)) return transition_workspace_bytes(p);
   Prefill2Config c;
   if (!prefill2_config(p, false, c) || c.ks == 1) return 0;
   return (int64_t)c.ks * p.M * p.N * (int64_t)sizeof(float);
@@ -796,6 +818,8 @@ static const char *kOneWaveFallback =
     "W4A16_PREFILL_V2=0), running the one-wave kernel";
 
 hipError_t launch_prefill(const Problem &p, void *workspace, hipStream_t s) {
+  TransConfig tc;
+  if (transition_config(p, tc)) return launch_transition(p, tc, workspace, s);
   Prefill2Config c;
   if (!prefill2_config(p, false, c)) {
     note_fallback(kOneWaveFallback, "fused prefill");
@@ -819,6 +843,8 @@ int tiled_describe(const Problem &p, bool dense, char *buf, size_t n) {
   const char *d = dense ? "true" : "false", *sw = p.swiglu ? "true" : "false";
   const char *bf = p.bf16 ? "true" : "false";
   const char *zp = p.zp && !dense ? "true" : "false";
+  TransConfig tc;
+  if (!dense && transition_config(p, tc)) return transition_describe(p, tc, buf, n);
   Prefill2Config c;
   if (prefill2_config(p, dense, c)) {
     int k = snprintf(buf, n,
