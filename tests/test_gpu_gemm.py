@@ -612,3 +612,40 @@ def test_group_size_32_bit_exact_integer_inputs(path):
         out = fp16_out(w4a16.gemm(to_dev(A), w, path=path))
         packed_o, s16_o = orc().quantize_pack(W, 32)
         assert np.array_equal(out.astype(np.float64), orc().gemm_f64(A, packed_o, s16_o, 32))
+
+
+@pytest.mark.parametrize("half,waves,depth", [(1, 8, 2), (0, 8, 2), (1, 4, 4), (0, 4, 4)])
+@pytest.mark.parametrize("K,N,swiglu", [(4096, 4096, False), (1152, 1064, False),
+                                        (14336, 1024, False), (2048, 2112, True)])
+def test_decode_dot_one_row(monkeypatch, half, waves, depth, K, N, swiglu):
+    """The one-row instances without the matrix unit (v_dot2_f32_f16 per lane,
+    ds_swizzle and v_permlane32_swap lane sums), forced, at both strip splits,
+    wave counts and pipeline depths; ragged N and an odd group count."""
+    monkeypatch.setenv("W4A16_DECODE_DOT", "1")
+    monkeypatch.setenv("W4A16_DECODE_COOP", "0")
+    monkeypatch.setenv("W4A16_DECODE_HALF", str(half))
+    monkeypatch.setenv("W4A16_DECODE_WAVES", str(waves))
+    monkeypatch.setenv("W4A16_DECODE_DEPTH", str(depth))
+    d = w4a16.describe(1, K, N, swiglu=swiglu, path="decode")
+    assert d.startswith("decode_kernel<16, %d, %d, %d, 0, " % (2 if swiglu else 1, waves, depth)), d
+    gemm_case(1, K, N, swiglu=swiglu, path="decode", seed=K + N + half)
+
+
+def test_decode_dot_one_row_bit_exact(monkeypatch):
+    """Exact sums (ternary activations, power-of-two scales) and one-hot rows
+    through the dot instances: bit for bit."""
+    monkeypatch.setenv("W4A16_DECODE_DOT", "1")
+    monkeypatch.setenv("W4A16_DECODE_COOP", "0")
+    for K, N in ((4096, 6144), (14336, 4096)):
+        W = synth.grid_weights(K, N, p=4, seed=K)
+        A = synth.ternary_activations(1, K, density=0.5, seed=K)
+        out = fp16_out(w4a16.gemm(to_dev(A), w4a16.load_weight(W), path="decode"))
+        packed_o, s16_o = orc().quantize_pack(W)
+        assert np.array_equal(out.astype(np.float64), orc().gemm_f64(A, packed_o, s16_o))
+    K, N = 2048, 1056
+    packed, scales = synth.random_words(K, N, seed=5)
+    w = w4a16.repack(to_dev(packed), to_dev(scales.view(np.int16)))
+    A, ks = synth.onehot_activations(1, K, seed=5)
+    out = fp16_out(w4a16.gemm(to_dev(A), w, path="decode"))
+    want = orc().dequant(packed, scales)[ks].view(np.float16).astype(np.float64)
+    assert np.array_equal(out.astype(np.float64), want)

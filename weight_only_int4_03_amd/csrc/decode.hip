@@ -73,7 +73,13 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
   static_assert(PRE || !ZP, "weights with zero points are scaled before the MFMA");
   static_assert(!HALF || MT == 16, "half strips need the 16-column MFMA");
   static_assert(BITS == 4 || (BITS == 8 && !ZP), "INT8 weights have no zero rows");
-  static_assert(MT == 16 ? (RPL >= 1 && RPL <= 4) : RPL == 16, "rows per lane");
+  static_assert(MT == 16 ? (RPL >= 0 && RPL <= 4) : RPL == 16, "rows per lane");
+  // RPL = 0: the one-row (M = 1) instance without the matrix unit: each lane
+  // takes v_dot2_f32_f16 products of its 32 k of the activation row with the
+  // exact u - 8 weights, and the four lanes that share a column are summed at
+  // the end by a ds_swizzle and a v_permlane32_swap.
+  constexpr bool DOT = RPL == 0;
+  static_assert(!DOT || (!PRE && !BF && !ZP && BITS == 4), "dot instances: fp16 INT4, G >= 128");
   // LDS: the cross-wave reduction [WAVES][SPW][M][32] floats; one-row
   // instances (M = 1) add the workgroup's activation slice after it.
   extern __shared__ float lds[];
@@ -120,7 +126,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
   // group's fragment from there one group ahead of its use; no other wave
   // touches the region, so no workgroup barrier is
   // needed.
-  constexpr bool AL = MT == 16 && RPL == 1;
+  constexpr bool AL = MT == 16 && RPL <= 1;
   const int wslice = (int)ceil_div((int64_t)p.KG, (int64_t)nunits) * 256;  // bytes per wave
   char *lds_a = (char *)lds + WAVES * SPW * 32 * 4 + wave * wslice;  // after the reduction tile
 
@@ -245,6 +251,28 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
                     wsc(f.b[s][x], j, (uint16_t)f.sc[s][0][x], (uint16_t)f.zs[s][0][x]),
                     acc[s][part]);
           }
+        }
+      }
+      return;
+    }
+    if constexpr (DOT) {
+      // k offsets 32 g4 + 8 j .. + 7 of the group: the lane's activation
+      // fragment f.a[j] and its weight word j, paired by v_dot2_f32_f16.
+#pragma unroll
+      for (int s = 0; s < SPW; ++s) {
+#pragma unroll
+        for (int part = 0; part < NPART; ++part) {
+          float t = 0.0f;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const half8_t w = dq(f.b[s][part][0][j]);
+            const half8_t a = bitcast<half8_t>(f.a[j]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              t = __builtin_amdgcn_fdot2(half2_t{a[2 * q], a[2 * q + 1]},
+                                         half2_t{w[2 * q], w[2 * q + 1]}, t, false);
+          }
+          acc[s][part][0] += t * (float)bitcast<_Float16>((uint16_t)f.sc[s][part][0]);
         }
       }
       return;
@@ -374,6 +402,23 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
       if (g + D + d < g1) {
         fill_a(f[d]);
         compute(f[d]);
+      }
+  }
+
+  if constexpr (DOT) {
+    // Each lane holds its quarter (k offsets 32 g4 ..) of its column's sum:
+    // add the quarters of lanes c16, c16 + 16 (ds_swizzle, swap of 16-lane
+    // groups) and of the two 32-lane halves (v_permlane32_swap), leaving the
+    // column sum as row 0 in every lane.
+#pragma unroll
+    for (int s = 0; s < SPW; ++s)
+#pragma unroll
+      for (int part = 0; part < NPART; ++part) {
+        float v = acc[s][part][0];
+        v += bitcast<float>(__builtin_amdgcn_ds_swizzle(bitcast<int>(v), 0x401F));
+        const auto x = __builtin_amdgcn_permlane32_swap(bitcast<unsigned>(v),
+                                                        bitcast<unsigned>(v), false, false);
+        acc[s][part][0] = bitcast<float>((unsigned)x[0]) + bitcast<float>((unsigned)x[1]);
       }
   }
 
@@ -524,6 +569,17 @@ static bool one_row(const Problem &p, const DecodeConfig &c) {
              kMaxLdsPerWorkgroup;
 }
 
+// The one-row instances without the matrix unit (v_dot2_f32_f16 products,
+// ds_swizzle / v_permlane32_swap lane sums) for fp16 INT4 weights with
+// groups of at least 128 k, when W4A16_DECODE_DOT=1.  Measured against the
+// MFMA instances (activation row padded to 16 rows) on MI355X; off unless
+// forced.
+static bool dot_row(const Problem &p, const DecodeConfig &c) {
+  const char *v = std::getenv("W4A16_DECODE_DOT");
+  return v != nullptr && *v == '1' && one_row(p, c) && !p.bf16 && !p.zp && p.bits == 4 &&
+         p.G >= kGroup;
+}
+
 // Rotated K order (each wave starts its K range, or the coop kernel its
 // sequence of rounds, at an offset hashed from the workgroup index).  Strips
 // are contiguous in K, so without it the concurrently running waves read
@@ -560,7 +616,7 @@ int decode_describe(const Problem &p, char *buf, size_t n) {
     return k;
   }
   const DecodeConfig c = decode_config(p);
-  const int rpl = c.MT == 16 ? (one_row(p, c) ? 1 : 4) : 16;
+  const int rpl = c.MT == 16 ? (dot_row(p, c) ? 0 : one_row(p, c) ? 1 : 4) : 16;
   const char *pre = (p.bf16 || p.G < kGroup || p.zp) ? "true" : "false";
   const char *zp = p.zp ? "true" : "false", *hf = c.half ? "true" : "false";
   int k = snprintf(buf, n,
@@ -590,7 +646,7 @@ template <int MT, int SPW, int WAVES, int D, int RPL, bool SWIGLU, bool BF, bool
           bool HALF, int BITS>
 static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t s) {
   const size_t lds = (size_t)WAVES * SPW * a.M * 32 * sizeof(float) +
-                     (MT == 16 && RPL == 1 ? one_row_slice_bytes(a.KG, a.KS, WAVES) : 0);
+                     (MT == 16 && RPL <= 1 ? one_row_slice_bytes(a.KG, a.KS, WAVES) : 0);
   hipLaunchKernelGGL((decode_kernel<MT, SPW, WAVES, D, RPL, SWIGLU, BF, PRE, ZP, HALF, BITS>),
                      dim3(a.nsg * a.KS * (HALF ? 2 : 1)), dim3(WAVES * 64), lds, s, a);
   hipError_t e = hipGetLastError();
@@ -618,6 +674,11 @@ static hipError_t launch_decode_w(const DecodeArgs &a, const DecodeConfig &c, hi
 template <bool BF, bool PRE, bool ZP, int BITS = 4>
 static hipError_t launch_decode_bf(const Problem &p, const DecodeArgs &a, const DecodeConfig &c,
                                    hipStream_t s) {
+  if constexpr (!BF && !PRE && !ZP && BITS == 4) {
+    if (dot_row(p, c))
+      return p.swiglu ? launch_decode_w<16, 2, 0, true, BF, PRE, ZP, BITS>(a, c, s)
+                      : launch_decode_w<16, 1, 0, false, BF, PRE, ZP, BITS>(a, c, s);
+  }
   if (one_row(p, c))
     return p.swiglu ? launch_decode_w<16, 2, 1, true, BF, PRE, ZP, BITS>(a, c, s)
                     : launch_decode_w<16, 1, 1, false, BF, PRE, ZP, BITS>(a, c, s);

@@ -390,13 +390,17 @@ static int device_cus_t() {
 constexpr int64_t kTransitionMaxM = 256;
 
 // Launch shape: MI (rows per tile / 32), the wave split, row tiles, column
-// groups and K slices.  MI = 2 (64-row tiles, four waves along K) up to
-// M = 64, else MI = 4 (128-row tiles, two waves along K: the 64 KiB
-// activation stage holds 128 rows of two groups).  K is split only while
-// the split grid still fits one workgroup per CU and each slice keeps at
-// least two rounds; the choice weighs the idle CUs of an unsplit grid
-// against the split's FP32 partial traffic (written and read once, at about
-// 5 TB/s, plus a few microseconds for the reduction launch).
+// groups and K slices.  Measured on MI355X over M = 48 .. 512 on the
+// Llama-8B gate/up (4096 x 28672) and down (14336 x 4096) projections:
+// 64-row tiles (MI = 2, four waves along K) wherever their grid fits one
+// workgroup per CU, else 128-row tiles (MI = 4, two waves along K: the
+// 64 KiB activation stage holds 128 rows of two groups); K is then split
+// while the split grid still fits one workgroup per CU and each slice keeps
+// at least two rounds (a larger grid runs in two passes and was slower in
+// every measured case, despite the partial traffic it avoids).  Up to
+// M = 256 this beats the prefill tiles (gate/up M = 64: 27.5 against
+// 36.6 us; down M = 64: 24.5 against 26.9 us; down M = 256: 44.1 against
+// 48.5 us); above it the prefill tiles win.
 // W4A16_TRANSITION (0 or 1), W4A16_TRANSITION_MI (2 or 4) and
 // W4A16_TRANSITION_KS override; any W4A16_PREFILL_* override (V2, BM, WM,
 // TPS, KS) selects the prefill kernels unless W4A16_TRANSITION=1.
@@ -418,7 +422,10 @@ bool transition_config(const Problem &p, TransConfig &c) {
   if (!(p.M * p.K * 2 < limit && ns * (p.K / kTileK) * 1024 * (p.bits == 8 ? 2 : 1) < limit &&
         ns * ceil_div(groups_of(p.K, p.G), 8) * 512 < limit && p.M * p.N * 4 < limit))
     return false;
-  c.mi = p.M <= 64 ? 2 : 4;
+  const int cus = device_cus_t();
+  const int64_t npairs = p.swiglu ? p.N / 64 : ceil_div(ns, 2);
+  const int64_t tiles2 = ceil_div(p.M, 64) * ceil_div(npairs, 2);
+  c.mi = tiles2 <= cus ? 2 : 4;
   const int mi_env = env_int("W4A16_TRANSITION_MI", 0);
   if (mi_env == 2 || mi_env == 4) c.mi = mi_env;
   // The 128-row tile fills the registers with INT4 weights and symmetric
@@ -427,27 +434,12 @@ bool transition_config(const Problem &p, TransConfig &c) {
   if (p.bits == 8 || p.zp) c.mi = 2;
   c.wk = c.mi == 2 ? 4 : 2;
   c.wc = 8 / c.wk;
-  const int64_t npairs = p.swiglu ? p.N / 64 : ceil_div(ns, 2);
   c.col_groups = (int)ceil_div(npairs, c.wc);
   c.row_tiles = (int)ceil_div(p.M, 32 * c.mi);
   const int64_t tiles = (int64_t)c.row_tiles * c.col_groups;
   const int64_t KG = p.K / kGroup;
-  const int cus = device_cus_t();
-  // Time model in arbitrary units: rounds of the grid times each
-  // workgroup's K range, plus the partial round trip.
-  double best = 0.0;
   c.ks = 1;
-  for (int ks = 1; ks <= 16; ks *= 2) {
-    if (ks > 1 && (tiles * ks > cus || KG / ks < 2 * c.wk)) break;
-    const double rounds = (double)ceil_div(tiles * ks, (int64_t)cus);
-    // One workgroup: 2 * BM * (64 * WC) * K / ks FLOPs at ~4.5 TFLOP/s.
-    double t = rounds * 2.0 * 32 * c.mi * 64 * c.wc * ((double)p.K / ks) / 4.5e12;
-    if (ks > 1) t += 2.0 * ks * (double)p.M * (double)p.N * 4.0 / 5e12 + 3e-6;
-    if (ks == 1 || t < best) {
-      best = t;
-      c.ks = ks;
-    }
-  }
+  while (c.ks < 16 && tiles * c.ks * 2 <= cus && KG / (c.ks * 2) >= 2 * c.wk) c.ks *= 2;
   const int ks_env = env_int("W4A16_TRANSITION_KS", 0);
   if (ks_env > 0) c.ks = (int)(ks_env < KG ? ks_env : KG);
   c.tiles = (int)(tiles * c.ks);
