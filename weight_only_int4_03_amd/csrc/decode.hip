@@ -527,7 +527,11 @@ static DecodeConfig decode_config(const Problem &p) {
   c.SPW = p.swiglu ? 2 : 1;
   c.nsg = (int)(p.swiglu ? (p.N / 2 / kStrip) : NS);
   const char *hv = std::getenv("W4A16_DECODE_HALF");
-  const bool half_fits = 2 * (int64_t)c.nsg <= 256 && (KG <= 64 || p.M <= 4);
+  // One-row GEMMs whose strip groups are more than 256 and not a multiple of
+  // it also take half strips (Llama-70B QKV, 320 strip groups: 640
+  // workgroups spread over the CUs more evenly than 320).
+  const bool uneven_row = p.M == 1 && c.nsg > 256 && c.nsg % 256 != 0 && !p.swiglu;
+  const bool half_fits = (2 * (int64_t)c.nsg <= 256 && (KG <= 64 || p.M <= 4)) || uneven_row;
   c.half = c.MT == 16 && (hv != nullptr && *hv != 0 ? *hv == '1' : half_fits);
   const int64_t units = (int64_t)c.nsg * (c.half ? 2 : 1);
   int waves = (units < 384 || KG >= 128) ? 8 : 4;

@@ -484,6 +484,14 @@ bool coop_config(const Problem &p, int &WC, int &WK, int &KS) {
     KS = 1;
     if (WC > 1)
       while ((int64_t)ceil_div(nsg, WC) * KS * 2 <= 256 && KG / (KS * 2) >= 8) KS *= 2;
+  } else if (p.M == 1 && !p.swiglu && (deep || uneven) && p.bits == 4 && !p.zp && !p.bf16) {
+    // One-row plain projections that are deep or spread unevenly over the
+    // CUs (Llama-70B down and QKV): the per-wave kernel with the activation
+    // row staged per wave, measured on MI355X at 22.7 against 24.7 us (down,
+    // K = 28672) and, with half strips, 11.2 against 12.8 us (QKV, 320 strip
+    // groups).
+    use = false;
+    WC = 1; WK = 4; KS = 1;
   } else if (p.M == 1 && p.swiglu && nsg >= 512 && p.bits == 4 && !p.zp && !p.bf16) {
     // The widest fused projections at M = 1 (Llama-70B gate/up): the
     // per-wave kernel, which stages the activation row per wave without

@@ -686,9 +686,13 @@ static int k_slices(int64_t tiles, int nsteps, int cus) {
   return ks;
 }
 
-// false: the one-wave kernel (prefill_kernel) runs instead.  Both the fused
-// path and the dense tier take prefill2_kernel unless an operand is too large
-// for 32-bit offsets (a logged fallback) or W4A16_PREFILL_V2=0.
+// false: the one-wave kernel (prefill_kernel) runs instead.  The fused path
+// takes prefill2_kernel unless an operand is too large for 32-bit offsets (a
+// logged fallback) or W4A16_PREFILL_V2=0.  The dense tier keeps the one-wave
+// kernel unless W4A16_PREFILL_V2=1: on its fp16 weights (four 16-byte vectors
+// per lane and 64-k tile) the 8-wave mainloop measured 482-488 TFLOP/s at
+// M = 16384 on MI355X against 700 or more for the one-wave mainloop, whose
+// 512 registers hold those vectors.
 //
 // Tile rows (64, 128 or 256) come from a small time model fitted to
 // measurements on MI355X: a workgroup of a BM-row tile over a k range of
@@ -705,7 +709,7 @@ static int k_slices(int64_t tiles, int nsteps, int cus) {
 // override.
 static bool prefill2_config(const Problem &p, bool dense, Prefill2Config &c) {
   const char *v = std::getenv("W4A16_PREFILL_V2");
-  const bool on = v == nullptr || *v != '0';
+  const bool on = v != nullptr && *v != 0 ? *v == '1' : !dense;
   if (!on || !fits_buffer_offsets(p, dense)) return false;
   const int cus = device_cus();
   const int64_t NS = ceil_div(p.N, kStrip);
@@ -877,7 +881,6 @@ hipError_t launch_dense(const Problem &p, void *workspace, hipStream_t s) {
   if (e != hipSuccess) return e;
   Prefill2Config c;
   if (prefill2_config(p, true, c)) return launch_prefill2_m<4, 2, true>(p, w16f, c, nullptr, s);
-  note_fallback(kOneWaveFallback, "dense tier");
   return launch_tiled<true>(p, w16f, s);
 }
 
