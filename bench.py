@@ -614,6 +614,100 @@ def roofline_entry(res, ceilings, zp, int8, suffix):
     return roof
 
 
+# Dispatch sweeps (--sweep NAME): GEMM shapes timed under launch-configuration
+# variants (the environment overrides the library reads at every call), each
+# variant's output compared with the first's.  Two passes (forward, then
+# reverse order) and the better of the two kept, so the first variant timed
+# after a weight change is not favoured or penalised.
+SWEEPS = {
+    "transition": {
+        "what": "the transition kernel against the 1 x 8 prefill tile it replaced (1% outlier "
+                "activations)",
+        "shapes": [(m, 4096, 28672, False) for m in (48, 64, 96, 128, 192, 256, 384)]
+                  + [(m, 14336, 4096, False) for m in (48, 64, 96, 128, 192, 256, 384)],
+        "outliers": True,
+        "variants": [("prefill tile", {"W4A16_TRANSITION": "0"}),
+                     ("transition", {"W4A16_TRANSITION": "1"}),
+                     ("transition MI=2", {"W4A16_TRANSITION": "1", "W4A16_TRANSITION_MI": "2"}),
+                     ("transition MI=4", {"W4A16_TRANSITION": "1", "W4A16_TRANSITION_MI": "4"})],
+    },
+    "dot": {
+        "what": "one-row GEMMs: the per-wave kernel with MFMA (activation row padded to 16 rows) "
+                "against its v_dot2_f32_f16 instances (lane sums by ds_swizzle and "
+                "v_permlane32_swap)",
+        "shapes": [(1, 4096, 4096, False), (1, 4096, 6144, False), (1, 14336, 4096, False),
+                   (1, 8192, 8192, False), (1, 8192, 10240, False), (1, 28672, 8192, False)],
+        "outliers": False,
+        "variants": [("MFMA", {"W4A16_DECODE_COOP": "0"}),
+                     ("v_dot2", {"W4A16_DECODE_COOP": "0", "W4A16_DECODE_DOT": "1"})],
+    },
+    "decode70b": {
+        "what": "Llama-70B one-row and small-M projections under both decode kernels",
+        "shapes": [(m, 28672, 8192, False) for m in (1, 4, 16)]
+                  + [(m, 8192, 10240, False) for m in (1, 4, 16)],
+        "outliers": False,
+        "variants": [("auto", {}),
+                     ("per-wave", {"W4A16_DECODE_COOP": "0"}),
+                     ("per-wave half", {"W4A16_DECODE_COOP": "0", "W4A16_DECODE_HALF": "1"}),
+                     ("cooperative", {"W4A16_DECODE_COOP": "1"})],
+    },
+}
+SWEEP_ENV = ("W4A16_TRANSITION", "W4A16_TRANSITION_MI", "W4A16_TRANSITION_KS",
+             "W4A16_DECODE_COOP", "W4A16_DECODE_DOT", "W4A16_DECODE_HALF")
+
+
+def run_sweep(name, reps, torch, dev):
+    sw = SWEEPS[name]
+    stream = torch.cuda.Stream()
+    print("# Sweep %s: %s" % (name, sw["what"]), flush=True)
+    print("", flush=True)
+    print("Command (repository root, one MI355X): `python bench.py --sweep %s`" % name, flush=True)
+    print("", flush=True)
+    print("Cold weights (one launch per weight copy, at least 800 MB between reuses of a copy) in a "
+          "HIP graph, median of three trials of %d replays; two passes over the variants (forward, "
+          "then reverse order), the better kept; rel = relative L2 distance of the output from the "
+          "first variant's." % reps, flush=True)
+    print("", flush=True)
+    print("| M | K | N | variant | launch | us (pass 1, pass 2) | best us | rel |", flush=True)
+    print("|---|---|---|---|---|---|---|---|", flush=True)
+    cache = {}
+    for M, K, N, swg in sw["shapes"]:
+        if (K, N) not in cache:
+            cache.clear()
+            w = w4a16.load_weight(synth.weights(K, N, seed=0))
+            ncp = max(2, math.ceil(ROTATE_BYTES / w.nbytes))
+            cache[(K, N)] = [w] + [w.clone() for _ in range(ncp - 1)]
+        copies = cache[(K, N)]
+        A = torch.from_numpy(synth.activations(M, K, seed=0, outliers=sw["outliers"])).to(dev)
+        out = torch.empty((M, N // 2 if swg else N), dtype=torch.float16, device=dev)
+        times, descs, rels, ref = {}, {}, {}, None
+        order = sw["variants"] + sw["variants"][::-1]
+        for vname, env in order:
+            for k in SWEEP_ENV:
+                os.environ.pop(k, None)
+            os.environ.update(env)
+            descs[vname] = w4a16.describe(M, K, N, swg)
+            w4a16.reserve_workspace(w4a16.workspace_bytes(M, K, N, swg))
+            with torch.cuda.stream(stream):
+                w4a16.gemm(A, copies[0], swiglu=swg, out=out)
+            torch.cuda.synchronize()
+            got = out.float().cpu().numpy()
+            if ref is None:
+                ref = got
+            rels[vname] = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30))
+            us = time_graph(torch, stream, lambda: [w4a16.gemm(A, c, swiglu=swg, out=out)
+                                                    for c in copies], reps) * 1e3 / len(copies)
+            times.setdefault(vname, []).append(us)
+        best = min(times, key=lambda v: min(times[v]))
+        for vname, _ in sw["variants"]:
+            t = times[vname]
+            print("| %d | %d | %d | %s%s | `%s` | %.2f, %.2f | %.2f | %.1e |" % (
+                M, K, N, vname, " (best)" if vname == best else "", descs[vname], t[0], t[1],
+                min(t), rels[vname]), flush=True)
+    for k in SWEEP_ENV:
+        os.environ.pop(k, None)
+
+
 def clocks_snapshot():
     """Current shader and memory clock levels and board power, read from the
     amdgpu sysfs files (best effort; no child process)."""
@@ -656,6 +750,8 @@ def main():
                     help="asymmetric weights: seeded zero points as prescaled zero rows")
     ap.add_argument("--int8", action="store_true",
                     help="INT8 weights (W8A16) instead of INT4")
+    ap.add_argument("--sweep", choices=sorted(SWEEPS),
+                    help="only time the dispatch sweep NAME (a markdown table on stdout)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for hardware-counter calibration)")
     args = ap.parse_args()
@@ -680,6 +776,9 @@ def main():
         print(json.dumps({"copy_bytes_read": 1 << 30, "copy_bytes_written": 1 << 30, "launches": 5}))
         return
     w4a16.lib()
+    if args.sweep:
+        run_sweep(args.sweep, 10, torch, dev)
+        return
 
     zp, int8, bf16 = args.zero_points, args.int8, args.dtype == "bf16"
     if zp and int8:

@@ -528,20 +528,21 @@ __global__ __launch_bounds__(256) void prefill_reduce_kernel(const float *ws, in
   const int m = (int)(idx / per_row), n = (int)(idx - (int64_t)m * per_row) * 4;
   const int64_t slice = (int64_t)M * N;
   const float *src = ws + (int64_t)m * N + n;
-  // Slices are added in order; the partials of up to four slices are loaded
+  // Slices are added in order; the partials of up to eight slices are loaded
   // before any is added, so their memory latencies overlap.
   float4_t g = {0.0f, 0.0f, 0.0f, 0.0f}, u = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int k0 = 0; k0 < KS; k0 += 4) {
-    float4_t tg[4], tu[4];
+  constexpr int B = 8;
+  for (int k0 = 0; k0 < KS; k0 += B) {
+    float4_t tg[B], tu[B];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < B; ++i) {
       if (k0 + i < KS) {
         tg[i] = *(const float4_t *)(src + (k0 + i) * slice);
         if constexpr (SWIGLU) tu[i] = *(const float4_t *)(src + (k0 + i) * slice + N / 2);
       }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < B; ++i) {
       if (k0 + i < KS) {
         g += tg[i];
         if constexpr (SWIGLU) u += tu[i];
