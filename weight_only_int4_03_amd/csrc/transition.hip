@@ -58,6 +58,11 @@ struct TransArgs {
   int gshift;             // group of k = k >> gshift
 };
 
+// s_waitcnt immediate (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt in
+// 6:4, lgkmcnt in 11:8) that waits until at most n vector-memory loads are
+// outstanding and for nothing else.
+constexpr int vm_wait(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
 template <int MI, int WC, int WK, bool SWIGLU, bool BF, bool ZP, int BITS>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void transition_kernel(TransArgs p) {
@@ -77,7 +82,10 @@ void transition_kernel(TransArgs p) {
   __shared__ uint4_t lds1[BM * CH];
   struct BRegs {
     uint4_t v[2][2][NV];  // [strip][64-k tile][vector]
-    uint32_t sc[2][2];    // [strip][tile]: scale bits (with ZP the zero row in the high half)
+    uint32_t sc[2][2];    // [strip][tile]: scale bits
+    // Zero-row bits, in registers of their own: combined with the scale right
+    // after the load, they would make the wave wait for the load there.
+    uint32_t zc[ZP ? 2 : 1][2];
   };
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -119,11 +127,9 @@ void transition_kernel(TransArgs p) {
   const int ge = (int)((int64_t)p.KG * (ks + 1) / p.KS);
   const int R = (ge - gb + WK - 1) / WK;
 
-  // Buffer resources.  The activation resource starts at this tile's first
-  // row and ends at row M, so rows past M read as zero.
+  // Buffer resources.  The activation resources (one per round, below) start
+  // at this tile's first row and end at row M, so rows past M read as zero.
   const int arows = p.M - m0 < BM ? p.M - m0 : BM;
-  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)(p.A + (int64_t)m0 * p.K), (short)0, arows * p.K * 2, kBufferConfig);
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
       (void *)p.rw, (short)0, p.NS * p.KT * 1024 * NV, kBufferConfig);
   const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
@@ -147,14 +153,22 @@ void transition_kernel(TransArgs p) {
   const int row0 = (wave * 64 + lane) / CH, ph = (wave * 64 + lane) % CH;
   const int a_even = row0 * p.K * 2 + ((ph ^ (row0 & 15)) * 16);
   const int a_odd = row0 * p.K * 2 + ((ph ^ ((row0 + RPC) & 15)) * 16);
+  // The round's k offset moves the resource's base instead of the lane
+  // offsets (which stay fixed for the whole loop, so no per-round address
+  // registers are written while loads are in flight); the resource shrinks by
+  // the same amount, so its range check still ends at row M.
   typedef __attribute__((address_space(3))) void *lds_ptr;
+  const char *a_tile = (const char *)(p.A + (int64_t)m0 * p.K);
+  const int a_bytes = arows * p.K * 2;
   auto load_a = [&](int r, uint4_t *stage) {
     const int kbyte = (gb + r * WK) * 256;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(a_tile + kbyte), (short)0, a_bytes - kbyte, kBufferConfig);
 #pragma unroll
     for (int i = 0; i < AV; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ra, (lds_ptr)(stage + (i * NW + wave) * 64), 16,
-          ((i & 1) ? a_odd : a_even) + i * RPC * p.K * 2 + kbyte, 0, 0, 0);
+          rk, (lds_ptr)(stage + (i * NW + wave) * 64), 16,
+          ((i & 1) ? a_odd : a_even) + i * RPC * p.K * 2, 0, 0, 0);
   };
 
   // Weights and scales: invalid strips read strip 0 and are never stored; a
@@ -164,7 +178,11 @@ void transition_kernel(TransArgs p) {
   for (int s = 0; s < 2; ++s) {
     const int st = sval[s] ? strip[s] : 0;
     w_off[s] = st * p.KT * 1024 * NV + lane * 16;
-    s_off[s] = (st * p.KG8 * 32 + c) * 16;
+    // Lane half h reads the scale of k + 32 h: with 32-k groups the next
+    // group (2 bytes on, never across an octet: the group of the half's
+    // first k is even), else the same one; the rest of the offset is the
+    // same for the whole wave and goes into the scalar offset.
+    s_off[s] = (st * p.KG8 * 32 + c) * 16 + (p.gshift == 5 ? 2 * h : 0);
   }
   auto load_b = [&](int r, BRegs &regs) {
     int grp = gb + r * WK + wk;
@@ -179,14 +197,13 @@ void transition_kernel(TransArgs p) {
               rw, w_off[s] + VSTEP * j, (2 * grp + t) * 1024 * NV, kBufferNT));
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const int g = (128 * grp + 64 * t + 32 * h) >> p.gshift;
+      const int g = (128 * grp + 64 * t) >> p.gshift;
       const int g_off = (g >> 3) * 512 + (g & 7) * 2;
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        regs.sc[s][t] = __builtin_amdgcn_raw_buffer_load_b16(rsc, s_off[s] + g_off, 0, 0);
+        regs.sc[s][t] = __builtin_amdgcn_raw_buffer_load_b16(rsc, s_off[s], g_off, 0);
         if constexpr (ZP)
-          regs.sc[s][t] |=
-              (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rzr, s_off[s] + g_off, 0, 0) << 16;
+          regs.zc[s][t] = __builtin_amdgcn_raw_buffer_load_b16(rzr, s_off[s], g_off, 0);
       }
     }
   };
@@ -211,7 +228,7 @@ void transition_kernel(TransArgs p) {
             bf[s] = dq.scaled8_bits<BF>(v[(j & 1) * 2], v[(j & 1) * 2 + 1], s16);
           } else if constexpr (ZP) {
             bf[s] = dq.scaled_bits<BF, true>(regs.v[s][t][0][j], s16,
-                                             (uint16_t)(regs.sc[s][t] >> 16));
+                                             (uint16_t)regs.zc[s][t]);
           } else if constexpr (BF) {
             bf[s] = bitcast<uint4_t>(dq.scaled_bf16(regs.v[s][t][0][j], Dequant::BScale(s16)));
           } else {
@@ -248,21 +265,41 @@ void transition_kernel(TransArgs p) {
   BRegs b0, b1, b2;
   load_a(0, lds0);
   load_b(0, b0);
+  __builtin_amdgcn_sched_barrier(0);
   load_b(R > 1 ? 1 : 0, b1);
+  __builtin_amdgcn_sched_barrier(0);
+  // Enter the loop in its steady state: round 0's activations and weights
+  // complete, only round 1's weights (the last eight loads) in flight.  (Left
+  // to itself the compiler merges the entry state, with round 0's weights
+  // still pending, into every iteration and then waits inside each round for
+  // loads issued a round early.)
+  __builtin_amdgcn_s_waitcnt(vm_wait(4 * NV + (ZP ? 8 : 4)));
   __syncthreads();
-  // Three register sets and two stages: six rounds per iteration.
-  for (int r = 0; r < R; r += 6) {
+  // Three register sets and two stages: six rounds per iteration, then up to
+  // five more after the loop.  (With the early exits inside the loop the
+  // compiler merges their pending loads into the loop head and waits there,
+  // every iteration, for weights issued a round early.)
+  int r = 0;
+  for (; r + 6 <= R; r += 6) {
     round(r, lds0, lds1, b0, b2);
-    if (r + 1 >= R) break;
     round(r + 1, lds1, lds0, b1, b0);
-    if (r + 2 >= R) break;
     round(r + 2, lds0, lds1, b2, b1);
-    if (r + 3 >= R) break;
     round(r + 3, lds1, lds0, b0, b2);
-    if (r + 4 >= R) break;
     round(r + 4, lds0, lds1, b1, b0);
-    if (r + 5 >= R) break;
     round(r + 5, lds1, lds0, b2, b1);
+  }
+  if (r < R) {
+    round(r, lds0, lds1, b0, b2);
+    if (r + 1 < R) {
+      round(r + 1, lds1, lds0, b1, b0);
+      if (r + 2 < R) {
+        round(r + 2, lds0, lds1, b2, b1);
+        if (r + 3 < R) {
+          round(r + 3, lds1, lds0, b0, b2);
+          if (r + 4 < R) round(r + 4, lds0, lds1, b1, b0);
+        }
+      }
+    }
   }
 
   // Cross-wave sum over wk: waves wk >= 1 write their tiles (one float4 per
