@@ -248,7 +248,7 @@ __global__ __launch_bounds__(64 * WM * WNW) __attribute__((amdgpu_waves_per_eu(2
 void prefill2_kernel(PrefillArgs p) {
   // TPS: 64-k tiles per pipeline step (2 = one whole 128-k scale group).
   // ZP: zero rows (AWQ zero points prescaled as fp16((8 - zp) s)), loaded
-  // with the scales into the high half of the same register.
+  // beside the scales.
   // All global reads are buffer loads: a per-lane 32-bit offset fixed for the
   // whole k loop plus a scalar offset that advances with k, so the loop does
   // no address arithmetic and holds no 64-bit pointers.  Buffer reads past the
@@ -274,7 +274,11 @@ void prefill2_kernel(PrefillArgs p) {
   struct BRegs {
     uint4_t v[2][TPS][NV];
     uint32_t sc[2][TPS];  // per strip and 64-k tile (tiles may lie in different groups):
-                          // scale bits, and with ZP the zero row's in the high half
+                          // scale bits
+    // Zero-row bits, in registers of their own: merged into the scale
+    // register right after the load, they would make the wave wait there for
+    // every load of the step (loads complete in issue order).
+    uint32_t zc[ZP ? 2 : 1][TPS];
   };
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -380,9 +384,7 @@ void prefill2_kernel(PrefillArgs p) {
         for (int w = 0; w < 2; ++w) {
           r.sc[w][t] = __builtin_amdgcn_raw_buffer_load_b16(rsc, s_off[w] + g_off, 0, 0);
           if constexpr (ZP)
-            r.sc[w][t] |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rzr, s_off[w] + g_off,
-                                                                          0, 0)
-                          << 16;
+            r.zc[w][t] = __builtin_amdgcn_raw_buffer_load_b16(rzr, s_off[w] + g_off, 0, 0);
         }
       }
     }
@@ -409,7 +411,7 @@ void prefill2_kernel(PrefillArgs p) {
           bf[w] = dq.scaled8_bits<BF>(v[(j & 1) * 2], v[(j & 1) * 2 + 1], (uint16_t)r.sc[w][t]);
         } else if constexpr (ZP) {
           bf[w] = dq.scaled_bits<BF, true>(r.v[w][t][0][j], (uint16_t)r.sc[w][t],
-                                           (uint16_t)(r.sc[w][t] >> 16));
+                                           (uint16_t)r.zc[w][t]);
         } else if constexpr (BF) {
           bf[w] = bitcast<uint4_t>(
               dq.scaled_bf16(r.v[w][t][0][j], Dequant::BScale((uint16_t)r.sc[w][t])));
