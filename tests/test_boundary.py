@@ -213,10 +213,17 @@ def test_describe_names_the_launches():
     assert d.endswith("ks=4; decode_reduce_kernel<1, false, false>"), d
     d = w4a16.describe(24, 4096, 4096, int8=True)
     assert d.startswith("decode_coop_kernel<32, 1, 2, 4, 16, false, false, false, 8>"), d
-    # Mid-width plain projections: one column group, no K split; the widest
-    # fused ones: four column groups, two groups of 128 k per round.
+    # Mid-width plain projections: one column group with eight waves along
+    # K, no K split; the widest fused ones: four column groups, two groups of
+    # 128 k per round.
     assert w4a16.describe(32, 4096, 6144).startswith(
-        "decode_coop_kernel<32, 1, 1, 4, 16, false, false, false, 4> workgroups=192 threads=256 ks=1")
+        "decode_coop_kernel<32, 1, 1, 8, 16, false, false, false, 4> workgroups=192 threads=512 ks=1")
+    # The same at M = 16 (and QKV above M = 8); O at M = 8-12 stays on the
+    # per-wave kernel.
+    assert w4a16.describe(16, 4096, 6144).startswith(
+        "decode_coop_kernel<16, 1, 1, 8, 4, false, false, false, 4> workgroups=192 threads=512 ks=1")
+    assert w4a16.describe(16, 4096, 4096).startswith("decode_coop_kernel<16, 1, 1, 8, 4, ")
+    assert w4a16.describe(12, 4096, 4096).startswith("decode_kernel<16, 1, 8, 2, 4, ")
     assert w4a16.describe(32, 8192, 57344, swiglu=True).startswith(
         "decode_coop_kernel<32, 2, 4, 2, 16, true, false, false, 4> workgroups=224 threads=512 ks=1")
     assert w4a16.describe(32, 28672, 8192).startswith(

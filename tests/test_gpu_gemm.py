@@ -135,7 +135,7 @@ def test_empty_and_single_group():
 
 
 COOP_CONFIGS = [(4, 1, 1), (8, 1, 1), (2, 2, 1), (4, 2, 1), (2, 4, 1), (1, 4, 1), (2, 4, 2), (1, 4, 3),
-                (4, 2, 2), (4, 2, 4), (2, 2, 4)]
+                (4, 2, 2), (4, 2, 4), (2, 2, 4), (1, 8, 1), (1, 8, 3)]
 
 
 @pytest.mark.parametrize("wc,wk,ks", COOP_CONFIGS)
@@ -152,7 +152,10 @@ def test_decode_cooperative_forced(monkeypatch, wc, wk, ks, M, K, N, swiglu):
     monkeypatch.setenv("W4A16_COOP_KS", str(ks))
     desc = w4a16.describe(M, K, N, swiglu, path="decode")
     say("coop forced:", desc)
-    if M <= 16:   # at M = 32 some configurations need more than 64 KiB of LDS and fall back
+    # At M = 32 some configurations need more LDS than a workgroup has, and
+    # one column group with eight waves along K exists for plain projections
+    # only: those fall back to the per-wave kernel.
+    if M <= 16 and not (swiglu and (wc, wk) == (1, 8)):
         assert desc.startswith("decode_coop_kernel"), desc
     gemm_case(M, K, N, swiglu=swiglu, path="decode", seed=wc * 100 + wk * 10 + ks + M)
 

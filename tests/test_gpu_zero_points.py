@@ -184,7 +184,8 @@ def test_zp_full_size_sampled(M, K, N, swiglu):
     zp_case(M, K, N, swiglu=swiglu, seed=M + K, rows=rows, cols=cols)
 
 
-@pytest.mark.parametrize("wc,wk,ks", [(1, 4, 1), (2, 4, 2), (4, 2, 1), (2, 2, 4), (4, 2, 4), (8, 1, 3)])
+@pytest.mark.parametrize("wc,wk,ks", [(1, 4, 1), (2, 4, 2), (4, 2, 1), (2, 2, 4), (4, 2, 4), (8, 1, 3),
+                                      (1, 8, 1), (1, 8, 2)])
 @pytest.mark.parametrize("M", [1, 7, 16, 24, 32])
 @pytest.mark.parametrize("bf16", [False, True])
 def test_zp_cooperative_decode(monkeypatch, wc, wk, ks, M, bf16):
@@ -198,7 +199,10 @@ def test_zp_cooperative_decode(monkeypatch, wc, wk, ks, M, bf16):
     swiglu = (wc + M) % 2 == 1
     K, N = (1152, 2112) if swiglu else (2560, 1064)
     d = w4a16.describe(M, K, N, swiglu, path="decode", bf16=bf16, zp=True)
-    if M <= 16:   # at M > 16 some configurations need more than 64 KiB of LDS and fall back
+    # At M > 16 some configurations need more LDS than a workgroup has, and
+    # one column group with eight waves along K exists for plain projections
+    # only: those fall back to the per-wave kernel.
+    if M <= 16 and not (swiglu and (wc, wk) == (1, 8)):
         assert d.startswith("decode_coop_kernel") and d.split(">")[0].endswith(", true, 4"), d
     zp_case(M, K, N, swiglu=swiglu, path="decode", bf16=bf16, seed=wc * 100 + wk * 10 + ks + M)
 

@@ -400,6 +400,8 @@ static hipError_t launch_coop_w(const DecodeArgs &a, int WC, int WK, hipStream_t
   if (WC == 2 && WK == 2) return launch_coop_t<MT, SPW, 2, 2, RPL, SWIGLU, BF, ZP, BITS>(a, s);
   if (WC == 4 && WK == 2) return launch_coop_t<MT, SPW, 4, 2, RPL, SWIGLU, BF, ZP, BITS>(a, s);
   if (WC == 2 && WK == 4) return launch_coop_t<MT, SPW, 2, 4, RPL, SWIGLU, BF, ZP, BITS>(a, s);
+  if constexpr (SPW == 1)  // (the fused form would spill at 32 rows)
+    if (WC == 1 && WK == 8) return launch_coop_t<MT, SPW, 1, 8, RPL, SWIGLU, BF, ZP, BITS>(a, s);
   return launch_coop_t<MT, SPW, 1, 4, RPL, SWIGLU, BF, ZP, BITS>(a, s);
 }
 
@@ -436,7 +438,8 @@ static int coop_env(const char *name, int fallback) {
 //    K and two column groups per workgroup (the fused projections with at
 //    least 512 strip groups and plain ones with K >= 24576: four column
 //    groups, two waves along K; plain ones with 129-255 strip groups: one
-//    column group); K is split (power of two) while the grid stays within
+//    column group and eight waves along K, Llama-8B QKV 10.56 -> 9.90 us
+//    against four); K is split (power of two) while the grid stays within
 //    256 workgroups.  Measured at M = 32 against two waves along K with two
 //    column groups: Llama-8B QKV 11.4 -> 10.6 us, gate/up 20.8 -> 19.6 us,
 //    down 15.9 -> 15.1 us; Llama-70B QKV 21.3 -> 19.6 us, O 17.0 -> 15.9 us,
@@ -450,9 +453,11 @@ static int coop_env(const char *name, int fallback) {
 //    workgroup); the fewest column groups per workgroup that keep the grid
 //    within 256 workgroups.  M = 1 on wide shapes keeps one column group;
 //    the widest fused ones (>= 512 strip groups, fp16 INT4) take the
-//    per-wave kernel.
-// Narrow, short-K shapes at small M keep the per-wave kernel (its half-strip
-// grid fills the CUs without sharing activations).  W4A16_DECODE_COOP=0/1
+//    per-wave kernel.  Narrow plain shapes with short K (K < 12288) and
+//    192-255 strip groups at M > 8, or 128-255 at M = 16: one strip per
+//    workgroup with eight waves along K.
+// Other narrow, short-K shapes at small M keep the per-wave kernel (its
+// half-strip grid fills the CUs without sharing activations).  W4A16_DECODE_COOP=0/1
 // forces the choice; W4A16_COOP_WC / _WK / _KS override the configuration.
 bool coop_config(const Problem &p, int &WC, int &WK, int &KS) {
   const int nsg = (int)(p.swiglu ? (p.N / 2 / kStrip) : ceil_div(p.N, kStrip));
@@ -469,7 +474,7 @@ bool coop_config(const Problem &p, int &WC, int &WK, int &KS) {
     // LDS at M = 32), except for the widest fused projections and the
     // deepest plain ones (four column groups, two groups per round) and
     // mid-width plain ones that fill the CUs with one column group per
-    // workgroup and no K split.
+    // workgroup, eight groups per round (133 KiB) and no K split.
     use = true;
     if (p.swiglu) {
       WC = nsg >= 512 ? 4 : 2;
@@ -479,7 +484,7 @@ bool coop_config(const Problem &p, int &WC, int &WK, int &KS) {
       WK = 2;
     } else {
       WC = nsg > 128 && nsg < 256 ? 1 : 2;
-      WK = 4;
+      WK = WC == 1 ? 8 : 4;
     }
     KS = 1;
     if (WC > 1)
@@ -498,6 +503,16 @@ bool coop_config(const Problem &p, int &WC, int &WK, int &KS) {
     // workgroup barriers, measured 42.7 us against 46.5 us.
     use = false;
     WC = 1; WK = 4; KS = 1;
+  } else if (!p.swiglu && KG < 96 && nsg < 256 &&
+             ((p.M > 8 && nsg >= 192) || (p.M == 16 && nsg >= 128))) {
+    // Narrow, short-K plain projections (Llama-8B QKV at M > 8, O at
+    // M = 16): one strip per workgroup, eight waves along K, no K split.
+    // Measured at M = 16: QKV 7.56 (four waves along K) -> 7.09 us, O 7.09
+    // (per-wave kernel, half strips) -> 6.91 us; at M = 8-12 the O
+    // projection stays faster on the per-wave kernel (M = 8: 5.66 against
+    // 6.57 us) and QKV ties with it at M = 8.
+    use = true;
+    WC = 1; WK = 8; KS = 1;
   } else if (p.M == 1 && wide) {
     use = true;
     WC = 1; WK = 4; KS = 1;
@@ -514,10 +529,10 @@ bool coop_config(const Problem &p, int &WC, int &WK, int &KS) {
   WC = coop_env("W4A16_COOP_WC", WC);
   WK = coop_env("W4A16_COOP_WK", WK);
   KS = coop_env("W4A16_COOP_KS", KS);
-  static const int allowed[6][2] = {{4, 1}, {8, 1}, {2, 2}, {4, 2}, {2, 4}, {1, 4}};
+  static const int allowed[7][2] = {{4, 1}, {8, 1}, {2, 2}, {4, 2}, {2, 4}, {1, 4}, {1, 8}};
   bool ok = false;
   for (auto &c : allowed) ok |= (c[0] == WC && c[1] == WK);
-  if (!ok) return false;
+  if (!ok || (SPW == 2 && WC == 1 && WK == 8)) return false;
   if (KS > KG) KS = KG;
   if (KS < 1) KS = 1;
   if (coop_lds_bytes((int)p.M, WC, WK, SPW, p.zp) > kMaxLdsPerWorkgroup) return false;
