@@ -230,9 +230,10 @@ def test_describe_names_the_launches():
         "decode_coop_kernel<32, 1, 4, 2, 16, false, false, false, 4> workgroups=256 threads=512 ks=4")
     assert w4a16.describe(32, 4096, 28672, swiglu=True).startswith(
         "decode_coop_kernel<32, 2, 2, 4, 16, true, false, false, 4> workgroups=224 threads=512 ks=1")
-    assert "prefill2_kernel<4, 2, 4, 2, false, true, false, false, 4>" in w4a16.describe(
-        4096, 4096, 28672, swiglu=True)
-    assert "prefill2_kernel<4, 2, 4, 2, false, true, true, false, 4>" in w4a16.describe(
+    # Large batches: 128 x 512 tiles, the eight waves side by side.
+    assert w4a16.describe(4096, 4096, 28672, swiglu=True).startswith(
+        "prefill2_kernel<4, 1, 8, 2, false, true, false, false, 4> workgroups=1792 threads=512 ks=1")
+    assert "prefill2_kernel<4, 1, 8, 2, false, true, true, false, 4>" in w4a16.describe(
         4096, 4096, 28672, swiglu=True, bf16=True)
     # Transition batches: the skinny-tile kernel (64-row tiles with four waves
     # along K up to M = 64, 128-row tiles with two above), K split only where
@@ -244,7 +245,7 @@ def test_describe_names_the_launches():
     assert w4a16.describe(64, 14336, 4096).startswith(
         "transition_kernel<2, 2, 4, false, false, false, 4> workgroups=256 threads=512 ks=8; "
         "prefill_reduce_kernel<false, false>")
-    assert w4a16.describe(300, 4096, 28672, swiglu=True).startswith("prefill2_kernel<4, 2, 4, 2")
+    assert w4a16.describe(300, 4096, 28672, swiglu=True).startswith("prefill2_kernel<4, 1, 8, 2")
     assert w4a16.describe(33, 4096, 4096).startswith("transition_kernel<2, ")
     assert w4a16.describe(257, 4096, 4096).startswith("prefill2_kernel<")
     # Zero rows: both decode kernels scale before the MFMA (ZP instances),
@@ -266,7 +267,7 @@ def test_describe_names_the_launches():
     assert w4a16.describe(100, 4096, 4096, path="dense", int8=True).startswith(
         "dequant8_kernel<false, false>; ")
     assert w4a16.select_path(100, 4096, 4096, int8=True) == "prefill"
-    assert "prefill2_kernel<4, 2, 4, 2, false, false, false, true, 4>" in w4a16.describe(
+    assert "prefill2_kernel<4, 1, 8, 2, false, false, false, true, 4>" in w4a16.describe(
         4096, 4096, 4096, zp=True)
     assert w4a16.describe(4096, 4096, 4096, path="dense", zp=True).startswith(
         "dequant_kernel<false, false>; prefill")
