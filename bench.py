@@ -641,6 +641,16 @@ SWEEPS = {
         "variants": [("MFMA", {"W4A16_DECODE_COOP": "0"}),
                      ("v_dot2", {"W4A16_DECODE_COOP": "0", "W4A16_DECODE_DOT": "1"})],
     },
+    "smallm": {
+        "what": "the decode kernels against the transition kernel forced down to M = 16-32 (the "
+                "prefill path with W4A16_TRANSITION=1), Llama-8B projections",
+        "shapes": [(m, k, n, sw) for m in (16, 24, 32)
+                   for k, n, sw in ((4096, 6144, False), (4096, 4096, False), (4096, 28672, True),
+                                    (14336, 4096, False))],
+        "outliers": False,
+        "variants": [("decode", {}),
+                     ("transition", {"_path": "prefill", "W4A16_TRANSITION": "1"})],
+    },
     "decode70b": {
         "what": "Llama-70B one-row and small-M projections under both decode kernels",
         "shapes": [(m, 28672, 8192, False) for m in (1, 4, 16)]
@@ -685,17 +695,18 @@ def run_sweep(name, reps, torch, dev):
         for vname, env in order:
             for k in SWEEP_ENV:
                 os.environ.pop(k, None)
-            os.environ.update(env)
-            descs[vname] = w4a16.describe(M, K, N, swg)
-            w4a16.reserve_workspace(w4a16.workspace_bytes(M, K, N, swg))
+            path = env.get("_path", "auto")  # a path for the call, not an environment variable
+            os.environ.update({k: v for k, v in env.items() if not k.startswith("_")})
+            descs[vname] = w4a16.describe(M, K, N, swg, path=path)
+            w4a16.reserve_workspace(w4a16.workspace_bytes(M, K, N, swg, path=path))
             with torch.cuda.stream(stream):
-                w4a16.gemm(A, copies[0], swiglu=swg, out=out)
+                w4a16.gemm(A, copies[0], swiglu=swg, out=out, path=path)
             torch.cuda.synchronize()
             got = out.float().cpu().numpy()
             if ref is None:
                 ref = got
             rels[vname] = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30))
-            us = time_graph(torch, stream, lambda: [w4a16.gemm(A, c, swiglu=swg, out=out)
+            us = time_graph(torch, stream, lambda: [w4a16.gemm(A, c, swiglu=swg, out=out, path=path)
                                                     for c in copies], reps) * 1e3 / len(copies)
             times.setdefault(vname, []).append(us)
         best = min(times, key=lambda v: min(times[v]))
