@@ -139,7 +139,7 @@ def kernel_key(M, K, N, swiglu, bf16=False, zp=False, int8=False, path="auto"):
     if first.startswith("dequant"):
         name = desc.split(";")[1].split(" workgroups=")[0].strip()
         return name + " (dense tier)"
-    return name + (" + reduce" if ";" in desc else "")
+    return name + (" + reduce" if "reduce_kernel" in desc else "")
 
 
 # HIP sources that define each kernel family (the digest of stored counters
@@ -661,9 +661,30 @@ SWEEPS = {
                      ("per-wave half", {"W4A16_DECODE_COOP": "0", "W4A16_DECODE_HALF": "1"}),
                      ("cooperative", {"W4A16_DECODE_COOP": "1"})],
     },
+    "splitk": {
+        "what": "decode GEMMs that split K: the reduction launch against finishing the splits "
+                "inside the GEMM launch (W4A16_SPLIT_FINISH: pairwise atomic exchanges of the "
+                "partial values, or the last workgroup of a tile summing partial tiles written "
+                "through to the point of coherence), with the automatic configuration and with one "
+                "strip per workgroup, eight waves along K and two K splits",
+        "shapes": [(8, 14336, 4096, False), (16, 14336, 4096, False), (16, 4096, 4096, False),
+                   (32, 4096, 4096, False), (32, 14336, 4096, False), (4, 28672, 8192, False),
+                   (16, 28672, 8192, False), (32, 8192, 8192, False), (32, 28672, 8192, False)],
+        "outliers": False,
+        "variants": [("reduction launch", {}),
+                     ("exchange", {"W4A16_SPLIT_FINISH": "exchange"}),
+                     ("last workgroup", {"W4A16_SPLIT_FINISH": "last"}),
+                     ("1x8 KS=2, reduction launch",
+                      {"W4A16_DECODE_COOP": "1", "W4A16_COOP_WC": "1", "W4A16_COOP_WK": "8",
+                       "W4A16_COOP_KS": "2"}),
+                     ("1x8 KS=2, exchange",
+                      {"W4A16_DECODE_COOP": "1", "W4A16_COOP_WC": "1", "W4A16_COOP_WK": "8",
+                       "W4A16_COOP_KS": "2", "W4A16_SPLIT_FINISH": "exchange"})],
+    },
 }
 SWEEP_ENV = ("W4A16_TRANSITION", "W4A16_TRANSITION_MI", "W4A16_TRANSITION_KS",
-             "W4A16_DECODE_COOP", "W4A16_DECODE_DOT", "W4A16_DECODE_HALF")
+             "W4A16_DECODE_COOP", "W4A16_DECODE_DOT", "W4A16_DECODE_HALF",
+             "W4A16_COOP_WC", "W4A16_COOP_WK", "W4A16_COOP_KS", "W4A16_SPLIT_FINISH")
 
 
 def run_sweep(name, reps, torch, dev):

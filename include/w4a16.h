@@ -43,7 +43,10 @@
  *     _BM, _WM, _TPS, _KS, any of which selects the prefill kernels over the
  *     transition kernel); a value no kernel supports is clamped to a
  *     supported one or ignored.  The result of a GEMM does not depend on them
- *     beyond FP32 summation order.
+ *     beyond FP32 summation order.  W4A16_SPLIT_FINISH=exchange or =last
+ *     finishes a decode launch's K splits inside the launch instead of a
+ *     second, reduction launch (slots and counters in a fixed array per
+ *     device, so with it set, calls that overlap in time on one device race).
  */
 #ifndef W4A16_H
 #define W4A16_H

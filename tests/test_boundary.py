@@ -213,6 +213,15 @@ def test_describe_names_the_launches():
     assert d.endswith("ks=4; decode_reduce_kernel<1, false, false>"), d
     d = w4a16.describe(24, 4096, 4096, int8=True)
     assert d.startswith("decode_coop_kernel<32, 1, 2, 4, 16, false, false, false, 8>"), d
+    # Two K splits of a small output (M * output columns <= 16 * 8192) are
+    # finished inside the launch by exchanging the partials; more splits or a
+    # larger output keep the reduction launch.
+    d = w4a16.describe(8, 14336, 4096)
+    assert d.endswith("ks=2; K splits finished in the launch (exchange)"), d
+    d = w4a16.describe(16, 28672, 8192)
+    assert d.endswith("ks=2; K splits finished in the launch (exchange)"), d
+    d = w4a16.describe(32, 8192, 8192)
+    assert "ks=2" in d and d.endswith("decode_reduce_kernel<1, false, false>"), d
     # Mid-width plain projections: one column group with eight waves along
     # K, no K split; the widest fused ones: four column groups, two groups of
     # 128 k per round.

@@ -1,11 +1,13 @@
 """GPU GEMM parity against the oracle on the same seeded inputs, at sizes the
 oracle finishes in seconds, spanning several tiles and ragged tails, on every
 path (decode, prefill, dense) and with the SwiGLU epilogue."""
+import re
+
 import numpy as np
 import pytest
 
 import parity
-from gpuhelp import fp16_out, gemm_case, orc, say, to_dev, torch
+from gpuhelp import fp16_out, gemm_case, orc, sample_indices, say, to_dev, torch
 from weight_only_int4_03_amd import synth, w4a16
 
 pytestmark = pytest.mark.gpu
@@ -189,6 +191,84 @@ def test_decode_cooperative_bit_exact_integer_inputs(monkeypatch):
         packed_o, s16_o = orc().quantize_pack(W)
         C = orc().gemm_f64(A, packed_o, s16_o)
         assert np.array_equal(out.astype(np.float64), C)
+
+
+SPLIT_CASES = [  # forced configurations with K splits
+    {"W4A16_DECODE_COOP": "1", "W4A16_COOP_WC": "2", "W4A16_COOP_WK": "4", "W4A16_COOP_KS": "2"},
+    {"W4A16_DECODE_COOP": "1", "W4A16_COOP_WC": "1", "W4A16_COOP_WK": "4", "W4A16_COOP_KS": "3"},
+    {"W4A16_DECODE_COOP": "1", "W4A16_COOP_WC": "4", "W4A16_COOP_WK": "2", "W4A16_COOP_KS": "4"},
+    {"W4A16_DECODE_COOP": "1", "W4A16_COOP_WC": "1", "W4A16_COOP_WK": "8", "W4A16_COOP_KS": "2"},
+    {"W4A16_DECODE_COOP": "0", "W4A16_DECODE_KS": "2", "W4A16_DECODE_HALF": "1"},
+    {"W4A16_DECODE_COOP": "0", "W4A16_DECODE_KS": "3", "W4A16_DECODE_HALF": "0"},
+]
+
+
+@pytest.mark.parametrize("finish", ["auto", "exchange", "last"])
+@pytest.mark.parametrize("case", range(len(SPLIT_CASES)))
+@pytest.mark.parametrize("M,K,N,swiglu", [(1, 1152, 1064, False), (16, 1024, 2112, True),
+                                          (7, 2560, 4160, False), (32, 1152, 1064, False),
+                                          (24, 1024, 2112, True)])
+def test_split_finish_in_launch(monkeypatch, finish, case, M, K, N, swiglu):
+    """K splits finished inside the launch, against the reduction launch that
+    a call with a caller's workspace runs.  By default (auto) a call on the
+    library's workspace exchanges the partials of two splits when the output
+    is small; W4A16_SPLIT_FINISH forces the exchange or the last-workgroup
+    sum.  The last workgroup sums the partials in split order and the
+    exchange adds two partials commutatively, so both equal the reduction
+    launch bit for bit (the exchange with more splits adds in a fixed tree:
+    compared with the oracle).  Three calls in a row (the second on another
+    shape) check that every call leaves the slots and counters clear."""
+    env = SPLIT_CASES[case]
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    t = torch()
+    W = synth.weights(K, N, seed=case)
+    w = w4a16.load_weight(W)
+    A = to_dev(synth.activations(M, K, seed=M + case))
+    monkeypatch.delenv("W4A16_SPLIT_FINISH", raising=False)
+    ws = t.zeros(max(w4a16.workspace_bytes(M, K, N, swiglu, path="decode"), 256), dtype=t.uint8,
+                 device="cuda")
+    want = fp16_out(w4a16.gemm(A, w, swiglu=swiglu, path="decode", workspace=ws))
+    if finish != "auto":
+        monkeypatch.setenv("W4A16_SPLIT_FINISH", finish)
+    desc = w4a16.describe(M, K, N, swiglu, path="decode")
+    say("split finish:", desc)
+    ks = int(re.search(r"ks=(\d+)", desc).group(1))  # a configuration that does not fit falls back
+    in_launch = finish != "auto" or (ks == 2 and M * (N // 2 if swiglu else N) <= 16 * 8192)
+    if ks > 1:
+        assert ("finished in the launch" in desc) == in_launch, desc
+        assert ("decode_reduce_kernel" in desc) == (not in_launch), desc
+    W2 = synth.weights(K, 2 * N, seed=case + 1)
+    w2 = w4a16.load_weight(W2)
+    for rep in range(3):
+        got = fp16_out(w4a16.gemm(A, w2 if rep == 1 else w, swiglu=swiglu, path="decode"))
+        if rep == 1:
+            continue
+        if finish != "exchange" or ks <= 2:
+            assert np.array_equal(got.view(np.uint16), want.view(np.uint16)), (rep, desc)
+    t.cuda.synchronize()
+    gemm_case(M, K, N, swiglu=swiglu, path="decode", seed=M + case, W=W, weight=w)
+
+
+def test_split_exchange_full_size():
+    """The shapes whose automatic configuration exchanges two K splits in the
+    launch (Llama-8B down at M = 8, Llama-70B down at M = 4 and 16): the
+    library-workspace call equals the caller-workspace call (reduction launch)
+    bit for bit, and sampled columns match the oracle."""
+    t = torch()
+    for M, K, N in [(8, 14336, 4096), (4, 28672, 8192), (16, 28672, 8192)]:
+        desc = w4a16.describe(M, K, N)
+        say("exchange full size:", desc)
+        assert "ks=2" in desc and "finished in the launch (exchange)" in desc, desc
+        W = synth.weights(K, N, seed=M)
+        w = w4a16.load_weight(W)
+        A = to_dev(synth.activations(M, K, seed=M))
+        ws = t.zeros(w4a16.workspace_bytes(M, K, N), dtype=t.uint8, device="cuda")
+        ref = fp16_out(w4a16.gemm(A, w, workspace=ws))
+        for _ in range(2):
+            got = fp16_out(w4a16.gemm(A, w))
+            assert np.array_equal(got.view(np.uint16), ref.view(np.uint16)), (M, K, N)
+        gemm_case(M, K, N, seed=M, W=W, weight=w, cols=sample_indices(N, 64, seed=M, edge=8))
 
 
 @pytest.mark.parametrize("path", ["prefill", "dense"])

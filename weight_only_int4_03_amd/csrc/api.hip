@@ -289,7 +289,7 @@ int run_gemm(const uint16_t *A, int64_t M, int64_t K, const void *rw, const void
   if (requested > W4A16_PATH_DENSE)
     return fail(W4A16_ERR_INVALID, "%s: unknown path %d", who, requested);
   Problem p{A, M, K, N, rw, rs, out, swiglu, bf16, rowscale, G, group_shift(K, G), rz,
-            rz != nullptr, bits};
+            rz != nullptr, bits, workspace == nullptr || no_alloc};
   const char *why = nullptr;
   const int path = resolve_path(p, requested, &why);
   if (path < 0)

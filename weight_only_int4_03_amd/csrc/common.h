@@ -315,6 +315,7 @@ struct Problem {
   const void *rz = nullptr;  // prescaled zero rows, laid out as rs, or null
   bool zp = false;           // zero rows in use (rz != null when launching)
   int bits = 4;              // weight code width: 4 (INT4) or 8 (INT8)
+  bool own_ws = true;        // runs on the library's workspace or fixed scratch, not a caller's
 };
 
 // Group sizes: a power of two >= 32 that divides K, or K itself

@@ -33,7 +33,10 @@
 //     run to run.
 #include <cstdio>
 #include <cstdlib>
+#include <cstring>
+#include <mutex>
 #include <type_traits>
+#include <vector>
 
 #include "common.h"
 #include "decode_args.h"
@@ -456,14 +459,52 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(DecodeArgs p) {
       decode_epilogue<SPW, SWIGLU, BF>(p, sg, owned(e), wave_sum);
     return;
   }
+  if (p.xs != nullptr) {
+    // The KS workgroups of a strip group finish it here (split_exchange).
+    constexpr int EPT = (SH * MT * OWN + nthreads - 1) / nthreads;
+    const int E = SH * M * 32;
+    int64_t el[EPT];
+    bool live[EPT];
+    float v[EPT], u[EPT];
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      const int x = threadIdx.x + i * nthreads;
+      const int e = owned(x);
+      live[i] = x < SH * M * OWN;
+      el[i] = (int64_t)sg * E + e;
+      v[i] = live[i] ? wave_sum(e) : 0.0f;
+      u[i] = live[i] && SWIGLU ? wave_sum(e + E) : 0.0f;
+    }
+    split_exchange<EPT>(p.xs, p.KS, split, (int64_t)p.nsg * E, el, live, v, u);
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      if (!live[i]) continue;
+      const int e = owned(threadIdx.x + i * nthreads);
+      decode_epilogue<SPW, SWIGLU, BF>(p, sg, e, [&](int y) { return y == e ? v[i] : u[i]; });
+    }
+    return;
+  }
+  if (p.sync != nullptr) {
+    float *mine = p.ws + ((int64_t)sg * p.KS + split) * tileE;
+    for (int e = threadIdx.x; e < SPW * M * OWN; e += nthreads)
+      store_partial(mine + owned(e), wave_sum(owned(e)));
+    if (!split_last(p.sync + sg * (HALF ? 2 : 1) + half, p.KS, (int *)lds)) return;
+    const float *all = p.ws + (int64_t)sg * p.KS * tileE;
+    for (int e = threadIdx.x; e < SH * M * OWN; e += nthreads)
+      decode_epilogue<SPW, SWIGLU, BF>(p, sg, owned(e), [&](int y) {
+        return sum_partials(all + y, tileE, p.KS);
+      });
+    return;
+  }
   float *mine = p.ws + ((int64_t)sg * p.KS + split) * tileE;
   for (int e = threadIdx.x; e < SPW * M * OWN; e += nthreads) mine[owned(e)] = wave_sum(owned(e));
 }
 
 // Second stage for KS > 1: one thread per output element sums the KS partial
-// tiles of its strip group in split order, then runs the epilogue.  The
-// partials of up to eight splits are loaded before any is added, so their
-// memory latencies overlap instead of adding up.
+// tiles of its strip group in split order (starting from the first partial,
+// so two partials give p0 + p1 exactly as split_exchange does), then runs
+// the epilogue.  The partials of up to eight splits are loaded before any is
+// added, so their memory latencies overlap instead of adding up.
 template <int SPW, bool SWIGLU, bool BF>
 __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs p) {
   constexpr int SH = SWIGLU ? SPW / 2 : SPW;
@@ -482,7 +523,7 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs p) {
         t[i] = sp0 + i < p.KS ? all[(int64_t)(sp0 + i) * tileE + x] : 0.0f;
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        if (sp0 + i < p.KS) v += t[i];
+        if (sp0 + i < p.KS) v = sp0 + i == 0 ? t[i] : v + t[i];
     }
     return v;
   });
@@ -601,6 +642,69 @@ static bool decode_stagger(const Problem &p) {
   return on;
 }
 
+// Split-K finish inside the launch (split_exchange).  Measured on MI355X
+// (bench.py --sweep splitk): with two K splits and a small output the
+// exchange beats the reduction launch (Llama-8B down at M = 8: 10.9 against
+// 12.2 us; Llama-70B down at M = 4 and 16: 24.3 and 26.9 against 25.5 and
+// 27.8 us); with more splits or rows its one memory transaction per 8 bytes
+// of partial values costs more than the launch it saves (M = 32, four splits:
+// 14.4 against 9.6 us).  The exchange slots live in this fixed array, zero
+// when the library loads and left zero by every call; so the exchange runs
+// only for calls on the library's own workspace or fixed scratch, whose calls
+// must not overlap in time on one device anyway.  A call with a caller's
+// workspace keeps the reduction launch, which gives the same bits (two
+// partials: p0 + p1 either way).  W4A16_SPLIT_FINISH=exchange, =last (the
+// last workgroup of a tile sums partial tiles written through to the point of
+// coherence: split_last) or =reduce overrides the choice for measurement;
+// with it set, calls that overlap in time on one device race.
+static __device__ __align__(256) unsigned long long split_sync[1 << 20];  // 8 MiB
+constexpr int64_t kExchangeMaxElems = 16 * 8192;  // M * output columns
+
+static std::mutex g_split_sync_mutex;
+static std::vector<void *> g_split_sync;  // device address of split_sync, per device
+
+static void *split_sync_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lock(g_split_sync_mutex);
+  if ((int)g_split_sync.size() <= dev) g_split_sync.resize(dev + 1, nullptr);
+  if (g_split_sync[dev] == nullptr) {
+    void *q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(split_sync)) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_split_sync[dev] = q;
+  }
+  return g_split_sync[dev];
+}
+
+// How a launch with KS > 1 K splits is finished: 0 reduction launch,
+// 1 exchange, 2 last workgroup.
+static int split_finish(const Problem &p, int KS) {
+  if (KS <= 1) return 0;
+  const int64_t el = (p.swiglu ? p.N / 2 : ceil_div(p.N, kStrip) * kStrip) * p.M;
+  int mode = p.own_ws && KS == 2 && el <= kExchangeMaxElems ? 1 : 0;
+  const char *v = std::getenv("W4A16_SPLIT_FINISH");
+  if (v != nullptr && std::strcmp(v, "exchange") == 0) mode = 1;
+  if (v != nullptr && std::strcmp(v, "last") == 0) mode = 2;
+  if (v != nullptr && std::strcmp(v, "reduce") == 0) mode = 0;
+  if (mode == 1 && split_exchange_bytes(KS, el) > (int64_t)sizeof(split_sync)) mode = 0;
+  // (last: one counter per strip group and half strip, or column group)
+  if (mode == 2 && 2 * ceil_div(p.N, kStrip) * (int64_t)sizeof(unsigned) > (int64_t)sizeof(split_sync))
+    mode = 0;
+  return mode;
+}
+
+static int describe_finish(const Problem &p, int KS, int spw, const char *sw, const char *bf,
+                           char *buf, size_t n) {
+  switch (split_finish(p, KS)) {
+    case 1: return snprintf(buf, n, "; K splits finished in the launch (exchange)");
+    case 2: return snprintf(buf, n, "; K splits finished in the launch (last workgroup)");
+    default: return snprintf(buf, n, "; decode_reduce_kernel<%d, %s, %s>", spw, sw, bf);
+  }
+}
+
 int decode_describe(const Problem &p, char *buf, size_t n) {
   int WC, WK, KS;
   const char *sw = p.swiglu ? "true" : "false", *bf = p.bf16 ? "true" : "false";
@@ -615,8 +719,7 @@ int decode_describe(const Problem &p, char *buf, size_t n) {
                      mt, spw, WC, WK, rpl, sw, bf, p.zp ? "true" : "false", p.bits,
                      (int)ceil_div(nsg, WC) * KS, WC * WK * 64, KS);
     if (decode_stagger(p) && k > 0 && (size_t)k < n) k += snprintf(buf + k, n - k, " stagger");
-    if (KS > 1 && k > 0 && (size_t)k < n)
-      k += snprintf(buf + k, n - k, "; decode_reduce_kernel<%d, %s, %s>", spw, sw, bf);
+    if (KS > 1 && k > 0 && (size_t)k < n) k += describe_finish(p, KS, spw, sw, bf, buf + k, n - k);
     return k;
   }
   const DecodeConfig c = decode_config(p);
@@ -629,8 +732,7 @@ int decode_describe(const Problem &p, char *buf, size_t n) {
                    c.MT, c.SPW, c.WAVES, c.D, rpl, sw, bf, pre, zp, hf, p.bits,
                    c.nsg * c.KS * (c.half ? 2 : 1), c.WAVES * 64, c.KS);
   if (decode_stagger(p) && k > 0 && (size_t)k < n) k += snprintf(buf + k, n - k, " stagger");
-  if (c.KS > 1 && k > 0 && (size_t)k < n)
-    k += snprintf(buf + k, n - k, "; decode_reduce_kernel<%d, %s, %s>", c.SPW, sw, bf);
+  if (c.KS > 1 && k > 0 && (size_t)k < n) k += describe_finish(p, c.KS, c.SPW, sw, bf, buf + k, n - k);
   return k;
 }
 
@@ -654,7 +756,7 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t s) {
   hipLaunchKernelGGL((decode_kernel<MT, SPW, WAVES, D, RPL, SWIGLU, BF, PRE, ZP, HALF, BITS>),
                      dim3(a.nsg * a.KS * (HALF ? 2 : 1)), dim3(WAVES * 64), lds, s, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.KS == 1) return e;
+  if (e != hipSuccess || a.KS == 1 || a.xs != nullptr || a.sync != nullptr) return e;
   return launch_decode_reduce(a, SWIGLU, BF, s);
 }
 
@@ -695,6 +797,11 @@ static hipError_t launch_decode_bf(const Problem &p, const DecodeArgs &a, const 
 
 DecodeArgs decode_args(const Problem &p, int KS, void *workspace) {
   DecodeArgs a;
+  a.xs = nullptr;
+  a.sync = nullptr;
+  const int finish = split_finish(p, KS);
+  if (finish == 1) a.xs = (unsigned long long *)split_sync_address();
+  if (finish == 2 && workspace != nullptr) a.sync = (unsigned *)split_sync_address();
   a.A = p.A;
   a.M = (int)p.M;
   a.K = (int)p.K;

@@ -21,7 +21,9 @@
 // stream per wave straight into registers, D rounds ahead, and are
 // dequantized in registers into MFMA operands.  At the end the WK partial
 // tiles of each column are summed through LDS; with KS > 1 the partial
-// tiles go to the workspace and decode_reduce_kernel finishes them.
+// tiles go to the workspace and decode_reduce_kernel finishes them (or, as a
+// measurement switch, the launch finishes them itself: split_exchange,
+// split_last).
 #include <cstdio>
 #include <cstdlib>
 #include <type_traits>
@@ -366,6 +368,52 @@ __global__ __launch_bounds__(WC * WK * 64) void decode_coop_kernel(DecodeArgs p)
     }
     return;
   }
+  if (p.xs != nullptr) {
+    // The KS workgroups of a strip group finish it here (split_exchange):
+    // each element's partials meet pairwise; the last holder runs the epilogue.
+    constexpr int EPT = (WC * SH * MT * 32 + NT - 1) / NT;
+    const int E = SH * M * 32;
+    int64_t el[EPT];
+    bool live[EPT];
+    float v[EPT], u[EPT];
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      const int x = tid + i * NT;
+      const int wcc = x / E, e = x - wcc * E;
+      live[i] = x < WC * E && cg * WC + wcc < p.nsg;
+      el[i] = (int64_t)(cg * WC + wcc) * E + e;
+      v[i] = live[i] ? sum_wk(wcc, e) : 0.0f;
+      u[i] = live[i] && SWIGLU ? sum_wk(wcc, e + E) : 0.0f;
+    }
+    split_exchange<EPT>(p.xs, p.KS, split, (int64_t)p.nsg * E, el, live, v, u);
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      if (!live[i]) continue;
+      const int x = tid + i * NT;
+      const int wcc = x / E, e = x - wcc * E;
+      decode_epilogue<SPW, SWIGLU, BF>(p, cg * WC + wcc, e,
+                                       [&](int y) { return y == e ? v[i] : u[i]; });
+    }
+    return;
+  }
+  if (p.sync != nullptr) {
+    for (int x = tid; x < WC * tileE; x += NT) {
+      const int wcc = x / tileE, e = x - wcc * tileE;
+      const int sgg = cg * WC + wcc;
+      if (sgg < p.nsg) store_partial(p.ws + ((int64_t)sgg * p.KS + split) * tileE + e, sum_wk(wcc, e));
+    }
+    if (!split_last(p.sync + cg, p.KS, (int *)lds)) return;
+    const int E = SH * M * 32;
+    for (int x = tid; x < WC * E; x += NT) {
+      const int wcc = x / E, e = x - wcc * E;
+      const int sgg = cg * WC + wcc;
+      if (sgg < p.nsg)
+        decode_epilogue<SPW, SWIGLU, BF>(p, sgg, e, [&](int y) {
+          return sum_partials(p.ws + (int64_t)sgg * p.KS * tileE + y, tileE, p.KS);
+        });
+    }
+    return;
+  }
   for (int x = tid; x < WC * tileE; x += NT) {
     const int wcc = x / tileE, e = x - wcc * tileE;
     const int sgg = cg * WC + wcc;
@@ -550,7 +598,7 @@ hipError_t launch_decode_coop(const Problem &p, void *workspace, int WC, int WK,
                             : launch_coop_bf<false, true, 4>(p, a, WC, WK, s))
                   : (p.bf16 ? launch_coop_bf<true, false, 4>(p, a, WC, WK, s)
                             : launch_coop_bf<false, false, 4>(p, a, WC, WK, s));
-  if (e != hipSuccess || KS == 1) return e;
+  if (e != hipSuccess || KS == 1 || a.xs != nullptr || a.sync != nullptr) return e;
   return launch_decode_reduce(a, p.swiglu, p.bf16, s);
 }
 
