@@ -238,7 +238,13 @@ int w4a16_gemm_int8(const uint16_t *A_d, int64_t M, int64_t K, const void *rw_d,
  * W4A16_ERR_WORKSPACE instead -- size it beforehand with
  * w4a16_reserve_workspace(w4a16_gemm_workspace_bytes(...)).  Calls that
  * overlap in time on one device (different streams) must use w4a16_gemm_ex
- * with separate workspaces.
+ * with separate workspaces.  A decode launch that splits K in two with a
+ * small output (M times output columns <= 131072) finishes the splits inside
+ * the launch, exchanging the two partial values of each output through slots
+ * the library holds per device (8 MiB with the library's code object, zero
+ * whenever no call runs; the first such call on a device looks up their
+ * address: make it outside stream capture); with a caller's workspace
+ * (w4a16_gemm_ex) a second launch sums them instead, with the same bits.
  * A shape the selected kernel cannot take (operands beyond a kernel's 32-bit
  * offsets) runs a slower kernel instead; each such fallback is reported once
  * per process on stderr and by w4a16_last_fallback (the INT4 kernels page,
@@ -288,7 +294,9 @@ int w4a16_gemm_ex(const uint16_t *A_d, int64_t M, int64_t K, const void *rw_d,
  * weight).  All calls on one GPU share its scratch: calls that overlap in
  * time on one GPU (different streams) race and must not be issued; calls on
  * one stream are safe.  The first call on each device looks up the scratch's
- * device address (make it outside capture). */
+ * device address (make it outside capture).  Like w4a16_gemm it finishes two
+ * K splits of a small decode output inside the launch, through the library's
+ * per-device exchange slots. */
 int w4a16_gemm_noalloc(const uint16_t *A_d, int64_t M, int64_t K, const void *rw_d,
                        const void *rs_d, int64_t N, int G, uint16_t *out_d, int flags,
                        w4a16_stream_t stream);
