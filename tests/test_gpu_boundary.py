@@ -71,6 +71,39 @@ def test_capture_refuses_to_allocate_then_replays_after_reserve():
     parity.assert_close(out.cpu().numpy(), C, "captured decode M=%d" % M)
 
 
+def test_captured_split_exchange_replays():
+    """A decode GEMM whose two K splits exchange their partials inside the
+    launch, captured in a HIP graph: every replay (with eager GEMMs of the
+    same kind between them) equals the eager result bit for bit, so each
+    call leaves the exchange slots clear for the next."""
+    T = torch()
+    M, K, N = 8, 14336, 4096
+    desc = w4a16.describe(M, K, N)
+    say("captured exchange:", desc)
+    assert "finished in the launch (exchange)" in desc, desc
+    w4a16.reserve_workspace(w4a16.workspace_bytes(M, K, N))
+    W = synth.weights(K, N, seed=31)
+    A = to_dev(synth.activations(M, K, seed=31))
+    w = w4a16.load_weight(W)
+    out = T.empty((M, N), dtype=T.float16, device="cuda")
+    eager = w4a16.gemm_plain(A, w).cpu().numpy()
+    s = T.cuda.Stream()
+    T.cuda.synchronize()
+    g = T.cuda.CUDAGraph()
+    with T.cuda.graph(g, stream=s):
+        rc = _raw_gemm(A, w, out, s)
+    assert rc == w4a16.OK, w4a16.last_error()
+    other = to_dev(synth.activations(M, K, seed=32))
+    for r in range(4):
+        out.fill_(7.0)
+        T.cuda.synchronize()
+        g.replay()
+        T.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy().view(np.uint16), eager.view(np.uint16)), r
+        w4a16.gemm_plain(other, w)
+        T.cuda.synchronize()
+
+
 def test_growth_outside_capture_keeps_earlier_results():
     """A larger call outside capture grows the workspace without
     synchronising or freeing: work queued on the old buffer stays valid."""
