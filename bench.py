@@ -621,15 +621,21 @@ def roofline_entry(res, ceilings, zp, int8, suffix):
 # after a weight change is not favoured or penalised.
 SWEEPS = {
     "transition": {
-        "what": "the transition kernel against the 1 x 8 prefill tile it replaced (1% outlier "
-                "activations)",
+        "what": "the transition kernel against the 1 x 8 prefill tile it replaced, and its "
+                "Stream-K form (1% outlier activations)",
         "shapes": [(m, 4096, 28672, False) for m in (48, 64, 96, 128, 192, 256, 384)]
                   + [(m, 14336, 4096, False) for m in (48, 64, 96, 128, 192, 256, 384)],
         "outliers": True,
         "variants": [("prefill tile", {"W4A16_TRANSITION": "0"}),
-                     ("transition", {"W4A16_TRANSITION": "1"}),
-                     ("transition MI=2", {"W4A16_TRANSITION": "1", "W4A16_TRANSITION_MI": "2"}),
-                     ("transition MI=4", {"W4A16_TRANSITION": "1", "W4A16_TRANSITION_MI": "4"})],
+                     ("transition (automatic)", {"W4A16_TRANSITION": "1"}),
+                     ("tiles", {"W4A16_TRANSITION": "1", "W4A16_TRANSITION_SK": "0"}),
+                     ("tiles MI=2", {"W4A16_TRANSITION": "1", "W4A16_TRANSITION_SK": "0",
+                                     "W4A16_TRANSITION_MI": "2"}),
+                     ("tiles MI=4", {"W4A16_TRANSITION": "1", "W4A16_TRANSITION_SK": "0",
+                                     "W4A16_TRANSITION_MI": "4"}),
+                     ("stream-K", {"W4A16_TRANSITION": "1", "W4A16_TRANSITION_SK": "1"}),
+                     ("stream-K MI=4", {"W4A16_TRANSITION": "1", "W4A16_TRANSITION_SK": "1",
+                                        "W4A16_TRANSITION_MI": "4"})],
     },
     "dot": {
         "what": "one-row GEMMs: the per-wave kernel with MFMA (activation row padded to 16 rows) "
@@ -682,7 +688,7 @@ SWEEPS = {
                        "W4A16_COOP_KS": "2", "W4A16_SPLIT_FINISH": "exchange"})],
     },
 }
-SWEEP_ENV = ("W4A16_TRANSITION", "W4A16_TRANSITION_MI", "W4A16_TRANSITION_KS",
+SWEEP_ENV = ("W4A16_TRANSITION", "W4A16_TRANSITION_MI", "W4A16_TRANSITION_KS", "W4A16_TRANSITION_SK",
              "W4A16_DECODE_COOP", "W4A16_DECODE_DOT", "W4A16_DECODE_HALF",
              "W4A16_COOP_WC", "W4A16_COOP_WK", "W4A16_COOP_KS", "W4A16_SPLIT_FINISH")
 

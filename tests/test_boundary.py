@@ -334,3 +334,24 @@ def test_workspace_calls_without_gpu():
     assert w4a16.lib().w4a16_reserve_workspace(-1) == w4a16.ERR_INVALID
     assert w4a16.lib().w4a16_reserve_workspace(1024) == w4a16.ERR_HIP
     assert w4a16.last_fallback() == ""
+
+
+def test_transition_stream_k_launch_and_workspace(monkeypatch):
+    """W4A16_TRANSITION_SK=1: one workgroup per CU, each with an equal run of
+    (tile, round) units; a tile's share of several workgroups goes to partial
+    slices, so the workspace holds as many slices as the most workgroups that
+    share a tile (transition_sk_reduce_kernel finishes them)."""
+    monkeypatch.setenv("W4A16_TRANSITION_SK", "1")
+    # 64 rows, 4096 x 28672: 224 tiles of 8 rounds = 1792 units, 7 per workgroup.
+    d = w4a16.describe(64, 4096, 28672)
+    assert d.startswith("transition_sk_kernel<2, 2, 4, false, false, false, 4> workgroups=256 "), d
+    assert "stream-k units=1792 per_workgroup=7; transition_sk_reduce_kernel<false, false>" in d, d
+    assert w4a16.workspace_bytes(64, 4096, 28672) == 2 * 64 * 28672 * 4
+    # 260 tiles of 3 rounds, 4 units per workgroup: tiles shared by at most two.
+    monkeypatch.setenv("W4A16_TRANSITION_MI", "2")
+    d = w4a16.describe(256, 1152, 8320)
+    assert "workgroups=195 " in d and "units=780 per_workgroup=4" in d, d
+    assert w4a16.workspace_bytes(256, 1152, 8320) == 2 * 256 * 8320 * 4
+    # Zero rows and INT8 weights keep the tiled form.
+    assert w4a16.describe(64, 4096, 4096, zp=True).startswith("transition_kernel<")
+    assert w4a16.describe(64, 4096, 4096, int8=True).startswith("transition_kernel<")

@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 
 def _kernel(M, K, N, swiglu=False, **kw):
     d = w4a16.describe(M, K, N, swiglu=swiglu, path="prefill", **kw)
-    assert d.startswith("transition_kernel<"), d
+    assert d.startswith(("transition_kernel<", "transition_sk_kernel<")), d
     return d
 
 
@@ -117,3 +117,60 @@ def test_transition_group_sizes(G):
     half) and channelwise scales."""
     _kernel(100, 2048, 1088)
     gemm_case(100, 2048, 1088, seed=G, G=G)
+
+
+SK_SHAPES = [(33, 1152, 1064, False), (64, 2048, 2112, True), (100, 3072, 1088, False),
+             (200, 1152, 2112, True), (256, 1152, 8320, False)]
+
+
+@pytest.mark.parametrize("mi", [2, 4])
+@pytest.mark.parametrize("M,K,N,swiglu", SK_SHAPES)
+def test_transition_stream_k(monkeypatch, mi, M, K, N, swiglu):
+    """The Stream-K form: (tile, round) units dealt in equal runs to one
+    workgroup per CU.  The shapes give tiles shared by up to four workgroups
+    (their partial slices summed in order by the reduction kernel), tiles
+    finished by the one workgroup that covers them (K = 1152 with 260 tiles),
+    ragged rows and column tails, partial last rounds (nine groups) and the
+    SwiGLU epilogue; two calls give the same bits."""
+    monkeypatch.setenv("W4A16_TRANSITION", "1")
+    monkeypatch.setenv("W4A16_TRANSITION_SK", "1")
+    monkeypatch.setenv("W4A16_TRANSITION_MI", str(mi))
+    d = w4a16.describe(M, K, N, swiglu=swiglu, path="prefill")
+    say(d)
+    assert d.startswith("transition_sk_kernel<%d, " % mi) and "stream-k" in d, d
+    W = synth.weights(K, N, seed=M + K)
+    w = w4a16.load_weight(W)
+    gemm_case(M, K, N, swiglu=swiglu, path="prefill", seed=M + N, W=W, weight=w)
+    A = to_dev(synth.activations(M, K, seed=M + N))
+    a = fp16_out(w4a16.gemm(A, w, swiglu=swiglu, path="prefill"))
+    b = fp16_out(w4a16.gemm(A, w, swiglu=swiglu, path="prefill"))
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+
+
+@pytest.mark.parametrize("M,K,N", [(128, 4096, 2048), (64, 8192, 1024), (256, 1152, 8320)])
+def test_transition_stream_k_integer_exact(monkeypatch, M, K, N):
+    """Integer-exact inputs through the Stream-K form: the output equals the
+    oracle's bit for bit, shared tiles included."""
+    monkeypatch.setenv("W4A16_TRANSITION", "1")
+    monkeypatch.setenv("W4A16_TRANSITION_SK", "1")
+    say(w4a16.describe(M, K, N, path="prefill"))
+    W = synth.grid_weights(K, N, p=4, seed=M + K)
+    A = synth.ternary_activations(M, K, density=0.5, seed=M)
+    out = fp16_out(w4a16.gemm(to_dev(A), w4a16.load_weight(W), path="prefill"))
+    packed_o, s16_o = orc().quantize_pack(W)
+    C = orc().gemm_f64(A, packed_o, s16_o)
+    assert np.abs(C).max() < 128, "inputs not fp16-exact"
+    assert np.array_equal(out.astype(np.float64), C)
+
+
+@pytest.mark.parametrize("M,swiglu,bf16", [(64, False, True), (200, True, True), (100, True, False)])
+def test_transition_stream_k_bf16_rowscale(monkeypatch, M, swiglu, bf16):
+    """bf16 activations and the row factor through the Stream-K form (the
+    factor applied in the reduction kernel for shared tiles)."""
+    from test_gpu_gemm import test_gemm_rowscale_each_path as rowscale_case
+    monkeypatch.setenv("W4A16_TRANSITION", "1")
+    monkeypatch.setenv("W4A16_TRANSITION_SK", "1")
+    assert w4a16.describe(M, 2048, 2112, swiglu=swiglu, path="prefill",
+                          bf16=bf16).startswith("transition_sk_kernel<")
+    gemm_case(M, 2048, 2112, swiglu=swiglu, path="prefill", seed=M, bf16=bf16)
+    rowscale_case("prefill", M, 2048, 2112, swiglu, bf16)

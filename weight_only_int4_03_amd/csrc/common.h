@@ -396,6 +396,9 @@ int tiled_describe(const Problem &p, bool dense, char *buf, size_t n);
 // returns false where the kernel does not take the problem.
 struct TransConfig {
   int mi, wc, wk, ks, tiles, row_tiles, col_groups;
+  // Stream-K: units per workgroup (0: one tile or K slice per workgroup),
+  // (tile, round) units, rounds per tile, most workgroups sharing a tile.
+  int sk_upw = 0, sk_units = 0, sk_rounds = 0, sk_parts = 1;
 };
 bool transition_config(const Problem &p, TransConfig &c);
 int64_t transition_workspace_bytes(const Problem &p);

@@ -53,7 +53,12 @@ struct TransArgs {
   int up_off;             // SwiGLU: strip offset from a gate strip to its up strip
   int npairs;             // strip pairs (SwiGLU: gate strips; plain: ceil(NS / 2))
   int row_tiles, col_groups, KS;
-  float *ws;              // KS > 1: FP32 partials [KS][M][N]
+  // Stream-K (upw > 0): the flat work is `units` (tile, round) units, tile by
+  // tile (row tile fastest) and round by round; each workgroup takes upw
+  // consecutive units.  A tile covered by several workgroups is finished by
+  // transition_sk_reduce_kernel from their partials.
+  int upw, units, rt_rounds;
+  float *ws;              // FP32 partials [slice][M][N]: K slice, or a tile's part in Stream-K
   const float *rowscale;  // per-row output factor, or null
   int gshift;             // group of k = k >> gshift
 };
@@ -63,9 +68,12 @@ struct TransArgs {
 // outstanding and for nothing else.
 constexpr int vm_wait(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
+// One tile of the transition GEMM: row tile rt, column group cg, over the
+// groups [gb, ge) of K, into the output or (slice >= 0) into FP32 partial
+// slice `slice` of the workspace.
 template <int MI, int WC, int WK, bool SWIGLU, bool BF, bool ZP, int BITS>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void transition_kernel(TransArgs p) {
+__device__ __forceinline__ void transition_tile(const TransArgs &p, const int rt, const int cg,
+                                                const int gb, const int ge, const int slice) {
   constexpr int NW = WC * WK;
   static_assert(NW == 8, "eight waves per workgroup");
   constexpr int BM = 32 * MI;
@@ -94,18 +102,6 @@ void transition_kernel(TransArgs p) {
   const int h = lane >> 5, c = lane & 31;
   const Dequant dq;
 
-  // XCD-aware walk: workgroup ids are dealt round-robin over the 8 XCDs; each
-  // XCD takes a contiguous range of (row tile, column group, K slice) triples
-  // with the row tile fastest, so the row tiles that read the same weights
-  // run together on one XCD's L2.
-  const int T = p.row_tiles * p.col_groups * p.KS;
-  const int b = blockIdx.x;
-  const int xcd = b & 7, local = b >> 3;
-  const int per = T >> 3, extra = T & 7;
-  const int tau = xcd * per + (xcd < extra ? xcd : extra) + local;
-  const int rt = tau % p.row_tiles;
-  const int rest = tau / p.row_tiles;
-  const int cg = rest % p.col_groups, ks = rest / p.col_groups;
   const int m0 = rt * BM;
 
   const int pair = cg * WC + wc;
@@ -122,9 +118,7 @@ void transition_kernel(TransArgs p) {
     sval[1] = strip[1] < p.NS;
   }
 
-  // K slice of this workgroup: groups [gb, ge), R rounds of WK groups.
-  const int gb = (int)((int64_t)p.KG * ks / p.KS);
-  const int ge = (int)((int64_t)p.KG * (ks + 1) / p.KS);
+  // R rounds of WK groups.
   const int R = (ge - gb + WK - 1) / WK;
 
   // Buffer resources.  The activation resources (one per round, below) start
@@ -343,13 +337,13 @@ void transition_kernel(TransArgs p) {
 
   // acc[s][i][4*rg + e] is the output at row m0 + 32 i + c and column
   // 32 strip[s] + 8 rg + 4 h + e.
-  if (p.KS > 1) {
-    float *slice = p.ws + (int64_t)ks * p.M * p.N;
+  if (slice >= 0) {
+    float *part = p.ws + (int64_t)slice * p.M * p.N;
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
       const int m = m0 + 32 * i + c;
       if (m >= p.M) continue;
-      float *prow = slice + (int64_t)m * p.N;
+      float *prow = part + (int64_t)m * p.N;
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         if (!sval[s]) continue;
@@ -397,6 +391,130 @@ void transition_kernel(TransArgs p) {
       }
     }
   }
+}
+
+template <int MI, int WC, int WK, bool SWIGLU, bool BF, bool ZP, int BITS>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void transition_kernel(TransArgs p) {
+  // XCD-aware walk: workgroup ids are dealt round-robin over the 8 XCDs; each
+  // XCD takes a contiguous range of (row tile, column group, K slice) triples
+  // with the row tile fastest, so the row tiles that read the same weights
+  // run together on one XCD's L2.
+  const int T = p.row_tiles * p.col_groups * p.KS;
+  const int b = blockIdx.x;
+  const int xcd = b & 7, local = b >> 3;
+  const int per = T >> 3, extra = T & 7;
+  const int tau = xcd * per + (xcd < extra ? xcd : extra) + local;
+  const int rt = tau % p.row_tiles;
+  const int rest = tau / p.row_tiles;
+  const int cg = rest % p.col_groups, ks = rest / p.col_groups;
+  // K slice of this workgroup: groups [gb, ge).
+  transition_tile<MI, WC, WK, SWIGLU, BF, ZP, BITS>(
+      p, rt, cg, (int)((int64_t)p.KG * ks / p.KS), (int)((int64_t)p.KG * (ks + 1) / p.KS),
+      p.KS > 1 ? ks : -1);
+}
+
+// Stream-K form (the Swordfish page, "Decode, counting memory-pipe slots": a
+// persistent kernel over flat (tile, k-slice) units for the batches above
+// M = 48): one workgroup per CU, each taking p.upw consecutive (tile, round)
+// units, tile by tile.  A tile whose units all fall in one workgroup's range
+// is finished there; otherwise each workgroup's share goes to partial slice
+// (workgroup - the tile's first workgroup) and transition_sk_reduce_kernel
+// adds the slices in that order.  The pages flush with atomic adds into the
+// output instead; the slices keep the sum deterministic.
+template <int MI, int WC, int WK, bool SWIGLU, bool BF, bool ZP, int BITS>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void transition_sk_kernel(TransArgs p) {
+  // The workgroups' unit ranges are dealt by the same XCD-aware walk.
+  const int T = (int)gridDim.x;
+  const int b = blockIdx.x;
+  const int xcd = b & 7, local = b >> 3;
+  const int per = T >> 3, extra = T & 7;
+  const int tau = xcd * per + (xcd < extra ? xcd : extra) + local;
+  const int u0 = tau * p.upw;
+  const int u1 = u0 + p.upw < p.units ? u0 + p.upw : p.units;
+  for (int u = u0; u < u1;) {
+    const int t = u / p.rt_rounds, r0 = u - t * p.rt_rounds;
+    const int len = p.rt_rounds - r0 < u1 - u ? p.rt_rounds - r0 : u1 - u;
+    const int first = t * p.rt_rounds / p.upw, last = ((t + 1) * p.rt_rounds - 1) / p.upw;
+    const int ge = (r0 + len) * WK < p.KG ? (r0 + len) * WK : p.KG;
+    // The previous tile's cross-wave sum (in the stages) has been read.
+    if (u != u0) __syncthreads();
+    transition_tile<MI, WC, WK, SWIGLU, BF, ZP, BITS>(p, t % p.row_tiles, t / p.row_tiles,
+                                                      r0 * WK, ge,
+                                                      first == last ? -1 : tau - first);
+    u += len;
+  }
+}
+
+// Second stage of a Stream-K launch: the tiles that several workgroups
+// shared.  Each thread takes 4 consecutive outputs of a row, finds its tile
+// and the workgroups that covered it, and (if more than one) sums their
+// partial slices in order (the tile's first K units first) and runs the
+// epilogue; a tile one workgroup covered was finished by that workgroup.
+template <bool SWIGLU, bool BF>
+__global__ __launch_bounds__(256) void transition_sk_reduce_kernel(TransArgs p, int BM, int WC) {
+  const int per_row = p.ldo >> 2;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)p.M * per_row) return;
+  const int m = (int)(idx / per_row), n = (int)(idx - (int64_t)m * per_row) * 4;
+  const int pair = SWIGLU ? n / 32 : n / 64;
+  const int t = (pair / WC) * p.row_tiles + m / BM;
+  const int first = t * p.rt_rounds / p.upw, last = ((t + 1) * p.rt_rounds - 1) / p.upw;
+  if (first == last) return;
+  const int parts = last - first + 1;
+  const int64_t slice = (int64_t)p.M * p.N;
+  const float *src = p.ws + (int64_t)m * p.N + n;
+  // The partials of up to eight parts are loaded before any is added, so
+  // their memory latencies overlap; they are added in part order.
+  float4_t g = {0.0f, 0.0f, 0.0f, 0.0f}, u = {0.0f, 0.0f, 0.0f, 0.0f};
+  constexpr int B = 8;
+  for (int k0 = 0; k0 < parts; k0 += B) {
+    float4_t tg[B], tu[B];
+#pragma unroll
+    for (int i = 0; i < B; ++i) {
+      if (k0 + i < parts) {
+        tg[i] = *(const float4_t *)(src + (k0 + i) * slice);
+        if constexpr (SWIGLU) tu[i] = *(const float4_t *)(src + (k0 + i) * slice + p.N / 2);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < B; ++i) {
+      if (k0 + i < parts) {
+        g = k0 + i == 0 ? tg[i] : g + tg[i];
+        if constexpr (SWIGLU) u = k0 + i == 0 ? tu[i] : u + tu[i];
+      }
+    }
+  }
+  if (p.rowscale != nullptr) {
+    g *= p.rowscale[m];
+    u *= p.rowscale[m];
+  }
+  uint2 o;
+  if constexpr (SWIGLU)
+    o = uint2{pack_out2<BF>(silu_mul(g[0], u[0]), silu_mul(g[1], u[1])),
+              pack_out2<BF>(silu_mul(g[2], u[2]), silu_mul(g[3], u[3]))};
+  else
+    o = uint2{pack_out2<BF>(g[0], g[1]), pack_out2<BF>(g[2], g[3])};
+  *(uint2 *)(p.out + (int64_t)m * p.ldo + n) = o;
+}
+
+static hipError_t launch_sk_reduce(const Problem &p, const TransArgs &a, int BM, int WC,
+                                   hipStream_t s) {
+  const dim3 grid((unsigned)ceil_div(p.M * (a.ldo / 4), 256));
+  const dim3 block(256);
+  if (p.swiglu) {
+    if (p.bf16)
+      hipLaunchKernelGGL((transition_sk_reduce_kernel<true, true>), grid, block, 0, s, a, BM, WC);
+    else
+      hipLaunchKernelGGL((transition_sk_reduce_kernel<true, false>), grid, block, 0, s, a, BM, WC);
+  } else {
+    if (p.bf16)
+      hipLaunchKernelGGL((transition_sk_reduce_kernel<false, true>), grid, block, 0, s, a, BM, WC);
+    else
+      hipLaunchKernelGGL((transition_sk_reduce_kernel<false, false>), grid, block, 0, s, a, BM, WC);
+  }
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -485,20 +603,58 @@ bool transition_config(const Problem &p, TransConfig &c) {
   const int ks_env = env_int("W4A16_TRANSITION_KS", 0);
   if (ks_env > 0) c.ks = (int)(ks_env < KG ? ks_env : KG);
   c.tiles = (int)(tiles * c.ks);
+  c.sk_upw = 0;
+  c.sk_parts = 1;
+  // Stream-K (W4A16_TRANSITION_SK=1; INT4 weights without zero rows): the
+  // (tile, round) units dealt evenly, upw consecutive units per workgroup,
+  // one workgroup per CU.  Not the default: measured on MI355X (bench.py
+  // --sweep transition, three runs on two boxes) it wins only on the
+  // Llama-8B down projection at M = 128 (1.0-1.4 us of 31) and within
+  // 0.1-0.5 us at M = 48 and 64; with the same K partition as the tiles'
+  // split (M = 96, 256) its walk order costs 0.4-1.7 us, where it shares
+  // tiles among more workgroups than the split (M = 192) 7 us, and where the
+  // tiles need no split (gate/up: every tile then writes two partial slices)
+  // 8-11 us.
+  if (p.bits == 4 && !p.zp) {
+    const int64_t rounds = ceil_div(KG, c.wk), units = tiles * rounds;
+    const int64_t upw = ceil_div(units, cus);
+    int parts = 1;
+    for (int64_t t = 0; t < tiles; ++t) {
+      const int64_t n = ((t + 1) * rounds - 1) / upw - t * rounds / upw + 1;
+      if (n > parts) parts = (int)n;
+    }
+    const char *sk = std::getenv("W4A16_TRANSITION_SK");
+    if (sk != nullptr && *sk == '1') {
+      c.ks = 1;
+      c.sk_rounds = (int)rounds;
+      c.sk_units = (int)units;
+      c.sk_upw = (int)upw;
+      c.sk_parts = parts;
+      c.tiles = (int)ceil_div(units, upw);
+    }
+  }
   return true;
 }
 
 int64_t transition_workspace_bytes(const Problem &p) {
   TransConfig c;
-  if (!transition_config(p, c) || c.ks == 1) return 0;
-  return (int64_t)c.ks * p.M * p.N * (int64_t)sizeof(float);
+  if (!transition_config(p, c)) return 0;
+  const int64_t slices = c.sk_upw > 0 ? c.sk_parts : c.ks;
+  return slices > 1 ? slices * p.M * p.N * (int64_t)sizeof(float) : 0;
 }
 
 int transition_describe(const Problem &p, const TransConfig &c, char *buf, size_t n) {
   const char *sw = p.swiglu ? "true" : "false", *bf = p.bf16 ? "true" : "false";
   int k = snprintf(buf, n,
-                   "transition_kernel<%d, %d, %d, %s, %s, %s, %d> workgroups=%d threads=512 ks=%d",
-                   c.mi, c.wc, c.wk, sw, bf, p.zp ? "true" : "false", p.bits, c.tiles, c.ks);
+                   "%s<%d, %d, %d, %s, %s, %s, %d> workgroups=%d threads=512 ks=%d",
+                   c.sk_upw > 0 ? "transition_sk_kernel" : "transition_kernel", c.mi, c.wc,
+                   c.wk, sw, bf, p.zp ? "true" : "false", p.bits, c.tiles, c.ks);
+  if (c.sk_upw > 0 && k > 0 && (size_t)k < n) {
+    k += snprintf(buf + k, n - k, " stream-k units=%d per_workgroup=%d", c.sk_units, c.sk_upw);
+    if (c.sk_parts > 1 && k > 0 && (size_t)k < n)
+      k += snprintf(buf + k, n - k, "; transition_sk_reduce_kernel<%s, %s>", sw, bf);
+    return k;
+  }
   if (c.ks > 1 && k > 0 && (size_t)k < n)
     k += snprintf(buf + k, n - k, "; prefill_reduce_kernel<%s, %s>", sw, bf);
   return k;
@@ -526,9 +682,22 @@ static hipError_t launch_transition_t(const Problem &p, const TransConfig &c, vo
   a.row_tiles = c.row_tiles;
   a.col_groups = c.col_groups;
   a.KS = c.ks;
+  a.upw = c.sk_upw;
+  a.units = c.sk_units;
+  a.rt_rounds = c.sk_rounds;
   a.ws = (float *)ws;
   a.rowscale = p.rowscale;
   a.gshift = p.gshift;
+  if constexpr (BITS == 4 && !ZP) {
+    if (c.sk_upw > 0) {
+      hipLaunchKernelGGL((transition_sk_kernel<MI, WC, WK, SWIGLU, BF, ZP, BITS>),
+                         dim3(c.tiles), dim3(512), 0, s, a);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess || c.sk_parts == 1) return e;
+      return launch_sk_reduce(p, a, 32 * MI, WC, s);
+    }
+  }
+  if (c.sk_upw > 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL((transition_kernel<MI, WC, WK, SWIGLU, BF, ZP, BITS>), dim3(c.tiles),
                      dim3(512), 0, s, a);
   hipError_t e = hipGetLastError();
@@ -558,7 +727,7 @@ static hipError_t launch_transition_mi(const Problem &p, const TransConfig &c, v
 }
 
 hipError_t launch_transition(const Problem &p, const TransConfig &c, void *ws, hipStream_t s) {
-  if (c.ks > 1 && ws == nullptr) return hipErrorInvalidValue;
+  if ((c.ks > 1 || c.sk_parts > 1) && ws == nullptr) return hipErrorInvalidValue;
   if (c.mi == 4 && p.bits == 4 && !p.zp)
     return p.bf16 ? launch_transition_sw<4, true, false, 4>(p, c, ws, s)
                   : launch_transition_sw<4, false, false, 4>(p, c, ws, s);
