@@ -675,7 +675,8 @@ SWEEPS = {
                 "strip per workgroup, eight waves along K and two K splits",
         "shapes": [(8, 14336, 4096, False), (16, 14336, 4096, False), (16, 4096, 4096, False),
                    (32, 4096, 4096, False), (32, 14336, 4096, False), (4, 28672, 8192, False),
-                   (16, 28672, 8192, False), (32, 8192, 8192, False), (32, 28672, 8192, False)],
+                   (16, 28672, 8192, False), (32, 8192, 8192, False), (32, 28672, 8192, False),
+                   (8, 4096, 28672, True), (16, 4096, 28672, True)],
         "outliers": False,
         "variants": [("reduction launch", {}),
                      ("exchange", {"W4A16_SPLIT_FINISH": "exchange"}),
@@ -685,6 +686,9 @@ SWEEPS = {
                        "W4A16_COOP_KS": "2"}),
                      ("1x8 KS=2, exchange",
                       {"W4A16_DECODE_COOP": "1", "W4A16_COOP_WC": "1", "W4A16_COOP_WK": "8",
+                       "W4A16_COOP_KS": "2", "W4A16_SPLIT_FINISH": "exchange"}),
+                     ("2x4 KS=2, exchange",
+                      {"W4A16_DECODE_COOP": "1", "W4A16_COOP_WC": "2", "W4A16_COOP_WK": "4",
                        "W4A16_COOP_KS": "2", "W4A16_SPLIT_FINISH": "exchange"})],
     },
 }
