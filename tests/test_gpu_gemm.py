@@ -732,3 +732,44 @@ def test_decode_dot_one_row_bit_exact(monkeypatch):
     out = fp16_out(w4a16.gemm(to_dev(A), w, path="decode"))
     want = orc().dequant(packed, scales)[ks].view(np.float16).astype(np.float64)
     assert np.array_equal(out.astype(np.float64), want)
+
+
+def _random_decode_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        swiglu = bool(rng.integers(2))
+        M = int(rng.integers(1, 33))
+        K = 128 * int(rng.integers(4, 41))
+        N = 64 * int(rng.integers(4, 48)) if swiglu else 8 * int(rng.integers(40, 400))
+        out.append((M, K, N, swiglu, int(rng.integers(2, 6)), bool(rng.integers(2))))
+    return out
+
+
+@pytest.mark.parametrize("M,K,N,swiglu,ks,coop", _random_decode_cases(24, seed=2026))
+def test_split_exchange_random_shapes(monkeypatch, M, K, N, swiglu, ks, coop):
+    """Seeded random decode shapes with K forced into 2-5 splits on either
+    decode kernel, finished inside the launch by the exchange tree: parity
+    with the oracle, and with two splits the same bits as the reduction
+    launch that a caller's workspace gets."""
+    monkeypatch.setenv("W4A16_SPLIT_FINISH", "exchange")
+    if coop:
+        monkeypatch.setenv("W4A16_DECODE_COOP", "1")
+        monkeypatch.setenv("W4A16_COOP_KS", str(ks))
+    else:
+        monkeypatch.setenv("W4A16_DECODE_COOP", "0")
+        monkeypatch.setenv("W4A16_DECODE_KS", str(ks))
+    d = w4a16.describe(M, K, N, swiglu, path="decode")
+    say("random exchange:", d)
+    W = synth.weights(K, N, seed=M + K + N)
+    w = w4a16.load_weight(W)
+    gemm_case(M, K, N, swiglu=swiglu, path="decode", seed=M + ks, W=W, weight=w)
+    if "ks=2;" in d:
+        t = torch()
+        A = to_dev(synth.activations(M, K, seed=M + ks))
+        got = fp16_out(w4a16.gemm(A, w, swiglu=swiglu, path="decode"))
+        monkeypatch.setenv("W4A16_SPLIT_FINISH", "reduce")
+        ws = t.zeros(max(w4a16.workspace_bytes(M, K, N, swiglu, path="decode"), 256),
+                     dtype=t.uint8, device="cuda")
+        want = fp16_out(w4a16.gemm(A, w, swiglu=swiglu, path="decode", workspace=ws))
+        assert np.array_equal(got.view(np.uint16), want.view(np.uint16)), d

@@ -174,3 +174,29 @@ def test_transition_stream_k_bf16_rowscale(monkeypatch, M, swiglu, bf16):
                           bf16=bf16).startswith("transition_sk_kernel<")
     gemm_case(M, 2048, 2112, swiglu=swiglu, path="prefill", seed=M, bf16=bf16)
     rowscale_case("prefill", M, 2048, 2112, swiglu, bf16)
+
+
+def _random_transition_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        swiglu = bool(rng.integers(2))
+        M = int(rng.integers(33, 257))
+        K = 128 * int(rng.integers(4, 49))
+        N = 64 * int(rng.integers(4, 64)) if swiglu else 8 * int(rng.integers(40, 600))
+        out.append((M, K, N, swiglu, int(rng.choice([2, 4]))))
+    return out
+
+
+@pytest.mark.parametrize("M,K,N,swiglu,mi", _random_transition_cases(20, seed=77))
+def test_transition_stream_k_random_shapes(monkeypatch, M, K, N, swiglu, mi):
+    """Seeded random transition shapes through the Stream-K form (runs of
+    units that start and end anywhere in a tile, tiles shared by several
+    workgroups or finished by one): parity with the oracle."""
+    monkeypatch.setenv("W4A16_TRANSITION", "1")
+    monkeypatch.setenv("W4A16_TRANSITION_SK", "1")
+    monkeypatch.setenv("W4A16_TRANSITION_MI", str(mi))
+    d = w4a16.describe(M, K, N, swiglu=swiglu, path="prefill")
+    say("random stream-k:", d)
+    assert d.startswith("transition_sk_kernel<"), d
+    gemm_case(M, K, N, swiglu=swiglu, path="prefill", seed=M + K + N)
