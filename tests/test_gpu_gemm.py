@@ -773,3 +773,45 @@ def test_split_exchange_random_shapes(monkeypatch, M, K, N, swiglu, ks, coop):
                      dtype=t.uint8, device="cuda")
         want = fp16_out(w4a16.gemm(A, w, swiglu=swiglu, path="decode", workspace=ws))
         assert np.array_equal(got.view(np.uint16), want.view(np.uint16)), d
+
+
+@pytest.mark.parametrize("variant", ["bf16", "zp", "int8", "zp_bf16", "int8_bf16"])
+@pytest.mark.parametrize("M,K,N", [(8, 14336, 4096), (4, 28672, 8192)])
+def test_split_exchange_variants_full_size(variant, M, K, N):
+    """The in-launch exchange in the bf16, zero-point and INT8 instances of
+    the decode kernels at the full Llama down-projection shapes whose
+    automatic configuration exchanges two K splits: the library-workspace
+    call equals the caller-workspace call (reduction launch) bit for bit, and
+    sampled columns match the oracle."""
+    from gpuhelp import bf16_dev, bf16_out
+    from test_gpu_int8 import gemm8_case
+    from test_gpu_zero_points import zp_case, zp_inputs
+    t = torch()
+    bf16 = variant.endswith("bf16")
+    zp, int8 = variant.startswith("zp"), variant.startswith("int8")
+    d = w4a16.describe(M, K, N, bf16=bf16, zp=zp, int8=int8)
+    say("exchange variant:", variant, d)
+    assert "ks=2" in d and "finished in the launch (exchange)" in d, d
+    if zp:
+        w = zp_inputs(K, N, 128, seed=M)[0]
+    elif int8:
+        w = w4a16.load_weight_int8(synth.weights(K, N, seed=M))
+    else:
+        w = w4a16.load_weight(synth.weights(K, N, seed=M))
+    if bf16:
+        A = bf16_dev(synth.activations_bf16(M, K, seed=M))
+    else:
+        A = to_dev(synth.activations(M, K, seed=M))
+    ws = t.zeros(w4a16.workspace_bytes(M, K, N, bf16=bf16, zp=zp, int8=int8), dtype=t.uint8,
+                 device="cuda")
+    conv = bf16_out if bf16 else fp16_out
+    ref = conv(w4a16.gemm(A, w, workspace=ws))
+    got = conv(w4a16.gemm(A, w))
+    assert np.array_equal(np.asarray(got).view(np.uint16), np.asarray(ref).view(np.uint16)), d
+    cols = sample_indices(N, 48, seed=M, edge=8)
+    if zp:
+        zp_case(M, K, N, bf16=bf16, seed=M, cols=cols)
+    elif int8:
+        gemm8_case(M, K, N, bf16=bf16, seed=M, cols=cols)
+    else:
+        gemm_case(M, K, N, seed=M, bf16=True, cols=cols)
