@@ -621,10 +621,12 @@ def roofline_entry(res, ceilings, zp, int8, suffix):
 # after a weight change is not favoured or penalised.
 SWEEPS = {
     "transition": {
-        "what": "the transition kernel against the 1 x 8 prefill tile it replaced, and its "
-                "Stream-K form (1% outlier activations)",
+        "what": "the transition kernel against the 1 x 8 prefill tile it replaced, its "
+                "four-wave tiles and its Stream-K form (1% outlier activations; Llama-8B gate/up "
+                "and down, Llama-70B gate/up)",
         "shapes": [(m, 4096, 28672, False) for m in (48, 64, 96, 128, 192, 256, 384)]
-                  + [(m, 14336, 4096, False) for m in (48, 64, 96, 128, 192, 256, 384)],
+                  + [(m, 14336, 4096, False) for m in (48, 64, 96, 128, 192, 256, 384)]
+                  + [(m, 8192, 57344, False) for m in (48, 64, 128)],
         "outliers": True,
         "variants": [("prefill tile", {"W4A16_TRANSITION": "0"}),
                      ("transition (automatic)", {"W4A16_TRANSITION": "1"}),
@@ -633,6 +635,8 @@ SWEEPS = {
                                      "W4A16_TRANSITION_MI": "2"}),
                      ("tiles MI=4", {"W4A16_TRANSITION": "1", "W4A16_TRANSITION_SK": "0",
                                      "W4A16_TRANSITION_MI": "4"}),
+                     ("four-wave tiles", {"W4A16_TRANSITION": "1", "W4A16_TRANSITION_SK": "0",
+                                          "W4A16_TRANSITION_WAVES": "4"}),
                      ("stream-K", {"W4A16_TRANSITION": "1", "W4A16_TRANSITION_SK": "1"}),
                      ("stream-K MI=4", {"W4A16_TRANSITION": "1", "W4A16_TRANSITION_SK": "1",
                                         "W4A16_TRANSITION_MI": "4"})],
@@ -693,6 +697,7 @@ SWEEPS = {
     },
 }
 SWEEP_ENV = ("W4A16_TRANSITION", "W4A16_TRANSITION_MI", "W4A16_TRANSITION_KS", "W4A16_TRANSITION_SK",
+             "W4A16_TRANSITION_WAVES",
              "W4A16_DECODE_COOP", "W4A16_DECODE_DOT", "W4A16_DECODE_HALF",
              "W4A16_COOP_WC", "W4A16_COOP_WK", "W4A16_COOP_KS", "W4A16_SPLIT_FINISH")
 

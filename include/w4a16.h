@@ -39,7 +39,8 @@
  *   - Launch configurations are the library's measured choices.  For tests
  *     and measurement, environment variables read at every call override
  *     them (W4A16_DECODE_COOP, _HALF, _WAVES, _DEPTH, _KS, _STAGGER, _DOT;
- *     W4A16_COOP_WC, _WK, _KS; W4A16_TRANSITION, _MI, _KS, _SK; W4A16_PREFILL_V2,
+ *     W4A16_COOP_WC, _WK, _KS; W4A16_TRANSITION, _MI, _KS, _SK, _WAVES;
+ *     W4A16_PREFILL_V2,
  *     _BM, _WM, _TPS, _KS, any of which selects the prefill kernels over the
  *     transition kernel); a value no kernel supports is clamped to a
  *     supported one or ignored.  The result of a GEMM does not depend on them

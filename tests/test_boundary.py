@@ -254,6 +254,13 @@ def test_describe_names_the_launches():
     assert w4a16.describe(64, 14336, 4096).startswith(
         "transition_kernel<2, 2, 4, false, false, false, 4> workgroups=256 threads=512 ks=8; "
         "prefill_reduce_kernel<false, false>")
+    # Where the 64-row grid exceeds one workgroup per CU but fits two: four-
+    # wave workgroups, two per CU, no K split.
+    assert w4a16.describe(100, 4096, 28672, swiglu=True).startswith(
+        "transition_kernel<2, 2, 2, true, false, false, 4> workgroups=448 threads=256 ks=1")
+    assert w4a16.describe(64, 8192, 57344).startswith(
+        "transition_kernel<2, 2, 2, false, false, false, 4> workgroups=448 threads=256 ks=1")
+    assert w4a16.describe(100, 4096, 28672, swiglu=True, zp=True).startswith("prefill2_kernel<2, 1, 8")
     assert w4a16.describe(300, 4096, 28672, swiglu=True).startswith("prefill2_kernel<4, 1, 8, 2")
     assert w4a16.describe(33, 4096, 4096).startswith("transition_kernel<2, ")
     assert w4a16.describe(257, 4096, 4096).startswith("prefill2_kernel<")

@@ -200,3 +200,36 @@ def test_transition_stream_k_random_shapes(monkeypatch, M, K, N, swiglu, mi):
     say("random stream-k:", d)
     assert d.startswith("transition_sk_kernel<"), d
     gemm_case(M, K, N, swiglu=swiglu, path="prefill", seed=M + K + N)
+
+
+@pytest.mark.parametrize("ks", [0, 1, 3])
+@pytest.mark.parametrize("M,K,N,swiglu,bf16", [(33, 1152, 1064, False, False), (64, 2048, 2112, True, False),
+                                               (100, 3072, 1088, False, True), (256, 1152, 2112, True, False)])
+def test_transition_four_waves(monkeypatch, ks, M, K, N, swiglu, bf16):
+    """Four-wave workgroups (two along N, two along K, 64-row tiles), two of
+    which share a CU: ragged rows and columns, partial rounds, the automatic
+    K split for two slots per CU (ks = 0) and forced ones, SwiGLU, bf16."""
+    monkeypatch.setenv("W4A16_TRANSITION", "1")
+    monkeypatch.setenv("W4A16_TRANSITION_WAVES", "4")
+    if ks:
+        monkeypatch.setenv("W4A16_TRANSITION_KS", str(ks))
+    d = w4a16.describe(M, K, N, swiglu=swiglu, path="prefill", bf16=bf16)
+    say(d)
+    assert d.startswith("transition_kernel<2, 2, 2, ") and "threads=256" in d, d
+    if ks:
+        assert "ks=%d" % ks in d, d
+    gemm_case(M, K, N, swiglu=swiglu, path="prefill", seed=M + ks, bf16=bf16)
+
+
+def test_transition_four_waves_integer_exact(monkeypatch):
+    monkeypatch.setenv("W4A16_TRANSITION", "1")
+    monkeypatch.setenv("W4A16_TRANSITION_WAVES", "4")
+    for M, K, N in [(64, 4096, 2048), (200, 2048, 1024)]:
+        say(w4a16.describe(M, K, N, path="prefill"))
+        W = synth.grid_weights(K, N, p=4, seed=M + K)
+        A = synth.ternary_activations(M, K, density=0.5, seed=M)
+        out = fp16_out(w4a16.gemm(to_dev(A), w4a16.load_weight(W), path="prefill"))
+        packed_o, s16_o = orc().quantize_pack(W)
+        C = orc().gemm_f64(A, packed_o, s16_o)
+        assert np.abs(C).max() < 128, "inputs not fp16-exact"
+        assert np.array_equal(out.astype(np.float64), C)

@@ -74,12 +74,12 @@ constexpr int vm_wait(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4
 template <int MI, int WC, int WK, bool SWIGLU, bool BF, bool ZP, int BITS>
 __device__ __forceinline__ void transition_tile(const TransArgs &p, const int rt, const int cg,
                                                 const int gb, const int ge, const int slice) {
-  constexpr int NW = WC * WK;
-  static_assert(NW == 8, "eight waves per workgroup");
+  constexpr int NW = WC * WK, NT = NW * 64;
+  static_assert(NW == 8 || NW == 4, "eight or four waves per workgroup");
   constexpr int BM = 32 * MI;
   constexpr int CH = WK * 16;          // 16-byte chunks per staged activation row
-  constexpr int AV = BM * CH / 512;    // activation copies per lane and round
-  static_assert(BM * CH % 512 == 0, "activation tile split");
+  constexpr int AV = BM * CH / NT;     // activation copies per lane and round
+  static_assert(BM * CH % NT == 0, "activation tile split");
   constexpr int NV = BITS == 8 ? 2 : 1;               // 16-byte vectors per lane, strip, tile
   constexpr int VSTEP = BITS == 8 ? 1024 : 16;        // bytes between a lane's vectors
   static_assert(BITS == 4 || (BITS == 8 && !ZP), "INT8 weights have no zero rows");
@@ -132,17 +132,17 @@ __device__ __forceinline__ void transition_tile(const TransArgs &p, const int rt
       (void *)(ZP ? p.rz : p.rs), (short)0, p.NS * p.KG8 * 512, kBufferConfig);
 
   // Activation staging: copy i of wave `wave` fills the 64 consecutive
-  // 16-byte LDS slots from (i * 8 + wave) * 64, one per lane.  Slot s holds
+  // 16-byte LDS slots from (i * NW + wave) * 64, one per lane.  Slot s holds
   // row s / CH, physical chunk s % CH, which is the logical chunk
   // (s % CH) ^ (row & 15) of the round's WK * 128 k; the XOR stays inside the
   // 16 chunks of one group.  A lane's physical chunk is the same in every
-  // copy and its row advances by RPC = 512 / CH rows per copy, so its
+  // copy and its row advances by RPC = NT / CH rows per copy, so its
   // logical chunk takes at most two values (even and odd copies when RPC is
   // 8).  The whole offset (row, k and chunk) goes into the lane offset, which
   // the buffer's range check covers: rows past M, and the k past the end of
   // the last row that a partial last round stages (never consumed), read as
   // zero.
-  constexpr int RPC = 512 / CH;
+  constexpr int RPC = NT / CH;
   static_assert(RPC == 8 || RPC == 16, "rows per copy");
   const int row0 = (wave * 64 + lane) / CH, ph = (wave * 64 + lane) % CH;
   const int a_even = row0 * p.K * 2 + ((ph ^ (row0 & 15)) * 16);
@@ -394,7 +394,7 @@ __device__ __forceinline__ void transition_tile(const TransArgs &p, const int rt
 }
 
 template <int MI, int WC, int WK, bool SWIGLU, bool BF, bool ZP, int BITS>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(WC * WK * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void transition_kernel(TransArgs p) {
   // XCD-aware walk: workgroup ids are dealt round-robin over the 8 XCDs; each
   // XCD takes a contiguous range of (row tile, column group, K slice) triples
@@ -423,7 +423,7 @@ void transition_kernel(TransArgs p) {
 // adds the slices in that order.  The pages flush with atomic adds into the
 // output instead; the slices keep the sum deterministic.
 template <int MI, int WC, int WK, bool SWIGLU, bool BF, bool ZP, int BITS>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(WC * WK * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void transition_sk_kernel(TransArgs p) {
   // The workgroups' unit ranges are dealt by the same XCD-aware walk.
   const int T = (int)gridDim.x;
@@ -594,12 +594,33 @@ bool transition_config(const Problem &p, TransConfig &c) {
   }
   c.wk = c.mi == 2 ? 4 : 2;
   c.wc = 8 / c.wk;
+  // Four-wave workgroups (64-row tiles, INT4 weights without zero rows): two
+  // waves along N and two along K and a 32 KiB activation stage, so two
+  // workgroups share a CU and one computes while the other waits at its
+  // round barrier; the grid then fills two slots per CU.  Taken where the
+  // 64-row grid exceeds one workgroup per CU but fits two, with no K split:
+  // measured on MI355X (bench.py --sweep transition) on the Llama-8B gate/up
+  // projection at M = 96 and 128, 42.5 and 44.7 against 47.7 and 51.6 us
+  // for the 128-row tiles; where the four-wave grid needs a K split (down
+  // projections, gate/up at M <= 64) or two passes (M >= 192) it was
+  // 3-19% slower.  W4A16_TRANSITION_WAVES (4 or 8) forces the choice.
+  int slots = cus;
+  const int waves_env = env_int("W4A16_TRANSITION_WAVES", 0);
+  const bool four = p.bits == 4 && !p.zp &&
+                    (waves_env == 4 || (waves_env == 0 && mi_env == 0 && tiles2 > cus &&
+                                        tiles2 <= 2 * cus));
+  if (four) {
+    c.mi = 2;
+    c.wk = 2;
+    c.wc = 2;
+    slots = 2 * cus;
+  }
   c.col_groups = (int)ceil_div(npairs, c.wc);
   c.row_tiles = (int)ceil_div(p.M, 32 * c.mi);
   const int64_t tiles = (int64_t)c.row_tiles * c.col_groups;
   const int64_t KG = p.K / kGroup;
   c.ks = 1;
-  while (c.ks < 16 && tiles * c.ks * 2 <= cus && KG / (c.ks * 2) >= 2 * c.wk) c.ks *= 2;
+  while (c.ks < 16 && tiles * c.ks * 2 <= slots && KG / (c.ks * 2) >= 2 * c.wk) c.ks *= 2;
   const int ks_env = env_int("W4A16_TRANSITION_KS", 0);
   if (ks_env > 0) c.ks = (int)(ks_env < KG ? ks_env : KG);
   c.tiles = (int)(tiles * c.ks);
@@ -646,9 +667,9 @@ int64_t transition_workspace_bytes(const Problem &p) {
 int transition_describe(const Problem &p, const TransConfig &c, char *buf, size_t n) {
   const char *sw = p.swiglu ? "true" : "false", *bf = p.bf16 ? "true" : "false";
   int k = snprintf(buf, n,
-                   "%s<%d, %d, %d, %s, %s, %s, %d> workgroups=%d threads=512 ks=%d",
+                   "%s<%d, %d, %d, %s, %s, %s, %d> workgroups=%d threads=%d ks=%d",
                    c.sk_upw > 0 ? "transition_sk_kernel" : "transition_kernel", c.mi, c.wc,
-                   c.wk, sw, bf, p.zp ? "true" : "false", p.bits, c.tiles, c.ks);
+                   c.wk, sw, bf, p.zp ? "true" : "false", p.bits, c.tiles, c.wc * c.wk * 64, c.ks);
   if (c.sk_upw > 0 && k > 0 && (size_t)k < n) {
     k += snprintf(buf + k, n - k, " stream-k units=%d per_workgroup=%d", c.sk_units, c.sk_upw);
     if (c.sk_parts > 1 && k > 0 && (size_t)k < n)
@@ -691,7 +712,7 @@ static hipError_t launch_transition_t(const Problem &p, const TransConfig &c, vo
   if constexpr (BITS == 4 && !ZP) {
     if (c.sk_upw > 0) {
       hipLaunchKernelGGL((transition_sk_kernel<MI, WC, WK, SWIGLU, BF, ZP, BITS>),
-                         dim3(c.tiles), dim3(512), 0, s, a);
+                         dim3(c.tiles), dim3(WC * WK * 64), 0, s, a);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess || c.sk_parts == 1) return e;
       return launch_sk_reduce(p, a, 32 * MI, WC, s);
@@ -699,7 +720,7 @@ static hipError_t launch_transition_t(const Problem &p, const TransConfig &c, vo
   }
   if (c.sk_upw > 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL((transition_kernel<MI, WC, WK, SWIGLU, BF, ZP, BITS>), dim3(c.tiles),
-                     dim3(512), 0, s, a);
+                     dim3(WC * WK * 64), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || c.ks == 1) return e;
   return launch_prefill_reduce((const float *)ws, c.ks, p, s);
@@ -728,6 +749,14 @@ static hipError_t launch_transition_mi(const Problem &p, const TransConfig &c, v
 
 hipError_t launch_transition(const Problem &p, const TransConfig &c, void *ws, hipStream_t s) {
   if ((c.ks > 1 || c.sk_parts > 1) && ws == nullptr) return hipErrorInvalidValue;
+  if (c.wc * c.wk == 4) {
+    if (c.mi != 2 || p.bits != 4 || p.zp) return hipErrorInvalidValue;
+    if (p.swiglu)
+      return p.bf16 ? launch_transition_t<2, 2, 2, true, true, false, 4>(p, c, ws, s)
+                    : launch_transition_t<2, 2, 2, true, false, false, 4>(p, c, ws, s);
+    return p.bf16 ? launch_transition_t<2, 2, 2, false, true, false, 4>(p, c, ws, s)
+                  : launch_transition_t<2, 2, 2, false, false, false, 4>(p, c, ws, s);
+  }
   if (c.mi == 4 && p.bits == 4 && !p.zp)
     return p.bf16 ? launch_transition_sw<4, true, false, 4>(p, c, ws, s)
                   : launch_transition_sw<4, false, false, 4>(p, c, ws, s);
