@@ -682,12 +682,13 @@ SWEEPS = {
                    (16, 28672, 8192, False), (32, 8192, 8192, False), (32, 28672, 8192, False),
                    (8, 4096, 28672, True), (16, 4096, 28672, True)],
         "outliers": False,
-        "variants": [("reduction launch", {}),
+        "variants": [("automatic", {}),
+                     ("reduction launch", {"W4A16_SPLIT_FINISH": "reduce"}),
                      ("exchange", {"W4A16_SPLIT_FINISH": "exchange"}),
                      ("last workgroup", {"W4A16_SPLIT_FINISH": "last"}),
                      ("1x8 KS=2, reduction launch",
                       {"W4A16_DECODE_COOP": "1", "W4A16_COOP_WC": "1", "W4A16_COOP_WK": "8",
-                       "W4A16_COOP_KS": "2"}),
+                       "W4A16_COOP_KS": "2", "W4A16_SPLIT_FINISH": "reduce"}),
                      ("1x8 KS=2, exchange",
                       {"W4A16_DECODE_COOP": "1", "W4A16_COOP_WC": "1", "W4A16_COOP_WK": "8",
                        "W4A16_COOP_KS": "2", "W4A16_SPLIT_FINISH": "exchange"}),
@@ -695,10 +696,40 @@ SWEEPS = {
                       {"W4A16_DECODE_COOP": "1", "W4A16_COOP_WC": "2", "W4A16_COOP_WK": "4",
                        "W4A16_COOP_KS": "2", "W4A16_SPLIT_FINISH": "exchange"})],
     },
+    "narrow": {
+        "what": "narrow, short-K decode GEMMs (Llama-8B QKV and O, and down at M = 16 and 32): "
+                "the automatic launch against the per-wave kernel with two K splits (whole and "
+                "half strips) and the cooperative kernel with one strip per workgroup and two or "
+                "four K splits (in-launch exchange or reduction launch)",
+        "shapes": [(m, 4096, n, False) for m in (1, 8, 16, 32) for n in (6144, 4096)]
+                  + [(16, 14336, 4096, False), (32, 14336, 4096, False)],
+        "outliers": False,
+        "variants": [("automatic", {}),
+                     ("per-wave KS=2",
+                      {"W4A16_DECODE_COOP": "0", "W4A16_DECODE_HALF": "0", "W4A16_DECODE_KS": "2"}),
+                     ("per-wave half strips KS=2",
+                      {"W4A16_DECODE_COOP": "0", "W4A16_DECODE_HALF": "1", "W4A16_DECODE_KS": "2"}),
+                     ("1x8 KS=1",
+                      {"W4A16_DECODE_COOP": "1", "W4A16_COOP_WC": "1", "W4A16_COOP_WK": "8",
+                       "W4A16_COOP_KS": "1"}),
+                     ("1x8 KS=2, exchange",
+                      {"W4A16_DECODE_COOP": "1", "W4A16_COOP_WC": "1", "W4A16_COOP_WK": "8",
+                       "W4A16_COOP_KS": "2", "W4A16_SPLIT_FINISH": "exchange"}),
+                     ("1x8 KS=2, reduction launch",
+                      {"W4A16_DECODE_COOP": "1", "W4A16_COOP_WC": "1", "W4A16_COOP_WK": "8",
+                       "W4A16_COOP_KS": "2", "W4A16_SPLIT_FINISH": "reduce"}),
+                     ("1x8 KS=4, exchange",
+                      {"W4A16_DECODE_COOP": "1", "W4A16_COOP_WC": "1", "W4A16_COOP_WK": "8",
+                       "W4A16_COOP_KS": "4", "W4A16_SPLIT_FINISH": "exchange"}),
+                     ("1x4 KS=2, exchange",
+                      {"W4A16_DECODE_COOP": "1", "W4A16_COOP_WC": "1", "W4A16_COOP_WK": "4",
+                       "W4A16_COOP_KS": "2", "W4A16_SPLIT_FINISH": "exchange"})],
+    },
 }
 SWEEP_ENV = ("W4A16_TRANSITION", "W4A16_TRANSITION_MI", "W4A16_TRANSITION_KS", "W4A16_TRANSITION_SK",
              "W4A16_TRANSITION_WAVES",
-             "W4A16_DECODE_COOP", "W4A16_DECODE_DOT", "W4A16_DECODE_HALF",
+             "W4A16_DECODE_COOP", "W4A16_DECODE_DOT", "W4A16_DECODE_HALF", "W4A16_DECODE_KS",
+             "W4A16_DECODE_WAVES",
              "W4A16_COOP_WC", "W4A16_COOP_WK", "W4A16_COOP_KS", "W4A16_SPLIT_FINISH")
 
 

@@ -246,6 +246,10 @@ int w4a16_gemm_int8(const uint16_t *A_d, int64_t M, int64_t K, const void *rw_d,
  * whenever no call runs; the first such call on a device looks up their
  * address: make it outside stream capture); with a caller's workspace
  * (w4a16_gemm_ex) a second launch sums them instead, with the same bits.
+ * Where the library's layout takes two K splits only because it finishes
+ * them itself (narrow plain projections at M = 9-16, e.g. Llama-8B O and
+ * down), a caller's workspace keeps the unsplit layout instead: the two
+ * calls then differ by FP32 summation order only.
  * A shape the selected kernel cannot take (operands beyond a kernel's 32-bit
  * offsets) runs a slower kernel instead; each such fallback is reported once
  * per process on stderr and by w4a16_last_fallback (the INT4 kernels page,
@@ -288,7 +292,8 @@ int w4a16_gemm_ex(const uint16_t *A_d, int64_t M, int64_t K, const void *rw_d,
  * per GPU (w4a16_noalloc_scratch_bytes() bytes, 64 MiB, allocated with the
  * library's code object and held until the process ends) instead of a
  * workspace.  Same flags (path | W4A16_FLAG_SWIGLU | W4A16_FLAG_BF16),
- * arguments, outputs and results as w4a16_gemm_ex; the call makes no
+ * arguments and outputs as w4a16_gemm_ex, and the results (bits) of
+ * w4a16_gemm_ex on the library's workspace (workspace_d NULL); the call makes no
  * allocation, free or synchronisation of any kind.  A problem whose
  * workspace (w4a16_gemm_workspace_bytes) exceeds the scratch returns
  * W4A16_ERR_WORKSPACE before any launch (e.g. the dense tier of a large
@@ -337,7 +342,8 @@ int w4a16_rms_rowscale(const uint16_t *A_d, int64_t M, int64_t K, float eps, int
                        float *rho_d, w4a16_stream_t stream);
 
 /* Workspace bytes that w4a16_gemm_ex (w4a16_gemm_zp: add W4A16_FLAG_ZP) needs
- * for this problem and flags. */
+ * for this problem and flags; the figure also covers the launch on the
+ * library's own workspace, so it serves w4a16_reserve_workspace too. */
 int64_t w4a16_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N, int G, int flags);
 
 /* The path (W4A16_PATH_DECODE / PREFILL / DENSE) that AUTO picks for this

@@ -332,6 +332,28 @@ def test_decode_offsets_fall_back_to_prefill():
     assert w4a16.select_path(1, 1 << 28, 64) == "prefill"
 
 
+def test_split_layout_on_the_library_workspace_and_its_size(monkeypatch):
+    """Llama-8B O and down at M = 9-16 take two K splits (one strip per
+    workgroup, eight waves along K) only where the launch finishes them
+    itself; the workspace query covers both that launch and the one a
+    caller's workspace gets (Llama-8B down at M = 16: two column groups, four
+    splits, 1 MiB of partials)."""
+    d = w4a16.describe(16, 4096, 4096)
+    assert d.startswith("decode_coop_kernel<16, 1, 1, 8, 4, false, false, false, 4> "
+                        "workgroups=256 threads=512 ks=2; K splits finished in the launch"), d
+    d = w4a16.describe(9, 14336, 4096)
+    assert d.startswith("decode_coop_kernel<16, 1, 1, 8, 4, false, false, false, 4> "
+                        "workgroups=256 threads=512 ks=2; K splits finished in the launch"), d
+    assert w4a16.workspace_bytes(16, 14336, 4096) == 128 * 4 * 16 * 32 * 4
+    assert w4a16.workspace_bytes(16, 4096, 4096) == 128 * 2 * 16 * 32 * 4
+    # With the reduction launch forced, the library workspace keeps the old layout.
+    monkeypatch.setenv("W4A16_SPLIT_FINISH", "reduce")
+    assert w4a16.describe(16, 4096, 4096).startswith(
+        "decode_coop_kernel<16, 1, 1, 8, 4, false, false, false, 4> workgroups=128 "), d
+    assert w4a16.describe(16, 14336, 4096).startswith(
+        "decode_coop_kernel<16, 1, 2, 4, 4, false, false, false, 4> workgroups=256 "), d
+
+
 def test_workspace_calls_without_gpu():
     """The workspace management calls report the HIP failure on a machine
     without a GPU instead of crashing."""

@@ -250,6 +250,35 @@ def test_split_finish_in_launch(monkeypatch, finish, case, M, K, N, swiglu):
     gemm_case(M, K, N, swiglu=swiglu, path="decode", seed=M + case, W=W, weight=w)
 
 
+@pytest.mark.parametrize("M,K,N", [(16, 4096, 4096), (16, 14336, 4096), (9, 14336, 4096)])
+def test_split_layout_finished_in_launch(M, K, N):
+    """Narrow decode GEMMs at M = 9-16 whose cooperative layout takes two K
+    splits only because the launch can finish them (Llama-8B O and down): the
+    library-workspace call (two splits, exchange) and the caller-workspace
+    call (the unsplit layout) both match the oracle on sampled columns, and
+    reruns of the library-workspace call are bit-identical."""
+    t = torch()
+    desc = w4a16.describe(M, K, N)
+    say("split layout:", desc)
+    assert desc.startswith("decode_coop_kernel<16, 1, 1, 8, 4, "), desc
+    assert "ks=2; K splits finished in the launch (exchange)" in desc, desc
+    W = synth.weights(K, N, seed=M + 3)
+    w = w4a16.load_weight(W)
+    A = synth.activations(M, K, seed=M + 3)
+    dA = to_dev(A)
+    ws = t.zeros(max(w4a16.workspace_bytes(M, K, N), 256), dtype=t.uint8, device="cuda")
+    own = [fp16_out(w4a16.gemm(dA, w)) for _ in range(2)]
+    caller = fp16_out(w4a16.gemm(dA, w, workspace=ws))
+    assert np.array_equal(own[0].view(np.uint16), own[1].view(np.uint16))
+    cols = sample_indices(N, 64, seed=M, edge=8)
+    o = orc()
+    packed_o, s16_o = o.quantize_pack(np.ascontiguousarray(W[:, cols]), 128)
+    ref = o.gemm_f64(A, packed_o, s16_o, 128)
+    for name, got in (("library workspace", own[0]), ("caller workspace", caller)):
+        stats = parity.assert_close(got[:, cols], ref, "%s M=%d K=%d N=%d" % (name, M, K, N))
+        say("  ", name, {k: (round(v, 6) if isinstance(v, float) else v) for k, v in stats.items()})
+
+
 def test_split_exchange_full_size():
     """The shapes whose automatic configuration exchanges two K splits in the
     launch (Llama-8B down at M = 8, Llama-70B down at M = 4 and 16): the

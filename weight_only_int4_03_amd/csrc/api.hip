@@ -674,7 +674,14 @@ int64_t w4a16_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N, int G, int f
   const int path = resolve_path(p, flags & 0xF, &why);
   if (path < 0)
     return fail(W4A16_ERR_UNSUPPORTED, "w4a16_gemm_workspace_bytes: beyond the decode path");
-  return workspace_for(path, p);
+  // The launch on a caller's workspace can differ from the one on the
+  // library's (K splits that only a launch on the library's workspace finishes
+  // itself): the size covers both, for w4a16_gemm_ex and for
+  // w4a16_reserve_workspace alike.
+  const int64_t own = workspace_for(path, p);
+  p.own_ws = false;
+  const int64_t caller = workspace_for(path, p);
+  return own > caller ? own : caller;
 }
 
 int w4a16_describe(int64_t M, int64_t K, int64_t N, int G, int flags, char *buf, int64_t len) {

@@ -653,7 +653,11 @@ static bool decode_stagger(const Problem &p) {
 // only for calls on the library's own workspace or fixed scratch, whose calls
 // must not overlap in time on one device anyway.  A call with a caller's
 // workspace keeps the reduction launch, which gives the same bits (two
-// partials: p0 + p1 either way).  W4A16_SPLIT_FINISH=exchange, =last (the
+// partials: p0 + p1 either way), except where the cooperative kernel's
+// configuration itself takes two K splits only because they can be finished
+// in the launch (coop_config: Llama-8B O and down at M = 9-16); a caller's
+// workspace then keeps the unsplit layout, and the two calls differ by FP32
+// summation order.  W4A16_SPLIT_FINISH=exchange, =last (the
 // last workgroup of a tile sums partial tiles written through to the point of
 // coherence: split_last) or =reduce overrides the choice for measurement;
 // with it set, calls that overlap in time on one device race.
@@ -679,9 +683,7 @@ static void *split_sync_address() {
   return g_split_sync[dev];
 }
 
-// How a launch with KS > 1 K splits is finished: 0 reduction launch,
-// 1 exchange, 2 last workgroup.
-static int split_finish(const Problem &p, int KS) {
+int split_finish(const Problem &p, int KS) {
   if (KS <= 1) return 0;
   const int64_t el = (p.swiglu ? p.N / 2 : ceil_div(p.N, kStrip) * kStrip) * p.M;
   int mode = p.own_ws && KS == 2 && el <= kExchangeMaxElems ? 1 : 0;

@@ -160,6 +160,11 @@ inline int64_t split_exchange_bytes(int64_t KS, int64_t elems) {
 // the split partial tiles when KS > 1).
 DecodeArgs decode_args(const Problem &p, int KS, void *workspace);
 
+// How a decode launch with KS > 1 K splits is finished: 0 reduction launch,
+// 1 in-launch exchange, 2 last workgroup (the library's choice, or the
+// W4A16_SPLIT_FINISH override).
+int split_finish(const Problem &p, int KS);
+
 // Second stage of a split-K decode launch: sums the KS partial tiles of each
 // strip group in split order and runs the epilogue.
 hipError_t launch_decode_reduce(const DecodeArgs &a, bool swiglu, bool bf16, hipStream_t s);

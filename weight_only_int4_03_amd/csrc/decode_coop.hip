@@ -503,7 +503,10 @@ static int coop_env(const char *name, int fallback) {
 //    the widest fused ones (>= 512 strip groups, fp16 INT4) take the
 //    per-wave kernel.  Narrow plain shapes with short K (K < 12288) and
 //    192-255 strip groups at M > 8, or 128-255 at M = 16: one strip per
-//    workgroup with eight waves along K.
+//    workgroup with eight waves along K (and two K splits at M = 16 where the
+//    split grid fits and the launch can finish it); the same layout with two
+//    splits for plain projections of medium depth (12288 <= K < 24576) and
+//    97-128 strip groups at M = 9-16.
 // Other narrow, short-K shapes at small M keep the per-wave kernel (its
 // half-strip grid fills the CUs without sharing activations).  W4A16_DECODE_COOP=0/1
 // forces the choice; W4A16_COOP_WC / _WK / _KS override the configuration.
@@ -561,6 +564,20 @@ bool coop_config(const Problem &p, int &WC, int &WK, int &KS) {
     // 6.57 us) and QKV ties with it at M = 8.
     use = true;
     WC = 1; WK = 8; KS = 1;
+    // Two K splits where the doubled grid still fits one workgroup per CU
+    // and the launch finishes them itself (exchange): O at M = 16, 7.05 ->
+    // 6.37 us; with the reduction launch instead (a caller's workspace) the
+    // split measured 7.95 us, so that keeps one split.
+    if (p.M == 16 && 2 * nsg <= 256 && split_finish(p, 2) == 1) KS = 2;
+  } else if (!p.swiglu && p.M > 8 && KG >= 96 && KG < 192 && nsg > 96 && 2 * nsg <= 256 &&
+             split_finish(p, 2) == 1) {
+    // Narrow plain projections of medium depth at M = 9-16 (Llama-8B down):
+    // one strip per workgroup, eight waves along K and two K splits finished
+    // in the launch, 11.77 -> 11.50 us against two column groups with four
+    // splits and the reduction launch (which a caller's workspace keeps:
+    // this layout with the reduction launch measured 13.0 us).
+    use = true;
+    WC = 1; WK = 8; KS = 2;
   } else if (p.M == 1 && wide) {
     use = true;
     WC = 1; WK = 4; KS = 1;
