@@ -2,12 +2,14 @@
 split K inside the workgroup) against the oracle on the same seeded inputs:
 ragged row counts and column tails, both tile heights, split and unsplit K
 (uneven slices, partial last rounds), the SwiGLU epilogue, bf16 activations,
-zero points, INT8 weights, other group sizes and the row factor; one-hot and
-integer-exact inputs bit for bit."""
+zero points, INT8 weights, other group sizes and the row factor, the Stream-K
+form and the four-wave workgroups (two per CU, also at full size on the
+automatic path); one-hot and integer-exact inputs bit for bit."""
 import numpy as np
 import pytest
 
-from gpuhelp import fp16_out, gemm_case, orc, say, to_dev
+import parity
+from gpuhelp import fp16_out, gemm_case, orc, sample_indices, say, to_dev
 from test_gpu_int8 import gemm8_case
 from test_gpu_zero_points import zp_case
 from weight_only_int4_03_amd import synth, w4a16
@@ -233,3 +235,39 @@ def test_transition_four_waves_integer_exact(monkeypatch):
         C = orc().gemm_f64(A, packed_o, s16_o)
         assert np.abs(C).max() < 128, "inputs not fp16-exact"
         assert np.array_equal(out.astype(np.float64), C)
+
+
+@pytest.mark.parametrize("M,K,N,swiglu", [(96, 4096, 28672, True), (128, 4096, 28672, True),
+                                          (48, 8192, 57344, True), (64, 8192, 57344, False)])
+def test_transition_four_waves_full_size(M, K, N, swiglu):
+    """The automatic launch where the 64-row grid fits two workgroups per CU
+    without a K split (Llama-8B gate/up at M = 96 and 128, Llama-70B gate/up
+    at M = 48 and 64): four-wave workgroups at full size, 1% outlier
+    activations, sampled columns with the edges.  The transition kernel
+    multiplies by the fp16-rounded dequantized weight (the pages' dequantize),
+    so the bound is taken against that reference, the one the INT4 kernels
+    page's test builds; against the exact weight (q - 8) s the outlier
+    channels' share of the weight rounding, amplified by SwiGLU, can pass the
+    2e-2 elementwise bound, so there the relative L2 and page-ratio bounds
+    apply and the distance is reported."""
+    d = w4a16.describe(M, K, N, swiglu=swiglu)
+    say("four-wave full size:", d)
+    assert d.startswith("transition_kernel<2, 2, 2, ") and "threads=256 ks=1" in d, d
+    W = synth.weights(K, N, seed=M)
+    A = synth.activations(M, K, seed=M, outliers=True)
+    out = fp16_out(w4a16.gemm(to_dev(A), w4a16.load_weight(W), swiglu=swiglu))
+    ncols = N // 2 if swiglu else N
+    cols = sample_indices(ncols, 64, seed=M, edge=8)
+    wcols = np.concatenate([cols, cols + N // 2]) if swiglu else cols
+    o = orc()
+    packed_o, s16_o = o.quantize_pack(np.ascontiguousarray(W[:, wcols]))
+    c16 = o.gemm_w16_f64(A, o.dequant(packed_o, s16_o))
+    cx = o.gemm_f64(A, packed_o, s16_o)
+    got = out[:, cols]
+    stats = parity.assert_close(got, o.swiglu_f64(c16) if swiglu else c16,
+                                "fp16-weight reference M=%d K=%d N=%d" % (M, K, N))
+    exact = parity.compare(got, o.swiglu_f64(cx) if swiglu else cx)
+    say("  fp16 weights", stats)
+    say("  exact weights", exact)
+    assert exact["finite"] and exact["rel_l2"] <= parity.REL_L2
+    assert exact["page_ratio"] < parity.PAGE_RATIO
