@@ -726,6 +726,20 @@ SWEEPS = {
                        "W4A16_COOP_KS": "2", "W4A16_SPLIT_FINISH": "exchange"})],
     },
 }
+for _kind, _what in (("int8", "INT8 weights"), ("zp", "INT4 weights with zero points")):
+    SWEEPS["transition_" + _kind] = {
+        "what": "%s in the transition window: the automatic launch against the prefill tile "
+                "and the transition kernel with eight- and four-wave workgroups (1%% outlier activations; Llama-8B "
+                "gate/up and down)" % _what,
+        "weights": _kind,
+        "shapes": [(m, 4096, 28672, True) for m in (64, 96, 128, 192)]
+                  + [(m, 14336, 4096, False) for m in (96, 128)],
+        "outliers": True,
+        "variants": [("automatic", {}),
+                     ("prefill tile", {"W4A16_TRANSITION": "0"}),
+                     ("tiles", {"W4A16_TRANSITION": "1", "W4A16_TRANSITION_WAVES": "8"}),
+                     ("four-wave tiles", {"W4A16_TRANSITION": "1", "W4A16_TRANSITION_WAVES": "4"})],
+    }
 SWEEP_ENV = ("W4A16_TRANSITION", "W4A16_TRANSITION_MI", "W4A16_TRANSITION_KS", "W4A16_TRANSITION_SK",
              "W4A16_TRANSITION_WAVES",
              "W4A16_DECODE_COOP", "W4A16_DECODE_DOT", "W4A16_DECODE_HALF", "W4A16_DECODE_KS",
@@ -749,9 +763,15 @@ def run_sweep(name, reps, torch, dev):
     print("|---|---|---|---|---|---|---|---|", flush=True)
     cache = {}
     for M, K, N, swg in sw["shapes"]:
+        kind = sw.get("weights", "int4")
         if (K, N) not in cache:
             cache.clear()
-            w = w4a16.load_weight(synth.weights(K, N, seed=0))
+            W = synth.weights(K, N, seed=0)
+            w = (w4a16.load_weight_int8 if kind == "int8" else w4a16.load_weight)(W)
+            if kind == "zp":
+                _, scales = w4a16.unrepack(w)
+                w = w4a16.zero_rows(w, scales, torch.from_numpy(
+                    synth.zero_points(K // G, N, seed=0)).to(dev))
             ncp = max(2, math.ceil(ROTATE_BYTES / w.nbytes))
             cache[(K, N)] = [w] + [w.clone() for _ in range(ncp - 1)]
         copies = cache[(K, N)]
@@ -764,8 +784,9 @@ def run_sweep(name, reps, torch, dev):
                 os.environ.pop(k, None)
             path = env.get("_path", "auto")  # a path for the call, not an environment variable
             os.environ.update({k: v for k, v in env.items() if not k.startswith("_")})
-            descs[vname] = w4a16.describe(M, K, N, swg, path=path)
-            w4a16.reserve_workspace(w4a16.workspace_bytes(M, K, N, swg, path=path))
+            flags = {"int8": kind == "int8", "zp": kind == "zp"}
+            descs[vname] = w4a16.describe(M, K, N, swg, path=path, **flags)
+            w4a16.reserve_workspace(w4a16.workspace_bytes(M, K, N, swg, path=path, **flags))
             with torch.cuda.stream(stream):
                 w4a16.gemm(A, copies[0], swiglu=swg, out=out, path=path)
             torch.cuda.synchronize()

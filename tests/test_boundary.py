@@ -260,7 +260,12 @@ def test_describe_names_the_launches():
         "transition_kernel<2, 2, 2, true, false, false, 4> workgroups=448 threads=256 ks=1")
     assert w4a16.describe(64, 8192, 57344).startswith(
         "transition_kernel<2, 2, 2, false, false, false, 4> workgroups=448 threads=256 ks=1")
-    assert w4a16.describe(100, 4096, 28672, swiglu=True, zp=True).startswith("prefill2_kernel<2, 1, 8")
+    assert w4a16.describe(100, 4096, 28672, swiglu=True, zp=True).startswith(
+        "transition_kernel<2, 2, 2, true, false, true, 4> workgroups=448 threads=256 ks=1")
+    assert w4a16.describe(128, 4096, 28672, swiglu=True, int8=True).startswith(
+        "transition_kernel<2, 2, 2, true, false, false, 8> workgroups=448 threads=256 ks=1")
+    # INT8 and zero rows leave to the prefill tile a 64-row grid beyond two workgroups per CU.
+    assert w4a16.describe(192, 4096, 28672, swiglu=True, int8=True).startswith("prefill2_kernel<")
     assert w4a16.describe(300, 4096, 28672, swiglu=True).startswith("prefill2_kernel<4, 1, 8, 2")
     assert w4a16.describe(33, 4096, 4096).startswith("transition_kernel<2, ")
     assert w4a16.describe(257, 4096, 4096).startswith("prefill2_kernel<")

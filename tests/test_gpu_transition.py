@@ -223,6 +223,29 @@ def test_transition_four_waves(monkeypatch, ks, M, K, N, swiglu, bf16):
     gemm_case(M, K, N, swiglu=swiglu, path="prefill", seed=M + ks, bf16=bf16)
 
 
+@pytest.mark.parametrize("ks", [0, 3])
+@pytest.mark.parametrize("M,G,swiglu,bf16", [(100, 128, True, False), (33, 32, False, True),
+                                             (200, 2048, True, True)])
+def test_transition_four_waves_int8_and_zero_points(monkeypatch, ks, M, G, swiglu, bf16):
+    """The four-wave instances with INT8 weights and with zero rows: ragged
+    rows and columns, group sizes 32 to 2048, SwiGLU, bf16, the row factor,
+    automatic and forced K splits."""
+    monkeypatch.setenv("W4A16_TRANSITION", "1")
+    monkeypatch.setenv("W4A16_TRANSITION_WAVES", "4")
+    if ks:
+        monkeypatch.setenv("W4A16_TRANSITION_KS", str(ks))
+    N = 2112 if swiglu else 1064
+    for kind in ("int8", "zp"):
+        d = _kernel(M, 2048, N, swiglu, bf16=bf16, **{kind: True})
+        say(kind, d)
+        assert d.startswith("transition_kernel<2, 2, 2, ") and "threads=256" in d, d
+        assert d.split(">")[0].endswith(", 8" if kind == "int8" else "true, 4"), d
+        if kind == "int8":
+            gemm8_case(M, 2048, N, G=G, swiglu=swiglu, bf16=bf16, seed=M + ks, rowscale=True)
+        else:
+            zp_case(M, 2048, N, G=G, swiglu=swiglu, bf16=bf16, seed=M + ks, rowscale=True)
+
+
 def test_transition_four_waves_integer_exact(monkeypatch):
     monkeypatch.setenv("W4A16_TRANSITION", "1")
     monkeypatch.setenv("W4A16_TRANSITION_WAVES", "4")

@@ -586,29 +586,31 @@ bool transition_config(const Problem &p, TransConfig &c) {
   // The 128-row tile fills the registers with INT4 weights and symmetric
   // scales; INT8 weights (two vectors per lane and tile) and zero rows take
   // the 64-row tile, and leave to the prefill tiles the batches whose 64-row
-  // grid would exceed one workgroup per CU (INT8 gate/up at M = 256: 106.6
-  // against 84.3 us).
+  // grid would exceed two workgroups per CU (INT8 gate/up at M = 256: 106.6
+  // against 84.3 us for the eight-wave tiles; at M = 192 the four-wave tiles
+  // tie with the prefill tile for INT8 and lose 4% with zero rows).
   if (p.bits == 8 || p.zp) {
-    if (!forced && tiles2 > cus) return false;
+    if (!forced && tiles2 > 2 * cus) return false;
     c.mi = 2;
   }
   c.wk = c.mi == 2 ? 4 : 2;
   c.wc = 8 / c.wk;
-  // Four-wave workgroups (64-row tiles, INT4 weights without zero rows): two
-  // waves along N and two along K and a 32 KiB activation stage, so two
-  // workgroups share a CU and one computes while the other waits at its
-  // round barrier; the grid then fills two slots per CU.  Taken where the
-  // 64-row grid exceeds one workgroup per CU but fits two, with no K split:
-  // measured on MI355X (bench.py --sweep transition) on the Llama-8B gate/up
-  // projection at M = 96 and 128, 42.5 and 44.7 against 47.7 and 51.6 us
-  // for the 128-row tiles; where the four-wave grid needs a K split (down
-  // projections, gate/up at M <= 64) or two passes (M >= 192) it was
-  // 3-19% slower.  W4A16_TRANSITION_WAVES (4 or 8) forces the choice.
+  // Four-wave workgroups (64-row tiles): two waves along N and two along K
+  // and a 32 KiB activation stage, so two workgroups share a CU and one
+  // computes while the other waits at its round barrier; the grid then fills
+  // two slots per CU.  Taken where the 64-row grid exceeds one workgroup per
+  // CU but fits two, with no K split: measured on MI355X (bench.py --sweep
+  // transition, transition_int8, transition_zp) on the Llama-8B gate/up
+  // projection at M = 96 and 128, INT4: 42.5 and 44.7 against 47.7 and
+  // 51.6 us for the 128-row tiles; INT8: 51.6 and 54.2 against 55.5 and
+  // 59.3 us, zero rows: 45.9 and 48.5 against 50.8 and 53.2 us for the
+  // prefill tile.  Where the four-wave grid needs a K split (down
+  // projections, gate/up at M <= 64) or two passes (M >= 192) it was 3-21%
+  // slower.  W4A16_TRANSITION_WAVES (4 or 8) forces the choice.
   int slots = cus;
   const int waves_env = env_int("W4A16_TRANSITION_WAVES", 0);
-  const bool four = p.bits == 4 && !p.zp &&
-                    (waves_env == 4 || (waves_env == 0 && mi_env == 0 && tiles2 > cus &&
-                                        tiles2 <= 2 * cus));
+  const bool four = waves_env == 4 || (waves_env == 0 && mi_env == 0 && tiles2 > cus &&
+                                       tiles2 <= 2 * cus);
   if (four) {
     c.mi = 2;
     c.wk = 2;
@@ -750,7 +752,17 @@ static hipError_t launch_transition_mi(const Problem &p, const TransConfig &c, v
 hipError_t launch_transition(const Problem &p, const TransConfig &c, void *ws, hipStream_t s) {
   if ((c.ks > 1 || c.sk_parts > 1) && ws == nullptr) return hipErrorInvalidValue;
   if (c.wc * c.wk == 4) {
-    if (c.mi != 2 || p.bits != 4 || p.zp) return hipErrorInvalidValue;
+    if (c.mi != 2) return hipErrorInvalidValue;
+    if (p.bits == 8)
+      return p.swiglu ? (p.bf16 ? launch_transition_t<2, 2, 2, true, true, false, 8>(p, c, ws, s)
+                                : launch_transition_t<2, 2, 2, true, false, false, 8>(p, c, ws, s))
+                      : (p.bf16 ? launch_transition_t<2, 2, 2, false, true, false, 8>(p, c, ws, s)
+                                : launch_transition_t<2, 2, 2, false, false, false, 8>(p, c, ws, s));
+    if (p.zp)
+      return p.swiglu ? (p.bf16 ? launch_transition_t<2, 2, 2, true, true, true, 4>(p, c, ws, s)
+                                : launch_transition_t<2, 2, 2, true, false, true, 4>(p, c, ws, s))
+                      : (p.bf16 ? launch_transition_t<2, 2, 2, false, true, true, 4>(p, c, ws, s)
+                                : launch_transition_t<2, 2, 2, false, false, true, 4>(p, c, ws, s));
     if (p.swiglu)
       return p.bf16 ? launch_transition_t<2, 2, 2, true, true, false, 4>(p, c, ws, s)
                     : launch_transition_t<2, 2, 2, true, false, false, 4>(p, c, ws, s);
