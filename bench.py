@@ -726,6 +726,20 @@ SWEEPS = {
                        "W4A16_COOP_KS": "2", "W4A16_SPLIT_FINISH": "exchange"})],
     },
 }
+SWEEPS["coop4"] = {
+    "what": "cooperative decode workgroups of four waves (two per CU) against the automatic "
+            "eight-wave layout on the fused and 32-row projections",
+    "shapes": [(m, 4096, 28672, True) for m in (8, 16, 32)] + [(m, 8192, 57344, True) for m in (16, 32)]
+              + [(32, 4096, 6144, False), (32, 14336, 4096, False), (32, 8192, 10240, False)],
+    "outliers": False,
+    "variants": [("automatic", {}),
+                 ("1x4", {"W4A16_DECODE_COOP": "1", "W4A16_COOP_WC": "1", "W4A16_COOP_WK": "4",
+                          "W4A16_COOP_KS": "1"}),
+                 ("2x2", {"W4A16_DECODE_COOP": "1", "W4A16_COOP_WC": "2", "W4A16_COOP_WK": "2",
+                          "W4A16_COOP_KS": "1"}),
+                 ("1x4 KS=2", {"W4A16_DECODE_COOP": "1", "W4A16_COOP_WC": "1", "W4A16_COOP_WK": "4",
+                               "W4A16_COOP_KS": "2"})],
+}
 for _kind, _what in (("int8", "INT8 weights"), ("zp", "INT4 weights with zero points")):
     SWEEPS["transition_" + _kind] = {
         "what": "%s in the transition window: the automatic launch against the prefill tile "
