@@ -601,8 +601,8 @@ bool transition_config(const Problem &p, TransConfig &c) {
   // two slots per CU.  Taken where the 64-row grid exceeds one workgroup per
   // CU but fits two, with no K split: measured on MI355X (bench.py --sweep
   // transition, transition_int8, transition_zp) on the Llama-8B gate/up
-  // projection at M = 96 and 128, INT4: 42.5 and 44.7 against 47.7 and
-  // 51.6 us for the 128-row tiles; INT8: 51.6 and 54.2 against 55.5 and
+  // projection at M = 96 and 128, INT4: 41.6 and 44.4 against 46.9 and
+  // 51.4 us for the 128-row tiles (prefill tile 47.7 and 50.0); INT8: 51.6 and 54.2 against 55.5 and
   // 59.3 us, zero rows: 45.9 and 48.5 against 50.8 and 53.2 us for the
   // prefill tile.  Where the four-wave grid needs a K split (down
   // projections, gate/up at M <= 64) or two passes (M >= 192) it was 3-21%
