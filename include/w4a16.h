@@ -372,8 +372,9 @@ const char *w4a16_last_fallback(void);
 
 /* Writes into buf (len bytes, NUL-terminated, truncated if short) a text
  * description of the launches w4a16_gemm_ex would make for this problem and
- * flags: each kernel instance as it is named in profiler output, with its
- * grid.  Host only; touches no device.  Returns the length written or a
+ * flags on the library's workspace (workspace_d NULL; a caller's workspace
+ * can change the decode layout, see w4a16_gemm): each kernel instance as it
+ * is named in profiler output, with its grid.  Host only; touches no device.  Returns the length written or a
  * negative error code (W4A16_ERR_INVALID for a bad shape, flag or buffer). */
 int w4a16_describe(int64_t M, int64_t K, int64_t N, int G, int flags, char *buf, int64_t len);
 
